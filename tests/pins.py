@@ -1,0 +1,348 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Every pin takes an oracle handle (``oracle.Oracle``) and raises ``AssertionError`` when the
+oracle disagrees with the fact it checks.  The same pins run against the real oracle
+(``test_oracle_pins.py``) and against copies of the oracle with a planted mistake
+(``test_oracle_mutants.py``), where at least one pin must fail for every mistake.
+
+None of these pins re-types the oracle's own code: they use hand-derived fixtures
+(``tests/golden``), exact rational arithmetic, closed forms of the Gaussian, invariants of
+the quantizers, numpy's library routines (``rint``, ``clip``, ``matmul``) on special cases,
+and brute force on tiny inputs.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def f32_of_fraction(fr: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) fp32 value of an exact rational."""
+    if fr == 0:
+        return np.float32(0.0)
+    sign = -1 if fr < 0 else 1
+    fr = abs(fr)
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    e = max(e, -126)  # below the normal range the spacing stays 2^-149
+    scaled = fr * Fraction(2) ** (23 - e)
+    n = scaled.numerator // scaled.denominator
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    value = Fraction(n) * Fraction(2) ** (e - 23)
+    return np.float32(sign * float(value))
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64([7, *key]))
+
+
+# ------------------------------------------------------------------ O1: gamma = mean |W|
+
+def pin_gamma_exact_rational(orc):
+    """gamma equals the correctly rounded exact mean of |W| on small tensors."""
+    for t in range(40):
+        g = _rng(1, t)
+        n = int(g.integers(1, 64))
+        W = (g.standard_normal(n) * 0.02).astype(np.float32)
+        exact = sum(Fraction(float(abs(w))) for w in W) / n
+        got, _ = orc.gamma(W)
+        assert got == f32_of_fraction(exact), (t, got, f32_of_fraction(exact))
+
+
+def pin_gamma_hand_example(orc):
+    fx = golden("round_clip_ties.json")
+    W = np.array(fx["W"], dtype=np.float32)
+    got, g64 = orc.gamma(W)
+    assert got == np.float32(fx["gamma"]) and g64 == fx["gamma"]
+
+
+def pin_gamma_closed_forms(orc):
+    """Constant magnitude gives that magnitude; all-zero gives 0; scaling by 2^j is exact."""
+    W = np.full((4, 32), -0.375, dtype=np.float32)
+    W[::2] *= -1
+    assert orc.gamma(W)[0] == np.float32(0.375)
+    assert orc.gamma(np.zeros((3, 16), np.float32))[0] == 0.0
+    X = workloads.gaussian((8, 64), (11,), 0.02)
+    g0 = orc.gamma(X)[0]
+    for j in (-3, 5):
+        assert orc.gamma(X * np.float32(2.0 ** j))[0] == g0 * np.float32(2.0 ** j)
+
+
+def pin_gamma_gaussian(orc):
+    """W ~ N(0, s^2): E|W| = s * sqrt(2/pi); std of the mean of |z| is sqrt(1 - 2/pi)/sqrt(n)."""
+    s = 0.02
+    W = workloads.gaussian((1024, 1024), (12,), s)
+    g, _ = orc.gamma(W)
+    n = W.size
+    tol = 5 * math.sqrt(1 - 2 / math.pi) / math.sqrt(n)
+    assert abs(float(g) / s - math.sqrt(2 / math.pi)) < tol, float(g) / s
+
+
+# ------------------------------------------------------------- O2: ternary codes
+
+def pin_codes_tie_example(orc):
+    fx = golden("round_clip_ties.json")
+    W = np.array(fx["W"], dtype=np.float32)
+    g, _ = orc.gamma(W)
+    assert orc.ternary_codes(W, g).tolist() == fx["codes"]
+
+
+def pin_codes_boundaries(orc):
+    fx = golden("round_clip_ties.json")["boundary_cases_gamma_2"]
+    ulp_up = 2.0 ** -24
+    ulp_dn = 2.0 ** -25
+    xs = [0.5, -0.5, 0.5 + ulp_up, -(0.5 + ulp_up), 0.5 - ulp_dn, -(0.5 - ulp_dn), 1, -1, 7, -7, 0]
+    W = np.array([2.0 * x for x in xs], dtype=np.float32)
+    assert orc.ternary_codes(W, np.float32(2.0)).tolist() == fx["codes"]
+
+
+def pin_codes_match_rint_clip(orc):
+    """round_clip(W/gamma) equals numpy rint(clip(W/gamma, -1, 1)) (round half to even) for
+    finite inputs, on a dense sweep of ratios around the boundaries and at random."""
+    gamma = np.float32(0.0173)
+    t = np.concatenate([np.linspace(-2, 2, 4001, dtype=np.float32),
+                        workloads.gaussian((4096,), (13,), 1.0)])
+    W = (t * gamma).astype(np.float32)
+    ref = np.rint(np.clip(W / gamma, np.float32(-1), np.float32(1))).astype(np.int8)
+    assert np.array_equal(orc.ternary_codes(W, gamma), ref)
+
+
+def pin_codes_ternary_and_gaussian_mix(orc):
+    """Codes lie in {-1, 0, +1}; for Gaussian W the zero share is P(|z| <= sqrt(2/pi)/2)."""
+    W = workloads.gaussian((1024, 1024), (14,), 0.02)
+    g, _ = orc.gamma(W)
+    c = orc.ternary_codes(W, g)
+    assert set(np.unique(c).tolist()) <= {-1, 0, 1}
+    n = c.size
+    p0 = math.erf(math.sqrt(2 / math.pi) / 2 / math.sqrt(2))
+    pm = (1 - p0) / 2
+    tol = 5 * math.sqrt(0.25 / n)
+    assert abs(np.mean(c == 0) - p0) < tol, (np.mean(c == 0), p0)
+    assert abs(np.mean(c == 1) - pm) < tol and abs(np.mean(c == -1) - pm) < tol
+
+
+def pin_codes_scaled_ternary_roundtrip(orc):
+    """quantize(alpha * C) == C for ternary C with a nonzero entry and alpha > 0."""
+    for t, alpha in enumerate((0.021, 1.0, 3.5e-3, 17.0)):
+        C = workloads.ternary((64, 96), (15, t))
+        W = (np.float32(alpha) * C.astype(np.float32)).astype(np.float32)
+        g, _ = orc.gamma(W)
+        assert np.array_equal(orc.ternary_codes(W, g), C)
+
+
+def pin_codes_zero_gamma(orc):
+    W = np.zeros((2, 16), np.float32)
+    assert not orc.ternary_codes(W, np.float32(0.0)).any()
+
+
+# ------------------------------------------------------------------ O3: packing
+
+def pin_pack_golden_word(orc):
+    fx = golden("pack_word.json")
+    codes = np.array([fx["codes"]], dtype=np.int8)
+    assert int(orc.pack(codes)[0, 0]) == int(fx["word_hex"], 16)
+
+
+def pin_pack_roundtrip_and_density(orc):
+    C = workloads.ternary((48, 160), (16,))
+    P = orc.pack(C)
+    assert P.shape == (48, 10) and P.nbytes == C.size // 4
+    assert np.array_equal(orc.unpack(P, 160), C)
+    fx = golden("footprint.json")
+    assert fx["weights"] / 4 / 1e6 == fx["packed_megabytes_2bit"]
+
+
+def pin_pack_fields_in_range(orc):
+    """Every 2-bit field is 00, 01 or 11; field 10 never appears."""
+    C = workloads.ternary((16, 256), (17,))
+    P = orc.pack(C).astype(np.uint64)
+    for s in range(0, 32, 2):
+        assert not np.any(((P >> np.uint64(s)) & np.uint64(3)) == 2)
+
+
+def pin_pack_locality(orc):
+    """Changing the code at (n, k) changes only word (n, k // 16)."""
+    C = workloads.ternary((4, 64), (18,))
+    base = orc.pack(C)
+    for n, k in ((0, 0), (1, 17), (3, 63), (2, 40)):
+        D = C.copy()
+        D[n, k] = 1 if C[n, k] != 1 else -1
+        diff = np.argwhere(orc.pack(D) != base)
+        assert diff.tolist() == [[n, k // 16]], (n, k, diff)
+
+
+# ------------------------------------------------------------ O4: activation quant
+
+def pin_acts_golden_ties(orc):
+    fx = golden("act_quant_ties.json")
+    q, s = orc.quantize_acts(np.array(fx["x"], dtype=np.float32))
+    assert q.tolist() == fx["q"] and s.tolist() == fx["s_x"]
+
+
+def pin_acts_properties(orc):
+    X = workloads.gaussian((33, 200), (19,), 1.0)
+    q, s = orc.quantize_acts(X)
+    assert q.min() >= -127 and q.max() <= 127
+    a = np.max(np.abs(X), axis=1)
+    assert np.array_equal(s, (a / np.float32(127)).astype(np.float32))
+    idx = np.argmax(np.abs(X), axis=1)
+    peak = q[np.arange(33), idx]
+    assert np.array_equal(peak, np.where(X[np.arange(33), idx] > 0, 127, -127))
+    # One-hot rows.
+    H = np.zeros((3, 64), np.float32)
+    H[0, 5], H[1, 0], H[2, 63] = 0.37, -2.0, 1e-3
+    qh, sh = orc.quantize_acts(H)
+    assert qh[0, 5] == 127 and qh[1, 0] == -127 and qh[2, 63] == 127
+    assert np.count_nonzero(qh) == 3
+    # Power-of-two scaling leaves codes unchanged and scales s_x exactly.
+    for j in (-4, 3):
+        q2, s2 = orc.quantize_acts(X * np.float32(2.0 ** j))
+        assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** j))
+    # All-zero row.
+    qz, sz = orc.quantize_acts(np.zeros((1, 32), np.float32))
+    assert not qz.any() and sz[0] == 0.0
+
+
+def pin_acts_match_fp64_rounding(orc):
+    """Codes equal round-half-even(u * 127 / a) evaluated in fp64, except possibly where the
+    fp32 and fp64 products straddle a .5 boundary (at most a one-step difference there)."""
+    X = workloads.gaussian((64, 512), (20,), 1.0)
+    q, _ = orc.quantize_acts(X)
+    a = np.max(np.abs(X.astype(np.float64)), axis=1, keepdims=True)
+    ref = np.rint(X.astype(np.float64) * 127.0 / a)
+    diff = np.abs(q.astype(np.float64) - ref)
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= 3, np.count_nonzero(diff)
+
+
+def pin_acts_bf16_widening(orc):
+    X = workloads.gaussian((9, 128), (21,), 1.0)
+    bits = workloads.f32_to_bf16_bits(X)
+    wide = workloads.bf16_bits_to_f32(bits)
+    g = workloads.gaussian((128,), (22,), 0.1) + np.float32(1)
+    for gg in (None, g):
+        qa, sa = orc.quantize_acts(bits, gg, bf16=True)
+        qb, sb = orc.quantize_acts(wide, gg)
+        assert np.array_equal(qa, qb) and np.array_equal(sa, sb)
+
+
+def pin_norm_constant_row(orc):
+    """x = c * 1, g = 1: every code is sign(c) * 127 and s_x = |c| / (127 sqrt(c^2 + eps))."""
+    getcontext().prec = 50
+    eps = np.float32(1e-6)
+    for c in (0.75, -3.0, 2.0 ** -9):
+        x = np.full((1, 96), c, np.float32)
+        q, s = orc.quantize_acts(x, np.ones(96, np.float32), float(eps))
+        assert np.all(q == (127 if c > 0 else -127))
+        ref = Decimal(abs(c)) / (Decimal(127) * (Decimal(c) ** 2 + Decimal(float(eps))).sqrt())
+        assert abs(float(s[0]) - float(ref)) <= 1e-7 * float(ref), (c, s[0], ref)
+
+
+def pin_norm_equals_normalize_then_quantize(orc):
+    """Fused SubLN + quant equals RMSNorm (fp64) followed by absmax quantization (fp64):
+    same codes except at rounding ties, same scale to fp32 precision."""
+    X = workloads.gaussian((32, 384), (23,), 1.0)
+    g = (np.float32(1) + workloads.gaussian((384,), (24,), 0.1)).astype(np.float32)
+    eps = 1e-6
+    q, s = orc.quantize_acts(X, g, eps)
+    x64 = X.astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x64 * x64, axis=1, keepdims=True) + np.float64(np.float32(eps)))
+    y = x64 * r * g.astype(np.float64)
+    a = np.max(np.abs(y), axis=1, keepdims=True)
+    ref_q = np.rint(y * 127.0 / a)
+    ref_s = a[:, 0] / 127.0
+    diff = np.abs(q - ref_q)
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= 3
+    assert np.max(np.abs(s / ref_s - 1)) < 1e-6
+
+
+# ------------------------------------------------------------ O5 + O6: product
+
+def pin_matmul_library(orc):
+    """acc equals numpy's int64 matmul Xq @ C^T on non-square shapes."""
+    Xq = _rng(25).integers(-127, 128, size=(5, 48), dtype=np.int8)
+    C = workloads.ternary((7, 48), (26,))
+    acc = orc.matmul(Xq, C)
+    assert acc.shape == (5, 7)
+    assert np.array_equal(acc, Xq.astype(np.int64) @ C.astype(np.int64).T)
+
+
+def pin_matmul_freivalds(orc):
+    """acc v == Xq (C^T v) exactly for random integer vectors v."""
+    Xq = _rng(27).integers(-127, 128, size=(40, 320), dtype=np.int8)
+    C = workloads.ternary((72, 320), (28,))
+    acc = orc.matmul(Xq, C).astype(np.int64)
+    for t in range(3):
+        v = _rng(29, t).integers(-1000, 1000, size=72)
+        lhs = acc @ v
+        rhs = Xq.astype(np.int64) @ (C.astype(np.int64).T @ v)
+        assert np.array_equal(lhs, rhs)
+
+
+def pin_forward_dequantized_product(orc):
+    """Tiny brute force: Y equals the fp64 product of the dequantized operands
+    (q * s_x) (c * gamma)^T to within fp32 output rounding."""
+    W = workloads.gaussian((24, 64), (30,), 0.02)
+    X = workloads.gaussian((6, 64), (31,), 1.0)
+    P, g, C = orc.quantize_weights(W)
+    q, s = orc.quantize_acts(X)
+    acc, Y = orc.forward(q, s, P, g)
+    deq = (q.astype(np.float64) * s.astype(np.float64)[:, None]) @ \
+        (C.astype(np.float64) * np.float64(g)).T
+    assert np.all(np.abs(Y.astype(np.float64) - deq) <= 2.0 ** -23 * np.abs(deq) + 1e-30)
+    assert np.array_equal(acc, q.astype(np.int64) @ C.astype(np.int64).T)
+
+
+def pin_forward_one_hot(orc):
+    """A one-hot token with value a at k gives y[n] = gamma * a * c[n, k] (within rounding)."""
+    W = workloads.gaussian((32, 48), (32,), 0.02)
+    P, g, C = orc.quantize_weights(W)
+    a, k = np.float32(1.75), 13
+    x = np.zeros((1, 48), np.float32)
+    x[0, k] = a
+    q, s = orc.quantize_acts(x)
+    _, Y = orc.forward(q, s, P, g)
+    ref = float(g) * float(a) * C[:, k].astype(np.float64)
+    assert np.allclose(Y[0], ref, rtol=3e-7, atol=0)
+
+
+def pin_forward_entries_match_full(orc):
+    W = workloads.gaussian((40, 96), (33,), 0.02)
+    X = workloads.gaussian((9, 96), (34,), 1.0)
+    P, g, _ = orc.quantize_weights(W)
+    q, s = orc.quantize_acts(X)
+    acc, Y = orc.forward(q, s, P, g)
+    m = np.array([0, 8, 3, 5]), np.array([39, 0, 17, 22])
+    ea, ey = orc.forward_entries(q, s, P, g, *m)
+    assert np.array_equal(ea, acc[m]) and np.array_equal(ey, Y[m])
+
+
+def pin_quantize_weights_chain(orc):
+    """The packed output of the whole weight chain unpacks to round_clip(W/gamma)."""
+    W = workloads.gaussian((20, 80), (35,), 0.02)
+    P, g, C = orc.quantize_weights(W)
+    g_ref = f32_of_fraction(sum(Fraction(float(abs(w))) for w in W.ravel()) / W.size)
+    assert g == g_ref
+    t = W.astype(np.float32) / g
+    ref = np.where(t > 0.5, 1, np.where(t < -0.5, -1, 0)).astype(np.int8)
+    assert np.array_equal(orc.unpack(P, 80), ref) and np.array_equal(C, ref)
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
