@@ -1,0 +1,281 @@
+"""Python binding of libbitlinear: the BitNet b1.58 BitLinear forward on MI355X (gfx950).
+
+Argument marshalling only.  Each function checks the tensors it is given, allocates missing
+outputs with torch (device memory is torch's), and calls the C entry point of the same name
+(``bitlinear_<name>`` in ``include/bitlinear.h``) on the current torch stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback: if the library is
+missing or a call is rejected, an exception is raised.
+
+Steps (see the header for the passages each follows):
+  quantize_weights  gamma = mean|W| and 2-bit packed ternary codes
+  pack_codes        pack pre-ternarized int8 codes
+  quantize_acts     per-token absmax int8 activations (optionally with the SubLN RMSNorm)
+  forward           exact int32 ternary x int8 product and the gamma * s_x epilogue
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libbitlinear.so")
+
+BL_F32, BL_BF16 = 0, 1
+MAX_GROUP = 16
+MAX_K = 262144
+DECODE_MAX_M = 16
+
+
+class BitLinearError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class _WeightProblem(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _ActProblem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("x_dtype", ctypes.c_int),
+                ("eps", ctypes.c_float)]
+
+
+class _ForwardProblem(ctypes.Structure):
+    _fields_ = [("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbitlinear.so (built by ``bit_gemm_02_amd.build``); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(f"{LIBRARY} is missing: build it with `python -m bit_gemm_02_amd.build`")
+    L = ctypes.CDLL(LIBRARY)
+    P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    L.bitlinear_status_string.argtypes = [ctypes.c_int]
+    L.bitlinear_status_string.restype = ctypes.c_char_p
+    L.bitlinear_abi_version.argtypes = []
+    L.bitlinear_abi_version.restype = ctypes.c_int
+    L.bitlinear_quantize_weights_workspace.argtypes = [I64, I64]
+    L.bitlinear_quantize_weights_workspace.restype = SZ
+    L.bitlinear_quantize_weights.argtypes = [P, I64, I64, P, P, P, SZ, P]
+    L.bitlinear_quantize_weights.restype = ctypes.c_int
+    L.bitlinear_quantize_weights_grouped_workspace.argtypes = [ctypes.c_int]
+    L.bitlinear_quantize_weights_grouped_workspace.restype = SZ
+    L.bitlinear_quantize_weights_grouped.argtypes = [P, ctypes.c_int, P, SZ, P]
+    L.bitlinear_quantize_weights_grouped.restype = ctypes.c_int
+    L.bitlinear_pack_codes.argtypes = [P, I64, I64, P, P]
+    L.bitlinear_pack_codes.restype = ctypes.c_int
+    L.bitlinear_quantize_acts.argtypes = [P, ctypes.c_int, I64, I64, P, ctypes.c_float, P, P, P]
+    L.bitlinear_quantize_acts.restype = ctypes.c_int
+    L.bitlinear_quantize_acts_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_quantize_acts_grouped.restype = ctypes.c_int
+    L.bitlinear_forward.argtypes = [P, P, P, P, I64, I64, I64, P, P, P]
+    L.bitlinear_forward.restype = ctypes.c_int
+    L.bitlinear_forward_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_forward_grouped.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().bitlinear_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise BitLinearError(fn, status)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def quantize_weights_workspace_bytes(count: int = 1) -> int:
+    return int(lib().bitlinear_quantize_weights_grouped_workspace(count))
+
+
+def quantize_weights(W: torch.Tensor, W_packed: Optional[torch.Tensor] = None,
+                     gamma: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """W fp32 [N, K] -> (W_packed int32 [N, K/16] holding uint32 words, gamma fp32 [1])."""
+    _dev(W, "W", torch.float32)
+    N, K = W.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+    if gamma is None:
+        gamma = torch.empty(1, dtype=torch.float32, device=W.device)
+    ws_bytes = quantize_weights_workspace_bytes(1)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=W.device)
+    _check("bitlinear_quantize_weights",
+           lib().bitlinear_quantize_weights(_ptr(W), N, K, _ptr(W_packed), _ptr(gamma),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
+    return W_packed, gamma
+
+
+def quantize_weights_grouped(Ws: Sequence[torch.Tensor],
+                             outputs: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor]]] = None,
+                             workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+    """Several independent weight tensors in one grouped call (two kernel launches)."""
+    count = len(Ws)
+    arr = (_WeightProblem * max(count, 1))()
+    outs = []
+    for i, W in enumerate(Ws):
+        _dev(W, f"W[{i}]", torch.float32)
+        N, K = W.shape
+        if outputs is not None:
+            P, g = outputs[i]
+        else:
+            P = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+            g = torch.empty(1, dtype=torch.float32, device=W.device)
+        outs.append((P, g))
+        arr[i] = _WeightProblem(_ptr(W), _ptr(P), _ptr(g), N, K)
+    ws_bytes = quantize_weights_workspace_bytes(max(count, 1))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
+    _check("bitlinear_quantize_weights_grouped",
+           lib().bitlinear_quantize_weights_grouped(ctypes.addressof(arr), count, _ptr(workspace),
+                                                    workspace.numel() * workspace.element_size(),
+                                                    _stream(stream)))
+    return outs
+
+
+def pack_codes(codes: torch.Tensor, W_packed: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Ternary int8 codes [N, K] in {-1, 0, +1} -> packed words [N, K/16] (int32 storage)."""
+    _dev(codes, "codes", torch.int8)
+    N, K = codes.shape
+    if W_packed is None:
+        W_packed = torch.empty((N, K // 16), dtype=torch.int32, device=codes.device)
+    _check("bitlinear_pack_codes",
+           lib().bitlinear_pack_codes(_ptr(codes), N, K, _ptr(W_packed), _stream(stream)))
+    return W_packed
+
+
+def _x_dtype(X: torch.Tensor) -> int:
+    if X.dtype == torch.float32:
+        return BL_F32
+    if X.dtype == torch.bfloat16:
+        return BL_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {X.dtype}")
+
+
+def quantize_acts(X: torch.Tensor, norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                  X_q: Optional[torch.Tensor] = None, x_scale: Optional[torch.Tensor] = None,
+                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """X fp32/bf16 [M, K] -> (X_q int8 [M, K], x_scale fp32 [M]); optional fused RMSNorm."""
+    _dev(X, "X")
+    dt = _x_dtype(X)
+    M, K = X.shape
+    if norm_weight is not None:
+        _dev(norm_weight, "norm_weight", torch.float32)
+    if X_q is None:
+        X_q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check("bitlinear_quantize_acts",
+           lib().bitlinear_quantize_acts(_ptr(X), dt, M, K, _ptr(norm_weight), float(eps),
+                                         _ptr(X_q), _ptr(x_scale), _stream(stream)))
+    return X_q, x_scale
+
+
+def quantize_acts_grouped(Xs: Sequence[torch.Tensor],
+                          norm_weights: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                          eps: float = 1e-6, outputs=None, stream=None):
+    """Several activation matrices in one launch; returns [(X_q, x_scale), ...]."""
+    count = len(Xs)
+    arr = (_ActProblem * max(count, 1))()
+    outs = []
+    for i, X in enumerate(Xs):
+        _dev(X, f"X[{i}]")
+        M, K = X.shape
+        g = None if norm_weights is None else norm_weights[i]
+        if outputs is not None:
+            Xq, sx = outputs[i]
+        else:
+            Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+            sx = torch.empty(M, dtype=torch.float32, device=X.device)
+        outs.append((Xq, sx))
+        arr[i] = _ActProblem(_ptr(X), _ptr(g), _ptr(Xq), _ptr(sx), M, K, _x_dtype(X), float(eps))
+    _check("bitlinear_quantize_acts_grouped",
+           lib().bitlinear_quantize_acts_grouped(ctypes.addressof(arr), count, _stream(stream)))
+    return outs
+
+
+def forward(X_q: torch.Tensor, x_scale: torch.Tensor, W_packed: torch.Tensor,
+            gamma: torch.Tensor, Y: Optional[torch.Tensor] = None,
+            acc: Optional[torch.Tensor] = None, return_acc: bool = False, stream=None):
+    """Y = (X_q . c^T) * gamma * x_scale[:, None] in fp32; optionally the int32 accumulators."""
+    _dev(X_q, "X_q", torch.int8)
+    M, K = X_q.shape
+    N = W_packed.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X_q.device)
+    if return_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=X_q.device)
+    _check("bitlinear_forward",
+           lib().bitlinear_forward(_ptr(X_q), _ptr(x_scale), _ptr(W_packed), _ptr(gamma), M, N, K,
+                                   _ptr(Y), _ptr(acc), _stream(stream)))
+    return (Y, acc) if return_acc else Y
+
+
+def forward_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Problems as dicts with keys X_q, x_scale, W_packed, gamma, Y and optional acc; all
+    outputs preallocated.  Decode-sized problems (M <= 16) share one launch, the rest another."""
+    count = len(problems)
+    arr = (_ForwardProblem * max(count, 1))()
+    for i, p in enumerate(problems):
+        M, K = p["X_q"].shape
+        N = p["W_packed"].shape[0]
+        arr[i] = _ForwardProblem(_ptr(p["X_q"]), _ptr(p["x_scale"]), _ptr(p["W_packed"]),
+                                 _ptr(p["gamma"]), _ptr(p["Y"]), _ptr(p.get("acc")), M, N, K)
+    _check("bitlinear_forward_grouped",
+           lib().bitlinear_forward_grouped(ctypes.addressof(arr), count, _stream(stream)))
+
+
+def linear(X: torch.Tensor, W_packed: torch.Tensor, gamma: torch.Tensor,
+           norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None):
+    """Convenience: quantize_acts followed by forward (two launches)."""
+    Xq, sx = quantize_acts(X, norm_weight, eps, stream=stream)
+    return forward(Xq, sx, W_packed, gamma, stream=stream)

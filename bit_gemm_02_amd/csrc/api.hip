@@ -1,0 +1,235 @@
+// api.hip — the C ABI entry points (include/bitlinear.h): argument validation, problem
+// tables and kernel dispatch.  Validation follows the input checks the bitone README lists
+// for its native bridge (null pointers, shapes/bounds, alignment, dtype) and runs entirely on
+// the host before anything is launched, so a rejected call touches no device memory.
+#include <limits.h>
+
+#include "common.hpp"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bl_status check_k(int64_t K)
+{
+    if (K <= 0 || K % 16 != 0 || K > BL_MAX_K)
+        return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+bl_status check_rows(int64_t R)
+{
+    if (R < 0 || R > BL_MAX_ROWS)
+        return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
+bl_status check_weight(const bl_weight_problem &p)
+{
+    // An empty tensor (N == 0) may come with NULL data pointers; gamma is still written.
+    if (!p.gamma || (p.N != 0 && (!p.W || !p.W_packed)))
+        return BL_ERR_NULL;
+    bl_status s = check_rows(p.N);
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (p.N * p.K / 4 > (int64_t)INT_MAX * 4096)
+        return BL_ERR_SHAPE;  // keeps the pack grid within 2^31 blocks
+    if (!aligned16(p.W) || !aligned16(p.W_packed) || (reinterpret_cast<uintptr_t>(p.gamma) & 3u))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status check_act(const bl_act_problem &p)
+{
+    if (p.M != 0 && (!p.X || !p.X_q || !p.x_scale))
+        return BL_ERR_NULL;
+    if (p.x_dtype != BL_F32 && p.x_dtype != BL_BF16)
+        return BL_ERR_DTYPE;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(p.X) || !aligned16(p.X_q) || (reinterpret_cast<uintptr_t>(p.x_scale) & 3u) ||
+        (p.norm_weight && !aligned16(p.norm_weight)))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status check_forward(const bl_forward_problem &p)
+{
+    // Empty products (M == 0 or N == 0) launch nothing and may pass NULL for empty tensors.
+    const bool empty = p.M == 0 || p.N == 0;
+    if (!p.gamma || (!empty && (!p.X_q || !p.x_scale || !p.W_packed || !p.Y)))
+        return BL_ERR_NULL;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK)
+        s = check_rows(p.N);
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(p.X_q) || !aligned16(p.W_packed) || (reinterpret_cast<uintptr_t>(p.x_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(p.gamma) & 3u) || (reinterpret_cast<uintptr_t>(p.Y) & 3u) ||
+        (reinterpret_cast<uintptr_t>(p.acc) & 3u))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *bitlinear_status_string(int status)
+{
+    switch (status) {
+    case BL_OK: return "ok";
+    case BL_ERR_NULL: return "null pointer argument";
+    case BL_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 16, or above limits)";
+    case BL_ERR_ALIGN: return "misaligned pointer (tensors need 16-byte alignment)";
+    case BL_ERR_DTYPE: return "unknown activation dtype";
+    case BL_ERR_WORKSPACE: return "workspace too small";
+    case BL_ERR_HIP: return "HIP launch failed";
+    case BL_ERR_COUNT: return "invalid problem count";
+    default: return "unknown status";
+    }
+}
+
+int bitlinear_abi_version(void) { return 100; }
+
+size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
+{
+    (void)N;
+    (void)K;
+    return bl::quantize_weights_workspace(1);
+}
+
+size_t bitlinear_quantize_weights_grouped_workspace(int count)
+{
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return 0;
+    return bl::quantize_weights_workspace(count);
+}
+
+bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, int count,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_weight(problems[i]);
+        if (s != BL_OK)
+            return s;
+    }
+    if (!workspace)
+        return BL_ERR_NULL;
+    if (!aligned16(workspace))
+        return BL_ERR_ALIGN;
+    if (workspace_bytes < bl::quantize_weights_workspace(count))
+        return BL_ERR_WORKSPACE;
+    return from_hip(bl::launch_quantize_weights(problems, count, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, uint32_t *W_packed,
+                                     float *gamma, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    bl_weight_problem p{W, W_packed, gamma, N, K};
+    return bitlinear_quantize_weights_grouped(&p, 1, workspace, workspace_bytes, stream);
+}
+
+bl_status bitlinear_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
+                               void *stream)
+{
+    bl_status s = check_rows(N);
+    if (s == BL_OK && N != 0 && (!codes || !W_packed))
+        return BL_ERR_NULL;
+    if (s == BL_OK)
+        s = check_k(K);
+    if (s != BL_OK)
+        return s;
+    if (N * K / 16 > (int64_t)INT_MAX * 256)
+        return BL_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(W_packed))
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_pack_codes(codes, N, K, W_packed, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_act(problems[i]);
+        if (s != BL_OK)
+            return s;
+        rows += problems[i].M;
+    }
+    if (rows > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_quantize_acts(problems, count, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quantize_acts(const void *X, int x_dtype, int64_t M, int64_t K,
+                                  const float *norm_weight, float eps, int8_t *X_q,
+                                  float *x_scale, void *stream)
+{
+    bl_act_problem p{X, norm_weight, X_q, x_scale, M, K, x_dtype, eps};
+    return bitlinear_quantize_acts_grouped(&p, 1, stream);
+}
+
+bl_status bitlinear_forward_grouped(const bl_forward_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl_forward_problem dec[BL_MAX_GROUP], pre[BL_MAX_GROUP];
+    int nd = 0, np = 0;
+    int64_t dec_blocks = 0, pre_blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_forward_problem &p = problems[i];
+        bl_status s = check_forward(p);
+        if (s != BL_OK)
+            return s;
+        if (p.M <= bl::kDecodeMaxM) {
+            dec[nd++] = p;
+            dec_blocks += (p.N + 15) / 16;
+        } else {
+            pre[np++] = p;
+            pre_blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        }
+    }
+    if (dec_blocks > INT_MAX || pre_blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (nd) {
+        bl_status s = from_hip(bl::launch_forward_decode(dec, nd, st));
+        if (s != BL_OK)
+            return s;
+    }
+    if (np)
+        return from_hip(bl::launch_forward_prefill(pre, np, st));
+    return BL_OK;
+}
+
+bl_status bitlinear_forward(const int8_t *X_q, const float *x_scale, const uint32_t *W_packed,
+                            const float *gamma, int64_t M, int64_t N, int64_t K, float *Y,
+                            int32_t *acc, void *stream)
+{
+    bl_forward_problem p{X_q, x_scale, W_packed, gamma, Y, acc, M, N, K};
+    return bitlinear_forward_grouped(&p, 1, stream);
+}
+
+}  // extern "C"

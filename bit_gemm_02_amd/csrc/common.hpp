@@ -1,0 +1,82 @@
+// common.hpp — device helpers and launcher declarations shared by the BitLinear kernels.
+//
+// Internal to libbitlinear: nothing here is part of the C ABI (include/bitlinear.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bitlinear.h"
+
+namespace bl {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- packed-code planes
+//
+// A packed word holds 16 codes; the code of weight k = 16w + 4i + b lives at bits
+// [8b + 2i, 8b + 2i + 1] in 2-bit two's complement.  Shifting left by 6 - 2i moves plane i
+// to the top two bits of every byte; masking with 0xC0C0C0C0 leaves four int8 lanes holding
+// 64 * c for k = 16w + 4i + 0..3 (01 -> 0x40 = 64, 11 -> 0xC0 = -64, 00 -> 0).  Integer
+// dot products of these bytes are therefore exactly 64x the ternary dot product; the kernels
+// divide by 64 (an exact arithmetic shift) before the epilogue.
+__device__ __forceinline__ uint32_t plane64(uint32_t word, int i)
+{
+    return (word << (6 - 2 * i)) & 0xC0C0C0C0u;
+}
+
+// The four planes of a word, as the 16-byte operand of one 16x16x64 int8 MFMA lane:
+// byte 4i + b of the result is 64 * c for k = 16w + 4i + b (natural k order).
+__device__ __forceinline__ v4i unpack_word64(uint32_t word)
+{
+    v4i r;
+    r.x = (int)plane64(word, 0);
+    r.y = (int)plane64(word, 1);
+    r.z = (int)plane64(word, 2);
+    r.w = (int)plane64(word, 3);
+    return r;
+}
+
+// 2-bit field of one code (+1 -> 01, 0 -> 00, -1 -> 11), from "is nonzero" and "is negative".
+__device__ __forceinline__ uint32_t code_field(bool nonzero, bool negative)
+{
+    return nonzero ? (negative ? 3u : 1u) : 0u;
+}
+
+// ----------------------------------------------------------------- wave reductions
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Fixed butterfly order: every lane ends with the same value, and the order of additions
+// depends only on the lane layout, so the result is reproducible bit for bit.
+__device__ __forceinline__ double wave_sum_fixed(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v = v + __shfl_xor(v, off, kWave);
+    return v;
+}
+
+// ----------------------------------------------------------------- launchers
+
+hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *workspace,
+                                   hipStream_t stream);
+size_t quantize_weights_workspace(int count);
+hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
+                             hipStream_t stream);
+hipError_t launch_quantize_acts(const bl_act_problem *p, int count, hipStream_t stream);
+hipError_t launch_forward_decode(const bl_forward_problem *p, int count, hipStream_t stream);
+hipError_t launch_forward_prefill(const bl_forward_problem *p, int count, hipStream_t stream);
+
+// Token count up to which bitlinear_forward uses the decode (streaming) kernel.
+constexpr int64_t kDecodeMaxM = 16;
+
+}  // namespace bl

@@ -1,0 +1,208 @@
+/*
+ * bitlinear.h — C ABI of the BitNet b1.58 BitLinear forward for AMD Instinct MI355X (gfx950).
+ *
+ * The forward has five steps (Distillix README, "Key Innovations 1. BitNet b1.58 Core";
+ * bitone README, "Features": Triton-fused BitLinear forward; SLM750-Edge 1.58-bit model card,
+ * §3.1 "Ternary Weight Quantization"; BitDistill article, "Stage 1 — Architectural refinement
+ * with SubLN" and its INT8-activation deployment):
+ *
+ *   1. gamma = mean(|W|) over one weight tensor W [N][K]          bitlinear_quantize_weights
+ *   2. ternary codes c = round(clip(W / gamma, -1, 1)), packed    bitlinear_quantize_weights
+ *      2 bits per weight, 16 per uint32                           (or bitlinear_pack_codes)
+ *   3. per-token absmax int8 activations (optionally with the     bitlinear_quantize_acts
+ *      SubLN RMSNorm folded in)
+ *   4. acc = X_q · c^T, exact int32                               bitlinear_forward
+ *   5. Y = acc · gamma · s_x, fp32                                bitlinear_forward
+ *
+ * General rules for every entry point:
+ *   * Every pointer argument is a DEVICE pointer (HIP device memory visible to the GPU that
+ *     owns `stream`), owned by the caller, 16-byte aligned, and the tensor behind it is dense
+ *     row-major.  Pointers to empty tensors (a zero dimension) may be NULL.  The library never
+ *     allocates, frees, copies to the host or synchronizes.
+ *   * `stream` is a hipStream_t passed as void* (NULL = the legacy default stream).  All work
+ *     is enqueued on it and the call returns at once; results are ready when the stream is.
+ *   * A non-zero status means the arguments were rejected: nothing was launched and no output
+ *     was written.  BL_ERR_HIP means a launch failed after validation (outputs undefined).
+ *     Faults inside kernels surface asynchronously, at the caller's next synchronization.
+ *   * Data values are not checked (NaN/Inf are outside the method's domain; see below for
+ *     the degenerate cases that are defined).
+ *   * Calls are stateless and thread-safe; two calls on different streams may run
+ *     concurrently when their output buffers do not overlap.
+ *
+ * Packed weight layout (the pages fix only the density — Distillix README, "Memory
+ * Footprint": ~25 MB for ~100M weights, 2 bits each): row n of W_packed holds K/16 uint32
+ * words; word w holds k in [16w, 16w+16); the code of weight k = 16w + 4i + b sits at bits
+ * [8b + 2i, 8b + 2i + 1] as a 2-bit two's complement value (+1 -> 01, 0 -> 00, -1 -> 11;
+ * 10 is never written and undefined on input).  Shifting a word left by 6 - 2i and masking
+ * with 0xC0C0C0C0 yields four int8 lanes equal to 64 * c for k = 16w + 4i + 0..3, which is
+ * how the kernels feed the integer dot-product and matrix units.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BL_OK = 0,
+    BL_ERR_NULL = -1,      /* a required pointer is NULL */
+    BL_ERR_SHAPE = -2,     /* a size is negative, K % 16 != 0, or K / M / N above the limits */
+    BL_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
+    BL_ERR_DTYPE = -4,     /* unknown activation dtype */
+    BL_ERR_WORKSPACE = -5, /* workspace smaller than bitlinear_quantize_weights_workspace() */
+    BL_ERR_HIP = -6,       /* a HIP launch failed */
+    BL_ERR_COUNT = -7      /* grouped call: count <= 0 or above BL_MAX_GROUP */
+} bl_status;
+
+typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
+
+/* K limit: 64 * 127 * K must fit in int32 (the kernels accumulate 64 * acc). */
+#define BL_MAX_K 262144
+/* M and N limit (row counts are held in 32-bit integers inside the kernels). */
+#define BL_MAX_ROWS 2147483647LL
+/* Largest number of problems one grouped call accepts. */
+#define BL_MAX_GROUP 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *bitlinear_status_string(int status);
+
+/* ABI version of this library (major * 100 + minor). */
+int bitlinear_abi_version(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Steps 1 + 2: weight quantization.
+ *
+ * Distillix README, "1. BitNet b1.58 Core": W_q = round(clip(W / mean(|W|), -1, 1)).
+ * bitone README, "Features": gamma = mean(|W|) comes from a separate one-dimensional
+ * reduction over W, and the quantized weights are never materialized as int8/fp tensors.
+ * SLM750-Edge card §3.1: round_clip(x) = +1 for x > 0.5, 0 for |x| <= 0.5, -1 below -0.5.
+ *
+ *   W          [N][K] fp32, row-major (N = output features, K = input features).
+ *   W_packed   [N][K/16] uint32 out, layout above.
+ *   gamma      [1] fp32 out: fl32(sum_{n,k} |W[n][k]| / (N K)), the sum taken in fp64 in a
+ *              fixed order (so repeated calls on the same data give the same bits).
+ *   workspace  device scratch of at least bitlinear_quantize_weights_workspace(N, K) bytes;
+ *              it may be reused between calls on the same stream.
+ * Codes are round_clip(fl32(W / gamma)) for every element, with the division rounded to
+ * nearest even; gamma == 0 gives all-zero codes.  N == 0 writes gamma = 0 and nothing else.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (N < 0, K <= 0, K % 16 != 0, K > BL_MAX_K),
+ * BL_ERR_ALIGN, BL_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------- */
+size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K);
+
+bl_status bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, uint32_t *W_packed,
+                                     float *gamma, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/* One weight tensor of a grouped weight quantization. */
+typedef struct {
+    const float *W;
+    uint32_t *W_packed;
+    float *gamma;
+    int64_t N, K;
+} bl_weight_problem;
+
+/* Grouped form: up to BL_MAX_GROUP independent tensors in two kernel launches.  Each problem
+ * has the same semantics as bitlinear_quantize_weights; the workspace must hold at least
+ * bitlinear_quantize_weights_grouped_workspace(count) bytes. */
+size_t bitlinear_quantize_weights_grouped_workspace(int count);
+
+bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, int count,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Step 2 for weights that are already ternary (pre-ternarized checkpoints): pack int8 codes.
+ *
+ *   codes      [N][K] int8 in {-1, 0, +1}; any other value gives an undefined field.
+ *   W_packed   [N][K/16] uint32 out.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN.
+ * ------------------------------------------------------------------------------------- */
+bl_status bitlinear_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Step 3: per-token absmax int8 activation quantization, optionally with SubLN RMSNorm.
+ *
+ * BitDistill article: ternary weights with INT8 activations; SubLN is inserted before the
+ * attention output projection and before the FFN output projection.  SLM750-Edge card,
+ * "Key Architectural Features": RMSNorm with epsilon 1e-6.
+ *
+ *   X          [M][K] fp32 (x_dtype = BL_F32) or bf16 (BL_BF16), row-major.
+ *   norm_weight NULL: u = x.  Otherwise [K] fp32 RMSNorm weight g, u = fl32(x * g).
+ *   eps        RMSNorm epsilon (ignored without norm_weight).
+ *   X_q        [M][K] int8 out: q = clamp(rint(fl32(u * fl32(127 / a))), -127, 127) with
+ *              a = max_k |u_k| and rint rounding half to even.
+ *   x_scale    [M] fp32 out: a / 127 without norm; fl32(a * r / 127) with norm, where
+ *              r = 1 / sqrt(mean_k(x_k^2) + eps) in fp64.  The RMS factor r > 0 cancels in
+ *              the codes, so it enters only the scale.
+ * A row with a == 0 gives q = 0 and x_scale = 0.  M == 0 is a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (M < 0, K <= 0, K % 16 != 0, K > BL_MAX_K),
+ * BL_ERR_ALIGN, BL_ERR_DTYPE.
+ * ------------------------------------------------------------------------------------- */
+bl_status bitlinear_quantize_acts(const void *X, int x_dtype, int64_t M, int64_t K,
+                                  const float *norm_weight, float eps, int8_t *X_q,
+                                  float *x_scale, void *stream);
+
+/* One activation matrix of a grouped activation quantization. */
+typedef struct {
+    const void *X;
+    const float *norm_weight;
+    int8_t *X_q;
+    float *x_scale;
+    int64_t M, K;
+    int x_dtype;
+    float eps;
+} bl_act_problem;
+
+/* Grouped form: up to BL_MAX_GROUP independent matrices in one kernel launch. */
+bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int count,
+                                          void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Steps 4 + 5: ternary x int8 product with int32 accumulation and the rescale epilogue.
+ *
+ * bitone README, "Features": Y = X @ W_q^T x gamma, weights [out, in] (nn.Linear layout);
+ * bitone README, "What is bitone?": ternary weights turn the product into additions and
+ * subtractions; the int8-activation scale s_x joins gamma in the epilogue.
+ *
+ *   X_q        [M][K] int8 (from bitlinear_quantize_acts).
+ *   x_scale    [M] fp32.
+ *   W_packed   [N][K/16] uint32.
+ *   gamma      [1] fp32 (device pointer, so a re-quantized gamma never visits the host).
+ *   Y          [M][N] fp32 out: fl32(fp64(acc * gamma * x_scale[m])).
+ *   acc        [M][N] int32 out, or NULL: acc[m][n] = sum_k X_q[m][k] * c[n][k], exact.
+ * M <= 16 runs a bandwidth-bound streaming kernel (decode); larger M runs the int8
+ * matrix-core kernel (prefill).  M == 0 or N == 0 is a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (M < 0, N < 0, K <= 0, K % 16 != 0, K > BL_MAX_K),
+ * BL_ERR_ALIGN.
+ * ------------------------------------------------------------------------------------- */
+bl_status bitlinear_forward(const int8_t *X_q, const float *x_scale, const uint32_t *W_packed,
+                            const float *gamma, int64_t M, int64_t N, int64_t K, float *Y,
+                            int32_t *acc, void *stream);
+
+/* One product of a grouped forward. */
+typedef struct {
+    const int8_t *X_q;
+    const float *x_scale;
+    const uint32_t *W_packed;
+    const float *gamma;
+    float *Y;
+    int32_t *acc;
+    int64_t M, N, K;
+} bl_forward_problem;
+
+/* Grouped form: up to BL_MAX_GROUP independent products.  Problems with M <= 16 share one
+ * decode launch and problems with M > 16 share one prefill launch. */
+bl_status bitlinear_forward_grouped(const bl_forward_problem *problems, int count,
+                                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,160 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared entry point, and
+rejects bad arguments on the host before launching anything.
+
+Rejected calls never dereference their pointers, so small fake addresses stand in for device
+buffers here.  Empty problems (M == 0) are accepted and launch nothing.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE, BL_ERR_HIP, \
+    BL_ERR_COUNT = 0, -1, -2, -3, -4, -5, -6, -7
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses
+B = 0x20000
+C = 0x30000
+D = 0x40000
+E = 0x50000
+
+
+@pytest.fixture(scope="module")
+def bl():
+    import bit_gemm_02_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def L(bl):
+    return bl.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(bl):
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(bl.library_path())
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", bl.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(bitlinear_\w+)\b", out))
+    assert set(names) <= exported
+
+
+def test_library_is_gfx950(bl):
+    data = open(bl.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(L):
+    for s in (BL_OK, BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE, BL_ERR_WORKSPACE,
+              BL_ERR_HIP, BL_ERR_COUNT):
+        assert L.bitlinear_status_string(s)
+    assert L.bitlinear_status_string(12345) == b"unknown status"
+    assert L.bitlinear_abi_version() == 100
+
+
+def test_quantize_weights_validation(L):
+    ws = L.bitlinear_quantize_weights_workspace(64, 64)
+    assert ws >= 8
+    q = L.bitlinear_quantize_weights
+    assert q(None, 4, 64, B, C, D, ws, None) == BL_ERR_NULL
+    assert q(A, 4, 64, None, C, D, ws, None) == BL_ERR_NULL
+    assert q(A, 4, 64, B, None, D, ws, None) == BL_ERR_NULL
+    assert q(A, 4, 64, B, C, None, ws, None) == BL_ERR_NULL
+    assert q(A, 4, 24, B, C, D, ws, None) == BL_ERR_SHAPE
+    assert q(A, 4, 0, B, C, D, ws, None) == BL_ERR_SHAPE
+    assert q(A, -1, 64, B, C, D, ws, None) == BL_ERR_SHAPE
+    assert q(A, 4, 262144 + 16, B, C, D, ws, None) == BL_ERR_SHAPE
+    assert q(A + 4, 4, 64, B, C, D, ws, None) == BL_ERR_ALIGN
+    assert q(A, 4, 64, B + 8, C, D, ws, None) == BL_ERR_ALIGN
+    assert q(A, 4, 64, B, C + 2, D, ws, None) == BL_ERR_ALIGN
+    assert q(A, 4, 64, B, C, D, ws - 1, None) == BL_ERR_WORKSPACE
+
+
+def test_grouped_count_validation(L, bl):
+    arr = (bl._WeightProblem * 1)()
+    arr[0] = bl._WeightProblem(A, B, C, 4, 64)
+    ws = L.bitlinear_quantize_weights_grouped_workspace(1)
+    assert L.bitlinear_quantize_weights_grouped(ctypes.addressof(arr), 0, D, ws, None) == BL_ERR_COUNT
+    assert L.bitlinear_quantize_weights_grouped(ctypes.addressof(arr), 17, D, ws, None) == BL_ERR_COUNT
+    assert L.bitlinear_quantize_weights_grouped(None, 1, D, ws, None) == BL_ERR_NULL
+    assert L.bitlinear_quantize_weights_grouped_workspace(0) == 0
+    assert L.bitlinear_quantize_weights_grouped_workspace(2) == 2 * ws
+    fa = (bl._ForwardProblem * 1)()
+    assert L.bitlinear_forward_grouped(ctypes.addressof(fa), 0, None) == BL_ERR_COUNT
+    aa = (bl._ActProblem * 1)()
+    assert L.bitlinear_quantize_acts_grouped(ctypes.addressof(aa), 17, None) == BL_ERR_COUNT
+
+
+def test_pack_codes_validation(L):
+    p = L.bitlinear_pack_codes
+    assert p(None, 4, 64, B, None) == BL_ERR_NULL
+    assert p(A, 4, 64, None, None) == BL_ERR_NULL
+    assert p(A, 4, 40, B, None) == BL_ERR_SHAPE
+    assert p(A + 1, 4, 64, B, None) == BL_ERR_ALIGN
+
+
+def test_quantize_acts_validation(L):
+    q = L.bitlinear_quantize_acts
+    assert q(None, 0, 2, 64, None, 1e-6, B, C, None) == BL_ERR_NULL
+    assert q(A, 0, 2, 64, None, 1e-6, None, C, None) == BL_ERR_NULL
+    assert q(A, 0, 2, 64, None, 1e-6, B, None, None) == BL_ERR_NULL
+    assert q(A, 2, 2, 64, None, 1e-6, B, C, None) == BL_ERR_DTYPE
+    assert q(A, -1, 2, 64, None, 1e-6, B, C, None) == BL_ERR_DTYPE
+    assert q(A, 0, -2, 64, None, 1e-6, B, C, None) == BL_ERR_SHAPE
+    assert q(A, 0, 2, 65, None, 1e-6, B, C, None) == BL_ERR_SHAPE
+    assert q(A, 0, 2, 64, D + 4, 1e-6, B, C, None) == BL_ERR_ALIGN
+    assert q(A, 1, 2, 64, None, 1e-6, B + 2, C, None) == BL_ERR_ALIGN
+    # M == 0 is a valid empty problem: accepted, nothing launched.
+    assert q(A, 0, 0, 64, None, 1e-6, B, C, None) == BL_OK
+
+
+def test_forward_validation(L):
+    f = L.bitlinear_forward
+    assert f(None, B, C, D, 1, 4, 64, E, None, None) == BL_ERR_NULL
+    assert f(A, None, C, D, 1, 4, 64, E, None, None) == BL_ERR_NULL
+    assert f(A, B, None, D, 1, 4, 64, E, None, None) == BL_ERR_NULL
+    assert f(A, B, C, None, 1, 4, 64, E, None, None) == BL_ERR_NULL
+    assert f(A, B, C, D, 1, 4, 64, None, None, None) == BL_ERR_NULL
+    assert f(A, B, C, D, 1, 4, 8, E, None, None) == BL_ERR_SHAPE
+    assert f(A, B, C, D, -1, 4, 64, E, None, None) == BL_ERR_SHAPE
+    assert f(A, B, C, D, 1, -4, 64, E, None, None) == BL_ERR_SHAPE
+    assert f(A + 8, B, C, D, 1, 4, 64, E, None, None) == BL_ERR_ALIGN
+    assert f(A, B, C + 4, D, 1, 4, 64, E, None, None) == BL_ERR_ALIGN
+    assert f(A, B, C, D, 1, 4, 64, E + 2, None, None) == BL_ERR_ALIGN
+    assert f(A, B, C, D, 1, 4, 64, E, 0x60001, None) == BL_ERR_ALIGN
+    # Empty problems are accepted and launch nothing.
+    assert f(A, B, C, D, 0, 4, 64, E, None, None) == BL_OK
+    assert f(A, B, C, D, 3, 0, 64, E, None, None) == BL_OK
+
+
+def test_binding_refuses_host_tensors(bl):
+    import torch
+    with pytest.raises(TypeError):
+        bl.quantize_weights(torch.zeros(4, 64))
+    with pytest.raises(TypeError):
+        bl.quantize_acts(torch.zeros(2, 64))
+
+
+def test_package_has_no_oracle_dependency():
+    """The product path never imports the oracle (only tests, smoke and the CPU baseline)."""
+    pkg = os.path.join(ROOT, "bit_gemm_02_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
