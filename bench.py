@@ -1,0 +1,460 @@
+#!/usr/bin/env python3
+"""Benchmark of the BitLinear forward on one MI355X.
+
+One step = one pass of the whole hot path over one layer set of the workload:
+  prefill leg (M = the workload's large token count):
+    gamma + quantize-and-pack of every fp32 master weight   (grouped: 2 launches)
+    int8 activation quantization of every input             (grouped: 1 launch)
+    ternary x int8 product + rescale epilogue               (grouped: 1 launch)
+  decode leg (M = 1, weights packed once outside timing):
+    int8 activation quantization                            (grouped: 1 launch)
+    streaming product + epilogue                            (grouped: 1 launch)
+Inputs are seeded synthetic tensors (``workloads``) resident in HBM before timing starts.
+Weights (fp32 masters for the prefill leg, packed words for the decode leg) and prefill
+activations rotate through distinct copies totalling about 1 GB, so each step reads them
+from HBM rather than from the 256 MB last-level cache.
+
+Output: one JSON line.  ``value`` is the step's algorithmic int8 operations (2 M N K summed
+over the prefill products) divided by the measured step time; decode GB/s, per-kernel
+durations, roofline fractions and the CPU-oracle baseline are reported beside it.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "BitLinear fwd: decode GB/s & prefill int8 TOPS, % of MI355X roofline"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, published (no sparsity)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "bit_gemm_02_amd", "csrc")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_distillix125m_layer",
+                    choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--prefill-tokens", type=int, default=None,
+                    help="override the prefill token count (default: the workload's largest)")
+    ap.add_argument("--rotate-bytes", type=float, default=1e9,
+                    help="bytes of distinct weight/activation copies to cycle through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="target seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--verbose", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(name: str) -> str:
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Setup:
+    """Device buffers and pre-built grouped problem tables for one workload."""
+
+    def __init__(self, torch, bl, wl: workloads.Workload, M_pre: int, rotate_bytes: float):
+        self.torch, self.bl, self.wl = torch, bl, wl
+        dev = "cuda"
+        mats = wl.matrices
+        self.count = len(mats)
+        self.M_pre = M_pre
+        self.M_dec = 1
+        t = torch
+
+        # Host inputs (seeded).
+        if wl.weights == "fp32":
+            W_host = [workloads.weight_fp32(wl, i) for i in range(self.count)]
+        else:
+            W_host = None
+        X_pre = [workloads.activations(wl, i, M_pre) for i in range(self.count)]
+        X_dec = [workloads.activations(wl, i, self.M_dec) for i in range(self.count)]
+        self.host = dict(W=W_host, X_pre=X_pre, X_dec=X_dec)
+
+        def to_dev(a):
+            if a.dtype == np.uint16:
+                return t.from_numpy(a.view(np.int16)).to(dev).view(t.bfloat16)
+            return t.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        norms = [to_dev(workloads.norm_weight(wl, i)) if m.norm else None for i, m in enumerate(mats)]
+        self.norms = norms
+
+        # Rotating copies of the prefill-leg inputs (fp32 masters + activations).
+        per_copy = sum(x.nbytes for x in X_pre) + (sum(w.nbytes for w in W_host) if W_host else 0)
+        self.R_pre = int(max(1, min(64, np.ceil(rotate_bytes / per_copy))))
+        base_X = [to_dev(x) for x in X_pre]
+        self.X_pre = [[x.clone() for x in base_X] for _ in range(self.R_pre)]
+        if W_host is not None:
+            base_W = [to_dev(w) for w in W_host]
+            self.W_pre = [[w.clone() for w in base_W] for _ in range(self.R_pre)]
+        else:
+            self.W_pre = None
+        del base_X
+
+        # Packed weights for the prefill product (written by the in-step quantization, or
+        # packed once from pre-ternarized codes).
+        self.P_pre = [t.empty((m.N, m.K // 16), dtype=t.int32, device=dev) for m in mats]
+        self.g_pre = [t.empty(1, dtype=t.float32, device=dev) for m in mats]
+        if W_host is None:
+            for i, m in enumerate(mats):
+                bl.pack_codes(to_dev(workloads.weight_codes(wl, i)), self.P_pre[i])
+                self.g_pre[i].fill_(wl.code_gamma)
+
+        # Decode weights: packed once outside timing, replicated to distinct addresses.
+        if W_host is not None:
+            dec_packed = bl.quantize_weights_grouped([to_dev(w) for w in W_host])
+        else:
+            dec_packed = list(zip(self.P_pre, self.g_pre))
+        packed_bytes = sum(p.numel() * 4 for p, _ in dec_packed)
+        self.R_dec = int(max(1, min(4096, np.ceil(rotate_bytes / packed_bytes))))
+        self.P_dec = [[p.clone() for p, _ in dec_packed] for _ in range(self.R_dec)]
+        self.g_dec = [g.clone() for _, g in dec_packed]
+        self.X_dec = [to_dev(x) for x in X_dec]
+
+        # Outputs.
+        self.act_pre = [(t.empty((M_pre, m.K), dtype=t.int8, device=dev),
+                         t.empty(M_pre, dtype=t.float32, device=dev)) for m in mats]
+        self.act_dec = [(t.empty((1, m.K), dtype=t.int8, device=dev),
+                         t.empty(1, dtype=t.float32, device=dev)) for m in mats]
+        self.Y_pre = [t.empty((M_pre, m.N), dtype=t.float32, device=dev) for m in mats]
+        self.Y_dec = [t.empty((1, m.N), dtype=t.float32, device=dev) for m in mats]
+        self.ws = t.empty(max(16, bl.quantize_weights_workspace_bytes(self.count)),
+                          dtype=t.uint8, device=dev)
+        self._build_tables()
+
+    def _build_tables(self):
+        """ctypes problem arrays, one per rotation copy, so the timed loop only calls C."""
+        import ctypes
+        bl = self.bl
+        mats = self.wl.matrices
+        n = self.count
+        self.wq_tables = []
+        if self.W_pre is not None:
+            for r in range(self.R_pre):
+                arr = (bl._WeightProblem * n)()
+                for i, m in enumerate(mats):
+                    arr[i] = bl._WeightProblem(self.W_pre[r][i].data_ptr(), self.P_pre[i].data_ptr(),
+                                               self.g_pre[i].data_ptr(), m.N, m.K)
+                self.wq_tables.append(arr)
+        self.aq_pre_tables = []
+        for r in range(self.R_pre):
+            arr = (bl._ActProblem * n)()
+            for i, m in enumerate(mats):
+                X = self.X_pre[r][i]
+                g = self.norms[i]
+                dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
+                arr[i] = bl._ActProblem(X.data_ptr(), None if g is None else g.data_ptr(),
+                                        self.act_pre[i][0].data_ptr(), self.act_pre[i][1].data_ptr(),
+                                        self.M_pre, m.K, dt, 1e-6)
+            self.aq_pre_tables.append(arr)
+        arr = (bl._ActProblem * n)()
+        for i, m in enumerate(mats):
+            X = self.X_dec[i]
+            g = self.norms[i]
+            dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
+            arr[i] = bl._ActProblem(X.data_ptr(), None if g is None else g.data_ptr(),
+                                    self.act_dec[i][0].data_ptr(), self.act_dec[i][1].data_ptr(),
+                                    1, m.K, dt, 1e-6)
+        self.aq_dec_table = arr
+        arr = (bl._ForwardProblem * n)()
+        for i, m in enumerate(mats):
+            arr[i] = bl._ForwardProblem(self.act_pre[i][0].data_ptr(), self.act_pre[i][1].data_ptr(),
+                                        self.P_pre[i].data_ptr(), self.g_pre[i].data_ptr(),
+                                        self.Y_pre[i].data_ptr(), None, self.M_pre, m.N, m.K)
+        self.fwd_pre_table = arr
+        self.fwd_dec_tables = []
+        for r in range(self.R_dec):
+            arr = (bl._ForwardProblem * n)()
+            for i, m in enumerate(mats):
+                arr[i] = bl._ForwardProblem(self.act_dec[i][0].data_ptr(), self.act_dec[i][1].data_ptr(),
+                                            self.P_dec[r][i].data_ptr(), self.g_dec[i].data_ptr(),
+                                            self.Y_dec[i].data_ptr(), None, 1, m.N, m.K)
+            self.fwd_dec_tables.append(arr)
+        import ctypes as C
+        self._addr = C.addressof
+        self.ws_ptr = self.ws.data_ptr()
+        self.ws_bytes = self.ws.numel()
+
+    # Work accounting (algorithmic, what the method must move or compute).
+    def prefill_ops(self) -> int:
+        return sum(2 * self.M_pre * m.N * m.K for m in self.wl.matrices)
+
+    def decode_bytes(self) -> int:
+        M = self.M_dec
+        return sum(m.N * m.K // 4 + M * m.K + 4 * M + 4 + 4 * M * m.N for m in self.wl.matrices)
+
+    def weight_quant_bytes(self) -> int:
+        if self.W_pre is None:
+            return 0
+        return sum(4 * m.N * m.K + m.N * m.K // 4 + 4 for m in self.wl.matrices)
+
+    def act_quant_bytes(self, M: int) -> int:
+        xb = 2 if self.wl.x_dtype == "bf16" else 4
+        return sum(M * m.K * xb + M * m.K + 4 * M + (4 * m.K if m.norm else 0) for m in self.wl.matrices)
+
+    def step(self, i: int, stream, ev=None):
+        """Enqueue one step; `ev` (dict of event lists) brackets each launch group."""
+        L = self.bl.lib()
+        rp = i % self.R_pre
+        rd = i % self.R_dec
+        n = self.count
+
+        def mark(key):
+            if ev is not None:
+                e = self.torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.setdefault(key, []).append(e)
+
+        mark("t0")
+        if self.wq_tables:
+            rc = L.bitlinear_quantize_weights_grouped(self._addr(self.wq_tables[rp]), n, self.ws_ptr,
+                                                       self.ws_bytes, stream)
+            assert rc == 0, rc
+        mark("t_wq")
+        rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[rp]), n, stream)
+        assert rc == 0, rc
+        mark("t_aq")
+        rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+        assert rc == 0, rc
+        mark("t_gemm")
+        rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_dec_table), n, stream)
+        assert rc == 0, rc
+        mark("t_aqd")
+        rc = L.bitlinear_forward_grouped(self._addr(self.fwd_dec_tables[rd]), n, stream)
+        assert rc == 0, rc
+        mark("t_dec")
+
+
+def interval_ms(ev, a, b):
+    xs = [s.elapsed_time(e) for s, e in zip(ev[a], ev[b])]
+    return float(np.mean(xs)) if xs else float("nan")
+
+
+def load_traffic():
+    """HBM traffic per launch from committed counter runs, if the kernel sources still match."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    out = {}
+    for kernel, r in rec.get("kernels", {}).items():
+        if r.get("source_sha") == source_hash(r["source"]) and r.get("workload"):
+            out[(kernel, r["workload"])] = r
+    return out
+
+
+def cpu_baseline(setup: Setup, budget_s: float):
+    """Time the CPU oracle (single thread, as written) on a bounded sample of the step."""
+    import oracle
+    orc = oracle.get()
+    wl = setup.wl
+    h = setup.host
+    mats = wl.matrices
+    macs = sum(m.N * m.K for m in mats)
+    rate_guess = 1.4e9  # MAC/s of the oracle's scalar loop on a current x86 core
+    M_s = int(max(1, min(setup.M_pre, round(budget_s * rate_guess / macs))))
+    t0 = time.perf_counter()
+    packed = []
+    for i, m in enumerate(mats):
+        if h["W"] is not None:
+            P, g, _ = orc.quantize_weights(h["W"][i])
+        else:
+            P, g = orc.pack(workloads.weight_codes(wl, i)), np.float32(wl.code_gamma)
+        packed.append((P, g))
+    t_w = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for i, m in enumerate(mats):
+        X = h["X_pre"][i][:M_s]
+        g = workloads.norm_weight(wl, i) if m.norm else None
+        q, s = orc.quantize_acts(X, g, 1e-6, bf16=(wl.x_dtype == "bf16"))
+        orc.forward(q, s, *packed[i])
+    t_pre = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    for i, m in enumerate(mats):
+        g = workloads.norm_weight(wl, i) if m.norm else None
+        q, s = orc.quantize_acts(h["X_dec"][i], g, 1e-6, bf16=(wl.x_dtype == "bf16"))
+        orc.forward(q, s, *packed[i])
+    t_dec = time.perf_counter() - t2
+    step_s = t_w + t_pre * (setup.M_pre / M_s) + t_dec
+    exact = M_s == setup.M_pre
+    sample = (f"one full step ({len(mats)} matrices: weight quantization, {setup.M_pre}-token "
+              f"prefill, 1-token decode)" if exact else
+              f"weight quantization of all {len(mats)} matrices, decode, and {M_s} of "
+              f"{setup.M_pre} prefill tokens, prefill time scaled by {setup.M_pre / M_s:.1f}")
+    return {
+        "value": setup.prefill_ops() / step_s / 1e12,
+        "unit": "TOPS",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": sample,
+        "seconds_measured": round(t_w + t_pre + t_dec, 3),
+        "seconds_per_step": round(step_s, 3),
+        "cpu": cpu_model(),
+    }
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of a known size, for scaling HBM counters."""
+    n = 256 * 1024 * 1024
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding "
+              "of this path is described in DESIGN.md and is not launched.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_gemm_02_amd as bl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = workloads.WORKLOADS[args.workload]
+    M_pre = args.prefill_tokens or max(wl.token_counts)
+    setup = Setup(torch, bl, wl, M_pre, args.rotate_bytes)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    if args.copy_calibration:
+        copy_calibration(torch)
+
+    for i in range(args.warmup):
+        setup.step(i, sptr)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, bracketed by synchronizations.
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        setup.step(args.warmup + i, sptr)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall0) * 1e3 / args.steps
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # Per-launch durations: the same steps again with events around every launch group.
+    ev = {}
+    for i in range(args.steps):
+        setup.step(args.warmup + args.steps + i, sptr, ev)
+    torch.cuda.synchronize()
+    ms = {
+        "weight_quant": interval_ms(ev, "t0", "t_wq"),
+        "act_quant_prefill": interval_ms(ev, "t_wq", "t_aq"),
+        "prefill_gemm": interval_ms(ev, "t_aq", "t_gemm"),
+        "act_quant_decode": interval_ms(ev, "t_gemm", "t_aqd"),
+        "decode_gemv": interval_ms(ev, "t_aqd", "t_dec"),
+    }
+    ms_with_events = interval_ms(ev, "t0", "t_dec")
+
+    ops = setup.prefill_ops()
+    dec_bytes = setup.decode_bytes()
+    gemm_tops = ops / (ms["prefill_gemm"] * 1e-3) / 1e12
+    dec_gbps = dec_bytes / (ms["decode_gemv"] * 1e-3) / 1e9
+    wq_bytes = setup.weight_quant_bytes()
+    aq_bytes = setup.act_quant_bytes(M_pre)
+    rooflines = {
+        "prefill_gemm": {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS,
+                         "unit": "TFLOP/s", "frac": gemm_tops / INT8_PEAK_TOPS,
+                         "us_per_launch": ms["prefill_gemm"] * 1e3,
+                         "algorithmic": f"{ops} int8 ops (2 M N K over {setup.count} products)"},
+        "decode_gemv": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
+                        "us_per_launch": ms["decode_gemv"] * 1e3,
+                        "algorithmic": f"{dec_bytes} bytes (N K / 4 + M K + 4 M + 4 + 4 M N summed)"},
+        "act_quant_prefill": {"bound": "hbm",
+                              "achieved": aq_bytes / (ms["act_quant_prefill"] * 1e-3) / 1e9,
+                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "us_per_launch": ms["act_quant_prefill"] * 1e3},
+    }
+    rooflines["act_quant_prefill"]["frac"] = rooflines["act_quant_prefill"]["achieved"] / HBM_PEAK_GBPS
+    if wq_bytes:
+        a = wq_bytes / (ms["weight_quant"] * 1e-3) / 1e9
+        rooflines["weight_quant"] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
+                                     "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
+                                     "us_per_launch_pair": ms["weight_quant"] * 1e3}
+    # Dominant kernel = largest share of the step.
+    dom = max(("prefill_gemm", "decode_gemv", "act_quant_prefill", "weight_quant"),
+              key=lambda k: ms.get(k, 0.0) if k in rooflines else -1)
+    traffic = load_traffic()
+    t = traffic.get((dom, wl.key))
+    roof = dict(rooflines[dom])
+    roof = {"kernel": dom, "bound": roof["bound"], "achieved": round(roof["achieved"], 2),
+            "peak": roof["peak"], "unit": roof["unit"], "frac": round(roof["frac"], 4),
+            "traffic": None if t is None else t["bytes_per_launch"]}
+
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "matrices": [f"{m.name} {m.K}->{m.N}" for m in wl.matrices],
+                   "prefill_tokens": M_pre, "decode_tokens": 1,
+                   "weights": wl.weights, "x_dtype": wl.x_dtype,
+                   "rotation_copies": {"prefill": setup.R_pre, "decode": setup.R_dec}},
+        "decode": {"gbps": round(dec_gbps, 2), "frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "bytes": dec_bytes, "us_gemv": round(ms["decode_gemv"] * 1e3, 3),
+                   "us_act_quant": round(ms["act_quant_decode"] * 1e3, 3)},
+        "prefill": {"gemm_tops": round(gemm_tops, 2), "frac_int8": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                    "ops": ops, "us_gemm": round(ms["prefill_gemm"] * 1e3, 3),
+                    "us_weight_quant": round(ms["weight_quant"] * 1e3, 3),
+                    "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3)},
+        "roofline": roof,
+        "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in rooflines.items()},
+        "timing": {"ms_per_step_wall": round(wall_ms, 4),
+                   "ms_per_step_with_launch_events": round(ms_with_events, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

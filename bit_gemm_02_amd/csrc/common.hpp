@@ -11,8 +11,45 @@
 namespace bl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- buffer loads
+//
+// Raw buffer loads through a buffer resource: an offset at or past `bytes` returns zeros
+// instead of touching memory, so ragged tiles need no per-lane branch (a branch around a
+// load forces the compiler to wait for it inside the branch).  Offsets are 32-bit, so each
+// resource covers at most one tile's rows (always far below 4 GiB).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// An offset that is out of range for every resource (each covers < 2^31 bytes) and does not
+// wrap when the access size is added: loads from it return zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // Third descriptor word for gfx9-family raw (untyped) buffer access.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ v4u buf_load16(rsrc_t r, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)offset, 0, 0);
+}
+
+// Bytes of rows [r0, min(r0 + rows, R)) of a row-major matrix with `row_bytes` per row.
+__device__ __forceinline__ uint32_t rows_bytes(int r0, int rows, int R, int row_bytes)
+{
+    const int live = R - r0 < rows ? R - r0 : rows;
+    return live > 0 ? (uint32_t)live * (uint32_t)row_bytes : 0u;
+}
 
 // ----------------------------------------------------------------- packed-code planes
 //

@@ -44,20 +44,9 @@ struct FwdBatch {
     int count;
 };
 
-// Loads the 4 words [w, w + 4) of a row (zero past `words`).  `aligned` when the row base
-// and w are 16-byte aligned (K % 64 == 0).
-__device__ __forceinline__ uint4 load_words4(const uint32_t *row, int w, int words, bool aligned)
-{
-    if (aligned && w + 3 < words)
-        return *reinterpret_cast<const uint4 *>(row + w);
-    uint4 r;
-    r.x = w + 0 < words ? row[w + 0] : 0u;
-    r.y = w + 1 < words ? row[w + 1] : 0u;
-    r.z = w + 2 < words ? row[w + 2] : 0u;
-    r.w = w + 3 < words ? row[w + 3] : 0u;
-    return r;
-}
-
+// FULL_K: every problem of the launch has K % 256 == 0, so super-steps never run past a
+// row and rows are 64-byte aligned (one 16-byte load per lane, no tail masking).
+template <bool FULL_K>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
     __shared__ v4i red[kDecWaves - 1][kWave];
@@ -74,12 +63,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     const int r = lane & 15;
     const int g = lane >> 4;
     const int words = p.K / 16;
-    const bool aligned = (words & 3) == 0;
-    const int n = n0 + r;
-    const bool row_ok = n < p.N;
-    const uint32_t *wrow = p.W + (int64_t)(row_ok ? n : 0) * words;
-    const bool tok_ok = r < p.M;  // A-operand row of this lane is a real token
-    const int8_t *xrow = p.Xq + (int64_t)(tok_ok ? r : 0) * p.K;
+    const int row_bytes = p.K / 4;
+    // Weight rows n0 .. n0+15 (rows past N read as zero); tokens 0 .. M-1 (rows past M zero).
+    const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * words, rows_bytes(n0, kDecRows, p.N, row_bytes));
+    const rsrc_t xres = make_rsrc(p.Xq, (uint32_t)p.M * (uint32_t)p.K);
+    const uint32_t wbase = (uint32_t)r * row_bytes;
+    const uint32_t xbase = (uint32_t)r * p.K;
 
     const int supers = (words + kSuperWords - 1) / kSuperWords;
     const int t_begin = (supers * wave) / kDecWaves;
@@ -87,27 +76,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 
     v4i acc = {0, 0, 0, 0};
     for (int t = t_begin; t < t_end; t += kDecUnroll) {
-        uint4 wv[kDecUnroll];
-        int4 xv[kDecUnroll][4];
+        v4u wv[kDecUnroll];
+        v4u xv[kDecUnroll][4];
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
             const int w = (t + u) * kSuperWords + 4 * g;
+            // A super-step past this wave's range is loaded from offset "infinity" (zeros).
             const bool live = (t + u) < t_end;
-            wv[u] = (row_ok && live) ? load_words4(wrow, w, words, aligned) : make_uint4(0, 0, 0, 0);
+            if (FULL_K) {
+                wv[u] = buf_load16(wres, live ? wbase + 4u * w : kOOB);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = live && (w + j) < words;
+                    wv[u][j] = buf_load4(wres, ok ? wbase + 4u * (w + j) : kOOB);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool ok = tok_ok && live && (w + j) < words;
-                xv[u][j] = ok ? *reinterpret_cast<const int4 *>(xrow + 16 * (w + j))
-                              : make_int4(0, 0, 0, 0);
+                const bool ok = live && (FULL_K || (w + j) < words);
+                xv[u][j] = buf_load16(xres, ok ? xbase + 16u * (w + j) : kOOB);
             }
         }
 #pragma unroll
         for (int u = 0; u < kDecUnroll; ++u) {
-            const uint32_t wj[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const v4i a = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word64(wj[j]), acc, 0, 0, 0);
+                const v4i a = {(int)xv[u][j].x, (int)xv[u][j].y, (int)xv[u][j].z, (int)xv[u][j].w};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word64(wv[u][j]), acc, 0, 0, 0);
             }
         }
     }
@@ -122,7 +118,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
         acc += red[w][lane];
 
     // acc holds 64 * D[m][n] for m = 4 * g + v (v = register index), n = n0 + r.
-    if (!row_ok)
+    const int n = n0 + r;
+    if (n >= p.N)
         return;
     const double gamma = (double)*p.gamma;
     const int accv[4] = {acc.x, acc.y, acc.z, acc.w};
@@ -143,9 +140,11 @@ hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStre
 {
     FwdBatch b{};
     int blocks = 0, n = 0;
+    bool full_k = true;
     for (int i = 0; i < count; ++i) {
         if (q[i].M == 0 || q[i].N == 0)
             continue;
+        full_k = full_k && (q[i].K % 256 == 0);
         FwdDev &d = b.p[n++];
         d.Xq = q[i].X_q;
         d.sx = q[i].x_scale;
@@ -162,7 +161,10 @@ hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStre
     b.count = n;
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(decode_kernel, dim3(blocks), dim3(kDecThreads), 0, stream, b);
+    if (full_k)
+        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kDecThreads), 0, stream, b);
+    else
+        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kDecThreads), 0, stream, b);
     return hipGetLastError();
 }
 

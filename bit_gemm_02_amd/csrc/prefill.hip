@@ -16,17 +16,13 @@
 // super-step's activations and weights are loaded into registers while the current one is
 // computed, and LDS is double-buffered, so one barrier per super-step suffices.
 // Epilogue: y = fl32(fp64(acc * gamma * s_x[m])), acc = (MFMA sum) / 64 (exact shift).
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.hpp"
 
 namespace bl {
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kPreThreads = 256;
-constexpr int kSuper = 256;                 // weights (k) per super-step
-constexpr int kXRow = kSuper + 16;          // LDS bytes per token row (16 B pad: no conflicts)
-constexpr int kXStage = kBM * kXRow;        // bytes per LDS buffer
-constexpr int kXLoads = kBM * kSuper / 16 / kPreThreads;  // 16-byte loads per thread per stage
 
 struct PreDev {
     const int8_t *Xq;
@@ -43,188 +39,372 @@ struct PreDev {
 struct PreBatch {
     PreDev p[BL_MAX_GROUP];
     int count;
+    int blocks;
 };
 
-__device__ __forceinline__ uint4 load_w4(const uint32_t *row, int w, int words, bool aligned)
+// Dispatch order -> work order.  Workgroups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8); remapping gives each XCD a contiguous range of a problem's
+// tiles, so tiles that share an activation row panel run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_order(int b, int nb)
 {
-    if (aligned && w + 3 < words)
-        return *reinterpret_cast<const uint4 *>(row + w);
-    uint4 r;
-    r.x = w + 0 < words ? row[w + 0] : 0u;
-    r.y = w + 1 < words ? row[w + 1] : 0u;
-    r.z = w + 2 < words ? row[w + 2] : 0u;
-    r.w = w + 3 < words ? row[w + 3] : 0u;
-    return r;
+    const int xcd = b & 7, i = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
 }
 
-__global__ __launch_bounds__(kPreThreads) void prefill_kernel(PreBatch b)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at lds + 16 * l; an
+// out-of-range offset writes zeros.  The LDS pointer must be wave-uniform.
+__device__ __forceinline__ void load_lds16(rsrc_t r, unsigned char *lds, uint32_t offset)
 {
-    __shared__ __align__(16) unsigned char smem[2 * kXStage];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)offset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave (direct-to-LDS
+// ones included) are still in flight.  Other counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile configuration: BM x BN block tile split over WM x WN waves (wave tile BM/WM x BN/WN,
+// MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS.
+template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KS = KS_, NST = NST_;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = WAVES * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
+    static constexpr int MI = TM / 16, NI = TN / 16;     // MFMA tiles per wave, each direction
+    static constexpr int CPR = KS / 16;                  // 16-byte activation chunks per row
+    static constexpr int WPS = KS / 16;                  // packed words per weight row
+    static constexpr int LPW = WPS / 4;                  // words per lane (one MFMA k-step each)
+    static constexpr int WROW = KS / 4;                  // bytes per weight row per stage
+    static constexpr int XBYTES = BM * KS;
+    static constexpr int WBYTES = BN * WROW;
+    static constexpr int STAGE = XBYTES + WBYTES;
+    static constexpr int XINST = XBYTES / 1024 / WAVES;  // 1 KB direct loads per wave per stage
+    static constexpr int WINST = WBYTES / 1024 / WAVES;
+    static constexpr int LOADS = XINST + WINST;          // vector-memory ops per wave per stage
+    static_assert(LPW >= 1 && LPW <= 4, "1..4 words per lane");
+    static_assert(XINST >= 1 && WINST >= 1, "every wave loads part of each operand");
+    static_assert(XINST * WAVES * 1024 == XBYTES && WINST * WAVES * 1024 == WBYTES, "even split");
+    static_assert(NST * STAGE <= 160 * 1024, "LDS budget");
+    static_assert((NST - 2) * LOADS < 64, "vmcnt range");
+};
+
+// Activation chunk swizzle: chunk c of tile row m sits at position c ^ f(m), chosen so that
+// the 16 rows of one MFMA A-operand read (same c) fall in 16 different 16-byte bank slots of
+// a 256-byte bank cycle: f(m) = (m / (16 / CPR)) % CPR.
+template <int CPR>
+__device__ __forceinline__ int xswz(int row)
+{
+    return (row / (16 / CPR)) & (CPR - 1);
+}
+
+// Weight chunk swizzle (16-byte chunks, WCH per row): rows m and m + 8 of a 16-row B-operand
+// read would share banks at a 32-byte row pitch; flipping the chunk order on every other
+// group of 8 rows separates them.
+template <int WCH>
+__device__ __forceinline__ int wswz(int row)
+{
+    return WCH > 1 ? ((row >> 3) & 1) : 0;
+}
+
+// One LDS buffer per pipeline stage, as distinct variables: the compiler can then tell that
+// a direct-to-LDS load into one stage does not alias reads from another, and does not force
+// a wait for every outstanding load before each LDS read.
+template <int S, int BYTES>
+__device__ __forceinline__ unsigned char *stage_buf()
+{
+    __shared__ __align__(1024) unsigned char buf[BYTES];
+    return buf;
+}
+
+template <int N>
+struct IC {
+    static constexpr int value = N;
+};
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// The prefill kernel.  Per stage, activations (BM rows x KS bytes, swizzled) and packed
+// weights (BN rows x KS/4 bytes) travel global -> LDS by direct buffer loads; NST - 1 stages
+// are in flight while one is computed, and one barrier per stage orders reuse of the buffers.
+// FULL_K: every problem has K % KS == 0 (no stage runs past a row).
+template <class T, bool FULL_K>
+__global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
+{
+    constexpr int BM = T::BM, BN = T::BN, KS = T::KS, NST = T::NST, WAVES = T::WAVES;
+    constexpr int MI = T::MI, NI = T::NI, CPR = T::CPR, LPW = T::LPW, WROW = T::WROW;
 
     int prob = 0;
 #pragma unroll 1
     while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
         ++prob;
     const PreDev &p = b.p[prob];
-    const int tile = blockIdx.x - p.block_begin;
-    const int m0 = (tile / p.tiles_n) * kBM;
-    const int n0 = (tile % p.tiles_n) * kBN;
+    // XCD-aware order inside each problem, so every XCD gets its share of every problem.
+    const int ntiles = (prob + 1 < b.count ? b.p[prob + 1].block_begin : b.blocks) - p.block_begin;
+    const int tile = xcd_order(blockIdx.x - p.block_begin, ntiles);
+    const int m0 = (tile / p.tiles_n) * BM;
+    const int n0 = (tile % p.tiles_n) * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WN, wn = wave % T::WN;
     const int r = lane & 15;
     const int g = lane >> 4;
     const int K = p.K;
-    const int words = K / 16;
-    const bool aligned = (words & 3) == 0;
-    const int supers = (K + kSuper - 1) / kSuper;
+    const int row_bytes = K / 4;
+    const int stages = (K + KS - 1) / KS;
 
-    // Weight rows of this lane, one per n sub-tile.
-    const uint32_t *wrow[4];
-    bool wok[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int n = n0 + wn * 64 + ni * 16 + r;
-        wok[ni] = n < p.N;
-        wrow[ni] = p.W + (int64_t)(wok[ni] ? n : 0) * words;
-    }
+    // Activation rows m0 .. m0+BM-1 and weight rows n0 .. n0+BN-1; rows past M / N read zero.
+    const rsrc_t xres = make_rsrc(p.Xq + (int64_t)m0 * K, rows_bytes(m0, BM, p.M, K));
+    const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * (K / 16), rows_bytes(n0, BN, p.N, row_bytes));
 
-    // Activation staging: chunk c = i * 256 + tid -> token row c / 16, 16-byte column c % 16.
-    auto load_x = [&](int t, int4 (&xr)[kXLoads]) {
+    // Load plan.  Activations: wave w fills rows w*BM/WAVES .. +BM/WAVES, 64/CPR rows per 1 KB
+    // load; lane l -> row (l / CPR), position l % CPR, global chunk position ^ swizzle.
+    // Weights: wave w fills rows w*BN/WAVES .. +BN/WAVES, 1024/WROW rows per load; lane l ->
+    // row l / (WROW/16), position l % (WROW/16), global chunk position ^ swizzle.
+    // Past-the-row chunks (only when !FULL_K) read as zero for activations; weight words past
+    // K meet those zero activations.
+    constexpr int XR = 64 / CPR;            // activation rows per load
+    constexpr int WCH = WROW / 16;          // 16-byte weight chunks per row
+    constexpr int WR = 64 / WCH;            // weight rows per load
+    const int xrow_l = lane / CPR, xpos = lane % CPR;
+    const int wrow_l = lane / WCH, wcol = lane % WCH;
+    // A stage at or past `stages` is still issued, from out-of-range offsets: it writes zeros
+    // into a buffer nobody reads again, and keeps the number of loads in flight per stage
+    // constant, so a single compile-time vmcnt wait fits every iteration.
+    // (The dead-stage flag is folded into bit 31 of the offset arithmetically: a select on a
+    // uniform flag would be turned into branches around the loads, and the compiler then
+    // waits conservatively for all of them before reading LDS.)
+    auto issue = [&](auto S, int t) {
+        unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
+        const uint32_t dead = (uint32_t)(t >= stages) << 31;   // == kOOB for a dead stage
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int c = i * kPreThreads + tid;
-            const int row = c >> 4, col = c & 15;
-            const int m = m0 + row;
-            const int k = t * kSuper + col * 16;
-            xr[i] = (m < p.M && k < K)
-                        ? *reinterpret_cast<const int4 *>(p.Xq + (int64_t)m * K + k)
-                        : make_int4(0, 0, 0, 0);
+        for (int i = 0; i < T::XINST; ++i) {
+            const int row0 = wave * (BM / WAVES) + i * XR;
+            const int row = row0 + xrow_l;
+            const int c = xpos ^ xswz<CPR>(row);
+            const int k = t * KS + 16 * c;
+            uint32_t off = ((uint32_t)row * K + (uint32_t)k) | dead;
+            if (!FULL_K)
+                off = k < K ? off : kOOB;
+            load_lds16(xres, st + row0 * KS, off);
+        }
+#pragma unroll
+        for (int i = 0; i < T::WINST; ++i) {
+            const int row0 = wave * (BN / WAVES) + i * WR;
+            const int row = row0 + wrow_l;
+            const int kb = t * WROW + 16 * (wcol ^ wswz<WCH>(row));   // byte offset in the row
+            uint32_t off = ((uint32_t)row * row_bytes + (uint32_t)kb) | dead;
+            if (!FULL_K)
+                off = kb < row_bytes ? off : kOOB;
+            load_lds16(wres, st + T::XBYTES + row0 * WROW, off);
         }
     };
-    auto store_x = [&](int buf, const int4 (&xr)[kXLoads]) {
-        unsigned char *base = smem + buf * kXStage;
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int c = i * kPreThreads + tid;
-            const int row = c >> 4, col = c & 15;
-            *reinterpret_cast<int4 *>(base + row * kXRow + col * 16) = xr[i];
-        }
-    };
-    auto load_w = [&](int t, uint4 (&wr)[4]) {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-            wr[ni] = wok[ni] ? load_w4(wrow[ni], t * 16 + 4 * g, words, aligned)
-                             : make_uint4(0, 0, 0, 0);
-    };
 
-    v4i acc[4][4];
+    v4i acc[MI][NI];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = v4i{0, 0, 0, 0};
 
-    int4 xr[kXLoads];
-    uint4 wcur[4], wnext[4];
-    load_x(0, xr);
-    load_w(0, wcur);
-    store_x(0, xr);
-    __syncthreads();
+    // Per-lane LDS offsets inside a stage.  Lane (r, g) reads words g*LPW .. +LPW-1 of its
+    // weight row: 16-byte chunk (g*LPW*4) / 16 (swizzled) at byte (g*LPW*4) % 16.
+    const int arow = (wm * T::TM + r) * KS;                  // + mi * 16 * KS
+    const int aswz = xswz<CPR>(wm * T::TM + r);              // same for every mi (16 | mi*16)
+    const int bch = (g * LPW * 4) / 16, bin = (g * LPW * 4) % 16;
+    const int brow = T::XBYTES + (wn * T::TN + r) * WROW +
+                     16 * (bch ^ wswz<WCH>(wn * T::TN + r)) + bin;           // + ni * 16 * WROW
 
-    for (int t = 0; t < supers; ++t) {
-        const bool more = t + 1 < supers;
-        if (more) {
-            load_x(t + 1, xr);
-            load_w(t + 1, wnext);
-        }
-        const unsigned char *xs = smem + (t & 1) * kXStage + (wm * 64 + r) * kXRow + 64 * g;
+    auto compute = [&](auto S) {
+        const unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
+        uint32_t wq[NI][LPW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            v4i bop[4];
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const uint32_t wj = j == 0 ? wcur[ni].x : j == 1 ? wcur[ni].y
-                                  : j == 2 ? wcur[ni].z : wcur[ni].w;
-                bop[ni] = unpack_word64(wj);
+        for (int ni = 0; ni < NI; ++ni) {
+            const unsigned char *src = st + brow + ni * 16 * WROW;
+            if constexpr (LPW == 4) {
+                const v4u v = *reinterpret_cast<const v4u *>(src);
+                wq[ni][0] = v.x; wq[ni][1] = v.y; wq[ni][2] = v.z; wq[ni][3] = v.w;
+            } else if constexpr (LPW == 2) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                wq[ni][0] = v.x; wq[ni][1] = v.y;
+            } else {
+                wq[ni][0] = *reinterpret_cast<const uint32_t *>(src);
             }
-            v4i aop[4];
+        }
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                aop[mi] = *reinterpret_cast<const v4i *>(xs + mi * 16 * kXRow + 16 * j);
+        for (int j = 0; j < LPW; ++j) {
+            v4i bop[NI];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
+            for (int ni = 0; ni < NI; ++ni)
+                bop[ni] = unpack_word64(wq[ni][j]);
+            const int pos = 16 * ((g * LPW + j) ^ aswz);
+            v4i aop[MI];
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+            for (int mi = 0; mi < MI; ++mi)
+                aop[mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * KS + pos);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mi], bop[ni],
                                                                        acc[mi][ni], 0, 0, 0);
         }
-        if (more) {
-            store_x((t + 1) & 1, xr);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                wcur[ni] = wnext[ni];
-        }
-        __syncthreads();
+    };
+
+    // Prologue: stages 0 .. NST-2 in flight.
+    static_for<0, NST - 1>([&](auto S) { issue(S, S.value); });
+    // Main loop, unrolled by NST so every stage buffer is a compile-time choice.  Stage t has
+    // landed once only the NST - 2 stages issued after it are still in flight.
+    for (int t0 = 0; t0 < stages; t0 += NST) {
+        static_for<0, NST>([&](auto S) {
+            const int t = t0 + S.value;
+            if (t < stages) {
+                wait_vmem<(NST - 2) * T::LOADS>();
+                __builtin_amdgcn_s_barrier();
+                issue(IC<(decltype(S)::value + NST - 1) % NST>{}, t + NST - 1);
+                compute(S);
+            }
+        });
     }
 
     // Epilogue: acc[mi][ni] register v holds 64 * D[m][n] for
-    // m = m0 + wm * 64 + mi * 16 + 4 * g + v and n = n0 + wn * 64 + ni * 16 + r.
+    // m = m0 + wm * TM + mi * 16 + 4 * g + v and n = n0 + wn * TN + ni * 16 + r.
     const double gamma = (double)*p.gamma;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int m = m0 + wm * 64 + mi * 16 + 4 * g + v;
+            const int m = m0 + wm * T::TM + mi * 16 + 4 * g + v;
             if (m >= p.M)
                 continue;
             const double scale = gamma * (double)p.sx[m];
             float *yrow = p.Y + (int64_t)m * p.N;
-            int32_t *arow = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
+            int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-                const int n = n0 + wn * 64 + ni * 16 + r;
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = n0 + wn * T::TN + ni * 16 + r;
                 if (n >= p.N)
                     continue;
-                const int s = v == 0 ? acc[mi][ni].x : v == 1 ? acc[mi][ni].y
-                            : v == 2 ? acc[mi][ni].z : acc[mi][ni].w;
-                const int a = s >> 6;
+                const int a = acc[mi][ni][v] >> 6;
                 yrow[n] = (float)((double)a * scale);
-                if (arow)
-                    arow[n] = a;
+                if (arow_out)
+                    arow_out[n] = a;
             }
         }
     }
 }
 
-hipError_t launch_forward_prefill(const bl_forward_problem *q, int count, hipStream_t stream)
+template <class T>
+static int build_batch(const bl_forward_problem *q, int count, PreBatch &b, bool &full_k)
 {
-    PreBatch b{};
-    int blocks = 0, n = 0;
-    for (int i = 0; i < count; ++i) {
-        if (q[i].M == 0 || q[i].N == 0)
-            continue;
-        PreDev &d = b.p[n++];
-        d.Xq = q[i].X_q;
-        d.sx = q[i].x_scale;
-        d.W = q[i].W_packed;
-        d.gamma = q[i].gamma;
-        d.Y = q[i].Y;
-        d.acc = q[i].acc;
-        d.M = (int)q[i].M;
-        d.N = (int)q[i].N;
-        d.K = (int)q[i].K;
-        d.tiles_n = (d.N + kBN - 1) / kBN;
+    // Longest-K problems first: their tiles take longest, so they should not start last.
+    int order[BL_MAX_GROUP];
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0 && q[i].N > 0)
+            order[n++] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && q[order[j]].K > q[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    int blocks = 0;
+    full_k = true;
+    for (int i = 0; i < n; ++i) {
+        const bl_forward_problem &s = q[order[i]];
+        PreDev &d = b.p[i];
+        d.Xq = s.X_q;
+        d.sx = s.x_scale;
+        d.W = s.W_packed;
+        d.gamma = s.gamma;
+        d.Y = s.Y;
+        d.acc = s.acc;
+        d.M = (int)s.M;
+        d.N = (int)s.N;
+        d.K = (int)s.K;
+        d.tiles_n = (d.N + T::BN - 1) / T::BN;
         d.block_begin = blocks;
-        blocks += ((d.M + kBM - 1) / kBM) * d.tiles_n;
+        blocks += ((d.M + T::BM - 1) / T::BM) * d.tiles_n;
+        full_k = full_k && (d.K % T::KS == 0);
     }
     b.count = n;
+    b.blocks = blocks;
+    return blocks;
+}
+
+template <class T>
+static hipError_t launch_tiles(const bl_forward_problem *q, int count, hipStream_t stream)
+{
+    PreBatch b{};
+    bool full_k;
+    const int blocks = build_batch<T>(q, count, b, full_k);
     if (blocks == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(prefill_kernel, dim3(blocks), dim3(kPreThreads), 0, stream, b);
+    if (full_k)
+        hipLaunchKernelGGL((prefill_kernel<T, true>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
+    else
+        hipLaunchKernelGGL((prefill_kernel<T, false>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
     return hipGetLastError();
+}
+
+using TileBig = Tile<256, 256, 4, 2, 128, 4>;    // 160 KB LDS, one block (8 waves) per CU
+using TileBigB = Tile<256, 256, 2, 4, 128, 4>;
+using TileBigC = Tile<256, 256, 2, 2, 128, 4>;
+using TileMid = Tile<256, 128, 2, 2, 128, 4>;
+using TileSmall = Tile<128, 128, 2, 2, 128, 4>;  // 80 KB LDS, two blocks per CU
+
+static int tile_override()
+{
+    // Measurement-only knob to A/B tile layouts (BITLINEAR_PREFILL_TILE=big|bigb|bigc|mid|small).
+    static int v = [] {
+        const char *e = getenv("BITLINEAR_PREFILL_TILE");
+        if (!e)
+            return 0;
+        if (!strcmp(e, "big")) return 1;
+        if (!strcmp(e, "bigb")) return 2;
+        if (!strcmp(e, "bigc")) return 3;
+        if (!strcmp(e, "mid")) return 4;
+        if (!strcmp(e, "small")) return 5;
+        return 0;
+    }();
+    return v;
+}
+
+// Large tiles (half the LDS and cache traffic per operation) when they still give every
+// compute unit at least two tiles; otherwise 128 x 128.
+hipError_t launch_forward_prefill(const bl_forward_problem *q, int count, hipStream_t stream)
+{
+    switch (tile_override()) {
+    case 1: return launch_tiles<TileBig>(q, count, stream);
+    case 2: return launch_tiles<TileBigB>(q, count, stream);
+    case 3: return launch_tiles<TileBigC>(q, count, stream);
+    case 4: return launch_tiles<TileMid>(q, count, stream);
+    case 5: return launch_tiles<TileSmall>(q, count, stream);
+    default: break;
+    }
+    int64_t big = 0;
+    for (int i = 0; i < count; ++i)
+        big += ((q[i].M + 255) / 256) * ((q[i].N + 255) / 256);
+    if (big >= 512)
+        return launch_tiles<TileBig>(q, count, stream);
+    return launch_tiles<TileSmall>(q, count, stream);
 }
 
 }  // namespace bl

@@ -10,8 +10,10 @@
 //
 // Activation path (BitDistill article: INT8 activations, SubLN before the attention and FFN
 // output projections; SLM750-Edge card: RMSNorm epsilon 1e-6):
-//   act_quant_kernel      one block per token row: absmax (+ sum of squares for the norm),
-//                         then q = rint(u * (127 / a)) and the row scale.
+//   act_quant_wave_kernel   one wave per token row (K <= 4096), row held in registers;
+//   act_quant_block_kernel  one block per token row for longer rows;
+//   both: absmax (+ fixed-order sum of squares for the norm), then q = rint(u * (127 / a))
+//   and the row scale.
 //
 // Rounding-sensitive arithmetic is written so that it matches IEEE-754 fp32 semantics:
 // the library is built with -ffp-contract=off, fp32 division is correctly rounded (the HIP
@@ -25,7 +27,7 @@ constexpr int kGammaThreads = 512;
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 8;      // float4 chunks per thread in quant_pack_kernel
 constexpr int kActThreads = 256;
-constexpr int kActCache = 12;       // 4-element chunks per thread kept in registers
+constexpr int kActCache = 16;       // 4-element chunks per thread kept in registers (block kernel)
 
 // ----------------------------------------------------------------------------- gamma
 
@@ -150,19 +152,25 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
     // Each lane turns 4 consecutive weights (one float4) into its plane of a packed word:
     // chunk j covers k = 4j .. 4j + 3, i.e. word j / 4, plane i = j % 4, bytes b = 0..3.
     // The four lanes of a quad hold the four planes of one word and OR them together.
+    // All loads first (out-of-range chunks of the last block read as zero), then the codes.
     const int64_t base = (int64_t)blk * kPackThreads * kPackUnroll;
+    const int64_t live = p.chunks - base < kPackThreads * kPackUnroll ? p.chunks - base
+                                                                       : kPackThreads * kPackUnroll;
+    const rsrc_t wres = make_rsrc(p.W + base, live > 0 ? (uint32_t)live * 16u : 0u);
+    v4u raw[kPackUnroll];
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u)
+        raw[u] = buf_load16(wres, (uint32_t)(u * kPackThreads + threadIdx.x) * 16u);
 #pragma unroll
     for (int u = 0; u < kPackUnroll; ++u) {
         const int64_t j = base + (int64_t)u * kPackThreads + threadIdx.x;
-        uint32_t bits = 0;
-        if (j < p.chunks) {
-            const float4 v = p.W[j];
-            const int sh = 2 * (int)(j & 3);
-            bits |= code_field(fabsf(v.x) > tau, v.x < 0.0f) << (0 + sh);
-            bits |= code_field(fabsf(v.y) > tau, v.y < 0.0f) << (8 + sh);
-            bits |= code_field(fabsf(v.z) > tau, v.z < 0.0f) << (16 + sh);
-            bits |= code_field(fabsf(v.w) > tau, v.w < 0.0f) << (24 + sh);
-        }
+        const float vx = __uint_as_float(raw[u].x), vy = __uint_as_float(raw[u].y);
+        const float vz = __uint_as_float(raw[u].z), vw = __uint_as_float(raw[u].w);
+        const int sh = 2 * (int)(j & 3);
+        uint32_t bits = code_field(fabsf(vx) > tau, vx < 0.0f) << (0 + sh);
+        bits |= code_field(fabsf(vy) > tau, vy < 0.0f) << (8 + sh);
+        bits |= code_field(fabsf(vz) > tau, vz < 0.0f) << (16 + sh);
+        bits |= code_field(fabsf(vw) > tau, vw < 0.0f) << (24 + sh);
         bits = quad_or(bits);
         if (j < p.chunks && (j & 3) == 0)
             p.packed[j >> 2] = bits;
@@ -252,18 +260,33 @@ struct ActBatch {
     int count;
 };
 
-__device__ __forceinline__ float4 load4(const void *X, int bf16, int64_t chunk)
+// Chunk j (4 activations) of a row through the row's buffer resource: fp32 rows use 16-byte
+// loads, bf16 rows 8-byte loads widened exactly to fp32.  Chunks past the row read as zero.
+__device__ __forceinline__ float4 load_chunk(rsrc_t row, int bf16, int j)
 {
     if (bf16) {
-        const uint2 r = reinterpret_cast<const uint2 *>(X)[chunk];
-        float4 v;
-        v.x = __uint_as_float(r.x << 16);
-        v.y = __uint_as_float(r.x & 0xFFFF0000u);
-        v.z = __uint_as_float(r.y << 16);
-        v.w = __uint_as_float(r.y & 0xFFFF0000u);
-        return v;
+        const uint32_t lo = buf_load4(row, (uint32_t)j * 8u);
+        const uint32_t hi = buf_load4(row, (uint32_t)j * 8u + 4u);
+        return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
+                           __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u));
     }
-    return reinterpret_cast<const float4 *>(X)[chunk];
+    const v4u v = buf_load16(row, (uint32_t)j * 16u);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
+__device__ __forceinline__ rsrc_t row_rsrc(const ActDev &p, int m)
+{
+    const int esize = p.bf16 ? 2 : 4;
+    return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
+                     (uint32_t)p.K * esize);
+}
+
+__device__ __forceinline__ float4 load_g(rsrc_t g, int j)
+{
+    const v4u v = buf_load16(g, (uint32_t)j * 16u);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
 }
 
 __device__ __forceinline__ int8_t quant_one(float u, float inv)
@@ -278,50 +301,137 @@ __device__ __forceinline__ int8_t quant_one(float u, float inv)
     return (int8_t)(int)v;
 }
 
-__global__ __launch_bounds__(kActThreads) void act_quant_kernel(ActBatch b)
+// Quantize one row given its absmax a: q = clamp(rint(u * fl32(127 / a))).
+__device__ __forceinline__ char4 quant4(float4 u, float inv)
+{
+    return make_char4(quant_one(u.x, inv), quant_one(u.y, inv), quant_one(u.z, inv),
+                      quant_one(u.w, inv));
+}
+
+__device__ __forceinline__ float4 mul4(float4 a, float4 b)
+{
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+__device__ __forceinline__ float absmax4(float4 u)
+{
+    return fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w)));
+}
+
+__device__ __forceinline__ double sumsq4(double s, float4 x)
+{
+    s += (double)x.x * (double)x.x;
+    s += (double)x.y * (double)x.y;
+    s += (double)x.z * (double)x.z;
+    s += (double)x.w * (double)x.w;
+    return s;
+}
+
+__device__ __forceinline__ void write_scale(const ActDev &p, int m, float a, double ss, bool norm)
+{
+    if (a == 0.0f) {
+        p.sx[m] = 0.0f;
+    } else if (!norm) {
+        p.sx[m] = a / 127.0f;  // correctly rounded fp32 division
+    } else {
+        const double r = 1.0 / sqrt(ss / (double)p.K + (double)p.eps);
+        p.sx[m] = (float)((double)a * r / 127.0);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ int find_problem(const T &b, int key)
+{
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && key >= b.p[prob + 1].row_begin)
+        ++prob;
+    return prob;
+}
+
+// One wave per token row, for K <= 256 * CACHE: each lane keeps its CACHE chunks of 4
+// activations in registers, so the row is read from HBM once; reductions are wave-local
+// (no LDS, no barriers).  Four rows per block.
+template <int CACHE>
+__global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int grow = blockIdx.x * (kActThreads / kWave) + threadIdx.x / kWave;
+    if (grow >= rows)
+        return;
+    const ActDev &p = b.p[find_problem(b, grow)];
+    const int m = grow - p.row_begin;
+    const int chunks = p.K / 4;
+    const bool norm = p.g != nullptr;
+    const rsrc_t xr = row_rsrc(p, m);
+    const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+
+    float4 x[CACHE], u[CACHE];
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c)
+        x[c] = load_chunk(xr, p.bf16, c * kWave + lane);
+    float amax = 0.0f;
+    double ss = 0.0;
+    if (norm) {
+#pragma unroll
+        for (int c = 0; c < CACHE; ++c) {
+            u[c] = mul4(x[c], load_g(gr, c * kWave + lane));
+            amax = fmaxf(amax, absmax4(u[c]));
+            ss = sumsq4(ss, x[c]);   // chunks past the row are zero and add nothing
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < CACHE; ++c) {
+            u[c] = x[c];
+            amax = fmaxf(amax, absmax4(u[c]));
+        }
+    }
+    const float a = wave_max(amax);
+    if (norm)
+        ss = wave_sum_fixed(ss);
+    char4 *q4 = reinterpret_cast<char4 *>(p.Xq) + (int64_t)m * chunks;
+    const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded fp32 division
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c) {
+        const int j = c * kWave + lane;
+        if (j < chunks)
+            q4[j] = quant4(u[c], inv);
+    }
+    if (lane == 0)
+        write_scale(p, m, a, ss, norm);
+}
+
+// One block per token row for long rows (K > 4096): the first kActCache chunks per thread
+// stay in registers, any remainder is read again (from L2) in the second pass.
+__global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
 {
     __shared__ float lds_max[kActThreads / kWave];
     __shared__ double lds_sum[kActThreads / kWave];
-    int prob = 0;
-#pragma unroll 1
-    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].row_begin)
-        ++prob;
-    const ActDev &p = b.p[prob];
+    const ActDev &p = b.p[find_problem(b, (int)blockIdx.x)];
     const int m = blockIdx.x - p.row_begin;
     const int chunks = p.K / 4;
-    const int64_t row0 = (int64_t)m * chunks;
     const bool norm = p.g != nullptr;
-    const float4 *g4 = reinterpret_cast<const float4 *>(p.g);
+    const rsrc_t xr = row_rsrc(p, m);
+    const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
 
     float4 cache[kActCache];
+#pragma unroll
+    for (int c = 0; c < kActCache; ++c)
+        cache[c] = load_chunk(xr, p.bf16, c * kActThreads + threadIdx.x);
     float amax = 0.0f;
     double ss = 0.0;
 #pragma unroll
     for (int c = 0; c < kActCache; ++c) {
         const int j = c * kActThreads + threadIdx.x;
-        if (j < chunks) {
-            const float4 x = load4(p.X, p.bf16, row0 + j);
-            cache[c] = x;
-            float4 u = x;
-            if (norm) {
-                const float4 g = g4[j];
-                u.x = x.x * g.x; u.y = x.y * g.y; u.z = x.z * g.z; u.w = x.w * g.w;
-                ss += (double)x.x * (double)x.x; ss += (double)x.y * (double)x.y;
-                ss += (double)x.z * (double)x.z; ss += (double)x.w * (double)x.w;
-            }
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
-        }
+        amax = fmaxf(amax, absmax4(norm ? mul4(cache[c], load_g(gr, j)) : cache[c]));
+        if (norm)
+            ss = sumsq4(ss, cache[c]);
     }
     for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        const float4 x = load4(p.X, p.bf16, row0 + j);
-        float4 u = x;
-        if (norm) {
-            const float4 g = g4[j];
-            u.x = x.x * g.x; u.y = x.y * g.y; u.z = x.z * g.z; u.w = x.w * g.w;
-            ss += (double)x.x * (double)x.x; ss += (double)x.y * (double)x.y;
-            ss += (double)x.z * (double)x.z; ss += (double)x.w * (double)x.w;
-        }
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
+        const float4 x = load_chunk(xr, p.bf16, j);
+        amax = fmaxf(amax, absmax4(norm ? mul4(x, load_g(gr, j)) : x));
+        if (norm)
+            ss = sumsq4(ss, x);
     }
 
     // Block max (exact, order-free) and fixed-order block sum of squares.
@@ -342,56 +452,34 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(ActBatch b)
         sum = sum + lds_sum[w];
     }
 
-    char4 *q4 = reinterpret_cast<char4 *>(p.Xq) + row0;
-    if (a == 0.0f) {
-        for (int j = threadIdx.x; j < chunks; j += kActThreads)
-            q4[j] = make_char4(0, 0, 0, 0);
-        if (threadIdx.x == 0)
-            p.sx[m] = 0.0f;
-        return;
-    }
-    const float inv = 127.0f / a;  // correctly rounded fp32 division
+    char4 *q4 = reinterpret_cast<char4 *>(p.Xq) + (int64_t)m * chunks;
+    const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded fp32 division
 #pragma unroll
     for (int c = 0; c < kActCache; ++c) {
         const int j = c * kActThreads + threadIdx.x;
-        if (j < chunks) {
-            float4 u = cache[c];
-            if (norm) {
-                const float4 g = g4[j];
-                u.x = u.x * g.x; u.y = u.y * g.y; u.z = u.z * g.z; u.w = u.w * g.w;
-            }
-            q4[j] = make_char4(quant_one(u.x, inv), quant_one(u.y, inv), quant_one(u.z, inv),
-                               quant_one(u.w, inv));
-        }
+        if (j < chunks)
+            q4[j] = quant4(norm ? mul4(cache[c], load_g(gr, j)) : cache[c], inv);
     }
     for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        float4 u = load4(p.X, p.bf16, row0 + j);
-        if (norm) {
-            const float4 g = g4[j];
-            u.x = u.x * g.x; u.y = u.y * g.y; u.z = u.z * g.z; u.w = u.w * g.w;
-        }
-        q4[j] = make_char4(quant_one(u.x, inv), quant_one(u.y, inv), quant_one(u.z, inv),
-                           quant_one(u.w, inv));
+        const float4 x = load_chunk(xr, p.bf16, j);
+        q4[j] = quant4(norm ? mul4(x, load_g(gr, j)) : x, inv);
     }
-    if (threadIdx.x == 0) {
-        if (!norm) {
-            p.sx[m] = a / 127.0f;  // correctly rounded fp32 division
-        } else {
-            const double r = 1.0 / sqrt(sum / (double)p.K + (double)p.eps);
-            p.sx[m] = (float)((double)a * r / 127.0);
-        }
-    }
+    if (threadIdx.x == 0)
+        write_scale(p, m, a, sum, norm);
 }
 
 hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t stream)
 {
-    ActBatch b{};
-    int rows = 0;
-    int n = 0;
+    // Rows up to 4096 wide go to the wave-per-row kernel, longer rows to the block kernel.
+    ActBatch wave_b{}, block_b{};
+    int wave_rows = 0, block_rows = 0, max_wave_k = 0;
     for (int i = 0; i < count; ++i) {
         if (q[i].M == 0)
             continue;
-        ActDev &d = b.p[n++];
+        const bool wide = q[i].K > 4096;
+        ActBatch &b = wide ? block_b : wave_b;
+        int &rows = wide ? block_rows : wave_rows;
+        ActDev &d = b.p[b.count++];
         d.X = q[i].X;
         d.g = q[i].norm_weight;
         d.Xq = q[i].X_q;
@@ -402,12 +490,27 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
         d.eps = q[i].eps;
         d.row_begin = rows;
         rows += d.M;
+        if (!wide && d.K > max_wave_k)
+            max_wave_k = d.K;
     }
-    b.count = n;
-    if (rows == 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(act_quant_kernel, dim3(rows), dim3(kActThreads), 0, stream, b);
-    return hipGetLastError();
+    if (wave_rows) {
+        const int per_block = kActThreads / kWave;
+        const dim3 grid((wave_rows + per_block - 1) / per_block);
+        if (max_wave_k <= 1024)
+            hipLaunchKernelGGL(act_quant_wave_kernel<4>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
+        else if (max_wave_k <= 2048)
+            hipLaunchKernelGGL(act_quant_wave_kernel<8>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
+        else
+            hipLaunchKernelGGL(act_quant_wave_kernel<16>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (block_rows) {
+        hipLaunchKernelGGL(act_quant_block_kernel, dim3(block_rows), dim3(kActThreads), 0, stream, block_b);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 }  // namespace bl
