@@ -59,6 +59,9 @@ def parse():
                     help="target seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -258,6 +261,70 @@ def interval_ms(ev, a, b):
     return float(np.mean(xs)) if xs else float("nan")
 
 
+# Kernel name fragment -> (roofline key, source file).  Activation quantization runs twice per
+# step (prefill and decode); the prefill launches are the ones with more than 64 blocks.
+KERNELS = {
+    "prefill_kernel": ("prefill_gemm", "prefill.hip"),
+    "decode_kernel": ("decode_gemv", "decode.hip"),
+    "act_quant": ("act_quant_prefill", "quant.hip"),
+    "gamma_partial_kernel": ("weight_quant", "quant.hip"),
+    "quant_pack_kernel": ("weight_quant", "quant.hip"),
+}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
+    """Per-launch HBM bytes of each kernel, scaled by a plain 256 MiB device copy."""
+    import csv
+    from collections import defaultdict
+
+    def per_dispatch(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            name, grid = r["Kernel_Name"], int(r["Grid_Size"])
+            prev = out.get(key, (name, grid, 0.0))
+            out[key] = (name, grid, prev[2] + float(r["Counter_Value"]))
+        return out
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+    copy_bytes = 256 * 1024 * 1024
+
+    def calib(d):
+        vals = [v for (n, g, v) in d.values() if "copyBuffer" in n]
+        return copy_bytes / (max(vals) * 1024.0)
+
+    f_fetch, f_write = calib(fetch), calib(write)
+
+    def by_kernel(d, factor):
+        acc = defaultdict(list)
+        for name, grid, kib in d.values():
+            for frag, (key, src) in KERNELS.items():
+                if frag in name:
+                    if key == "act_quant_prefill" and grid <= 64 * 256:
+                        key = "act_quant_decode"
+                    acc[(key, src)].append((name, kib * 1024.0 * factor))
+        return acc
+
+    fk, wk = by_kernel(fetch, f_fetch), by_kernel(write, f_write)
+    kernels = {}
+    for (key, src), vals in fk.items():
+        # Weight quantization is a pair of launches per call: report the pair.
+        per_launch = float(np.mean([v for _, v in vals]))
+        wvals = [v for _, v in wk.get((key, src), [])]
+        wr = float(np.mean(wvals)) if wvals else 0.0
+        pair = 2 if key == "weight_quant" else 1
+        kernels[key] = {"source": src, "source_sha": source_hash(src), "workload": workload,
+                        "launches": len(vals) // pair,
+                        "fetch_bytes_per_launch": round(per_launch * pair),
+                        "write_bytes_per_launch": round(wr * pair),
+                        "bytes_per_launch": round((per_launch + wr) * pair)}
+    return {"command": command, "copy_calibration_bytes": copy_bytes,
+            "fetch_scale": f_fetch, "write_scale": f_write, "kernels": kernels}
+
+
 def load_traffic():
     """HBM traffic per launch from committed counter runs, if the kernel sources still match."""
     try:
@@ -335,6 +402,22 @@ def copy_calibration(torch):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 "
+               f"bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline "
+               "--copy-calibration")
+        rec = summarize_pmc(*args.summarize_pmc, args.workload, cmd)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        old = {}
+        if os.path.exists(TRAFFIC_FILE):
+            old = json.load(open(TRAFFIC_FILE)).get("kernels", {})
+        # Keep other workloads' records; replace this workload's.
+        merged = {k: v for k, v in old.items() if v.get("workload") != args.workload}
+        merged.update({f"{k}": v for k, v in rec["kernels"].items()})
+        rec["kernels"] = merged
+        json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding "
               "of this path is described in DESIGN.md and is not launched.", file=sys.stderr)
