@@ -84,12 +84,26 @@ __device__ __forceinline__ uint32_t code_field(bool nonzero, bool negative)
 
 // ----------------------------------------------------------------- wave reductions
 
+// Wave maximum with DPP lane moves (no LDS round trips): quad permutes and row mirrors give
+// every lane its 16-lane row maximum, two row broadcasts carry rows 0-2 into row 3, and lane
+// 63 is read back.  max is exact, so the order does not matter.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v)
+{
+    const int o = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                              0xF, false);
+    return fmaxf(v, __int_as_float(o));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+    v = dpp_max<0x140, 0xF>(v);  // row_mirror
+    v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Fixed butterfly order: every lane ends with the same value, and the order of additions

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     const int n0 = (blockIdx.x - p.block_begin) * kDecRows;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int r = lane & 15;
     const int g = lane >> 4;
     const int words = p.K / 16;

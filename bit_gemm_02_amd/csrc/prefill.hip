@@ -161,7 +161,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int wm = wave / T::WN, wn = wave % T::WN;
     const int r = lane & 15;
     const int g = lane >> 4;

@@ -4,13 +4,13 @@
 // Weight path (Distillix README, "1. BitNet b1.58 Core": W_q = round(clip(W / mean|W|, -1, 1));
 // bitone README, "Features": gamma from a separate one-dimensional reduction over W, and the
 // quantized weights never materialized in HBM):
-//   gamma_partial_kernel  reads W once, writes kGammaParts fp64 partial sums per tensor;
-//   quant_pack_kernel     reduces the partials (same fixed order in every block, so every
-//                         block sees the same gamma), reads W again and writes packed words.
+//   gamma_partial_kernel  reads W once, writes up to kGammaParts fp64 partial sums per tensor;
+//   quant_pack_kernel     reduces the partials (same fixed order in every wave, so every wave
+//                         sees the same gamma), reads W again and writes packed words.
 //
 // Activation path (BitDistill article: INT8 activations, SubLN before the attention and FFN
 // output projections; SLM750-Edge card: RMSNorm epsilon 1e-6):
-//   act_quant_wave_kernel   one wave per token row (K <= 4096), row held in registers;
+//   act_quant_wave_kernel   persistent waves, one row at a time (K <= 4096), next row in flight;
 //   act_quant_block_kernel  one block per token row for longer rows;
 //   both: absmax (+ fixed-order sum of squares for the norm), then q = rint(u * (127 / a))
 //   and the row scale.
@@ -18,12 +18,14 @@
 // Rounding-sensitive arithmetic is written so that it matches IEEE-754 fp32 semantics:
 // the library is built with -ffp-contract=off, fp32 division is correctly rounded (the HIP
 // default), and rintf lowers to round-to-nearest-even.
+#include <stdlib.h>
+
 #include "common.hpp"
 
 namespace bl {
 
 constexpr int kGammaParts = 256;    // partial sums per tensor; fixed, so the order is fixed
-constexpr int kGammaThreads = 512;
+constexpr int kGammaThreads = 256;
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 8;      // float4 chunks per thread in quant_pack_kernel
 constexpr int kActThreads = 256;
@@ -35,9 +37,10 @@ struct WeightDev {
     const float4 *W;
     uint32_t *packed;
     float *gamma;
-    double *partials;   // [kGammaParts]
+    double *partials;   // [parts]
     int64_t chunks;     // N * K / 4 float4 chunks
-    int pack_blocks;    // blocks of quant_pack_kernel for this tensor
+    int parts;          // partial sums (blocks of gamma_partial_kernel) for this tensor
+    int part_begin;     // first block of this tensor in gamma_partial_kernel's grid
     int pack_begin;     // first block of this tensor in quant_pack_kernel's grid
 };
 
@@ -46,32 +49,25 @@ struct WeightBatch {
     int count;
 };
 
-// Block sum of one fp64 value per thread in a fixed order (wave butterfly, then waves in
-// index order).  Result valid in every thread.
-template <int THREADS>
-__device__ __forceinline__ double block_sum_fixed(double v, double *lds)
+// Number of partial sums for a tensor: about 4 float4 chunks per thread, at most kGammaParts.
+// A function of the shape only, so the summation order is fixed for a given shape.
+static int gamma_parts(int64_t chunks)
 {
-    constexpr int W = THREADS / kWave;
-    v = wave_sum_fixed(v);
-    const int wave = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0)
-        lds[wave] = v;
-    __syncthreads();
-    double s = lds[0];
-#pragma unroll
-    for (int i = 1; i < W; ++i)
-        s = s + lds[i];
-    __syncthreads();
-    return s;
+    const int64_t per = 4 * kGammaThreads;
+    const int64_t parts = (chunks + per - 1) / per;
+    return (int)(parts < 1 ? 1 : parts > kGammaParts ? kGammaParts : parts);
 }
 
 __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(WeightBatch b)
 {
     __shared__ double lds[kGammaThreads / kWave];
-    const int prob = blockIdx.x / kGammaParts;
-    const int part = blockIdx.x % kGammaParts;
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].part_begin)
+        ++prob;
     const WeightDev &p = b.p[prob];
-    const int64_t stride = (int64_t)kGammaParts * kGammaThreads;
+    const int part = blockIdx.x - p.part_begin;
+    const int64_t stride = (int64_t)p.parts * kGammaThreads;
     double s = 0.0;
     int64_t i = (int64_t)part * kGammaThreads + threadIdx.x;
     // Four loads in flight per thread; the additions stay in index order.
@@ -92,9 +88,19 @@ __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(WeightBatc
         s += fabs((double)v.x); s += fabs((double)v.y);
         s += fabs((double)v.z); s += fabs((double)v.w);
     }
-    s = block_sum_fixed<kGammaThreads>(s, lds);
-    if (threadIdx.x == 0)
-        p.partials[part] = s;
+    // Fixed-order block sum: wave butterfly, then the waves in index order.
+    s = wave_sum_fixed(s);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        lds[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = lds[0];
+#pragma unroll
+        for (int w = 1; w < kGammaThreads / kWave; ++w)
+            t = t + lds[w];
+        p.partials[part] = t;
+    }
 }
 
 // ------------------------------------------------------------------- quantize + pack
@@ -130,7 +136,6 @@ __device__ __forceinline__ uint32_t quad_or(uint32_t v)
 
 __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
 {
-    __shared__ double lds[kPackThreads / kWave];
     int prob = 0;
 #pragma unroll 1
     while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].pack_begin)
@@ -138,11 +143,25 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
     const WeightDev &p = b.p[prob];
     const int blk = blockIdx.x - p.pack_begin;
 
-    // gamma = fl32(sum / count), the partial sums reduced in the same order in every block.
+    // Issue this block's weight loads first (they do not depend on gamma), then reduce gamma
+    // while they are in flight.  Out-of-range chunks of the last block read as zero.
+    const int64_t base = (int64_t)blk * kPackThreads * kPackUnroll;
+    const int64_t live = p.chunks - base < kPackThreads * kPackUnroll ? p.chunks - base
+                                                                       : kPackThreads * kPackUnroll;
+    const rsrc_t wres = make_rsrc(p.W + base, live > 0 ? (uint32_t)live * 16u : 0u);
+    v4u raw[kPackUnroll];
+#pragma unroll
+    for (int u = 0; u < kPackUnroll; ++u)
+        raw[u] = buf_load16(wres, (uint32_t)(u * kPackThreads + threadIdx.x) * 16u);
+
+    // gamma = fl32(sum / count).  Every wave reduces the partial sums itself in the same
+    // fixed order (lane-sequential, then the wave butterfly), so every wave of every block
+    // holds the same gamma without a barrier.
+    const int lane = threadIdx.x & (kWave - 1);
     double part = 0.0;
-    for (int i = threadIdx.x; i < kGammaParts; i += kPackThreads)
+    for (int i = lane; i < p.parts; i += kWave)
         part += p.partials[i];
-    const double sum = block_sum_fixed<kPackThreads>(part, lds);
+    const double sum = wave_sum_fixed(part);
     const double count = (double)(p.chunks * 4);
     const float gamma = p.chunks > 0 ? (float)(sum / count) : 0.0f;
     if (blk == 0 && threadIdx.x == 0)
@@ -152,15 +171,6 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
     // Each lane turns 4 consecutive weights (one float4) into its plane of a packed word:
     // chunk j covers k = 4j .. 4j + 3, i.e. word j / 4, plane i = j % 4, bytes b = 0..3.
     // The four lanes of a quad hold the four planes of one word and OR them together.
-    // All loads first (out-of-range chunks of the last block read as zero), then the codes.
-    const int64_t base = (int64_t)blk * kPackThreads * kPackUnroll;
-    const int64_t live = p.chunks - base < kPackThreads * kPackUnroll ? p.chunks - base
-                                                                       : kPackThreads * kPackUnroll;
-    const rsrc_t wres = make_rsrc(p.W + base, live > 0 ? (uint32_t)live * 16u : 0u);
-    v4u raw[kPackUnroll];
-#pragma unroll
-    for (int u = 0; u < kPackUnroll; ++u)
-        raw[u] = buf_load16(wres, (uint32_t)(u * kPackThreads + threadIdx.x) * 16u);
 #pragma unroll
     for (int u = 0; u < kPackUnroll; ++u) {
         const int64_t j = base + (int64_t)u * kPackThreads + threadIdx.x;
@@ -182,33 +192,60 @@ size_t quantize_weights_workspace(int count)
     return (size_t)count * kGammaParts * sizeof(double);
 }
 
+// Tensors are processed in groups of at most group_bytes() of fp32 weights, each group as
+// one gamma launch followed by one pack launch, so that the pack launch can re-read W from
+// the 256 MB last-level cache (MALL) instead of HBM.  Default: one group (2 launches);
+// BITLINEAR_WQ_GROUP_MB is a measurement-only knob to A/B smaller groups.
+static int64_t group_bytes()
+{
+    static int64_t v = [] {
+        const char *e = getenv("BITLINEAR_WQ_GROUP_MB");
+        return e ? (int64_t)atoll(e) << 20 : (int64_t)1 << 62;
+    }();
+    return v;
+}
+
 hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
                                    hipStream_t stream)
 {
-    WeightBatch b{};
-    b.count = count;
-    int blocks = 0;
-    for (int i = 0; i < count; ++i) {
-        WeightDev &d = b.p[i];
-        d.W = reinterpret_cast<const float4 *>(q[i].W);
-        d.packed = q[i].W_packed;
-        d.gamma = q[i].gamma;
-        d.partials = static_cast<double *>(workspace) + (size_t)i * kGammaParts;
-        d.chunks = q[i].N * q[i].K / 4;
-        const int64_t per_block = (int64_t)kPackThreads * kPackUnroll;
-        d.pack_blocks = (int)((d.chunks + per_block - 1) / per_block);
-        if (d.pack_blocks == 0)
-            d.pack_blocks = 1;  // still writes gamma (= 0 for an empty tensor)
-        d.pack_begin = blocks;
-        blocks += d.pack_blocks;
+    int i0 = 0;
+    while (i0 < count) {
+        WeightBatch b{};
+        int parts = 0, blocks = 0;
+        int64_t bytes = 0;
+        int i = i0;
+        for (; i < count; ++i) {
+            const int64_t tb = q[i].N * q[i].K * 4;
+            if (i > i0 && bytes + tb > group_bytes())
+                break;
+            bytes += tb;
+            WeightDev &d = b.p[b.count++];
+            d.W = reinterpret_cast<const float4 *>(q[i].W);
+            d.packed = q[i].W_packed;
+            d.gamma = q[i].gamma;
+            d.partials = static_cast<double *>(workspace) + (size_t)i * kGammaParts;
+            d.chunks = q[i].N * q[i].K / 4;
+            d.parts = gamma_parts(d.chunks);
+            d.part_begin = parts;
+            parts += d.parts;
+            const int64_t per_block = (int64_t)kPackThreads * kPackUnroll;
+            int pb = (int)((d.chunks + per_block - 1) / per_block);
+            if (pb == 0)
+                pb = 1;  // still writes gamma (= 0 for an empty tensor)
+            d.pack_begin = blocks;
+            blocks += pb;
+        }
+        i0 = i;
+        hipLaunchKernelGGL(gamma_partial_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(quant_pack_kernel, dim3(blocks), dim3(kPackThreads), 0, stream, b);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
     }
-    hipLaunchKernelGGL(gamma_partial_kernel, dim3(count * kGammaParts), dim3(kGammaThreads), 0,
-                       stream, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(quant_pack_kernel, dim3(blocks), dim3(kPackThreads), 0, stream, b);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // ------------------------------------------------------------------------ pack codes
@@ -252,7 +289,7 @@ struct ActDev {
     int M, K;
     int bf16;
     float eps;
-    int row_begin;  // first block (row) of this problem in the grid
+    int row_begin;  // first row of this problem in the launch's row space
 };
 
 struct ActBatch {
@@ -260,52 +297,26 @@ struct ActBatch {
     int count;
 };
 
-// Chunk j (4 activations) of a row through the row's buffer resource: fp32 rows use 16-byte
-// loads, bf16 rows 8-byte loads widened exactly to fp32.  Chunks past the row read as zero.
-__device__ __forceinline__ float4 load_chunk(rsrc_t row, int bf16, int j)
+// q = clamp(rint(u * inv), -127, 127) as an integer.  rint of the fp32 product (round half
+// to even), then an exact integer clamp; the conversion maps NaN to 0 and saturates
+// infinities, so the degenerate rows (127/a overflowing to inf, 0 * inf = NaN) give the
+// same codes as clamping in floating point and sending NaN to 0.
+__device__ __forceinline__ int quant_one(float u, float inv)
 {
-    if (bf16) {
-        const uint32_t lo = buf_load4(row, (uint32_t)j * 8u);
-        const uint32_t hi = buf_load4(row, (uint32_t)j * 8u + 4u);
-        return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
-                           __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u));
-    }
-    const v4u v = buf_load16(row, (uint32_t)j * 16u);
-    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                       __uint_as_float(v.w));
+    const int i = (int)__builtin_rintf(u * inv);
+    return min(max(i, -127), 127);
 }
 
-__device__ __forceinline__ rsrc_t row_rsrc(const ActDev &p, int m)
-{
-    const int esize = p.bf16 ? 2 : 4;
-    return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
-                     (uint32_t)p.K * esize);
-}
-
-__device__ __forceinline__ float4 load_g(rsrc_t g, int j)
-{
-    const v4u v = buf_load16(g, (uint32_t)j * 16u);
-    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                       __uint_as_float(v.w));
-}
-
-__device__ __forceinline__ int8_t quant_one(float u, float inv)
-{
-    const float v = __builtin_rintf(u * inv);  // fp32 product, round half to even
-    if (v > 127.0f)
-        return 127;
-    if (v < -127.0f)
-        return -127;
-    if (v != v)
-        return 0;
-    return (int8_t)(int)v;
-}
-
-// Quantize one row given its absmax a: q = clamp(rint(u * fl32(127 / a))).
 __device__ __forceinline__ char4 quant4(float4 u, float inv)
 {
-    return make_char4(quant_one(u.x, inv), quant_one(u.y, inv), quant_one(u.z, inv),
-                      quant_one(u.w, inv));
+    const uint32_t b0 = (uint32_t)quant_one(u.x, inv) & 0xFFu;
+    const uint32_t b1 = (uint32_t)quant_one(u.y, inv) & 0xFFu;
+    const uint32_t b2 = (uint32_t)quant_one(u.z, inv) & 0xFFu;
+    const uint32_t b3 = (uint32_t)quant_one(u.w, inv) & 0xFFu;
+    const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    char4 c;
+    __builtin_memcpy(&c, &w, 4);
+    return c;
 }
 
 __device__ __forceinline__ float4 mul4(float4 a, float4 b)
@@ -325,6 +336,49 @@ __device__ __forceinline__ double sumsq4(double s, float4 x)
     s += (double)x.z * (double)x.z;
     s += (double)x.w * (double)x.w;
     return s;
+}
+
+// Raw storage of one chunk of 4 activations: fp32 -> 16 bytes, bf16 -> 8 bytes (kept packed
+// in registers and widened exactly when used).
+template <bool BF16>
+struct Chunk;
+template <>
+struct Chunk<false> {
+    v4u v;
+    __device__ __forceinline__ void load(rsrc_t r, int j) { v = buf_load16(r, (uint32_t)j * 16u); }
+    __device__ __forceinline__ float4 f() const
+    {
+        return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                           __uint_as_float(v.w));
+    }
+};
+template <>
+struct Chunk<true> {
+    uint32_t lo, hi;
+    __device__ __forceinline__ void load(rsrc_t r, int j)
+    {
+        lo = buf_load4(r, (uint32_t)j * 8u);
+        hi = buf_load4(r, (uint32_t)j * 8u + 4u);
+    }
+    __device__ __forceinline__ float4 f() const
+    {
+        return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
+                           __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u));
+    }
+};
+
+__device__ __forceinline__ rsrc_t row_rsrc(const ActDev &p, int m)
+{
+    const int esize = p.bf16 ? 2 : 4;
+    return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
+                     (uint32_t)p.K * esize);
+}
+
+__device__ __forceinline__ float4 load_g(rsrc_t g, int j)
+{
+    const v4u v = buf_load16(g, (uint32_t)j * 16u);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
 }
 
 __device__ __forceinline__ void write_scale(const ActDev &p, int m, float a, double ss, bool norm)
@@ -349,42 +403,68 @@ __device__ __forceinline__ int find_problem(const T &b, int key)
     return prob;
 }
 
-// One wave per token row, for K <= 256 * CACHE: each lane keeps its CACHE chunks of 4
-// activations in registers, so the row is read from HBM once; reductions are wave-local
-// (no LDS, no barriers).  Four rows per block.
-template <int CACHE>
-__global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int grow = blockIdx.x * (kActThreads / kWave) + threadIdx.x / kWave;
-    if (grow >= rows)
-        return;
-    const ActDev &p = b.p[find_problem(b, grow)];
-    const int m = grow - p.row_begin;
-    const int chunks = p.K / 4;
-    const bool norm = p.g != nullptr;
-    const rsrc_t xr = row_rsrc(p, m);
-    const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+// One wave per token row, K <= 256 * CACHE, persistent and software-pipelined: each wave
+// walks rows w, w + S, w + 2S, ... (S = waves in the grid) and issues the loads of its next
+// row before it quantizes the current one, so every wave always has a row in flight.  The
+// row's activations stay in registers (raw), the row is read from HBM once, and all
+// reductions are wave-local (no LDS, no barriers).  A row past the end loads from an empty
+// buffer resource (zeros) so the two register sets alternate without copies or waits.
+template <int CACHE, bool BF16>
+struct RowBuf {
+    Chunk<BF16> x[CACHE];
+};
 
-    float4 x[CACHE], u[CACHE];
+__device__ __forceinline__ rsrc_t act_row_rsrc(const ActBatch &b, int row, int rows, int &prob)
+{
+    if (row >= rows) {
+        prob = 0;
+        return make_rsrc(b.p[0].X, 0u);
+    }
+    prob = find_problem(b, row);
+    return row_rsrc(b.p[prob], row - b.p[prob].row_begin);
+}
+
+template <int CACHE, bool BF16>
+__device__ __forceinline__ void act_load(RowBuf<CACHE, BF16> &r, rsrc_t xr, int lane)
+{
 #pragma unroll
     for (int c = 0; c < CACHE; ++c)
-        x[c] = load_chunk(xr, p.bf16, c * kWave + lane);
+        r.x[c].load(xr, c * kWave + lane);  // chunks past the row read as zero
+}
+
+// RMSNorm weights of a row's problem (zeros, unused, without a norm).  Issued before the
+// next row's prefetch: vector-memory loads complete in order, so waiting for them later does
+// not wait for the prefetch.
+template <int CACHE>
+struct NormBuf {
+    float4 g[CACHE];
+};
+
+template <int CACHE>
+__device__ __forceinline__ void norm_load(NormBuf<CACHE> &n, const ActDev &p, int lane)
+{
+    const rsrc_t gr = make_rsrc(p.g, p.g ? (uint32_t)p.K * 4u : 0u);
+#pragma unroll
+    for (int c = 0; c < CACHE; ++c)
+        n.g[c] = load_g(gr, c * kWave + lane);
+}
+
+template <int CACHE, bool BF16>
+__device__ __forceinline__ void act_quant_row(const RowBuf<CACHE, BF16> &r, const NormBuf<CACHE> &n,
+                                              const ActDev &p, int m, int lane)
+{
+    const int chunks = p.K / 4;
+    const bool norm = p.g != nullptr;
     float amax = 0.0f;
     double ss = 0.0;
-    if (norm) {
+    float4 u[CACHE];
 #pragma unroll
-        for (int c = 0; c < CACHE; ++c) {
-            u[c] = mul4(x[c], load_g(gr, c * kWave + lane));
-            amax = fmaxf(amax, absmax4(u[c]));
-            ss = sumsq4(ss, x[c]);   // chunks past the row are zero and add nothing
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < CACHE; ++c) {
-            u[c] = x[c];
-            amax = fmaxf(amax, absmax4(u[c]));
-        }
+    for (int c = 0; c < CACHE; ++c) {
+        const float4 f = r.x[c].f();
+        u[c] = norm ? mul4(f, n.g[c]) : f;
+        amax = fmaxf(amax, absmax4(u[c]));
+        if (norm)
+            ss = sumsq4(ss, f);  // chunks past the row are zero and add nothing
     }
     const float a = wave_max(amax);
     if (norm)
@@ -401,8 +481,32 @@ __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b,
         write_scale(p, m, a, ss, norm);
 }
 
-// One block per token row for long rows (K > 4096): the first kActCache chunks per thread
-// stay in registers, any remainder is read again (from L2) in the second pass.
+template <int CACHE, bool BF16>
+__global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    // Wave-uniform indices (readfirstlane keeps the problem lookup and the buffer
+    // descriptors in scalar registers; otherwise every load is wrapped in a per-lane loop).
+    const int w0 = blockIdx.x * (kActThreads / kWave) +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int S = gridDim.x * (kActThreads / kWave);
+    RowBuf<CACHE, BF16> A, B;
+    NormBuf<CACHE> G;
+    int pa, pb;
+    act_load(A, act_row_rsrc(b, w0, rows, pa), lane);
+    for (int r = w0; r < rows; r += 2 * S) {
+        norm_load(G, b.p[pa], lane);
+        act_load(B, act_row_rsrc(b, r + S, rows, pb), lane);
+        act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
+        norm_load(G, b.p[pb], lane);
+        act_load(A, act_row_rsrc(b, r + 2 * S, rows, pa), lane);
+        if (r + S < rows)
+            act_quant_row(B, G, b.p[pb], r + S - b.p[pb].row_begin, lane);
+    }
+}
+
+// One block per token row for rows longer than the largest wave class: the first kActCache
+// chunks per thread stay in registers, any remainder is read again (from L2).
 __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
 {
     __shared__ float lds_max[kActThreads / kWave];
@@ -413,11 +517,21 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
     const bool norm = p.g != nullptr;
     const rsrc_t xr = row_rsrc(p, m);
     const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+    auto load = [&](int j) {
+        if (p.bf16) {
+            Chunk<true> c;
+            c.load(xr, j);
+            return c.f();
+        }
+        Chunk<false> c;
+        c.load(xr, j);
+        return c.f();
+    };
 
     float4 cache[kActCache];
 #pragma unroll
     for (int c = 0; c < kActCache; ++c)
-        cache[c] = load_chunk(xr, p.bf16, c * kActThreads + threadIdx.x);
+        cache[c] = load(c * kActThreads + threadIdx.x);
     float amax = 0.0f;
     double ss = 0.0;
 #pragma unroll
@@ -428,7 +542,7 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
             ss = sumsq4(ss, cache[c]);
     }
     for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        const float4 x = load_chunk(xr, p.bf16, j);
+        const float4 x = load(j);
         amax = fmaxf(amax, absmax4(norm ? mul4(x, load_g(gr, j)) : x));
         if (norm)
             ss = sumsq4(ss, x);
@@ -461,54 +575,98 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
             q4[j] = quant4(norm ? mul4(cache[c], load_g(gr, j)) : cache[c], inv);
     }
     for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        const float4 x = load_chunk(xr, p.bf16, j);
+        const float4 x = load(j);
         q4[j] = quant4(norm ? mul4(x, load_g(gr, j)) : x, inv);
     }
     if (threadIdx.x == 0)
         write_scale(p, m, a, sum, norm);
 }
 
+// Row-length classes of the wave kernel (chunks of 4 per lane): K <= 256 * class.  Longer
+// rows go to the block kernel.
+constexpr int kActClasses[] = {4, 8, 16};
+constexpr int kActNumClasses = 3;
+
+// Persistent grid: enough blocks to fill every CU at the kernel's occupancy, no more than
+// the rows need.
+template <int CACHE, bool BF16>
+static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
+{
+    static int resident = [] {
+        int dev = 0, cus = 0, per_cu = 0;
+        hipGetDevice(&dev);
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, act_quant_wave_kernel<CACHE, BF16>,
+                                                     kActThreads, 0);
+        return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+    }();
+    const int per_block = kActThreads / kWave;
+    int blocks = (rows + per_block - 1) / per_block;
+    if (blocks > resident)
+        blocks = resident;
+    hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16>), dim3(blocks), dim3(kActThreads), 0,
+                       stream, b, rows);
+}
+
 hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t stream)
 {
-    // Rows up to 4096 wide go to the wave-per-row kernel, longer rows to the block kernel.
-    ActBatch wave_b{}, block_b{};
-    int wave_rows = 0, block_rows = 0, max_wave_k = 0;
-    for (int i = 0; i < count; ++i) {
-        if (q[i].M == 0)
-            continue;
-        const bool wide = q[i].K > 4096;
-        ActBatch &b = wide ? block_b : wave_b;
-        int &rows = wide ? block_rows : wave_rows;
-        ActDev &d = b.p[b.count++];
-        d.X = q[i].X;
-        d.g = q[i].norm_weight;
-        d.Xq = q[i].X_q;
-        d.sx = q[i].x_scale;
-        d.M = (int)q[i].M;
-        d.K = (int)q[i].K;
-        d.bf16 = q[i].x_dtype == BL_BF16;
-        d.eps = q[i].eps;
-        d.row_begin = rows;
-        rows += d.M;
-        if (!wide && d.K > max_wave_k)
-            max_wave_k = d.K;
-    }
-    if (wave_rows) {
-        const int per_block = kActThreads / kWave;
-        const dim3 grid((wave_rows + per_block - 1) / per_block);
-        if (max_wave_k <= 1024)
-            hipLaunchKernelGGL(act_quant_wave_kernel<4>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
-        else if (max_wave_k <= 2048)
-            hipLaunchKernelGGL(act_quant_wave_kernel<8>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
-        else
-            hipLaunchKernelGGL(act_quant_wave_kernel<16>, grid, dim3(kActThreads), 0, stream, wave_b, wave_rows);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    if (block_rows) {
-        hipLaunchKernelGGL(act_quant_block_kernel, dim3(block_rows), dim3(kActThreads), 0, stream, block_b);
-        return hipGetLastError();
+    // Problems with rows up to 4096 share one wave-kernel launch per dtype, sized by their
+    // longest row (shorter rows load zeros past their end); longer rows use the block kernel.
+    // Longest rows first inside a launch.
+    int order[BL_MAX_GROUP];
+    int n = 0;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0)
+            order[n++] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && q[order[j]].K > q[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    for (int wide = 0; wide < 2; ++wide) {
+        for (int bf = 0; bf < 2; ++bf) {
+            ActBatch b{};
+            int rows = 0, cls = 0;
+            for (int i = 0; i < n; ++i) {
+                const bl_act_problem &s = q[order[i]];
+                const int cpl = (int)((s.K / 4 + kWave - 1) / kWave);  // chunks per lane
+                int c = 0;
+                while (c < kActNumClasses && cpl > kActClasses[c])
+                    ++c;
+                if ((c == kActNumClasses) != (wide == 1) || (s.x_dtype == BL_BF16) != (bf == 1))
+                    continue;
+                if (c > cls)
+                    cls = c;
+                ActDev &d = b.p[b.count++];
+                d.X = s.X;
+                d.g = s.norm_weight;
+                d.Xq = s.X_q;
+                d.sx = s.x_scale;
+                d.M = (int)s.M;
+                d.K = (int)s.K;
+                d.bf16 = bf;
+                d.eps = s.eps;
+                d.row_begin = rows;
+                rows += d.M;
+            }
+            if (!rows)
+                continue;
+            if (wide) {
+                hipLaunchKernelGGL(act_quant_block_kernel, dim3(rows), dim3(kActThreads), 0, stream, b);
+            } else if (bf) {
+                if (cls == 0) launch_wave<4, true>(b, rows, stream);
+                else if (cls == 1) launch_wave<8, true>(b, rows, stream);
+                else launch_wave<16, true>(b, rows, stream);
+            } else {
+                if (cls == 0) launch_wave<4, false>(b, rows, stream);
+                else if (cls == 1) launch_wave<8, false>(b, rows, stream);
+                else launch_wave<16, false>(b, rows, stream);
+            }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
     }
     return hipSuccess;
 }
