@@ -9,24 +9,27 @@
 // 16 weight rows as the B operand.  Wasting MFMA rows costs nothing here: the MFMA pipe and
 // the VALU both have several times the throughput the memory stream needs.
 //
-// Work split: one block = 4 waves = 16 weight rows.  The K range of those rows is cut into
-// four contiguous pieces, one per wave; each wave walks its piece in "super-steps" of 16
-// words (256 weights) per row: lane (r = l % 16, g = l / 16) loads words 4g .. 4g+3 of row
-// n0 + r with one 16-byte load and feeds them to four MFMAs.  In MFMA j, lane group g
-// contributes word 16t + 4g + j; the A operand of the same lane takes the matching 16 int8
-// activations, so both operands see the same k in the same byte positions whatever order
-// the hardware uses inside a lane group.  The four waves' integer partial sums are added
-// through LDS (exact, order-free) and wave 0 applies the epilogue
-// y = fl32(fp64(acc * gamma * s_x[m])).
+// Work split: one block = 4 waves = RG groups of 16 weight rows.  The K range of those rows
+// is cut into four contiguous pieces, one per wave; each wave walks its piece in
+// "super-steps" of 256 weights (16 packed words) per row: lane (r = l % 16, g = l / 16)
+// loads words 4g .. 4g+3 of row r of every row group with one 16-byte load per group and
+// feeds them to four MFMAs per group.  In MFMA j, lane group g contributes word 16t + 4g + j;
+// the A operand of the same lane takes the matching 16 int8 activations, loaded once and
+// used by all RG groups (so the activation loads, L2 hits, are 4/RG of the weight loads).
+// Super-steps go in chunks of PF with the next chunk's loads in flight while one chunk is
+// multiplied.  The four waves' integer partial sums are added through LDS (exact, order-
+// free); wave q applies the epilogue y = fl32(fp64(acc * gamma * s_x[m])) to row group q.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bl {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecRows = 16;       // weight rows per block
 constexpr int kSuperWords = 16;    // words per row per super-step
-constexpr int kDecUnroll = 2;      // super-steps with loads in flight per wave
+constexpr int kDecXldsMaxM = 4;    // activations staged in LDS for at most this many tokens
+constexpr int kDecXldsBytes = 48 * 1024;   // ... and at most this many activation bytes
 
 struct FwdDev {
     const int8_t *Xq;
@@ -46,17 +49,24 @@ struct FwdBatch {
 
 // FULL_K: every problem of the launch has K % 256 == 0, so super-steps never run past a
 // row and rows are 64-byte aligned (one 16-byte load per lane, no tail masking).
-template <bool FULL_K>
+template <int RG, bool XLDS, bool FULL_K>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
-    __shared__ v4i red[kDecWaves - 1][kWave];
+    constexpr int ROWS = 16 * RG;
+    // Super-steps per chunk (two chunks of loads in flight).  Four per chunk measured slower:
+    // the dead loads past a short wave's range cost more than the deeper queue gains.
+    constexpr int kDecPF = 2;
+    __shared__ v4i red[kDecWaves][RG][kWave];
+    // XLDS: the activations X[0..M)[0..K) staged in LDS (row stride K), each wave copying
+    // only its own K piece, followed by one zeroed 16-byte chunk per wave.
+    extern __shared__ __align__(16) unsigned char xs[];
 
     int prob = 0;
 #pragma unroll 1
     while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
         ++prob;
     const FwdDev &p = b.p[prob];
-    const int n0 = (blockIdx.x - p.block_begin) * kDecRows;
+    const int n0 = (blockIdx.x - p.block_begin) * ROWS;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -64,65 +74,134 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     const int g = lane >> 4;
     const int words = p.K / 16;
     const int row_bytes = p.K / 4;
-    // Weight rows n0 .. n0+15 (rows past N read as zero); tokens 0 .. M-1 (rows past M zero).
-    const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * words, rows_bytes(n0, kDecRows, p.N, row_bytes));
+    // Weight rows n0 .. n0+ROWS-1 (rows past N read as zero); tokens 0 .. M-1 (rows past M
+    // read as zero: their offsets r * K + ... lie at or past M * K).
+    const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * words, rows_bytes(n0, ROWS, p.N, row_bytes));
     const rsrc_t xres = make_rsrc(p.Xq, (uint32_t)p.M * (uint32_t)p.K);
     const uint32_t wbase = (uint32_t)r * row_bytes;
     const uint32_t xbase = (uint32_t)r * p.K;
+    const uint32_t gstride = 16u * (uint32_t)row_bytes;   // bytes between row groups
+    const uint32_t zero_off = (uint32_t)p.M * (uint32_t)p.K + 16u * (uint32_t)wave;
 
     const int supers = (words + kSuperWords - 1) / kSuperWords;
     const int t_begin = (supers * wave) / kDecWaves;
     const int t_end = (supers * (wave + 1)) / kDecWaves;
 
-    v4i acc = {0, 0, 0, 0};
-    for (int t = t_begin; t < t_end; t += kDecUnroll) {
-        v4u wv[kDecUnroll];
-        v4u xv[kDecUnroll][4];
+    struct Chunk {
+        v4u x[kDecPF][4];
+        v4u w[kDecPF][RG];
+    };
+    // Super-steps t0 .. t0+PF-1; those at or past t_end load zeros (offset "infinity"), so
+    // every chunk issues the same loads and the wait before a chunk's use is a fixed count.
+    auto load = [&](Chunk &c, int t0) {
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
-            const int w = (t + u) * kSuperWords + 4 * g;
-            // A super-step past this wave's range is loaded from offset "infinity" (zeros).
-            const bool live = (t + u) < t_end;
-            if (FULL_K) {
-                wv[u] = buf_load16(wres, live ? wbase + 4u * w : kOOB);
-            } else {
+        for (int u = 0; u < kDecPF; ++u) {
+            const int w = (t0 + u) * kSuperWords + 4 * g;
+            const bool live = (t0 + u) < t_end;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool ok = live && (w + j) < words;
-                    wv[u][j] = buf_load4(wres, ok ? wbase + 4u * (w + j) : kOOB);
+            for (int q = 0; q < RG; ++q) {
+                const uint32_t rowoff = wbase + (uint32_t)q * gstride;
+                if (FULL_K) {
+                    c.w[u][q] = buf_load16(wres, live ? rowoff + 4u * w : kOOB);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bool ok = live && (w + j) < words;
+                        c.w[u][q][j] = buf_load4(wres, ok ? rowoff + 4u * (w + j) : kOOB);
+                    }
                 }
             }
+            if (!XLDS) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool ok = live && (FULL_K || (w + j) < words);
-                xv[u][j] = buf_load16(xres, ok ? xbase + 16u * (w + j) : kOOB);
+                for (int j = 0; j < 4; ++j) {
+                    const bool ok = live && (FULL_K || (w + j) < words);
+                    c.x[u][j] = buf_load16(xres, ok ? xbase + 16u * (w + j) : kOOB);
+                }
             }
         }
+    };
+    // Activation operand of super-step t, word j: from registers, or read from LDS (token
+    // rows past M, dead super-steps and words past K read the zero chunk).
+    auto xop = [&](const Chunk &c, int t0, int u, int j) -> v4i {
+        if (!XLDS)
+            return v4i{(int)c.x[u][j].x, (int)c.x[u][j].y, (int)c.x[u][j].z, (int)c.x[u][j].w};
+        const int w = (t0 + u) * kSuperWords + 4 * g + j;
+        const bool ok = r < p.M && (t0 + u) < t_end && (FULL_K || w < words);
+        return *reinterpret_cast<const v4i *>(xs + (ok ? xbase + 16u * w : zero_off));
+    };
+    v4i acc[RG];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+    for (int q = 0; q < RG; ++q)
+        acc[q] = v4i{0, 0, 0, 0};
+    auto compute = [&](const Chunk &c, int t0) {
+#pragma unroll
+        for (int u = 0; u < kDecPF; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const v4i a = {(int)xv[u][j].x, (int)xv[u][j].y, (int)xv[u][j].z, (int)xv[u][j].w};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word64(wv[u][j]), acc, 0, 0, 0);
+                const v4i a = xop(c, t0, u, j);
+#pragma unroll
+                for (int q = 0; q < RG; ++q)
+                    acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word64(c.w[u][q][j]),
+                                                                  acc[q], 0, 0, 0);
             }
+    };
+
+    // Two chunks of weight loads in flight from the start; then the activation piece is
+    // staged (its loads queue behind them); then each step multiplies the older chunk and
+    // refills it with the chunk two ahead (past the wave's range, loads and multiplies see
+    // zeros).  (The scheduling barrier keeps the refill where it
+    // is: left alone, the compiler sinks it below the next multiplies, halving the loads in
+    // flight.)
+    Chunk c0, c1;
+    load(c0, t_begin);
+    __builtin_amdgcn_sched_barrier(0);
+    load(c1, t_begin + kDecPF);
+    __builtin_amdgcn_sched_barrier(0);
+    if (XLDS) {
+        // Copy this wave's piece, rows 0 .. M-1, k in [16 * kw0, 16 * kw1), 16 bytes per lane.
+        const int kw0 = t_begin * kSuperWords;
+        const int kw1 = min(t_end * kSuperWords, words);
+        const int span = kw1 - kw0;
+        const int chunks = p.M * span;
+        for (int c = lane; c < chunks; c += kWave) {
+            const int m = c / span, kw = kw0 + c % span;
+            const uint32_t off = (uint32_t)m * p.K + 16u * (uint32_t)kw;
+            *reinterpret_cast<v4u *>(xs + off) = buf_load16(xres, off);
         }
+        if (lane == 0)
+            *reinterpret_cast<v4u *>(xs + zero_off) = v4u{0, 0, 0, 0};
+        // Lanes read what other lanes of the same wave wrote: LDS operations of one wave
+        // complete in order, so a wave-scope fence (no instruction, no wait) suffices.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    if (wave > 0)
-        red[wave - 1][lane] = acc;
-    __syncthreads();
-    if (wave != 0)
-        return;
-#pragma unroll
-    for (int w = 0; w < kDecWaves - 1; ++w)
-        acc += red[w][lane];
+    for (int t = t_begin; t < t_end; t += 2 * kDecPF) {
+        compute(c0, t);
+        load(c0, t + 2 * kDecPF);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(c1, t + kDecPF);       // all zeros when past t_end
+        load(c1, t + 3 * kDecPF);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    // acc holds 64 * D[m][n] for m = 4 * g + v (v = register index), n = n0 + r.
-    const int n = n0 + r;
+#pragma unroll
+    for (int q = 0; q < RG; ++q)
+        red[wave][q][lane] = acc[q];
+    __syncthreads();
+    if (wave >= RG)
+        return;
+    v4i s = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w)
+        s += red[w][wave][lane];
+
+    // s holds 64 * D[m][n] for m = 4 * g + v (v = register index), n = n0 + 16 * wave + r.
+    const int n = n0 + 16 * wave + r;
     if (n >= p.N)
         return;
     const double gamma = (double)*p.gamma;
-    const int accv[4] = {acc.x, acc.y, acc.z, acc.w};
+    const int accv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
@@ -136,36 +215,67 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     }
 }
 
-hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStream_t stream)
+template <int RG, bool XLDS>
+static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t stream)
 {
+    // Longest-K problems first: their blocks take longest, so they should not start last.
+    int order[BL_MAX_GROUP];
+    int m = 0;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0 && q[i].N > 0)
+            order[m++] = i;
+    std::stable_sort(order, order + m, [&](int a, int c) { return q[a].K > q[c].K; });
     FwdBatch b{};
     int blocks = 0, n = 0;
     bool full_k = true;
-    for (int i = 0; i < count; ++i) {
-        if (q[i].M == 0 || q[i].N == 0)
-            continue;
-        full_k = full_k && (q[i].K % 256 == 0);
+    for (int o = 0; o < m; ++o) {
+        const bl_forward_problem &s = q[order[o]];
+        full_k = full_k && (s.K % 256 == 0);
         FwdDev &d = b.p[n++];
-        d.Xq = q[i].X_q;
-        d.sx = q[i].x_scale;
-        d.W = q[i].W_packed;
-        d.gamma = q[i].gamma;
-        d.Y = q[i].Y;
-        d.acc = q[i].acc;
-        d.M = (int)q[i].M;
-        d.N = (int)q[i].N;
-        d.K = (int)q[i].K;
+        d.Xq = s.X_q;
+        d.sx = s.x_scale;
+        d.W = s.W_packed;
+        d.gamma = s.gamma;
+        d.Y = s.Y;
+        d.acc = s.acc;
+        d.M = (int)s.M;
+        d.N = (int)s.N;
+        d.K = (int)s.K;
         d.block_begin = blocks;
-        blocks += (d.N + kDecRows - 1) / kDecRows;
+        blocks += (d.N + 16 * RG - 1) / (16 * RG);
     }
     b.count = n;
     if (blocks == 0)
         return hipSuccess;
+    size_t lds = 0;
+    if (XLDS)
+        for (int i = 0; i < n; ++i)
+            lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
     if (full_k)
-        hipLaunchKernelGGL(decode_kernel<true>, dim3(blocks), dim3(kDecThreads), 0, stream, b);
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, true>), dim3(blocks), dim3(kDecThreads), lds, stream, b);
     else
-        hipLaunchKernelGGL(decode_kernel<false>, dim3(blocks), dim3(kDecThreads), 0, stream, b);
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, false>), dim3(blocks), dim3(kDecThreads), lds, stream, b);
     return hipGetLastError();
+}
+
+// Row groups per block: as many as still leave at least one block per compute unit
+// (fewer activation loads per weight byte), else one (more blocks for small layers).
+hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStream_t stream)
+{
+    int64_t rows = 0;
+    bool xlds = true;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0 && q[i].N > 0) {
+            rows += q[i].N;
+            xlds = xlds && q[i].M <= kDecXldsMaxM && q[i].M * q[i].K <= kDecXldsBytes;
+        }
+    if (xlds)
+        return launch_rg<1, true>(q, count, stream);
+    if (rows >= 256 * 64)
+        return launch_rg<4, false>(q, count, stream);
+    if (rows >= 256 * 32)
+        return launch_rg<2, false>(q, count, stream);
+    return launch_rg<1, false>(q, count, stream);
 }
 
 }  // namespace bl

@@ -4,17 +4,17 @@
 // zeros are multiplied, the method computes the dense ternary product), so it belongs on the
 // int8 matrix cores: v_mfma_i32_16x16x64_i8.  bitone README, "Features": the quantized
 // weights stay in on-chip memory inside the GEMM and are never materialized in HBM; here the
-// packed 2-bit words go straight from global memory into registers and are expanded there
-// (plane64: one shift and one mask per four weights, giving 64 * c as int8), while the int8
-// activations are staged through LDS because every wave of the block reads them.
+// packed 2-bit words (0.25 B per weight) travel to LDS and are expanded to int8 in registers
+// right before the multiply (plane64: one shift and one mask per four weights, giving 64 * c).
 //
-// Block tile 128 (tokens) x 128 (weight rows); 4 waves in a 2 x 2 arrangement, each owning a
-// 64 x 64 sub-tile = 4 x 4 MFMA tiles.  The K loop advances in super-steps of 256 weights
-// (16 packed words per row): lane (r = l % 16, g = l / 16) loads words 4g .. 4g+3 of its
-// weight row with one 16-byte load and uses word 4g + j in MFMA j; the matching activation
-// bytes 16 (4g + j) .. +15 of its token row come from LDS with one 16-byte read.  The next
-// super-step's activations and weights are loaded into registers while the current one is
-// computed, and LDS is double-buffered, so one barrier per super-step suffices.
+// Block tile BM (tokens) x BN (weight rows), 256 x 256 with 8 waves (4 x 2) or 128 x 128
+// with 4 waves (2 x 2); each wave owns a (BM/WM) x (BN/WN) sub-tile of 16 x 16 MFMA tiles.
+// The K loop runs in stages of KS = 128 weights through an NST = 4 deep ring of LDS buffers:
+// activation rows (BM x 128 bytes) and packed weight rows (BN x 32 bytes) go global -> LDS
+// by gfx950 direct-to-LDS buffer loads, three stages in flight while one is multiplied, one
+// barrier per stage.  Per stage and lane (r = l % 16, g = l / 16): the packed words of its
+// weight rows from LDS, expanded into B operands; the A operands (16 activation bytes of
+// token row r, k group g) from LDS with one 16-byte read each.
 // Epilogue: y = fl32(fp64(acc * gamma * s_x[m])), acc = (MFMA sum) / 64 (exact shift).
 #include <stdlib.h>
 #include <string.h>
@@ -365,23 +365,17 @@ static hipError_t launch_tiles(const bl_forward_problem *q, int count, hipStream
 }
 
 using TileBig = Tile<256, 256, 4, 2, 128, 4>;    // 160 KB LDS, one block (8 waves) per CU
-using TileBigB = Tile<256, 256, 2, 4, 128, 4>;
-using TileBigC = Tile<256, 256, 2, 2, 128, 4>;
-using TileMid = Tile<256, 128, 2, 2, 128, 4>;
 using TileSmall = Tile<128, 128, 2, 2, 128, 4>;  // 80 KB LDS, two blocks per CU
 
 static int tile_override()
 {
-    // Measurement-only knob to A/B tile layouts (BITLINEAR_PREFILL_TILE=big|bigb|bigc|mid|small).
+    // Measurement-only knob to A/B the two tile layouts (BITLINEAR_PREFILL_TILE=big|small).
     static int v = [] {
         const char *e = getenv("BITLINEAR_PREFILL_TILE");
         if (!e)
             return 0;
         if (!strcmp(e, "big")) return 1;
-        if (!strcmp(e, "bigb")) return 2;
-        if (!strcmp(e, "bigc")) return 3;
-        if (!strcmp(e, "mid")) return 4;
-        if (!strcmp(e, "small")) return 5;
+        if (!strcmp(e, "small")) return 2;
         return 0;
     }();
     return v;
@@ -393,10 +387,7 @@ hipError_t launch_forward_prefill(const bl_forward_problem *q, int count, hipStr
 {
     switch (tile_override()) {
     case 1: return launch_tiles<TileBig>(q, count, stream);
-    case 2: return launch_tiles<TileBigB>(q, count, stream);
-    case 3: return launch_tiles<TileBigC>(q, count, stream);
-    case 4: return launch_tiles<TileMid>(q, count, stream);
-    case 5: return launch_tiles<TileSmall>(q, count, stream);
+    case 2: return launch_tiles<TileSmall>(q, count, stream);
     default: break;
     }
     int64_t big = 0;

@@ -196,6 +196,9 @@ FWD_SHAPES = [
     (3, 33, 80), (8, 1536, 1536), (16, 2048, 768), (16, 100, 272),
     (17, 40, 64), (100, 130, 272), (129, 129, 1040), (256, 512, 768), (300, 257, 4096),
     (517, 1000, 1536),
+    # Decode launch variants: activations staged in LDS up to its byte limit, and the
+    # two- and four-row-group blocks that large layers get, with K a multiple of 256 or not.
+    (4, 70, 12288), (2, 16400, 1040), (6, 8200, 80), (5, 16448, 272), (12, 16400, 512),
 ]
 
 
