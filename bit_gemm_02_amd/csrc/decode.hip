@@ -146,6 +146,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
             }
     };
 
+    // Epilogue inputs first (gamma, the row scales of this lane's tokens m = 4g + v): the
+    // epilogue then does not wait on a memory round trip of its own.
+    const rsrc_t sres = make_rsrc(p.sx, (uint32_t)p.M * 4u);
+    float sxv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        sxv[v] = __uint_as_float(buf_load4(sres, (uint32_t)(4 * g + v) * 4u));   // past M: 0
+    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    __builtin_amdgcn_sched_barrier(0);
+
     // Two chunks of weight loads in flight from the start; then the activation piece is
     // staged (its loads queue behind them); then each step multiplies the older chunk and
     // refills it with the chunk two ahead (past the wave's range, loads and multiplies see
@@ -200,14 +210,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     const int n = n0 + 16 * wave + r;
     if (n >= p.N)
         return;
-    const double gamma = (double)*p.gamma;
+    const double gamma = (double)gammaf;
     const int accv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < p.M) {
             const int a = accv[v] >> 6;  // exact: the sum is a multiple of 64
-            const double scale = gamma * (double)p.sx[m];
+            const double scale = gamma * (double)sxv[v];
             p.Y[(int64_t)m * p.N + n] = (float)((double)a * scale);
             if (p.acc)
                 p.acc[(int64_t)m * p.N + n] = a;

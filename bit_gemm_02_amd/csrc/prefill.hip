@@ -52,13 +52,50 @@ __device__ __forceinline__ int xcd_order(int b, int nb)
     return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at lds + 16 * l; an
-// out-of-range offset writes zeros.  The LDS pointer must be wave-uniform.
-__device__ __forceinline__ void load_lds16(rsrc_t r, unsigned char *lds, uint32_t offset)
+// Raw buffer descriptor as four scalar dwords: base address, stride 0, size in bytes, and
+// the gfx9-family raw-access word.  Offsets at or past `bytes` read zero.
+__device__ __forceinline__ v4i make_desc(const void *base, uint32_t bytes)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, (int)offset, 0, 0, 0);
+    const uint64_t a = (uint64_t)base;
+    v4i d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.w = 0x00020000;
+    return d;
+}
+
+// LDS byte address of a shared-memory pointer, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
+{
+    typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_uchar *)p);
+}
+
+// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at LDS address
+// lds + 16 * l; an out-of-range offset writes zeros.  Issued from inline assembly so that the
+// compiler does not model it: modelled, it cannot tell the in-flight stages apart and drains
+// every load before the first LDS read of each unrolled group of stages.  The instruction
+// has no register result; its completion is ordered by the pipeline's explicit vmcnt waits
+// and barriers, and the "memory" clobber keeps LDS accesses from moving across it.
+__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, uint32_t offset)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(offset), "s"(desc)
+                 : "memory", "m0");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations (the barrier
+// instruction alone does not stop the compiler from moving LDS accesses across it), without
+// the waits a memory fence would add.
+__device__ __forceinline__ void block_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave (direct-to-LDS
@@ -170,8 +207,8 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     const int stages = (K + KS - 1) / KS;
 
     // Activation rows m0 .. m0+BM-1 and weight rows n0 .. n0+BN-1; rows past M / N read zero.
-    const rsrc_t xres = make_rsrc(p.Xq + (int64_t)m0 * K, rows_bytes(m0, BM, p.M, K));
-    const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * (K / 16), rows_bytes(n0, BN, p.N, row_bytes));
+    const v4i xres = make_desc(p.Xq + (int64_t)m0 * K, rows_bytes(m0, BM, p.M, K));
+    const v4i wres = make_desc(p.W + (int64_t)n0 * (K / 16), rows_bytes(n0, BN, p.N, row_bytes));
 
     // Load plan.  Activations: wave w fills rows w*BM/WAVES .. +BM/WAVES, 64/CPR rows per 1 KB
     // load; lane l -> row (l / CPR), position l % CPR, global chunk position ^ swizzle.
@@ -202,7 +239,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             uint32_t off = ((uint32_t)row * K + (uint32_t)k) | dead;
             if (!FULL_K)
                 off = k < K ? off : kOOB;
-            load_lds16(xres, st + row0 * KS, off);
+            dma16(xres, lds_addr(st + row0 * KS), off);
         }
 #pragma unroll
         for (int i = 0; i < T::WINST; ++i) {
@@ -212,7 +249,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             uint32_t off = ((uint32_t)row * row_bytes + (uint32_t)kb) | dead;
             if (!FULL_K)
                 off = kb < row_bytes ? off : kOOB;
-            load_lds16(wres, st + T::XBYTES + row0 * WROW, off);
+            dma16(wres, lds_addr(st + T::XBYTES + row0 * WROW), off);
         }
     };
 
@@ -267,6 +304,21 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
         }
     };
 
+    // Row scales and gamma, loaded before the pipeline starts: older than every stage load,
+    // they have landed by the first stage wait, and the epilogue does not wait on memory.
+    float sxv[MI][4];
+    {
+        const rsrc_t sres = make_rsrc(p.sx, (uint32_t)p.M * 4u);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + wm * T::TM + mi * 16 + 4 * g + v;   // rows past M read 0
+                sxv[mi][v] = __uint_as_float(buf_load4(sres, (uint32_t)m * 4u));
+            }
+    }
+    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+
     // Prologue: stages 0 .. NST-2 in flight.
     static_for<0, NST - 1>([&](auto S) { issue(S, S.value); });
     // Main loop, unrolled by NST so every stage buffer is a compile-time choice.  Stage t has
@@ -276,7 +328,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             const int t = t0 + S.value;
             if (t < stages) {
                 wait_vmem<(NST - 2) * T::LOADS>();
-                __builtin_amdgcn_s_barrier();
+                block_sync();
                 issue(IC<(decltype(S)::value + NST - 1) % NST>{}, t + NST - 1);
                 compute(S);
             }
@@ -285,7 +337,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 
     // Epilogue: acc[mi][ni] register v holds 64 * D[m][n] for
     // m = m0 + wm * TM + mi * 16 + 4 * g + v and n = n0 + wn * TN + ni * 16 + r.
-    const double gamma = (double)*p.gamma;
+    const double gamma = (double)gammaf;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -293,7 +345,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             const int m = m0 + wm * T::TM + mi * 16 + 4 * g + v;
             if (m >= p.M)
                 continue;
-            const double scale = gamma * (double)p.sx[m];
+            const double scale = gamma * (double)sxv[mi][v];
             float *yrow = p.Y + (int64_t)m * p.N;
             int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
 #pragma unroll
