@@ -7,8 +7,7 @@ One step = one pass of the whole hot path over one layer set of the workload:
     int8 activation quantization of every input             (grouped: 1 launch)
     ternary x int8 product + rescale epilogue               (grouped: 1 launch)
   decode leg (M = 1, weights packed once outside timing):
-    int8 activation quantization                            (grouped: 1 launch)
-    streaming product + epilogue                            (grouped: 1 launch)
+    int8 activation quantization + streaming product + epilogue, fused  (grouped: 1 launch)
 Inputs are seeded synthetic tensors (``workloads``) resident in HBM before timing starts.
 Weights (fp32 masters for the prefill leg, packed words for the decode leg) and prefill
 activations rotate through distinct copies totalling about 1 GB, so each step reads them
@@ -178,29 +177,26 @@ class Setup:
                                         self.act_pre[i][0].data_ptr(), self.act_pre[i][1].data_ptr(),
                                         self.M_pre, m.K, dt, 1e-6)
             self.aq_pre_tables.append(arr)
-        arr = (bl._ActProblem * n)()
-        for i, m in enumerate(mats):
-            X = self.X_dec[i]
-            g = self.norms[i]
-            dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
-            arr[i] = bl._ActProblem(X.data_ptr(), None if g is None else g.data_ptr(),
-                                    self.act_dec[i][0].data_ptr(), self.act_dec[i][1].data_ptr(),
-                                    1, m.K, dt, 1e-6)
-        self.aq_dec_table = arr
         arr = (bl._ForwardProblem * n)()
         for i, m in enumerate(mats):
             arr[i] = bl._ForwardProblem(self.act_pre[i][0].data_ptr(), self.act_pre[i][1].data_ptr(),
                                         self.P_pre[i].data_ptr(), self.g_pre[i].data_ptr(),
                                         self.Y_pre[i].data_ptr(), None, self.M_pre, m.N, m.K)
         self.fwd_pre_table = arr
-        self.fwd_dec_tables = []
+        # Decode leg: the fused layer call (activation quantization inside the product).
+        self.lin_dec_tables = []
         for r in range(self.R_dec):
-            arr = (bl._ForwardProblem * n)()
+            arr = (bl._LinearProblem * n)()
             for i, m in enumerate(mats):
-                arr[i] = bl._ForwardProblem(self.act_dec[i][0].data_ptr(), self.act_dec[i][1].data_ptr(),
-                                            self.P_dec[r][i].data_ptr(), self.g_dec[i].data_ptr(),
-                                            self.Y_dec[i].data_ptr(), None, 1, m.N, m.K)
-            self.fwd_dec_tables.append(arr)
+                X = self.X_dec[i]
+                g = self.norms[i]
+                dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
+                assert bl.linear_fused(self.M_dec, m.K)
+                arr[i] = bl._LinearProblem(X.data_ptr(), None if g is None else g.data_ptr(),
+                                           self.P_dec[r][i].data_ptr(), self.g_dec[i].data_ptr(),
+                                           self.Y_dec[i].data_ptr(), None, None,
+                                           self.M_dec, m.N, m.K, dt, 1e-6)
+            self.lin_dec_tables.append(arr)
         import ctypes as C
         self._addr = C.addressof
         self.ws_ptr = self.ws.data_ptr()
@@ -211,8 +207,18 @@ class Setup:
         return sum(2 * self.M_pre * m.N * m.K for m in self.wl.matrices)
 
     def decode_bytes(self) -> int:
+        # Packed weights, the raw activations (fp32 or bf16) and norm weights read, gamma, and
+        # the fp32 outputs written.
         M = self.M_dec
-        return sum(m.N * m.K // 4 + M * m.K + 4 * M + 4 + 4 * M * m.N for m in self.wl.matrices)
+        xb = 2 if self.wl.x_dtype == "bf16" else 4
+        return sum(m.N * m.K // 4 + M * m.K * xb + (4 * m.K if m.norm else 0) + 4 + 4 * M * m.N
+                   for m in self.wl.matrices)
+
+    def prefill_bytes(self) -> int:
+        # What the prefill product must move: int8 activations, packed weights, scales, gamma
+        # and the fp32 outputs.
+        M = self.M_pre
+        return sum(M * m.K + m.N * m.K // 4 + 4 * M + 4 + 4 * M * m.N for m in self.wl.matrices)
 
     def weight_quant_bytes(self) -> int:
         if self.W_pre is None:
@@ -248,12 +254,38 @@ class Setup:
         rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
         assert rc == 0, rc
         mark("t_gemm")
-        rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_dec_table), n, stream)
-        assert rc == 0, rc
-        mark("t_aqd")
-        rc = L.bitlinear_forward_grouped(self._addr(self.fwd_dec_tables[rd]), n, stream)
+        rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[rd]), n, stream)
         assert rc == 0, rc
         mark("t_dec")
+
+    def launch_only(self, key: str, i: int, stream):
+        """One launch group of the step by itself (same tables as in the step)."""
+        L = self.bl.lib()
+        n = self.count
+        if key == "prefill_gemm":
+            rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+        elif key == "decode_linear":
+            rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
+        elif key == "act_quant_prefill":
+            rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[i % self.R_pre]), n, stream)
+        else:
+            rc = L.bitlinear_quantize_weights_grouped(self._addr(self.wq_tables[i % self.R_pre]), n,
+                                                       self.ws_ptr, self.ws_bytes, stream)
+        assert rc == 0, rc
+
+
+def isolated_ms(torch, setup: Setup, key: str, stream, reps: int) -> float:
+    """Average duration of one launch group run alone, back to back (events around the loop)."""
+    for i in range(3):
+        setup.launch_only(key, i, stream)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        setup.launch_only(key, i, stream)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
 
 
 def interval_ms(ev, a, b):
@@ -261,11 +293,11 @@ def interval_ms(ev, a, b):
     return float(np.mean(xs)) if xs else float("nan")
 
 
-# Kernel name fragment -> (roofline key, source file).  Activation quantization runs twice per
-# step (prefill and decode); the prefill launches are the ones with more than 64 blocks.
+# Kernel name fragment -> (roofline key, source file).  (The decode leg quantizes its
+# activations inside decode_kernel, so every act_quant launch belongs to the prefill leg.)
 KERNELS = {
     "prefill_kernel": ("prefill_gemm", "prefill.hip"),
-    "decode_kernel": ("decode_gemv", "decode.hip"),
+    "decode_kernel": ("decode_linear", "decode.hip"),
     "act_quant": ("act_quant_prefill", "quant.hip"),
     "gamma_partial_kernel": ("weight_quant", "quant.hip"),
     "quant_pack_kernel": ("weight_quant", "quant.hip"),
@@ -303,8 +335,6 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -
         for name, grid, kib in d.values():
             for frag, (key, src) in KERNELS.items():
                 if frag in name:
-                    if key == "act_quant_prefill" and grid <= 64 * 256:
-                        key = "act_quant_decode"
                     acc[(key, src)].append((name, kib * 1024.0 * factor))
         return acc
 
@@ -453,49 +483,69 @@ def main():
     wall_ms = (time.perf_counter() - t_wall0) * 1e3 / args.steps
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # Per-launch durations: the same steps again with events around every launch group.
+    # Per-launch durations, two ways, both outside the timed region: (a) the same steps again
+    # with events around every launch group (includes the dispatch gap each launch pays inside
+    # the step); (b) each launch group alone, back to back, events around the loop (what a
+    # kernel trace reports as its duration; used for the roofline figures).
     ev = {}
     for i in range(args.steps):
         setup.step(args.warmup + args.steps + i, sptr, ev)
     torch.cuda.synchronize()
-    ms = {
+    in_step = {
         "weight_quant": interval_ms(ev, "t0", "t_wq"),
         "act_quant_prefill": interval_ms(ev, "t_wq", "t_aq"),
         "prefill_gemm": interval_ms(ev, "t_aq", "t_gemm"),
-        "act_quant_decode": interval_ms(ev, "t_gemm", "t_aqd"),
-        "decode_gemv": interval_ms(ev, "t_aqd", "t_dec"),
+        "decode_linear": interval_ms(ev, "t_gemm", "t_dec"),
     }
+    if not setup.wq_tables:
+        in_step.pop("weight_quant")
     ms_with_events = interval_ms(ev, "t0", "t_dec")
+    ms = {k: isolated_ms(torch, setup, k, sptr, args.steps) for k in in_step}
 
     ops = setup.prefill_ops()
+    pre_bytes = setup.prefill_bytes()
     dec_bytes = setup.decode_bytes()
-    gemm_tops = ops / (ms["prefill_gemm"] * 1e-3) / 1e12
-    dec_gbps = dec_bytes / (ms["decode_gemv"] * 1e-3) / 1e9
     wq_bytes = setup.weight_quant_bytes()
     aq_bytes = setup.act_quant_bytes(M_pre)
+    ridge = INT8_PEAK_TOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)          # ops per byte
+    ai = ops / pre_bytes
+    gemm_tops = ops / (ms["prefill_gemm"] * 1e-3) / 1e12
+    gemm_gbps = pre_bytes / (ms["prefill_gemm"] * 1e-3) / 1e9
+    attainable = min(INT8_PEAK_TOPS, ai * HBM_PEAK_GBPS / 1e3)     # TOPS
+    dec_gbps = dec_bytes / (ms["decode_linear"] * 1e-3) / 1e9
+
+    def hbm(nbytes, key, what):
+        a = nbytes / (ms[key] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBPS, "us_per_launch": ms[key] * 1e3,
+                "us_per_launch_in_step": in_step[key] * 1e3, "algorithmic": what}
+
+    pre_what = (f"{ops} int8 ops (2 M N K over {setup.count} products); {pre_bytes} bytes "
+                f"(M K + N K / 4 + 4 M + 4 + 4 M N summed); {ai:.0f} ops/B vs ridge {ridge:.0f}")
+    if ai < ridge:
+        # Below the ridge the product is bound by HBM: judge it in bytes.
+        pre_roof = hbm(pre_bytes, "prefill_gemm", pre_what)
+    else:
+        pre_roof = {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS,
+                    "unit": "TFLOP/s", "frac": gemm_tops / INT8_PEAK_TOPS,
+                    "us_per_launch": ms["prefill_gemm"] * 1e3,
+                    "us_per_launch_in_step": in_step["prefill_gemm"] * 1e3, "algorithmic": pre_what}
+    pre_roof.update({"tops": gemm_tops, "frac_int8_peak": gemm_tops / INT8_PEAK_TOPS,
+                     "attainable_tops": attainable, "frac_attainable": gemm_tops / attainable})
     rooflines = {
-        "prefill_gemm": {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS,
-                         "unit": "TFLOP/s", "frac": gemm_tops / INT8_PEAK_TOPS,
-                         "us_per_launch": ms["prefill_gemm"] * 1e3,
-                         "algorithmic": f"{ops} int8 ops (2 M N K over {setup.count} products)"},
-        "decode_gemv": {"bound": "hbm", "achieved": dec_gbps, "peak": HBM_PEAK_GBPS,
-                        "unit": "GB/s", "frac": dec_gbps / HBM_PEAK_GBPS,
-                        "us_per_launch": ms["decode_gemv"] * 1e3,
-                        "algorithmic": f"{dec_bytes} bytes (N K / 4 + M K + 4 M + 4 + 4 M N summed)"},
-        "act_quant_prefill": {"bound": "hbm",
-                              "achieved": aq_bytes / (ms["act_quant_prefill"] * 1e-3) / 1e9,
-                              "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "us_per_launch": ms["act_quant_prefill"] * 1e3},
+        "prefill_gemm": pre_roof,
+        "decode_linear": hbm(dec_bytes, "decode_linear",
+                             f"{dec_bytes} bytes (N K / 4 + M K x-bytes (+ 4 K norm) + 4 + 4 M N "
+                             "summed; activation quantization fused)"),
+        "act_quant_prefill": hbm(aq_bytes, "act_quant_prefill",
+                                 f"{aq_bytes} bytes (M K x-bytes + M K + 4 M (+ 4 K norm) summed)"),
     }
-    rooflines["act_quant_prefill"]["frac"] = rooflines["act_quant_prefill"]["achieved"] / HBM_PEAK_GBPS
-    if wq_bytes:
-        a = wq_bytes / (ms["weight_quant"] * 1e-3) / 1e9
-        rooflines["weight_quant"] = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS,
-                                     "unit": "GB/s", "frac": a / HBM_PEAK_GBPS,
-                                     "us_per_launch_pair": ms["weight_quant"] * 1e3}
+    if "weight_quant" in ms:
+        rooflines["weight_quant"] = hbm(wq_bytes, "weight_quant",
+                                        f"{wq_bytes} bytes (4 N K + N K / 4 + 4 summed; one read "
+                                        "of W is the minimum, the two launches read it twice)")
     # Dominant kernel = largest share of the step.
-    dom = max(("prefill_gemm", "decode_gemv", "act_quant_prefill", "weight_quant"),
-              key=lambda k: ms.get(k, 0.0) if k in rooflines else -1)
+    dom = max(in_step, key=lambda k: in_step[k])
     traffic = load_traffic()
     t = traffic.get((dom, wl.key))
     roof = dict(rooflines[dom])
@@ -522,11 +572,12 @@ def main():
                    "weights": wl.weights, "x_dtype": wl.x_dtype,
                    "rotation_copies": {"prefill": setup.R_pre, "decode": setup.R_dec}},
         "decode": {"gbps": round(dec_gbps, 2), "frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "bytes": dec_bytes, "us_gemv": round(ms["decode_gemv"] * 1e3, 3),
-                   "us_act_quant": round(ms["act_quant_decode"] * 1e3, 3)},
+                   "bytes": dec_bytes, "us_linear": round(ms["decode_linear"] * 1e3, 3)},
         "prefill": {"gemm_tops": round(gemm_tops, 2), "frac_int8": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                    "gemm_gbps": round(gemm_gbps, 1), "ops_per_byte": round(ai, 1),
+                    "frac_attainable": round(gemm_tops / attainable, 4),
                     "ops": ops, "us_gemm": round(ms["prefill_gemm"] * 1e3, 3),
-                    "us_weight_quant": round(ms["weight_quant"] * 1e3, 3),
+                    "us_weight_quant": round(ms["weight_quant"] * 1e3, 3) if "weight_quant" in ms else None,
                     "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3)},
         "roofline": roof,
         "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -11,6 +11,7 @@ Steps (see the header for the passages each follows):
   pack_codes        pack pre-ternarized int8 codes
   quantize_acts     per-token absmax int8 activations (optionally with the SubLN RMSNorm)
   forward           exact int32 ternary x int8 product and the gamma * s_x epilogue
+  linear_grouped    steps 3 to 5 in one launch for decode-sized token counts
 """
 
 from __future__ import annotations
@@ -28,6 +29,8 @@ BL_F32, BL_BF16 = 0, 1
 MAX_GROUP = 16
 MAX_K = 262144
 DECODE_MAX_M = 16
+LINEAR_FUSED_MAX_M = 4
+LINEAR_FUSED_MAX_BYTES = 49152
 
 
 class BitLinearError(RuntimeError):
@@ -55,6 +58,14 @@ class _ForwardProblem(ctypes.Structure):
                 ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
                 ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _LinearProblem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("x_dtype", ctypes.c_int), ("eps", ctypes.c_float)]
 
 
 _lib = None
@@ -95,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward.restype = ctypes.c_int
     L.bitlinear_forward_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_forward_grouped.restype = ctypes.c_int
+    L.bitlinear_linear_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_linear_grouped.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -274,8 +287,39 @@ def forward_grouped(problems: Sequence[dict], stream=None) -> None:
            lib().bitlinear_forward_grouped(ctypes.addressof(arr), count, _stream(stream)))
 
 
+def linear_fused(M: int, K: int) -> bool:
+    """Whether a layer call of M tokens and K inputs takes the one-launch decode form."""
+    return M <= LINEAR_FUSED_MAX_M and M * K <= LINEAR_FUSED_MAX_BYTES
+
+
+def linear_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Layer calls as dicts with keys X (fp32/bf16 [M, K]), W_packed, gamma, Y (preallocated
+    fp32 [M, N]) and optional norm_weight, eps, X_q, x_scale (code/scale outputs; required
+    when the call is not decode-sized).  Decode-sized calls share one fused launch."""
+    count = len(problems)
+    arr = (_LinearProblem * max(count, 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        N = p["W_packed"].shape[0]
+        arr[i] = _LinearProblem(_ptr(X), _ptr(p.get("norm_weight")), _ptr(p["W_packed"]),
+                                _ptr(p["gamma"]), _ptr(p["Y"]), _ptr(p.get("X_q")),
+                                _ptr(p.get("x_scale")), M, N, K, _x_dtype(X),
+                                float(p.get("eps", 1e-6)))
+    _check("bitlinear_linear_grouped",
+           lib().bitlinear_linear_grouped(ctypes.addressof(arr), count, _stream(stream)))
+
+
 def linear(X: torch.Tensor, W_packed: torch.Tensor, gamma: torch.Tensor,
            norm_weight: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None):
-    """Convenience: quantize_acts followed by forward (two launches)."""
-    Xq, sx = quantize_acts(X, norm_weight, eps, stream=stream)
-    return forward(Xq, sx, W_packed, gamma, stream=stream)
+    """Y = BitLinear(X): steps 3 to 5 (one fused launch when decode-sized, else two)."""
+    _dev(X, "X")
+    M, K = X.shape
+    N = W_packed.shape[0]
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    p = dict(X=X, W_packed=W_packed, gamma=gamma, Y=Y, norm_weight=norm_weight, eps=eps)
+    if not linear_fused(M, K):
+        p["X_q"] = torch.empty((M, K), dtype=torch.int8, device=X.device)
+        p["x_scale"] = torch.empty(M, dtype=torch.float32, device=X.device)
+    linear_grouped([p], stream=stream)
+    return Y

@@ -80,6 +80,36 @@ bl_status check_forward(const bl_forward_problem &p)
 
 bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
 
+bool linear_fused(const bl_linear_problem &p)
+{
+    return p.M <= BL_LINEAR_FUSED_MAX_M && p.M * p.K <= BL_LINEAR_FUSED_MAX_BYTES;
+}
+
+bl_status check_linear(const bl_linear_problem &p)
+{
+    const bool empty = p.M == 0 || p.N == 0;
+    if (!p.gamma || (!empty && (!p.X || !p.W_packed || !p.Y)))
+        return BL_ERR_NULL;
+    if (p.x_dtype != BL_F32 && p.x_dtype != BL_BF16)
+        return BL_ERR_DTYPE;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK)
+        s = check_rows(p.N);
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    // The two-step form needs the intermediate codes and scales.
+    if (!empty && !linear_fused(p) && (!p.X_q || !p.x_scale))
+        return BL_ERR_NULL;
+    if (!aligned16(p.X) || !aligned16(p.W_packed) || !aligned16(p.X_q) ||
+        (p.norm_weight && !aligned16(p.norm_weight)) ||
+        (reinterpret_cast<uintptr_t>(p.x_scale) & 3u) || (reinterpret_cast<uintptr_t>(p.gamma) & 3u) ||
+        (reinterpret_cast<uintptr_t>(p.Y) & 3u))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +260,51 @@ bl_status bitlinear_forward(const int8_t *X_q, const float *x_scale, const uint3
 {
     bl_forward_problem p{X_q, x_scale, W_packed, gamma, Y, acc, M, N, K};
     return bitlinear_forward_grouped(&p, 1, stream);
+}
+
+bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl_linear_problem fused[BL_MAX_GROUP];
+    bl_act_problem act[BL_MAX_GROUP];
+    bl_forward_problem fwd[BL_MAX_GROUP];
+    int nf = 0, nt = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_linear_problem &p = problems[i];
+        bl_status s = check_linear(p);
+        if (s != BL_OK)
+            return s;
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (linear_fused(p)) {
+            fused[nf++] = p;
+            blocks += (p.N + 15) / 16;
+        } else {
+            act[nt] = bl_act_problem{p.X, p.norm_weight, p.X_q, p.x_scale, p.M, p.K, p.x_dtype, p.eps};
+            fwd[nt] = bl_forward_problem{p.X_q, p.x_scale, p.W_packed, p.gamma, p.Y, nullptr,
+                                         p.M, p.N, p.K};
+            ++nt;
+        }
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (nf) {
+        bl_status s = from_hip(bl::launch_linear_decode(fused, nf, st));
+        if (s != BL_OK)
+            return s;
+    }
+    if (nt) {
+        bl_status s = bitlinear_quantize_acts_grouped(act, nt, stream);
+        if (s != BL_OK)
+            return s;
+        return bitlinear_forward_grouped(fwd, nt, stream);
+    }
+    return BL_OK;
 }
 
 }  // extern "C"

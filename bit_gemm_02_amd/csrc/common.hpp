@@ -116,6 +116,64 @@ __device__ __forceinline__ double wave_sum_fixed(double v)
     return v;
 }
 
+// ----------------------------------------------------------------- activation quantization
+//
+// Shared by the activation-quantization kernels and the fused decode path, so both produce
+// the same codes and scales from the same absmax (and sum of squares).
+
+// q = clamp(rint(u * inv), -127, 127) as an integer.  rint of the fp32 product (round half
+// to even), then an exact integer clamp; the conversion maps NaN to 0 and saturates
+// infinities, so the degenerate rows (127/a overflowing to inf, 0 * inf = NaN) give the
+// same codes as clamping in floating point and sending NaN to 0.
+__device__ __forceinline__ int quant_one(float u, float inv)
+{
+    const int i = (int)__builtin_rintf(u * inv);
+    return min(max(i, -127), 127);
+}
+
+__device__ __forceinline__ char4 quant4(float4 u, float inv)
+{
+    const uint32_t b0 = (uint32_t)quant_one(u.x, inv) & 0xFFu;
+    const uint32_t b1 = (uint32_t)quant_one(u.y, inv) & 0xFFu;
+    const uint32_t b2 = (uint32_t)quant_one(u.z, inv) & 0xFFu;
+    const uint32_t b3 = (uint32_t)quant_one(u.w, inv) & 0xFFu;
+    const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    char4 c;
+    __builtin_memcpy(&c, &w, 4);
+    return c;
+}
+
+__device__ __forceinline__ float4 mul4(float4 a, float4 b)
+{
+    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+
+__device__ __forceinline__ float absmax4(float4 u)
+{
+    return fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w)));
+}
+
+__device__ __forceinline__ double sumsq4(double s, float4 x)
+{
+    s += (double)x.x * (double)x.x;
+    s += (double)x.y * (double)x.y;
+    s += (double)x.z * (double)x.z;
+    s += (double)x.w * (double)x.w;
+    return s;
+}
+
+// s_x of a row: a / 127, or a * r / 127 with r = 1 / sqrt(sum(x^2) / K + eps) in fp64 when the
+// RMSNorm is fused; 0 for an all-zero row.
+__device__ __forceinline__ float act_scale(float a, double ss, int K, float eps, bool norm)
+{
+    if (a == 0.0f)
+        return 0.0f;
+    if (!norm)
+        return a / 127.0f;  // correctly rounded fp32 division
+    const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    return (float)((double)a * r / 127.0);
+}
+
 // ----------------------------------------------------------------- launchers
 
 hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *workspace,
@@ -125,6 +183,9 @@ hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t
                              hipStream_t stream);
 hipError_t launch_quantize_acts(const bl_act_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_decode(const bl_forward_problem *p, int count, hipStream_t stream);
+// Fused decode form: every problem has M <= BL_LINEAR_FUSED_MAX_M and M * K within
+// BL_LINEAR_FUSED_MAX_BYTES.
+hipError_t launch_linear_decode(const bl_linear_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_problem *p, int count, hipStream_t stream);
 
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.

@@ -28,8 +28,8 @@ namespace bl {
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kSuperWords = 16;    // words per row per super-step
-constexpr int kDecXldsMaxM = 4;    // activations staged in LDS for at most this many tokens
-constexpr int kDecXldsBytes = 48 * 1024;   // ... and at most this many activation bytes
+constexpr int kDecXldsMaxM = BL_LINEAR_FUSED_MAX_M;       // activations staged in LDS for at
+constexpr int kDecXldsBytes = BL_LINEAR_FUSED_MAX_BYTES;  // most this many tokens and bytes
 
 struct FwdDev {
     const int8_t *Xq;
@@ -40,6 +40,13 @@ struct FwdDev {
     int32_t *acc;
     int M, N, K;
     int block_begin;
+    // Fused decode form only: raw activations, norm, and optional copies of codes / scales.
+    const void *X;
+    const float *g;
+    int8_t *Xq_out;
+    float *sx_out;
+    float eps;
+    int bf16;
 };
 
 struct FwdBatch {
@@ -47,11 +54,31 @@ struct FwdBatch {
     int count;
 };
 
+// Four activations (fp32 or bf16) of row resource `xr`, elements 4j .. 4j+3, as fp32.
+__device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
+{
+    if (bf16) {
+        const uint32_t lo = buf_load4(xr, (uint32_t)j * 8u), hi = buf_load4(xr, (uint32_t)j * 8u + 4u);
+        return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
+                           __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u));
+    }
+    const v4u v = buf_load16(xr, (uint32_t)j * 16u);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
 // FULL_K: every problem of the launch has K % 256 == 0, so super-steps never run past a
 // row and rows are 64-byte aligned (one 16-byte load per lane, no tail masking).
-template <int RG, bool XLDS, bool FULL_K>
+// QUANT (with XLDS, RG = 1): the fused decode form.  The activations arrive unquantized;
+// each wave reduces absmax (and the sum of squares for the norm) over its K piece of every
+// token row, the four waves combine them through LDS in a fixed order, and each wave then
+// quantizes its piece straight into the LDS operand buffer (the same quant4 / act_scale
+// arithmetic as the activation-quantization kernels).  The first block of a problem also
+// writes the codes and scales out when asked to.
+template <int RG, bool XLDS, bool QUANT, bool FULL_K>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
+    static_assert(!QUANT || (XLDS && RG == 1), "the fused form stages codes in LDS");
     constexpr int ROWS = 16 * RG;
     // Super-steps per chunk (two chunks of loads in flight).  Four per chunk measured slower:
     // the dead loads past a short wave's range cost more than the deeper queue gains.
@@ -148,11 +175,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 
     // Epilogue inputs first (gamma, the row scales of this lane's tokens m = 4g + v): the
     // epilogue then does not wait on a memory round trip of its own.
-    const rsrc_t sres = make_rsrc(p.sx, (uint32_t)p.M * 4u);
+    const rsrc_t sres = make_rsrc(p.sx, QUANT ? 0u : (uint32_t)p.M * 4u);   // past M: 0
     float sxv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-        sxv[v] = __uint_as_float(buf_load4(sres, (uint32_t)(4 * g + v) * 4u));   // past M: 0
+        sxv[v] = QUANT ? 0.0f : __uint_as_float(buf_load4(sres, (uint32_t)(4 * g + v) * 4u));
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
     __builtin_amdgcn_sched_barrier(0);
 
@@ -167,7 +194,91 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     __builtin_amdgcn_sched_barrier(0);
     load(c1, t_begin + kDecPF);
     __builtin_amdgcn_sched_barrier(0);
-    if (XLDS) {
+    __shared__ float q_amax[kDecWaves][kDecXldsMaxM];
+    __shared__ double q_ss[kDecWaves][kDecXldsMaxM];
+    if (QUANT) {
+        const int e0 = t_begin * kSuperWords * 16;                 // first element of the piece
+        const int e1 = min(t_end * kSuperWords, words) * 16;
+        const int quads = (e1 - e0) / 4;
+        const bool norm = p.g != nullptr;
+        const bool bf16 = p.bf16 != 0;
+        const int esize = bf16 ? 2 : 4;
+        const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+        auto row = [&](int m) {
+            return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
+                             (uint32_t)p.K * esize);
+        };
+        auto quad_g = [&](int j) {
+            const v4u v = buf_load16(gr, (uint32_t)j * 16u);
+            return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                               __uint_as_float(v.w));
+        };
+        // Partial absmax of u (u = x, or fl32(x * g)) and sum of x^2 over this wave's piece.
+#pragma unroll
+        for (int m = 0; m < kDecXldsMaxM; ++m) {
+            if (m < p.M) {
+                const rsrc_t xr = row(m);
+                float amax = 0.0f;
+                double ss = 0.0;
+                for (int q = lane; q < quads; q += kWave) {
+                    const int j = e0 / 4 + q;
+                    const float4 f = load_quad(xr, j, bf16);
+                    const float4 u = norm ? mul4(f, quad_g(j)) : f;
+                    amax = fmaxf(amax, absmax4(u));
+                    if (norm)
+                        ss = sumsq4(ss, f);
+                }
+                amax = wave_max(amax);
+                ss = wave_sum_fixed(ss);
+                if (lane == 0) {
+                    q_amax[wave][m] = amax;
+                    q_ss[wave][m] = ss;
+                }
+            }
+        }
+        __syncthreads();
+        const bool first = (int)blockIdx.x == p.block_begin;
+#pragma unroll
+        for (int m = 0; m < kDecXldsMaxM; ++m) {
+            if (m < p.M) {
+                float a = q_amax[0][m];
+#pragma unroll
+                for (int w = 1; w < kDecWaves; ++w)
+                    a = fmaxf(a, q_amax[w][m]);
+                const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
+                const rsrc_t xr = row(m);
+                for (int q = lane; q < quads; q += kWave) {
+                    const int j = e0 / 4 + q;
+                    const float4 f = load_quad(xr, j, bf16);
+                    const char4 c = quant4(norm ? mul4(f, quad_g(j)) : f, inv);
+                    *reinterpret_cast<char4 *>(xs + (uint32_t)m * p.K + 4u * j) = c;
+                    if (first && p.Xq_out)
+                        *reinterpret_cast<char4 *>(p.Xq_out + (int64_t)m * p.K + 4 * j) = c;
+                }
+            }
+        }
+        // Scales of this lane's epilogue tokens m = 4g + v (and the optional copy).
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * g + v;
+            if (m < p.M) {
+                float a = q_amax[0][m];
+                double ss = q_ss[0][m];
+#pragma unroll
+                for (int w = 1; w < kDecWaves; ++w) {
+                    a = fmaxf(a, q_amax[w][m]);
+                    ss += q_ss[w][m];
+                }
+                sxv[v] = act_scale(a, ss, p.K, p.eps, norm);
+                if (first && p.sx_out && wave == 0 && r == 0)
+                    p.sx_out[m] = sxv[v];
+            }
+        }
+        if (lane == 0)
+            *reinterpret_cast<v4u *>(xs + zero_off) = v4u{0, 0, 0, 0};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if (XLDS) {
         // Copy this wave's piece, rows 0 .. M-1, k in [16 * kw0, 16 * kw1), 16 bytes per lane.
         const int kw0 = t_begin * kSuperWords;
         const int kw1 = min(t_end * kSuperWords, words);
@@ -225,6 +336,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     }
 }
 
+template <int RG, bool XLDS, bool QUANT = false>
+static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t stream)
+{
+    if (blocks == 0)
+        return hipSuccess;
+    size_t lds = 0;
+    if (XLDS)
+        for (int i = 0; i < b.count; ++i)
+            lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
+    if (full_k)
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true>), dim3(blocks), dim3(kDecThreads),
+                           lds, stream, b);
+    else
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, false>), dim3(blocks), dim3(kDecThreads),
+                           lds, stream, b);
+    return hipGetLastError();
+}
+
 template <int RG, bool XLDS>
 static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t stream)
 {
@@ -255,17 +384,7 @@ static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t 
         blocks += (d.N + 16 * RG - 1) / (16 * RG);
     }
     b.count = n;
-    if (blocks == 0)
-        return hipSuccess;
-    size_t lds = 0;
-    if (XLDS)
-        for (int i = 0; i < n; ++i)
-            lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
-    if (full_k)
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, true>), dim3(blocks), dim3(kDecThreads), lds, stream, b);
-    else
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, false>), dim3(blocks), dim3(kDecThreads), lds, stream, b);
-    return hipGetLastError();
+    return launch_batch<RG, XLDS>(b, blocks, full_k, stream);
 }
 
 // Row groups per block: as many as still leave at least one block per compute unit
@@ -286,6 +405,42 @@ hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStre
     if (rows >= 256 * 32)
         return launch_rg<2, false>(q, count, stream);
     return launch_rg<1, false>(q, count, stream);
+}
+
+// The fused decode form: every problem has M <= 4 and M * K <= the LDS budget (checked by
+// the caller).  Longest K first, one launch.
+hipError_t launch_linear_decode(const bl_linear_problem *q, int count, hipStream_t stream)
+{
+    int order[BL_MAX_GROUP];
+    int m = 0;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0 && q[i].N > 0)
+            order[m++] = i;
+    std::stable_sort(order, order + m, [&](int a, int c) { return q[a].K > q[c].K; });
+    FwdBatch b{};
+    int blocks = 0;
+    bool full_k = true;
+    for (int o = 0; o < m; ++o) {
+        const bl_linear_problem &s = q[order[o]];
+        full_k = full_k && (s.K % 256 == 0);
+        FwdDev &d = b.p[o];
+        d.W = s.W_packed;
+        d.gamma = s.gamma;
+        d.Y = s.Y;
+        d.M = (int)s.M;
+        d.N = (int)s.N;
+        d.K = (int)s.K;
+        d.block_begin = blocks;
+        d.X = s.X;
+        d.g = s.norm_weight;
+        d.Xq_out = s.X_q;
+        d.sx_out = s.x_scale;
+        d.eps = s.eps;
+        d.bf16 = s.x_dtype == BL_BF16;
+        blocks += (d.N + 15) / 16;
+    }
+    b.count = m;
+    return launch_batch<1, true, true>(b, blocks, full_k, stream);
 }
 
 }  // namespace bl

@@ -297,47 +297,6 @@ struct ActBatch {
     int count;
 };
 
-// q = clamp(rint(u * inv), -127, 127) as an integer.  rint of the fp32 product (round half
-// to even), then an exact integer clamp; the conversion maps NaN to 0 and saturates
-// infinities, so the degenerate rows (127/a overflowing to inf, 0 * inf = NaN) give the
-// same codes as clamping in floating point and sending NaN to 0.
-__device__ __forceinline__ int quant_one(float u, float inv)
-{
-    const int i = (int)__builtin_rintf(u * inv);
-    return min(max(i, -127), 127);
-}
-
-__device__ __forceinline__ char4 quant4(float4 u, float inv)
-{
-    const uint32_t b0 = (uint32_t)quant_one(u.x, inv) & 0xFFu;
-    const uint32_t b1 = (uint32_t)quant_one(u.y, inv) & 0xFFu;
-    const uint32_t b2 = (uint32_t)quant_one(u.z, inv) & 0xFFu;
-    const uint32_t b3 = (uint32_t)quant_one(u.w, inv) & 0xFFu;
-    const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-    char4 c;
-    __builtin_memcpy(&c, &w, 4);
-    return c;
-}
-
-__device__ __forceinline__ float4 mul4(float4 a, float4 b)
-{
-    return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
-}
-
-__device__ __forceinline__ float absmax4(float4 u)
-{
-    return fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w)));
-}
-
-__device__ __forceinline__ double sumsq4(double s, float4 x)
-{
-    s += (double)x.x * (double)x.x;
-    s += (double)x.y * (double)x.y;
-    s += (double)x.z * (double)x.z;
-    s += (double)x.w * (double)x.w;
-    return s;
-}
-
 // Raw storage of one chunk of 4 activations: fp32 -> 16 bytes, bf16 -> 8 bytes (kept packed
 // in registers and widened exactly when used).
 template <bool BF16>
@@ -383,14 +342,7 @@ __device__ __forceinline__ float4 load_g(rsrc_t g, int j)
 
 __device__ __forceinline__ void write_scale(const ActDev &p, int m, float a, double ss, bool norm)
 {
-    if (a == 0.0f) {
-        p.sx[m] = 0.0f;
-    } else if (!norm) {
-        p.sx[m] = a / 127.0f;  // correctly rounded fp32 division
-    } else {
-        const double r = 1.0 / sqrt(ss / (double)p.K + (double)p.eps);
-        p.sx[m] = (float)((double)a * r / 127.0);
-    }
+    p.sx[m] = act_scale(a, ss, p.K, p.eps, norm);
 }
 
 template <typename T>

@@ -201,6 +201,49 @@ typedef struct {
 bl_status bitlinear_forward_grouped(const bl_forward_problem *problems, int count,
                                     void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Steps 3 + 4 + 5 for a few tokens in one launch: the decode form of the layer call.
+ *
+ * Same arithmetic as bitlinear_quantize_acts followed by bitlinear_forward (BitDistill
+ * article: INT8 activations into ternary-weight projections, SubLN before the output
+ * projections), for the decode case where the activations are a handful of tokens and two
+ * launches would cost more than the work: each block of the product quantizes the token rows
+ * itself (absmax and, with a norm, the sum of squares over the whole row) and feeds the codes
+ * to the product without a trip through global memory.
+ *
+ *   X, x_dtype, norm_weight, eps   as for bitlinear_quantize_acts ([M][K] activations).
+ *   W_packed, gamma, Y             as for bitlinear_forward.
+ *   X_q, x_scale                   optional outputs ([M][K] int8, [M] fp32), or NULL: the
+ *                                  codes and scales the product used, identical to what
+ *                                  bitlinear_quantize_acts returns for the same input.
+ * The codes equal bitlinear_quantize_acts' bit for bit; x_scale and Y equal the two-call
+ * result except that, with a norm, the sum of squares is added in another fixed order (the
+ * scale may differ in its last bit).
+ * Fused when M <= 4 and M * K <= 49152; other problems take the two-step path and then need
+ * X_q and x_scale as the intermediate buffers (BL_ERR_NULL otherwise).  M == 0 or N == 0 is
+ * a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN, BL_ERR_DTYPE.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    const void *X;
+    const float *norm_weight;
+    const uint32_t *W_packed;
+    const float *gamma;
+    float *Y;
+    int8_t *X_q;
+    float *x_scale;
+    int64_t M, N, K;
+    int x_dtype;
+    float eps;
+} bl_linear_problem;
+
+/* Largest token count and activation bytes (M * K) of the fused decode form. */
+#define BL_LINEAR_FUSED_MAX_M 4
+#define BL_LINEAR_FUSED_MAX_BYTES 49152
+
+/* Up to BL_MAX_GROUP independent layer calls; all fused ones share one launch. */
+bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,6 +142,41 @@ def test_forward_validation(L):
     assert f(A, B, C, D, 3, 0, 64, E, None, None) == BL_OK
 
 
+def test_linear_grouped_validation(L, bl):
+    g = L.bitlinear_linear_grouped
+
+    def call(**kw):
+        d = dict(X=A, norm_weight=None, W_packed=B, gamma=C, Y=D, X_q=None, x_scale=None,
+                 M=1, N=4, K=64, x_dtype=0, eps=1e-6)
+        d.update(kw)
+        arr = (bl._LinearProblem * 1)()
+        arr[0] = bl._LinearProblem(**d)
+        return g(ctypes.addressof(arr), 1, None)
+
+    arr = (bl._LinearProblem * 1)()
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert g(ctypes.addressof(arr), 0, None) == BL_ERR_COUNT
+    assert g(ctypes.addressof(arr), 17, None) == BL_ERR_COUNT
+    assert call(X=None) == BL_ERR_NULL
+    assert call(W_packed=None) == BL_ERR_NULL
+    assert call(gamma=None) == BL_ERR_NULL
+    assert call(Y=None) == BL_ERR_NULL
+    assert call(x_dtype=2) == BL_ERR_DTYPE
+    assert call(K=40) == BL_ERR_SHAPE
+    assert call(M=-1) == BL_ERR_SHAPE
+    assert call(X=A + 4) == BL_ERR_ALIGN
+    assert call(norm_weight=E + 8) == BL_ERR_ALIGN
+    assert call(X_q=E + 1) == BL_ERR_ALIGN
+    # Beyond the fused form (M > 4, or M * K above its byte limit) the intermediate codes
+    # and scales are required.
+    assert call(M=5) == BL_ERR_NULL
+    assert call(M=2, K=32768) == BL_ERR_NULL
+    assert call(M=5, X_q=E) == BL_ERR_NULL
+    # Empty problems are accepted and launch nothing.
+    assert call(M=0) == BL_OK
+    assert call(N=0) == BL_OK
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):

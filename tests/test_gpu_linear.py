@@ -1,0 +1,166 @@
+"""The layer call (bitlinear_linear_grouped): steps 3 to 5 in one launch for decode-sized
+token counts, against the CPU oracle and against the two-call GPU path.
+
+Per call: codes and scales the product used (optional outputs) bit-exact / within 1e-6 of
+the oracle's activation quantization, Y within 1e-6 of the oracle epilogue over the oracle's
+exact integer product (zero exactly where the oracle gives zero), and Y equal to the two-call
+path (bit for bit without the norm; with the norm the sum of squares is added in another
+fixed order, so within 1e-6).
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-6
+GAMMA = np.float32(0.021)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def bl(torch):
+    import bit_gemm_02_amd as m
+    m.lib()
+    return m
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300))) if a.size else 0.0
+
+
+def make_call(torch, bl, M, N, K, dtype, norm, key, zero_row=False):
+    """Inputs on both sides: host copies for the oracle, device tensors for the library."""
+    X = workloads.gaussian((M, K), (200, M, N, K) + key, 1.0)
+    if zero_row and M > 1:
+        X[1] = 0.0
+    g = (np.float32(1) + workloads.gaussian((K,), (201, K) + key, 0.1)) if norm else None
+    C = workloads.ternary((N, K), (202, N, K) + key)
+    P = bl.pack_codes(dev(torch, C))
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(X)
+        Xt = dev(torch, bits.view(np.int16)).view(torch.bfloat16)
+        xin = bits
+    else:
+        Xt = dev(torch, X)
+        xin = X
+    call = dict(X=Xt, W_packed=P, gamma=dev(torch, np.array([GAMMA], np.float32)),
+                Y=torch.empty((M, N), dtype=torch.float32, device="cuda"),
+                X_q=torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                x_scale=torch.empty(M, dtype=torch.float32, device="cuda"),
+                norm_weight=None if g is None else dev(torch, g), eps=1e-6)
+    ref = dict(x=xin, g=g, C=C, bf16=dtype == "bf16")
+    return call, ref
+
+
+def check_call(torch, bl, orc, call, ref, label):
+    q_ref, s_ref = orc.quantize_acts(ref["x"], ref["g"], 1e-6, bf16=ref["bf16"])
+    q, s, Y = host(call["X_q"]), host(call["x_scale"]), host(call["Y"])
+    assert np.array_equal(q, q_ref), label
+    nz = s_ref != 0
+    assert np.array_equal(s == 0, ~nz), label
+    assert rel_err(s[nz], s_ref[nz]) <= REL, label
+    if ref["g"] is None:
+        assert np.array_equal(s, s_ref), label
+    Y_ref = orc.epilogue(orc.matmul(q_ref, ref["C"]), s_ref, GAMMA)
+    assert np.array_equal(Y == 0, Y_ref == 0), label
+    assert rel_err(Y[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL, label
+    # The two-call path on the same input.
+    q2, s2 = bl.quantize_acts(call["X"], call["norm_weight"], 1e-6)
+    Y2 = bl.forward(q2, s2, call["W_packed"], call["gamma"])
+    torch.cuda.synchronize()
+    assert torch.equal(call["X_q"], q2), label
+    if ref["g"] is None:
+        assert torch.equal(call["Y"], Y2), label
+    else:
+        assert rel_err(Y[Y_ref != 0], host(Y2)[Y_ref != 0]) <= 2 * REL, label
+
+
+LINEAR_SHAPES = [
+    (1, 1, 16), (1, 37, 48), (1, 768, 768), (2, 300, 272), (3, 2048, 768), (4, 129, 2048),
+    (1, 96, 9728), (4, 40, 12288), (2, 5000, 1040),
+]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("norm", [False, True])
+def test_linear_fused(torch, bl, orc, M, N, K, dtype, norm):
+    assert bl.linear_fused(M, K)
+    call, ref = make_call(torch, bl, M, N, K, dtype, norm, (0,), zero_row=True)
+    bl.linear_grouped([call])
+    torch.cuda.synchronize()
+    check_call(torch, bl, orc, call, ref, (M, N, K, dtype, norm))
+
+
+def test_linear_grouped_mixed(torch, bl, orc):
+    """Fused calls of several K in one launch, next to calls that take the two-step path."""
+    specs = [(1, 768, 768, "f32", False), (1, 256, 2048, "f32", True), (4, 100, 16384, "f32", False),
+             (2, 64, 80, "bf16", True), (8, 300, 768, "f32", False), (1, 50, 65536, "f32", False),
+             (33, 128, 1024, "bf16", True)]
+    calls, refs = [], []
+    for i, (M, N, K, dt, nm) in enumerate(specs):
+        c, r = make_call(torch, bl, M, N, K, dt, nm, (1, i))
+        calls.append(c)
+        refs.append(r)
+    assert [bl.linear_fused(c["X"].shape[0], c["X"].shape[1]) for c in calls] == \
+        [True, True, False, True, False, False, False]
+    bl.linear_grouped(calls)
+    torch.cuda.synchronize()
+    for i, (c, r) in enumerate(zip(calls, refs)):
+        check_call(torch, bl, orc, c, r, specs[i])
+
+
+def test_linear_optional_outputs_and_convenience(torch, bl, orc):
+    """Without the X_q / x_scale outputs the fused call gives the same Y; bl.linear agrees."""
+    call, ref = make_call(torch, bl, 3, 700, 1536, "f32", True, (2,))
+    bl.linear_grouped([call])
+    Y_full = call["Y"].clone()
+    call2 = dict(call, X_q=None, x_scale=None, Y=torch.empty_like(Y_full))
+    bl.linear_grouped([call2])
+    Y3 = bl.linear(call["X"], call["W_packed"], call["gamma"], call["norm_weight"], 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(call2["Y"], Y_full)
+    assert torch.equal(Y3, Y_full)
+    check_call(torch, bl, orc, call, ref, "outputs")
+    # Beyond the fused size the convenience call takes the two-step path.
+    X = dev(torch, workloads.gaussian((9, 256), (203,), 1.0))
+    Y9 = bl.linear(X, call["W_packed"][:, :16].contiguous(), call["gamma"])
+    q9, s9 = bl.quantize_acts(X)
+    assert torch.equal(Y9, bl.forward(q9, s9, call["W_packed"][:, :16].contiguous(), call["gamma"]))
+
+
+def test_linear_degenerate(torch, bl):
+    """All-zero activations give zero codes, zero scales and Y == 0; empty calls are no-ops."""
+    C = workloads.ternary((64, 512), (204,))
+    P = bl.pack_codes(dev(torch, C))
+    gamma = dev(torch, np.array([GAMMA], np.float32))
+    X = torch.zeros((2, 512), dtype=torch.float32, device="cuda")
+    Y = torch.full((2, 64), 7.0, device="cuda")
+    Xq = torch.full((2, 512), 5, dtype=torch.int8, device="cuda")
+    sx = torch.full((2,), 3.0, device="cuda")
+    bl.linear_grouped([dict(X=X, W_packed=P, gamma=gamma, Y=Y, X_q=Xq, x_scale=sx)])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Y) == 0 and torch.count_nonzero(Xq) == 0 and torch.count_nonzero(sx) == 0
+    empty = torch.empty((0, 512), dtype=torch.float32, device="cuda")
+    bl.linear_grouped([dict(X=empty, W_packed=P, gamma=gamma, Y=torch.empty((0, 64), device="cuda"))])
+    torch.cuda.synchronize()
