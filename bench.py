@@ -583,7 +583,9 @@ def main():
         "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in rooflines.items()},
         "timing": {"ms_per_step_wall": round(wall_ms, 4),
-                   "ms_per_step_with_launch_events": round(ms_with_events, 4)},
+                   "ms_per_step_with_launch_events": round(ms_with_events, 4),
+                   "schedule": "one stream, launches in step order (three streams, weight quant "
+                               "beside act quant and decode beside prefill, measured slower)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)

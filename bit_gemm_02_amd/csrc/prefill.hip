@@ -299,23 +299,21 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[mi], bop[ni],
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[ni], aop[mi],
                                                                        acc[mi][ni], 0, 0, 0);
         }
     };
 
     // Row scales and gamma, loaded before the pipeline starts: older than every stage load,
     // they have landed by the first stage wait, and the epilogue does not wait on memory.
-    float sxv[MI][4];
+    float sxv[MI];
     {
         const rsrc_t sres = make_rsrc(p.sx, (uint32_t)p.M * 4u);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + wm * T::TM + mi * 16 + 4 * g + v;   // rows past M read 0
-                sxv[mi][v] = __uint_as_float(buf_load4(sres, (uint32_t)m * 4u));
-            }
+        for (int mi = 0; mi < MI; ++mi) {
+            const int m = m0 + wm * T::TM + mi * 16 + r;   // rows past M read 0
+            sxv[mi] = __uint_as_float(buf_load4(sres, (uint32_t)m * 4u));
+        }
     }
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
 
@@ -335,28 +333,45 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
         });
     }
 
-    // Epilogue: acc[mi][ni] register v holds 64 * D[m][n] for
-    // m = m0 + wm * TM + mi * 16 + 4 * g + v and n = n0 + wn * TN + ni * 16 + r.
+    // Epilogue.  The MFMA takes the weights as its row operand, so acc[mi][ni] register v
+    // holds 64 * D[m][n] for m = m0 + wm * TM + mi * 16 + r and n = n0 + wn * TN + ni * 16 +
+    // 4 * g + v: each lane owns four consecutive outputs of one row and writes them with one
+    // 16-byte store (scalar stores when the row pitch or the base is not 16-byte aligned, and
+    // in a ragged last column group).
     const double gamma = (double)gammaf;
+    const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0 &&
+                     (!p.acc || ((uintptr_t)p.acc & 15) == 0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+        const int m = m0 + wm * T::TM + mi * 16 + r;
+        if (m >= p.M)
+            continue;
+        const double scale = gamma * (double)sxv[mi];
+        float *yrow = p.Y + (int64_t)m * p.N;
+        int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int m = m0 + wm * T::TM + mi * 16 + 4 * g + v;
-            if (m >= p.M)
-                continue;
-            const double scale = gamma * (double)sxv[mi][v];
-            float *yrow = p.Y + (int64_t)m * p.N;
-            int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
+        for (int ni = 0; ni < NI; ++ni) {
+            const int n = n0 + wn * T::TN + ni * 16 + 4 * g;
+            int a[4];
+            float y[4];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const int n = n0 + wn * T::TN + ni * 16 + r;
-                if (n >= p.N)
-                    continue;
-                const int a = acc[mi][ni][v] >> 6;
-                yrow[n] = (float)((double)a * scale);
+            for (int v = 0; v < 4; ++v) {
+                a[v] = acc[mi][ni][v] >> 6;
+                y[v] = (float)((double)a[v] * scale);
+            }
+            if (vec && n + 3 < p.N) {
+                *reinterpret_cast<float4 *>(yrow + n) = make_float4(y[0], y[1], y[2], y[3]);
                 if (arow_out)
-                    arow_out[n] = a;
+                    *reinterpret_cast<int4 *>(arow_out + n) = make_int4(a[0], a[1], a[2], a[3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (n + v < p.N) {
+                        yrow[n + v] = y[v];
+                        if (arow_out)
+                            arow_out[n + v] = a[v];
+                    }
+                }
             }
         }
     }
