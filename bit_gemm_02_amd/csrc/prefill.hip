@@ -268,6 +268,35 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     const int brow = T::XBYTES + (wn * T::TN + r) * WROW +
                      16 * (bch ^ wswz<WCH>(wn * T::TN + r)) + bin;           // + ni * 16 * WROW
 
+    // The last k-step of each stage is deferred to the next stage: its operands (activation
+    // fragments and raw packed words) stay in registers, and its MFMAs are issued right after
+    // the next stage's barrier and LDS reads, so the matrix pipe has work while those reads
+    // are in flight instead of idling after every barrier.  (Zero operands before the first
+    // stage add nothing.)
+    v4i da[MI];
+    uint32_t dw[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+        da[mi] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+        dw[ni] = 0;
+    auto mfma_step = [&](const uint32_t (&w)[NI], const v4i (&a)[MI]) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            const v4i b = unpack_word64(w[ni]);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a[mi], acc[mi][ni], 0, 0, 0);
+        }
+    };
+    auto read_a = [&](const unsigned char *st, int j, v4i (&a)[MI]) {
+        const int pos = 16 * ((g * LPW + j) ^ aswz);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            a[mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * KS + pos);
+    };
+
     auto compute = [&](auto S) {
         const unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
         uint32_t wq[NI][LPW];
@@ -284,24 +313,28 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
                 wq[ni][0] = *reinterpret_cast<const uint32_t *>(src);
             }
         }
+        v4i a0[MI];
+        read_a(st, 0, a0);
+        mfma_step(dw, da);          // previous stage's last k-step
+        static_assert(LPW >= 2, "one k-step per stage is deferred");
 #pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            v4i bop[NI];
+        for (int j = 0; j < LPW - 1; ++j) {
+            uint32_t w[NI];
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
-                bop[ni] = unpack_word64(wq[ni][j]);
-            const int pos = 16 * ((g * LPW + j) ^ aswz);
-            v4i aop[MI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                aop[mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * KS + pos);
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[ni], aop[mi],
-                                                                       acc[mi][ni], 0, 0, 0);
+                w[ni] = wq[ni][j];
+            if (j == 0) {
+                mfma_step(w, a0);
+            } else {
+                v4i a[MI];
+                read_a(st, j, a);
+                mfma_step(w, a);
+            }
         }
+        read_a(st, LPW - 1, da);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+            dw[ni] = wq[ni][LPW - 1];
     };
 
     // Row scales and gamma, loaded before the pipeline starts: older than every stage load,
@@ -332,6 +365,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             }
         });
     }
+    mfma_step(dw, da);              // the last stage's deferred k-step
 
     // Epilogue.  The MFMA takes the weights as its row operand, so acc[mi][ni] register v
     // holds 64 * D[m][n] for m = m0 + wm * TM + mi * 16 + r and n = n0 + wn * TN + ni * 16 +
