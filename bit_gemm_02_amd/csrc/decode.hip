@@ -69,7 +69,7 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
 
 // FULL_K: every problem of the launch has K % 256 == 0, so super-steps never run past a
 // row and rows are 64-byte aligned (one 16-byte load per lane, no tail masking).
-// QUANT (with XLDS, RG = 1): the fused decode form.  The activations arrive unquantized;
+// QUANT (with XLDS): the fused decode form.  The activations arrive unquantized;
 // each wave reduces absmax (and the sum of squares for the norm) over its K piece of every
 // token row, the four waves combine them through LDS in a fixed order, and each wave then
 // quantizes its piece straight into the LDS operand buffer (the same quant4 / act_scale
@@ -78,7 +78,7 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
 template <int RG, bool XLDS, bool QUANT, bool FULL_K>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
-    static_assert(!QUANT || (XLDS && RG == 1), "the fused form stages codes in LDS");
+    static_assert(!QUANT || XLDS, "the fused form stages codes in LDS");
     constexpr int ROWS = 16 * RG;
     // Super-steps per chunk (two chunks of loads in flight).  Four per chunk measured slower:
     // the dead loads past a short wave's range cost more than the deeper queue gains.
@@ -408,8 +408,11 @@ hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStre
 }
 
 // The fused decode form: every problem has M <= 4 and M * K <= the LDS budget (checked by
-// the caller).  Longest K first, one launch.
-hipError_t launch_linear_decode(const bl_linear_problem *q, int count, hipStream_t stream)
+// the caller).  Longest K first, one launch.  Every block quantizes the token rows it needs
+// from the raw activations, so larger blocks (more row groups) read them fewer times: row
+// groups as in the unfused decode launch.
+template <int RG>
+static hipError_t launch_linear_rg(const bl_linear_problem *q, int count, hipStream_t stream)
 {
     int order[BL_MAX_GROUP];
     int m = 0;
@@ -437,10 +440,23 @@ hipError_t launch_linear_decode(const bl_linear_problem *q, int count, hipStream
         d.sx_out = s.x_scale;
         d.eps = s.eps;
         d.bf16 = s.x_dtype == BL_BF16;
-        blocks += (d.N + 15) / 16;
+        blocks += (d.N + 16 * RG - 1) / (16 * RG);
     }
     b.count = m;
-    return launch_batch<1, true, true>(b, blocks, full_k, stream);
+    return launch_batch<RG, true, true>(b, blocks, full_k, stream);
+}
+
+hipError_t launch_linear_decode(const bl_linear_problem *q, int count, hipStream_t stream)
+{
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i)
+        if (q[i].M > 0)
+            rows += q[i].N;
+    if (rows >= 256 * 64)
+        return launch_linear_rg<4>(q, count, stream);
+    if (rows >= 256 * 32)
+        return launch_linear_rg<2>(q, count, stream);
+    return launch_linear_rg<1>(q, count, stream);
 }
 
 }  // namespace bl

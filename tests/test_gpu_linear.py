@@ -98,6 +98,8 @@ def check_call(torch, bl, orc, call, ref, label):
 LINEAR_SHAPES = [
     (1, 1, 16), (1, 37, 48), (1, 768, 768), (2, 300, 272), (3, 2048, 768), (4, 129, 2048),
     (1, 96, 9728), (4, 40, 12288), (2, 5000, 1040),
+    # Large layers: blocks of two and four 16-row groups.
+    (1, 16400, 768), (3, 9000, 272),
 ]
 
 
