@@ -274,18 +274,30 @@ class Setup:
         assert rc == 0, rc
 
 
-def isolated_ms(torch, setup: Setup, key: str, stream, reps: int) -> float:
-    """Average duration of one launch group run alone, back to back (events around the loop)."""
-    for i in range(3):
-        setup.launch_only(key, i, stream)
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(reps):
-        setup.launch_only(key, i, stream)
-    e.record()
+def isolated_ms(torch, setup: Setup, key: str, reps: int) -> float:
+    """Average duration of one launch group run alone, back to back.  The launches are
+    captured into a HIP graph and replayed, so the host's per-launch cost (several us, as
+    long as the shortest kernels here) stays out of the figure; events on the replay stream."""
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        for i in range(3):
+            setup.launch_only(key, i, s_.cuda_stream)
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / reps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s_):
+        for i in range(reps):
+            setup.launch_only(key, i, s_.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_):
+        graph.replay()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(s_)
+        for _ in range(3):
+            graph.replay()
+        e.record(s_)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (3 * reps)
 
 
 def interval_ms(ev, a, b):
@@ -485,7 +497,7 @@ def main():
 
     # Per-launch durations, two ways, both outside the timed region: (a) the same steps again
     # with events around every launch group (includes the dispatch gap each launch pays inside
-    # the step); (b) each launch group alone, back to back, events around the loop (what a
+    # the step); (b) each launch group alone, back to back from a replayed graph (what a
     # kernel trace reports as its duration; used for the roofline figures).
     ev = {}
     for i in range(args.steps):
@@ -500,7 +512,7 @@ def main():
     if not setup.wq_tables:
         in_step.pop("weight_quant")
     ms_with_events = interval_ms(ev, "t0", "t_dec")
-    ms = {k: isolated_ms(torch, setup, k, sptr, args.steps) for k in in_step}
+    ms = {k: isolated_ms(torch, setup, k, args.steps) for k in in_step}
 
     ops = setup.prefill_ops()
     pre_bytes = setup.prefill_bytes()
