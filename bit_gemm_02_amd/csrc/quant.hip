@@ -20,6 +20,8 @@
 // default), and rintf lowers to round-to-nearest-even.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace bl {
@@ -29,7 +31,6 @@ constexpr int kGammaThreads = 256;
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 8;      // float4 chunks per thread in quant_pack_kernel
 constexpr int kActThreads = 256;
-constexpr int kActCache = 16;       // 4-element chunks per thread kept in registers (block kernel)
 
 // ----------------------------------------------------------------------------- gamma
 
@@ -457,55 +458,88 @@ __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b,
     }
 }
 
-// One block per token row for rows longer than the largest wave class: the first kActCache
-// chunks per thread stay in registers, any remainder is read again (from L2).
+// One block per token row for rows longer than the largest wave class.  Thread t handles the
+// 16-byte groups j = t + 256 c of the row (four fp32 or eight bf16 activations each); the first
+// C groups per thread stay in registers between the reduction and the quantization, any
+// remainder is read again (from L2).  Groups past the row load zeros.  The norm weights are
+// read per group in both passes (L2 hits: every row of the problem shares them).
+template <int C, bool BF16>
 __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
 {
+    constexpr int EPG = BF16 ? 8 : 4;   // activations per 16-byte group
     __shared__ float lds_max[kActThreads / kWave];
     __shared__ double lds_sum[kActThreads / kWave];
     const ActDev &p = b.p[find_problem(b, (int)blockIdx.x)];
     const int m = blockIdx.x - p.row_begin;
-    const int chunks = p.K / 4;
+    const int groups = p.K / EPG;
     const bool norm = p.g != nullptr;
     const rsrc_t xr = row_rsrc(p, m);
     const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
-    auto load = [&](int j) {
-        if (p.bf16) {
-            Chunk<true> c;
-            c.load(xr, j);
-            return c.f();
+    const int tid = threadIdx.x;
+
+    auto widen = [&](const v4u &r, float4 &lo, float4 &hi) {
+        if (BF16) {
+            lo = make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                             __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+            hi = make_float4(__uint_as_float(r.z << 16), __uint_as_float(r.z & 0xFFFF0000u),
+                             __uint_as_float(r.w << 16), __uint_as_float(r.w & 0xFFFF0000u));
+        } else {
+            lo = make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                             __uint_as_float(r.w));
+            hi = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-        Chunk<false> c;
-        c.load(xr, j);
-        return c.f();
+    };
+    // u = x (or fl32(x * g)) for the group's activations; ss gets x^2 in element order.
+    auto absmax_group = [&](const v4u &r, int j, float &amax, double &ss) {
+        float4 lo, hi;
+        widen(r, lo, hi);
+        const uint32_t goff = j < groups ? (uint32_t)j * EPG * 4u : kOOB;
+        const float4 ulo = norm ? mul4(lo, load_g(gr, (int)(goff / 16u))) : lo;
+        amax = fmaxf(amax, absmax4(ulo));
+        if (norm)
+            ss = sumsq4(ss, lo);
+        if (BF16) {
+            const float4 uhi = norm ? mul4(hi, load_g(gr, (int)(goff / 16u) + 1)) : hi;
+            amax = fmaxf(amax, absmax4(uhi));
+            if (norm)
+                ss = sumsq4(ss, hi);
+        }
+    };
+    auto quant_group = [&](const v4u &r, int j, float inv) {
+        float4 lo, hi;
+        widen(r, lo, hi);
+        const int gj = j * EPG / 4;
+        const char4 q0 = quant4(norm ? mul4(lo, load_g(gr, gj)) : lo, inv);
+        if (BF16) {
+            const char4 q1 = quant4(norm ? mul4(hi, load_g(gr, gj + 1)) : hi, inv);
+            char4 *dst = reinterpret_cast<char4 *>(p.Xq + (int64_t)m * p.K + (int64_t)j * EPG);
+            dst[0] = q0;
+            dst[1] = q1;
+        } else {
+            reinterpret_cast<char4 *>(p.Xq + (int64_t)m * p.K)[j] = q0;
+        }
     };
 
-    float4 cache[kActCache];
+    v4u raw[C];
 #pragma unroll
-    for (int c = 0; c < kActCache; ++c)
-        cache[c] = load(c * kActThreads + threadIdx.x);
+    for (int c = 0; c < C; ++c) {
+        const int j = c * kActThreads + tid;
+        raw[c] = buf_load16(xr, j < groups ? (uint32_t)j * 16u : kOOB);
+    }
     float amax = 0.0f;
     double ss = 0.0;
 #pragma unroll
-    for (int c = 0; c < kActCache; ++c) {
-        const int j = c * kActThreads + threadIdx.x;
-        amax = fmaxf(amax, absmax4(norm ? mul4(cache[c], load_g(gr, j)) : cache[c]));
-        if (norm)
-            ss = sumsq4(ss, cache[c]);
-    }
-    for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        const float4 x = load(j);
-        amax = fmaxf(amax, absmax4(norm ? mul4(x, load_g(gr, j)) : x));
-        if (norm)
-            ss = sumsq4(ss, x);
-    }
+    for (int c = 0; c < C; ++c)
+        absmax_group(raw[c], c * kActThreads + tid, amax, ss);
+    for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
+        absmax_group(buf_load16(xr, (uint32_t)j * 16u), j, amax, ss);
 
     // Block max (exact, order-free) and fixed-order block sum of squares.
     amax = wave_max(amax);
     if (norm)
         ss = wave_sum_fixed(ss);
-    const int wave = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) {
+    const int wave = tid / kWave;
+    if ((tid & (kWave - 1)) == 0) {
         lds_max[wave] = amax;
         lds_sum[wave] = ss;
     }
@@ -518,21 +552,22 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
         sum = sum + lds_sum[w];
     }
 
-    char4 *q4 = reinterpret_cast<char4 *>(p.Xq) + (int64_t)m * chunks;
     const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded fp32 division
 #pragma unroll
-    for (int c = 0; c < kActCache; ++c) {
-        const int j = c * kActThreads + threadIdx.x;
-        if (j < chunks)
-            q4[j] = quant4(norm ? mul4(cache[c], load_g(gr, j)) : cache[c], inv);
+    for (int c = 0; c < C; ++c) {
+        const int j = c * kActThreads + tid;
+        if (j < groups)
+            quant_group(raw[c], j, inv);
     }
-    for (int j = kActCache * kActThreads + threadIdx.x; j < chunks; j += kActThreads) {
-        const float4 x = load(j);
-        q4[j] = quant4(norm ? mul4(x, load_g(gr, j)) : x, inv);
-    }
-    if (threadIdx.x == 0)
+    for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
+        quant_group(buf_load16(xr, (uint32_t)j * 16u), j, inv);
+    if (tid == 0)
         write_scale(p, m, a, sum, norm);
 }
+
+// Groups per thread kept in registers by the block kernel: the smallest class that holds
+// the longest row of the launch (longer rows re-read the rest).
+constexpr int kActBlockClasses[] = {4, 8, 16};
 
 // Row-length classes of the wave kernel (chunks of 4 per lane): K <= 256 * class.  Longer
 // rows go to the block kernel.
@@ -605,7 +640,26 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
             if (!rows)
                 continue;
             if (wide) {
-                hipLaunchKernelGGL(act_quant_block_kernel, dim3(rows), dim3(kActThreads), 0, stream, b);
+                int gpt = 0;   // 16-byte groups per thread of the longest row
+                for (int i = 0; i < b.count; ++i) {
+                    const int groups = b.p[i].K / (bf ? 8 : 4);
+                    gpt = std::max(gpt, (groups + kActThreads - 1) / kActThreads);
+                }
+                if (bf) {
+                    if (gpt <= kActBlockClasses[0])
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                    else if (gpt <= kActBlockClasses[1])
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                    else
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                } else {
+                    if (gpt <= kActBlockClasses[0])
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                    else if (gpt <= kActBlockClasses[1])
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                    else
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                }
             } else if (bf) {
                 if (cls == 0) launch_wave<4, true>(b, rows, stream);
                 else if (cls == 1) launch_wave<8, true>(b, rows, stream);
