@@ -298,32 +298,23 @@ struct ActBatch {
     int count;
 };
 
-// Raw storage of one chunk of 4 activations: fp32 -> 16 bytes, bf16 -> 8 bytes (kept packed
-// in registers and widened exactly when used).
+// Raw storage of one 16-byte group of activations (four fp32 or eight bf16 values, kept packed
+// in registers and widened exactly when used).  Group j covers activations EPG*j .. +EPG-1.
 template <bool BF16>
-struct Chunk;
-template <>
-struct Chunk<false> {
+struct Group {
+    static constexpr int EPG = BF16 ? 8 : 4;
     v4u v;
     __device__ __forceinline__ void load(rsrc_t r, int j) { v = buf_load16(r, (uint32_t)j * 16u); }
-    __device__ __forceinline__ float4 f() const
+    // The group's values as one (fp32) or two (bf16: lo then hi) float4.
+    __device__ __forceinline__ float4 f(int half) const
     {
+        if (BF16) {
+            const uint32_t a = half ? v.z : v.x, b = half ? v.w : v.y;
+            return make_float4(__uint_as_float(a << 16), __uint_as_float(a & 0xFFFF0000u),
+                               __uint_as_float(b << 16), __uint_as_float(b & 0xFFFF0000u));
+        }
         return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                            __uint_as_float(v.w));
-    }
-};
-template <>
-struct Chunk<true> {
-    uint32_t lo, hi;
-    __device__ __forceinline__ void load(rsrc_t r, int j)
-    {
-        lo = buf_load4(r, (uint32_t)j * 8u);
-        hi = buf_load4(r, (uint32_t)j * 8u + 4u);
-    }
-    __device__ __forceinline__ float4 f() const
-    {
-        return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xFFFF0000u),
-                           __uint_as_float(hi << 16), __uint_as_float(hi & 0xFFFF0000u));
     }
 };
 
@@ -362,9 +353,11 @@ __device__ __forceinline__ int find_problem(const T &b, int key)
 // row's activations stay in registers (raw), the row is read from HBM once, and all
 // reductions are wave-local (no LDS, no barriers).  A row past the end loads from an empty
 // buffer resource (zeros) so the two register sets alternate without copies or waits.
+// Lane l holds the 16-byte groups c * 64 + l (CACHE fp32 groups, or CACHE / 2 bf16 groups).
 template <int CACHE, bool BF16>
 struct RowBuf {
-    Chunk<BF16> x[CACHE];
+    static constexpr int NG = BF16 ? CACHE / 2 : CACHE;
+    Group<BF16> x[NG];
 };
 
 __device__ __forceinline__ rsrc_t act_row_rsrc(const ActBatch &b, int row, int rows, int &prob)
@@ -381,54 +374,69 @@ template <int CACHE, bool BF16>
 __device__ __forceinline__ void act_load(RowBuf<CACHE, BF16> &r, rsrc_t xr, int lane)
 {
 #pragma unroll
-    for (int c = 0; c < CACHE; ++c)
-        r.x[c].load(xr, c * kWave + lane);  // chunks past the row read as zero
+    for (int c = 0; c < RowBuf<CACHE, BF16>::NG; ++c)
+        r.x[c].load(xr, c * kWave + lane);  // groups past the row read as zero
 }
 
-// RMSNorm weights of a row's problem (zeros, unused, without a norm).  Issued before the
-// next row's prefetch: vector-memory loads complete in order, so waiting for them later does
-// not wait for the prefetch.
+// RMSNorm weights of a row's problem (zeros, unused, without a norm): the fp32 quads that
+// match the lane's groups.  Issued before the next row's prefetch: vector-memory loads
+// complete in order, so waiting for them later does not wait for the prefetch.
 template <int CACHE>
 struct NormBuf {
     float4 g[CACHE];
 };
 
-template <int CACHE>
+template <int CACHE, bool BF16>
 __device__ __forceinline__ void norm_load(NormBuf<CACHE> &n, const ActDev &p, int lane)
 {
     const rsrc_t gr = make_rsrc(p.g, p.g ? (uint32_t)p.K * 4u : 0u);
+    constexpr int H = BF16 ? 2 : 1;
 #pragma unroll
-    for (int c = 0; c < CACHE; ++c)
-        n.g[c] = load_g(gr, c * kWave + lane);
+    for (int c = 0; c < CACHE / H; ++c)
+#pragma unroll
+        for (int h = 0; h < H; ++h)
+            n.g[c * H + h] = load_g(gr, (c * kWave + lane) * H + h);
 }
 
 template <int CACHE, bool BF16>
 __device__ __forceinline__ void act_quant_row(const RowBuf<CACHE, BF16> &r, const NormBuf<CACHE> &n,
                                               const ActDev &p, int m, int lane)
 {
-    const int chunks = p.K / 4;
+    constexpr int NG = RowBuf<CACHE, BF16>::NG, H = BF16 ? 2 : 1;
+    const int groups = p.K / Group<BF16>::EPG;
     const bool norm = p.g != nullptr;
     float amax = 0.0f;
     double ss = 0.0;
     float4 u[CACHE];
 #pragma unroll
-    for (int c = 0; c < CACHE; ++c) {
-        const float4 f = r.x[c].f();
-        u[c] = norm ? mul4(f, n.g[c]) : f;
-        amax = fmaxf(amax, absmax4(u[c]));
-        if (norm)
-            ss = sumsq4(ss, f);  // chunks past the row are zero and add nothing
-    }
+    for (int c = 0; c < NG; ++c)
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            const float4 f = r.x[c].f(h);
+            u[c * H + h] = norm ? mul4(f, n.g[c * H + h]) : f;
+            amax = fmaxf(amax, absmax4(u[c * H + h]));
+            if (norm)
+                ss = sumsq4(ss, f);  // groups past the row are zero and add nothing
+        }
     const float a = wave_max(amax);
     if (norm)
         ss = wave_sum_fixed(ss);
-    char4 *q4 = reinterpret_cast<char4 *>(p.Xq) + (int64_t)m * chunks;
+    char4 *q4 = reinterpret_cast<char4 *>(p.Xq + (int64_t)m * p.K);
     const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded fp32 division
 #pragma unroll
-    for (int c = 0; c < CACHE; ++c) {
+    for (int c = 0; c < NG; ++c) {
         const int j = c * kWave + lane;
-        if (j < chunks)
-            q4[j] = quant4(u[c], inv);
+        if (j < groups) {
+            if (BF16) {
+                const char4 lo = quant4(u[2 * c], inv), hi = quant4(u[2 * c + 1], inv);
+                uint2 w;
+                __builtin_memcpy(&w.x, &lo, 4);
+                __builtin_memcpy(&w.y, &hi, 4);
+                reinterpret_cast<uint2 *>(q4)[j] = w;
+            } else {
+                q4[j] = quant4(u[c], inv);
+            }
+        }
     }
     if (lane == 0)
         write_scale(p, m, a, ss, norm);
@@ -448,10 +456,10 @@ __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b,
     int pa, pb;
     act_load(A, act_row_rsrc(b, w0, rows, pa), lane);
     for (int r = w0; r < rows; r += 2 * S) {
-        norm_load(G, b.p[pa], lane);
+        norm_load<CACHE, BF16>(G, b.p[pa], lane);
         act_load(B, act_row_rsrc(b, r + S, rows, pb), lane);
         act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
-        norm_load(G, b.p[pb], lane);
+        norm_load<CACHE, BF16>(G, b.p[pb], lane);
         act_load(A, act_row_rsrc(b, r + 2 * S, rows, pa), lane);
         if (r + S < rows)
             act_quant_row(B, G, b.p[pb], r + S - b.p[pb].row_begin, lane);
