@@ -68,6 +68,12 @@ class Oracle:
         lib.oracle_matmul.restype = ctypes.c_int
         lib.oracle_epilogue.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P]
         lib.oracle_epilogue.restype = None
+        lib.oracle_ffn_act1.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float]
+        lib.oracle_ffn_act1.restype = ctypes.c_float
+        lib.oracle_ffn_act.argtypes = [ctypes.c_int, _P, _P, _I64, _P]
+        lib.oracle_ffn_act.restype = None
+        lib.oracle_epilogue_residual.argtypes = [_P, _P, ctypes.c_float, _P, _I64, _I64, _P]
+        lib.oracle_epilogue_residual.restype = None
         lib.oracle_forward_entries.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _P, _P, _I64,
                                                _P, _P, _P]
         lib.oracle_forward_entries.restype = ctypes.c_int
@@ -185,6 +191,34 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle_forward_entries failed: {rc}")
         return acc, Y
+
+    # O7 (layer chain): FFN activation, kinds as in oracle.c
+    SWIGLU, RELU2_GLU, RELU2 = 1, 2, 3
+
+    def ffn_act(self, kind: int, X: np.ndarray, X2: Optional[np.ndarray] = None) -> np.ndarray:
+        X = _c(X, np.float32)
+        X2 = None if X2 is None else _c(X2, np.float32)
+        if X2 is not None:
+            assert X2.shape == X.shape
+        H = np.empty_like(X)
+        self._lib.oracle_ffn_act(int(kind), _ptr(X), _ptr(X2), X.size, _ptr(H))
+        return H
+
+    def ffn_act1(self, kind: int, x: float, x2: float = 0.0) -> np.float32:
+        return np.float32(self._lib.oracle_ffn_act1(int(kind), float(np.float32(x)),
+                                                    float(np.float32(x2))))
+
+    # O8 (layer chain): residual epilogue
+    def epilogue_residual(self, acc: np.ndarray, sx: np.ndarray, gamma, R: np.ndarray) -> np.ndarray:
+        acc = _c(acc, np.int32)
+        sx = _c(sx, np.float32)
+        R = _c(R, np.float32)
+        M, N = acc.shape
+        assert R.shape == (M, N)
+        Y = np.empty((M, N), dtype=np.float32)
+        self._lib.oracle_epilogue_residual(_ptr(acc), _ptr(sx), float(np.float32(gamma)), _ptr(R),
+                                           M, N, _ptr(Y))
+        return Y
 
 
 _default: Optional[Oracle] = None

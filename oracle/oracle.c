@@ -36,6 +36,17 @@
  *                  README "Features": Triton forward computes Y = X @ W_q^T x gamma).
  *   O6  epilogue — y[m][n] = fp32(acc * gamma * s_x[m]) evaluated in fp64.
  *
+ * Layer chain (the BitLinear sub-graph of one transformer layer, for the chain tests):
+ *   O7  FFN act  — the activation between the gate/up products and the down product's
+ *                  quantization.  SLM750-Edge card, "Key Architectural Features": FFN
+ *                  activation ReLU2 = relu(x)^2, and §2.3: a gate, an up and a down matrix per
+ *                  layer, read as h = relu(gate)^2 * up (gated) or h = relu(x)^2 (one input);
+ *                  the Distillix and Qwen3-shaped layer sets name SwiGLU gate/up projections:
+ *                  h = silu(gate) * up with silu(g) = g / (1 + exp(-g)).  Each is evaluated in
+ *                  fp64 from the fp32 inputs and rounded to fp32 once (a reading).
+ *   O8  residual — y_out = fp32(y + r): the BitLinear output added to the residual stream,
+ *                  y from O6, one fp32 addition.
+ *
  * Degenerate data (defined here, the pages are silent): gamma == 0 gives all codes 0; a row
  * with absmax 0 gives q = 0 and s_x = 0.  NaN inputs are outside the method's domain; where
  * a comparison meets a NaN the result is code 0.
@@ -277,4 +288,43 @@ int oracle_forward_entries(const int8_t *Xq, const float *s_x, const uint32_t *p
         Y[i] = (float)((double)acc[i] * (double)gamma * (double)s_x[m]);
     }
     return 0;
+}
+
+/* ---------------------------------------------------------- O7: FFN activation (chain) */
+
+/* Activation kinds: 1 = SwiGLU h = silu(x) * x2, 2 = gated ReLU^2 h = relu(x)^2 * x2,
+ * 3 = ReLU^2 h = relu(x)^2 (x2 unused).  fp64 evaluation, one rounding to fp32. */
+float oracle_ffn_act1(int kind, float x, float x2)
+{
+    double v;
+    if (kind == 1) {
+        v = ((double)x / (1.0 + exp(-(double)x))) * (double)x2;
+    } else if (kind == 2) {
+        double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r * (double)x2;
+    } else {
+        double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r;
+    }
+    return (float)v;
+}
+
+/* H = act(X, X2) elementwise over `count` values (X2 may be NULL for kind 3). */
+void oracle_ffn_act(int kind, const float *X, const float *X2, int64_t count, float *H)
+{
+    for (int64_t i = 0; i < count; ++i)
+        H[i] = oracle_ffn_act1(kind, X[i], X2 ? X2[i] : 0.0f);
+}
+
+/* ------------------------------------------------------- O8: residual epilogue (chain) */
+
+/* y[m][n] = fp32( fp32((double)acc * (double)gamma * (double)s_x[m]) + r[m][n] ). */
+void oracle_epilogue_residual(const int32_t *acc, const float *s_x, float gamma,
+                              const float *R, int64_t M, int64_t N, float *Y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            float y = (float)((double)acc[m * N + n] * (double)gamma * (double)s_x[m]);
+            Y[m * N + n] = y + R[m * N + n];
+        }
 }

@@ -345,4 +345,99 @@ def pin_quantize_weights_chain(orc):
     assert np.array_equal(orc.unpack(P, 80), ref) and np.array_equal(C, ref)
 
 
+# ------------------------------------------------- O7 / O8: layer-chain FFN act, residual
+
+def _f32(x):
+    return np.float32(x)
+
+
+def _ulp32(v):
+    v = abs(float(v))
+    return float(np.spacing(np.float32(v))) if v > 0 else float(np.float32(1.4e-45))
+
+
+def pin_relu2_exact(orc):
+    """ReLU^2 (SLM750-Edge card, "Key Architectural Features": relu(x)^2) is the correctly
+    rounded square of the positive part: exact rational arithmetic, including 0, -0,
+    subnormal inputs, squares that overflow fp32 and negative inputs (all zero)."""
+    xs = list(_rng(70).standard_normal(400).astype(np.float32) * np.float32(3))
+    xs += [0.0, -0.0, 1e-40, -1e-40, 1.5, -1.5, 3e19, 2.0 ** -75, 65504.0, 1.0 + 2.0 ** -23]
+    for x in xs:
+        x = _f32(x)
+        want = f32_of_fraction(Fraction(float(x)) ** 2) if x > 0 else np.float32(0.0)
+        got = orc.ffn_act1(orc.RELU2, x)
+        assert got == want or (np.isinf(want) and np.isinf(got)), (x, got, want)
+
+
+def pin_relu2_glu_near_exact(orc):
+    """Gated ReLU^2 h = relu(g)^2 * u against exact rationals: within one fp32 ulp always and
+    equal to the correctly rounded value in all but a sliver of cases (the fp64 evaluation
+    rounds twice); exact zeros for g <= 0 or u = 0, and relu(g)^2 for u = 1."""
+    r = _rng(71)
+    G = r.standard_normal(2000).astype(np.float32) * np.float32(2)
+    U = r.standard_normal(2000).astype(np.float32)
+    H = orc.ffn_act(orc.RELU2_GLU, G, U)
+    equal = 0
+    for g, u, h in zip(G, U, H):
+        want = f32_of_fraction(Fraction(float(g)) ** 2 * Fraction(float(u))) if g > 0 else np.float32(0.0)
+        assert abs(float(h) - float(want)) <= _ulp32(want), (g, u, h, want)
+        equal += h == want
+    assert equal >= 1995, equal
+    for g in (-2.0, -0.0, 0.0):
+        assert orc.ffn_act1(orc.RELU2_GLU, g, 5.0) == 0.0
+    assert orc.ffn_act1(orc.RELU2_GLU, 3.0, 0.0) == 0.0
+    assert orc.ffn_act1(orc.RELU2_GLU, 1.25, 1.0) == np.float32(1.5625)
+
+
+def _silu_times(g, u):
+    """silu(g) * u correctly rounded to fp32, from a 60-digit decimal evaluation."""
+    getcontext().prec = 60
+    dg = Decimal(float(g))
+    val = dg / (Decimal(1) + (-dg).exp()) * Decimal(float(u))
+    return f32_of_fraction(Fraction(val))
+
+
+def pin_swiglu_high_precision(orc):
+    """SwiGLU h = silu(g) * u, silu(g) = g / (1 + e^-g), against a 60-digit decimal evaluation:
+    within one fp32 ulp always, equal in all but a sliver of cases; silu(0) = 0; for large g
+    silu(g) * u rounds to g * u; for very negative g the product underflows to zero."""
+    r = _rng(72)
+    G = r.standard_normal(600).astype(np.float32) * np.float32(4)
+    U = r.standard_normal(600).astype(np.float32)
+    H = orc.ffn_act(orc.SWIGLU, G, U)
+    equal = 0
+    for g, u, h in zip(G, U, H):
+        want = _silu_times(g, u)
+        assert abs(float(h) - float(want)) <= _ulp32(want), (g, u, h, want)
+        equal += h == want
+    assert equal >= 597, equal
+    assert orc.ffn_act1(orc.SWIGLU, 0.0, 3.0) == 0.0
+    assert orc.ffn_act1(orc.SWIGLU, 200.0, 1.5) == np.float32(300.0)
+    assert orc.ffn_act1(orc.SWIGLU, -300.0, 1.0) == 0.0
+    # silu(x) - silu(-x) = x (odd part), checked through one rounding each.
+    for x in (0.5, 1.0, 2.5, 7.0):
+        a, b = float(orc.ffn_act1(orc.SWIGLU, x, 1.0)), float(orc.ffn_act1(orc.SWIGLU, -x, 1.0))
+        assert abs((a - b) - x) <= 2 * _ulp32(x), (x, a, b)
+
+
+def pin_residual_epilogue_exact(orc):
+    """Residual epilogue: fp32(fp32(acc * gamma * s_x) + r), the second step one exactly
+    rounded fp32 addition; r = 0 gives the plain epilogue, r = -y gives +0."""
+    r = _rng(73)
+    M, N = 5, 37
+    acc = r.integers(-200000, 200000, (M, N)).astype(np.int32)
+    sx = (r.random(M) * 0.05).astype(np.float32)
+    gamma = np.float32(0.021)
+    R = (r.standard_normal((M, N)) * 3).astype(np.float32)
+    Y0 = orc.epilogue(acc, sx, gamma)
+    Y = orc.epilogue_residual(acc, sx, gamma, R)
+    for m in range(M):
+        for n in range(N):
+            want = f32_of_fraction(Fraction(float(Y0[m, n])) + Fraction(float(R[m, n])))
+            assert Y[m, n] == want, (m, n, Y[m, n], want)
+    assert np.array_equal(orc.epilogue_residual(acc, sx, gamma, np.zeros_like(R)), Y0)
+    Z = orc.epilogue_residual(acc, sx, gamma, -Y0)
+    assert np.all(Z == 0.0) and not np.any(np.signbit(Z[Y0 != 0]))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

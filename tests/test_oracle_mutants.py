@@ -42,6 +42,15 @@ MUTANTS = {
                              "Y[m * N + n] = (float)((double)acc[m * N + n] * (double)s_x[m]);"),
     "epilogue_wrong_row_scale": ("Y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma * (double)s_x[m]);",
                                  "Y[m * N + n] = (float)((double)acc[m * N + n] * (double)gamma * (double)s_x[0]);"),
+    "silu_wrong_sign": ("(1.0 + exp(-(double)x))", "(1.0 + exp((double)x))"),
+    "swiglu_drops_up": ("v = ((double)x / (1.0 + exp(-(double)x))) * (double)x2;",
+                        "v = ((double)x / (1.0 + exp(-(double)x)));"),
+    "relu2_glu_no_square": ("v = r * r * (double)x2;", "v = r * (double)x2;"),
+    "relu2_no_square": ("        v = r * r;\n    }", "        v = r;\n    }"),
+    "relu2_keeps_negatives": ("        double r = x > 0.0f ? (double)x : 0.0;\n        v = r * r;",
+                              "        double r = (double)x;\n        v = r * r;"),
+    "residual_dropped": ("Y[m * N + n] = y + R[m * N + n];", "Y[m * N + n] = y;"),
+    "residual_subtracted": ("Y[m * N + n] = y + R[m * N + n];", "Y[m * N + n] = y - R[m * N + n];"),
 }
 
 
