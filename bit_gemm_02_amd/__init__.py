@@ -12,6 +12,9 @@ Steps (see the header for the passages each follows):
   quantize_acts     per-token absmax int8 activations (optionally with the SubLN RMSNorm)
   forward           exact int32 ternary x int8 product and the gamma * s_x epilogue
   linear_grouped    steps 3 to 5 in one launch for decode-sized token counts
+  quantize_acts_ex_grouped / forward_ex_grouped
+                    the layer chain's FFN activation before quantization, and products that
+                    add a residual in their epilogue (see layer.py)
 """
 
 from __future__ import annotations
@@ -30,6 +33,7 @@ MAX_GROUP = 16
 MAX_K = 262144
 DECODE_MAX_M = 16
 LINEAR_FUSED_MAX_M = 4
+ACT_NONE, ACT_SWIGLU, ACT_RELU2_GLU, ACT_RELU2 = 0, 1, 2, 3
 LINEAR_FUSED_MAX_BYTES = 49152
 
 
@@ -66,6 +70,20 @@ class _LinearProblem(ctypes.Structure):
                 ("Y", ctypes.c_void_p), ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("x_dtype", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
+class _ActExProblem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("X2", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("x_dtype", ctypes.c_int),
+                ("act", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
+class _ForwardExProblem(ctypes.Structure):
+    _fields_ = [("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 _lib = None
@@ -108,6 +126,10 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_grouped.restype = ctypes.c_int
     L.bitlinear_linear_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_grouped.restype = ctypes.c_int
+    L.bitlinear_quantize_acts_ex_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_quantize_acts_ex_grouped.restype = ctypes.c_int
+    L.bitlinear_forward_ex_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_forward_ex_grouped.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -323,3 +345,56 @@ def linear(X: torch.Tensor, W_packed: torch.Tensor, gamma: torch.Tensor,
         p["x_scale"] = torch.empty(M, dtype=torch.float32, device=X.device)
     linear_grouped([p], stream=stream)
     return Y
+
+
+def act_ex_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_quantize_acts_ex_grouped: dicts with X, X_q, x_scale and
+    optional X2, norm_weight, act (ACT_*), eps."""
+    arr = (_ActExProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        X2 = p.get("X2")
+        if X2 is not None:
+            _dev(X2, f"X2[{i}]", torch.float32)
+            if tuple(X2.shape) != (M, K):
+                raise ValueError(f"X2[{i}] must have the shape of X")
+        arr[i] = _ActExProblem(_ptr(X), _ptr(X2), _ptr(p.get("norm_weight")), _ptr(p["X_q"]),
+                               _ptr(p["x_scale"]), M, K, _x_dtype(X), int(p.get("act", ACT_NONE)),
+                               float(p.get("eps", 1e-6)))
+    return arr
+
+
+def quantize_acts_ex_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Activation quantization with an optional FFN activation in front (see act_ex_table);
+    outputs preallocated."""
+    arr = act_ex_table(problems)
+    _check("bitlinear_quantize_acts_ex_grouped",
+           lib().bitlinear_quantize_acts_ex_grouped(ctypes.addressof(arr), len(problems),
+                                                    _stream(stream)))
+
+
+def forward_ex_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_forward_ex_grouped: dicts as for forward_grouped plus an
+    optional fp32 residual [M, N]."""
+    arr = (_ForwardExProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        M, K = p["X_q"].shape
+        N = p["W_packed"].shape[0]
+        R = p.get("residual")
+        if R is not None:
+            _dev(R, f"residual[{i}]", torch.float32)
+            if tuple(R.shape) != (M, N):
+                raise ValueError(f"residual[{i}] must be [M, N]")
+        arr[i] = _ForwardExProblem(_ptr(p["X_q"]), _ptr(p["x_scale"]), _ptr(p["W_packed"]),
+                                   _ptr(p["gamma"]), _ptr(p["Y"]), _ptr(p.get("acc")), _ptr(R),
+                                   M, N, K)
+    return arr
+
+
+def forward_ex_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Products with an optional residual added in the epilogue; outputs preallocated."""
+    arr = forward_ex_table(problems)
+    _check("bitlinear_forward_ex_grouped",
+           lib().bitlinear_forward_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+

@@ -78,7 +78,88 @@ bl_status check_forward(const bl_forward_problem &p)
     return BL_OK;
 }
 
+bl_status check_act_ex(const bl_act_ex_problem &p)
+{
+    bl_act_problem base{p.X, p.norm_weight, p.X_q, p.x_scale, p.M, p.K, p.x_dtype, p.eps};
+    bl_status s = check_act(base);
+    if (s != BL_OK)
+        return s;
+    if (p.act < BL_ACT_NONE || p.act > BL_ACT_RELU2)
+        return BL_ERR_DTYPE;
+    if (p.act != BL_ACT_NONE && p.x_dtype != BL_F32)
+        return BL_ERR_DTYPE;
+    const bool glu = p.act == BL_ACT_SWIGLU || p.act == BL_ACT_RELU2_GLU;
+    if (glu && p.M != 0 && !p.X2)
+        return BL_ERR_NULL;
+    if (glu && !aligned16(p.X2))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status check_forward_ex(const bl_forward_ex_problem &p)
+{
+    bl_forward_problem base{p.X_q, p.x_scale, p.W_packed, p.gamma, p.Y, p.acc, p.M, p.N, p.K};
+    bl_status s = check_forward(base);
+    if (s != BL_OK)
+        return s;
+    if (reinterpret_cast<uintptr_t>(p.residual) & 3u)
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_act_ex_problem to_ex(const bl_act_problem &p)
+{
+    return bl_act_ex_problem{p.X, nullptr, p.norm_weight, p.X_q, p.x_scale, p.M, p.K,
+                             p.x_dtype, BL_ACT_NONE, p.eps};
+}
+
+bl_forward_ex_problem to_ex(const bl_forward_problem &p)
+{
+    return bl_forward_ex_problem{p.X_q, p.x_scale, p.W_packed, p.gamma, p.Y, p.acc, nullptr,
+                                 p.M, p.N, p.K};
+}
+
 bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+// Validated problems -> launches: act quant of any form in one call.
+bl_status run_acts(const bl_act_ex_problem *q, int count, void *stream)
+{
+    int64_t rows = 0;
+    for (int i = 0; i < count; ++i)
+        rows += q[i].M;
+    if (rows > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_quantize_acts(q, count, static_cast<hipStream_t>(stream)));
+}
+
+// Validated products -> one decode launch (M <= 16) and one prefill launch (the rest).
+bl_status run_forward(const bl_forward_ex_problem *q, int count, void *stream)
+{
+    bl_forward_ex_problem dec[BL_MAX_GROUP], pre[BL_MAX_GROUP];
+    int nd = 0, np = 0;
+    int64_t dec_blocks = 0, pre_blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_forward_ex_problem &p = q[i];
+        if (p.M <= bl::kDecodeMaxM) {
+            dec[nd++] = p;
+            dec_blocks += (p.N + 15) / 16;
+        } else {
+            pre[np++] = p;
+            pre_blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        }
+    }
+    if (dec_blocks > INT_MAX || pre_blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (nd) {
+        bl_status s = from_hip(bl::launch_forward_decode(dec, nd, st));
+        if (s != BL_OK)
+            return s;
+    }
+    if (np)
+        return from_hip(bl::launch_forward_prefill(pre, np, st));
+    return BL_OK;
+}
 
 bool linear_fused(const bl_linear_problem &p)
 {
@@ -199,16 +280,29 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int co
         return BL_ERR_NULL;
     if (count <= 0 || count > BL_MAX_GROUP)
         return BL_ERR_COUNT;
-    int64_t rows = 0;
+    bl_act_ex_problem ex[BL_MAX_GROUP];
     for (int i = 0; i < count; ++i) {
         bl_status s = check_act(problems[i]);
         if (s != BL_OK)
             return s;
-        rows += problems[i].M;
+        ex[i] = to_ex(problems[i]);
     }
-    if (rows > INT_MAX)
-        return BL_ERR_SHAPE;
-    return from_hip(bl::launch_quantize_acts(problems, count, static_cast<hipStream_t>(stream)));
+    return run_acts(ex, count, stream);
+}
+
+bl_status bitlinear_quantize_acts_ex_grouped(const bl_act_ex_problem *problems, int count,
+                                             void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_act_ex(problems[i]);
+        if (s != BL_OK)
+            return s;
+    }
+    return run_acts(problems, count, stream);
 }
 
 bl_status bitlinear_quantize_acts(const void *X, int x_dtype, int64_t M, int64_t K,
@@ -225,33 +319,29 @@ bl_status bitlinear_forward_grouped(const bl_forward_problem *problems, int coun
         return BL_ERR_NULL;
     if (count <= 0 || count > BL_MAX_GROUP)
         return BL_ERR_COUNT;
-    bl_forward_problem dec[BL_MAX_GROUP], pre[BL_MAX_GROUP];
-    int nd = 0, np = 0;
-    int64_t dec_blocks = 0, pre_blocks = 0;
+    bl_forward_ex_problem ex[BL_MAX_GROUP];
     for (int i = 0; i < count; ++i) {
-        const bl_forward_problem &p = problems[i];
-        bl_status s = check_forward(p);
+        bl_status s = check_forward(problems[i]);
         if (s != BL_OK)
             return s;
-        if (p.M <= bl::kDecodeMaxM) {
-            dec[nd++] = p;
-            dec_blocks += (p.N + 15) / 16;
-        } else {
-            pre[np++] = p;
-            pre_blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
-        }
+        ex[i] = to_ex(problems[i]);
     }
-    if (dec_blocks > INT_MAX || pre_blocks > INT_MAX)
-        return BL_ERR_SHAPE;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (nd) {
-        bl_status s = from_hip(bl::launch_forward_decode(dec, nd, st));
+    return run_forward(ex, count, stream);
+}
+
+bl_status bitlinear_forward_ex_grouped(const bl_forward_ex_problem *problems, int count,
+                                       void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_forward_ex(problems[i]);
         if (s != BL_OK)
             return s;
     }
-    if (np)
-        return from_hip(bl::launch_forward_prefill(pre, np, st));
-    return BL_OK;
+    return run_forward(problems, count, stream);
 }
 
 bl_status bitlinear_forward(const int8_t *X_q, const float *x_scale, const uint32_t *W_packed,
@@ -269,8 +359,8 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
     if (count <= 0 || count > BL_MAX_GROUP)
         return BL_ERR_COUNT;
     bl_linear_problem fused[BL_MAX_GROUP];
-    bl_act_problem act[BL_MAX_GROUP];
-    bl_forward_problem fwd[BL_MAX_GROUP];
+    bl_act_ex_problem act[BL_MAX_GROUP];
+    bl_forward_ex_problem fwd[BL_MAX_GROUP];
     int nf = 0, nt = 0;
     int64_t blocks = 0;
     for (int i = 0; i < count; ++i) {
@@ -284,9 +374,10 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
             fused[nf++] = p;
             blocks += (p.N + 15) / 16;
         } else {
-            act[nt] = bl_act_problem{p.X, p.norm_weight, p.X_q, p.x_scale, p.M, p.K, p.x_dtype, p.eps};
-            fwd[nt] = bl_forward_problem{p.X_q, p.x_scale, p.W_packed, p.gamma, p.Y, nullptr,
-                                         p.M, p.N, p.K};
+            act[nt] = bl_act_ex_problem{p.X, nullptr, p.norm_weight, p.X_q, p.x_scale, p.M, p.K,
+                                        p.x_dtype, BL_ACT_NONE, p.eps};
+            fwd[nt] = bl_forward_ex_problem{p.X_q, p.x_scale, p.W_packed, p.gamma, p.Y, nullptr,
+                                            nullptr, p.M, p.N, p.K};
             ++nt;
         }
     }
@@ -299,10 +390,10 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
             return s;
     }
     if (nt) {
-        bl_status s = bitlinear_quantize_acts_grouped(act, nt, stream);
+        bl_status s = run_acts(act, nt, stream);
         if (s != BL_OK)
             return s;
-        return bitlinear_forward_grouped(fwd, nt, stream);
+        return run_forward(fwd, nt, stream);
     }
     return BL_OK;
 }

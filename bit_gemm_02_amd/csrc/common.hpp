@@ -181,12 +181,12 @@ hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *
 size_t quantize_weights_workspace(int count);
 hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
                              hipStream_t stream);
-hipError_t launch_quantize_acts(const bl_act_problem *p, int count, hipStream_t stream);
-hipError_t launch_forward_decode(const bl_forward_problem *p, int count, hipStream_t stream);
+hipError_t launch_quantize_acts(const bl_act_ex_problem *p, int count, hipStream_t stream);
+hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 // Fused decode form: every problem has M <= BL_LINEAR_FUSED_MAX_M and M * K within
 // BL_LINEAR_FUSED_MAX_BYTES.
 hipError_t launch_linear_decode(const bl_linear_problem *p, int count, hipStream_t stream);
-hipError_t launch_forward_prefill(const bl_forward_problem *p, int count, hipStream_t stream);
+hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.
 constexpr int64_t kDecodeMaxM = 16;

@@ -40,6 +40,7 @@ struct FwdDev {
     int32_t *acc;
     int M, N, K;
     int block_begin;
+    const float *R;     // residual added to the output, or NULL
     // Fused decode form only: raw activations, norm, and optional copies of codes / scales.
     const void *X;
     const float *g;
@@ -329,7 +330,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
         if (m < p.M) {
             const int a = accv[v] >> 6;  // exact: the sum is a multiple of 64
             const double scale = gamma * (double)sxv[v];
-            p.Y[(int64_t)m * p.N + n] = (float)((double)a * scale);
+            float y = (float)((double)a * scale);
+            if (p.R)
+                y = y + p.R[(int64_t)m * p.N + n];
+            p.Y[(int64_t)m * p.N + n] = y;
             if (p.acc)
                 p.acc[(int64_t)m * p.N + n] = a;
         }
@@ -355,7 +359,7 @@ static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t
 }
 
 template <int RG, bool XLDS>
-static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t stream)
+static hipError_t launch_rg(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
     // Longest-K problems first: their blocks take longest, so they should not start last.
     int order[BL_MAX_GROUP];
@@ -368,7 +372,7 @@ static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t 
     int blocks = 0, n = 0;
     bool full_k = true;
     for (int o = 0; o < m; ++o) {
-        const bl_forward_problem &s = q[order[o]];
+        const bl_forward_ex_problem &s = q[order[o]];
         full_k = full_k && (s.K % 256 == 0);
         FwdDev &d = b.p[n++];
         d.Xq = s.X_q;
@@ -377,6 +381,7 @@ static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t 
         d.gamma = s.gamma;
         d.Y = s.Y;
         d.acc = s.acc;
+        d.R = s.residual;
         d.M = (int)s.M;
         d.N = (int)s.N;
         d.K = (int)s.K;
@@ -389,7 +394,7 @@ static hipError_t launch_rg(const bl_forward_problem *q, int count, hipStream_t 
 
 // Row groups per block: as many as still leave at least one block per compute unit
 // (fewer activation loads per weight byte), else one (more blocks for small layers).
-hipError_t launch_forward_decode(const bl_forward_problem *q, int count, hipStream_t stream)
+hipError_t launch_forward_decode(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
     int64_t rows = 0;
     bool xlds = true;

@@ -31,6 +31,7 @@ struct PreDev {
     const float *gamma;
     float *Y;
     int32_t *acc;
+    const float *R;     // residual added to the output, or NULL
     int M, N, K;
     int tiles_n;
     int block_begin;
@@ -374,7 +375,8 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     // in a ragged last column group).
     const double gamma = (double)gammaf;
     const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0 &&
-                     (!p.acc || ((uintptr_t)p.acc & 15) == 0);
+                     (!p.acc || ((uintptr_t)p.acc & 15) == 0) &&
+                     (!p.R || ((uintptr_t)p.R & 15) == 0);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
         const int m = m0 + wm * T::TM + mi * 16 + r;
@@ -382,6 +384,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             continue;
         const double scale = gamma * (double)sxv[mi];
         float *yrow = p.Y + (int64_t)m * p.N;
+        const float *rrow = p.R ? p.R + (int64_t)m * p.N : nullptr;
         int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
@@ -394,6 +397,13 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
                 y[v] = (float)((double)a[v] * scale);
             }
             if (vec && n + 3 < p.N) {
+                if (rrow) {
+                    const float4 rv = *reinterpret_cast<const float4 *>(rrow + n);
+                    y[0] = y[0] + rv.x;
+                    y[1] = y[1] + rv.y;
+                    y[2] = y[2] + rv.z;
+                    y[3] = y[3] + rv.w;
+                }
                 *reinterpret_cast<float4 *>(yrow + n) = make_float4(y[0], y[1], y[2], y[3]);
                 if (arow_out)
                     *reinterpret_cast<int4 *>(arow_out + n) = make_int4(a[0], a[1], a[2], a[3]);
@@ -401,7 +411,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     if (n + v < p.N) {
-                        yrow[n + v] = y[v];
+                        yrow[n + v] = rrow ? y[v] + rrow[n + v] : y[v];
                         if (arow_out)
                             arow_out[n + v] = a[v];
                     }
@@ -412,7 +422,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 }
 
 template <class T>
-static int build_batch(const bl_forward_problem *q, int count, PreBatch &b, bool &full_k)
+static int build_batch(const bl_forward_ex_problem *q, int count, PreBatch &b, bool &full_k)
 {
     // Longest-K problems first: their tiles take longest, so they should not start last.
     int order[BL_MAX_GROUP];
@@ -429,7 +439,7 @@ static int build_batch(const bl_forward_problem *q, int count, PreBatch &b, bool
     int blocks = 0;
     full_k = true;
     for (int i = 0; i < n; ++i) {
-        const bl_forward_problem &s = q[order[i]];
+        const bl_forward_ex_problem &s = q[order[i]];
         PreDev &d = b.p[i];
         d.Xq = s.X_q;
         d.sx = s.x_scale;
@@ -437,6 +447,7 @@ static int build_batch(const bl_forward_problem *q, int count, PreBatch &b, bool
         d.gamma = s.gamma;
         d.Y = s.Y;
         d.acc = s.acc;
+        d.R = s.residual;
         d.M = (int)s.M;
         d.N = (int)s.N;
         d.K = (int)s.K;
@@ -451,7 +462,7 @@ static int build_batch(const bl_forward_problem *q, int count, PreBatch &b, bool
 }
 
 template <class T>
-static hipError_t launch_tiles(const bl_forward_problem *q, int count, hipStream_t stream)
+static hipError_t launch_tiles(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
     PreBatch b{};
     bool full_k;
@@ -484,7 +495,7 @@ static int tile_override()
 
 // Large tiles (half the LDS and cache traffic per operation) when they still give every
 // compute unit at least two tiles; otherwise 128 x 128.
-hipError_t launch_forward_prefill(const bl_forward_problem *q, int count, hipStream_t stream)
+hipError_t launch_forward_prefill(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
     switch (tile_override()) {
     case 1: return launch_tiles<TileBig>(q, count, stream);

@@ -291,6 +291,8 @@ struct ActDev {
     int bf16;
     float eps;
     int row_begin;  // first row of this problem in the launch's row space
+    const float *x2;  // FFN activation's second input (GLU kinds), or NULL
+    int act;          // bl_act_kind
 };
 
 struct ActBatch {
@@ -573,6 +575,113 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
         write_scale(p, m, a, sum, norm);
 }
 
+// FFN activation in front of the down projection's quantization: h = act(x, x2) evaluated in
+// fp64 from the fp32 inputs, rounded to fp32 once (SwiGLU: silu(x) * x2 with
+// silu(g) = g / (1 + exp(-g)); gated ReLU^2: relu(x)^2 * x2; ReLU^2: relu(x)^2).
+__device__ __forceinline__ float ffn_act(int kind, float x, float x2)
+{
+    double v;
+    if (kind == BL_ACT_SWIGLU) {
+        v = ((double)x / (1.0 + exp(-(double)x))) * (double)x2;
+    } else if (kind == BL_ACT_RELU2_GLU) {
+        const double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r * (double)x2;
+    } else {
+        const double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r;
+    }
+    return (float)v;
+}
+
+__device__ __forceinline__ float4 ffn_act4(int kind, float4 x, float4 x2)
+{
+    return make_float4(ffn_act(kind, x.x, x2.x), ffn_act(kind, x.y, x2.y),
+                       ffn_act(kind, x.z, x2.z), ffn_act(kind, x.w, x2.w));
+}
+
+// One block per token row of an FFN hidden state: h = act(gate, up) from two fp32 rows, then
+// the same absmax (+ SubLN over h) quantization as the block kernel.  The first C groups of
+// four per thread of both inputs stay in registers; h is recomputed for the second pass
+// (deterministic, the same value).
+template <int C>
+__global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
+{
+    __shared__ float lds_max[kActThreads / kWave];
+    __shared__ double lds_sum[kActThreads / kWave];
+    const ActDev &p = b.p[find_problem(b, (int)blockIdx.x)];
+    const int m = blockIdx.x - p.row_begin;
+    const int groups = p.K / 4;
+    const bool norm = p.g != nullptr;
+    const int kind = p.act;
+    const rsrc_t xr = row_rsrc(p, m);
+    const rsrc_t x2r = make_rsrc(p.x2 ? p.x2 + (int64_t)m * p.K : p.x2, p.x2 ? (uint32_t)p.K * 4u : 0u);
+    const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+    const int tid = threadIdx.x;
+
+    auto f4 = [](const v4u &r) {
+        return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
+                           __uint_as_float(r.w));
+    };
+    auto absmax_group = [&](const v4u &r, const v4u &r2, int j, float &amax, double &ss) {
+        const float4 h = ffn_act4(kind, f4(r), f4(r2));
+        const float4 u = norm ? mul4(h, load_g(gr, j < groups ? j : (int)(kOOB / 16u))) : h;
+        amax = fmaxf(amax, absmax4(u));
+        if (norm)
+            ss = sumsq4(ss, h);
+    };
+    auto quant_group = [&](const v4u &r, const v4u &r2, int j, float inv) {
+        const float4 h = ffn_act4(kind, f4(r), f4(r2));
+        reinterpret_cast<char4 *>(p.Xq + (int64_t)m * p.K)[j] =
+            quant4(norm ? mul4(h, load_g(gr, j)) : h, inv);
+    };
+
+    v4u raw[C], raw2[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * kActThreads + tid;
+        const uint32_t off = j < groups ? (uint32_t)j * 16u : kOOB;
+        raw[c] = buf_load16(xr, off);
+        raw2[c] = buf_load16(x2r, off);
+    }
+    float amax = 0.0f;
+    double ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        absmax_group(raw[c], raw2[c], c * kActThreads + tid, amax, ss);
+    for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
+        absmax_group(buf_load16(xr, (uint32_t)j * 16u), buf_load16(x2r, (uint32_t)j * 16u), j,
+                     amax, ss);
+
+    amax = wave_max(amax);
+    if (norm)
+        ss = wave_sum_fixed(ss);
+    const int wave = tid / kWave;
+    if ((tid & (kWave - 1)) == 0) {
+        lds_max[wave] = amax;
+        lds_sum[wave] = ss;
+    }
+    __syncthreads();
+    float a = lds_max[0];
+    double sum = lds_sum[0];
+#pragma unroll
+    for (int w = 1; w < kActThreads / kWave; ++w) {
+        a = fmaxf(a, lds_max[w]);
+        sum = sum + lds_sum[w];
+    }
+
+    const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded fp32 division
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int j = c * kActThreads + tid;
+        if (j < groups)
+            quant_group(raw[c], raw2[c], j, inv);
+    }
+    for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
+        quant_group(buf_load16(xr, (uint32_t)j * 16u), buf_load16(x2r, (uint32_t)j * 16u), j, inv);
+    if (tid == 0)
+        write_scale(p, m, a, sum, norm);
+}
+
 // Groups per thread kept in registers by the block kernel: the smallest class that holds
 // the longest row of the launch (longer rows re-read the rest).
 constexpr int kActBlockClasses[] = {4, 8, 16};
@@ -603,7 +712,7 @@ static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
                        stream, b, rows);
 }
 
-hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t stream)
+hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream_t stream)
 {
     // Problems with rows up to 4096 share one wave-kernel launch per dtype, sized by their
     // longest row (shorter rows load zeros past their end); longer rows use the block kernel.
@@ -611,7 +720,7 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
     int order[BL_MAX_GROUP];
     int n = 0;
     for (int i = 0; i < count; ++i)
-        if (q[i].M > 0)
+        if (q[i].M > 0 && q[i].act == BL_ACT_NONE)
             order[n++] = i;
     for (int i = 1; i < n; ++i)
         for (int j = i; j > 0 && q[order[j]].K > q[order[j - 1]].K; --j) {
@@ -624,7 +733,7 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
             ActBatch b{};
             int rows = 0, cls = 0;
             for (int i = 0; i < n; ++i) {
-                const bl_act_problem &s = q[order[i]];
+                const bl_act_ex_problem &s = q[order[i]];
                 const int cpl = (int)((s.K / 4 + kWave - 1) / kWave);  // chunks per lane
                 int c = 0;
                 while (c < kActNumClasses && cpl > kActClasses[c])
@@ -643,6 +752,8 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
                 d.bf16 = bf;
                 d.eps = s.eps;
                 d.row_begin = rows;
+                d.x2 = nullptr;
+                d.act = BL_ACT_NONE;
                 rows += d.M;
             }
             if (!rows)
@@ -677,6 +788,39 @@ hipError_t launch_quantize_acts(const bl_act_problem *q, int count, hipStream_t 
                 else if (cls == 1) launch_wave<8, false>(b, rows, stream);
                 else launch_wave<16, false>(b, rows, stream);
             }
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    // Problems with an FFN activation: one block-kernel launch (fp32 inputs).
+    {
+        ActBatch b{};
+        int rows = 0, gpt = 0;
+        for (int i = 0; i < count; ++i) {
+            const bl_act_ex_problem &s = q[i];
+            if (s.M == 0 || s.act == BL_ACT_NONE)
+                continue;
+            ActDev &d = b.p[b.count++];
+            d.X = s.X;
+            d.g = s.norm_weight;
+            d.Xq = s.X_q;
+            d.sx = s.x_scale;
+            d.M = (int)s.M;
+            d.K = (int)s.K;
+            d.bf16 = 0;
+            d.eps = s.eps;
+            d.row_begin = rows;
+            d.x2 = s.X2;
+            d.act = s.act;
+            rows += d.M;
+            gpt = std::max(gpt, (int)((s.K / 4 + kActThreads - 1) / kActThreads));
+        }
+        if (rows) {
+            if (gpt <= 4)
+                hipLaunchKernelGGL((act_quant_ffn_kernel<4>), dim3(rows), dim3(kActThreads), 0, stream, b);
+            else
+                hipLaunchKernelGGL((act_quant_ffn_kernel<12>), dim3(rows), dim3(kActThreads), 0, stream, b);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;

@@ -244,6 +244,67 @@ typedef struct {
 /* Up to BL_MAX_GROUP independent layer calls; all fused ones share one launch. */
 bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count, void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Layer chain: the two extensions the BitLinear sub-graph of a transformer layer needs.
+ *
+ * BitDistill article, "Stage 1 — Architectural refinement with SubLN": SubLN before the
+ * attention output projection and before the FFN output projection.  SLM750-Edge card, "Key
+ * Architectural Features": FFN activation ReLU2 = relu(x)^2, RMSNorm epsilon 1e-6; §2.3: a
+ * gate, an up and a down matrix per layer.  The Distillix and Qwen3-shaped layer sets name
+ * SwiGLU gate/up projections.
+ *
+ * (1) Activation quantization with the FFN activation in front (the down projection's input):
+ *     h = act(X, X2) per element, evaluated in fp64 from the fp32 inputs and rounded to fp32
+ *     once, then quantized exactly as bitlinear_quantize_acts quantizes x (with the optional
+ *     SubLN RMSNorm over h: codes from fl32(h * g), scale from the RMS of h):
+ *       BL_ACT_SWIGLU     h = silu(X) * X2, silu(g) = g / (1 + exp(-g))
+ *       BL_ACT_RELU2_GLU  h = relu(X)^2 * X2
+ *       BL_ACT_RELU2      h = relu(X)^2            (X2 unused, may be NULL)
+ *     With an activation, X and X2 are fp32 (the gate and up products' outputs) [M][K].
+ *     Otherwise (BL_ACT_NONE) the problem is exactly a bitlinear_quantize_acts problem.
+ *     The fp64 exp is the device library's; it may differ from another libm in its last
+ *     bit, which changes the fp32 h only when that value lies within 2^-52 (relative) of an
+ *     fp32 rounding midpoint.
+ * (2) Products with a residual: Y = fl32(fl32(fp64(acc * gamma * x_scale[m])) + R[m][n]) —
+ *     the projection's output added to the residual stream in the epilogue, R fp32 [M][N]
+ *     (may alias Y; each element is read before it is written by the same thread).
+ * ------------------------------------------------------------------------------------- */
+typedef enum { BL_ACT_NONE = 0, BL_ACT_SWIGLU = 1, BL_ACT_RELU2_GLU = 2, BL_ACT_RELU2 = 3 } bl_act_kind;
+
+typedef struct {
+    const void *X;            /* [M][K]; the gate output for the GLU kinds */
+    const float *X2;          /* [M][K] fp32 up output for the GLU kinds, else NULL */
+    const float *norm_weight; /* [K] SubLN / RMSNorm weight, or NULL */
+    int8_t *X_q;
+    float *x_scale;
+    int64_t M, K;
+    int x_dtype;              /* BL_F32 or BL_BF16 (BL_F32 whenever act != BL_ACT_NONE) */
+    int act;                  /* bl_act_kind */
+    float eps;
+} bl_act_ex_problem;
+
+/* Up to BL_MAX_GROUP activation problems of either form in one call.  Errors as for
+ * bitlinear_quantize_acts_grouped, plus BL_ERR_DTYPE for an unknown act kind or a bf16
+ * input with an activation, and BL_ERR_NULL for a GLU kind without X2. */
+bl_status bitlinear_quantize_acts_ex_grouped(const bl_act_ex_problem *problems, int count,
+                                             void *stream);
+
+typedef struct {
+    const int8_t *X_q;
+    const float *x_scale;
+    const uint32_t *W_packed;
+    const float *gamma;
+    float *Y;
+    int32_t *acc;
+    const float *residual;    /* [M][N] fp32 added to the output, or NULL */
+    int64_t M, N, K;
+} bl_forward_ex_problem;
+
+/* Up to BL_MAX_GROUP products, each with an optional residual.  Errors as for
+ * bitlinear_forward_grouped (BL_ERR_ALIGN also for a residual not 4-byte aligned). */
+bl_status bitlinear_forward_ex_grouped(const bl_forward_ex_problem *problems, int count,
+                                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -177,6 +177,43 @@ def test_linear_grouped_validation(L, bl):
     assert call(N=0) == BL_OK
 
 
+def test_chain_entry_points_validation(L, bl):
+    qa = L.bitlinear_quantize_acts_ex_grouped
+
+    def act(**kw):
+        d = dict(X=A, X2=B, norm_weight=None, X_q=C, x_scale=D, M=2, K=64, x_dtype=0, act=1, eps=1e-6)
+        d.update(kw)
+        arr = (bl._ActExProblem * 1)()
+        arr[0] = bl._ActExProblem(**d)
+        return qa(ctypes.addressof(arr), 1, None)
+
+    assert qa(None, 1, None) == BL_ERR_NULL
+    assert act(act=4) == BL_ERR_DTYPE
+    assert act(act=-1) == BL_ERR_DTYPE
+    assert act(x_dtype=1) == BL_ERR_DTYPE          # activations need fp32 inputs
+    assert act(X2=None) == BL_ERR_NULL             # gated kinds need the up output
+    assert act(act=2, X2=None) == BL_ERR_NULL
+    assert act(X2=B + 4) == BL_ERR_ALIGN
+    assert act(K=40) == BL_ERR_SHAPE
+    assert act(X_q=None) == BL_ERR_NULL
+    assert act(M=0) == BL_OK
+    assert act(act=3, X2=None, M=0) == BL_OK
+    fe = L.bitlinear_forward_ex_grouped
+
+    def fwd(**kw):
+        d = dict(X_q=A, x_scale=B, W_packed=C, gamma=D, Y=E, acc=None, residual=None, M=1, N=4, K=64)
+        d.update(kw)
+        arr = (bl._ForwardExProblem * 1)()
+        arr[0] = bl._ForwardExProblem(**d)
+        return fe(ctypes.addressof(arr), 1, None)
+
+    assert fe(None, 1, None) == BL_ERR_NULL
+    assert fwd(residual=0x60002) == BL_ERR_ALIGN
+    assert fwd(W_packed=None) == BL_ERR_NULL
+    assert fwd(K=8) == BL_ERR_SHAPE
+    assert fwd(M=0, residual=0x60000) == BL_OK
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):
