@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole layer chain (six launches per layer, residuals and the "
+                         "FFN activation included) instead of the step; prints its own JSON line")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -446,6 +449,81 @@ def copy_calibration(torch):
     return n
 
 
+def layer_bench(torch, bl, wl: workloads.Workload, M_pre: int, rotate_bytes: float, reps: int):
+    """The workload's projections assembled into one transformer layer's BitLinear sub-graph
+    (bit_gemm_02_amd.layer), timed at one token and at the prefill token count.  Distinct
+    weight copies (about `rotate_bytes` in all) run one after another from a replayed HIP
+    graph, so every layer reads its weights from HBM; activation buffers are shared."""
+    from bit_gemm_02_amd import layer as L
+    act = {"swiglu": bl.ACT_SWIGLU, "relu2": bl.ACT_RELU2}[wl.ffn]
+    mats = {m.name: (i, m) for i, m in enumerate(wl.matrices)}
+    if not {"o", "up", "down"} <= set(mats):
+        raise SystemExit(f"{wl.key} is not a layer set (needs o, up and down projections)")
+    if wl.weights == "fp32":
+        names = list(mats)
+        packed = bl.quantize_weights_grouped(
+            [torch.from_numpy(workloads.weight_fp32(wl, mats[n][0])).cuda() for n in names])
+        base = {n: pg for n, pg in zip(names, packed)}
+    else:
+        base = {}
+        for n, (i, m) in mats.items():
+            P = bl.pack_codes(torch.from_numpy(workloads.weight_codes(wl, i)).cuda())
+            base[n] = (P, torch.full((1,), wl.code_gamma, device="cuda"))
+    d = mats["down"][1].N
+    norms = {}
+    for j, (key, K) in enumerate((("attn", d), ("o", mats["o"][1].K), ("ffn", d),
+                                  ("down", mats["down"][1].K))):
+        g = np.float32(1) + workloads.gaussian((K,), (wl.index, 70 + j), 0.1)
+        norms[key] = torch.from_numpy(g).cuda()
+    w_bytes = sum(P.numel() * 4 for P, _ in base.values())
+    R = int(max(1, min(1024, np.ceil(rotate_bytes / w_bytes))))
+    layers = [L.LayerWeights(packed={n: P.clone() for n, (P, _) in base.items()},
+                             gamma={n: g for n, (_, g) in base.items()}, norms=norms, act=act)
+              for _ in range(R)]
+    out = {"layer_copies": R, "ffn": wl.ffn, "projections": sorted(base)}
+    for M in (1, M_pre):
+        chains = [L.LayerChain(layers[0], M)]
+        chains += [L.LayerChain(w, M, like=chains[0]) for w in layers[1:]]
+        c0 = chains[0]
+        c0.x.copy_(torch.from_numpy(workloads.gaussian((M, d), (wl.index, 80, M), 1.0)))
+        c0.attn.copy_(torch.from_numpy(workloads.gaussian(tuple(c0.attn.shape), (wl.index, 81, M), 1.0)))
+        s_ = torch.cuda.Stream()
+        with torch.cuda.stream(s_):
+            for c in chains[:3]:
+                c(s_.cuda_stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s_):
+            for c in chains:
+                c(s_.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s_):
+            graph.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s_)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(s_)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+        ops = c0.ops()
+        # Bytes a layer must move at least: packed weights, gammas, norm weights, the layer
+        # input, the attention output and the layer output (intermediates not counted).
+        nbytes = (w_bytes + 4 * len(base) + sum(4 * g.numel() for g in norms.values())
+                  + 4 * M * (2 * d + c0.attn.shape[1]))
+        key = "decode" if M == 1 else "prefill"
+        out[key] = {"tokens": M, "us_per_layer": round(us, 3), "launches_per_layer": 6,
+                    "tokens_per_s_per_layer": round(M / (us * 1e-6), 1),
+                    "tops": round(ops / (us * 1e-6) / 1e12, 2),
+                    "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "bytes": nbytes, "ops": ops}
+        del chains, graph
+        torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -476,6 +554,11 @@ def main():
         sys.exit(1)
     wl = workloads.WORKLOADS[args.workload]
     M_pre = args.prefill_tokens or max(wl.token_counts)
+    if args.layer:
+        rec = layer_bench(torch, bl, wl, M_pre, args.rotate_bytes, max(1, args.steps // 10))
+        print(json.dumps({"metric": "BitLinear layer chain: us per layer (decode, prefill)",
+                          "workload": wl.key, "data": "synthetic", "n_gpus": 1, **rec}), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration(torch)     # first device work of the process (see summarize_pmc)
     setup = Setup(torch, bl, wl, M_pre, args.rotate_bytes)

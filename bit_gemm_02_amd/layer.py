@@ -63,7 +63,10 @@ class LayerWeights:
 class LayerChain:
     """Buffers and call tables for one layer at M tokens."""
 
-    def __init__(self, w: LayerWeights, M: int, eps: float = 1e-6, device: str = "cuda"):
+    def __init__(self, w: LayerWeights, M: int, eps: float = 1e-6, device: str = "cuda",
+                 like: Optional["LayerChain"] = None):
+        """`like`: another chain of the same shapes whose buffers this one shares (layers run
+        one after another, so a stack of layers needs one set of activation buffers)."""
         if "o" not in w.packed or "up" not in w.packed or "down" not in w.packed:
             raise ValueError("a layer needs o, up and down projections")
         glu = w.act in (ACT_SWIGLU, ACT_RELU2_GLU)
@@ -75,7 +78,16 @@ class LayerChain:
             raise ValueError("inconsistent layer shapes")
         self.w, self.M, self.eps = w, M, eps
         f32, i8 = torch.float32, torch.int8
-        t = lambda *shape, dt=f32: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+        pool = {} if like is None else like._pool
+        self._pool = pool
+        counter = iter(range(1 << 30))
+
+        def t(*shape, dt=f32):
+            key = (next(counter), shape, dt)
+            if key not in pool:
+                pool[key] = torch.empty(shape, dtype=dt, device=device)
+            return pool[key]
+
         self.x = t(M, d)                       # layer input (caller fills)
         self.attn = t(M, w.K("o"))             # attention output (caller fills)
         self.xq, self.xs = t(M, d, dt=i8), t(M)

@@ -63,6 +63,7 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_gain: float = 20.0
     decode_prepacked: bool = True  # token counts <= 16 use weights packed once, outside timing
+    ffn: str = "swiglu"  # FFN activation of the layer the set belongs to: swiglu or relu2 (ungated)
 
 
 WORKLOADS = {
@@ -83,7 +84,8 @@ WORKLOADS = {
         description="1.4B edge shape with pre-ternarized packed weights, 1 / 8 / 512 tokens",
         matrices=(Matrix("up", 4096, 1536), Matrix("down", 1536, 4096),
                   Matrix("qkv", 2560, 1536), Matrix("o", 1536, 1536)),
-        token_counts=(1, 8, 512), weights="codes", x_dtype="f32", outlier_frac=0.01),
+        token_counts=(1, 8, 512), weights="codes", x_dtype="f32", outlier_frac=0.01,
+        ffn="relu2"),
     "c4_qwen3_1p7b_subln": Workload(
         key="c4_qwen3_1p7b_subln", index=3,
         description="Qwen3-1.7B-shaped SubLN block, 4096 tokens, bf16 activations",
