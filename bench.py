@@ -513,7 +513,7 @@ def layer_bench(torch, bl, wl: workloads.Workload, M_pre: int, rotate_bytes: flo
         nbytes = (w_bytes + 4 * len(base) + sum(4 * g.numel() for g in norms.values())
                   + 4 * M * (2 * d + c0.attn.shape[1]))
         key = "decode" if M == 1 else "prefill"
-        out[key] = {"tokens": M, "us_per_layer": round(us, 3), "launches_per_layer": 6,
+        out[key] = {"tokens": M, "us_per_layer": round(us, 3), "launches_per_layer": len(c0._calls),
                     "tokens_per_s_per_layer": round(M / (us * 1e-6), 1),
                     "tops": round(ops / (us * 1e-6) / 1e12, 2),
                     "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),

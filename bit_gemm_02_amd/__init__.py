@@ -86,6 +86,16 @@ class _ForwardExProblem(ctypes.Structure):
                 ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
+class _LinearExProblem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("W2_packed", ctypes.c_void_p), ("gamma2", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("x_dtype", ctypes.c_int), ("act", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -130,6 +140,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_quantize_acts_ex_grouped.restype = ctypes.c_int
     L.bitlinear_forward_ex_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_forward_ex_grouped.restype = ctypes.c_int
+    L.bitlinear_linear_ex_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_linear_ex_grouped.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -398,3 +410,35 @@ def forward_ex_grouped(problems: Sequence[dict], stream=None) -> None:
     _check("bitlinear_forward_ex_grouped",
            lib().bitlinear_forward_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
 
+
+def linear_ex_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_linear_ex_grouped: dicts as for linear_grouped plus the
+    optional W2_packed / gamma2 (the up projection of a gated pair), act (ACT_*) and an fp32
+    residual [M, N]."""
+    arr = (_LinearExProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        N = p["W_packed"].shape[0]
+        W2 = p.get("W2_packed")
+        if W2 is not None and tuple(W2.shape) != tuple(p["W_packed"].shape):
+            raise ValueError(f"W2_packed[{i}] must have the shape of W_packed")
+        R = p.get("residual")
+        if R is not None:
+            _dev(R, f"residual[{i}]", torch.float32)
+            if tuple(R.shape) != (M, N):
+                raise ValueError(f"residual[{i}] must be [M, N]")
+        arr[i] = _LinearExProblem(_ptr(X), _ptr(p.get("norm_weight")), _ptr(p["W_packed"]),
+                                  _ptr(p["gamma"]), _ptr(W2), _ptr(p.get("gamma2")), _ptr(p["Y"]),
+                                  _ptr(R), _ptr(p.get("X_q")), _ptr(p.get("x_scale")), M, N, K,
+                                  _x_dtype(X), int(p.get("act", ACT_NONE)), float(p.get("eps", 1e-6)))
+    return arr
+
+
+def linear_ex_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Decode-sized layer calls with the output stages in the epilogue (gated-pair
+    activation, ReLU^2, residual); outputs preallocated.  Every call must fit the fused form
+    (linear_fused(M, K))."""
+    arr = linear_ex_table(problems)
+    _check("bitlinear_linear_ex_grouped",
+           lib().bitlinear_linear_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))

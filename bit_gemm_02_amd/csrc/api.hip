@@ -191,6 +191,36 @@ bl_status check_linear(const bl_linear_problem &p)
     return BL_OK;
 }
 
+bl_status check_linear_ex(const bl_linear_ex_problem &p)
+{
+    bl_linear_problem base{p.X, p.norm_weight, p.W_packed, p.gamma, p.Y, p.X_q, p.x_scale,
+                           p.M, p.N, p.K, p.x_dtype, p.eps};
+    const bool empty = p.M == 0 || p.N == 0;
+    if (!empty && !linear_fused(base))
+        return BL_ERR_SHAPE;       // only the fused form exists
+    bl_status s = check_linear(base);
+    if (s != BL_OK)
+        return s;
+    if (p.act < BL_ACT_NONE || p.act > BL_ACT_RELU2)
+        return BL_ERR_DTYPE;
+    const bool glu = p.act == BL_ACT_SWIGLU || p.act == BL_ACT_RELU2_GLU;
+    if (glu && (!p.gamma2 || (!empty && !p.W2_packed)))
+        return BL_ERR_NULL;
+    if (!glu && p.W2_packed)
+        return BL_ERR_DTYPE;
+    if (!aligned16(p.W2_packed) || (reinterpret_cast<uintptr_t>(p.gamma2) & 3u) ||
+        (reinterpret_cast<uintptr_t>(p.residual) & 3u))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_linear_ex_problem to_ex(const bl_linear_problem &p)
+{
+    return bl_linear_ex_problem{p.X, p.norm_weight, p.W_packed, p.gamma, nullptr, nullptr,
+                                p.Y, nullptr, p.X_q, p.x_scale, p.M, p.N, p.K, p.x_dtype,
+                                BL_ACT_NONE, p.eps};
+}
+
 }  // namespace
 
 extern "C" {
@@ -358,7 +388,7 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
         return BL_ERR_NULL;
     if (count <= 0 || count > BL_MAX_GROUP)
         return BL_ERR_COUNT;
-    bl_linear_problem fused[BL_MAX_GROUP];
+    bl_linear_ex_problem fused[BL_MAX_GROUP];
     bl_act_ex_problem act[BL_MAX_GROUP];
     bl_forward_ex_problem fwd[BL_MAX_GROUP];
     int nf = 0, nt = 0;
@@ -371,7 +401,7 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
         if (p.M == 0 || p.N == 0)
             continue;
         if (linear_fused(p)) {
-            fused[nf++] = p;
+            fused[nf++] = to_ex(p);
             blocks += (p.N + 15) / 16;
         } else {
             act[nt] = bl_act_ex_problem{p.X, nullptr, p.norm_weight, p.X_q, p.x_scale, p.M, p.K,
@@ -396,6 +426,25 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
         return run_forward(fwd, nt, stream);
     }
     return BL_OK;
+}
+
+bl_status bitlinear_linear_ex_grouped(const bl_linear_ex_problem *problems, int count,
+                                      void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_linear_ex(problems[i]);
+        if (s != BL_OK)
+            return s;
+        blocks += (problems[i].N + 15) / 16;
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_linear_decode(problems, count, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -174,6 +174,30 @@ __device__ __forceinline__ float act_scale(float a, double ss, int K, float eps,
     return (float)((double)a * r / 127.0);
 }
 
+// FFN activation (the down projection's input): h = act(x, x2) evaluated in fp64 from the
+// fp32 inputs, rounded to fp32 once (SwiGLU: silu(x) * x2 with
+// silu(g) = g / (1 + exp(-g)); gated ReLU^2: relu(x)^2 * x2; ReLU^2: relu(x)^2).
+__device__ __forceinline__ float ffn_act(int kind, float x, float x2)
+{
+    double v;
+    if (kind == BL_ACT_SWIGLU) {
+        v = ((double)x / (1.0 + exp(-(double)x))) * (double)x2;
+    } else if (kind == BL_ACT_RELU2_GLU) {
+        const double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r * (double)x2;
+    } else {
+        const double r = x > 0.0f ? (double)x : 0.0;
+        v = r * r;
+    }
+    return (float)v;
+}
+
+__device__ __forceinline__ float4 ffn_act4(int kind, float4 x, float4 x2)
+{
+    return make_float4(ffn_act(kind, x.x, x2.x), ffn_act(kind, x.y, x2.y),
+                       ffn_act(kind, x.z, x2.z), ffn_act(kind, x.w, x2.w));
+}
+
 // ----------------------------------------------------------------- launchers
 
 hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *workspace,
@@ -185,7 +209,7 @@ hipError_t launch_quantize_acts(const bl_act_ex_problem *p, int count, hipStream
 hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 // Fused decode form: every problem has M <= BL_LINEAR_FUSED_MAX_M and M * K within
 // BL_LINEAR_FUSED_MAX_BYTES.
-hipError_t launch_linear_decode(const bl_linear_problem *p, int count, hipStream_t stream);
+hipError_t launch_linear_decode(const bl_linear_ex_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.

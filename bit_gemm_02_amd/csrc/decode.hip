@@ -30,6 +30,7 @@ constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kSuperWords = 16;    // words per row per super-step
 constexpr int kDecXldsMaxM = BL_LINEAR_FUSED_MAX_M;       // activations staged in LDS for at
 constexpr int kDecXldsBytes = BL_LINEAR_FUSED_MAX_BYTES;  // most this many tokens and bytes
+constexpr int kDecCQ = 12;    // fused form, one token: quads per lane kept in registers
 
 struct FwdDev {
     const int8_t *Xq;
@@ -48,6 +49,10 @@ struct FwdDev {
     float *sx_out;
     float eps;
     int bf16;
+    // Layer-call epilogue (fused form): the up projection of a gated pair and the activation.
+    const uint32_t *W2;
+    const float *gamma2;
+    int act;
 };
 
 struct FwdBatch {
@@ -76,11 +81,16 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
 // quantizes its piece straight into the LDS operand buffer (the same quant4 / act_scale
 // arithmetic as the activation-quantization kernels).  The first block of a problem also
 // writes the codes and scales out when asked to.
-template <int RG, bool XLDS, bool QUANT, bool FULL_K>
+// PAIR (fused form only): a gated pair of projections with one set of activations; the
+// block's first RG/2 row groups are rows of W, the other RG/2 the same rows of W2, and the
+// epilogue combines the two outputs of each row through the activation.
+template <int RG, bool XLDS, bool QUANT, bool FULL_K, bool PAIR = false>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
     static_assert(!QUANT || XLDS, "the fused form stages codes in LDS");
-    constexpr int ROWS = 16 * RG;
+    static_assert(!PAIR || (QUANT && RG % 2 == 0), "pairs: fused form, even row groups");
+    constexpr int GN = PAIR ? RG / 2 : RG;    // row groups of output rows per block
+    constexpr int ROWS = 16 * GN;
     // Super-steps per chunk (two chunks of loads in flight).  Four per chunk measured slower:
     // the dead loads past a short wave's range cost more than the deeper queue gains.
     constexpr int kDecPF = 2;
@@ -105,6 +115,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     // Weight rows n0 .. n0+ROWS-1 (rows past N read as zero); tokens 0 .. M-1 (rows past M
     // read as zero: their offsets r * K + ... lie at or past M * K).
     const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * words, rows_bytes(n0, ROWS, p.N, row_bytes));
+    const rsrc_t wres2 = PAIR ? make_rsrc(p.W2 + (int64_t)n0 * words, rows_bytes(n0, ROWS, p.N, row_bytes))
+                              : wres;
     const rsrc_t xres = make_rsrc(p.Xq, (uint32_t)p.M * (uint32_t)p.K);
     const uint32_t wbase = (uint32_t)r * row_bytes;
     const uint32_t xbase = (uint32_t)r * p.K;
@@ -128,14 +140,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
             const bool live = (t0 + u) < t_end;
 #pragma unroll
             for (int q = 0; q < RG; ++q) {
-                const uint32_t rowoff = wbase + (uint32_t)q * gstride;
+                const bool second = PAIR && q >= GN;
+                const rsrc_t res = second ? wres2 : wres;
+                const uint32_t rowoff = wbase + (uint32_t)(second ? q - GN : q) * gstride;
                 if (FULL_K) {
-                    c.w[u][q] = buf_load16(wres, live ? rowoff + 4u * w : kOOB);
+                    c.w[u][q] = buf_load16(res, live ? rowoff + 4u * w : kOOB);
                 } else {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const bool ok = live && (w + j) < words;
-                        c.w[u][q][j] = buf_load4(wres, ok ? rowoff + 4u * (w + j) : kOOB);
+                        c.w[u][q][j] = buf_load4(res, ok ? rowoff + 4u * (w + j) : kOOB);
                     }
                 }
             }
@@ -182,6 +196,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     for (int v = 0; v < 4; ++v)
         sxv[v] = QUANT ? 0.0f : __uint_as_float(buf_load4(sres, (uint32_t)(4 * g + v) * 4u));
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    const float gamma2f = PAIR ? __uint_as_float(buf_load4(make_rsrc(p.gamma2, 4u), 0u)) : 0.0f;
     __builtin_amdgcn_sched_barrier(0);
 
     // Two chunks of weight loads in flight from the start; then the activation piece is
@@ -215,46 +230,104 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
                                __uint_as_float(v.w));
         };
         // Partial absmax of u (u = x, or fl32(x * g)) and sum of x^2 over this wave's piece.
+        // One token whose piece takes 3 to kDecCQ quads per lane: every load issued at once
+        // and u kept in registers for the quantization pass (the same per-lane order of the
+        // sums: quads past the piece read as zeros and add nothing).  Otherwise one quad per
+        // lane at a time, re-read for the quantization pass (measured faster for short
+        // pieces).
+        const bool cached = p.M == 1 && quads > 2 * kWave && quads <= kDecCQ * kWave;
+        const bool first = (int)blockIdx.x == p.block_begin;
+        float4 uc[kDecCQ];
+        if (cached) {
+            const rsrc_t xr = row(0);
+            float4 xc[kDecCQ];
 #pragma unroll
-        for (int m = 0; m < kDecXldsMaxM; ++m) {
-            if (m < p.M) {
-                const rsrc_t xr = row(m);
-                float amax = 0.0f;
-                double ss = 0.0;
-                for (int q = lane; q < quads; q += kWave) {
-                    const int j = e0 / 4 + q;
-                    const float4 f = load_quad(xr, j, bf16);
-                    const float4 u = norm ? mul4(f, quad_g(j)) : f;
-                    amax = fmaxf(amax, absmax4(u));
-                    if (norm)
-                        ss = sumsq4(ss, f);
+            for (int c = 0; c < kDecCQ; ++c) {
+                const int q = lane + c * kWave;
+                const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);   // past: zeros
+                if (c * kWave < quads) {       // wave-uniform: no loads past the piece
+                    xc[c] = load_quad(xr, j, bf16);
+                    uc[c] = norm ? quad_g(j) : xc[c];
+                } else {
+                    xc[c] = uc[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
-                amax = wave_max(amax);
-                ss = wave_sum_fixed(ss);
-                if (lane == 0) {
-                    q_amax[wave][m] = amax;
-                    q_ss[wave][m] = ss;
+            }
+            float amax = 0.0f;
+            double ss = 0.0;
+#pragma unroll
+            for (int c = 0; c < kDecCQ; ++c) {
+                if (norm) {
+                    uc[c] = mul4(xc[c], uc[c]);
+                    ss = sumsq4(ss, xc[c]);
+                }
+                amax = fmaxf(amax, absmax4(uc[c]));
+            }
+            amax = wave_max(amax);
+            ss = wave_sum_fixed(ss);
+            if (lane == 0) {
+                q_amax[wave][0] = amax;
+                q_ss[wave][0] = ss;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kDecXldsMaxM; ++m) {
+                if (m < p.M) {
+                    const rsrc_t xr = row(m);
+                    float amax = 0.0f;
+                    double ss = 0.0;
+                    for (int q = lane; q < quads; q += kWave) {
+                        const int j = e0 / 4 + q;
+                        const float4 f = load_quad(xr, j, bf16);
+                        const float4 u = norm ? mul4(f, quad_g(j)) : f;
+                        amax = fmaxf(amax, absmax4(u));
+                        if (norm)
+                            ss = sumsq4(ss, f);
+                    }
+                    amax = wave_max(amax);
+                    ss = wave_sum_fixed(ss);
+                    if (lane == 0) {
+                        q_amax[wave][m] = amax;
+                        q_ss[wave][m] = ss;
+                    }
                 }
             }
         }
         __syncthreads();
-        const bool first = (int)blockIdx.x == p.block_begin;
+        if (cached) {
+            float a = q_amax[0][0];
 #pragma unroll
-        for (int m = 0; m < kDecXldsMaxM; ++m) {
-            if (m < p.M) {
-                float a = q_amax[0][m];
+            for (int w = 1; w < kDecWaves; ++w)
+                a = fmaxf(a, q_amax[w][0]);
+            const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
 #pragma unroll
-                for (int w = 1; w < kDecWaves; ++w)
-                    a = fmaxf(a, q_amax[w][m]);
-                const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
-                const rsrc_t xr = row(m);
-                for (int q = lane; q < quads; q += kWave) {
+            for (int c = 0; c < kDecCQ; ++c) {
+                const int q = lane + c * kWave;
+                if (q < quads) {
                     const int j = e0 / 4 + q;
-                    const float4 f = load_quad(xr, j, bf16);
-                    const char4 c = quant4(norm ? mul4(f, quad_g(j)) : f, inv);
-                    *reinterpret_cast<char4 *>(xs + (uint32_t)m * p.K + 4u * j) = c;
+                    const char4 cq = quant4(uc[c], inv);
+                    *reinterpret_cast<char4 *>(xs + 4u * j) = cq;
                     if (first && p.Xq_out)
-                        *reinterpret_cast<char4 *>(p.Xq_out + (int64_t)m * p.K + 4 * j) = c;
+                        *reinterpret_cast<char4 *>(p.Xq_out + 4 * j) = cq;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kDecXldsMaxM; ++m) {
+                if (m < p.M) {
+                    float a = q_amax[0][m];
+#pragma unroll
+                    for (int w = 1; w < kDecWaves; ++w)
+                        a = fmaxf(a, q_amax[w][m]);
+                    const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
+                    const rsrc_t xr = row(m);
+                    for (int q = lane; q < quads; q += kWave) {
+                        const int j = e0 / 4 + q;
+                        const float4 f = load_quad(xr, j, bf16);
+                        const char4 c = quant4(norm ? mul4(f, quad_g(j)) : f, inv);
+                        *reinterpret_cast<char4 *>(xs + (uint32_t)m * p.K + 4u * j) = c;
+                        if (first && p.Xq_out)
+                            *reinterpret_cast<char4 *>(p.Xq_out + (int64_t)m * p.K + 4 * j) = c;
+                    }
                 }
             }
         }
@@ -311,12 +384,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     for (int q = 0; q < RG; ++q)
         red[wave][q][lane] = acc[q];
     __syncthreads();
-    if (wave >= RG)
+    if (wave >= GN)
         return;
     v4i s = red[0][wave][lane];
 #pragma unroll
     for (int w = 1; w < kDecWaves; ++w)
         s += red[w][wave][lane];
+    v4i s2 = v4i{0, 0, 0, 0};
+    if (PAIR) {
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w)
+            s2 += red[w][wave + GN][lane];
+    }
 
     // s holds 64 * D[m][n] for m = 4 * g + v (v = register index), n = n0 + 16 * wave + r.
     const int n = n0 + 16 * wave + r;
@@ -324,6 +403,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
         return;
     const double gamma = (double)gammaf;
     const int accv[4] = {s.x, s.y, s.z, s.w};
+    const int accv2[4] = {s2.x, s2.y, s2.z, s2.w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
@@ -331,16 +411,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
             const int a = accv[v] >> 6;  // exact: the sum is a multiple of 64
             const double scale = gamma * (double)sxv[v];
             float y = (float)((double)a * scale);
+            if (PAIR) {
+                const float y2 = (float)((double)(accv2[v] >> 6) * ((double)gamma2f * (double)sxv[v]));
+                y = ffn_act(p.act, y, y2);
+            } else if (QUANT && p.act != BL_ACT_NONE) {
+                y = ffn_act(p.act, y, 0.0f);
+            }
             if (p.R)
                 y = y + p.R[(int64_t)m * p.N + n];
             p.Y[(int64_t)m * p.N + n] = y;
-            if (p.acc)
+            if (!QUANT && p.acc)
                 p.acc[(int64_t)m * p.N + n] = a;
         }
     }
 }
 
-template <int RG, bool XLDS, bool QUANT = false>
+template <int RG, bool XLDS, bool QUANT = false, bool PAIR = false>
 static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t stream)
 {
     if (blocks == 0)
@@ -350,11 +436,11 @@ static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t
         for (int i = 0; i < b.count; ++i)
             lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
     if (full_k)
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true>), dim3(blocks), dim3(kDecThreads),
-                           lds, stream, b);
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true, PAIR>), dim3(blocks),
+                           dim3(kDecThreads), lds, stream, b);
     else
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, false>), dim3(blocks), dim3(kDecThreads),
-                           lds, stream, b);
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, false, PAIR>), dim3(blocks),
+                           dim3(kDecThreads), lds, stream, b);
     return hipGetLastError();
 }
 
@@ -413,28 +499,30 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *q, int count, hipS
 }
 
 // The fused decode form: every problem has M <= 4 and M * K <= the LDS budget (checked by
-// the caller).  Longest K first, one launch.  Every block quantizes the token rows it needs
-// from the raw activations, so larger blocks (more row groups) read them fewer times: row
-// groups as in the unfused decode launch.
-template <int RG>
-static hipError_t launch_linear_rg(const bl_linear_problem *q, int count, hipStream_t stream)
+// the caller).  Longest K first, one launch per kind (single projections, gated pairs).
+// Every block quantizes the token rows it needs from the raw activations, so larger blocks
+// (more row groups) read them fewer times: row groups as in the unfused decode launch, by
+// weight rows (a pair's block holds both projections' rows).
+template <int RG, bool PAIR>
+static hipError_t launch_linear_rg(const bl_linear_ex_problem *const *q, int count,
+                                   hipStream_t stream)
 {
+    constexpr int ROWS = 16 * (PAIR ? RG / 2 : RG);
     int order[BL_MAX_GROUP];
-    int m = 0;
     for (int i = 0; i < count; ++i)
-        if (q[i].M > 0 && q[i].N > 0)
-            order[m++] = i;
-    std::stable_sort(order, order + m, [&](int a, int c) { return q[a].K > q[c].K; });
+        order[i] = i;
+    std::stable_sort(order, order + count, [&](int a, int c) { return q[a]->K > q[c]->K; });
     FwdBatch b{};
     int blocks = 0;
     bool full_k = true;
-    for (int o = 0; o < m; ++o) {
-        const bl_linear_problem &s = q[order[o]];
+    for (int o = 0; o < count; ++o) {
+        const bl_linear_ex_problem &s = *q[order[o]];
         full_k = full_k && (s.K % 256 == 0);
         FwdDev &d = b.p[o];
         d.W = s.W_packed;
         d.gamma = s.gamma;
         d.Y = s.Y;
+        d.R = s.residual;
         d.M = (int)s.M;
         d.N = (int)s.N;
         d.K = (int)s.K;
@@ -445,23 +533,49 @@ static hipError_t launch_linear_rg(const bl_linear_problem *q, int count, hipStr
         d.sx_out = s.x_scale;
         d.eps = s.eps;
         d.bf16 = s.x_dtype == BL_BF16;
-        blocks += (d.N + 16 * RG - 1) / (16 * RG);
+        d.W2 = s.W2_packed;
+        d.gamma2 = s.gamma2;
+        d.act = s.act;
+        blocks += (d.N + ROWS - 1) / ROWS;
     }
-    b.count = m;
-    return launch_batch<RG, true, true>(b, blocks, full_k, stream);
+    b.count = count;
+    return launch_batch<RG, true, true, PAIR>(b, blocks, full_k, stream);
 }
 
-hipError_t launch_linear_decode(const bl_linear_problem *q, int count, hipStream_t stream)
+hipError_t launch_linear_decode(const bl_linear_ex_problem *q, int count, hipStream_t stream)
 {
-    int64_t rows = 0;
-    for (int i = 0; i < count; ++i)
-        if (q[i].M > 0)
-            rows += q[i].N;
-    if (rows >= 256 * 64)
-        return launch_linear_rg<4>(q, count, stream);
-    if (rows >= 256 * 32)
-        return launch_linear_rg<2>(q, count, stream);
-    return launch_linear_rg<1>(q, count, stream);
+    const bl_linear_ex_problem *single[BL_MAX_GROUP], *pair[BL_MAX_GROUP];
+    int ns = 0, np = 0;
+    int64_t rows_s = 0, rows_p = 0;
+    for (int i = 0; i < count; ++i) {
+        if (q[i].M == 0 || q[i].N == 0)
+            continue;
+        if (q[i].W2_packed) {
+            pair[np++] = &q[i];
+            rows_p += 2 * q[i].N;
+        } else {
+            single[ns++] = &q[i];
+            rows_s += q[i].N;
+        }
+    }
+    hipError_t e = hipSuccess;
+    if (ns) {
+        if (rows_s >= 256 * 64)
+            e = launch_linear_rg<4, false>(single, ns, stream);
+        else if (rows_s >= 256 * 32)
+            e = launch_linear_rg<2, false>(single, ns, stream);
+        else
+            e = launch_linear_rg<1, false>(single, ns, stream);
+        if (e != hipSuccess)
+            return e;
+    }
+    if (np) {
+        if (rows_p >= 256 * 64)
+            e = launch_linear_rg<4, true>(pair, np, stream);
+        else
+            e = launch_linear_rg<2, true>(pair, np, stream);
+    }
+    return e;
 }
 
 }  // namespace bl

@@ -575,34 +575,10 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
         write_scale(p, m, a, sum, norm);
 }
 
-// FFN activation in front of the down projection's quantization: h = act(x, x2) evaluated in
-// fp64 from the fp32 inputs, rounded to fp32 once (SwiGLU: silu(x) * x2 with
-// silu(g) = g / (1 + exp(-g)); gated ReLU^2: relu(x)^2 * x2; ReLU^2: relu(x)^2).
-__device__ __forceinline__ float ffn_act(int kind, float x, float x2)
-{
-    double v;
-    if (kind == BL_ACT_SWIGLU) {
-        v = ((double)x / (1.0 + exp(-(double)x))) * (double)x2;
-    } else if (kind == BL_ACT_RELU2_GLU) {
-        const double r = x > 0.0f ? (double)x : 0.0;
-        v = r * r * (double)x2;
-    } else {
-        const double r = x > 0.0f ? (double)x : 0.0;
-        v = r * r;
-    }
-    return (float)v;
-}
-
-__device__ __forceinline__ float4 ffn_act4(int kind, float4 x, float4 x2)
-{
-    return make_float4(ffn_act(kind, x.x, x2.x), ffn_act(kind, x.y, x2.y),
-                       ffn_act(kind, x.z, x2.z), ffn_act(kind, x.w, x2.w));
-}
-
 // One block per token row of an FFN hidden state: h = act(gate, up) from two fp32 rows, then
 // the same absmax (+ SubLN over h) quantization as the block kernel.  The first C groups of
-// four per thread of both inputs stay in registers; h is recomputed for the second pass
-// (deterministic, the same value).
+// four per thread of h stay in registers between the two passes (the activation is evaluated
+// once per element there); groups past them are re-read and re-evaluated (the same value).
 template <int C>
 __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
 {
@@ -622,35 +598,41 @@ __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
         return make_float4(__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z),
                            __uint_as_float(r.w));
     };
-    auto absmax_group = [&](const v4u &r, const v4u &r2, int j, float &amax, double &ss) {
-        const float4 h = ffn_act4(kind, f4(r), f4(r2));
+    auto h_at = [&](int j) {
+        return ffn_act4(kind, f4(buf_load16(xr, (uint32_t)j * 16u)), f4(buf_load16(x2r, (uint32_t)j * 16u)));
+    };
+    auto absmax_group = [&](const float4 &h, int j, float &amax, double &ss) {
         const float4 u = norm ? mul4(h, load_g(gr, j < groups ? j : (int)(kOOB / 16u))) : h;
         amax = fmaxf(amax, absmax4(u));
         if (norm)
             ss = sumsq4(ss, h);
     };
-    auto quant_group = [&](const v4u &r, const v4u &r2, int j, float inv) {
-        const float4 h = ffn_act4(kind, f4(r), f4(r2));
+    auto quant_group = [&](const float4 &h, int j, float inv) {
         reinterpret_cast<char4 *>(p.Xq + (int64_t)m * p.K)[j] =
             quant4(norm ? mul4(h, load_g(gr, j)) : h, inv);
     };
 
-    v4u raw[C], raw2[C];
+    float4 h[C];
+    {
+        v4u raw[C], raw2[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int j = c * kActThreads + tid;
-        const uint32_t off = j < groups ? (uint32_t)j * 16u : kOOB;
-        raw[c] = buf_load16(xr, off);
-        raw2[c] = buf_load16(x2r, off);
+        for (int c = 0; c < C; ++c) {
+            const int j = c * kActThreads + tid;
+            const uint32_t off = j < groups ? (uint32_t)j * 16u : kOOB;
+            raw[c] = buf_load16(xr, off);
+            raw2[c] = buf_load16(x2r, off);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            h[c] = ffn_act4(kind, f4(raw[c]), f4(raw2[c]));   // zeros past the row: h = 0
     }
     float amax = 0.0f;
     double ss = 0.0;
 #pragma unroll
     for (int c = 0; c < C; ++c)
-        absmax_group(raw[c], raw2[c], c * kActThreads + tid, amax, ss);
+        absmax_group(h[c], c * kActThreads + tid, amax, ss);
     for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
-        absmax_group(buf_load16(xr, (uint32_t)j * 16u), buf_load16(x2r, (uint32_t)j * 16u), j,
-                     amax, ss);
+        absmax_group(h_at(j), j, amax, ss);
 
     amax = wave_max(amax);
     if (norm)
@@ -674,10 +656,10 @@ __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
     for (int c = 0; c < C; ++c) {
         const int j = c * kActThreads + tid;
         if (j < groups)
-            quant_group(raw[c], raw2[c], j, inv);
+            quant_group(h[c], j, inv);
     }
     for (int j = C * kActThreads + tid; j < groups; j += kActThreads)
-        quant_group(buf_load16(xr, (uint32_t)j * 16u), buf_load16(x2r, (uint32_t)j * 16u), j, inv);
+        quant_group(h_at(j), j, inv);
     if (tid == 0)
         write_scale(p, m, a, sum, norm);
 }

@@ -20,6 +20,19 @@ Qwen3-shaped layer sets use SwiGLU):
 Six launches per layer, no host synchronization; the call sequence can be captured into a
 HIP graph.  Argument marshalling only: the tables of device pointers are built once per
 (weights, buffers) pair and each call hands them to the C entry points.
+
+At decode sizes (every input of the layer fits the fused form: M <= 4 tokens and M * K
+within the LDS budget) the same sub-graph takes three launches of the fused layer call, each
+product quantizing its own input rows:
+
+  L1  q, k, v from x (input RMSNorm); o from the attention output (SubLN) + residual -> x1
+  L2  gate and up from x1 (FFN RMSNorm) as one gated pair: h = act(gate, up) in the epilogue
+      (ReLU^2 of up alone for the ungated kind)
+  L3  down from h (SubLN) + residual x1 -> out
+
+Every intermediate value is the one the six-launch form computes (the same codes, scales,
+fp32 products and activation), so the two forms agree element for element up to the fixed
+order of the norms' sums of squares.
 """
 
 from __future__ import annotations
@@ -31,7 +44,7 @@ from typing import Dict, List, Optional
 import torch
 
 from . import (ACT_NONE, ACT_RELU2, ACT_RELU2_GLU, ACT_SWIGLU, _check, _stream, act_ex_table,
-               forward_ex_table, lib)
+               forward_ex_table, lib, linear_ex_table, linear_fused)
 
 ATTN_IN = ("q", "k", "v", "qkv")
 
@@ -64,9 +77,13 @@ class LayerChain:
     """Buffers and call tables for one layer at M tokens."""
 
     def __init__(self, w: LayerWeights, M: int, eps: float = 1e-6, device: str = "cuda",
-                 like: Optional["LayerChain"] = None):
+                 like: Optional["LayerChain"] = None, fused: Optional[bool] = None,
+                 keep_codes: bool = False):
         """`like`: another chain of the same shapes whose buffers this one shares (layers run
-        one after another, so a stack of layers needs one set of activation buffers)."""
+        one after another, so a stack of layers needs one set of activation buffers).
+        `fused`: the three-launch decode form (default: whenever every input fits it).
+        `keep_codes`: in the fused form, also write the codes and scales each product used
+        (xq/xs, aq/as_, fq/fs, hq/hs; the six-launch form always has them)."""
         if "o" not in w.packed or "up" not in w.packed or "down" not in w.packed:
             raise ValueError("a layer needs o, up and down projections")
         glu = w.act in (ACT_SWIGLU, ACT_RELU2_GLU)
@@ -77,6 +94,10 @@ class LayerChain:
                 or w.K("up") != d or (glu and (w.K("gate") != d or w.N("gate") != w.N("up"))):
             raise ValueError("inconsistent layer shapes")
         self.w, self.M, self.eps = w, M, eps
+        fits = all(linear_fused(M, k) for k in (d, w.K("o"), w.K("down")))
+        self.fused = fits if fused is None else fused
+        if self.fused and not fits:
+            raise ValueError("the fused form needs M <= 4 and M * K within its LDS budget")
         f32, i8 = torch.float32, torch.int8
         pool = {} if like is None else like._pool
         self._pool = pool
@@ -95,11 +116,20 @@ class LayerChain:
         self.y = {n: t(M, w.N(n)) for n in w.attn_in}
         self.x1 = t(M, d)
         self.fq, self.fs = t(M, d, dt=i8), t(M)
-        self.gate = t(M, w.N("gate")) if glu else None
-        self.up = t(M, w.N("up"))
+        if self.fused:
+            self.gate = self.up = None
+            self.h = t(M, w.N("up"))           # FFN hidden state act(gate, up)
+        else:
+            self.gate = t(M, w.N("gate")) if glu else None
+            self.up = t(M, w.N("up"))
+            self.h = None
         self.hq, self.hs = t(M, w.K("down"), dt=i8), t(M)
         self.out = t(M, d)
         nrm = w.norms.get
+        L = lib()
+        if self.fused:
+            self._build_fused(nrm, glu, keep_codes, L)
+            return
         self._a1 = [dict(X=self.x, X_q=self.xq, x_scale=self.xs, norm_weight=nrm("attn"), eps=eps),
                     dict(X=self.attn, X_q=self.aq, x_scale=self.as_, norm_weight=nrm("o"), eps=eps)]
         if not w.attn_in:
@@ -117,7 +147,6 @@ class LayerChain:
                    X_q=self.hq, x_scale=self.hs, norm_weight=nrm("down"), eps=eps)]
         p3 = [dict(X_q=self.hq, x_scale=self.hs, W_packed=w.packed["down"], gamma=w.gamma["down"],
                    Y=self.out, residual=self.x1)]
-        L = lib()
         self._calls = [
             (L.bitlinear_quantize_acts_ex_grouped, act_ex_table(self._a1), len(self._a1)),
             (L.bitlinear_forward_ex_grouped, forward_ex_table(p1), len(p1)),
@@ -126,6 +155,29 @@ class LayerChain:
             (L.bitlinear_quantize_acts_ex_grouped, act_ex_table(a3), 1),
             (L.bitlinear_forward_ex_grouped, forward_ex_table(p3), 1),
         ]
+        self._addr = [ctypes.addressof(arr) for _, arr, _ in self._calls]
+
+    def _build_fused(self, nrm, glu, keep, L):
+        w, eps = self.w, self.eps
+
+        def codes(q, s):
+            return dict(X_q=q, x_scale=s) if keep else {}
+
+        l1 = [dict(X=self.x, norm_weight=nrm("attn"), eps=eps, W_packed=w.packed[n], gamma=w.gamma[n],
+                   Y=self.y[n], **(codes(self.xq, self.xs) if i == 0 else {}))
+              for i, n in enumerate(w.attn_in)]
+        l1.append(dict(X=self.attn, norm_weight=nrm("o"), eps=eps, W_packed=w.packed["o"],
+                       gamma=w.gamma["o"], Y=self.x1, residual=self.x, **codes(self.aq, self.as_)))
+        if glu:
+            l2 = [dict(X=self.x1, norm_weight=nrm("ffn"), eps=eps, W_packed=w.packed["gate"],
+                       gamma=w.gamma["gate"], W2_packed=w.packed["up"], gamma2=w.gamma["up"],
+                       act=w.act, Y=self.h, **codes(self.fq, self.fs))]
+        else:
+            l2 = [dict(X=self.x1, norm_weight=nrm("ffn"), eps=eps, W_packed=w.packed["up"],
+                       gamma=w.gamma["up"], act=w.act, Y=self.h, **codes(self.fq, self.fs))]
+        l3 = [dict(X=self.h, norm_weight=nrm("down"), eps=eps, W_packed=w.packed["down"],
+                   gamma=w.gamma["down"], Y=self.out, residual=self.x1, **codes(self.hq, self.hs))]
+        self._calls = [(L.bitlinear_linear_ex_grouped, linear_ex_table(c), len(c)) for c in (l1, l2, l3)]
         self._addr = [ctypes.addressof(arr) for _, arr, _ in self._calls]
 
     def __call__(self, stream=None) -> torch.Tensor:

@@ -305,6 +305,55 @@ typedef struct {
 bl_status bitlinear_forward_ex_grouped(const bl_forward_ex_problem *problems, int count,
                                        void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * (3) The decode form of a layer's product calls: bitlinear_linear_grouped's fused call
+ *     (activation quantization inside the product) with the layer's output stages in the
+ *     epilogue, so that a layer's BitLinear sub-graph at a few tokens takes three launches
+ *     (attention projections, FFN gate/up, FFN down) instead of six.
+ *
+ *   X, x_dtype, norm_weight, eps, X_q, x_scale   as for bl_linear_problem.
+ *   W_packed, gamma    the projection (or the gate projection of a gated pair), [N][K/16].
+ *   W2_packed, gamma2  the up projection of a gated pair ([N][K/16], the same codes layout),
+ *                      or NULL for a single projection.
+ *   act                BL_ACT_NONE or BL_ACT_RELU2 for a single projection; BL_ACT_SWIGLU or
+ *                      BL_ACT_RELU2_GLU for a gated pair.
+ *   residual           [M][N] fp32 added last, or NULL (may alias Y).
+ *   Y                  [M][N] fp32:
+ *     y1 = fl32(fp64(acc1 * gamma * x_scale[m]))   (the bitlinear_forward output)
+ *     y2 = fl32(fp64(acc2 * gamma2 * x_scale[m]))  (gated pairs: the up output)
+ *     h  = act(y1, y2) as in (1): fp64 evaluation from the fp32 inputs, one fp32 rounding
+ *          (BL_ACT_NONE: h = y1)
+ *     Y  = residual ? fl32(h + residual) : h
+ *   So Y equals bitlinear_forward of both projections followed by the activation (and the
+ *   residual add) element for element; only the fused form exists: every problem with
+ *   M > 0 and N > 0 needs M <= BL_LINEAR_FUSED_MAX_M and M * K <= BL_LINEAR_FUSED_MAX_BYTES.
+ *   M == 0 or N == 0 is a no-op.
+ * Errors: BL_ERR_NULL (X, W_packed, gamma or Y missing; W2_packed or gamma2 missing for a
+ * gated kind), BL_ERR_DTYPE (unknown x_dtype or act, a gated kind without a pair or a pair
+ * with a single kind), BL_ERR_SHAPE (as for bl_linear_problem, and sizes past the fused
+ * form), BL_ERR_ALIGN (16 bytes for X, W_packed, W2_packed, X_q, norm_weight; 4 bytes for
+ * the fp32 arrays).  Pair problems and single problems of one call take one launch each.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+    const void *X;
+    const float *norm_weight;
+    const uint32_t *W_packed;
+    const float *gamma;
+    const uint32_t *W2_packed;
+    const float *gamma2;
+    float *Y;
+    const float *residual;
+    int8_t *X_q;
+    float *x_scale;
+    int64_t M, N, K;
+    int x_dtype;
+    int act;
+    float eps;
+} bl_linear_ex_problem;
+
+bl_status bitlinear_linear_ex_grouped(const bl_linear_ex_problem *problems, int count,
+                                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,6 +214,43 @@ def test_chain_entry_points_validation(L, bl):
     assert fwd(M=0, residual=0x60000) == BL_OK
 
 
+def test_linear_ex_validation(L, bl):
+    g = L.bitlinear_linear_ex_grouped
+
+    def call(**kw):
+        d = dict(X=A, norm_weight=None, W_packed=B, gamma=C, W2_packed=None, gamma2=None, Y=D,
+                 residual=None, X_q=None, x_scale=None, M=1, N=4, K=64, x_dtype=0, act=0, eps=1e-6)
+        d.update(kw)
+        arr = (bl._LinearExProblem * 1)()
+        arr[0] = bl._LinearExProblem(**d)
+        return g(ctypes.addressof(arr), 1, None)
+
+    arr = (bl._LinearExProblem * 1)()
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert g(ctypes.addressof(arr), 0, None) == BL_ERR_COUNT
+    assert g(ctypes.addressof(arr), 17, None) == BL_ERR_COUNT
+    assert call(X=None) == BL_ERR_NULL
+    assert call(Y=None) == BL_ERR_NULL
+    assert call(act=5) == BL_ERR_DTYPE
+    assert call(act=-1) == BL_ERR_DTYPE
+    assert call(x_dtype=3) == BL_ERR_DTYPE
+    # Gated kinds need the pair; single kinds refuse one.
+    assert call(act=1) == BL_ERR_NULL
+    assert call(act=2, W2_packed=E) == BL_ERR_NULL
+    assert call(act=0, W2_packed=E, gamma2=C) == BL_ERR_DTYPE
+    assert call(act=3, W2_packed=E, gamma2=C) == BL_ERR_DTYPE
+    assert call(act=1, W2_packed=E + 4, gamma2=C) == BL_ERR_ALIGN
+    assert call(act=1, W2_packed=E, gamma2=C + 2) == BL_ERR_ALIGN
+    assert call(residual=E + 2) == BL_ERR_ALIGN
+    # Only the fused form exists.
+    assert call(M=5) == BL_ERR_SHAPE
+    assert call(M=2, K=32768) == BL_ERR_SHAPE
+    assert call(K=40) == BL_ERR_SHAPE
+    assert call(M=-1) == BL_ERR_SHAPE
+    assert call(M=0, act=1, gamma2=C) == BL_OK
+    assert call(N=0) == BL_OK
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):

@@ -9,7 +9,11 @@
   same codes and scales (vector and scalar store paths, decode and prefill, residual
   aliasing the output).
 * The whole chain of one layer (layer.py): every stage's output against the oracle run on the
-  GPU's own inputs to that stage, so a legal difference cannot cascade.
+  GPU's own inputs to that stage, so a legal difference cannot cascade.  At one and three
+  tokens the chain takes the three-launch fused form (gate/up pair with the activation in
+  the epilogue); its FFN hidden state h is checked against the oracle's activation of the
+  oracle's gate and up outputs on the GPU's codes and scales.  The two forms also agree with
+  each other on the same layer.
 """
 
 import numpy as np
@@ -175,7 +179,9 @@ LAYERS = [
 def test_layer_chain_stagewise(torch, bl, orc, d, F, names, act, M):
     from bit_gemm_02_amd.layer import LayerChain
     w, codes = make_layer(torch, bl, d, F, names, act, (M, act, d))
-    ch = LayerChain(w, M)
+    ch = LayerChain(w, M, keep_codes=True)
+    assert ch.fused == (M <= 4)
+    assert len(ch._calls) == (3 if ch.fused else 6)
     x = workloads.gaussian((M, d), (330, M, d), 1.0)
     a = workloads.gaussian((M, w.K("o")), (331, M, d), 1.0)
     ch.x.copy_(dev(torch, x))
@@ -204,16 +210,27 @@ def test_layer_chain_stagewise(torch, bl, orc, d, F, names, act, M):
     assert np.array_equal(host(ch.fq), q3), label
     check_scales(host(ch.fs), s3, True, label)
     up = orc.epilogue(orc.matmul(host(ch.fq), codes["up"]), host(ch.fs), gv["up"])
-    assert np.array_equal(host(ch.up), up), label
+    gate = None
     if "gate" in names:
         gate = orc.epilogue(orc.matmul(host(ch.fq), codes["gate"]), host(ch.fs), gv["gate"])
-        assert np.array_equal(host(ch.gate), gate), label
-        H = orc.ffn_act(act, host(ch.gate), host(ch.up))
+    if ch.fused:
+        # L2's epilogue: h = act(gate, up) from the pair's fp32 outputs.
+        H_ref = orc.ffn_act(act, gate, up) if gate is not None else orc.ffn_act(act, up)
+        H = host(ch.h)
+        check_hidden(H, H_ref, act, orc, label)
     else:
-        H = orc.ffn_act(act, host(ch.up))
-    # A3: FFN activation + SubLN on the GPU's gate/up.
+        assert np.array_equal(host(ch.up), up), label
+        if gate is not None:
+            assert np.array_equal(host(ch.gate), gate), label
+            H = orc.ffn_act(act, host(ch.gate), host(ch.up))
+        else:
+            H = orc.ffn_act(act, host(ch.up))
+    # A3 (or L3's quantization): FFN activation + SubLN.
     q4, s4 = orc.quantize_acts(H, nv["down"], 1e-6)
-    check_codes(host(ch.hq), q4, act, orc, label)
+    if ch.fused:
+        assert np.array_equal(host(ch.hq), q4), label     # quantization of the GPU's own h
+    else:
+        check_codes(host(ch.hq), q4, act, orc, label)
     check_scales(host(ch.hs), s4, True, label)
     # P3: down with the residual x1, on the GPU's codes.
     out = orc.epilogue_residual(orc.matmul(host(ch.hq), codes["down"]), host(ch.hs), gv["down"],
@@ -221,14 +238,59 @@ def test_layer_chain_stagewise(torch, bl, orc, d, F, names, act, M):
     assert np.array_equal(host(ch.out), out), label
 
 
-def test_layer_chain_graph_replay(torch, bl):
-    """The six launches captured in a HIP graph give the eager result on every replay, with
-    eager work and synchronizations between the replays."""
+def check_hidden(H, H_ref, kind, orc, label):
+    """h bit-exact, except SwiGLU's rare one-ulp differences (two libraries' fp64 exp)."""
+    if kind != orc.SWIGLU:
+        assert np.array_equal(H, H_ref), label
+        return
+    bad = H != H_ref
+    assert np.count_nonzero(bad) <= max(1, H.size // 100000), (label, np.count_nonzero(bad))
+    assert rel_err(H[bad], H_ref[bad]) <= 2.0 ** -23, label
+
+
+@pytest.mark.parametrize("d,F,names,act", LAYERS)
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_layer_chain_forms_agree(torch, bl, d, F, names, act, M):
+    """Three-launch and six-launch forms on the same layer and input: the same codes at
+    every stage and outputs within the last-bit differences of the norms' scales."""
     from bit_gemm_02_amd.layer import LayerChain
+    w, _ = make_layer(torch, bl, d, F, names, act, (M, act, d, 7))
+    fz = LayerChain(w, M, keep_codes=True)
+    sx = LayerChain(w, M, fused=False)
+    assert fz.fused and not sx.fused
+    x = dev(torch, workloads.gaussian((M, d), (332, M, d), 1.0))
+    a = dev(torch, workloads.gaussian((M, w.K("o")), (333, M, d), 1.0))
+    for ch in (fz, sx):
+        ch.x.copy_(x)
+        ch.attn.copy_(a)
+        ch()
+    torch.cuda.synchronize()
+    for name in ("xq", "aq", "fq", "hq"):
+        if name == "xq" and not w.attn_in:
+            continue
+        diff = np.count_nonzero(host(getattr(fz, name)) != host(getattr(sx, name)))
+        assert diff <= max(1, getattr(fz, name).numel() // 10000), (name, diff)
+    for name in ["x1", "out"] + [f"y:{n}" for n in w.attn_in]:
+        get = (lambda c: c.y[name[2:]]) if name.startswith("y:") else (lambda c: getattr(c, name))
+        A, B = host(get(fz)), host(get(sx))
+        scale = float(np.max(np.abs(B))) or 1.0
+        assert np.allclose(A, B, rtol=1e-4, atol=1e-4 * scale), name
+
+
+def test_layer_chain_graph_replay(torch, bl):
+    """The chain's launches (six; three in the fused form at two tokens) captured in a HIP
+    graph give the eager result on every replay, with eager work and synchronizations
+    between the replays."""
+    from bit_gemm_02_amd.layer import LayerChain
+    for M in (64, 2):
+        check_graph_replay(torch, bl, LayerChain, M)
+
+
+def check_graph_replay(torch, bl, LayerChain, M):
     w, _ = make_layer(torch, bl, 256, 512, ("q", "k", "v", "o", "gate", "up", "down"), 1, (9,))
-    ch = LayerChain(w, 64)
-    ch.x.copy_(dev(torch, workloads.gaussian((64, 256), (340,), 1.0)))
-    ch.attn.copy_(dev(torch, workloads.gaussian((64, 256), (341,), 1.0)))
+    ch = LayerChain(w, M)
+    ch.x.copy_(dev(torch, workloads.gaussian((M, 256), (340,), 1.0)))
+    ch.attn.copy_(dev(torch, workloads.gaussian((M, 256), (341,), 1.0)))
     ch()
     torch.cuda.synchronize()
     ref = ch.out.clone()

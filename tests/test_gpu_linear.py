@@ -1,5 +1,8 @@
 """The layer call (bitlinear_linear_grouped): steps 3 to 5 in one launch for decode-sized
-token counts, against the CPU oracle and against the two-call GPU path.
+token counts, against the CPU oracle and against the two-call GPU path.  Its layer form
+(bitlinear_linear_ex_grouped) adds the output stages: a gated pair's activation, ReLU^2 and
+the residual, checked against the oracle's activation (O7) and residual epilogue (O8) over
+the oracle's products on the codes and scales the call reports.
 
 Per call: codes and scales the product used (optional outputs) bit-exact / within 1e-6 of
 the oracle's activation quantization, Y within 1e-6 of the oracle epilogue over the oracle's
@@ -166,3 +169,98 @@ def test_linear_degenerate(torch, bl):
     empty = torch.empty((0, 512), dtype=torch.float32, device="cuda")
     bl.linear_grouped([dict(X=empty, W_packed=P, gamma=gamma, Y=torch.empty((0, 64), device="cuda"))])
     torch.cuda.synchronize()
+
+
+EX_SHAPES = [(1, 16, 16), (1, 300, 768), (2, 1000, 2048), (3, 129, 272), (4, 2048, 9728),
+             (1, 4100, 1536)]
+
+
+def ex_reference(orc, call, ref, C2, gamma2, kind, R):
+    """Y from the oracle on the call's reported codes and scales."""
+    q, s = host(call["X_q"]), host(call["x_scale"])
+    y1 = orc.epilogue(orc.matmul(q, ref["C"]), s, GAMMA)
+    if C2 is not None:
+        h = orc.ffn_act(kind, y1, orc.epilogue(orc.matmul(q, C2), s, gamma2))
+    elif kind != 0:
+        h = orc.ffn_act(kind, y1)
+    else:
+        h = y1
+    if R is not None:
+        h = (h + R).astype(np.float32)      # one fp32 rounding of the fp32 sum
+    return h
+
+
+@pytest.mark.parametrize("M,N,K", EX_SHAPES)
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("norm,residual", [(False, False), (True, True), (True, False)])
+def test_linear_ex(torch, bl, orc, M, N, K, kind, norm, residual):
+    label = (M, N, K, kind, norm, residual)
+    call, ref = make_call(torch, bl, M, N, K, "f32", norm, (3, kind), zero_row=True)
+    glu = kind in (bl.ACT_SWIGLU, bl.ACT_RELU2_GLU)
+    C2 = workloads.ternary((N, K), (205, N, K, kind)) if glu else None
+    gamma2 = np.float32(0.017)
+    R = workloads.gaussian((M, N), (206, M, N), 3.0) if residual else None
+    ex = dict(call, act=kind, residual=None if R is None else dev(torch, R))
+    if glu:
+        ex.update(W2_packed=bl.pack_codes(dev(torch, C2)), gamma2=dev(torch, np.array([gamma2], np.float32)))
+    bl.linear_ex_grouped([ex])
+    torch.cuda.synchronize()
+    # Codes and scales the call used: the activation quantizer's.
+    q_ref, s_ref = orc.quantize_acts(ref["x"], ref["g"], 1e-6)
+    assert np.array_equal(host(call["X_q"]), q_ref), label
+    s = host(call["x_scale"])
+    nz = s_ref != 0
+    assert np.array_equal(s == 0, ~nz), label
+    assert rel_err(s[nz], s_ref[nz]) <= REL, label
+    Y_ref = ex_reference(orc, call, ref, C2, gamma2, kind, R)
+    Y = host(call["Y"])
+    if kind == bl.ACT_SWIGLU:
+        bad = Y != Y_ref
+        assert np.count_nonzero(bad) <= max(1, Y.size // 100000), label
+        assert rel_err(Y[bad], Y_ref[bad]) <= 2.0 ** -22, label
+    else:
+        assert np.array_equal(Y, Y_ref), label
+
+
+def test_linear_ex_mixed_group(torch, bl, orc):
+    """Single projections and gated pairs of several K in one call (two launches), with and
+    without the optional code outputs; the outputs equal those of one call per problem."""
+    specs = [(1, 768, 768, 0, True), (1, 2048, 768, 1, False), (2, 640, 2048, 3, True),
+             (4, 96, 9728, 2, True), (3, 1000, 1536, 0, False)]
+    calls = []
+    for i, (M, N, K, kind, res) in enumerate(specs):
+        c, _ = make_call(torch, bl, M, N, K, "f32", True, (4, i))
+        c["act"] = kind
+        if kind in (bl.ACT_SWIGLU, bl.ACT_RELU2_GLU):
+            c["W2_packed"] = bl.pack_codes(dev(torch, workloads.ternary((N, K), (207, i))))
+            c["gamma2"] = dev(torch, np.array([0.019], np.float32))
+        if res:
+            c["residual"] = dev(torch, workloads.gaussian((M, N), (208, i), 1.0))
+        if i % 2:
+            c["X_q"] = c["x_scale"] = None
+        calls.append(c)
+    bl.linear_ex_grouped(calls)
+    torch.cuda.synchronize()
+    together = [c["Y"].clone() for c in calls]
+    for c, Y in zip(calls, together):
+        c["Y"].zero_()
+        bl.linear_ex_grouped([c])
+        torch.cuda.synchronize()
+        assert torch.equal(c["Y"], Y)
+
+
+def test_linear_ex_rejects(torch, bl):
+    """Sizes past the fused form, a gated kind without its pair and a pair with a single
+    kind are refused before anything runs."""
+    call, _ = make_call(torch, bl, 5, 64, 256, "f32", False, (5,))
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.linear_ex_grouped([call])
+    assert e.value.status == -2
+    call, _ = make_call(torch, bl, 2, 64, 256, "f32", False, (6,))
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.linear_ex_grouped([dict(call, act=bl.ACT_SWIGLU)])
+    assert e.value.status == -1
+    with pytest.raises(bl.BitLinearError) as e:
+        bl.linear_ex_grouped([dict(call, act=bl.ACT_NONE, W2_packed=call["W_packed"],
+                                   gamma2=call["gamma"])])
+    assert e.value.status == -4
