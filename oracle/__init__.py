@@ -77,6 +77,15 @@ class Oracle:
         lib.oracle_forward_entries.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _P, _P, _I64,
                                                _P, _P, _P]
         lib.oracle_forward_entries.restype = ctypes.c_int
+        lib.oracle_forward_wonly.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _I64, _P]
+        lib.oracle_forward_wonly.restype = None
+        lib.oracle_grad_input.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _I64, _P]
+        lib.oracle_grad_input.restype = None
+        lib.oracle_ste_scale.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_double]
+        lib.oracle_ste_scale.restype = ctypes.c_double
+        lib.oracle_grad_weight.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int,
+                                           ctypes.c_double, _I64, _I64, _I64, _P]
+        lib.oracle_grad_weight.restype = None
 
     # O1
     def gamma(self, W: np.ndarray) -> Tuple[np.float32, float]:
@@ -219,6 +228,61 @@ class Oracle:
         self._lib.oracle_epilogue_residual(_ptr(acc), _ptr(sx), float(np.float32(gamma)), _ptr(R),
                                            M, N, _ptr(Y))
         return Y
+
+
+    # O9: weight-only ternary forward (full-precision activations)
+    def forward_wonly(self, X: np.ndarray, codes: np.ndarray, gamma) -> np.ndarray:
+        """X fp32 [M, K] (bf16 inputs widened by the caller), codes int8 [N, K]."""
+        X = _c(X, np.float32)
+        codes = _c(codes, np.int8)
+        M, K = X.shape
+        N = codes.shape[0]
+        assert codes.shape[1] == K
+        Y = np.empty((M, N), dtype=np.float32)
+        self._lib.oracle_forward_wonly(_ptr(X), _ptr(codes), float(np.float32(gamma)), M, N, K, _ptr(Y))
+        return Y
+
+    # O10: input gradient
+    def grad_input(self, dY: np.ndarray, codes: np.ndarray, gamma) -> np.ndarray:
+        """dY fp32 [M, N], codes int8 [N, K] -> dX fp32 [M, K]."""
+        dY = _c(dY, np.float32)
+        codes = _c(codes, np.int8)
+        M, N = dY.shape
+        K = codes.shape[1]
+        assert codes.shape[0] == N
+        dX = np.empty((M, K), dtype=np.float32)
+        self._lib.oracle_grad_input(_ptr(dY), _ptr(codes), float(np.float32(gamma)), M, N, K, _ptr(dX))
+        return dX
+
+    # O11: STE gradient scale
+    STE_PASS, STE_HARD, STE_SOFT = 0, 1, 2
+
+    def ste_scale(self, kind: int, w, gamma, beta: float = 2.0) -> float:
+        return self._lib.oracle_ste_scale(int(kind), float(np.float32(w)), float(np.float32(gamma)),
+                                          float(beta))
+
+    # O12: weight gradient
+    def grad_weight(self, dY: np.ndarray, kind: int = 0, W: Optional[np.ndarray] = None, gamma=0.0,
+                    beta: float = 2.0, Xq: Optional[np.ndarray] = None,
+                    sx: Optional[np.ndarray] = None, Xf: Optional[np.ndarray] = None) -> np.ndarray:
+        """dY fp32 [M, N]; activations as (Xq int8 [M, K], sx fp32 [M]) or Xf fp32 [M, K];
+        W fp32 [N, K] for the hard and soft kinds -> dW fp32 [N, K]."""
+        dY = _c(dY, np.float32)
+        M, N = dY.shape
+        if Xq is not None:
+            Xq = _c(Xq, np.int8)
+            sx = _c(sx, np.float32)
+            K = Xq.shape[1]
+        else:
+            Xf = _c(Xf, np.float32)
+            K = Xf.shape[1]
+        if kind != 0:
+            W = _c(W, np.float32)
+            assert W.shape == (N, K)
+        dW = np.empty((N, K), dtype=np.float32)
+        self._lib.oracle_grad_weight(_ptr(dY), _ptr(Xq), _ptr(sx), _ptr(Xf), _ptr(W if kind else None),
+                                     float(np.float32(gamma)), int(kind), float(beta), M, N, K, _ptr(dW))
+        return dW
 
 
 _default: Optional[Oracle] = None

@@ -47,6 +47,26 @@
  *   O8  residual — y_out = fp32(y + r): the BitLinear output added to the residual stream,
  *                  y from O6, one fp32 addition.
  *
+ * Weight-only forward and the straight-through backward (training-side rows):
+ *   O9  fwd W1.58A16 — y[m][n] = fp32(gamma * sum_k x[m][k] * c[n][k]), x fp32 (bf16 widened
+ *                  exactly), the sum in fp64 in k order (bitone README, "Features": the QAT
+ *                  forward Y = X @ W_q^T x gamma with full-precision activations).
+ *   O10 grad X   — dx[m][k] = fp32(gamma * sum_n dy[m][n] * c[n][k]), the sum in fp64 in n
+ *                  order: the product's input gradient through the dequantized weights
+ *                  gamma * c, the activation quantizer passing it unchanged (Distillix README,
+ *                  "Key Innovations 1": STE, gradients pass through quantization unchanged;
+ *                  BitDistill article: gradients through the quantizer use the STE).
+ *   O11 STE scale— grad_scale(t) for t = fp32(W / gamma) (the O2 division): pass-through 1;
+ *                  hard: 1 if |t| <= 1 else 0; soft: sech^2(beta t) = 1 - tanh^2(beta t), beta
+ *                  2 by default (bitone README, "Soft-STE": the hard mask and its smooth
+ *                  replacement).  fp64, sech^2 as 1 / cosh^2 (the same function without the
+ *                  cancellation of 1 - tanh^2 for large |beta t|).
+ *   O12 grad W   — dw[n][k] = fp32(grad_scale(t[n][k]) * sum_m dy[m][n] * xh[m][k]), the sum in
+ *                  fp64 in m order, xh[m][k] = q[m][k] * s_x[m] the dequantized activation the
+ *                  forward multiplied (fp64 product), or a full-precision x for the weight-only
+ *                  forward.  gamma's own dependence on W is not differentiated (a reading: the
+ *                  STE treats W_q * gamma as W).
+ *
  * Degenerate data (defined here, the pages are silent): gamma == 0 gives all codes 0; a row
  * with absmax 0 gives q = 0 and s_x = 0.  NaN inputs are outside the method's domain; where
  * a comparison meets a NaN the result is code 0.
@@ -326,5 +346,70 @@ void oracle_epilogue_residual(const int32_t *acc, const float *s_x, float gamma,
         for (int64_t n = 0; n < N; ++n) {
             float y = (float)((double)acc[m * N + n] * (double)gamma * (double)s_x[m]);
             Y[m * N + n] = y + R[m * N + n];
+        }
+}
+
+/* ------------------------------------------- O9: weight-only ternary forward (W1.58A16) */
+
+/* Y[m][n] = fp32(gamma * sum_k X[m][k] * c[n][k]); codes [N][K] int8. */
+void oracle_forward_wonly(const float *X, const int8_t *C, float gamma, int64_t M, int64_t N,
+                          int64_t K, float *Y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (double)X[m * K + k] * (double)C[n * K + k];
+            Y[m * N + n] = (float)((double)gamma * s);
+        }
+}
+
+/* ---------------------------------------------------- O10: input gradient through the STE */
+
+/* dX[m][k] = fp32(gamma * sum_n dY[m][n] * c[n][k]); dY [M][N], codes [N][K]. */
+void oracle_grad_input(const float *dY, const int8_t *C, float gamma, int64_t M, int64_t N,
+                       int64_t K, float *dX)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += (double)dY[m * N + n] * (double)C[n * K + k];
+            dX[m * K + k] = (float)((double)gamma * s);
+        }
+}
+
+/* ---------------------------------------------------------- O11: STE gradient scale */
+
+/* kind 0: pass-through, 1: hard mask, 2: soft sech^2(beta t).  t = fp32(w / gamma) as in O2
+ * (gamma == 0: t is taken as 0, the scale of a zero tensor's weights). */
+double oracle_ste_scale(int kind, float w, float gamma, double beta)
+{
+    const float t = gamma == 0.0f ? 0.0f : w / gamma;
+    if (kind == 0)
+        return 1.0;
+    if (kind == 1)
+        return fabsf(t) <= 1.0f ? 1.0 : 0.0;
+    const double c = cosh(beta * (double)t);
+    return 1.0 / (c * c);
+}
+
+/* --------------------------------------------------------- O12: weight gradient (STE) */
+
+/* dW[n][k] = fp32(scale(W[n][k]) * sum_m dY[m][n] * xh[m][k]) with xh = Xq * s_x (Xq != NULL)
+ * or xh = Xf.  W may be NULL for the pass-through kind.  dY [M][N], activations [M][K]. */
+void oracle_grad_weight(const float *dY, const int8_t *Xq, const float *s_x, const float *Xf,
+                        const float *W, float gamma, int kind, double beta, int64_t M,
+                        int64_t N, int64_t K, float *dW)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                const double xh = Xq ? (double)Xq[m * K + k] * (double)s_x[m] : (double)Xf[m * K + k];
+                s += (double)dY[m * N + n] * xh;
+            }
+            const double sc = kind == 0 ? 1.0 : oracle_ste_scale(kind, W[n * K + k], gamma, beta);
+            dW[n * K + k] = (float)(sc * s);
         }
 }

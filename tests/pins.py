@@ -440,4 +440,173 @@ def pin_residual_epilogue_exact(orc):
     assert np.all(Z == 0.0) and not np.any(np.signbit(Z[Y0 != 0]))
 
 
+# ------------------------------------------- O9: weight-only ternary forward (W1.58A16)
+
+def _dyadic(shape, key, bits=3, span=8):
+    """Values k / 2^bits with |k| < span * 2^bits: sums of a few of them are exact in fp64."""
+    return (_rng(*key).integers(-span * 2 ** bits, span * 2 ** bits, size=shape)
+            / 2.0 ** bits).astype(np.float32)
+
+
+def pin_wonly_brute_force(orc):
+    """Tiny brute force in exact rationals: y = fp32(gamma * sum_k x c)."""
+    X = _dyadic((3, 16), (60,))
+    C = workloads.ternary((5, 16), (61,))
+    g = np.float32(0.0213)
+    Y = orc.forward_wonly(X, C, g)
+    for m in range(3):
+        for n in range(5):
+            exact = sum(Fraction(float(X[m, k])) * int(C[n, k]) for k in range(16))
+            assert Y[m, n] == f32_of_fraction(Fraction(float(g)) * exact), (m, n)
+
+
+def pin_wonly_integer_inputs_match_int_path(orc):
+    """Integer-valued activations: the weight-only forward equals the int8 path's epilogue
+    with unit row scales, bit for bit (both are fp32(gamma * exact integer sum))."""
+    q = _rng(62).integers(-127, 128, size=(4, 96), dtype=np.int8)
+    C = workloads.ternary((33, 96), (63,))
+    g = np.float32(0.0187)
+    Y = orc.forward_wonly(q.astype(np.float32), C, g)
+    ref = orc.epilogue(q.astype(np.int64) @ C.astype(np.int64).T, np.ones(4, np.float32), g)
+    assert np.array_equal(Y, ref)
+
+
+def pin_wonly_one_hot(orc):
+    """A one-hot token with value a at k gives y[n] = fp32(gamma * a * c[n, k])."""
+    C = workloads.ternary((20, 48), (64,))
+    g, a, k = np.float32(0.031), np.float32(-2.625), 29
+    X = np.zeros((2, 48), np.float32)
+    X[1, k] = a
+    Y = orc.forward_wonly(X, C, g)
+    assert np.count_nonzero(Y[0]) == 0
+    for n in range(20):
+        assert Y[1, n] == f32_of_fraction(Fraction(float(g)) * Fraction(float(a)) * int(C[n, k]))
+
+
+# ------------------------------------------------------------ O10: input gradient (STE)
+
+def pin_grad_input_adjoint(orc):
+    """<dY, X W^T> == <dX, X> with dX = dY W (the adjoint of the weight-only product),
+    non-square and square shapes, to the accuracy of the fp32 outputs."""
+    for (M, N, K), key in (((5, 24, 40), 65), ((3, 32, 32), 66)):
+        C = workloads.ternary((N, K), (key, 1))
+        X = workloads.gaussian((M, K), (key, 2), 1.0)
+        dY = workloads.gaussian((M, N), (key, 3), 1.0)
+        g = np.float32(0.027)
+        Y = orc.forward_wonly(X, C, g).astype(np.float64)
+        dX = orc.grad_input(dY, C, g).astype(np.float64)
+        lhs = np.sum(dY.astype(np.float64) * Y)
+        rhs = np.sum(dX * X.astype(np.float64))
+        scale = np.sum(np.abs(dY.astype(np.float64)) @ np.abs(C.astype(np.float64))
+                       * np.abs(X.astype(np.float64))) * float(g)
+        assert abs(lhs - rhs) <= 1e-6 * scale, (M, N, K, lhs, rhs)
+
+
+def pin_grad_input_one_hot(orc):
+    """dY one-hot at (m, n) with value a: dx[m] = fp32(gamma * a * c[n, :]), other rows 0."""
+    C = workloads.ternary((12, 40), (67,))
+    g, a = np.float32(0.019), np.float32(1.375)
+    dY = np.zeros((3, 12), np.float32)
+    dY[2, 7] = a
+    dX = orc.grad_input(dY, C, g)
+    assert np.count_nonzero(dX[:2]) == 0
+    for k in range(40):
+        assert dX[2, k] == f32_of_fraction(Fraction(float(g)) * Fraction(float(a)) * int(C[7, k]))
+
+
+def pin_grad_input_brute_force(orc):
+    dY = _dyadic((2, 9), (68,))
+    C = workloads.ternary((9, 16), (69,))
+    g = np.float32(0.0411)
+    dX = orc.grad_input(dY, C, g)
+    for m in range(2):
+        for k in range(16):
+            exact = sum(Fraction(float(dY[m, n])) * int(C[n, k]) for n in range(9))
+            assert dX[m, k] == f32_of_fraction(Fraction(float(g)) * exact), (m, k)
+
+
+# --------------------------------------------------------------- O11: STE gradient scale
+
+def pin_ste_scale_page_values(orc):
+    """bitone README, Soft-STE: scale 1 at w/gamma = 0, about 0.07 at 1, effectively zero but
+    positive at 3 (beta = 2); the hard mask keeps |w/gamma| <= 1 (boundary included)."""
+    S, H, P = orc.STE_SOFT, orc.STE_HARD, orc.STE_PASS
+    assert orc.ste_scale(S, 0.0, 0.5) == 1.0
+    assert abs(orc.ste_scale(S, 0.5, 0.5) - 0.07) < 1e-3          # t = 1 exactly
+    assert abs(orc.ste_scale(S, 0.5, 0.5) - (1.0 - math.tanh(2.0) ** 2)) < 1e-15
+    v3 = orc.ste_scale(S, 1.5, 0.5)                                   # t = 3
+    assert 0.0 < v3 < 1e-4
+    assert orc.ste_scale(H, 0.5, 0.5) == 1.0
+    assert orc.ste_scale(H, -0.5, 0.5) == 1.0
+    assert orc.ste_scale(H, float(np.nextafter(np.float32(0.5), np.float32(1))), 0.5) == 0.0
+    assert orc.ste_scale(H, 0.0, 0.5) == 1.0
+    assert orc.ste_scale(P, 123.0, 0.5) == 1.0
+    # Symmetric in w.
+    assert orc.ste_scale(S, -0.3, 0.5) == orc.ste_scale(S, 0.3, 0.5)
+
+
+def pin_ste_soft_is_tanh_derivative(orc):
+    """The soft scale is d/dt [tanh(beta t) / beta] (central differences, beta 2 and 1), and
+    is computed from t = fp32(w / gamma)."""
+    for beta in (2.0, 1.0):
+        for t in (-2.2, -0.7, 0.0, 0.35, 1.0, 1.9, 4.5):
+            w = np.float32(t) * np.float32(0.25)
+            tt = float(np.float32(w) / np.float32(0.25))
+            h = 1e-5
+            fd = (math.tanh(beta * (tt + h)) - math.tanh(beta * (tt - h))) / (2 * h * beta)
+            s = orc.ste_scale(orc.STE_SOFT, w, 0.25, beta)
+            assert abs(s - fd) <= 1e-8 + 1e-8 * abs(fd), (beta, t, s, fd)
+
+
+# --------------------------------------------------------------- O12: weight gradient (STE)
+
+def pin_grad_weight_adjoint(orc):
+    """Pass-through: <dW, gamma c> == <dY, Y> for Y the int8-path forward of the same
+    codes and activations (dW = dY^T (q s_x) is the adjoint of W -> X_hat W^T)."""
+    M, N, K = 6, 20, 48
+    C = workloads.ternary((N, K), (70,))
+    X = workloads.gaussian((M, K), (71,), 1.0)
+    dY = workloads.gaussian((M, N), (72,), 1.0)
+    g = np.float32(0.023)
+    q, s = orc.quantize_acts(X)
+    Y = orc.epilogue(orc.matmul(q, C), s, g).astype(np.float64)
+    dW = orc.grad_weight(dY, orc.STE_PASS, Xq=q, sx=s).astype(np.float64)
+    lhs = np.sum(dW * C.astype(np.float64)) * float(g)
+    rhs = np.sum(dY.astype(np.float64) * Y)
+    scale = float(g) * np.sum(np.abs(dY.astype(np.float64)).T @ np.abs(q * s[:, None].astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-6 * scale
+
+
+def pin_grad_weight_masks_elementwise(orc):
+    """Hard and soft gradients are the pass-through gradient times the scale of the same
+    weight (non-square: a transposed mask index fails), with t spanning both sides of 1."""
+    M, N, K = 5, 12, 32
+    Xf = workloads.gaussian((M, K), (73,), 1.0)
+    dY = workloads.gaussian((M, N), (74,), 1.0)
+    W = workloads.gaussian((N, K), (75,), 0.03)
+    g = np.float32(0.02)
+    base = orc.grad_weight(dY, orc.STE_PASS, Xf=Xf).astype(np.float64)
+    hard = orc.grad_weight(dY, orc.STE_HARD, W=W, gamma=g, Xf=Xf)
+    soft = orc.grad_weight(dY, orc.STE_SOFT, W=W, gamma=g, beta=2.0, Xf=Xf)
+    t = (W / g).astype(np.float32)
+    assert 0 < np.count_nonzero(np.abs(t) > 1) < t.size
+    ref_h = np.where(np.abs(t) <= 1, base, 0.0).astype(np.float32)
+    assert np.array_equal(hard, ref_h)
+    ref_s = base / np.cosh(2.0 * t.astype(np.float64)) ** 2
+    assert np.all(np.abs(soft - ref_s) <= 2.0 ** -23 * np.abs(ref_s) + 1e-37)
+
+
+def pin_grad_weight_brute_force(orc):
+    """Tiny brute force in exact rationals, dequantized activations q * s_x."""
+    dY = _dyadic((3, 4), (76,))
+    q = _rng(77).integers(-127, 128, size=(3, 16), dtype=np.int8)
+    s = np.array([0.5, 0.0078125, 3.25], np.float32)
+    dW = orc.grad_weight(dY, orc.STE_PASS, Xq=q, sx=s)
+    for n in range(4):
+        for k in range(16):
+            exact = sum(Fraction(float(dY[m, n])) * int(q[m, k]) * Fraction(float(s[m]))
+                        for m in range(3))
+            assert dW[n, k] == f32_of_fraction(exact), (n, k)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

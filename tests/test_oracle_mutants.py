@@ -51,6 +51,27 @@ MUTANTS = {
                               "        double r = (double)x;\n        v = r * r;"),
     "residual_dropped": ("Y[m * N + n] = y + R[m * N + n];", "Y[m * N + n] = y;"),
     "residual_subtracted": ("Y[m * N + n] = y + R[m * N + n];", "Y[m * N + n] = y - R[m * N + n];"),
+    "wonly_transposed_codes": ("s += (double)X[m * K + k] * (double)C[n * K + k];",
+                               "s += (double)X[m * K + k] * (double)C[k * N + n];"),
+    "wonly_drops_gamma": ("Y[m * N + n] = (float)((double)gamma * s);", "Y[m * N + n] = (float)s;"),
+    "grad_input_untransposed": ("s += (double)dY[m * N + n] * (double)C[n * K + k];",
+                                "s += (double)dY[m * N + n] * (double)C[k * N + n];"),
+    "grad_input_subtracts": ("s += (double)dY[m * N + n] * (double)C[n * K + k];",
+                             "s -= (double)dY[m * N + n] * (double)C[n * K + k];"),
+    "grad_input_drops_gamma": ("dX[m * K + k] = (float)((double)gamma * s);", "dX[m * K + k] = (float)s;"),
+    "ste_hard_strict": ("return fabsf(t) <= 1.0f ? 1.0 : 0.0;", "return fabsf(t) < 1.0f ? 1.0 : 0.0;"),
+    "ste_soft_no_beta": ("cosh(beta * (double)t)", "cosh((double)t)"),
+    "ste_soft_fp32_tanh": ("return 1.0 / (c * c);",
+                           "return (double)(1.0f - tanhf((float)(beta * t)) * tanhf((float)(beta * t)));"),
+    "ste_multiplies": ("const float t = gamma == 0.0f ? 0.0f : w / gamma;",
+                       "const float t = gamma == 0.0f ? 0.0f : w * gamma;"),
+    "grad_weight_drops_row_scale": ("(double)Xq[m * K + k] * (double)s_x[m] : (double)Xf",
+                                    "(double)Xq[m * K + k] : (double)Xf"),
+    "grad_weight_first_row_scale": ("(double)Xq[m * K + k] * (double)s_x[m] : (double)Xf",
+                                    "(double)Xq[m * K + k] * (double)s_x[0] : (double)Xf"),
+    "grad_weight_mask_transposed": ("oracle_ste_scale(kind, W[n * K + k], gamma, beta)",
+                                    "oracle_ste_scale(kind, W[k * N + n], gamma, beta)"),
+    "grad_weight_dy_transposed": ("s += (double)dY[m * N + n] * xh;", "s += (double)dY[n * M + m] * xh;"),
 }
 
 
