@@ -96,6 +96,27 @@ class _LinearExProblem(ctypes.Structure):
                 ("x_dtype", ctypes.c_int), ("act", ctypes.c_int), ("eps", ctypes.c_float)]
 
 
+class _WonlyProblem(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("W_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("x_dtype", ctypes.c_int)]
+
+
+class _GradInputProblem(ctypes.Structure):
+    _fields_ = [("dY", ctypes.c_void_p), ("Wt_packed", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("dX", ctypes.c_void_p), ("M", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("dy_dtype", ctypes.c_int)]
+
+
+class _GradWeightProblem(ctypes.Structure):
+    _fields_ = [("dY", ctypes.c_void_p), ("X_q", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("W", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("dW", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("ste", ctypes.c_int), ("beta", ctypes.c_float)]
+
+
+STE_PASS, STE_HARD, STE_SOFT = 0, 1, 2
+
 _lib = None
 
 
@@ -142,6 +163,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_ex_grouped.restype = ctypes.c_int
     L.bitlinear_linear_ex_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_ex_grouped.restype = ctypes.c_int
+    for fn in ("bitlinear_forward_wonly_grouped", "bitlinear_grad_input_grouped",
+               "bitlinear_grad_weight_grouped"):
+        getattr(L, fn).argtypes = [P, ctypes.c_int, P]
+        getattr(L, fn).restype = ctypes.c_int
+    L.bitlinear_transpose_packed.argtypes = [P, I64, I64, P, P]
+    L.bitlinear_transpose_packed.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -442,3 +469,87 @@ def linear_ex_grouped(problems: Sequence[dict], stream=None) -> None:
     arr = linear_ex_table(problems)
     _check("bitlinear_linear_ex_grouped",
            lib().bitlinear_linear_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+# ------------------------------------------------------------- training side
+
+def forward_wonly_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Weight-only ternary forward Y = gamma * X C^T: dicts with X (fp32/bf16 [M, K]),
+    W_packed, gamma, Y (preallocated fp32 [M, N])."""
+    arr = (_WonlyProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        N = p["W_packed"].shape[0]
+        arr[i] = _WonlyProblem(_ptr(X), _ptr(p["W_packed"]), _ptr(p["gamma"]), _ptr(p["Y"]), M, N, K,
+                               _x_dtype(X))
+    _check("bitlinear_forward_wonly_grouped",
+           lib().bitlinear_forward_wonly_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+def forward_wonly(X: torch.Tensor, W_packed: torch.Tensor, gamma: torch.Tensor, stream=None):
+    Y = torch.empty((X.shape[0], W_packed.shape[0]), dtype=torch.float32, device=X.device)
+    forward_wonly_grouped([dict(X=X, W_packed=W_packed, gamma=gamma, Y=Y)], stream)
+    return Y
+
+
+def transpose_packed(W_packed: torch.Tensor, K: Optional[int] = None,
+                     Wt_packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed codes [N, K/16] -> the transposed codes packed [K, N/16] (N % 16 == 0)."""
+    _dev(W_packed, "W_packed", torch.int32)
+    N = W_packed.shape[0]
+    K = W_packed.shape[1] * 16 if K is None else K
+    if Wt_packed is None:
+        Wt_packed = torch.empty((K, N // 16), dtype=torch.int32, device=W_packed.device)
+    _check("bitlinear_transpose_packed",
+           lib().bitlinear_transpose_packed(_ptr(W_packed), N, K, _ptr(Wt_packed), _stream(stream)))
+    return Wt_packed
+
+
+def grad_input_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Input gradient dX = gamma * dY C: dicts with dY (fp32/bf16 [M, N]), Wt_packed
+    (transpose_packed of the forward's codes, [K, N/16]), gamma, dX (preallocated [M, K])."""
+    arr = (_GradInputProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        dY = _dev(p["dY"], f"dY[{i}]")
+        M, N = dY.shape
+        K = p["Wt_packed"].shape[0]
+        if p["Wt_packed"].shape[1] * 16 != N:
+            raise ValueError(f"Wt_packed[{i}] must be [K, N/16]")
+        arr[i] = _GradInputProblem(_ptr(dY), _ptr(p["Wt_packed"]), _ptr(p["gamma"]), _ptr(p["dX"]),
+                                   M, N, K, _x_dtype(dY))
+    _check("bitlinear_grad_input_grouped",
+           lib().bitlinear_grad_input_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+def grad_input(dY: torch.Tensor, Wt_packed: torch.Tensor, gamma: torch.Tensor, stream=None):
+    dX = torch.empty((dY.shape[0], Wt_packed.shape[0]), dtype=torch.float32, device=dY.device)
+    grad_input_grouped([dict(dY=dY, Wt_packed=Wt_packed, gamma=gamma, dX=dX)], stream)
+    return dX
+
+
+def grad_weight_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Weight gradient through the STE: dicts with dY (fp32 [M, N]), X_q (int8 [M, K]),
+    x_scale ([M]), gamma, dW (preallocated fp32 [N, K]) and optional W (fp32 masters [N, K],
+    needed by STE_HARD / STE_SOFT), ste (STE_*), beta (default 2)."""
+    arr = (_GradWeightProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        dY = _dev(p["dY"], f"dY[{i}]", torch.float32)
+        Xq = _dev(p["X_q"], f"X_q[{i}]", torch.int8)
+        M, N = dY.shape
+        K = Xq.shape[1]
+        if Xq.shape[0] != M or tuple(p["dW"].shape) != (N, K):
+            raise ValueError(f"problem {i}: dY [M, N], X_q [M, K], dW [N, K]")
+        arr[i] = _GradWeightProblem(_ptr(dY), _ptr(Xq), _ptr(p["x_scale"]), _ptr(p.get("W")),
+                                    _ptr(p["gamma"]), _ptr(p["dW"]), M, N, K, int(p.get("ste", STE_PASS)),
+                                    float(p.get("beta", 2.0)))
+    _check("bitlinear_grad_weight_grouped",
+           lib().bitlinear_grad_weight_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+def grad_weight(dY: torch.Tensor, X_q: torch.Tensor, x_scale: torch.Tensor, gamma: torch.Tensor,
+                W: Optional[torch.Tensor] = None, ste: int = STE_PASS, beta: float = 2.0, stream=None):
+    dW = torch.empty((dY.shape[1], X_q.shape[1]), dtype=torch.float32, device=dY.device)
+    grad_weight_grouped([dict(dY=dY, X_q=X_q, x_scale=x_scale, gamma=gamma, dW=dW, W=W, ste=ste,
+                              beta=beta)], stream)
+    return dW

@@ -214,6 +214,67 @@ bl_status check_linear_ex(const bl_linear_ex_problem &p)
     return BL_OK;
 }
 
+bool a4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bl_status check_wonly(const bl_wonly_problem &p)
+{
+    const bool empty = p.M == 0 || p.N == 0;
+    if (!p.gamma || (!empty && (!p.X || !p.W_packed || !p.Y)))
+        return BL_ERR_NULL;
+    if (p.x_dtype != BL_F32 && p.x_dtype != BL_BF16)
+        return BL_ERR_DTYPE;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK)
+        s = check_rows(p.N);
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(p.X) || !aligned16(p.W_packed) || !a4(p.gamma) || !a4(p.Y))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status check_grad_input(const bl_grad_input_problem &p)
+{
+    const bool empty = p.M == 0;
+    if (!p.gamma || (!empty && (!p.dY || !p.Wt_packed || !p.dX)))
+        return BL_ERR_NULL;
+    if (p.dy_dtype != BL_F32 && p.dy_dtype != BL_BF16)
+        return BL_ERR_DTYPE;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK)
+        s = check_k(p.N);            // the contraction: N % 16 == 0, 0 < N <= BL_MAX_K
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(p.dY) || !aligned16(p.Wt_packed) || !a4(p.gamma) || !a4(p.dX))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
+bl_status check_grad_weight(const bl_grad_weight_problem &p)
+{
+    const bool empty = p.N == 0;
+    if (p.ste < BL_STE_PASS || p.ste > BL_STE_SOFT)
+        return BL_ERR_DTYPE;
+    if (!p.gamma || (!empty && (!p.dW || (p.M != 0 && (!p.dY || !p.X_q || !p.x_scale)) ||
+                                (p.ste != BL_STE_PASS && !p.W))))
+        return BL_ERR_NULL;
+    bl_status s = check_rows(p.M);
+    if (s == BL_OK && (p.N < 0 || p.N > BL_MAX_K))
+        s = BL_ERR_SHAPE;
+    if (s == BL_OK)
+        s = check_k(p.K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(p.dY) || !aligned16(p.X_q) || !aligned16(p.W) || !aligned16(p.dW) ||
+        !a4(p.gamma) || !a4(p.x_scale))
+        return BL_ERR_ALIGN;
+    return BL_OK;
+}
+
 bl_linear_ex_problem to_ex(const bl_linear_problem &p)
 {
     return bl_linear_ex_problem{p.X, p.norm_weight, p.W_packed, p.gamma, nullptr, nullptr,
@@ -445,6 +506,86 @@ bl_status bitlinear_linear_ex_grouped(const bl_linear_ex_problem *problems, int 
     if (blocks > INT_MAX)
         return BL_ERR_SHAPE;
     return from_hip(bl::launch_linear_decode(problems, count, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_forward_wonly_grouped(const bl_wonly_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl::WgProblem q[BL_MAX_GROUP];
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_wonly_problem &p = problems[i];
+        bl_status s = check_wonly(p);
+        if (s != BL_OK)
+            return s;
+        q[i] = bl::WgProblem{p.X, p.x_dtype == BL_F32, p.W_packed, p.gamma, p.Y, p.M, p.N, p.K};
+        blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_wgemm(q, count, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_transpose_packed(const uint32_t *W_packed, int64_t N, int64_t K,
+                                     uint32_t *Wt_packed, void *stream)
+{
+    if (N < 0 || N > BL_MAX_K || N % 16 != 0)
+        return BL_ERR_SHAPE;
+    bl_status s = check_k(K);
+    if (s != BL_OK)
+        return s;
+    if (N != 0 && (!W_packed || !Wt_packed))
+        return BL_ERR_NULL;
+    if (!aligned16(W_packed) || !aligned16(Wt_packed))
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_transpose_packed(W_packed, N, K, Wt_packed,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_grad_input_grouped(const bl_grad_input_problem *problems, int count,
+                                       void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl::WgProblem q[BL_MAX_GROUP];
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_grad_input_problem &p = problems[i];
+        bl_status s = check_grad_input(p);
+        if (s != BL_OK)
+            return s;
+        // dX = gamma * dY C = gamma * dY (C^T)^T: the weight-only product with A = dY and the
+        // transposed codes (K rows of N/16 words).
+        q[i] = bl::WgProblem{p.dY, p.dy_dtype == BL_F32, p.Wt_packed, p.gamma, p.dX, p.M, p.K, p.N};
+        blocks += ((p.M + 127) / 128) * ((p.K + 127) / 128);
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_wgemm(q, count, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_grad_weight_grouped(const bl_grad_weight_problem *problems, int count,
+                                        void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_grad_weight(problems[i]);
+        if (s != BL_OK)
+            return s;
+        blocks += ((problems[i].N + 127) / 128) * ((problems[i].K + 127) / 128);
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_grad_weight(problems, count, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -212,6 +212,22 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipS
 hipError_t launch_linear_decode(const bl_linear_ex_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 
+// Training-side products (train.hip).  Y[M][O] = gamma * A[M][Kc] T^T with T packed codes
+// [O][Kc/16] and A fp32 or bf16: the weight-only forward, and the input gradient with the
+// transposed codes.
+struct WgProblem {
+    const void *A;
+    bool f32;
+    const uint32_t *T;
+    const float *gamma;
+    float *Y;
+    int64_t M, O, Kc;
+};
+hipError_t launch_wgemm(const WgProblem *p, int count, hipStream_t stream);
+hipError_t launch_transpose_packed(const uint32_t *P, int64_t N, int64_t K, uint32_t *Pt,
+                                   hipStream_t stream);
+hipError_t launch_grad_weight(const bl_grad_weight_problem *p, int count, hipStream_t stream);
+
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.
 constexpr int64_t kDecodeMaxM = 16;
 

@@ -1,0 +1,585 @@
+// train.hip — the training-side products on the bf16 matrix cores.
+//
+// (1) The weight-only ternary forward (bitone README, "Features": the QAT forward computes
+//     Y = X @ W_q^T x gamma with full-precision activations): Y = gamma * X C^T.
+// (2) The input gradient through the straight-through estimator (Distillix README, "Key
+//     Innovations 1": gradients pass through quantization unchanged): dX = gamma * dY C.
+//     It is (1) with the transposed code matrix, so (3) re-packs C^T once per weight update
+//     and the same kernel runs it.
+// (4) The weight gradient: dW = grad_scale(W / gamma) . (dY^T X_hat), X_hat = q * s_x the
+//     dequantized activations the forward multiplied; grad_scale is 1 (pass-through), the
+//     hard mask |W / gamma| <= 1, or sech^2(beta W / gamma) (bitone README, "Soft-STE").
+//
+// The codes are exact in bf16 (0, +-1.0) and so are int8 activation codes, so products on
+// the bf16 matrix unit (v_mfma_f32_16x16x32_bf16, fp32 accumulation) lose nothing on that
+// side.  fp32 operands are split x = hi + lo with hi = bf16(x) and lo = bf16(x - hi)
+// (x - hi is exact in fp32): two MFMAs per fragment carry 16 significant bits of x, a
+// relative representation error of at most 2^-16 (2^-8 of 2^-8), below the fp32 accumulation error of any
+// contraction longer than a few hundred terms.  bf16 operands take one MFMA.
+//
+// Both GEMMs stage operands through LDS in bf16 with the contraction index contiguous (the
+// MFMA operand layout): (1)/(2) read activation rows and packed code rows that are already
+// contraction-major and expand the 2-bit codes to bf16 in registers; (4) contracts over
+// tokens, which are the slow index of both dY and q, so its staging loads two token rows at
+// once and writes them transposed (two tokens per LDS dword).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace bl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// bf16 bits (round to nearest, ties to even) of a finite fp32 value.
+__device__ __forceinline__ uint32_t bf16_bits(float x)
+{
+    const uint32_t b = __float_as_uint(x);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo)
+{
+    hi = bf16_bits(x);
+    lo = bf16_bits(x - __uint_as_float(hi << 16));   // exact difference
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(v4u a, v4u b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Eight codes of a packed word as eight bf16 values (0, +1.0, -1.0): half j holds weights
+// 8j .. 8j+7 of the word's 16, i.e. planes 2j and 2j+1 (weight 4i + b at bits 8b + 2i).
+// Each byte of t = (w >> 2i) & 0x03030303 is one 2-bit field f (00 -> 0, 01 -> +1, 11 -> -1);
+// v_perm_b32 looks the bf16 bytes up: selector byte f picks the low byte from kLutLo
+// (0x00 or 0x80) and f + 4 the high byte from kLutHi (0x00, 0x3F or 0xBF).  The unused field
+// value 10 maps to 0.
+constexpr uint32_t kLutLo = 0x80008000u;   // bytes for f = 0..3: 00 80 00 80
+constexpr uint32_t kLutHi = 0xBF003F00u;   // bytes for f = 0..3: 00 3F 00 BF
+
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t t, uint32_t t4, uint32_t sel)
+{
+    // sel picks [t.byte a, t4.byte a, t.byte a+1, t4.byte a+1] = [f, f + 4, f', f' + 4].
+    return __builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(t4, t, sel));
+}
+
+__device__ __forceinline__ v4u ternary_bf16(uint32_t w, int j)
+{
+    const uint32_t t0 = (w >> (4 * j)) & 0x03030303u;
+    const uint32_t t1 = (w >> (4 * j + 2)) & 0x03030303u;
+    const uint32_t u0 = t0 + 0x04040404u, u1 = t1 + 0x04040404u;
+    return v4u{bf16_pair(t0, u0, 0x05010400u), bf16_pair(t0, u0, 0x07030602u),
+               bf16_pair(t1, u1, 0x05010400u), bf16_pair(t1, u1, 0x07030602u)};
+}
+
+// ------------------------------------------------------- (1)/(2): Y = gamma * A T^T
+
+struct WgDev {
+    const void *A;        // [M][Kc] fp32 or bf16, row-major
+    const uint32_t *T;    // [O][Kc/16] packed codes
+    const float *gamma;
+    float *Y;             // [M][O]
+    int M, O, Kc;
+    int tiles_o;
+    int block_begin;
+};
+
+struct WgBatch {
+    WgDev p[BL_MAX_GROUP];
+    int count;
+};
+
+constexpr int kWgThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
+constexpr int kWgBM = 128, kWgBO = 128;      // block tile: A rows x code rows
+constexpr int kWgKC = 64;                    // contraction per stage (4 packed words a row)
+constexpr int kWgPitch = 2 * kWgKC + 16;     // LDS bytes per bf16 A row (padded: no bank
+                                             // conflicts between the 16 rows of a read)
+constexpr int kWgABytes = kWgBM * kWgPitch;
+constexpr int kWgTBytes = kWgBO * 16;
+
+// F32: A is fp32, split into hi / lo parts while staging.  Block tile 128 x 128, stages of
+// 64 contraction indices double-buffered in LDS: the next stage's global loads are in
+// flight while the current one is multiplied, one barrier per stage.  Lane (r, g) reads the
+// A fragment of row r, contraction 16g + 8j .. +7 (16 bytes of LDS) and word g of its code
+// row, expanded to the same eight contraction indices (half j).
+template <bool F32>
+__global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
+{
+    constexpr int PARTS = F32 ? 2 : 1;
+    constexpr int STAGE = PARTS * kWgABytes + kWgTBytes;
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int CHUNKS = kWgBM * kWgKC * ESZ / 16 / kWgThreads;   // 16-byte A loads a thread
+    constexpr int CPR = kWgKC * ESZ / 16;                            // 16-byte chunks per row
+    __shared__ __align__(16) unsigned char lds[2][STAGE];
+
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
+        ++prob;
+    const WgDev &p = b.p[prob];
+    const int tile = blockIdx.x - p.block_begin;
+    const int m0 = (tile / p.tiles_o) * kWgBM;
+    const int o0 = (tile % p.tiles_o) * kWgBO;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r = lane & 15, g = lane >> 4;
+    const int Kc = p.Kc;
+    const int words = Kc / 16;
+    const int stages = (Kc + kWgKC - 1) / kWgKC;
+
+    // Rows past M / O read as zero.  Activation chunks past Kc read as zero (offset kOOB);
+    // code words past Kc may belong to the next row: they meet those zero activations.
+    const rsrc_t ares = make_rsrc(static_cast<const unsigned char *>(p.A) + (int64_t)m0 * Kc * ESZ,
+                                  rows_bytes(m0, kWgBM, p.M, Kc * ESZ));
+    const rsrc_t tres = make_rsrc(p.T + (int64_t)o0 * words, rows_bytes(o0, kWgBO, p.O, words * 4));
+
+    v4u ra[CHUNKS];
+    v4u rt = v4u{0, 0, 0, 0};
+    auto load = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int q = tid + kWgThreads * i;
+            const int row = q / CPR, c = (q % CPR) * (16 / ESZ);   // c: element in the stage
+            const int k = s * kWgKC + c;
+            ra[i] = buf_load16(ares, k < Kc ? (uint32_t)(row * Kc + k) * ESZ : kOOB);
+        }
+        if (tid < kWgBO) {
+            const uint32_t off = (uint32_t)(tid * words + s * 4) * 4u;
+            if ((words & 3) == 0) {
+                rt = buf_load16(tres, off);
+            } else {
+                // A 16-byte load running past the resource may come back all zero: with a
+                // ragged word count take the row's words one by one (past the row: zero).
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    rt[j] = buf_load4(tres, s * 4 + j < words ? off + 4u * j : kOOB);
+            }
+        }
+    };
+    auto store = [&](int buf) {
+        unsigned char *st = lds[buf];
+#pragma unroll
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int q = tid + kWgThreads * i;
+            const int row = q / CPR, c = (q % CPR) * (16 / ESZ);
+            unsigned char *dst = st + row * kWgPitch + 2 * c;
+            if (F32) {
+                uint32_t h[4], l[4];
+                split_bf16(__uint_as_float(ra[i].x), h[0], l[0]);
+                split_bf16(__uint_as_float(ra[i].y), h[1], l[1]);
+                split_bf16(__uint_as_float(ra[i].z), h[2], l[2]);
+                split_bf16(__uint_as_float(ra[i].w), h[3], l[3]);
+                *reinterpret_cast<v2u *>(dst) = v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                *reinterpret_cast<v2u *>(dst + kWgABytes) = v2u{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+            } else {
+                *reinterpret_cast<v4u *>(dst) = ra[i];
+            }
+        }
+        if (tid < kWgBO)
+            *reinterpret_cast<v4u *>(st + PARTS * kWgABytes + tid * 16) = rt;
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf) {
+        const unsigned char *st = lds[buf];
+        uint32_t wd[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            wd[ni] = *reinterpret_cast<const uint32_t *>(st + PARTS * kWgABytes +
+                                                         (wn * 64 + ni * 16 + r) * 16 + 4 * g);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v4u bw[4];
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                bw[ni] = ternary_bf16(wd[ni], j);
+#pragma unroll
+            for (int part = 0; part < PARTS; ++part)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const v4u a = *reinterpret_cast<const v4u *>(
+                        st + part * kWgABytes + (wm * 64 + mi * 16 + r) * kWgPitch + 32 * g + 16 * j);
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        acc[mi][ni] = mfma_bf16(bw[ni], a, acc[mi][ni]);
+                }
+        }
+    };
+
+    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < stages; ++s) {
+        const bool more = s + 1 < stages;
+        if (more)
+            load(s + 1);
+        compute(s & 1);
+        if (more)
+            store((s + 1) & 1);
+        __syncthreads();
+    }
+
+    // acc[mi][ni] register v: D[o][m] for o = o0 + wn * 64 + ni * 16 + 4g + v and
+    // m = m0 + wm * 64 + mi * 16 + r (the codes are the MFMA's row operand): four
+    // consecutive outputs of one row per lane.
+    const bool vec = (p.O & 3) == 0 && ((uintptr_t)p.Y & 15) == 0;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int m = m0 + wm * 64 + mi * 16 + r;
+        if (m >= p.M)
+            continue;
+        float *yrow = p.Y + (int64_t)m * p.O;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int o = o0 + wn * 64 + ni * 16 + 4 * g;
+            const f32x4 y = acc[mi][ni] * gammaf;
+            if (vec && o + 3 < p.O) {
+                *reinterpret_cast<float4 *>(yrow + o) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (o + v < p.O)
+                        yrow[o + v] = y[v];
+            }
+        }
+    }
+}
+
+hipError_t launch_wgemm(const WgProblem *q, int count, hipStream_t stream)
+{
+    for (int f32 = 0; f32 < 2; ++f32) {
+        WgBatch b{};
+        int blocks = 0;
+        for (int i = 0; i < count; ++i) {
+            const WgProblem &s = q[i];
+            if (s.f32 != (f32 != 0) || s.M == 0 || s.O == 0)
+                continue;
+            WgDev &d = b.p[b.count++];
+            d.A = s.A;
+            d.T = s.T;
+            d.gamma = s.gamma;
+            d.Y = s.Y;
+            d.M = (int)s.M;
+            d.O = (int)s.O;
+            d.Kc = (int)s.Kc;
+            d.tiles_o = (d.O + kWgBO - 1) / kWgBO;
+            d.block_begin = blocks;
+            blocks += ((d.M + kWgBM - 1) / kWgBM) * d.tiles_o;
+        }
+        if (!blocks)
+            continue;
+        if (f32)
+            hipLaunchKernelGGL((wgemm_kernel<true>), dim3(blocks), dim3(kWgThreads), 0, stream, b);
+        else
+            hipLaunchKernelGGL((wgemm_kernel<false>), dim3(blocks), dim3(kWgThreads), 0, stream, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// ------------------------------------------------------- (3): packed C -> packed C^T
+
+// Block: 64 code rows (n) x 64 columns (k).  Each thread loads one input word into LDS, then
+// assembles one output word: column k's codes of 16 consecutive rows, in the canonical field
+// layout (row 16w' + 4i + b of the output word at bits 8b + 2i).
+__global__ __launch_bounds__(256) void transpose_packed_kernel(const uint32_t *P, int N, int K,
+                                                                uint32_t *Pt, int tiles_k)
+{
+    __shared__ uint32_t in[64][5];
+    const int n0 = (blockIdx.x / tiles_k) * 64, k0 = (blockIdx.x % tiles_k) * 64;
+    const int words = K / 16, owords = N / 16;
+    const int t = threadIdx.x;
+    {
+        const int n = n0 + (t >> 2), w = k0 / 16 + (t & 3);
+        in[t >> 2][t & 3] = (n < N && w < words) ? P[(int64_t)n * words + w] : 0u;
+    }
+    __syncthreads();
+    const int kk = t >> 2, ow = t & 3;
+    const int k = k0 + kk, wo = n0 / 16 + ow;
+    if (k >= K || wo >= owords)
+        return;
+    const int kin = kk & 15;
+    const int sh_in = 8 * (kin & 3) + 2 * (kin >> 2);
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t f = (in[16 * ow + j][kk >> 4] >> sh_in) & 3u;
+        out |= f << (8 * (j & 3) + 2 * (j >> 2));
+    }
+    Pt[(int64_t)k * owords + wo] = out;
+}
+
+hipError_t launch_transpose_packed(const uint32_t *P, int64_t N, int64_t K, uint32_t *Pt,
+                                   hipStream_t stream)
+{
+    if (N == 0)
+        return hipSuccess;
+    const int tiles_n = (int)((N + 63) / 64), tiles_k = (int)((K + 63) / 64);
+    hipLaunchKernelGGL(transpose_packed_kernel, dim3(tiles_n * tiles_k), dim3(256), 0, stream,
+                       P, (int)N, (int)K, Pt, tiles_k);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- (4): weight gradient
+
+struct GwDev {
+    const float *dY;      // [M][N]
+    const int8_t *Xq;     // [M][K]
+    const float *sx;      // [M]
+    const float *W;       // [N][K] (hard / soft scale) or NULL
+    const float *gamma;
+    float *dW;            // [N][K]
+    int M, N, K;
+    int ste;
+    float beta;
+    int tiles_k;
+    int block_begin;
+};
+
+struct GwBatch {
+    GwDev p[BL_MAX_GROUP];
+    int count;
+};
+
+constexpr int kGwThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
+constexpr int kGwBN = 128, kGwBK = 128;      // block tile: dW rows (n) x columns (k)
+constexpr int kGwKC = 32;                    // tokens per stage (one MFMA k-step)
+constexpr int kGwPitch = 2 * kGwKC + 16;     // LDS bytes per bf16 row (padded)
+constexpr int kGwPart = kGwBN * kGwPitch;    // one bf16 part of the dY tile
+constexpr int kGwStage = 3 * kGwPart;        // dY hi, dY lo, q
+
+// Stage s covers tokens 32s .. 32s+31.  Staging: a thread takes two consecutive tokens of
+// four dY columns (two 16-byte loads) and of eight q columns (two 8-byte loads), scales dY
+// by s_x (one fp32 product, as the dequantized activation q * s_x is folded into dY's side),
+// splits it, converts q (exact), and writes each (token pair, column) as one LDS dword, so
+// the tiles land transposed: row = column of dW, contiguous in tokens.
+__global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
+{
+    __shared__ __align__(16) unsigned char lds[2][kGwStage];
+
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
+        ++prob;
+    const GwDev &p = b.p[prob];
+    const int tile = blockIdx.x - p.block_begin;
+    const int n0 = (tile / p.tiles_k) * kGwBN;
+    const int k0 = (tile % p.tiles_k) * kGwBK;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r = lane & 15, g = lane >> 4;
+    const int M = p.M, N = p.N, K = p.K;
+    const int stages = (M + kGwKC - 1) / kGwKC;
+    const rsrc_t sres = make_rsrc(p.sx, (uint32_t)M * 4u);
+
+    // Per stage: the tokens' rows from column n0 (k0) on; tokens past M read zero.  Columns
+    // past N (K) belong to the next row: they only reach dW rows (columns) that are not
+    // stored.
+    v4u ry[2][2];      // [unit][token of the pair]: four dY columns
+    v2u rq[2];         // [token of the pair]: eight q columns
+    float rs[2][2];
+    auto load = [&](int s) {
+        const int t0 = s * kGwKC;
+        const int live = min(kGwKC, M - t0);
+        const int64_t ybytes = (int64_t)live * N * 4 - (int64_t)n0 * 4;
+        const int64_t qbytes = (int64_t)live * K - (int64_t)k0;
+        const rsrc_t yres = make_rsrc(p.dY + (int64_t)t0 * N + n0, ybytes > 0 ? (uint32_t)ybytes : 0u);
+        const rsrc_t qres = make_rsrc(p.Xq + (int64_t)t0 * K + k0, qbytes > 0 ? (uint32_t)qbytes : 0u);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int unit = tid + kGwThreads * u;           // 16 token pairs x 32 column quads
+            const int pr = unit >> 5, c4 = (unit & 31) * 4;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t off = (uint32_t)((2 * pr + h) * N + c4) * 4u;
+                if ((N & 3) == 0) {
+                    ry[u][h] = buf_load16(yres, off);
+                } else {
+                    // Rows not 16-byte multiples: one dword at a time (see wgemm_kernel).
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ry[u][h][e] = buf_load4(yres, off + 4u * e);
+                }
+                rs[u][h] = __uint_as_float(buf_load4(sres, (uint32_t)(t0 + 2 * pr + h) * 4u));
+            }
+        }
+        {
+            const int pr = tid >> 4, c8 = (tid & 15) * 8;   // 16 token pairs x 16 column octets
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                rq[h] = __builtin_amdgcn_raw_buffer_load_b64(qres, (2 * pr + h) * K + c8, 0, 0);
+        }
+    };
+    auto store = [&](int buf) {
+        unsigned char *st = lds[buf];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int unit = tid + kGwThreads * u;
+            const int pr = unit >> 5, c4 = (unit & 31) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h0, l0, h1, l1;
+                split_bf16(__uint_as_float(ry[u][0][e]) * rs[u][0], h0, l0);
+                split_bf16(__uint_as_float(ry[u][1][e]) * rs[u][1], h1, l1);
+                unsigned char *dst = st + (c4 + e) * kGwPitch + 4 * pr;
+                *reinterpret_cast<uint32_t *>(dst) = h0 | (h1 << 16);
+                *reinterpret_cast<uint32_t *>(dst + kGwPart) = l0 | (l1 << 16);
+            }
+        }
+        {
+            const int pr = tid >> 4, c8 = (tid & 15) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w0 = rq[0][e >> 2], w1 = rq[1][e >> 2];
+                const int sh = 8 * (e & 3);
+                const float f0 = (float)((int)(w0 << (24 - sh)) >> 24);
+                const float f1 = (float)((int)(w1 << (24 - sh)) >> 24);
+                *reinterpret_cast<uint32_t *>(st + 2 * kGwPart + (c8 + e) * kGwPitch + 4 * pr) =
+                    (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+            }
+        }
+    };
+
+    f32x4 acc[4][4];   // [ni][mi]
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            acc[ni][mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf) {
+        const unsigned char *st = lds[buf];
+        v4u bq[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            bq[ni] = *reinterpret_cast<const v4u *>(st + 2 * kGwPart + (wn * 64 + ni * 16 + r) * kGwPitch + 16 * g);
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+                const v4u a = *reinterpret_cast<const v4u *>(st + part * kGwPart +
+                                                             (wm * 64 + mi * 16 + r) * kGwPitch + 16 * g);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[ni][mi] = mfma_bf16(bq[ni], a, acc[ni][mi]);
+            }
+    };
+
+    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    if (stages > 0) {
+        load(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int s = 0; s < stages; ++s) {
+        const bool more = s + 1 < stages;
+        if (more)
+            load(s + 1);
+        compute(s & 1);
+        if (more)
+            store((s + 1) & 1);
+        __syncthreads();
+    }
+
+    // acc[ni][mi] register v: dW[n][k] for k = k0 + wn * 64 + ni * 16 + 4g + v and
+    // n = n0 + wm * 64 + mi * 16 + r.  Gradient scale from t = fl32(W / gamma) (the
+    // quantizer's division; gamma == 0 gives t = 0).
+    const bool vec = ((uintptr_t)p.dW & 15) == 0 && (!p.W || ((uintptr_t)p.W & 15) == 0);
+    const double beta = (double)p.beta;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int n = n0 + wm * 64 + mi * 16 + r;
+        if (n >= N)
+            continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int k = k0 + wn * 64 + ni * 16 + 4 * g;
+            if (k >= K)
+                continue;     // K % 16 == 0: the four columns are all in or all out
+            float y[4];
+            float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.ste != 0) {
+                const float *wrow = p.W + (int64_t)n * K + k;
+                if (vec) {
+                    const float4 wv = *reinterpret_cast<const float4 *>(wrow);
+                    w[0] = wv.x; w[1] = wv.y; w[2] = wv.z; w[3] = wv.w;
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        w[v] = wrow[v];
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float a = acc[ni][mi][v];
+                if (p.ste == 0) {
+                    y[v] = a;
+                } else {
+                    const float t = gammaf == 0.0f ? 0.0f : w[v] / gammaf;   // correctly rounded
+                    if (p.ste == 1) {
+                        y[v] = fabsf(t) <= 1.0f ? a : 0.0f;
+                    } else {
+                        const double c = cosh(beta * (double)t);
+                        y[v] = (float)((1.0 / (c * c)) * (double)a);
+                    }
+                }
+            }
+            float *dst = p.dW + (int64_t)n * K + k;
+            if (vec) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    dst[v] = y[v];
+            }
+        }
+    }
+}
+
+hipError_t launch_grad_weight(const bl_grad_weight_problem *q, int count, hipStream_t stream)
+{
+    GwBatch b{};
+    int blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_grad_weight_problem &s = q[i];
+        if (s.N == 0)
+            continue;
+        GwDev &d = b.p[b.count++];
+        d.dY = s.dY;
+        d.Xq = s.X_q;
+        d.sx = s.x_scale;
+        d.W = s.W;
+        d.gamma = s.gamma;
+        d.dW = s.dW;
+        d.M = (int)s.M;
+        d.N = (int)s.N;
+        d.K = (int)s.K;
+        d.ste = s.ste;
+        d.beta = s.beta;
+        d.tiles_k = (d.K + kGwBK - 1) / kGwBK;
+        d.block_begin = blocks;
+        blocks += ((d.N + kGwBN - 1) / kGwBN) * d.tiles_k;
+    }
+    if (!blocks)
+        return hipSuccess;
+    hipLaunchKernelGGL(gradw_kernel, dim3(blocks), dim3(kGwThreads), 0, stream, b);
+    return hipGetLastError();
+}
+
+}  // namespace bl

@@ -354,6 +354,96 @@ typedef struct {
 bl_status bitlinear_linear_ex_grouped(const bl_linear_ex_problem *problems, int count,
                                       void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Training side: the weight-only forward and the straight-through backward.
+ *
+ * bitone README, "Features": the QAT forward Y = X @ W_q^T x gamma with full-precision
+ * activations, and "Soft-STE": the weight gradient's hard mask and its smooth replacement
+ * grad_scale = 1 - tanh^2(beta * W / gamma) = sech^2(beta * W / gamma), beta 2 by default.
+ * Distillix README, "Key Innovations 1" and the BitDistill article: gradients pass through
+ * the quantizers unchanged (STE).
+ *
+ * Arithmetic: the products run on the bf16 matrix cores with fp32 accumulation.  Codes
+ * (0, +-1) and int8 activation codes are exact in bf16; fp32 operands are carried as two
+ * bf16 parts (16 significant bits, relative error <= 2^-16 per term); bf16 operands are
+ * exact.  Results are the exact sums up to fp32 accumulation: for a contraction of length L
+ * over terms a_i, |error| <= (L * 2^-24 + 2^-16 [fp32 operands] ) * sum |a_i| + one fp32
+ * rounding of the scaled result.  Sums are not bit-reproducible against a serial order.
+ * ------------------------------------------------------------------------------------- */
+
+/* (1) Weight-only ternary forward: Y[m][n] = fp32(gamma * sum_k X[m][k] * c[n][k]).
+ *   X          [M][K] fp32 or bf16 (x_dtype), 16-byte aligned.
+ *   W_packed   [N][K/16] packed codes (the bitlinear_quantize_weights layout).
+ *   gamma      [1] fp32.   Y  [M][N] fp32.
+ * M == 0 or N == 0 is a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE (as bitlinear_forward), BL_ERR_ALIGN, BL_ERR_DTYPE. */
+typedef struct {
+    const void *X;
+    const uint32_t *W_packed;
+    const float *gamma;
+    float *Y;
+    int64_t M, N, K;
+    int x_dtype;
+} bl_wonly_problem;
+
+bl_status bitlinear_forward_wonly_grouped(const bl_wonly_problem *problems, int count,
+                                          void *stream);
+
+/* (2) The transposed code matrix: Wt_packed [K][N/16] holds c[n][k] at row k, field n, in the
+ * same packed layout (needs N % 16 == 0 and N <= BL_MAX_K).  Run once per weight update; the
+ * input gradient reads it.  N == 0 is a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN. */
+bl_status bitlinear_transpose_packed(const uint32_t *W_packed, int64_t N, int64_t K,
+                                     uint32_t *Wt_packed, void *stream);
+
+/* (3) Input gradient: dX[m][k] = fp32(gamma * sum_n dY[m][n] * c[n][k]) (through the
+ * activation quantizer unchanged; the caller applies the norm's backward if the forward
+ * fused one).
+ *   dY         [M][N] fp32 or bf16 (dy_dtype).
+ *   Wt_packed  [K][N/16]: bitlinear_transpose_packed of the forward's W_packed.
+ *   gamma      the forward's gamma.   dX  [M][K] fp32.
+ * Needs N % 16 == 0, N <= BL_MAX_K, K > 0, K % 16 == 0.  M == 0 is a no-op. */
+typedef struct {
+    const void *dY;
+    const uint32_t *Wt_packed;
+    const float *gamma;
+    float *dX;
+    int64_t M, N, K;
+    int dy_dtype;
+} bl_grad_input_problem;
+
+bl_status bitlinear_grad_input_grouped(const bl_grad_input_problem *problems, int count,
+                                       void *stream);
+
+/* (4) Weight gradient: dW[n][k] = fp32(scale(W[n][k]) * sum_m dY[m][n] * X_q[m][k] * x_scale[m])
+ * (dY times the dequantized activations the forward multiplied, through the weight
+ * quantizer by the STE), scale from t = fl32(W / gamma) (the quantizer's division; gamma ==
+ * 0 gives t = 0):
+ *   BL_STE_PASS  1                      (W may be NULL)
+ *   BL_STE_HARD  1 if |t| <= 1, else 0
+ *   BL_STE_SOFT  sech^2(beta * t), evaluated in fp64
+ *   dY [M][N] fp32; X_q [M][K] int8 and x_scale [M] from the forward's activation
+ *   quantization; W [N][K] fp32 masters; dW [N][K] fp32 (M == 0 writes zeros).
+ * Needs K > 0, K % 16 == 0, K <= BL_MAX_K, N <= BL_MAX_K.  N == 0 is a no-op.
+ * Errors: BL_ERR_NULL, BL_ERR_SHAPE, BL_ERR_ALIGN (16 bytes for every array but gamma and
+ * x_scale), BL_ERR_DTYPE (unknown ste kind). */
+typedef enum { BL_STE_PASS = 0, BL_STE_HARD = 1, BL_STE_SOFT = 2 } bl_ste_kind;
+
+typedef struct {
+    const float *dY;
+    const int8_t *X_q;
+    const float *x_scale;
+    const float *W;
+    const float *gamma;
+    float *dW;
+    int64_t M, N, K;
+    int ste;
+    float beta;
+} bl_grad_weight_problem;
+
+bl_status bitlinear_grad_weight_grouped(const bl_grad_weight_problem *problems, int count,
+                                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

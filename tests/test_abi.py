@@ -251,6 +251,69 @@ def test_linear_ex_validation(L, bl):
     assert call(N=0) == BL_OK
 
 
+def test_training_entry_points_validation(L, bl):
+    fw = L.bitlinear_forward_wonly_grouped
+
+    def wonly(**kw):
+        d = dict(X=A, W_packed=B, gamma=C, Y=D, M=2, N=4, K=64, x_dtype=0)
+        d.update(kw)
+        arr = (bl._WonlyProblem * 1)()
+        arr[0] = bl._WonlyProblem(**d)
+        return fw(ctypes.addressof(arr), 1, None)
+
+    assert fw(None, 1, None) == BL_ERR_NULL
+    assert wonly(X=None) == BL_ERR_NULL
+    assert wonly(gamma=None) == BL_ERR_NULL
+    assert wonly(x_dtype=2) == BL_ERR_DTYPE
+    assert wonly(K=40) == BL_ERR_SHAPE
+    assert wonly(N=-1) == BL_ERR_SHAPE
+    assert wonly(X=A + 8) == BL_ERR_ALIGN
+    assert wonly(Y=D + 2) == BL_ERR_ALIGN
+    assert wonly(M=0) == BL_OK and wonly(N=0, X=None) == BL_OK
+    tp = L.bitlinear_transpose_packed
+    assert tp(A, 40, 64, B, None) == BL_ERR_SHAPE          # N % 16 != 0
+    assert tp(A, 32, 40, B, None) == BL_ERR_SHAPE          # K % 16 != 0
+    assert tp(A, 16 * 20000, 64, B, None) == BL_ERR_SHAPE  # N above BL_MAX_K
+    assert tp(None, 32, 64, B, None) == BL_ERR_NULL
+    assert tp(A + 4, 32, 64, B, None) == BL_ERR_ALIGN
+    assert tp(None, 0, 64, None, None) == BL_OK
+    gi = L.bitlinear_grad_input_grouped
+
+    def gin(**kw):
+        d = dict(dY=A, Wt_packed=B, gamma=C, dX=D, M=2, N=64, K=32, dy_dtype=0)
+        d.update(kw)
+        arr = (bl._GradInputProblem * 1)()
+        arr[0] = bl._GradInputProblem(**d)
+        return gi(ctypes.addressof(arr), 1, None)
+
+    assert gin(dY=None) == BL_ERR_NULL
+    assert gin(N=40) == BL_ERR_SHAPE
+    assert gin(K=0) == BL_ERR_SHAPE
+    assert gin(dy_dtype=5) == BL_ERR_DTYPE
+    assert gin(Wt_packed=B + 4) == BL_ERR_ALIGN
+    assert gin(M=0, dY=None, dX=None) == BL_OK
+    gw = L.bitlinear_grad_weight_grouped
+
+    def gwt(**kw):
+        d = dict(dY=A, X_q=B, x_scale=C, W=None, gamma=D, dW=E, M=2, N=4, K=64, ste=0, beta=2.0)
+        d.update(kw)
+        arr = (bl._GradWeightProblem * 1)()
+        arr[0] = bl._GradWeightProblem(**d)
+        return gw(ctypes.addressof(arr), 1, None)
+
+    assert gw(None, 1, None) == BL_ERR_NULL
+    assert gwt(ste=3) == BL_ERR_DTYPE
+    assert gwt(ste=1) == BL_ERR_NULL                      # hard / soft need W
+    assert gwt(ste=2, W=None) == BL_ERR_NULL
+    assert gwt(dY=None) == BL_ERR_NULL
+    assert gwt(K=40) == BL_ERR_SHAPE
+    assert gwt(N=300000) == BL_ERR_SHAPE
+    assert gwt(dY=A + 4) == BL_ERR_ALIGN
+    assert gwt(ste=1, W=E + 8) == BL_ERR_ALIGN
+    assert gwt(x_scale=C + 2) == BL_ERR_ALIGN
+    assert gwt(N=0, dW=None) == BL_OK
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):
