@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="time the whole layer chain (six launches per layer, residuals and the "
                          "FFN activation included) instead of the step; prints its own JSON line")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training-side products (weight-only forward, input and weight "
+                         "gradients through the STE, transposed packing) over the workload's "
+                         "matrices at the prefill token count; prints its own JSON line")
     ap.add_argument("--verbose", action="store_true")
     return ap.parse_args()
 
@@ -524,6 +528,94 @@ def layer_bench(torch, bl, wl: workloads.Workload, M_pre: int, rotate_bytes: flo
     return out
 
 
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published (no sparsity)
+
+
+def graph_ms(torch, fn, reps: int) -> float:
+    """Average time of fn(stream) replayed from a captured HIP graph (events on its stream)."""
+    s_ = torch.cuda.Stream()
+    with torch.cuda.stream(s_):
+        fn(s_.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s_):
+        for _ in range(reps):
+            fn(s_.cuda_stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_):
+        graph.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s_)
+        for _ in range(3):
+            graph.replay()
+        e1.record(s_)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (3 * reps)
+
+
+def train_bench(torch, bl, wl: workloads.Workload, M: int, reps: int):
+    """The workload's projections as one grouped call per training-side product at M tokens:
+    the weight-only forward (fp32 and bf16 activations), the input gradient (fp32 dY), the
+    weight gradient with the soft STE scale, and the transposed packing of every matrix.
+    Inputs are seeded and resident; each product is timed from a replayed graph."""
+    mats = wl.matrices
+    dev = "cuda"
+    g = torch.full((1,), wl.code_gamma, device=dev)
+    Ps, Wts, Ws = [], [], []
+    for i, m in enumerate(mats):
+        C = torch.from_numpy(workloads.ternary((m.N, m.K), (wl.index, 90, i), wl.code_mix)).to(dev)
+        Ps.append(bl.pack_codes(C))
+        Wts.append(bl.transpose_packed(Ps[-1]))
+        Ws.append(torch.from_numpy(workloads.gaussian((m.N, m.K), (wl.index, 91, i), wl.w_sigma)).to(dev))
+    X = [torch.from_numpy(workloads.gaussian((M, m.K), (wl.index, 92, i), 1.0)).to(dev) for i, m in enumerate(mats)]
+    Xb = [x.to(torch.bfloat16) for x in X]
+    dY = [torch.from_numpy(workloads.gaussian((M, m.N), (wl.index, 93, i), 1.0)).to(dev) for i, m in enumerate(mats)]
+    Y = [torch.empty((M, m.N), device=dev) for m in mats]
+    dX = [torch.empty((M, m.K), device=dev) for m in mats]
+    dW = [torch.empty((m.N, m.K), device=dev) for m in mats]
+    qs = [bl.quantize_acts(x) for x in X]
+    L = bl.lib()
+    import ctypes
+    tabs = {}
+    arr = (bl._WonlyProblem * len(mats))()
+    arrb = (bl._WonlyProblem * len(mats))()
+    gi = (bl._GradInputProblem * len(mats))()
+    gw = (bl._GradWeightProblem * len(mats))()
+    for i, m in enumerate(mats):
+        arr[i] = bl._WonlyProblem(X[i].data_ptr(), Ps[i].data_ptr(), g.data_ptr(), Y[i].data_ptr(), M, m.N, m.K, bl.BL_F32)
+        arrb[i] = bl._WonlyProblem(Xb[i].data_ptr(), Ps[i].data_ptr(), g.data_ptr(), Y[i].data_ptr(), M, m.N, m.K, bl.BL_BF16)
+        gi[i] = bl._GradInputProblem(dY[i].data_ptr(), Wts[i].data_ptr(), g.data_ptr(), dX[i].data_ptr(), M, m.N, m.K, bl.BL_F32)
+        gw[i] = bl._GradWeightProblem(dY[i].data_ptr(), qs[i][0].data_ptr(), qs[i][1].data_ptr(), Ws[i].data_ptr(),
+                                      g.data_ptr(), dW[i].data_ptr(), M, m.N, m.K, bl.STE_SOFT, 2.0)
+    n = len(mats)
+
+    def call(fn, a):
+        return lambda st: bl._check(fn.__name__, fn(ctypes.addressof(a), n, st))
+
+    def transpose_all(st):
+        for i, m in enumerate(mats):
+            bl._check("transpose", L.bitlinear_transpose_packed(Ps[i].data_ptr(), m.N, m.K, Wts[i].data_ptr(), st))
+
+    flops = sum(2 * M * m.N * m.K for m in mats)
+    packed = sum(m.N * m.K // 4 for m in mats)
+    out = {"tokens": M, "matrices": [f"{m.name} {m.K}->{m.N}" for m in mats], "flops_per_product": flops}
+    for key, fn, f32 in (("forward_wonly_f32", call(L.bitlinear_forward_wonly_grouped, arr), True),
+                         ("forward_wonly_bf16", call(L.bitlinear_forward_wonly_grouped, arrb), False),
+                         ("grad_input_f32", call(L.bitlinear_grad_input_grouped, gi), True),
+                         ("grad_weight_soft", call(L.bitlinear_grad_weight_grouped, gw), True)):
+        ms = graph_ms(torch, fn, reps)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[key] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                    "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "mfma_per_product": 2 if f32 else 1,
+                    "frac_attainable": round(tf * (2 if f32 else 1) / BF16_PEAK_TFLOPS, 4)}
+    ms = graph_ms(torch, transpose_all, reps)
+    out["transpose_packed"] = {"us": round(ms * 1e3, 2), "bytes": 2 * packed,
+                               "gbps": round(2 * packed / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -554,6 +646,11 @@ def main():
         sys.exit(1)
     wl = workloads.WORKLOADS[args.workload]
     M_pre = args.prefill_tokens or max(wl.token_counts)
+    if args.train:
+        rec = train_bench(torch, bl, wl, M_pre, max(2, args.steps // 10))
+        print(json.dumps({"metric": "BitLinear training-side products: TFLOP/s vs bf16 MFMA peak",
+                          "workload": wl.key, "data": "synthetic", "n_gpus": 1, **rec}), flush=True)
+        return
     if args.layer:
         rec = layer_bench(torch, bl, wl, M_pre, args.rotate_bytes, max(1, args.steps // 10))
         print(json.dumps({"metric": "BitLinear layer chain: us per layer (decode, prefill)",
