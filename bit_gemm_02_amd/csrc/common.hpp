@@ -51,6 +51,16 @@ __device__ __forceinline__ uint32_t rows_bytes(int r0, int rows, int R, int row_
     return live > 0 ? (uint32_t)live * (uint32_t)row_bytes : 0u;
 }
 
+// Dispatch order -> work order.  Workgroups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8); remapping gives each XCD a contiguous range of a problem's
+// nb tiles, so tiles that share an operand panel run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_order(int b, int nb)
+{
+    const int xcd = b & 7, i = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
+}
+
 // ----------------------------------------------------------------- packed-code planes
 //
 // A packed word holds 16 codes; the code of weight k = 16w + 4i + b lives at bits

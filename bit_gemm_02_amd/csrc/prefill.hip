@@ -43,16 +43,6 @@ struct PreBatch {
     int blocks;
 };
 
-// Dispatch order -> work order.  Workgroups are handed to the 8 XCDs round-robin
-// (block b runs on XCD b % 8); remapping gives each XCD a contiguous range of a problem's
-// tiles, so tiles that share an activation row panel run on the same XCD and share its L2.
-__device__ __forceinline__ int xcd_order(int b, int nb)
-{
-    const int xcd = b & 7, i = b >> 3;
-    const int q = nb >> 3, r = nb & 7;
-    return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
-}
-
 // Raw buffer descriptor as four scalar dwords: base address, stride 0, size in bytes, and
 // the gfx9-family raw-access word.  Offsets at or past `bytes` read zero.
 __device__ __forceinline__ v4i make_desc(const void *base, uint32_t bytes)

@@ -20,8 +20,8 @@
 // Both GEMMs stage operands through LDS in bf16 with the contraction index contiguous (the
 // MFMA operand layout): (1)/(2) read activation rows and packed code rows that are already
 // contraction-major and expand the 2-bit codes to bf16 in registers; (4) contracts over
-// tokens, which are the slow index of both dY and q, so its staging loads two token rows at
-// once and writes them transposed (two tokens per LDS dword).
+// tokens, which are the slow index of both dY and q, so its staging loads four token rows
+// at once and writes them transposed (four tokens per 8-byte LDS store).
 #include <algorithm>
 
 #include "common.hpp"
@@ -32,17 +32,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
-// bf16 bits (round to nearest, ties to even) of a finite fp32 value.
-__device__ __forceinline__ uint32_t bf16_bits(float x)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as a bf16 pair (x0 in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16(float x0, float x1)
 {
-    const uint32_t b = __float_as_uint(x);
-    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
 }
 
-__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo)
+// hi / lo parts of a pair: hi = bf16(x), lo = bf16(x - hi) (the difference is exact).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo)
 {
-    hi = bf16_bits(x);
-    lo = bf16_bits(x - __uint_as_float(hi << 16));   // exact difference
+    hi = pack_bf16(x0, x1);
+    lo = pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(v4u a, v4u b, f32x4 c)
@@ -90,6 +94,7 @@ struct WgDev {
 struct WgBatch {
     WgDev p[BL_MAX_GROUP];
     int count;
+    int blocks;
 };
 
 constexpr int kWgThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
@@ -120,7 +125,9 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
     while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
         ++prob;
     const WgDev &p = b.p[prob];
-    const int tile = blockIdx.x - p.block_begin;
+    // XCD-aware order inside the problem: neighbouring tiles share an activation row panel.
+    const int ntiles = (prob + 1 < b.count ? b.p[prob + 1].block_begin : b.blocks) - p.block_begin;
+    const int tile = xcd_order(blockIdx.x - p.block_begin, ntiles);
     const int m0 = (tile / p.tiles_o) * kWgBM;
     const int o0 = (tile % p.tiles_o) * kWgBO;
     const int tid = threadIdx.x;
@@ -138,30 +145,36 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
                                   rows_bytes(m0, kWgBM, p.M, Kc * ESZ));
     const rsrc_t tres = make_rsrc(p.T + (int64_t)o0 * words, rows_bytes(o0, kWgBO, p.O, words * 4));
 
-    v4u ra[CHUNKS];
-    v4u rt = v4u{0, 0, 0, 0};
-    auto load = [&](int s) {
+    // One stage's global loads, held in registers until they are written to LDS (issued
+    // before the previous stage is multiplied).  (Two alternating register sets, two stages
+    // in flight, measured slower: past 256 registers a SIMD holds one wave instead of two.)
+    struct Regs {
+        v4u a[CHUNKS];
+        v4u t;
+    };
+    auto load = [&](Regs &R, int s) {
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
             const int q = tid + kWgThreads * i;
             const int row = q / CPR, c = (q % CPR) * (16 / ESZ);   // c: element in the stage
             const int k = s * kWgKC + c;
-            ra[i] = buf_load16(ares, k < Kc ? (uint32_t)(row * Kc + k) * ESZ : kOOB);
+            R.a[i] = buf_load16(ares, k < Kc ? (uint32_t)(row * Kc + k) * ESZ : kOOB);
         }
+        R.t = v4u{0, 0, 0, 0};
         if (tid < kWgBO) {
             const uint32_t off = (uint32_t)(tid * words + s * 4) * 4u;
             if ((words & 3) == 0) {
-                rt = buf_load16(tres, off);
+                R.t = buf_load16(tres, off);
             } else {
                 // A 16-byte load running past the resource may come back all zero: with a
                 // ragged word count take the row's words one by one (past the row: zero).
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    rt[j] = buf_load4(tres, s * 4 + j < words ? off + 4u * j : kOOB);
+                    R.t[j] = buf_load4(tres, s * 4 + j < words ? off + 4u * j : kOOB);
             }
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](const Regs &R, int buf) {
         unsigned char *st = lds[buf];
 #pragma unroll
         for (int i = 0; i < CHUNKS; ++i) {
@@ -169,19 +182,17 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
             const int row = q / CPR, c = (q % CPR) * (16 / ESZ);
             unsigned char *dst = st + row * kWgPitch + 2 * c;
             if (F32) {
-                uint32_t h[4], l[4];
-                split_bf16(__uint_as_float(ra[i].x), h[0], l[0]);
-                split_bf16(__uint_as_float(ra[i].y), h[1], l[1]);
-                split_bf16(__uint_as_float(ra[i].z), h[2], l[2]);
-                split_bf16(__uint_as_float(ra[i].w), h[3], l[3]);
-                *reinterpret_cast<v2u *>(dst) = v2u{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-                *reinterpret_cast<v2u *>(dst + kWgABytes) = v2u{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+                uint32_t h0, l0, h1, l1;
+                split_pair(__uint_as_float(R.a[i].x), __uint_as_float(R.a[i].y), h0, l0);
+                split_pair(__uint_as_float(R.a[i].z), __uint_as_float(R.a[i].w), h1, l1);
+                *reinterpret_cast<v2u *>(dst) = v2u{h0, h1};
+                *reinterpret_cast<v2u *>(dst + kWgABytes) = v2u{l0, l1};
             } else {
-                *reinterpret_cast<v4u *>(dst) = ra[i];
+                *reinterpret_cast<v4u *>(dst) = R.a[i];
             }
         }
         if (tid < kWgBO)
-            *reinterpret_cast<v4u *>(st + PARTS * kWgABytes + tid * 16) = rt;
+            *reinterpret_cast<v4u *>(st + PARTS * kWgABytes + tid * 16) = R.t;
     };
 
     f32x4 acc[4][4];
@@ -218,16 +229,17 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
     };
 
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
-    load(0);
-    store(0);
+    Regs R;
+    load(R, 0);
+    store(R, 0);
     __syncthreads();
     for (int s = 0; s < stages; ++s) {
         const bool more = s + 1 < stages;
         if (more)
-            load(s + 1);
+            load(R, s + 1);
         compute(s & 1);
         if (more)
-            store((s + 1) & 1);
+            store(R, (s + 1) & 1);
         __syncthreads();
     }
 
@@ -280,6 +292,7 @@ hipError_t launch_wgemm(const WgProblem *q, int count, hipStream_t stream)
         }
         if (!blocks)
             continue;
+        b.blocks = blocks;
         if (f32)
             hipLaunchKernelGGL((wgemm_kernel<true>), dim3(blocks), dim3(kWgThreads), 0, stream, b);
         else
@@ -353,6 +366,7 @@ struct GwDev {
 struct GwBatch {
     GwDev p[BL_MAX_GROUP];
     int count;
+    int blocks;
 };
 
 constexpr int kGwThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
@@ -362,11 +376,11 @@ constexpr int kGwPitch = 2 * kGwKC + 16;     // LDS bytes per bf16 row (padded)
 constexpr int kGwPart = kGwBN * kGwPitch;    // one bf16 part of the dY tile
 constexpr int kGwStage = 3 * kGwPart;        // dY hi, dY lo, q
 
-// Stage s covers tokens 32s .. 32s+31.  Staging: a thread takes two consecutive tokens of
-// four dY columns (two 16-byte loads) and of eight q columns (two 8-byte loads), scales dY
+// Stage s covers tokens 32s .. 32s+31.  Staging: a thread takes four consecutive tokens of
+// four dY columns (four 16-byte loads) and of four q columns (four dword loads), scales dY
 // by s_x (one fp32 product, as the dequantized activation q * s_x is folded into dY's side),
-// splits it, converts q (exact), and writes each (token pair, column) as one LDS dword, so
-// the tiles land transposed: row = column of dW, contiguous in tokens.
+// splits it, converts q (exact), and writes each (column, four tokens) as one 8-byte LDS
+// store, so the tiles land transposed: row = column of dW, contiguous in tokens.
 __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
 {
     __shared__ __align__(16) unsigned char lds[2][kGwStage];
@@ -376,7 +390,10 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
     while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
         ++prob;
     const GwDev &p = b.p[prob];
-    const int tile = blockIdx.x - p.block_begin;
+    // XCD-aware order inside the problem: neighbouring tiles share a dY column panel, and
+    // run through the tokens together, so the panel's current stage is read once per XCD.
+    const int ntiles = (prob + 1 < b.count ? b.p[prob + 1].block_begin : b.blocks) - p.block_begin;
+    const int tile = xcd_order(blockIdx.x - p.block_begin, ntiles);
     const int n0 = (tile / p.tiles_k) * kGwBN;
     const int k0 = (tile % p.tiles_k) * kGwBK;
     const int tid = threadIdx.x;
@@ -390,69 +407,54 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
 
     // Per stage: the tokens' rows from column n0 (k0) on; tokens past M read zero.  Columns
     // past N (K) belong to the next row: they only reach dW rows (columns) that are not
-    // stored.
-    v4u ry[2][2];      // [unit][token of the pair]: four dY columns
-    v2u rq[2];         // [token of the pair]: eight q columns
-    float rs[2][2];
-    auto load = [&](int s) {
-        const int t0 = s * kGwKC;
+    // stored.  A thread stages four tokens x four columns of dY and of q (units of
+    // 8 token quads x 32 column quads).
+    const int tq = tid >> 5, c4 = (tid & 31) * 4;
+    struct Regs {
+        v4u y[4];      // [token]: four dY columns
+        float s[4];
+        uint32_t q[4]; // [token]: four q columns
+    };
+    auto load = [&](Regs &R, int st) {
+        const int t0 = st * kGwKC;
         const int live = min(kGwKC, M - t0);
         const int64_t ybytes = (int64_t)live * N * 4 - (int64_t)n0 * 4;
         const int64_t qbytes = (int64_t)live * K - (int64_t)k0;
         const rsrc_t yres = make_rsrc(p.dY + (int64_t)t0 * N + n0, ybytes > 0 ? (uint32_t)ybytes : 0u);
         const rsrc_t qres = make_rsrc(p.Xq + (int64_t)t0 * K + k0, qbytes > 0 ? (uint32_t)qbytes : 0u);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int unit = tid + kGwThreads * u;           // 16 token pairs x 32 column quads
-            const int pr = unit >> 5, c4 = (unit & 31) * 4;
+        for (int h = 0; h < 4; ++h) {
+            const int t = 4 * tq + h;
+            const uint32_t off = (uint32_t)(t * N + c4) * 4u;
+            if ((N & 3) == 0) {
+                R.y[h] = buf_load16(yres, off);
+            } else {
+                // Rows not 16-byte multiples: one dword at a time (see wgemm_kernel).
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint32_t off = (uint32_t)((2 * pr + h) * N + c4) * 4u;
-                if ((N & 3) == 0) {
-                    ry[u][h] = buf_load16(yres, off);
-                } else {
-                    // Rows not 16-byte multiples: one dword at a time (see wgemm_kernel).
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ry[u][h][e] = buf_load4(yres, off + 4u * e);
-                }
-                rs[u][h] = __uint_as_float(buf_load4(sres, (uint32_t)(t0 + 2 * pr + h) * 4u));
+                for (int e = 0; e < 4; ++e)
+                    R.y[h][e] = buf_load4(yres, off + 4u * e);
             }
-        }
-        {
-            const int pr = tid >> 4, c8 = (tid & 15) * 8;   // 16 token pairs x 16 column octets
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                rq[h] = __builtin_amdgcn_raw_buffer_load_b64(qres, (2 * pr + h) * K + c8, 0, 0);
+            R.s[h] = __uint_as_float(buf_load4(sres, (uint32_t)(t0 + t) * 4u));
+            R.q[h] = buf_load4(qres, (uint32_t)(t * K + c4));
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](const Regs &R, int buf) {
         unsigned char *st = lds[buf];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int unit = tid + kGwThreads * u;
-            const int pr = unit >> 5, c4 = (unit & 31) * 4;
+        for (int e = 0; e < 4; ++e) {
+            float v[4], f[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t h0, l0, h1, l1;
-                split_bf16(__uint_as_float(ry[u][0][e]) * rs[u][0], h0, l0);
-                split_bf16(__uint_as_float(ry[u][1][e]) * rs[u][1], h1, l1);
-                unsigned char *dst = st + (c4 + e) * kGwPitch + 4 * pr;
-                *reinterpret_cast<uint32_t *>(dst) = h0 | (h1 << 16);
-                *reinterpret_cast<uint32_t *>(dst + kGwPart) = l0 | (l1 << 16);
+            for (int h = 0; h < 4; ++h) {
+                v[h] = __uint_as_float(R.y[h][e]) * R.s[h];
+                f[h] = (float)((int)(R.q[h] << (24 - 8 * e)) >> 24);   // exact in bf16
             }
-        }
-        {
-            const int pr = tid >> 4, c8 = (tid & 15) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = rq[0][e >> 2], w1 = rq[1][e >> 2];
-                const int sh = 8 * (e & 3);
-                const float f0 = (float)((int)(w0 << (24 - sh)) >> 24);
-                const float f1 = (float)((int)(w1 << (24 - sh)) >> 24);
-                *reinterpret_cast<uint32_t *>(st + 2 * kGwPart + (c8 + e) * kGwPitch + 4 * pr) =
-                    (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-            }
+            uint32_t h01, l01, h23, l23;
+            split_pair(v[0], v[1], h01, l01);
+            split_pair(v[2], v[3], h23, l23);
+            unsigned char *dst = st + (c4 + e) * kGwPitch + 8 * tq;
+            *reinterpret_cast<v2u *>(dst) = v2u{h01, h23};
+            *reinterpret_cast<v2u *>(dst + kGwPart) = v2u{l01, l23};
+            *reinterpret_cast<v2u *>(dst + 2 * kGwPart) = v2u{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
         }
     };
 
@@ -482,18 +484,19 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
     };
 
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    Regs R;
     if (stages > 0) {
-        load(0);
-        store(0);
+        load(R, 0);
+        store(R, 0);
     }
     __syncthreads();
     for (int s = 0; s < stages; ++s) {
         const bool more = s + 1 < stages;
         if (more)
-            load(s + 1);
+            load(R, s + 1);
         compute(s & 1);
         if (more)
-            store((s + 1) & 1);
+            store(R, (s + 1) & 1);
         __syncthreads();
     }
 
@@ -578,6 +581,7 @@ hipError_t launch_grad_weight(const bl_grad_weight_problem *q, int count, hipStr
     }
     if (!blocks)
         return hipSuccess;
+    b.blocks = blocks;
     hipLaunchKernelGGL(gradw_kernel, dim3(blocks), dim3(kGwThreads), 0, stream, b);
     return hipGetLastError();
 }
