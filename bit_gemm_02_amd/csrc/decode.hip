@@ -84,7 +84,7 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
 // PAIR (fused form only): a gated pair of projections with one set of activations; the
 // block's first RG/2 row groups are rows of W, the other RG/2 the same rows of W2, and the
 // epilogue combines the two outputs of each row through the activation.
-template <int RG, bool XLDS, bool QUANT, bool FULL_K, bool PAIR = false>
+template <int RG, bool XLDS, bool QUANT, bool FULL_K, bool PAIR = false, bool BF16 = false>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
     static_assert(!QUANT || XLDS, "the fused form stages codes in LDS");
@@ -205,6 +205,55 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     // zeros).  (The scheduling barrier keeps the refill where it
     // is: left alone, the compiler sinks it below the next multiplies, halving the loads in
     // flight.)
+    // Fused form: this wave's piece of the activations, elements [e0, e1) of each token row.
+    const int e0 = t_begin * kSuperWords * 16;
+    const int e1 = min(t_end * kSuperWords, words) * 16;
+    const int quads = (e1 - e0) / 4;
+    const bool norm = QUANT && p.g != nullptr;
+    constexpr bool bf16 = BF16;      // the activation dtype is a launch-wide constant
+    constexpr int esize = bf16 ? 2 : 4;
+    const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
+    auto row = [&](int m) {
+        return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
+                         (uint32_t)p.K * esize);
+    };
+    auto quad_g = [&](int j) {
+        const v4u v = buf_load16(gr, (uint32_t)j * 16u);
+        return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                           __uint_as_float(v.w));
+    };
+    // One token whose piece takes up to kDecCQ quads per lane: every activation (and norm
+    // weight) load is issued before the weight loads, so the quantization does not wait
+    // behind the weight stream (loads complete in issue order), and u stays in registers for
+    // the quantization pass (the same per-lane order of the sums: quads past the piece read
+    // as zeros and add nothing).  The loads land in raw registers and are converted only
+    // after the weight loads are out: a use next to a load makes the wave wait for it, which
+    // would serialize the loads.  Otherwise four quads per lane at a time after the weight
+    // loads, re-read for the quantization pass.
+    const bool cached = QUANT && p.M == 1 && quads <= kDecCQ * kWave;
+    float4 xc[kDecCQ], uc[kDecCQ];
+    v4u rx[kDecCQ], rgw[kDecCQ];
+    if (cached) {
+        const rsrc_t xr = row(0);
+#pragma unroll
+        for (int c = 0; c < kDecCQ; ++c) {
+            const int q = lane + c * kWave;
+            const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);   // past: zeros
+            rx[c] = rgw[c] = v4u{0, 0, 0, 0};
+            if (c * kWave < quads) {       // wave-uniform: no loads past the piece
+                if (bf16) {
+                    rx[c].x = buf_load4(xr, (uint32_t)j * 8u);
+                    rx[c].y = buf_load4(xr, (uint32_t)j * 8u + 4u);
+                } else {
+                    rx[c] = buf_load16(xr, (uint32_t)j * 16u);
+                }
+                if (norm)
+                    rgw[c] = buf_load16(gr, (uint32_t)j * 16u);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     Chunk c0, c1;
     load(c0, t_begin);
     __builtin_amdgcn_sched_barrier(0);
@@ -213,44 +262,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     __shared__ float q_amax[kDecWaves][kDecXldsMaxM];
     __shared__ double q_ss[kDecWaves][kDecXldsMaxM];
     if (QUANT) {
-        const int e0 = t_begin * kSuperWords * 16;                 // first element of the piece
-        const int e1 = min(t_end * kSuperWords, words) * 16;
-        const int quads = (e1 - e0) / 4;
-        const bool norm = p.g != nullptr;
-        const bool bf16 = p.bf16 != 0;
-        const int esize = bf16 ? 2 : 4;
-        const rsrc_t gr = make_rsrc(p.g, norm ? (uint32_t)p.K * 4u : 0u);
-        auto row = [&](int m) {
-            return make_rsrc(static_cast<const unsigned char *>(p.X) + (int64_t)m * p.K * esize,
-                             (uint32_t)p.K * esize);
-        };
-        auto quad_g = [&](int j) {
-            const v4u v = buf_load16(gr, (uint32_t)j * 16u);
-            return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                               __uint_as_float(v.w));
-        };
         // Partial absmax of u (u = x, or fl32(x * g)) and sum of x^2 over this wave's piece.
-        // One token whose piece takes 3 to kDecCQ quads per lane: every load issued at once
-        // and u kept in registers for the quantization pass (the same per-lane order of the
-        // sums: quads past the piece read as zeros and add nothing).  Otherwise one quad per
-        // lane at a time, re-read for the quantization pass (measured faster for short
-        // pieces).
-        const bool cached = p.M == 1 && quads > 2 * kWave && quads <= kDecCQ * kWave;
         const bool first = (int)blockIdx.x == p.block_begin;
-        float4 uc[kDecCQ];
         if (cached) {
-            const rsrc_t xr = row(0);
-            float4 xc[kDecCQ];
 #pragma unroll
             for (int c = 0; c < kDecCQ; ++c) {
-                const int q = lane + c * kWave;
-                const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);   // past: zeros
-                if (c * kWave < quads) {       // wave-uniform: no loads past the piece
-                    xc[c] = load_quad(xr, j, bf16);
-                    uc[c] = norm ? quad_g(j) : xc[c];
-                } else {
-                    xc[c] = uc[c] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                }
+                if (bf16)
+                    xc[c] = make_float4(__uint_as_float(rx[c].x << 16), __uint_as_float(rx[c].x & 0xFFFF0000u),
+                                        __uint_as_float(rx[c].y << 16), __uint_as_float(rx[c].y & 0xFFFF0000u));
+                else
+                    xc[c] = make_float4(__uint_as_float(rx[c].x), __uint_as_float(rx[c].y),
+                                        __uint_as_float(rx[c].z), __uint_as_float(rx[c].w));
+                uc[c] = norm ? make_float4(__uint_as_float(rgw[c].x), __uint_as_float(rgw[c].y),
+                                           __uint_as_float(rgw[c].z), __uint_as_float(rgw[c].w))
+                             : xc[c];
             }
             float amax = 0.0f;
             double ss = 0.0;
@@ -263,7 +288,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
                 amax = fmaxf(amax, absmax4(uc[c]));
             }
             amax = wave_max(amax);
-            ss = wave_sum_fixed(ss);
+            if (norm)
+                ss = wave_sum_fixed(ss);
             if (lane == 0) {
                 q_amax[wave][0] = amax;
                 q_ss[wave][0] = ss;
@@ -275,16 +301,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
                     const rsrc_t xr = row(m);
                     float amax = 0.0f;
                     double ss = 0.0;
-                    for (int q = lane; q < quads; q += kWave) {
-                        const int j = e0 / 4 + q;
-                        const float4 f = load_quad(xr, j, bf16);
-                        const float4 u = norm ? mul4(f, quad_g(j)) : f;
-                        amax = fmaxf(amax, absmax4(u));
-                        if (norm)
-                            ss = sumsq4(ss, f);
+                    for (int q0 = lane; q0 < quads; q0 += 4 * kWave) {
+                        float4 f[4], gq[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {     // four loads in flight (zeros past)
+                            const int q = q0 + u * kWave;
+                            const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);
+                            f[u] = load_quad(xr, j, bf16);
+                            if (norm)
+                                gq[u] = quad_g(j);
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float4 uu = norm ? mul4(f[u], gq[u]) : f[u];
+                            amax = fmaxf(amax, absmax4(uu));
+                            if (norm)
+                                ss = sumsq4(ss, f[u]);
+                        }
                     }
                     amax = wave_max(amax);
-                    ss = wave_sum_fixed(ss);
+                    if (norm)
+                        ss = wave_sum_fixed(ss);
                     if (lane == 0) {
                         q_amax[wave][m] = amax;
                         q_ss[wave][m] = ss;
@@ -320,13 +357,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
                         a = fmaxf(a, q_amax[w][m]);
                     const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
                     const rsrc_t xr = row(m);
-                    for (int q = lane; q < quads; q += kWave) {
-                        const int j = e0 / 4 + q;
-                        const float4 f = load_quad(xr, j, bf16);
-                        const char4 c = quant4(norm ? mul4(f, quad_g(j)) : f, inv);
-                        *reinterpret_cast<char4 *>(xs + (uint32_t)m * p.K + 4u * j) = c;
-                        if (first && p.Xq_out)
-                            *reinterpret_cast<char4 *>(p.Xq_out + (int64_t)m * p.K + 4 * j) = c;
+                    for (int q0 = lane; q0 < quads; q0 += 4 * kWave) {
+                        float4 f[4], gq[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int q = q0 + u * kWave;
+                            const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);
+                            f[u] = load_quad(xr, j, bf16);
+                            if (norm)
+                                gq[u] = quad_g(j);
+                        }
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int q = q0 + u * kWave;
+                            if (q < quads) {
+                                const int j = e0 / 4 + q;
+                                const char4 c = quant4(norm ? mul4(f[u], gq[u]) : f[u], inv);
+                                *reinterpret_cast<char4 *>(xs + (uint32_t)m * p.K + 4u * j) = c;
+                                if (first && p.Xq_out)
+                                    *reinterpret_cast<char4 *>(p.Xq_out + (int64_t)m * p.K + 4 * j) = c;
+                            }
+                        }
                     }
                 }
             }
@@ -426,7 +477,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     }
 }
 
-template <int RG, bool XLDS, bool QUANT = false, bool PAIR = false>
+template <int RG, bool XLDS, bool QUANT = false, bool PAIR = false, bool BF16 = false>
 static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t stream)
 {
     if (blocks == 0)
@@ -436,10 +487,10 @@ static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t
         for (int i = 0; i < b.count; ++i)
             lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
     if (full_k)
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true, PAIR>), dim3(blocks),
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true, PAIR, BF16>), dim3(blocks),
                            dim3(kDecThreads), lds, stream, b);
     else
-        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, false, PAIR>), dim3(blocks),
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, false, PAIR, BF16>), dim3(blocks),
                            dim3(kDecThreads), lds, stream, b);
     return hipGetLastError();
 }
@@ -503,7 +554,7 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *q, int count, hipS
 // Every block quantizes the token rows it needs from the raw activations, so larger blocks
 // (more row groups) read them fewer times: row groups as in the unfused decode launch, by
 // weight rows (a pair's block holds both projections' rows).
-template <int RG, bool PAIR>
+template <int RG, bool PAIR, bool BF16>
 static hipError_t launch_linear_rg(const bl_linear_ex_problem *const *q, int count,
                                    hipStream_t stream)
 {
@@ -539,42 +590,48 @@ static hipError_t launch_linear_rg(const bl_linear_ex_problem *const *q, int cou
         blocks += (d.N + ROWS - 1) / ROWS;
     }
     b.count = count;
-    return launch_batch<RG, true, true, PAIR>(b, blocks, full_k, stream);
+    return launch_batch<RG, true, true, PAIR, BF16>(b, blocks, full_k, stream);
 }
 
+// Row groups per block by weight rows (a pair's block holds both projections' rows; pairs
+// need an even count).
+template <bool PAIR, bool BF16>
+static hipError_t launch_linear_kind(const bl_linear_ex_problem *const *q, int n, int64_t wrows,
+                                     hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    if (wrows >= 256 * 64)
+        return launch_linear_rg<4, PAIR, BF16>(q, n, stream);
+    if constexpr (PAIR) {
+        return launch_linear_rg<2, PAIR, BF16>(q, n, stream);
+    } else {
+        if (wrows >= 256 * 32)
+            return launch_linear_rg<2, PAIR, BF16>(q, n, stream);
+        return launch_linear_rg<1, PAIR, BF16>(q, n, stream);
+    }
+}
+
+// One launch per kind present: single projections or gated pairs, fp32 or bf16 activations.
 hipError_t launch_linear_decode(const bl_linear_ex_problem *q, int count, hipStream_t stream)
 {
-    const bl_linear_ex_problem *single[BL_MAX_GROUP], *pair[BL_MAX_GROUP];
-    int ns = 0, np = 0;
-    int64_t rows_s = 0, rows_p = 0;
+    const bl_linear_ex_problem *part[4][BL_MAX_GROUP];
+    int n[4] = {0, 0, 0, 0};
+    int64_t rows[4] = {0, 0, 0, 0};
     for (int i = 0; i < count; ++i) {
         if (q[i].M == 0 || q[i].N == 0)
             continue;
-        if (q[i].W2_packed) {
-            pair[np++] = &q[i];
-            rows_p += 2 * q[i].N;
-        } else {
-            single[ns++] = &q[i];
-            rows_s += q[i].N;
-        }
+        const int k = (q[i].W2_packed ? 2 : 0) + (q[i].x_dtype == BL_BF16 ? 1 : 0);
+        part[k][n[k]++] = &q[i];
+        rows[k] += (q[i].W2_packed ? 2 : 1) * q[i].N;
     }
-    hipError_t e = hipSuccess;
-    if (ns) {
-        if (rows_s >= 256 * 64)
-            e = launch_linear_rg<4, false>(single, ns, stream);
-        else if (rows_s >= 256 * 32)
-            e = launch_linear_rg<2, false>(single, ns, stream);
-        else
-            e = launch_linear_rg<1, false>(single, ns, stream);
-        if (e != hipSuccess)
-            return e;
-    }
-    if (np) {
-        if (rows_p >= 256 * 64)
-            e = launch_linear_rg<4, true>(pair, np, stream);
-        else
-            e = launch_linear_rg<2, true>(pair, np, stream);
-    }
+    hipError_t e = launch_linear_kind<false, false>(part[0], n[0], rows[0], stream);
+    if (e == hipSuccess)
+        e = launch_linear_kind<false, true>(part[1], n[1], rows[1], stream);
+    if (e == hipSuccess)
+        e = launch_linear_kind<true, false>(part[2], n[2], rows[2], stream);
+    if (e == hipSuccess)
+        e = launch_linear_kind<true, true>(part[3], n[3], rows[3], stream);
     return e;
 }
 
