@@ -86,6 +86,12 @@ class Oracle:
         lib.oracle_grad_weight.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, ctypes.c_int,
                                            ctypes.c_double, _I64, _I64, _I64, _P]
         lib.oracle_grad_weight.restype = None
+        lib.oracle_b3_row_bytes.argtypes = [_I64]
+        lib.oracle_b3_row_bytes.restype = _I64
+        lib.oracle_pack_b3.argtypes = [_P, _I64, _I64, _P]
+        lib.oracle_pack_b3.restype = ctypes.c_int
+        lib.oracle_unpack_b3.argtypes = [_P, _I64, _I64, _P]
+        lib.oracle_unpack_b3.restype = ctypes.c_int
 
     # O1
     def gamma(self, W: np.ndarray) -> Tuple[np.float32, float]:
@@ -283,6 +289,30 @@ class Oracle:
         self._lib.oracle_grad_weight(_ptr(dY), _ptr(Xq), _ptr(sx), _ptr(Xf), _ptr(W if kind else None),
                                      float(np.float32(gamma)), int(kind), float(beta), M, N, K, _ptr(dW))
         return dW
+
+
+    # O13: base-3 packing
+    def b3_row_bytes(self, K: int) -> int:
+        return int(self._lib.oracle_b3_row_bytes(int(K)))
+
+    def pack_b3(self, codes: np.ndarray) -> np.ndarray:
+        codes = _c(codes, np.int8)
+        N, K = codes.shape
+        out = np.empty((N, self.b3_row_bytes(K)), dtype=np.uint8)
+        rc = self._lib.oracle_pack_b3(_ptr(codes), N, K, _ptr(out))
+        if rc:
+            raise ValueError(f"oracle_pack_b3 failed: {rc}")
+        return out
+
+    def unpack_b3(self, packed: np.ndarray, K: int) -> np.ndarray:
+        packed = _c(packed, np.uint8)
+        N = packed.shape[0]
+        assert packed.shape[1] == self.b3_row_bytes(K)
+        codes = np.empty((N, K), dtype=np.int8)
+        rc = self._lib.oracle_unpack_b3(_ptr(packed), N, K, _ptr(codes))
+        if rc:
+            raise ValueError(f"oracle_unpack_b3 failed: {rc}")
+        return codes
 
 
 _default: Optional[Oracle] = None

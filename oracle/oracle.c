@@ -67,6 +67,15 @@
  *                  forward.  gamma's own dependence on W is not differentiated (a reading: the
  *                  STE treats W_q * gamma as W).
  *
+ * Base-3 packing (the denser weight format, for the decode product):
+ *   O13 packing  — five ternary codes per byte (3^5 = 243 <= 256), 1.6 bits per weight: the
+ *                  bitone README's "3B parameter model fits in 600 MB" and its size table
+ *                  (700M -> 0.14 GB, 3B -> 0.6 GB, 8B -> 1.6 GB) are 1.6 bits per weight.  Layout (a
+ *                  reading; the pages give only the density): a row of K weights is cut into
+ *                  blocks of 80 (16 bytes, the last block padded with code 0); byte b of block j
+ *                  holds the five weights k = 80j + 16i + b, i = 0..4, as the base-3 number
+ *                  sum_i (c_k + 1) * 3^i (values 0..242).  Row n takes 16 * ceil(K / 80) bytes.
+ *
  * Degenerate data (defined here, the pages are silent): gamma == 0 gives all codes 0; a row
  * with absmax 0 gives q = 0 and s_x = 0.  NaN inputs are outside the method's domain; where
  * a comparison meets a NaN the result is code 0.
@@ -412,4 +421,57 @@ void oracle_grad_weight(const float *dY, const int8_t *Xq, const float *s_x, con
             const double sc = kind == 0 ? 1.0 : oracle_ste_scale(kind, W[n * K + k], gamma, beta);
             dW[n * K + k] = (float)(sc * s);
         }
+}
+
+/* ------------------------------------------------------------- O13: base-3 packing */
+
+/* Bytes per row of the base-3 layout. */
+int64_t oracle_b3_row_bytes(int64_t K)
+{
+    return 16 * ((K + 79) / 80);
+}
+
+/* codes [N][K] in {-1, 0, +1} -> bytes [N][16 * ceil(K/80)].  Returns 0, or -2 for a code
+ * outside {-1, 0, +1}. */
+int oracle_pack_b3(const int8_t *codes, int64_t N, int64_t K, uint8_t *out)
+{
+    const int64_t rb = oracle_b3_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < rb / 16; ++j)
+            for (int b = 0; b < 16; ++b) {
+                unsigned v = 0, p = 1;
+                for (int i = 0; i < 5; ++i) {
+                    const int64_t k = 80 * j + 16 * i + b;
+                    int c = 0;
+                    if (k < K) {
+                        c = codes[n * K + k];
+                        if (c < -1 || c > 1)
+                            return -2;
+                    }
+                    v += (unsigned)(c + 1) * p;
+                    p *= 3;
+                }
+                out[n * rb + 16 * j + b] = (uint8_t)v;
+            }
+    return 0;
+}
+
+/* bytes [N][16 * ceil(K/80)] -> codes [N][K].  Returns 0, or -3 for a byte above 242. */
+int oracle_unpack_b3(const uint8_t *in, int64_t N, int64_t K, int8_t *codes)
+{
+    const int64_t rb = oracle_b3_row_bytes(K);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < rb / 16; ++j)
+            for (int b = 0; b < 16; ++b) {
+                unsigned v = in[n * rb + 16 * j + b];
+                if (v > 242)
+                    return -3;
+                for (int i = 0; i < 5; ++i) {
+                    const int64_t k = 80 * j + 16 * i + b;
+                    if (k < K)
+                        codes[n * K + k] = (int8_t)((int)(v % 3) - 1);
+                    v /= 3;
+                }
+            }
+    return 0;
 }

@@ -609,4 +609,61 @@ def pin_grad_weight_brute_force(orc):
             assert dW[n, k] == f32_of_fraction(exact), (n, k)
 
 
+# ------------------------------------------------------------------ O13: base-3 packing
+
+def pin_b3_golden_block(orc):
+    """The hand-derived block of tests/golden/b3_block.json, and the extreme bytes."""
+    gold = golden("b3_block.json")
+    C = np.zeros((1, 80), np.int8)
+    for k, c in gold["block_codes_nonzero"].items():
+        C[0, int(k)] = c
+    assert list(orc.pack_b3(C)[0]) == gold["bytes"]
+    ex = gold["extremes"]
+    assert set(orc.pack_b3(np.ones((1, 80), np.int8))[0]) == {ex["all_plus_one"]}
+    assert set(orc.pack_b3(-np.ones((1, 80), np.int8))[0]) == {ex["all_minus_one"]}
+    assert set(orc.pack_b3(np.zeros((1, 80), np.int8))[0]) == {ex["all_zero"]}
+
+
+def pin_b3_density_matches_the_pages(orc):
+    """1.6 bits per weight: the bitone README's model sizes follow from the row bytes."""
+    for n, gb in golden("b3_block.json")["model_sizes_gb"].items():
+        K = 80 * 1000
+        per_weight = orc.b3_row_bytes(K) / K
+        assert abs(int(n) * per_weight / 1e9 - gb) < 1e-9, (n, gb)
+    assert orc.b3_row_bytes(2560) == 512 and orc.b3_row_bytes(768) == 160
+    assert orc.b3_row_bytes(16) == 16 and orc.b3_row_bytes(80) == 16 and orc.b3_row_bytes(96) == 32
+
+
+def pin_b3_roundtrip_and_range(orc):
+    """unpack(pack(C)) == C for ragged K; every byte <= 242; padding weights are code 0."""
+    for K in (16, 80, 96, 768, 2000):
+        C = workloads.ternary((7, K), (80, K))
+        B = orc.pack_b3(C)
+        assert B.max() <= 242
+        assert np.array_equal(orc.unpack_b3(B, K), C)
+    C = workloads.ternary((3, 16), (81,))
+    B = orc.pack_b3(C)
+    # K = 16: planes 1..4 of the single block are padding (digit 1 each).
+    assert np.array_equal(B.astype(int), C.astype(int) + 1 + 3 + 9 + 27 + 81)
+
+
+def pin_b3_digit_weights_and_locality(orc):
+    """Changing the code of weight k by +1 changes exactly one byte, by 3^i, where
+    k = 80j + 16i + b (byte 16j + b)."""
+    C = np.zeros((2, 400), np.int8)
+    base = orc.pack_b3(C).astype(int)
+    for k in (0, 15, 16, 79, 80, 163, 399):
+        D = C.copy()
+        D[1, k] = 1
+        diff = orc.pack_b3(D).astype(int) - base
+        j, i, b = k // 80, (k % 80) // 16, k % 16
+        assert np.count_nonzero(diff) == 1 and diff[1, 16 * j + b] == 3 ** i, k
+
+
+def pin_b3_agrees_with_two_bit_packing(orc):
+    """The same codes through both layouts: unpack_b3(pack_b3(C)) == unpack(pack(C))."""
+    C = workloads.ternary((9, 320), (82,))
+    assert np.array_equal(orc.unpack_b3(orc.pack_b3(C), 320), orc.unpack(orc.pack(C), 320))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
