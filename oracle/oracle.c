@@ -73,8 +73,9 @@
  *                  (700M -> 0.14 GB, 3B -> 0.6 GB, 8B -> 1.6 GB) are 1.6 bits per weight.  Layout (a
  *                  reading; the pages give only the density): a row of K weights is cut into
  *                  blocks of 80 (16 bytes, the last block padded with code 0); byte b of block j
- *                  holds the five weights k = 80j + 16i + b, i = 0..4, as the base-3 number
- *                  sum_i (c_k + 1) * 3^i (values 0..242).  Row n takes 16 * ceil(K / 80) bytes.
+ *                  holds the five weights k_0..k_4 = 80j + 4b + 0..3 and 80j + 64 + b as the
+ *                  base-3 number sum_i (c_{k_i} + 1) * 3^i (values 0..242).  Row n takes
+ *                  16 * ceil(K / 80) bytes.
  *
  * Degenerate data (defined here, the pages are silent): gamma == 0 gives all codes 0; a row
  * with absmax 0 gives q = 0 and s_x = 0.  NaN inputs are outside the method's domain; where
@@ -425,6 +426,12 @@ void oracle_grad_weight(const float *dY, const int8_t *Xq, const float *s_x, con
 
 /* ------------------------------------------------------------- O13: base-3 packing */
 
+/* Weight index of digit i of byte b in block j. */
+static int64_t b3_weight(int64_t j, int b, int i)
+{
+    return 80 * j + (i < 4 ? 4 * b + i : 64 + b);
+}
+
 /* Bytes per row of the base-3 layout. */
 int64_t oracle_b3_row_bytes(int64_t K)
 {
@@ -441,7 +448,7 @@ int oracle_pack_b3(const int8_t *codes, int64_t N, int64_t K, uint8_t *out)
             for (int b = 0; b < 16; ++b) {
                 unsigned v = 0, p = 1;
                 for (int i = 0; i < 5; ++i) {
-                    const int64_t k = 80 * j + 16 * i + b;
+                    const int64_t k = b3_weight(j, b, i);
                     int c = 0;
                     if (k < K) {
                         c = codes[n * K + k];
@@ -467,7 +474,7 @@ int oracle_unpack_b3(const uint8_t *in, int64_t N, int64_t K, int8_t *codes)
                 if (v > 242)
                     return -3;
                 for (int i = 0; i < 5; ++i) {
-                    const int64_t k = 80 * j + 16 * i + b;
+                    const int64_t k = b3_weight(j, b, i);
                     if (k < K)
                         codes[n * K + k] = (int8_t)((int)(v % 3) - 1);
                     v /= 3;

@@ -642,21 +642,26 @@ def pin_b3_roundtrip_and_range(orc):
         assert B.max() <= 242
         assert np.array_equal(orc.unpack_b3(B, K), C)
     C = workloads.ternary((3, 16), (81,))
-    B = orc.pack_b3(C)
-    # K = 16: planes 1..4 of the single block are padding (digit 1 each).
-    assert np.array_equal(B.astype(int), C.astype(int) + 1 + 3 + 9 + 27 + 81)
+    B = orc.pack_b3(C).astype(int)
+    # K = 16: bytes 0..3 hold weights 4b .. 4b+3 and the padding weight 64 + b (digit 1);
+    # bytes 4..15 hold padding only.
+    for b in range(4):
+        v = sum((C[:, 4 * b + i].astype(int) + 1) * 3 ** i for i in range(4)) + 81
+        assert np.array_equal(B[:, b], v)
+    assert np.all(B[:, 4:] == 121)
 
 
 def pin_b3_digit_weights_and_locality(orc):
-    """Changing the code of weight k by +1 changes exactly one byte, by 3^i, where
-    k = 80j + 16i + b (byte 16j + b)."""
+    """Changing the code of weight k by +1 changes exactly one byte, by 3^i: within block
+    j = k // 80, r = k % 80 < 64 is digit r % 4 of byte r // 4, r >= 64 digit 4 of byte r - 64."""
     C = np.zeros((2, 400), np.int8)
     base = orc.pack_b3(C).astype(int)
-    for k in (0, 15, 16, 79, 80, 163, 399):
+    for k in (0, 3, 15, 16, 63, 64, 79, 80, 163, 399):
         D = C.copy()
         D[1, k] = 1
         diff = orc.pack_b3(D).astype(int) - base
-        j, i, b = k // 80, (k % 80) // 16, k % 16
+        j, r = k // 80, k % 80
+        b, i = (r // 4, r % 4) if r < 64 else (r - 64, 4)
         assert np.count_nonzero(diff) == 1 and diff[1, 16 * j + b] == 3 ** i, k
 
 

@@ -73,8 +73,8 @@ MUTANTS = {
                                     "oracle_ste_scale(kind, W[k * N + n], gamma, beta)"),
     "grad_weight_dy_transposed": ("s += (double)dY[m * N + n] * xh;", "s += (double)dY[n * M + m] * xh;"),
     "b3_digit_without_offset": ("v += (unsigned)(c + 1) * p;", "v += (unsigned)(c + 3) % 3 * p;"),
-    "b3_plane_mapping": ("const int64_t k = 80 * j + 16 * i + b;\n                    int c = 0;",
-                         "const int64_t k = 80 * j + 5 * b + i;\n                    int c = 0;"),
+    "b3_plane_mapping": ("return 80 * j + (i < 4 ? 4 * b + i : 64 + b);", "return 80 * j + 16 * i + b;"),
+    "b3_last_digit_mapping": ("return 80 * j + (i < 4 ? 4 * b + i : 64 + b);", "return 80 * j + (i < 4 ? 4 * b + i : 79 - b);"),
     "b3_base_four": ("p *= 3;", "p *= 4;"),
     "b3_unpack_sign": ("codes[n * K + k] = (int8_t)((int)(v % 3) - 1);", "codes[n * K + k] = (int8_t)(1 - (int)(v % 3));"),
     "b3_padding_minus_one": ("                    int c = 0;\n                    if (k < K) {", "                    int c = -1;\n                    if (k < K) {"),
