@@ -145,6 +145,9 @@ class Setup:
         packed_bytes = sum(p.numel() * 4 for p, _ in dec_packed)
         self.R_dec = int(max(1, min(4096, np.ceil(rotate_bytes / packed_bytes))))
         self.P_dec = [[p.clone() for p, _ in dec_packed] for _ in range(self.R_dec)]
+        # The same decode weights in the base-3 layout (five codes per byte), for the
+        # base-3 decode figure reported beside the step (not part of the step).
+        self.B3_dec = [[bl.pack_b3(p) for p in Ps] for Ps in self.P_dec]
         self.g_dec = [g.clone() for _, g in dec_packed]
         self.X_dec = [to_dev(x) for x in X_dec]
 
@@ -204,6 +207,18 @@ class Setup:
                                            self.Y_dec[i].data_ptr(), None, None,
                                            self.M_dec, m.N, m.K, dt, 1e-6)
             self.lin_dec_tables.append(arr)
+        self.lin_dec_b3_tables = []
+        for r in range(self.R_dec):
+            arr = (bl._LinearProblem * n)()
+            for i, m in enumerate(mats):
+                X = self.X_dec[i]
+                g = self.norms[i]
+                dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
+                arr[i] = bl._LinearProblem(X.data_ptr(), None if g is None else g.data_ptr(),
+                                           self.B3_dec[r][i].data_ptr(), self.g_dec[i].data_ptr(),
+                                           self.Y_dec[i].data_ptr(), None, None,
+                                           self.M_dec, m.N, m.K, dt, 1e-6)
+            self.lin_dec_b3_tables.append(arr)
         import ctypes as C
         self._addr = C.addressof
         self.ws_ptr = self.ws.data_ptr()
@@ -219,6 +234,12 @@ class Setup:
         M = self.M_dec
         xb = 2 if self.wl.x_dtype == "bf16" else 4
         return sum(m.N * m.K // 4 + M * m.K * xb + (4 * m.K if m.norm else 0) + 4 + 4 * M * m.N
+                   for m in self.wl.matrices)
+
+    def decode_b3_bytes(self) -> int:
+        M = self.M_dec
+        xb = 2 if self.wl.x_dtype == "bf16" else 4
+        return sum(m.N * self.bl.b3_row_bytes(m.K) + M * m.K * xb + (4 * m.K if m.norm else 0) + 4 + 4 * M * m.N
                    for m in self.wl.matrices)
 
     def prefill_bytes(self) -> int:
@@ -273,6 +294,8 @@ class Setup:
             rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
         elif key == "decode_linear":
             rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
+        elif key == "decode_linear_b3":
+            rc = L.bitlinear_linear_b3_grouped(self._addr(self.lin_dec_b3_tables[i % self.R_dec]), n, stream)
         elif key == "act_quant_prefill":
             rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[i % self.R_pre]), n, stream)
         else:
@@ -697,6 +720,7 @@ def main():
         in_step.pop("weight_quant")
     ms_with_events = interval_ms(ev, "t0", "t_dec")
     ms = {k: isolated_ms(torch, setup, k, args.steps) for k in in_step}
+    ms_b3 = isolated_ms(torch, setup, "decode_linear_b3", args.steps)
 
     ops = setup.prefill_ops()
     pre_bytes = setup.prefill_bytes()
@@ -768,7 +792,12 @@ def main():
                    "weights": wl.weights, "x_dtype": wl.x_dtype,
                    "rotation_copies": {"prefill": setup.R_pre, "decode": setup.R_dec}},
         "decode": {"gbps": round(dec_gbps, 2), "frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "bytes": dec_bytes, "us_linear": round(ms["decode_linear"] * 1e3, 3)},
+                   "bytes": dec_bytes, "us_linear": round(ms["decode_linear"] * 1e3, 3),
+                   "base3": {"us_linear": round(ms_b3 * 1e3, 3), "bytes": setup.decode_b3_bytes(),
+                             "gbps": round(setup.decode_b3_bytes() / (ms_b3 * 1e-3) / 1e9, 2),
+                             "speedup_vs_two_bit": round(ms["decode_linear"] / ms_b3, 3),
+                             "note": "same codes in the base-3 layout (1.6 bits per weight), "
+                                     "fused decode call; not part of the step"}},
         "prefill": {"gemm_tops": round(gemm_tops, 2), "frac_int8": round(gemm_tops / INT8_PEAK_TOPS, 4),
                     "gemm_gbps": round(gemm_gbps, 1), "ops_per_byte": round(ai, 1),
                     "frac_attainable": round(gemm_tops / attainable, 4),

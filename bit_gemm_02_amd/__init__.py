@@ -169,6 +169,12 @@ def lib() -> ctypes.CDLL:
         getattr(L, fn).restype = ctypes.c_int
     L.bitlinear_transpose_packed.argtypes = [P, I64, I64, P, P]
     L.bitlinear_transpose_packed.restype = ctypes.c_int
+    L.bitlinear_b3_row_bytes.argtypes = [I64]
+    L.bitlinear_b3_row_bytes.restype = I64
+    L.bitlinear_pack_b3.argtypes = [P, I64, I64, P, P]
+    L.bitlinear_pack_b3.restype = ctypes.c_int
+    L.bitlinear_linear_b3_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_linear_b3_grouped.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -553,3 +559,46 @@ def grad_weight(dY: torch.Tensor, X_q: torch.Tensor, x_scale: torch.Tensor, gamm
     grad_weight_grouped([dict(dY=dY, X_q=X_q, x_scale=x_scale, gamma=gamma, dW=dW, W=W, ste=ste,
                               beta=beta)], stream)
     return dW
+
+
+# ------------------------------------------------------------- base-3 weights
+
+def b3_row_bytes(K: int) -> int:
+    """Bytes per row of the base-3 layout (five codes per byte, 80 weights per 16 bytes)."""
+    return int(lib().bitlinear_b3_row_bytes(int(K)))
+
+
+def pack_b3(W_packed: torch.Tensor, K: Optional[int] = None, W_b3: Optional[torch.Tensor] = None,
+            stream=None) -> torch.Tensor:
+    """Two-bit packed codes [N, K/16] -> base-3 bytes (uint8 [N, b3_row_bytes(K)])."""
+    _dev(W_packed, "W_packed", torch.int32)
+    N = W_packed.shape[0]
+    K = W_packed.shape[1] * 16 if K is None else K
+    if W_b3 is None:
+        W_b3 = torch.empty((N, b3_row_bytes(K)), dtype=torch.uint8, device=W_packed.device)
+    _check("bitlinear_pack_b3", lib().bitlinear_pack_b3(_ptr(W_packed), N, K, _ptr(W_b3), _stream(stream)))
+    return W_b3
+
+
+def linear_b3_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_linear_b3_grouped: dicts as for linear_grouped, with
+    W_b3 (uint8 [N, b3_row_bytes(K)]) in place of W_packed."""
+    arr = (_LinearProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        Wb = _dev(p["W_b3"], f"W_b3[{i}]", torch.uint8)
+        N = Wb.shape[0]
+        if Wb.shape[1] != b3_row_bytes(K):
+            raise ValueError(f"W_b3[{i}] must be [N, b3_row_bytes(K)]")
+        arr[i] = _LinearProblem(_ptr(X), _ptr(p.get("norm_weight")), _ptr(Wb), _ptr(p["gamma"]),
+                                _ptr(p["Y"]), _ptr(p.get("X_q")), _ptr(p.get("x_scale")), M, N, K,
+                                _x_dtype(X), float(p.get("eps", 1e-6)))
+    return arr
+
+
+def linear_b3_grouped(problems: Sequence[dict], stream=None) -> None:
+    """The fused decode layer call on base-3 weights (every call decode-sized)."""
+    arr = linear_b3_table(problems)
+    _check("bitlinear_linear_b3_grouped",
+           lib().bitlinear_linear_b3_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))

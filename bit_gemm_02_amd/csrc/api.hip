@@ -588,4 +588,50 @@ bl_status bitlinear_grad_weight_grouped(const bl_grad_weight_problem *problems, 
     return from_hip(bl::launch_grad_weight(problems, count, static_cast<hipStream_t>(stream)));
 }
 
+int64_t bitlinear_b3_row_bytes(int64_t K)
+{
+    return K <= 0 ? 0 : 16 * ((K + 79) / 80);
+}
+
+bl_status bitlinear_pack_b3(const uint32_t *W_packed, int64_t N, int64_t K, uint8_t *W_b3,
+                            void *stream)
+{
+    bl_status s = check_rows(N);
+    if (s == BL_OK && N != 0 && (!W_packed || !W_b3))
+        return BL_ERR_NULL;
+    if (s == BL_OK)
+        s = check_k(K);
+    if (s != BL_OK)
+        return s;
+    if (N * ((K + 79) / 80) > (int64_t)INT_MAX * 256)
+        return BL_ERR_SHAPE;
+    if (!aligned16(W_packed) || !aligned16(W_b3))
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_pack_b3(W_packed, N, K, W_b3, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl_linear_ex_problem ex[BL_MAX_GROUP];
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_linear_problem &p = problems[i];
+        const bool empty = p.M == 0 || p.N == 0;
+        if (!empty && !linear_fused(p))
+            return BL_ERR_SHAPE;         // only the fused form exists
+        bl_status s = check_linear(p);
+        if (s != BL_OK)
+            return s;
+        ex[i] = to_ex(p);
+        blocks += (p.N + 15) / 16;
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    return from_hip(bl::launch_linear_decode_b3(ex, count, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

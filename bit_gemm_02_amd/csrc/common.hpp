@@ -238,6 +238,10 @@ hipError_t launch_transpose_packed(const uint32_t *P, int64_t N, int64_t K, uint
                                    hipStream_t stream);
 hipError_t launch_grad_weight(const bl_grad_weight_problem *p, int count, hipStream_t stream);
 
+// Base-3 weights (five codes per byte): the packer and the fused decode call on them.
+hipError_t launch_pack_b3(const uint32_t *P, int64_t N, int64_t K, uint8_t *out, hipStream_t stream);
+hipError_t launch_linear_decode_b3(const bl_linear_ex_problem *p, int count, hipStream_t stream);
+
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.
 constexpr int64_t kDecodeMaxM = 16;
 

@@ -55,6 +55,8 @@ struct FwdDev {
     int act;
 };
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
 struct FwdBatch {
     FwdDev p[BL_MAX_GROUP];
     int count;
@@ -73,6 +75,44 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
                        __uint_as_float(v.w));
 }
 
+// Base-3 weights (five codes per byte in blocks of 80 weights per 16 bytes; byte b of a block
+// holds weights 4b .. 4b+3 and 64 + b as sum_i (c + 1) * 3^i): the four dwords of a block give
+// five 16-byte MFMA operands, weights 0..15, 16..31, 32..47, 48..63 and 64..79 of the block,
+// each byte 64 * c as in the two-bit planes.  Each block keeps a 256-entry table in LDS:
+// entry v holds the codes of byte value v, the first four (consecutive weights) in one dword
+// and the fifth in the low byte of a second.  Dword d of the block (bytes 4d .. 4d+3) then
+// gives operand d as the four first dwords of its bytes' entries, unchanged, and dword d of
+// operand 4 from the four second dwords with two v_perm_b32 selects.  (Digits extracted
+// arithmetically, q = (v * 171) >> 9 = floor(v / 3) in 16-bit lanes, and a layout that
+// needed a 4 x 4 byte transpose after the lookup both measured slower.)
+__device__ __forceinline__ void b3_table_entry(uint32_t v, uint32_t &lo, uint32_t &hi)
+{
+    uint32_t c[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const uint32_t d = v % 3u;                     // digit = code + 1
+        c[i] = d == 0 ? 0xC0u : (d == 1 ? 0x00u : 0x40u);
+        v /= 3u;
+    }
+    lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    hi = c[4];
+}
+
+// Dword d of a block -> operand d (four dwords) and dword d of operand 4.
+__device__ __forceinline__ void unpack_b3_dword(uint32_t w, const uint32_t *lut, v4i &op, uint32_t &op4)
+{
+    uint32_t a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t idx = (w >> (8 * e)) & 0xFFu;
+        const v2u ent = *reinterpret_cast<const v2u *>(lut + 2 * idx);
+        a[e] = ent.x;
+        b[e] = ent.y;
+    }
+    op = v4i{(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+    op4 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u) | __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);
+}
+
 // FULL_K: every problem of the launch has K % 256 == 0, so super-steps never run past a
 // row and rows are 64-byte aligned (one 16-byte load per lane, no tail masking).
 // QUANT (with XLDS): the fused decode form.  The activations arrive unquantized;
@@ -84,11 +124,23 @@ __device__ __forceinline__ float4 load_quad(rsrc_t xr, int j, bool bf16)
 // PAIR (fused form only): a gated pair of projections with one set of activations; the
 // block's first RG/2 row groups are rows of W, the other RG/2 the same rows of W2, and the
 // epilogue combines the two outputs of each row through the activation.
-template <int RG, bool XLDS, bool QUANT, bool FULL_K, bool PAIR = false, bool BF16 = false>
+// B3 (fused form only): base-3 weights; a super-step is 320 weights (four 16-byte blocks a
+// row, one per lane group), five MFMAs per row group.
+template <int RG, bool XLDS, bool QUANT, bool FULL_K, bool PAIR = false, bool BF16 = false,
+          bool B3 = false>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
 {
     static_assert(!QUANT || XLDS, "the fused form stages codes in LDS");
     static_assert(!PAIR || (QUANT && RG % 2 == 0), "pairs: fused form, even row groups");
+    static_assert(!B3 || QUANT, "base-3 weights: fused form");
+    constexpr int EPS = B3 ? 320 : 256;    // weights per super-step
+    // Base-3 decode table (ready after the quantization phase's barrier).
+    __shared__ __align__(8) uint32_t b3lut[B3 ? 512 : 2];
+    if (B3) {
+        uint32_t lo, hi;
+        b3_table_entry(threadIdx.x, lo, hi);     // 256 threads, one entry each
+        *reinterpret_cast<v2u *>(b3lut + 2 * threadIdx.x) = v2u{lo, hi};
+    }
     constexpr int GN = PAIR ? RG / 2 : RG;    // row groups of output rows per block
     constexpr int ROWS = 16 * GN;
     // Super-steps per chunk (two chunks of loads in flight).  Four per chunk measured slower:
@@ -110,8 +162,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int r = lane & 15;
     const int g = lane >> 4;
-    const int words = p.K / 16;
-    const int row_bytes = p.K / 4;
+    const int row_bytes = B3 ? 16 * ((p.K + 79) / 80) : p.K / 4;
+    const int words = row_bytes / 4;
     // Weight rows n0 .. n0+ROWS-1 (rows past N read as zero); tokens 0 .. M-1 (rows past M
     // read as zero: their offsets r * K + ... lie at or past M * K).
     const rsrc_t wres = make_rsrc(p.W + (int64_t)n0 * words, rows_bytes(n0, ROWS, p.N, row_bytes));
@@ -143,7 +195,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
                 const bool second = PAIR && q >= GN;
                 const rsrc_t res = second ? wres2 : wres;
                 const uint32_t rowoff = wbase + (uint32_t)(second ? q - GN : q) * gstride;
-                if (FULL_K) {
+                if (B3) {
+                    // Rows are whole 16-byte blocks: a block is all in or all past the row.
+                    const int blk = (t0 + u) * 4 + g;
+                    c.w[u][q] = buf_load16(res, live && blk < row_bytes / 16 ? rowoff + 16u * blk : kOOB);
+                } else if (FULL_K) {
                     c.w[u][q] = buf_load16(res, live ? rowoff + 4u * w : kOOB);
                 } else {
 #pragma unroll
@@ -176,6 +232,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     for (int q = 0; q < RG; ++q)
         acc[q] = v4i{0, 0, 0, 0};
     auto compute = [&](const Chunk &c, int t0) {
+        if constexpr (B3) {
+#pragma unroll
+            for (int u = 0; u < kDecPF; ++u) {
+                // Operand i of lane group g's block: 16-weight chunk 20 (t0 + u) + 5g + i.
+                v4i a[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    const int ch = (t0 + u) * 20 + 5 * g + i;
+                    const bool ok = r < p.M && (t0 + u) < t_end && ch < p.K / 16;
+                    a[i] = *reinterpret_cast<const v4i *>(xs + (ok ? xbase + 16u * ch : zero_off));
+                }
+#pragma unroll
+                for (int q = 0; q < RG; ++q) {
+                    v4i op[4];
+                    uint32_t op4[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        unpack_b3_dword(c.w[u][q][v], b3lut, op[v], op4[v]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], op[i], acc[q], 0, 0, 0);
+                    acc[q] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        a[4], v4i{(int)op4[0], (int)op4[1], (int)op4[2], (int)op4[3]}, acc[q], 0, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < kDecPF; ++u)
 #pragma unroll
@@ -206,8 +289,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     // is: left alone, the compiler sinks it below the next multiplies, halving the loads in
     // flight.)
     // Fused form: this wave's piece of the activations, elements [e0, e1) of each token row.
-    const int e0 = t_begin * kSuperWords * 16;
-    const int e1 = min(t_end * kSuperWords, words) * 16;
+    const int e0 = t_begin * EPS;
+    const int e1 = min(t_end * EPS, p.K);
     const int quads = (e1 - e0) / 4;
     const bool norm = QUANT && p.g != nullptr;
     constexpr bool bf16 = BF16;      // the activation dtype is a launch-wide constant
@@ -477,7 +560,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(FwdBatch b)
     }
 }
 
-template <int RG, bool XLDS, bool QUANT = false, bool PAIR = false, bool BF16 = false>
+template <int RG, bool XLDS, bool QUANT = false, bool PAIR = false, bool BF16 = false, bool B3 = false>
 static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t stream)
 {
     if (blocks == 0)
@@ -486,7 +569,10 @@ static hipError_t launch_batch(FwdBatch &b, int blocks, bool full_k, hipStream_t
     if (XLDS)
         for (int i = 0; i < b.count; ++i)
             lds = std::max(lds, (size_t)b.p[i].M * (size_t)b.p[i].K + 16 * kDecWaves);
-    if (full_k)
+    if (B3)      // rows are whole blocks: no ragged-word form
+        hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true, PAIR, BF16, B3>), dim3(blocks),
+                           dim3(kDecThreads), lds, stream, b);
+    else if (full_k)
         hipLaunchKernelGGL((decode_kernel<RG, XLDS, QUANT, true, PAIR, BF16>), dim3(blocks),
                            dim3(kDecThreads), lds, stream, b);
     else
@@ -554,7 +640,7 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *q, int count, hipS
 // Every block quantizes the token rows it needs from the raw activations, so larger blocks
 // (more row groups) read them fewer times: row groups as in the unfused decode launch, by
 // weight rows (a pair's block holds both projections' rows).
-template <int RG, bool PAIR, bool BF16>
+template <int RG, bool PAIR, bool BF16, bool B3 = false>
 static hipError_t launch_linear_rg(const bl_linear_ex_problem *const *q, int count,
                                    hipStream_t stream)
 {
@@ -590,7 +676,7 @@ static hipError_t launch_linear_rg(const bl_linear_ex_problem *const *q, int cou
         blocks += (d.N + ROWS - 1) / ROWS;
     }
     b.count = count;
-    return launch_batch<RG, true, true, PAIR, BF16>(b, blocks, full_k, stream);
+    return launch_batch<RG, true, true, PAIR, BF16, B3>(b, blocks, full_k, stream);
 }
 
 // Row groups per block by weight rows (a pair's block holds both projections' rows; pairs
@@ -632,6 +718,39 @@ hipError_t launch_linear_decode(const bl_linear_ex_problem *q, int count, hipStr
         e = launch_linear_kind<true, false>(part[2], n[2], rows[2], stream);
     if (e == hipSuccess)
         e = launch_linear_kind<true, true>(part[3], n[3], rows[3], stream);
+    return e;
+}
+
+// The fused decode call on base-3 weights (single projections, no epilogue stages): row
+// groups as for the two-bit form, by weight rows.
+template <bool BF16>
+static hipError_t launch_b3_kind(const bl_linear_ex_problem *const *q, int n, int64_t rows,
+                                 hipStream_t stream)
+{
+    if (n == 0)
+        return hipSuccess;
+    if (rows >= 256 * 64)
+        return launch_linear_rg<4, false, BF16, true>(q, n, stream);
+    if (rows >= 256 * 32)
+        return launch_linear_rg<2, false, BF16, true>(q, n, stream);
+    return launch_linear_rg<1, false, BF16, true>(q, n, stream);
+}
+
+hipError_t launch_linear_decode_b3(const bl_linear_ex_problem *q, int count, hipStream_t stream)
+{
+    const bl_linear_ex_problem *part[2][BL_MAX_GROUP];
+    int n[2] = {0, 0};
+    int64_t rows[2] = {0, 0};
+    for (int i = 0; i < count; ++i) {
+        if (q[i].M == 0 || q[i].N == 0)
+            continue;
+        const int k = q[i].x_dtype == BL_BF16 ? 1 : 0;
+        part[k][n[k]++] = &q[i];
+        rows[k] += q[i].N;
+    }
+    hipError_t e = launch_b3_kind<false>(part[0], n[0], rows[0], stream);
+    if (e == hipSuccess)
+        e = launch_b3_kind<true>(part[1], n[1], rows[1], stream);
     return e;
 }
 

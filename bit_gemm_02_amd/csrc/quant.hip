@@ -811,4 +811,48 @@ hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream
     return hipSuccess;
 }
 
+// Two-bit packed rows -> base-3 rows (five codes per byte, 80 weights per 16-byte block; byte
+// b of block j holds weights 80j + 4b + i, i = 0..3, and 80j + 64 + b as sum_i (c + 1) * 3^i).
+// One thread per output block, which reads input words 5j .. 5j+4 (word 5j + w holds weights
+// 80j + 16w .. +15); words past the row are padding (code 0).
+__global__ __launch_bounds__(256) void pack_b3_kernel(const uint32_t *P, int K, uint8_t *out,
+                                                      int64_t total)
+{
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total)
+        return;
+    const int bpr = (K + 79) / 80, words = K / 16;
+    const int64_t n = t / bpr;
+    const int j = (int)(t % bpr);
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+        w[i] = 5 * j + i < words ? P[n * words + 5 * j + i] : 0u;
+    v4u o = v4u{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        uint32_t v = 0, pw = 1;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int k = i < 4 ? 4 * b + i : 64 + b;          // weight within the block
+            const int kk = k & 15;                              // = 4 * plane + byte in its word
+            const uint32_t f = (w[k >> 4] >> (8 * (kk & 3) + 2 * (kk >> 2))) & 3u;   // 00, 01, 11
+            v += ((f + 1u) & 3u) * pw;                          // digit c + 1
+            pw *= 3u;
+        }
+        o[b >> 2] |= v << (8 * (b & 3));
+    }
+    *reinterpret_cast<v4u *>(out + n * 16 * bpr + 16 * j) = o;
+}
+
+hipError_t launch_pack_b3(const uint32_t *P, int64_t N, int64_t K, uint8_t *out, hipStream_t stream)
+{
+    const int64_t total = N * ((K + 79) / 80);
+    if (total == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pack_b3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       P, (int)K, out, total);
+    return hipGetLastError();
+}
+
 }  // namespace bl

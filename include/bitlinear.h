@@ -444,6 +444,36 @@ typedef struct {
 bl_status bitlinear_grad_weight_grouped(const bl_grad_weight_problem *problems, int count,
                                         void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Base-3 weights: five codes per byte, 1.6 bits per weight.
+ *
+ * bitone README, "What is bitone?" and its size table: a 3B-parameter model in 600 MB (700M in
+ * 0.14 GB, 8B in 1.6 GB), i.e. 1.6 bits per weight (3^5 = 243 <= 256).  Layout (a reading; the
+ * pages give only the density): each row of K weights is cut into blocks of 80 weights stored
+ * in 16 bytes (the last block padded with code 0); byte b of block j holds the five weights
+ * k = 80j + 4b + 0..3 and 80j + 64 + b, as the base-3 number sum_i (c_{k_i} + 1) * 3^i (0..242:
+ * digit i of the first four is weight 4b + i).  A row takes
+ * bitlinear_b3_row_bytes(K) = 16 * ceil(K / 80) bytes; rows are contiguous.  The decode product
+ * reads 20 % fewer weight bytes than the two-bit layout (K a multiple of 80) and expands the
+ * codes with integer arithmetic in registers.
+ * ------------------------------------------------------------------------------------- */
+int64_t bitlinear_b3_row_bytes(int64_t K);
+
+/* Two-bit packed codes W_packed [N][K/16] -> base-3 bytes W_b3 [N][bitlinear_b3_row_bytes(K)].
+ * N == 0 is a no-op.  Errors: BL_ERR_NULL, BL_ERR_SHAPE (as bitlinear_pack_codes),
+ * BL_ERR_ALIGN (both 16-byte aligned). */
+bl_status bitlinear_pack_b3(const uint32_t *W_packed, int64_t N, int64_t K, uint8_t *W_b3,
+                            void *stream);
+
+/* The fused decode layer call (bitlinear_linear_grouped's fused form: activation quantization,
+ * product and epilogue in one launch) on base-3 weights: each problem's W_packed points to the
+ * problem's base-3 bytes [N][bitlinear_b3_row_bytes(K)] (16-byte aligned).  Results are
+ * bit-identical to bitlinear_linear_grouped on the same codes in the two-bit layout.  Every
+ * problem with M > 0 and N > 0 needs M <= BL_LINEAR_FUSED_MAX_M and M * K <=
+ * BL_LINEAR_FUSED_MAX_BYTES (BL_ERR_SHAPE otherwise); X_q and x_scale are optional outputs.
+ * Errors as for bitlinear_linear_grouped. */
+bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int count, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -314,6 +314,35 @@ def test_training_entry_points_validation(L, bl):
     assert gwt(N=0, dW=None) == BL_OK
 
 
+def test_b3_entry_points_validation(L, bl):
+    assert L.bitlinear_b3_row_bytes(80) == 16 and L.bitlinear_b3_row_bytes(96) == 32
+    assert L.bitlinear_b3_row_bytes(2560) == 512 and L.bitlinear_b3_row_bytes(0) == 0
+    pk = L.bitlinear_pack_b3
+    assert pk(None, 4, 64, B, None) == BL_ERR_NULL
+    assert pk(A, 4, 40, B, None) == BL_ERR_SHAPE
+    assert pk(A, -1, 64, B, None) == BL_ERR_SHAPE
+    assert pk(A + 4, 4, 64, B, None) == BL_ERR_ALIGN
+    assert pk(None, 0, 64, None, None) == BL_OK
+    g = L.bitlinear_linear_b3_grouped
+
+    def call(**kw):
+        d = dict(X=A, norm_weight=None, W_packed=B, gamma=C, Y=D, X_q=None, x_scale=None,
+                 M=1, N=4, K=64, x_dtype=0, eps=1e-6)
+        d.update(kw)
+        arr = (bl._LinearProblem * 1)()
+        arr[0] = bl._LinearProblem(**d)
+        return g(ctypes.addressof(arr), 1, None)
+
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert call(X=None) == BL_ERR_NULL
+    assert call(M=5) == BL_ERR_SHAPE              # fused form only
+    assert call(M=2, K=32768) == BL_ERR_SHAPE
+    assert call(K=40) == BL_ERR_SHAPE
+    assert call(x_dtype=2) == BL_ERR_DTYPE
+    assert call(W_packed=B + 4) == BL_ERR_ALIGN
+    assert call(M=0) == BL_OK
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):
