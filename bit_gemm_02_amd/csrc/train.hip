@@ -408,8 +408,11 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
     // Per stage: the tokens' rows from column n0 (k0) on; tokens past M read zero.  Columns
     // past N (K) belong to the next row: they only reach dW rows (columns) that are not
     // stored.  A thread stages four tokens x four columns of dY and of q (units of
-    // 8 token quads x 32 column quads).
-    const int tq = tid >> 5, c4 = (tid & 31) * 4;
+    // 8 token quads x 32 column quads).  Lane l of a half-wave takes token quad l % 8 and
+    // column quad l / 8: its four 8-byte LDS stores (one per column) then fall in 32 distinct
+    // 8-byte bank slots (columns four apart are 320 bytes apart, 64 modulo the 256-byte bank
+    // cycle, and the token quads fill the 64), where token-quad-major lanes collided 8 ways.
+    const int tq = tid & 7, c4 = (tid >> 3) * 4;
     struct Regs {
         v4u y[4];      // [token]: four dY columns
         float s[4];
