@@ -541,8 +541,10 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
                     if (p.ste == 1) {
                         y[v] = fabsf(t) <= 1.0f ? a : 0.0f;
                     } else {
-                        const double c = cosh(beta * (double)t);
-                        y[v] = (float)((1.0 / (c * c)) * (double)a);
+                        // sech^2(x) = 4 e / (1 + e)^2 with e = exp(-2 |x|): one exponential.
+                        const double e = exp(-2.0 * fabs(beta * (double)t));
+                        const double d = 1.0 + e;
+                        y[v] = (float)((4.0 * e / (d * d)) * (double)a);
                     }
                 }
             }
