@@ -20,6 +20,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace bl {
@@ -100,19 +102,21 @@ __device__ __forceinline__ void wait_vmem()
 }
 
 // Tile configuration: BM x BN block tile split over WM x WN waves (wave tile BM/WM x BN/WN,
-// MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS.
-template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_>
+// MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS, EA bytes per
+// activation (1: int8 codes on the int8 matrix unit; 2: bf16 activations on the bf16 one).
+template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_, int EA_ = 1>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KS = KS_, NST = NST_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KS = KS_, NST = NST_, EA = EA_;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
     static constexpr int MI = TM / 16, NI = TN / 16;     // MFMA tiles per wave, each direction
-    static constexpr int CPR = KS / 16;                  // 16-byte activation chunks per row
+    static constexpr int XROW = KS * EA;                 // activation bytes per row per stage
+    static constexpr int CPR = XROW / 16;                // 16-byte activation chunks per row
     static constexpr int WPS = KS / 16;                  // packed words per weight row
     static constexpr int LPW = WPS / 4;                  // words per lane (one MFMA k-step each)
     static constexpr int WROW = KS / 4;                  // bytes per weight row per stage
-    static constexpr int XBYTES = BM * KS;
+    static constexpr int XBYTES = BM * XROW;
     static constexpr int WBYTES = BN * WROW;
     static constexpr int STAGE = XBYTES + WBYTES;
     static constexpr int XINST = XBYTES / 1024 / WAVES;  // 1 KB direct loads per wave per stage
@@ -176,6 +180,10 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 {
     constexpr int BM = T::BM, BN = T::BN, KS = T::KS, NST = T::NST, WAVES = T::WAVES;
     constexpr int MI = T::MI, NI = T::NI, CPR = T::CPR, LPW = T::LPW, WROW = T::WROW;
+    constexpr int EA = T::EA, XROW = T::XROW;
+    constexpr bool BF = EA == 2;      // bf16 activations: the weight-only product
+    constexpr int AH = EA;            // activation fragments per packed word (16 / 8 weights)
+    using AccT = typename std::conditional<BF, f32x4, v4i>::type;
 
     int prob = 0;
 #pragma unroll 1
@@ -199,7 +207,8 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     const int stages = (K + KS - 1) / KS;
 
     // Activation rows m0 .. m0+BM-1 and weight rows n0 .. n0+BN-1; rows past M / N read zero.
-    const v4i xres = make_desc(p.Xq + (int64_t)m0 * K, rows_bytes(m0, BM, p.M, K));
+    const v4i xres = make_desc(reinterpret_cast<const unsigned char *>(p.Xq) + (int64_t)m0 * K * EA,
+                               rows_bytes(m0, BM, p.M, K * EA));
     const v4i wres = make_desc(p.W + (int64_t)n0 * (K / 16), rows_bytes(n0, BN, p.N, row_bytes));
 
     // Load plan.  Activations: wave w fills rows w*BM/WAVES .. +BM/WAVES, 64/CPR rows per 1 KB
@@ -227,11 +236,11 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             const int row0 = wave * (BM / WAVES) + i * XR;
             const int row = row0 + xrow_l;
             const int c = xpos ^ xswz<CPR>(row);
-            const int k = t * KS + 16 * c;
-            uint32_t off = ((uint32_t)row * K + (uint32_t)k) | dead;
+            const int k = t * KS + c * (16 / EA);                     // first element of the chunk
+            uint32_t off = ((uint32_t)row * K + (uint32_t)k) * EA | dead;
             if (!FULL_K)
                 off = k < K ? off : kOOB;
-            dma16(xres, lds_addr(st + row0 * KS), off);
+            dma16(xres, lds_addr(st + row0 * XROW), off);
         }
 #pragma unroll
         for (int i = 0; i < T::WINST; ++i) {
@@ -245,16 +254,16 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
         }
     };
 
-    v4i acc[MI][NI];
+    AccT acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = v4i{0, 0, 0, 0};
+            acc[mi][ni] = AccT{0, 0, 0, 0};
 
     // Per-lane LDS offsets inside a stage.  Lane (r, g) reads words g*LPW .. +LPW-1 of its
     // weight row: 16-byte chunk (g*LPW*4) / 16 (swizzled) at byte (g*LPW*4) % 16.
-    const int arow = (wm * T::TM + r) * KS;                  // + mi * 16 * KS
+    const int arow = (wm * T::TM + r) * XROW;                // + mi * 16 * XROW
     const int aswz = xswz<CPR>(wm * T::TM + r);              // same for every mi (16 | mi*16)
     const int bch = (g * LPW * 4) / 16, bin = (g * LPW * 4) % 16;
     const int brow = T::XBYTES + (wn * T::TN + r) * WROW +
@@ -265,28 +274,47 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     // the next stage's barrier and LDS reads, so the matrix pipe has work while those reads
     // are in flight instead of idling after every barrier.  (Zero operands before the first
     // stage add nothing.)
-    v4i da[MI];
+    v4i da[AH][MI];
     uint32_t dw[NI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-        da[mi] = v4i{0, 0, 0, 0};
+    for (int h = 0; h < AH; ++h)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            da[h][mi] = v4i{0, 0, 0, 0};
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
         dw[ni] = 0;
-    auto mfma_step = [&](const uint32_t (&w)[NI], const v4i (&a)[MI]) {
+    // One packed word per lane and weight row: int8, its four planes as one 16 x 16 x 64
+    // operand; bf16, its two halves of eight codes as two 16 x 16 x 32 operands.
+    auto mfma_step = [&](const uint32_t (&w)[NI], const v4i (&a)[AH][MI]) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-            const v4i b = unpack_word64(w[ni]);
+            if constexpr (BF) {
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a[mi], acc[mi][ni], 0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    const v4u b = ternary_bf16(w[ni], h);
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+                        acc[mi][ni] = mfma_bf16(b, __builtin_bit_cast(v4u, a[h][mi]), acc[mi][ni]);
+                }
+            } else {
+                const v4i b = unpack_word64(w[ni]);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a[0][mi], acc[mi][ni], 0, 0, 0);
+            }
         }
     };
-    auto read_a = [&](const unsigned char *st, int j, v4i (&a)[MI]) {
-        const int pos = 16 * ((g * LPW + j) ^ aswz);
+    // Activations of word j of the lane's share: 16 int8 (one chunk), or 16 bf16 (two
+    // chunks, one per half).
+    auto read_a = [&](const unsigned char *st, int j, v4i (&a)[AH][MI]) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            a[mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * KS + pos);
+        for (int h = 0; h < AH; ++h) {
+            const int pos = 16 * ((AH * (g * LPW + j) + h) ^ aswz);
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                a[h][mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * XROW + pos);
+        }
     };
 
     auto compute = [&](auto S) {
@@ -305,7 +333,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
                 wq[ni][0] = *reinterpret_cast<const uint32_t *>(src);
             }
         }
-        v4i a0[MI];
+        v4i a0[AH][MI];
         read_a(st, 0, a0);
         mfma_step(dw, da);          // previous stage's last k-step
         static_assert(LPW >= 2, "one k-step per stage is deferred");
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
             if (j == 0) {
                 mfma_step(w, a0);
             } else {
-                v4i a[MI];
+                v4i a[AH][MI];
                 read_a(st, j, a);
                 mfma_step(w, a);
             }
@@ -333,7 +361,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     // they have landed by the first stage wait, and the epilogue does not wait on memory.
     float sxv[MI];
     {
-        const rsrc_t sres = make_rsrc(p.sx, (uint32_t)p.M * 4u);
+        const rsrc_t sres = make_rsrc(p.sx, BF ? 0u : (uint32_t)p.M * 4u);   // bf16: unused
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const int m = m0 + wm * T::TM + mi * 16 + r;   // rows past M read 0
@@ -364,6 +392,31 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     // 4 * g + v: each lane owns four consecutive outputs of one row and writes them with one
     // 16-byte store (scalar stores when the row pitch or the base is not 16-byte aligned, and
     // in a ragged last column group).
+    if constexpr (BF) {
+        // Weight-only product: y = fl32(gamma * acc), acc the fp32 matrix-unit sum.
+        const bool vecb = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int m = m0 + wm * T::TM + mi * 16 + r;
+            if (m >= p.M)
+                continue;
+            float *yrow = p.Y + (int64_t)m * p.N;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int n = n0 + wn * T::TN + ni * 16 + 4 * g;
+                const f32x4 y = acc[mi][ni] * gammaf;
+                if (vecb && n + 3 < p.N) {
+                    *reinterpret_cast<float4 *>(yrow + n) = make_float4(y[0], y[1], y[2], y[3]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (n + v < p.N)
+                            yrow[n + v] = y[v];
+                }
+            }
+        }
+        return;
+    } else {
     const double gamma = (double)gammaf;
     const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0 &&
                      (!p.acc || ((uintptr_t)p.acc & 15) == 0) &&
@@ -409,6 +462,7 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
                 }
             }
         }
+    }
     }
 }
 
@@ -484,6 +538,31 @@ static int tile_override()
         return 0;
     }();
     return v;
+}
+
+// The weight-only product with bf16 activations (the W1.58.A16 forward and the input gradient
+// with bf16 dY): the same pipeline with 2-byte activations and the bf16 matrix unit.
+using TileWBig = Tile<256, 256, 4, 2, 128, 2, 2>;     // 144 KB LDS, one block per CU
+using TileWSmall = Tile<128, 128, 2, 2, 128, 2, 2>;   // 72 KB, two blocks per CU
+
+hipError_t launch_wonly_prefill(const WgProblem *q, int count, hipStream_t stream)
+{
+    bl_forward_ex_problem ex[BL_MAX_GROUP];
+    int n = 0;
+    int64_t big = 0;
+    for (int i = 0; i < count; ++i) {
+        if (q[i].f32 || q[i].M == 0 || q[i].O == 0)
+            continue;
+        ex[n++] = bl_forward_ex_problem{static_cast<const int8_t *>(q[i].A), nullptr, q[i].T,
+                                        q[i].gamma, q[i].Y, nullptr, nullptr, q[i].M, q[i].O,
+                                        q[i].Kc};
+        big += ((q[i].M + 255) / 256) * ((q[i].O + 255) / 256);
+    }
+    if (n == 0)
+        return hipSuccess;
+    if (big >= 512)
+        return launch_tiles<TileWBig>(ex, n, stream);
+    return launch_tiles<TileWSmall>(ex, n, stream);
 }
 
 // Large tiles (half the LDS and cache traffic per operation) when they still give every

@@ -28,8 +28,6 @@
 
 namespace bl {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -47,36 +45,6 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uin
 {
     hi = pack_bf16(x0, x1);
     lo = pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16(v4u a, v4u b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Eight codes of a packed word as eight bf16 values (0, +1.0, -1.0): half j holds weights
-// 8j .. 8j+7 of the word's 16, i.e. planes 2j and 2j+1 (weight 4i + b at bits 8b + 2i).
-// Each byte of t = (w >> 2i) & 0x03030303 is one 2-bit field f (00 -> 0, 01 -> +1, 11 -> -1);
-// v_perm_b32 looks the bf16 bytes up: selector byte f picks the low byte from kLutLo
-// (0x00 or 0x80) and f + 4 the high byte from kLutHi (0x00, 0x3F or 0xBF).  The unused field
-// value 10 maps to 0.
-constexpr uint32_t kLutLo = 0x80008000u;   // bytes for f = 0..3: 00 80 00 80
-constexpr uint32_t kLutHi = 0xBF003F00u;   // bytes for f = 0..3: 00 3F 00 BF
-
-__device__ __forceinline__ uint32_t bf16_pair(uint32_t t, uint32_t t4, uint32_t sel)
-{
-    // sel picks [t.byte a, t4.byte a, t.byte a+1, t4.byte a+1] = [f, f + 4, f', f' + 4].
-    return __builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(t4, t, sel));
-}
-
-__device__ __forceinline__ v4u ternary_bf16(uint32_t w, int j)
-{
-    const uint32_t t0 = (w >> (4 * j)) & 0x03030303u;
-    const uint32_t t1 = (w >> (4 * j + 2)) & 0x03030303u;
-    const uint32_t u0 = t0 + 0x04040404u, u1 = t1 + 0x04040404u;
-    return v4u{bf16_pair(t0, u0, 0x05010400u), bf16_pair(t0, u0, 0x07030602u),
-               bf16_pair(t1, u1, 0x05010400u), bf16_pair(t1, u1, 0x07030602u)};
 }
 
 // ------------------------------------------------------- (1)/(2): Y = gamma * A T^T
@@ -271,7 +239,11 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
 
 hipError_t launch_wgemm(const WgProblem *q, int count, hipStream_t stream)
 {
-    for (int f32 = 0; f32 < 2; ++f32) {
+    // bf16 activations: the prefill pipeline (direct-to-LDS loads, no conversion to stage).
+    hipError_t e0 = launch_wonly_prefill(q, count, stream);
+    if (e0 != hipSuccess)
+        return e0;
+    for (int f32 = 1; f32 < 2; ++f32) {
         WgBatch b{};
         int blocks = 0;
         for (int i = 0; i < count; ++i) {
