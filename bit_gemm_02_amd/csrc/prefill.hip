@@ -193,8 +193,15 @@ __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
     // XCD-aware order inside each problem, so every XCD gets its share of every problem.
     const int ntiles = (prob + 1 < b.count ? b.p[prob + 1].block_begin : b.blocks) - p.block_begin;
     const int tile = xcd_order(blockIdx.x - p.block_begin, ntiles);
-    const int m0 = (tile / p.tiles_n) * BM;
-    const int n0 = (tile % p.tiles_n) * BN;
+    // On large grids, consecutive tiles of one XCD walk two activation panels side by side,
+    // so each weight panel fetched into that XCD's L2 serves two tiles; small grids keep
+    // the plain row-major order (one panel of each is all an XCD holds anyway).
+    const int gm_max = ntiles >= 1024 ? 2 : 1;
+    const int tiles_m = ntiles / p.tiles_n;
+    const int grp = tile / (gm_max * p.tiles_n), within = tile % (gm_max * p.tiles_n);
+    const int gm = min(gm_max, tiles_m - grp * gm_max);
+    const int m0 = (grp * gm_max + within % gm) * BM;
+    const int n0 = (within / gm) * BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
