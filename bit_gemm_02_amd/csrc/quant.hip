@@ -10,7 +10,7 @@
 //
 // Activation path (BitDistill article: INT8 activations, SubLN before the attention and FFN
 // output projections; SLM750-Edge card: RMSNorm epsilon 1e-6):
-//   act_quant_wave_kernel   persistent waves, one row at a time (K <= 4096), next row in flight;
+//   act_quant_wave_kernel   one wave per token row (K <= 4096);
 //   act_quant_block_kernel  one block per token row for longer rows;
 //   both: absmax (+ fixed-order sum of squares for the norm), then q = rint(u * (127 / a))
 //   and the row scale.
@@ -71,23 +71,40 @@ __global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(WeightBatc
     const int64_t stride = (int64_t)p.parts * kGammaThreads;
     double s = 0.0;
     int64_t i = (int64_t)part * kGammaThreads + threadIdx.x;
-    // Four loads in flight per thread; the additions stay in index order.
-    for (; i + 3 * stride < p.chunks; i += 4 * stride) {
-        float4 v0 = p.W[i], v1 = p.W[i + stride], v2 = p.W[i + 2 * stride],
-               v3 = p.W[i + 3 * stride];
-        s += fabs((double)v0.x); s += fabs((double)v0.y);
-        s += fabs((double)v0.z); s += fabs((double)v0.w);
-        s += fabs((double)v1.x); s += fabs((double)v1.y);
-        s += fabs((double)v1.z); s += fabs((double)v1.w);
-        s += fabs((double)v2.x); s += fabs((double)v2.y);
-        s += fabs((double)v2.z); s += fabs((double)v2.w);
-        s += fabs((double)v3.x); s += fabs((double)v3.y);
-        s += fabs((double)v3.z); s += fabs((double)v3.w);
-    }
-    for (; i < p.chunks; i += stride) {
-        float4 v = p.W[i];
-        s += fabs((double)v.x); s += fabs((double)v.y);
-        s += fabs((double)v.z); s += fabs((double)v.w);
+    auto add4 = [&s](float x, float y, float z, float w) {
+        s += fabs((double)x); s += fabs((double)y);
+        s += fabs((double)z); s += fabs((double)w);
+    };
+    if (p.chunks * 16 < ((int64_t)1 << 31)) {
+        // Eight loads in flight per thread through a buffer resource (chunks past the tensor
+        // read as zeros and add nothing); the additions stay in index order.
+        const rsrc_t wr = make_rsrc(p.W, (uint32_t)(p.chunks * 16));
+        for (; i < p.chunks; i += 8 * stride) {
+            v4u v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t j = i + u * stride;
+                v[u] = buf_load16(wr, j < p.chunks ? (uint32_t)(j * 16) : kOOB);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                add4(__uint_as_float(v[u].x), __uint_as_float(v[u].y), __uint_as_float(v[u].z),
+                     __uint_as_float(v[u].w));
+        }
+    } else {
+        // Tensors of 2 GiB and more: four loads in flight, plain pointers.
+        for (; i + 3 * stride < p.chunks; i += 4 * stride) {
+            const float4 v0 = p.W[i], v1 = p.W[i + stride], v2 = p.W[i + 2 * stride],
+                         v3 = p.W[i + 3 * stride];
+            add4(v0.x, v0.y, v0.z, v0.w);
+            add4(v1.x, v1.y, v1.z, v1.w);
+            add4(v2.x, v2.y, v2.z, v2.w);
+            add4(v3.x, v3.y, v3.z, v3.w);
+        }
+        for (; i < p.chunks; i += stride) {
+            const float4 v = p.W[i];
+            add4(v.x, v.y, v.z, v.w);
+        }
     }
     // Fixed-order block sum: wave butterfly, then the waves in index order.
     s = wave_sum_fixed(s);
@@ -160,8 +177,19 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
     // holds the same gamma without a barrier.
     const int lane = threadIdx.x & (kWave - 1);
     double part = 0.0;
-    for (int i = lane; i < p.parts; i += kWave)
-        part += p.partials[i];
+    {
+        // All of a lane's partials (parts <= 256: four) loaded at once; slots past the
+        // partials read as zeros and add nothing.
+        const rsrc_t pr = make_rsrc(p.partials, (uint32_t)p.parts * 8u);
+        v2u v[kGammaParts / kWave];
+#pragma unroll
+        for (int k = 0; k < kGammaParts / kWave; ++k)
+            v[k] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                               pr, (lane + k * kWave) * 8, 0, 0));
+#pragma unroll
+        for (int k = 0; k < kGammaParts / kWave; ++k)
+            part += __longlong_as_double((long long)(((uint64_t)v[k].y << 32) | v[k].x));
+    }
     const double sum = wave_sum_fixed(part);
     const double count = (double)(p.chunks * 4);
     const float gamma = p.chunks > 0 ? (float)(sum / count) : 0.0f;
@@ -349,12 +377,12 @@ __device__ __forceinline__ int find_problem(const T &b, int key)
     return prob;
 }
 
-// One wave per token row, K <= 256 * CACHE, persistent and software-pipelined: each wave
-// walks rows w, w + S, w + 2S, ... (S = waves in the grid) and issues the loads of its next
-// row before it quantizes the current one, so every wave always has a row in flight.  The
-// row's activations stay in registers (raw), the row is read from HBM once, and all
-// reductions are wave-local (no LDS, no barriers).  A row past the end loads from an empty
-// buffer resource (zeros) so the two register sets alternate without copies or waits.
+// One wave per token row, K <= 256 * CACHE: the grid has a wave for every row and the
+// hardware keeps each CU full as waves retire (a persistent grid that prefetched its next row
+// measured slower: at a few rows per wave the prefetch never paid for its second register
+// set).  The row's activations stay in registers (raw), the row is read from HBM once, and
+// all reductions are wave-local (no LDS, no barriers).  Groups past the row load from
+// outside the buffer resource (zeros).
 // Lane l holds the 16-byte groups c * 64 + l (CACHE fp32 groups, or CACHE / 2 bf16 groups).
 template <int CACHE, bool BF16>
 struct RowBuf {
@@ -381,8 +409,7 @@ __device__ __forceinline__ void act_load(RowBuf<CACHE, BF16> &r, rsrc_t xr, int 
 }
 
 // RMSNorm weights of a row's problem (zeros, unused, without a norm): the fp32 quads that
-// match the lane's groups.  Issued before the next row's prefetch: vector-memory loads
-// complete in order, so waiting for them later does not wait for the prefetch.
+// match the lane's groups.
 template <int CACHE>
 struct NormBuf {
     float4 g[CACHE];
@@ -448,24 +475,18 @@ template <int CACHE, bool BF16>
 __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    // Wave-uniform indices (readfirstlane keeps the problem lookup and the buffer
+    // Wave-uniform row index (readfirstlane keeps the problem lookup and the buffer
     // descriptors in scalar registers; otherwise every load is wrapped in a per-lane loop).
-    const int w0 = blockIdx.x * (kActThreads / kWave) +
-                   __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int S = gridDim.x * (kActThreads / kWave);
-    RowBuf<CACHE, BF16> A, B;
+    const int r = blockIdx.x * (kActThreads / kWave) +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (r >= rows)
+        return;
+    RowBuf<CACHE, BF16> A;
     NormBuf<CACHE> G;
-    int pa, pb;
-    act_load(A, act_row_rsrc(b, w0, rows, pa), lane);
-    for (int r = w0; r < rows; r += 2 * S) {
-        norm_load<CACHE, BF16>(G, b.p[pa], lane);
-        act_load(B, act_row_rsrc(b, r + S, rows, pb), lane);
-        act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
-        norm_load<CACHE, BF16>(G, b.p[pb], lane);
-        act_load(A, act_row_rsrc(b, r + 2 * S, rows, pa), lane);
-        if (r + S < rows)
-            act_quant_row(B, G, b.p[pb], r + S - b.p[pb].row_begin, lane);
-    }
+    int pa;
+    act_load(A, act_row_rsrc(b, r, rows, pa), lane);
+    norm_load<CACHE, BF16>(G, b.p[pa], lane);
+    act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
 }
 
 // One block per token row for rows longer than the largest wave class.  Thread t handles the
@@ -673,25 +694,12 @@ constexpr int kActBlockClasses[] = {4, 8, 16};
 constexpr int kActClasses[] = {4, 8, 16};
 constexpr int kActNumClasses = 3;
 
-// Persistent grid: enough blocks to fill every CU at the kernel's occupancy, no more than
-// the rows need.
 template <int CACHE, bool BF16>
 static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
 {
-    static int resident = [] {
-        int dev = 0, cus = 0, per_cu = 0;
-        hipGetDevice(&dev);
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, act_quant_wave_kernel<CACHE, BF16>,
-                                                     kActThreads, 0);
-        return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
-    }();
     const int per_block = kActThreads / kWave;
-    int blocks = (rows + per_block - 1) / per_block;
-    if (blocks > resident)
-        blocks = resident;
-    hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16>), dim3(blocks), dim3(kActThreads), 0,
-                       stream, b, rows);
+    hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16>), dim3((rows + per_block - 1) / per_block),
+                       dim3(kActThreads), 0, stream, b, rows);
 }
 
 hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream_t stream)
