@@ -55,7 +55,6 @@ struct FwdDev {
     int act;
 };
 
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 struct FwdBatch {
     FwdDev p[BL_MAX_GROUP];
