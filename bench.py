@@ -554,6 +554,41 @@ def layer_bench(torch, bl, wl: workloads.Workload, M_pre: int, rotate_bytes: flo
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published (no sparsity)
 
 
+def measured_peaks(torch, bl) -> dict:
+    """What this GPU attains, from the library's calibration kernels, run once outside any timed
+    region: a plain 16-byte-load read stream over 2 GiB (HBM, well past the 256 MB last-level
+    cache) and loops of independent int8 and bf16 matrix-unit operations on every compute unit
+    (at the clock the matrix units actually run at).  The rooflines are quoted against these
+    beside the published peaks."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.empty(1 << 31, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sums = torch.empty(256 * 4 * cus, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps * 1e-3          # seconds per call
+
+    hbm = buf.numel() / timed(lambda: bl.calib_stream(buf, out), 5) / 1e9
+    iters = 4096
+    ops = {k: bl.calib_mfma(k, iters, 4 * cus, sums) for k in (bl.CALIB_INT8, bl.CALIB_BF16)}
+    int8 = ops[bl.CALIB_INT8] / timed(lambda: bl.calib_mfma(bl.CALIB_INT8, iters, 4 * cus, sums), 3) / 1e12
+    bf16 = ops[bl.CALIB_BF16] / timed(lambda: bl.calib_mfma(bl.CALIB_BF16, iters, 4 * cus, sums), 3) / 1e12
+    del buf
+    return {"hbm_read_GBps": round(hbm, 1), "int8_mfma_TOPS": round(int8, 1),
+            "bf16_mfma_TFLOPS": round(bf16, 1),
+            "how": "bitlinear_calib_stream over 2 GiB; bitlinear_calib_mfma, 4 blocks of 4 waves "
+                   "per compute unit, 8 independent accumulators per wave, 4096 iterations"}
+
+
 def graph_ms(torch, fn, reps: int) -> float:
     """Average time of fn(stream) replayed from a captured HIP graph (events on its stream)."""
     s_ = torch.cuda.Stream()
@@ -622,7 +657,10 @@ def train_bench(torch, bl, wl: workloads.Workload, M: int, reps: int):
 
     flops = sum(2 * M * m.N * m.K for m in mats)
     packed = sum(m.N * m.K // 4 for m in mats)
-    out = {"tokens": M, "matrices": [f"{m.name} {m.K}->{m.N}" for m in mats], "flops_per_product": flops}
+    peaks = measured_peaks(torch, bl)
+    bf16_meas = peaks["bf16_mfma_TFLOPS"]
+    out = {"tokens": M, "matrices": [f"{m.name} {m.K}->{m.N}" for m in mats], "flops_per_product": flops,
+           "measured_peaks": peaks}
     for key, fn, f32 in (("forward_wonly_f32", call(L.bitlinear_forward_wonly_grouped, arr), True),
                          ("forward_wonly_bf16", call(L.bitlinear_forward_wonly_grouped, arrb), False),
                          ("grad_input_f32", call(L.bitlinear_grad_input_grouped, gi), True),
@@ -632,7 +670,8 @@ def train_bench(torch, bl, wl: workloads.Workload, M: int, reps: int):
         out[key] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                     "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
                     "mfma_per_product": 2 if f32 else 1,
-                    "frac_attainable": round(tf * (2 if f32 else 1) / BF16_PEAK_TFLOPS, 4)}
+                    "frac_attainable": round(tf * (2 if f32 else 1) / BF16_PEAK_TFLOPS, 4),
+                    "frac_attainable_measured": round(tf * (2 if f32 else 1) / bf16_meas, 4)}
     ms = graph_ms(torch, transpose_all, reps)
     out["transpose_packed"] = {"us": round(ms * 1e3, 2), "bytes": 2 * packed,
                                "gbps": round(2 * packed / (ms * 1e-3) / 1e9, 1)}
@@ -721,6 +760,7 @@ def main():
     ms_with_events = interval_ms(ev, "t0", "t_dec")
     ms = {k: isolated_ms(torch, setup, k, args.steps) for k in in_step}
     ms_b3 = isolated_ms(torch, setup, "decode_linear_b3", args.steps)
+    peaks = measured_peaks(torch, bl)
 
     ops = setup.prefill_ops()
     pre_bytes = setup.prefill_bytes()
@@ -737,7 +777,8 @@ def main():
     def hbm(nbytes, key, what):
         a = nbytes / (ms[key] * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBPS, "us_per_launch": ms[key] * 1e3,
+                "frac": a / HBM_PEAK_GBPS, "peak_measured": peaks["hbm_read_GBps"],
+                "frac_measured": a / peaks["hbm_read_GBps"], "us_per_launch": ms[key] * 1e3,
                 "us_per_launch_in_step": in_step[key] * 1e3, "algorithmic": what}
 
     pre_what = (f"{ops} int8 ops (2 M N K over {setup.count} products); {pre_bytes} bytes "
@@ -748,10 +789,15 @@ def main():
     else:
         pre_roof = {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS,
                     "unit": "TFLOP/s", "frac": gemm_tops / INT8_PEAK_TOPS,
+                    "peak_measured": peaks["int8_mfma_TOPS"],
+                    "frac_measured": gemm_tops / peaks["int8_mfma_TOPS"],
                     "us_per_launch": ms["prefill_gemm"] * 1e3,
                     "us_per_launch_in_step": in_step["prefill_gemm"] * 1e3, "algorithmic": pre_what}
+    attainable_meas = min(peaks["int8_mfma_TOPS"], ai * peaks["hbm_read_GBps"] / 1e3)
     pre_roof.update({"tops": gemm_tops, "frac_int8_peak": gemm_tops / INT8_PEAK_TOPS,
-                     "attainable_tops": attainable, "frac_attainable": gemm_tops / attainable})
+                     "attainable_tops": attainable, "frac_attainable": gemm_tops / attainable,
+                     "attainable_tops_measured": attainable_meas,
+                     "frac_attainable_measured": gemm_tops / attainable_meas})
     rooflines = {
         "prefill_gemm": pre_roof,
         "decode_linear": hbm(dec_bytes, "decode_linear",
@@ -771,7 +817,8 @@ def main():
     roof = dict(rooflines[dom])
     roof = {"kernel": dom, "bound": roof["bound"], "achieved": round(roof["achieved"], 2),
             "peak": roof["peak"], "unit": roof["unit"], "frac": round(roof["frac"], 4),
-            "traffic": None if t is None else t["bytes_per_launch"]}
+            "traffic": None if t is None else t["bytes_per_launch"],
+            "peak_measured": roof["peak_measured"], "frac_measured": round(roof["frac_measured"], 4)}
 
     value = ops / (ms_per_step * 1e-3) / 1e12
     result = {
@@ -805,12 +852,14 @@ def main():
                     "us_weight_quant": round(ms["weight_quant"] * 1e3, 3) if "weight_quant" in ms else None,
                     "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3)},
         "roofline": roof,
+        "measured_peaks": peaks,
         "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in rooflines.items()},
         "timing": {"ms_per_step_wall": round(wall_ms, 4),
                    "ms_per_step_with_launch_events": round(ms_with_events, 4),
                    "schedule": "one stream, launches in step order (three streams, weight quant "
-                               "beside act quant and decode beside prefill, measured slower)"},
+                               "beside act quant and decode beside prefill, and the decode leg "
+                               "alone on a second stream, measured slower)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)

@@ -175,6 +175,10 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_b3.restype = ctypes.c_int
     L.bitlinear_linear_b3_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_b3_grouped.restype = ctypes.c_int
+    L.bitlinear_calib_stream.argtypes = [P, I64, P, P]
+    L.bitlinear_calib_stream.restype = ctypes.c_int
+    L.bitlinear_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    L.bitlinear_calib_mfma.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -602,3 +606,26 @@ def linear_b3_grouped(problems: Sequence[dict], stream=None) -> None:
     arr = linear_b3_table(problems)
     _check("bitlinear_linear_b3_grouped",
            lib().bitlinear_linear_b3_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+# ----------------------------------------------------------------- measurement helpers
+
+CALIB_INT8, CALIB_BF16 = 0, 1
+CALIB_OPS = {CALIB_INT8: 32768, CALIB_BF16: 16384}   # operations per matrix-unit instruction
+
+
+def calib_stream(buf: torch.Tensor, xor_out: torch.Tensor, stream=None) -> None:
+    """XOR of buf's 32-bit words into xor_out (int32 [1], zeroed by the caller): one read of
+    buf, the HBM read-stream calibration."""
+    buf = _dev(buf, "buf")
+    _check("bitlinear_calib_stream",
+           lib().bitlinear_calib_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(xor_out),
+                                        _stream(stream)))
+
+
+def calib_mfma(kind: int, iters: int, blocks: int, out: torch.Tensor, stream=None) -> int:
+    """Matrix-unit loop (kind CALIB_INT8 or CALIB_BF16) into out (int32 [256 * blocks]);
+    returns the number of operations it performs."""
+    _check("bitlinear_calib_mfma",
+           lib().bitlinear_calib_mfma(int(kind), int(iters), int(blocks), _ptr(out), _stream(stream)))
+    return blocks * 4 * 8 * iters * CALIB_OPS[kind]

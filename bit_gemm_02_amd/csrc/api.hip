@@ -634,4 +634,30 @@ bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int cou
     return from_hip(bl::launch_linear_decode_b3(ex, count, static_cast<hipStream_t>(stream)));
 }
 
+bl_status bitlinear_calib_stream(const void *buf, int64_t bytes, uint32_t *xor_out, void *stream)
+{
+    if (bytes < 0 || bytes % 16 != 0)
+        return BL_ERR_SHAPE;
+    if (!xor_out || (bytes > 0 && !buf))
+        return BL_ERR_NULL;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(xor_out) & 3u))
+        return BL_ERR_ALIGN;
+    if (bytes == 0)
+        return BL_OK;
+    return from_hip(bl::launch_calib_stream(buf, bytes, xor_out, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_calib_mfma(int kind, int iters, int blocks, int32_t *out, void *stream)
+{
+    if (kind != 0 && kind != 1)
+        return BL_ERR_DTYPE;
+    if (iters <= 0 || blocks <= 0 || iters > (kind == 1 ? (1 << 16) : (1 << 21)))
+        return BL_ERR_SHAPE;
+    if (!out)
+        return BL_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(out) & 3u)
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_calib_mfma(kind, iters, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

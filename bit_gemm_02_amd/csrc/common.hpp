@@ -280,6 +280,8 @@ hipError_t launch_grad_weight(const bl_grad_weight_problem *p, int count, hipStr
 // Base-3 weights (five codes per byte): the packer and the fused decode call on them.
 hipError_t launch_pack_b3(const uint32_t *P, int64_t N, int64_t K, uint8_t *out, hipStream_t stream);
 hipError_t launch_linear_decode_b3(const bl_linear_ex_problem *p, int count, hipStream_t stream);
+hipError_t launch_calib_stream(const void *buf, int64_t bytes, uint32_t *out, hipStream_t stream);
+hipError_t launch_calib_mfma(int kind, int iters, int blocks, int32_t *out, hipStream_t stream);
 
 // Token count up to which bitlinear_forward uses the decode (streaming) kernel.
 constexpr int64_t kDecodeMaxM = 16;

@@ -474,6 +474,27 @@ bl_status bitlinear_pack_b3(const uint32_t *W_packed, int64_t N, int64_t K, uint
  * Errors as for bitlinear_linear_grouped. */
 bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int count, void *stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Measurement helpers (not part of the method): what this GPU attains, so that a kernel's
+ * roofline can be quoted against a measured peak beside the published one.
+ * ------------------------------------------------------------------------------------- */
+
+/* Reads buf [bytes] once with 16-byte loads (a grid of up to 8 blocks per compute unit,
+ * eight loads in flight per thread) and XORs all its 32-bit words into *xor_out, which the
+ * caller zeroes first (so the result is the XOR of the buffer's words and no load can be
+ * skipped).  bytes % 16 == 0; buf 16-byte aligned, xor_out 4-byte aligned; bytes == 0 is a
+ * no-op.  Errors: BL_ERR_SHAPE, BL_ERR_NULL, BL_ERR_ALIGN. */
+bl_status bitlinear_calib_stream(const void *buf, int64_t bytes, uint32_t *xor_out, void *stream);
+
+/* `blocks` blocks of 256 threads; every wave runs 8 independent accumulators through `iters`
+ * matrix-unit operations on constant operands: kind 0 = int8 16x16x64 (A = B = 1; 32768
+ * operations each), kind 1 = bf16 16x16x32 (A = B = 1.0; 16384 floating-point operations
+ * each).  Total operations = blocks * 4 * 8 * iters * (32768 or 16384).  Thread t of block b
+ * writes out[256 b + t] = 8 * iters * 64 (int8) or 8 * iters * 32 (bf16).  1 <= iters <= 2^21
+ * (int8) or 2^16 (bf16, so the sums stay exact in fp32); out holds 256 * blocks int32.
+ * Errors: BL_ERR_DTYPE (kind), BL_ERR_SHAPE, BL_ERR_NULL, BL_ERR_ALIGN. */
+bl_status bitlinear_calib_mfma(int kind, int iters, int blocks, int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

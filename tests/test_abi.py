@@ -343,6 +343,24 @@ def test_b3_entry_points_validation(L, bl):
     assert call(M=0) == BL_OK
 
 
+def test_calib_validation(L):
+    cs, cm = L.bitlinear_calib_stream, L.bitlinear_calib_mfma
+    assert cs(A, 40, B, None) == BL_ERR_SHAPE
+    assert cs(A, -16, B, None) == BL_ERR_SHAPE
+    assert cs(None, 16, B, None) == BL_ERR_NULL
+    assert cs(A, 16, None, None) == BL_ERR_NULL
+    assert cs(A + 4, 16, B, None) == BL_ERR_ALIGN
+    assert cs(A, 16, B + 2, None) == BL_ERR_ALIGN
+    assert cs(None, 0, B, None) == BL_OK
+    assert cm(2, 10, 1, B, None) == BL_ERR_DTYPE
+    assert cm(0, 0, 1, B, None) == BL_ERR_SHAPE
+    assert cm(0, 10, 0, B, None) == BL_ERR_SHAPE
+    assert cm(0, (1 << 21) + 1, 1, B, None) == BL_ERR_SHAPE
+    assert cm(1, (1 << 16) + 1, 1, B, None) == BL_ERR_SHAPE
+    assert cm(0, 10, 1, None, None) == BL_ERR_NULL
+    assert cm(1, 10, 1, B + 2, None) == BL_ERR_ALIGN
+
+
 def test_binding_refuses_host_tensors(bl):
     import torch
     with pytest.raises(TypeError):
