@@ -209,6 +209,52 @@ __device__ __forceinline__ float4 ffn_act4(int kind, float4 x, float4 x2)
                        ffn_act(kind, x.z, x2.z), ffn_act(kind, x.w, x2.w));
 }
 
+// The same activation for the bulk kernels, with a table-driven fp64 exp: e^t = 2^(k/64) e^r,
+// k = rint(64 t / ln 2), r = t - k ln2/64 (two-part constant, |r| <= ln2/128), e^r by its
+// degree-6 Taylor polynomial (truncation < 2^-64), 2^(j/64) = tab[j] from a 64-entry table in
+// LDS (tab[j] = exp2(j / 64), built by the caller), then ldexp; silu(g) = g * (1 / (1 + e))
+// with the reciprocal refined by one Newton step.  A few fp64 ulps from the exact value (the
+// general-purpose exp and division are one to two ulps), so h, rounded to fp32, differs from
+// that of any accurate fp64 evaluation only within a few 2^-52 of an fp32 midpoint.  Large
+// |g| saturates as the library's exp does (e^800 = inf, e^-800 = 0); NaN propagates.
+// About 12 fp64 operations per element instead of about 40.
+__device__ __forceinline__ double exp_f64_tab(double t, const double *tab)
+{
+    t = t < -800.0 ? -800.0 : (t > 800.0 ? 800.0 : t);          // NaN compares false: kept
+    constexpr double kInvStep = 92.332482616893656877;           // 64 / ln 2
+    constexpr double kStepHi = 0x1.62e42fefa39efp-7;             // ln 2 / 64, leading part
+    constexpr double kStepLo = 0x1.abc9e3b39803fp-62;            // ln 2 / 64 - kStepHi
+    const double k = __builtin_rint(t * kInvStep);
+    const int ki = (int)k;                                       // NaN -> 0: index stays valid
+    double r = __builtin_fma(-k, kStepHi, t);
+    r = __builtin_fma(-k, kStepLo, r);
+    double q = __builtin_fma(r, 1.0 / 720.0, 1.0 / 120.0);
+    q = __builtin_fma(q, r, 1.0 / 24.0);
+    q = __builtin_fma(q, r, 1.0 / 6.0);
+    q = __builtin_fma(q, r, 0.5);
+    q = __builtin_fma(q, r, 1.0);
+    q = __builtin_fma(q, r, 1.0);
+    return __builtin_ldexp(tab[ki & 63] * q, ki >> 6);
+}
+
+__device__ __forceinline__ float ffn_act_tab(int kind, float x, float x2, const double *tab)
+{
+    if (kind != BL_ACT_SWIGLU)
+        return ffn_act(kind, x, x2);
+    const double g = (double)x;
+    const double d = 1.0 + exp_f64_tab(-g, tab);                 // >= 1, or inf, or NaN
+    double y = __builtin_amdgcn_rcp(d);
+    y = __builtin_fma(y, __builtin_fma(-d, y, 1.0), y);         // one Newton step
+    y = d == __builtin_inf() ? 0.0 : y;                          // 1 / inf = 0 (the step gives NaN)
+    return (float)((g * y) * (double)x2);
+}
+
+__device__ __forceinline__ float4 ffn_act4_tab(int kind, float4 x, float4 x2, const double *tab)
+{
+    return make_float4(ffn_act_tab(kind, x.x, x2.x, tab), ffn_act_tab(kind, x.y, x2.y, tab),
+                       ffn_act_tab(kind, x.z, x2.z, tab), ffn_act_tab(kind, x.w, x2.w, tab));
+}
+
 // ----------------------------------------------------------------- bf16 matrix operands
 //
 // Ternary codes as bf16 MFMA operands (the weight-only product and the input gradient).

@@ -605,6 +605,7 @@ __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
 {
     __shared__ float lds_max[kActThreads / kWave];
     __shared__ double lds_sum[kActThreads / kWave];
+    __shared__ double exp_tab[64];         // 2^(j/64) for ffn_act_tab
     const ActDev &p = b.p[find_problem(b, (int)blockIdx.x)];
     const int m = blockIdx.x - p.row_begin;
     const int groups = p.K / 4;
@@ -620,7 +621,8 @@ __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
                            __uint_as_float(r.w));
     };
     auto h_at = [&](int j) {
-        return ffn_act4(kind, f4(buf_load16(xr, (uint32_t)j * 16u)), f4(buf_load16(x2r, (uint32_t)j * 16u)));
+        return ffn_act4_tab(kind, f4(buf_load16(xr, (uint32_t)j * 16u)),
+                            f4(buf_load16(x2r, (uint32_t)j * 16u)), exp_tab);
     };
     auto absmax_group = [&](const float4 &h, int j, float &amax, double &ss) {
         const float4 u = norm ? mul4(h, load_g(gr, j < groups ? j : (int)(kOOB / 16u))) : h;
@@ -643,9 +645,13 @@ __global__ __launch_bounds__(kActThreads) void act_quant_ffn_kernel(ActBatch b)
             raw[c] = buf_load16(xr, off);
             raw2[c] = buf_load16(x2r, off);
         }
+        // The exp table, built while the row is in flight.
+        if (tid < 64)
+            exp_tab[tid] = exp2((double)tid * (1.0 / 64.0));
+        __syncthreads();
 #pragma unroll
         for (int c = 0; c < C; ++c)
-            h[c] = ffn_act4(kind, f4(raw[c]), f4(raw2[c]));   // zeros past the row: h = 0
+            h[c] = ffn_act4_tab(kind, f4(raw[c]), f4(raw2[c]), exp_tab);   // zeros past the row: h = 0
     }
     float amax = 0.0f;
     double ss = 0.0;
