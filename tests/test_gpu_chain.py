@@ -102,6 +102,31 @@ def test_act_quant_ffn(torch, bl, orc, M, K, kind, norm):
     check_scales(host(sx), s_ref, norm, (M, K, kind, norm))
 
 
+@pytest.mark.parametrize("K", [272, 9728])
+def test_act_quant_ffn_extreme_gates(torch, bl, orc, K):
+    """SwiGLU with gate values where exp(-g) saturates or is tiny (|g| of 100, 700, 750),
+    denormal and signed-zero gates, mixed with ordinary values: codes and scales as the
+    oracle's (its exp from the host library) under the same rare-difference allowance."""
+    M = 6
+    G = workloads.gaussian((M, K), (310, K), 2.0)
+    U = workloads.gaussian((M, K), (311, K), 1.0)
+    special = np.array([100.0, -100.0, 700.0, -700.0, 750.0, -750.0, 1e-40, -1e-40, 0.0, -0.0,
+                        30.0, -30.0], np.float32)
+    for m in range(M):
+        idx = np.random.Generator(np.random.PCG64([312, m, K])).choice(K, size=special.size, replace=False)
+        G[m, idx] = special
+    G[M - 1, :] = np.float32(-750.0)        # a row whose h is all -0 or tiny: absmax from zeros
+    H = orc.ffn_act(orc.SWIGLU, G, U)
+    q_ref, s_ref = orc.quantize_acts(H)
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    bl.quantize_acts_ex_grouped([dict(X=dev(torch, G), X2=dev(torch, U), act=orc.SWIGLU, X_q=Xq,
+                                      x_scale=sx)])
+    torch.cuda.synchronize()
+    check_codes(host(Xq), q_ref, orc.SWIGLU, orc, ("extremes", K))
+    check_scales(host(sx), s_ref, False, ("extremes", K))
+
+
 def test_act_quant_ex_mixed_group(torch, bl, orc):
     """Plain, bf16 and activation problems in one call give what separate calls give."""
     A = workloads.gaussian((40, 768), (303,), 1.0)
