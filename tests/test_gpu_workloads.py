@@ -149,3 +149,46 @@ def test_workload(torch, bl, orc, key, M):
         assert np.array_equal(Y == 0, Y_ref == 0), label
         assert rel_err(Y[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL, label
     print(f"{key} M={M}: {n} matrices ok, code flips in the 1e-6 band: {flips_total}")
+
+
+@pytest.mark.parametrize("key", sorted(workloads.WORKLOADS))
+def test_workload_decode_leg(torch, bl, orc, key):
+    """The benchmark's decode leg at full size: every matrix of the layer set in one grouped
+    fused call at one token (activation quantization inside the product), on weights packed
+    as the benchmark packs them (from the fp32 masters, or from the pre-ternarized codes) and
+    the workload's own one-token activations and norm weights.  Codes bit-exact and scales
+    within 1e-6 (through the call's optional outputs); Y equal to the oracle's product and
+    epilogue on the oracle's own codes and scales, within 1e-6 relative, zeros exact."""
+    wl = workloads.WORKLOADS[key]
+    mats = wl.matrices
+    calls, refs = [], []
+    for i, m in enumerate(mats):
+        if wl.weights == "fp32":
+            P, g = bl.quantize_weights(dev(torch, workloads.weight_fp32(wl, i)))
+        else:
+            P = bl.pack_codes(dev(torch, workloads.weight_codes(wl, i)))
+            g = torch.full((1,), wl.code_gamma, device="cuda")
+        x = workloads.activations(wl, i, 1)
+        nw = workloads.norm_weight(wl, i) if m.norm else None
+        calls.append(dict(X=dev(torch, x), W_packed=P, gamma=g, norm_weight=None if nw is None else dev(torch, nw),
+                          Y=torch.empty((1, m.N), device="cuda"),
+                          X_q=torch.empty((1, m.K), dtype=torch.int8, device="cuda"),
+                          x_scale=torch.empty(1, device="cuda"), eps=1e-6))
+        refs.append((x, nw))
+    assert all(bl.linear_fused(1, m.K) for m in mats)
+    bl.linear_grouped(calls)
+    torch.cuda.synchronize()
+    bf16 = wl.x_dtype == "bf16"
+    for i, m in enumerate(mats):
+        x, nw = refs[i]
+        c = calls[i]
+        q_ref, s_ref = orc.quantize_acts(x, nw, 1e-6, bf16=bf16)
+        q, s, Y = host(c["X_q"]), host(c["x_scale"]), host(c["Y"])
+        assert np.array_equal(q, q_ref), (key, m.name)
+        assert rel_err(s, s_ref) <= REL, (key, m.name)
+        codes = orc.unpack(host(c["W_packed"]).view(np.uint32), m.K)
+        gamma = np.float32(host(c["gamma"])[0])
+        Y_ref = orc.epilogue(orc.matmul(q_ref, codes), s_ref, gamma)
+        assert np.array_equal(Y == 0, Y_ref == 0), (key, m.name)
+        nz = Y_ref != 0
+        assert rel_err(Y[nz], Y_ref[nz]) <= REL, (key, m.name)
