@@ -21,14 +21,15 @@
 // MFMA operand layout): (1)/(2) read activation rows and packed code rows that are already
 // contraction-major and expand the 2-bit codes to bf16 in registers; (4) contracts over
 // tokens, which are the slow index of both dY and q, so its staging loads four token rows
-// at once and writes them transposed (four tokens per 8-byte LDS store).
+// at once and writes them transposed (four tokens per 8-byte LDS store).  (1)/(2) with bf16
+// activations need no conversion while staging and run on the prefill product's pipeline
+// instead (prefill.hip: direct-to-LDS loads, the bf16 form of its kernel).
 #include <algorithm>
 
 #include "common.hpp"
 
 namespace bl {
 
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
