@@ -342,18 +342,19 @@ struct GwBatch {
     int blocks;
 };
 
-constexpr int kGwThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
-constexpr int kGwBN = 128, kGwBK = 128;      // block tile: dW rows (n) x columns (k)
+constexpr int kGwThreads = 512;              // 2 x 4 waves, 64 x 64 outputs each
+constexpr int kGwBN = 128, kGwBK = 256;      // block tile: dW rows (n) x columns (k)
 constexpr int kGwKC = 32;                    // tokens per stage (one MFMA k-step)
 constexpr int kGwPitch = 2 * kGwKC + 16;     // LDS bytes per bf16 row (padded)
-constexpr int kGwPart = kGwBN * kGwPitch;    // one bf16 part of the dY tile
-constexpr int kGwStage = 3 * kGwPart;        // dY hi, dY lo, q
+constexpr int kGwPartY = kGwBN * kGwPitch;   // one bf16 part of the dY tile
+constexpr int kGwPartQ = kGwBK * kGwPitch;   // the q tile
+constexpr int kGwStage = 2 * kGwPartY + kGwPartQ;   // dY hi, dY lo, q
 
-// Stage s covers tokens 32s .. 32s+31.  Staging: a thread takes four consecutive tokens of
-// four dY columns (four 16-byte loads) and of four q columns (four dword loads), scales dY
-// by s_x (one fp32 product, as the dequantized activation q * s_x is folded into dY's side),
-// splits it, converts q (exact), and writes each (column, four tokens) as one 8-byte LDS
-// store, so the tiles land transposed: row = column of dW, contiguous in tokens.
+// Stage s covers tokens 32s .. 32s+31.  Staging: dY is scaled by s_x (one fp32 product, as
+// the dequantized activation q * s_x is folded into dY's side) and split, q converted
+// (exact), and both land transposed: row = column of dW, contiguous in tokens.  The tile is
+// twice as wide in k as in n because the dY conversion (product, split) costs several
+// instructions per value and q's one: every staged dY value then feeds twice the MFMAs.
 __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
 {
     __shared__ __align__(16) unsigned char lds[2][kGwStage];
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int r = lane & 15, g = lane >> 4;
     const int M = p.M, N = p.N, K = p.K;
     const int stages = (M + kGwKC - 1) / kGwKC;
@@ -380,15 +381,19 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
 
     // Per stage: the tokens' rows from column n0 (k0) on; tokens past M read zero.  Columns
     // past N (K) belong to the next row: they only reach dW rows (columns) that are not
-    // stored.  A thread stages four tokens x four columns of dY and of q (units of
-    // 8 token quads x 32 column quads).  Lane l of a half-wave takes token quad l % 8 and
-    // column quad l / 8: its four 8-byte LDS stores (one per column) then fall in 32 distinct
-    // 8-byte bank slots (columns four apart are 320 bytes apart, 64 modulo the 256-byte bank
-    // cycle, and the token quads fill the 64), where token-quad-major lanes collided 8 ways.
-    const int tq = tid & 7, c4 = (tid >> 3) * 4;
+    // stored.  dY: thread t takes tokens 4 (t % 8) + 2 (t / 256) + {0, 1} of the four columns
+    // 4 ((t / 8) % 32) .. +3 (two 16-byte loads) and writes each (column, token pair) with
+    // one 4-byte store per part; q: tokens 4 (t % 8) .. +3 of the columns 4 (t / 8) .. +3 (four
+    // dword loads), one 8-byte store per column.  In both, lane l of a half-wave takes token
+    // quad l % 8 and column quad l / 8, so a store instruction's lanes fall in 32 distinct
+    // banks (columns four apart are 320 bytes apart, 64 modulo the 256-byte bank cycle, and
+    // the token quads fill the 64), where token-quad-major lanes collided 8 ways.
+    const int tq = tid & 7;
+    const int yc = ((tid >> 3) & 31) * 4, yh = tid >> 8;   // dY: column quad, token pair
+    const int qc = (tid >> 3) * 4;                          // q: column quad
     struct Regs {
-        v4u y[4];      // [token]: four dY columns
-        float s[4];
+        v4u y[2];      // [token of the pair]: four dY columns
+        float s[2];
         uint32_t q[4]; // [token]: four q columns
     };
     auto load = [&](Regs &R, int st) {
@@ -399,9 +404,9 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
         const rsrc_t yres = make_rsrc(p.dY + (int64_t)t0 * N + n0, ybytes > 0 ? (uint32_t)ybytes : 0u);
         const rsrc_t qres = make_rsrc(p.Xq + (int64_t)t0 * K + k0, qbytes > 0 ? (uint32_t)qbytes : 0u);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const int t = 4 * tq + h;
-            const uint32_t off = (uint32_t)(t * N + c4) * 4u;
+        for (int h = 0; h < 2; ++h) {
+            const int t = 4 * tq + 2 * yh + h;
+            const uint32_t off = (uint32_t)(t * N + yc) * 4u;
             if ((N & 3) == 0) {
                 R.y[h] = buf_load16(yres, off);
             } else {
@@ -411,26 +416,26 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
                     R.y[h][e] = buf_load4(yres, off + 4u * e);
             }
             R.s[h] = __uint_as_float(buf_load4(sres, (uint32_t)(t0 + t) * 4u));
-            R.q[h] = buf_load4(qres, (uint32_t)(t * K + c4));
         }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            R.q[h] = buf_load4(qres, (uint32_t)((4 * tq + h) * K + qc));
     };
     auto store = [&](const Regs &R, int buf) {
         unsigned char *st = lds[buf];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v[4], f[4];
+            uint32_t hi, lo;
+            split_pair(__uint_as_float(R.y[0][e]) * R.s[0], __uint_as_float(R.y[1][e]) * R.s[1], hi, lo);
+            unsigned char *dy = st + (yc + e) * kGwPitch + 8 * tq + 4 * yh;
+            *reinterpret_cast<uint32_t *>(dy) = hi;
+            *reinterpret_cast<uint32_t *>(dy + kGwPartY) = lo;
+            float f[4];
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                v[h] = __uint_as_float(R.y[h][e]) * R.s[h];
+            for (int h = 0; h < 4; ++h)
                 f[h] = (float)((int)(R.q[h] << (24 - 8 * e)) >> 24);   // exact in bf16
-            }
-            uint32_t h01, l01, h23, l23;
-            split_pair(v[0], v[1], h01, l01);
-            split_pair(v[2], v[3], h23, l23);
-            unsigned char *dst = st + (c4 + e) * kGwPitch + 8 * tq;
-            *reinterpret_cast<v2u *>(dst) = v2u{h01, h23};
-            *reinterpret_cast<v2u *>(dst + kGwPart) = v2u{l01, l23};
-            *reinterpret_cast<v2u *>(dst + 2 * kGwPart) = v2u{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
+            *reinterpret_cast<v2u *>(st + 2 * kGwPartY + (qc + e) * kGwPitch + 8 * tq) =
+                v2u{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3])};
         }
     };
 
@@ -446,12 +451,12 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
         v4u bq[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-            bq[ni] = *reinterpret_cast<const v4u *>(st + 2 * kGwPart + (wn * 64 + ni * 16 + r) * kGwPitch + 16 * g);
+            bq[ni] = *reinterpret_cast<const v4u *>(st + 2 * kGwPartY + (wn * 64 + ni * 16 + r) * kGwPitch + 16 * g);
 #pragma unroll
         for (int part = 0; part < 2; ++part)
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi) {
-                const v4u a = *reinterpret_cast<const v4u *>(st + part * kGwPart +
+                const v4u a = *reinterpret_cast<const v4u *>(st + part * kGwPartY +
                                                              (wm * 64 + mi * 16 + r) * kGwPitch + 16 * g);
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
