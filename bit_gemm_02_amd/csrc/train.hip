@@ -66,15 +66,16 @@ struct WgBatch {
     int blocks;
 };
 
-constexpr int kWgThreads = 256;              // 2 x 2 waves, 64 x 64 outputs each
-constexpr int kWgBM = 128, kWgBO = 128;      // block tile: A rows x code rows
+constexpr int kWgThreads = 512;              // 2 x 4 waves, 64 x 64 outputs each
+constexpr int kWgBM = 128, kWgBO = 256;      // block tile: A rows x code rows
 constexpr int kWgKC = 64;                    // contraction per stage (4 packed words a row)
 constexpr int kWgPitch = 2 * kWgKC + 16;     // LDS bytes per bf16 A row (padded: no bank
                                              // conflicts between the 16 rows of a read)
 constexpr int kWgABytes = kWgBM * kWgPitch;
 constexpr int kWgTBytes = kWgBO * 16;
 
-// F32: A is fp32, split into hi / lo parts while staging.  Block tile 128 x 128, stages of
+// F32: A is fp32, split into hi / lo parts while staging.  Block tile 128 x 256 (twice as
+// many code rows as A rows: each split A value then feeds twice the MFMAs), stages of
 // 64 contraction indices double-buffered in LDS: the next stage's global loads are in
 // flight while the current one is multiplied, one barrier per stage.  Lane (r, g) reads the
 // A fragment of row r, contraction 16g + 8j .. +7 (16 bytes of LDS) and word g of its code
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int r = lane & 15, g = lane >> 4;
     const int Kc = p.Kc;
     const int words = Kc / 16;
