@@ -784,7 +784,7 @@ def main():
     pre_what = (f"{ops} int8 ops (2 M N K over {setup.count} products); {pre_bytes} bytes "
                 f"(M K + N K / 4 + 4 M + 4 + 4 M N summed); {ai:.0f} ops/B vs ridge {ridge:.0f}")
     if ai < ridge:
-        # Below the ridge the product is bound by HBM: judge it in bytes.
+        # Below the ridge the product is bound by HBM: measure it in bytes.
         pre_roof = hbm(pre_bytes, "prefill_gemm", pre_what)
     else:
         pre_roof = {"bound": "mfma", "achieved": gemm_tops, "peak": INT8_PEAK_TOPS,
