@@ -72,9 +72,13 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(name: str) -> str:
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(names: str) -> str:
+    """Hash of the sources a kernel is built from ("a.hip+b.hpp": every file, in order)."""
+    h = hashlib.sha256()
+    for name in names.split("+"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_model() -> str:
@@ -193,6 +197,12 @@ class Setup:
                                         self.P_pre[i].data_ptr(), self.g_pre[i].data_ptr(),
                                         self.Y_pre[i].data_ptr(), None, self.M_pre, m.N, m.K)
         self.fwd_pre_table = arr
+        ex = (bl._ForwardExProblem * n)()
+        for i, m in enumerate(mats):
+            ex[i] = bl._ForwardExProblem(self.act_pre[i][0].data_ptr(), self.act_pre[i][1].data_ptr(),
+                                         self.P_pre[i].data_ptr(), self.g_pre[i].data_ptr(),
+                                         self.Y_pre[i].data_ptr(), None, None, self.M_pre, m.N, m.K)
+        self.fwd_pre_ex_table = ex
         # Decode leg: the fused layer call (activation quantization inside the product).
         self.lin_dec_tables = []
         for r in range(self.R_dec):
@@ -225,6 +235,13 @@ class Setup:
         self.ws_bytes = self.ws.numel()
 
     # Work accounting (algorithmic, what the method must move or compute).
+    def mixed_one_launch(self) -> bool:
+        """Whether bitlinear_forward_mixed runs the step's products and decode leg as one launch:
+        every product has more than 16 tokens on 128 x 128 tiles (fewer than 512 tiles of
+        256 x 256), and the decode calls are fused with one activation dtype (always here)."""
+        big = sum(-(-self.M_pre // 256) * -(-m.N // 256) for m in self.wl.matrices)
+        return self.M_pre > 16 and big < 512 and self.M_dec <= 4
+
     def prefill_ops(self) -> int:
         return sum(2 * self.M_pre * m.N * m.K for m in self.wl.matrices)
 
@@ -279,12 +296,12 @@ class Setup:
         rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[rp]), n, stream)
         assert rc == 0, rc
         mark("t_aq")
-        rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+        # The prefill products and the decode leg in one launch (a mixed batch): the decode
+        # blocks fill the compute units the products' last tiles leave idle.
+        rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
+                                       self._addr(self.lin_dec_tables[rd]), n, stream)
         assert rc == 0, rc
-        mark("t_gemm")
-        rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[rd]), n, stream)
-        assert rc == 0, rc
-        mark("t_dec")
+        mark("t_mix")
 
     def launch_only(self, key: str, i: int, stream):
         """One launch group of the step by itself (same tables as in the step)."""
@@ -292,6 +309,9 @@ class Setup:
         n = self.count
         if key == "prefill_gemm":
             rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+        elif key == "prefill_and_decode":
+            rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
+                                           self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
         elif key == "decode_linear":
             rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
         elif key == "decode_linear_b3":
@@ -338,8 +358,9 @@ def interval_ms(ev, a, b):
 # Kernel name fragment -> (roofline key, source file).  (The decode leg quantizes its
 # activations inside decode_kernel, so every act_quant launch belongs to the prefill leg.)
 KERNELS = {
-    "prefill_kernel": ("prefill_gemm", "prefill.hip"),
-    "decode_kernel": ("decode_linear", "decode.hip"),
+    "mixed_kernel": ("prefill_and_decode", "mixed.hip+prefill_core.hpp+decode_core.hpp"),
+    "prefill_kernel": ("prefill_gemm", "prefill.hip+prefill_core.hpp"),
+    "decode_kernel": ("decode_linear", "decode.hip+decode_core.hpp"),
     "act_quant": ("act_quant_prefill", "quant.hip"),
     "gamma_partial_kernel": ("weight_quant", "quant.hip"),
     "quant_pack_kernel": ("weight_quant", "quant.hip"),
@@ -752,13 +773,14 @@ def main():
     in_step = {
         "weight_quant": interval_ms(ev, "t0", "t_wq"),
         "act_quant_prefill": interval_ms(ev, "t_wq", "t_aq"),
-        "prefill_gemm": interval_ms(ev, "t_aq", "t_gemm"),
-        "decode_linear": interval_ms(ev, "t_gemm", "t_dec"),
+        "prefill_and_decode": interval_ms(ev, "t_aq", "t_mix"),
     }
     if not setup.wq_tables:
         in_step.pop("weight_quant")
-    ms_with_events = interval_ms(ev, "t0", "t_dec")
-    ms = {k: isolated_ms(torch, setup, k, args.steps) for k in in_step}
+    ms_with_events = interval_ms(ev, "t0", "t_mix")
+    # Isolated launches: the step's own, plus the product and the decode leg each alone.
+    ms = {k: isolated_ms(torch, setup, k, args.steps)
+          for k in list(in_step) + ["prefill_gemm", "decode_linear"]}
     ms_b3 = isolated_ms(torch, setup, "decode_linear_b3", args.steps)
     peaks = measured_peaks(torch, bl)
 
@@ -779,7 +801,8 @@ def main():
         return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": a / HBM_PEAK_GBPS, "peak_measured": peaks["hbm_read_GBps"],
                 "frac_measured": a / peaks["hbm_read_GBps"], "us_per_launch": ms[key] * 1e3,
-                "us_per_launch_in_step": in_step[key] * 1e3, "algorithmic": what}
+                "us_per_launch_in_step": in_step[key] * 1e3 if key in in_step else None,
+                "algorithmic": what}
 
     pre_what = (f"{ops} int8 ops (2 M N K over {setup.count} products); {pre_bytes} bytes "
                 f"(M K + N K / 4 + 4 M + 4 + 4 M N summed); {ai:.0f} ops/B vs ridge {ridge:.0f}")
@@ -792,7 +815,7 @@ def main():
                     "peak_measured": peaks["int8_mfma_TOPS"],
                     "frac_measured": gemm_tops / peaks["int8_mfma_TOPS"],
                     "us_per_launch": ms["prefill_gemm"] * 1e3,
-                    "us_per_launch_in_step": in_step["prefill_gemm"] * 1e3, "algorithmic": pre_what}
+                    "us_per_launch_in_step": None, "algorithmic": pre_what}
     attainable_meas = min(peaks["int8_mfma_TOPS"], ai * peaks["hbm_read_GBps"] / 1e3)
     pre_roof.update({"tops": gemm_tops, "frac_int8_peak": gemm_tops / INT8_PEAK_TOPS,
                      "attainable_tops": attainable, "frac_attainable": gemm_tops / attainable,
@@ -806,12 +829,22 @@ def main():
         "act_quant_prefill": hbm(aq_bytes, "act_quant_prefill",
                                  f"{aq_bytes} bytes (M K x-bytes + M K + 4 M (+ 4 K norm) summed)"),
     }
+    mix_bytes = pre_bytes + dec_bytes
+    rooflines["prefill_and_decode"] = hbm(
+        mix_bytes, "prefill_and_decode",
+        f"{mix_bytes} bytes (the prefill products' {pre_bytes} and the decode leg's {dec_bytes}, "
+        f"one launch); {ops} int8 ops; {ops / mix_bytes:.0f} ops/B vs ridge {ridge:.0f}")
     if "weight_quant" in ms:
         rooflines["weight_quant"] = hbm(wq_bytes, "weight_quant",
                                         f"{wq_bytes} bytes (4 N K + N K / 4 + 4 summed; one read "
                                         "of W is the minimum, the two launches read it twice)")
-    # Dominant kernel = largest share of the step.
+    # Dominant kernel = largest share of the step.  Where the mixed call could not share one
+    # launch (products on 256 x 256 tiles), its interval is the product's launch followed by
+    # the decode leg's, and the product is the kernel that dominates it.
+    fused = setup.mixed_one_launch()
     dom = max(in_step, key=lambda k: in_step[k])
+    if dom == "prefill_and_decode" and not fused:
+        dom = "prefill_gemm"
     traffic = load_traffic()
     t = traffic.get((dom, wl.key))
     roof = dict(rooflines[dom])
@@ -850,16 +883,21 @@ def main():
                     "frac_attainable": round(gemm_tops / attainable, 4),
                     "ops": ops, "us_gemm": round(ms["prefill_gemm"] * 1e3, 3),
                     "us_weight_quant": round(ms["weight_quant"] * 1e3, 3) if "weight_quant" in ms else None,
-                    "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3)},
+                    "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3),
+                    "us_prefill_and_decode": round(ms["prefill_and_decode"] * 1e3, 3),
+                    "us_prefill_plus_decode_separate": round((ms["prefill_gemm"] + ms["decode_linear"]) * 1e3, 3)},
         "roofline": roof,
         "measured_peaks": peaks,
         "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in rooflines.items()},
         "timing": {"ms_per_step_wall": round(wall_ms, 4),
+                   "mixed_launch": "one launch" if fused else "two launches (256 x 256 product tiles)",
                    "ms_per_step_with_launch_events": round(ms_with_events, 4),
-                   "schedule": "one stream, launches in step order (three streams, weight quant "
-                               "beside act quant and decode beside prefill, and the decode leg "
-                               "alone on a second stream, measured slower)"},
+                   "schedule": "one stream, launches in step order: weight quantization, "
+                               "activation quantization, then the prefill products and the decode "
+                               "leg as one mixed launch (three streams, weight quant beside act "
+                               "quant and decode beside prefill, and the decode leg alone on a "
+                               "second stream, measured slower than one stream)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)

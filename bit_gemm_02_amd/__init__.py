@@ -161,6 +161,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_quantize_acts_ex_grouped.restype = ctypes.c_int
     L.bitlinear_forward_ex_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_forward_ex_grouped.restype = ctypes.c_int
+    L.bitlinear_forward_mixed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P]
+    L.bitlinear_forward_mixed.restype = ctypes.c_int
     L.bitlinear_linear_ex_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_ex_grouped.restype = ctypes.c_int
     for fn in ("bitlinear_forward_wonly_grouped", "bitlinear_grad_input_grouped",
@@ -363,12 +365,11 @@ def linear_fused(M: int, K: int) -> bool:
     return M <= LINEAR_FUSED_MAX_M and M * K <= LINEAR_FUSED_MAX_BYTES
 
 
-def linear_grouped(problems: Sequence[dict], stream=None) -> None:
-    """Layer calls as dicts with keys X (fp32/bf16 [M, K]), W_packed, gamma, Y (preallocated
-    fp32 [M, N]) and optional norm_weight, eps, X_q, x_scale (code/scale outputs; required
-    when the call is not decode-sized).  Decode-sized calls share one fused launch."""
-    count = len(problems)
-    arr = (_LinearProblem * max(count, 1))()
+def linear_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_linear_grouped: dicts with keys X (fp32/bf16 [M, K]),
+    W_packed, gamma, Y (preallocated fp32 [M, N]) and optional norm_weight, eps, X_q, x_scale
+    (code/scale outputs; required when the call is not decode-sized)."""
+    arr = (_LinearProblem * max(len(problems), 1))()
     for i, p in enumerate(problems):
         X = _dev(p["X"], f"X[{i}]")
         M, K = X.shape
@@ -377,8 +378,14 @@ def linear_grouped(problems: Sequence[dict], stream=None) -> None:
                                 _ptr(p["gamma"]), _ptr(p["Y"]), _ptr(p.get("X_q")),
                                 _ptr(p.get("x_scale")), M, N, K, _x_dtype(X),
                                 float(p.get("eps", 1e-6)))
+    return arr
+
+
+def linear_grouped(problems: Sequence[dict], stream=None) -> None:
+    """Layer calls (dicts as for linear_table); decode-sized calls share one fused launch."""
+    arr = linear_table(problems)
     _check("bitlinear_linear_grouped",
-           lib().bitlinear_linear_grouped(ctypes.addressof(arr), count, _stream(stream)))
+           lib().bitlinear_linear_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
 
 
 def linear(X: torch.Tensor, W_packed: torch.Tensor, gamma: torch.Tensor,
@@ -446,6 +453,17 @@ def forward_ex_grouped(problems: Sequence[dict], stream=None) -> None:
     arr = forward_ex_table(problems)
     _check("bitlinear_forward_ex_grouped",
            lib().bitlinear_forward_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+def forward_mixed(prefill: Sequence[dict], decode: Sequence[dict], stream=None) -> None:
+    """A mixed batch: prefill products (dicts as for forward_ex_table) and decode layer calls
+    (dicts as for linear_table), in one launch when both sets allow it; results equal
+    forward_ex_grouped(prefill) followed by linear_grouped(decode)."""
+    pre = forward_ex_table(prefill)
+    dec = linear_table(decode)
+    _check("bitlinear_forward_mixed",
+           lib().bitlinear_forward_mixed(ctypes.addressof(pre), len(prefill), ctypes.addressof(dec),
+                                         len(decode), _stream(stream)))
 
 
 def linear_ex_table(problems: Sequence[dict]):

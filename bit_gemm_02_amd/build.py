@@ -14,7 +14,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.hip", "quant.hip", "decode.hip", "prefill.hip", "train.hip", "calib.hip"]
+SOURCES = ["api.hip", "quant.hip", "decode.hip", "prefill.hip", "mixed.hip", "train.hip", "calib.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -301,7 +301,7 @@ const char *bitlinear_status_string(int status)
     }
 }
 
-int bitlinear_abi_version(void) { return 100; }
+int bitlinear_abi_version(void) { return 101; }
 
 size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
 {
@@ -487,6 +487,51 @@ bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count,
         return run_forward(fwd, nt, stream);
     }
     return BL_OK;
+}
+
+bl_status bitlinear_forward_mixed(const bl_forward_ex_problem *prefill, int npre,
+                                  const bl_linear_problem *decode, int ndec, void *stream)
+{
+    if (npre < 0 || ndec < 0 || npre > BL_MAX_GROUP || ndec > BL_MAX_GROUP || npre + ndec == 0)
+        return BL_ERR_COUNT;
+    if ((npre && !prefill) || (ndec && !decode))
+        return BL_ERR_NULL;
+    // Every problem is validated before anything is launched.
+    bl_forward_ex_problem pre[BL_MAX_GROUP];
+    bl_linear_ex_problem dec[BL_MAX_GROUP];
+    int np = 0, nd = 0;
+    int64_t pre_blocks = 0, dec_blocks = 0;
+    for (int i = 0; i < npre; ++i) {
+        bl_status s = check_forward_ex(prefill[i]);
+        if (s != BL_OK)
+            return s;
+        if (prefill[i].M > 0 && prefill[i].N > 0) {
+            pre[np++] = prefill[i];
+            pre_blocks += ((prefill[i].M + 127) / 128) * ((prefill[i].N + 127) / 128);
+        }
+    }
+    bool fused = true;
+    for (int i = 0; i < ndec; ++i) {
+        bl_status s = check_linear(decode[i]);
+        if (s != BL_OK)
+            return s;
+        if (decode[i].M > 0 && decode[i].N > 0) {
+            fused = fused && linear_fused(decode[i]);
+            dec[nd++] = to_ex(decode[i]);
+            dec_blocks += (decode[i].N + 15) / 16;
+        }
+    }
+    if (pre_blocks + dec_blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    if (fused && bl::mixed_eligible(pre, np, dec, nd))
+        return from_hip(bl::launch_mixed(pre, np, dec, nd, static_cast<hipStream_t>(stream)));
+    // Otherwise the two calls, prefill first.
+    if (npre) {
+        bl_status s = bitlinear_forward_ex_grouped(prefill, npre, stream);
+        if (s != BL_OK)
+            return s;
+    }
+    return ndec ? bitlinear_linear_grouped(decode, ndec, stream) : BL_OK;
 }
 
 bl_status bitlinear_linear_ex_grouped(const bl_linear_ex_problem *problems, int count,

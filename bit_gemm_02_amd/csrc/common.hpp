@@ -304,6 +304,13 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipS
 // BL_LINEAR_FUSED_MAX_BYTES.
 hipError_t launch_linear_decode(const bl_linear_ex_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
+// Mixed batch (prefill products + fused decode calls) in one launch: eligible when every
+// prefill product has M > 16 and takes the 128 x 128 tile, and every decode call is a fused
+// single projection (no pair, activation or residual) with one activation dtype.
+bool mixed_eligible(const bl_forward_ex_problem *pre, int npre, const bl_linear_ex_problem *dec,
+                    int ndec);
+hipError_t launch_mixed(const bl_forward_ex_problem *pre, int npre, const bl_linear_ex_problem *dec,
+                        int ndec, hipStream_t stream);
 
 // Training-side products (train.hip).  Y[M][O] = gamma * A[M][Kc] T^T with T packed codes
 // [O][Kc/16] and A fp32 or bf16: the weight-only forward, and the input gradient with the

@@ -17,500 +17,14 @@
 // weight rows from LDS, expanded into B operands; the A operands (16 activation bytes of
 // token row r, k group g) from LDS with one 16-byte read each.
 // Epilogue: y = fl32(fp64(acc * gamma * s_x[m])), acc = (MFMA sum) / 64 (exact shift).
-#include <stdlib.h>
-#include <string.h>
-
-#include <type_traits>
-
-#include "common.hpp"
+#include "prefill_core.hpp"
 
 namespace bl {
 
-
-struct PreDev {
-    const int8_t *Xq;
-    const float *sx;
-    const uint32_t *W;
-    const float *gamma;
-    float *Y;
-    int32_t *acc;
-    const float *R;     // residual added to the output, or NULL
-    int M, N, K;
-    int tiles_n;
-    int block_begin;
-};
-
-struct PreBatch {
-    PreDev p[BL_MAX_GROUP];
-    int count;
-    int blocks;
-};
-
-// Raw buffer descriptor as four scalar dwords: base address, stride 0, size in bytes, and
-// the gfx9-family raw-access word.  Offsets at or past `bytes` read zero.
-__device__ __forceinline__ v4i make_desc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)base;
-    v4i d;
-    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
-    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    d.w = 0x00020000;
-    return d;
-}
-
-// LDS byte address of a shared-memory pointer, wave-uniform.
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
-{
-    typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_uchar *)p);
-}
-
-// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at LDS address
-// lds + 16 * l; an out-of-range offset writes zeros.  Issued from inline assembly so that the
-// compiler does not model it: modelled, it cannot tell the in-flight stages apart and drains
-// every load before the first LDS read of each unrolled group of stages.  The instruction
-// has no register result; its completion is ordered by the pipeline's explicit vmcnt waits
-// and barriers, and the "memory" clobber keeps LDS accesses from moving across it.
-__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, uint32_t offset)
-{
-    asm volatile("s_mov_b32 m0, %0\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(offset), "s"(desc)
-                 : "memory", "m0");
-}
-
-// Workgroup barrier that is also a compiler barrier for memory operations (the barrier
-// instruction alone does not stop the compiler from moving LDS accesses across it), without
-// the waits a memory fence would add.
-__device__ __forceinline__ void block_sync()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N): wait until at most N vector-memory loads of this wave (direct-to-LDS
-// ones included) are still in flight.  Other counters are left alone.
-template <int N>
-__device__ __forceinline__ void wait_vmem()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Tile configuration: BM x BN block tile split over WM x WN waves (wave tile BM/WM x BN/WN,
-// MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS, EA bytes per
-// activation (1: int8 codes on the int8 matrix unit; 2: bf16 activations on the bf16 one).
-template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_, int EA_ = 1>
-struct Tile {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KS = KS_, NST = NST_, EA = EA_;
-    static constexpr int WAVES = WM * WN;
-    static constexpr int THREADS = WAVES * 64;
-    static constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
-    static constexpr int MI = TM / 16, NI = TN / 16;     // MFMA tiles per wave, each direction
-    static constexpr int XROW = KS * EA;                 // activation bytes per row per stage
-    static constexpr int CPR = XROW / 16;                // 16-byte activation chunks per row
-    static constexpr int WPS = KS / 16;                  // packed words per weight row
-    static constexpr int LPW = WPS / 4;                  // words per lane (one MFMA k-step each)
-    static constexpr int WROW = KS / 4;                  // bytes per weight row per stage
-    static constexpr int XBYTES = BM * XROW;
-    static constexpr int WBYTES = BN * WROW;
-    static constexpr int STAGE = XBYTES + WBYTES;
-    static constexpr int XINST = XBYTES / 1024 / WAVES;  // 1 KB direct loads per wave per stage
-    static constexpr int WINST = WBYTES / 1024 / WAVES;
-    static constexpr int LOADS = XINST + WINST;          // vector-memory ops per wave per stage
-    static_assert(LPW >= 1 && LPW <= 4, "1..4 words per lane");
-    static_assert(XINST >= 1 && WINST >= 1, "every wave loads part of each operand");
-    static_assert(XINST * WAVES * 1024 == XBYTES && WINST * WAVES * 1024 == WBYTES, "even split");
-    static_assert(NST * STAGE <= 160 * 1024, "LDS budget");
-    static_assert((NST - 2) * LOADS < 64, "vmcnt range");
-};
-
-// Activation chunk swizzle: chunk c of tile row m sits at position c ^ f(m), chosen so that
-// the 16 rows of one MFMA A-operand read (same c) fall in 16 different 16-byte bank slots of
-// a 256-byte bank cycle: f(m) = (m / (16 / CPR)) % CPR.
-template <int CPR>
-__device__ __forceinline__ int xswz(int row)
-{
-    return (row / (16 / CPR)) & (CPR - 1);
-}
-
-// Weight chunk swizzle (16-byte chunks, WCH per row): rows m and m + 8 of a 16-row B-operand
-// read would share banks at a 32-byte row pitch; flipping the chunk order on every other
-// group of 8 rows separates them.
-template <int WCH>
-__device__ __forceinline__ int wswz(int row)
-{
-    return WCH > 1 ? ((row >> 3) & 1) : 0;
-}
-
-// One LDS buffer per pipeline stage, as distinct variables: the compiler can then tell that
-// a direct-to-LDS load into one stage does not alias reads from another, and does not force
-// a wait for every outstanding load before each LDS read.
-template <int S, int BYTES>
-__device__ __forceinline__ unsigned char *stage_buf()
-{
-    __shared__ __align__(1024) unsigned char buf[BYTES];
-    return buf;
-}
-
-template <int N>
-struct IC {
-    static constexpr int value = N;
-};
-
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (B < E) {
-        f(IC<B>{});
-        static_for<B + 1, E>(f);
-    }
-}
-
-// The prefill kernel.  Per stage, activations (BM rows x KS bytes, swizzled) and packed
-// weights (BN rows x KS/4 bytes) travel global -> LDS by direct buffer loads; NST - 1 stages
-// are in flight while one is computed, and one barrier per stage orders reuse of the buffers.
-// FULL_K: every problem has K % KS == 0 (no stage runs past a row).
 template <class T, bool FULL_K>
 __global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
 {
-    constexpr int BM = T::BM, BN = T::BN, KS = T::KS, NST = T::NST, WAVES = T::WAVES;
-    constexpr int MI = T::MI, NI = T::NI, CPR = T::CPR, LPW = T::LPW, WROW = T::WROW;
-    constexpr int EA = T::EA, XROW = T::XROW;
-    constexpr bool BF = EA == 2;      // bf16 activations: the weight-only product
-    constexpr int AH = EA;            // activation fragments per packed word (16 / 8 weights)
-    using AccT = typename std::conditional<BF, f32x4, v4i>::type;
-
-    int prob = 0;
-#pragma unroll 1
-    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
-        ++prob;
-    const PreDev &p = b.p[prob];
-    // XCD-aware order inside each problem, so every XCD gets its share of every problem.
-    const int ntiles = (prob + 1 < b.count ? b.p[prob + 1].block_begin : b.blocks) - p.block_begin;
-    const int tile = xcd_order(blockIdx.x - p.block_begin, ntiles);
-    // On large grids, consecutive tiles of one XCD walk two activation panels side by side,
-    // so each weight panel fetched into that XCD's L2 serves two tiles; small grids keep
-    // the plain row-major order (one panel of each is all an XCD holds anyway).
-    const int gm_max = ntiles >= 1024 ? 2 : 1;
-    const int tiles_m = ntiles / p.tiles_n;
-    const int grp = tile / (gm_max * p.tiles_n), within = tile % (gm_max * p.tiles_n);
-    const int gm = min(gm_max, tiles_m - grp * gm_max);
-    const int m0 = (grp * gm_max + within % gm) * BM;
-    const int n0 = (within / gm) * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-    const int wm = wave / T::WN, wn = wave % T::WN;
-    const int r = lane & 15;
-    const int g = lane >> 4;
-    const int K = p.K;
-    const int row_bytes = K / 4;
-    const int stages = (K + KS - 1) / KS;
-
-    // Activation rows m0 .. m0+BM-1 and weight rows n0 .. n0+BN-1; rows past M / N read zero.
-    const v4i xres = make_desc(reinterpret_cast<const unsigned char *>(p.Xq) + (int64_t)m0 * K * EA,
-                               rows_bytes(m0, BM, p.M, K * EA));
-    const v4i wres = make_desc(p.W + (int64_t)n0 * (K / 16), rows_bytes(n0, BN, p.N, row_bytes));
-
-    // Load plan.  Activations: wave w fills rows w*BM/WAVES .. +BM/WAVES, 64/CPR rows per 1 KB
-    // load; lane l -> row (l / CPR), position l % CPR, global chunk position ^ swizzle.
-    // Weights: wave w fills rows w*BN/WAVES .. +BN/WAVES, 1024/WROW rows per load; lane l ->
-    // row l / (WROW/16), position l % (WROW/16), global chunk position ^ swizzle.
-    // Past-the-row chunks (only when !FULL_K) read as zero for activations; weight words past
-    // K meet those zero activations.
-    constexpr int XR = 64 / CPR;            // activation rows per load
-    constexpr int WCH = WROW / 16;          // 16-byte weight chunks per row
-    constexpr int WR = 64 / WCH;            // weight rows per load
-    const int xrow_l = lane / CPR, xpos = lane % CPR;
-    const int wrow_l = lane / WCH, wcol = lane % WCH;
-    // A stage at or past `stages` is still issued, from out-of-range offsets: it writes zeros
-    // into a buffer nobody reads again, and keeps the number of loads in flight per stage
-    // constant, so a single compile-time vmcnt wait fits every iteration.
-    // (The dead-stage flag is folded into bit 31 of the offset arithmetically: a select on a
-    // uniform flag would be turned into branches around the loads, and the compiler then
-    // waits conservatively for all of them before reading LDS.)
-    auto issue = [&](auto S, int t) {
-        unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
-        const uint32_t dead = (uint32_t)(t >= stages) << 31;   // == kOOB for a dead stage
-#pragma unroll
-        for (int i = 0; i < T::XINST; ++i) {
-            const int row0 = wave * (BM / WAVES) + i * XR;
-            const int row = row0 + xrow_l;
-            const int c = xpos ^ xswz<CPR>(row);
-            const int k = t * KS + c * (16 / EA);                     // first element of the chunk
-            uint32_t off = ((uint32_t)row * K + (uint32_t)k) * EA | dead;
-            if (!FULL_K)
-                off = k < K ? off : kOOB;
-            dma16(xres, lds_addr(st + row0 * XROW), off);
-        }
-#pragma unroll
-        for (int i = 0; i < T::WINST; ++i) {
-            const int row0 = wave * (BN / WAVES) + i * WR;
-            const int row = row0 + wrow_l;
-            const int kb = t * WROW + 16 * (wcol ^ wswz<WCH>(row));   // byte offset in the row
-            uint32_t off = ((uint32_t)row * row_bytes + (uint32_t)kb) | dead;
-            if (!FULL_K)
-                off = kb < row_bytes ? off : kOOB;
-            dma16(wres, lds_addr(st + T::XBYTES + row0 * WROW), off);
-        }
-    };
-
-    AccT acc[MI][NI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = AccT{0, 0, 0, 0};
-
-    // Per-lane LDS offsets inside a stage.  Lane (r, g) reads words g*LPW .. +LPW-1 of its
-    // weight row: 16-byte chunk (g*LPW*4) / 16 (swizzled) at byte (g*LPW*4) % 16.
-    const int arow = (wm * T::TM + r) * XROW;                // + mi * 16 * XROW
-    const int aswz = xswz<CPR>(wm * T::TM + r);              // same for every mi (16 | mi*16)
-    const int bch = (g * LPW * 4) / 16, bin = (g * LPW * 4) % 16;
-    const int brow = T::XBYTES + (wn * T::TN + r) * WROW +
-                     16 * (bch ^ wswz<WCH>(wn * T::TN + r)) + bin;           // + ni * 16 * WROW
-
-    // The last k-step of each stage is deferred to the next stage: its operands (activation
-    // fragments and raw packed words) stay in registers, and its MFMAs are issued right after
-    // the next stage's barrier and LDS reads, so the matrix pipe has work while those reads
-    // are in flight instead of idling after every barrier.  (Zero operands before the first
-    // stage add nothing.)
-    v4i da[AH][MI];
-    uint32_t dw[NI];
-#pragma unroll
-    for (int h = 0; h < AH; ++h)
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            da[h][mi] = v4i{0, 0, 0, 0};
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-        dw[ni] = 0;
-    // One packed word per lane and weight row: int8, its four planes as one 16 x 16 x 64
-    // operand; bf16, its two halves of eight codes as two 16 x 16 x 32 operands.
-    auto mfma_step = [&](const uint32_t (&w)[NI], const v4i (&a)[AH][MI]) {
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            if constexpr (BF) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const v4u b = ternary_bf16(w[ni], h);
-#pragma unroll
-                    for (int mi = 0; mi < MI; ++mi)
-                        acc[mi][ni] = mfma_bf16(b, __builtin_bit_cast(v4u, a[h][mi]), acc[mi][ni]);
-                }
-            } else {
-                const v4i b = unpack_word64(w[ni]);
-#pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b, a[0][mi], acc[mi][ni], 0, 0, 0);
-            }
-        }
-    };
-    // Activations of word j of the lane's share: 16 int8 (one chunk), or 16 bf16 (two
-    // chunks, one per half).
-    auto read_a = [&](const unsigned char *st, int j, v4i (&a)[AH][MI]) {
-#pragma unroll
-        for (int h = 0; h < AH; ++h) {
-            const int pos = 16 * ((AH * (g * LPW + j) + h) ^ aswz);
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                a[h][mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * XROW + pos);
-        }
-    };
-
-    auto compute = [&](auto S) {
-        const unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
-        uint32_t wq[NI][LPW];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            const unsigned char *src = st + brow + ni * 16 * WROW;
-            if constexpr (LPW == 4) {
-                const v4u v = *reinterpret_cast<const v4u *>(src);
-                wq[ni][0] = v.x; wq[ni][1] = v.y; wq[ni][2] = v.z; wq[ni][3] = v.w;
-            } else if constexpr (LPW == 2) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(src);
-                wq[ni][0] = v.x; wq[ni][1] = v.y;
-            } else {
-                wq[ni][0] = *reinterpret_cast<const uint32_t *>(src);
-            }
-        }
-        v4i a0[AH][MI];
-        read_a(st, 0, a0);
-        mfma_step(dw, da);          // previous stage's last k-step
-        static_assert(LPW >= 2, "one k-step per stage is deferred");
-#pragma unroll
-        for (int j = 0; j < LPW - 1; ++j) {
-            uint32_t w[NI];
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                w[ni] = wq[ni][j];
-            if (j == 0) {
-                mfma_step(w, a0);
-            } else {
-                v4i a[AH][MI];
-                read_a(st, j, a);
-                mfma_step(w, a);
-            }
-        }
-        read_a(st, LPW - 1, da);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            dw[ni] = wq[ni][LPW - 1];
-    };
-
-    // Row scales and gamma, loaded before the pipeline starts: older than every stage load,
-    // they have landed by the first stage wait, and the epilogue does not wait on memory.
-    float sxv[MI];
-    {
-        const rsrc_t sres = make_rsrc(p.sx, BF ? 0u : (uint32_t)p.M * 4u);   // bf16: unused
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int m = m0 + wm * T::TM + mi * 16 + r;   // rows past M read 0
-            sxv[mi] = __uint_as_float(buf_load4(sres, (uint32_t)m * 4u));
-        }
-    }
-    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
-
-    // Prologue: stages 0 .. NST-2 in flight.
-    static_for<0, NST - 1>([&](auto S) { issue(S, S.value); });
-    // Main loop, unrolled by NST so every stage buffer is a compile-time choice.  Stage t has
-    // landed once only the NST - 2 stages issued after it are still in flight.
-    for (int t0 = 0; t0 < stages; t0 += NST) {
-        static_for<0, NST>([&](auto S) {
-            const int t = t0 + S.value;
-            if (t < stages) {
-                wait_vmem<(NST - 2) * T::LOADS>();
-                block_sync();
-                issue(IC<(decltype(S)::value + NST - 1) % NST>{}, t + NST - 1);
-                compute(S);
-            }
-        });
-    }
-    mfma_step(dw, da);              // the last stage's deferred k-step
-
-    // Epilogue.  The MFMA takes the weights as its row operand, so acc[mi][ni] register v
-    // holds 64 * D[m][n] for m = m0 + wm * TM + mi * 16 + r and n = n0 + wn * TN + ni * 16 +
-    // 4 * g + v: each lane owns four consecutive outputs of one row and writes them with one
-    // 16-byte store (scalar stores when the row pitch or the base is not 16-byte aligned, and
-    // in a ragged last column group).
-    if constexpr (BF) {
-        // Weight-only product: y = fl32(gamma * acc), acc the fp32 matrix-unit sum.
-        const bool vecb = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0;
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int m = m0 + wm * T::TM + mi * 16 + r;
-            if (m >= p.M)
-                continue;
-            float *yrow = p.Y + (int64_t)m * p.N;
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const int n = n0 + wn * T::TN + ni * 16 + 4 * g;
-                const f32x4 y = acc[mi][ni] * gammaf;
-                if (vecb && n + 3 < p.N) {
-                    *reinterpret_cast<float4 *>(yrow + n) = make_float4(y[0], y[1], y[2], y[3]);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (n + v < p.N)
-                            yrow[n + v] = y[v];
-                }
-            }
-        }
-        return;
-    } else {
-    const double gamma = (double)gammaf;
-    const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0 &&
-                     (!p.acc || ((uintptr_t)p.acc & 15) == 0) &&
-                     (!p.R || ((uintptr_t)p.R & 15) == 0);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-        const int m = m0 + wm * T::TM + mi * 16 + r;
-        if (m >= p.M)
-            continue;
-        const double scale = gamma * (double)sxv[mi];
-        float *yrow = p.Y + (int64_t)m * p.N;
-        const float *rrow = p.R ? p.R + (int64_t)m * p.N : nullptr;
-        int32_t *arow_out = p.acc ? p.acc + (int64_t)m * p.N : nullptr;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-            const int n = n0 + wn * T::TN + ni * 16 + 4 * g;
-            int a[4];
-            float y[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                a[v] = acc[mi][ni][v] >> 6;
-                y[v] = (float)((double)a[v] * scale);
-            }
-            if (vec && n + 3 < p.N) {
-                if (rrow) {
-                    const float4 rv = *reinterpret_cast<const float4 *>(rrow + n);
-                    y[0] = y[0] + rv.x;
-                    y[1] = y[1] + rv.y;
-                    y[2] = y[2] + rv.z;
-                    y[3] = y[3] + rv.w;
-                }
-                *reinterpret_cast<float4 *>(yrow + n) = make_float4(y[0], y[1], y[2], y[3]);
-                if (arow_out)
-                    *reinterpret_cast<int4 *>(arow_out + n) = make_int4(a[0], a[1], a[2], a[3]);
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    if (n + v < p.N) {
-                        yrow[n + v] = rrow ? y[v] + rrow[n + v] : y[v];
-                        if (arow_out)
-                            arow_out[n + v] = a[v];
-                    }
-                }
-            }
-        }
-    }
-    }
-}
-
-template <class T>
-static int build_batch(const bl_forward_ex_problem *q, int count, PreBatch &b, bool &full_k)
-{
-    // Longest-K problems first: their tiles take longest, so they should not start last.
-    int order[BL_MAX_GROUP];
-    int n = 0;
-    for (int i = 0; i < count; ++i)
-        if (q[i].M > 0 && q[i].N > 0)
-            order[n++] = i;
-    for (int i = 1; i < n; ++i)
-        for (int j = i; j > 0 && q[order[j]].K > q[order[j - 1]].K; --j) {
-            const int t = order[j];
-            order[j] = order[j - 1];
-            order[j - 1] = t;
-        }
-    int blocks = 0;
-    full_k = true;
-    for (int i = 0; i < n; ++i) {
-        const bl_forward_ex_problem &s = q[order[i]];
-        PreDev &d = b.p[i];
-        d.Xq = s.X_q;
-        d.sx = s.x_scale;
-        d.W = s.W_packed;
-        d.gamma = s.gamma;
-        d.Y = s.Y;
-        d.acc = s.acc;
-        d.R = s.residual;
-        d.M = (int)s.M;
-        d.N = (int)s.N;
-        d.K = (int)s.K;
-        d.tiles_n = (d.N + T::BN - 1) / T::BN;
-        d.block_begin = blocks;
-        blocks += ((d.M + T::BM - 1) / T::BM) * d.tiles_n;
-        full_k = full_k && (d.K % T::KS == 0);
-    }
-    b.count = n;
-    b.blocks = blocks;
-    return blocks;
+    prefill_block<T, FULL_K>(b, blockIdx.x);
 }
 
 template <class T>
@@ -527,30 +41,6 @@ static hipError_t launch_tiles(const bl_forward_ex_problem *q, int count, hipStr
         hipLaunchKernelGGL((prefill_kernel<T, false>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
     return hipGetLastError();
 }
-
-using TileBig = Tile<256, 256, 4, 2, 128, 4>;    // 160 KB LDS, one block (8 waves) per CU
-// Small tiles: a 3-stage ring (60 KB LDS, two blocks per CU) measured faster than 4 stages
-// (80 KB, c2 product 27.3 -> 25.9 us) and than 2 stages (40 KB, four blocks per CU).
-using TileSmall = Tile<128, 128, 2, 2, 128, 3>;
-
-static int tile_override()
-{
-    // Measurement-only knob to A/B the two tile layouts (BITLINEAR_PREFILL_TILE=big|small).
-    static int v = [] {
-        const char *e = getenv("BITLINEAR_PREFILL_TILE");
-        if (!e)
-            return 0;
-        if (!strcmp(e, "big")) return 1;
-        if (!strcmp(e, "small")) return 2;
-        return 0;
-    }();
-    return v;
-}
-
-// The weight-only product with bf16 activations (the W1.58.A16 forward and the input gradient
-// with bf16 dY): the same pipeline with 2-byte activations and the bf16 matrix unit.
-using TileWBig = Tile<256, 256, 4, 2, 128, 2, 2>;     // 144 KB LDS, one block per CU
-using TileWSmall = Tile<128, 128, 2, 2, 128, 2, 2>;   // 72 KB, two blocks per CU
 
 hipError_t launch_wonly_prefill(const WgProblem *q, int count, hipStream_t stream)
 {
@@ -572,19 +62,9 @@ hipError_t launch_wonly_prefill(const WgProblem *q, int count, hipStream_t strea
     return launch_tiles<TileWSmall>(ex, n, stream);
 }
 
-// Large tiles (half the LDS and cache traffic per operation) when they still give every
-// compute unit at least two tiles; otherwise 128 x 128.
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
-    switch (tile_override()) {
-    case 1: return launch_tiles<TileBig>(q, count, stream);
-    case 2: return launch_tiles<TileSmall>(q, count, stream);
-    default: break;
-    }
-    int64_t big = 0;
-    for (int i = 0; i < count; ++i)
-        big += ((q[i].M + 255) / 256) * ((q[i].N + 255) / 256);
-    if (big >= 512)
+    if (prefill_big_tiles(q, count))
         return launch_tiles<TileBig>(q, count, stream);
     return launch_tiles<TileSmall>(q, count, stream);
 }

@@ -306,6 +306,34 @@ bl_status bitlinear_forward_ex_grouped(const bl_forward_ex_problem *problems, in
                                        void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Mixed batch: one chunk of prompt tokens (prefill) and a few decode tokens in one call.
+ *
+ * SLM750-Edge card, "Performance": inference has a prompt-processing phase and a single-token
+ * decode phase (the latter bandwidth-bound); both run the same BitLinear forward (steps 3 to
+ * 5), and a serving step that batches a prompt chunk with other requests' decode tokens runs
+ * both sets of products.
+ *
+ *   prefill, npre   products with quantized activations, as for bitlinear_forward_ex_grouped
+ *                   (0 <= npre <= BL_MAX_GROUP; may be NULL when npre == 0).
+ *   decode, ndec    layer calls, as for bitlinear_linear_grouped (0 <= ndec <= BL_MAX_GROUP;
+ *                   may be NULL when ndec == 0).
+ * Results: bit for bit those of bitlinear_forward_ex_grouped(prefill, npre) followed by
+ * bitlinear_linear_grouped(decode, ndec).  When every non-empty prefill product has M > 16
+ * and the products take 128 x 128 tiles (fewer than 512 tiles of 256 x 256), and every
+ * non-empty decode call takes the fused form with one activation dtype, both sets share one
+ * launch: the decode blocks run on the compute units the product's last tiles leave idle.
+ * Otherwise the two calls run in that order on the stream.
+ * The two sets run concurrently: no buffer one set writes may be read or written by the
+ * other.
+ * Errors: BL_ERR_COUNT (npre or ndec outside 0 .. BL_MAX_GROUP, or both 0), BL_ERR_NULL (a
+ * NULL array with a nonzero count), then each problem's errors as for the two calls, and
+ * BL_ERR_SHAPE when the launch would exceed 2^31 - 1 blocks.  Every problem is validated
+ * before anything is launched.
+ * ------------------------------------------------------------------------------------- */
+bl_status bitlinear_forward_mixed(const bl_forward_ex_problem *prefill, int npre,
+                                  const bl_linear_problem *decode, int ndec, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * (3) The decode form of a layer's product calls: bitlinear_linear_grouped's fused call
  *     (activation quantization inside the product) with the layer's output stages in the
  *     epilogue, so that a layer's BitLinear sub-graph at a few tokens takes three launches

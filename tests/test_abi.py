@@ -64,7 +64,7 @@ def test_status_strings(L):
               BL_ERR_HIP, BL_ERR_COUNT):
         assert L.bitlinear_status_string(s)
     assert L.bitlinear_status_string(12345) == b"unknown status"
-    assert L.bitlinear_abi_version() == 100
+    assert L.bitlinear_abi_version() == 101
 
 
 def test_quantize_weights_validation(L):
@@ -98,6 +98,44 @@ def test_grouped_count_validation(L, bl):
     assert L.bitlinear_forward_grouped(ctypes.addressof(fa), 0, None) == BL_ERR_COUNT
     aa = (bl._ActProblem * 1)()
     assert L.bitlinear_quantize_acts_grouped(ctypes.addressof(aa), 17, None) == BL_ERR_COUNT
+
+
+def test_forward_mixed_validation(L, bl):
+    """Counts, NULL arrays and each problem's own checks; every case is rejected on the host
+    (or is all empty), so nothing is launched."""
+    m = L.bitlinear_forward_mixed
+    pre = (bl._ForwardExProblem * 2)()
+    pre[0] = bl._ForwardExProblem(A, B, C, D, E, None, None, 300, 64, 256)
+    dec = (bl._LinearProblem * 2)()
+    dec[0] = bl._LinearProblem(A, None, B, C, D, None, None, 1, 64, 256, 0, 1e-6)
+    pa, da = ctypes.addressof(pre), ctypes.addressof(dec)
+    assert m(pa, 0, da, 0, None) == BL_ERR_COUNT
+    assert m(pa, -1, da, 1, None) == BL_ERR_COUNT
+    assert m(pa, 1, da, -1, None) == BL_ERR_COUNT
+    assert m(pa, 17, da, 1, None) == BL_ERR_COUNT
+    assert m(pa, 1, da, 17, None) == BL_ERR_COUNT
+    assert m(None, 1, da, 1, None) == BL_ERR_NULL
+    assert m(pa, 1, None, 1, None) == BL_ERR_NULL
+    # Problem errors on either side.
+    pre[0].K = 250
+    assert m(pa, 1, da, 1, None) == BL_ERR_SHAPE
+    pre[0].K = 256
+    pre[0].residual = 0x60002
+    assert m(pa, 1, da, 1, None) == BL_ERR_ALIGN
+    pre[0].residual = None
+    dec[0].x_dtype = 5
+    assert m(pa, 1, da, 1, None) == BL_ERR_DTYPE
+    dec[0].x_dtype = 0
+    dec[0].W_packed = None
+    assert m(pa, 1, da, 1, None) == BL_ERR_NULL
+    dec[0].W_packed = B
+    dec[1] = bl._LinearProblem(A, None, B, C, D, None, None, 8, 64, 256, 0, 1e-6)
+    assert m(pa, 1, da, 2, None) == BL_ERR_NULL     # past the fused size: needs X_q, x_scale
+    # All-empty sets are accepted and launch nothing.
+    pre[0].M = 0
+    dec[0].N = 0
+    assert m(pa, 1, da, 1, None) == BL_OK
+    assert m(None, 0, da, 1, None) == BL_OK
 
 
 def test_pack_codes_validation(L):
