@@ -289,11 +289,13 @@ class Setup:
 
         mark("t0")
         if self.wq_tables:
-            rc = L.bitlinear_quantize_weights_grouped(self._addr(self.wq_tables[rp]), n, self.ws_ptr,
-                                                       self.ws_bytes, stream)
-            assert rc == 0, rc
-        mark("t_wq")
-        rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[rp]), n, stream)
+            # Weight quantization and the prefill activations' quantization in one call: the
+            # gamma pass and the activation codes share a launch, the pack pass follows.
+            rc = L.bitlinear_quantize_step(self._addr(self.wq_tables[rp]), n, self.ws_ptr,
+                                           self.ws_bytes, self._addr(self.aq_pre_tables[rp]), n,
+                                           stream)
+        else:
+            rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[rp]), n, stream)
         assert rc == 0, rc
         mark("t_aq")
         # The prefill products and the decode leg in one launch (a mixed batch): the decode
@@ -309,6 +311,10 @@ class Setup:
         n = self.count
         if key == "prefill_gemm":
             rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+        elif key == "weight_and_act_quant":
+            rc = L.bitlinear_quantize_step(self._addr(self.wq_tables[i % self.R_pre]), n, self.ws_ptr,
+                                           self.ws_bytes, self._addr(self.aq_pre_tables[i % self.R_pre]),
+                                           n, stream)
         elif key == "prefill_and_decode":
             rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
                                            self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
@@ -363,6 +369,7 @@ KERNELS = {
     "decode_kernel": ("decode_linear", "decode.hip+decode_core.hpp"),
     "act_quant": ("act_quant_prefill", "quant.hip"),
     "gamma_partial_kernel": ("weight_quant", "quant.hip"),
+    "gamma_act_kernel": ("gamma_and_act_quant", "quant.hip"),
     "quant_pack_kernel": ("weight_quant", "quant.hip"),
 }
 
@@ -771,16 +778,14 @@ def main():
         setup.step(args.warmup + args.steps + i, sptr, ev)
     torch.cuda.synchronize()
     in_step = {
-        "weight_quant": interval_ms(ev, "t0", "t_wq"),
-        "act_quant_prefill": interval_ms(ev, "t_wq", "t_aq"),
+        ("weight_and_act_quant" if setup.wq_tables else "act_quant_prefill"): interval_ms(ev, "t0", "t_aq"),
         "prefill_and_decode": interval_ms(ev, "t_aq", "t_mix"),
     }
-    if not setup.wq_tables:
-        in_step.pop("weight_quant")
     ms_with_events = interval_ms(ev, "t0", "t_mix")
     # Isolated launches: the step's own, plus the product and the decode leg each alone.
     ms = {k: isolated_ms(torch, setup, k, args.steps)
-          for k in list(in_step) + ["prefill_gemm", "decode_linear"]}
+          for k in set(in_step) | {"prefill_gemm", "decode_linear", "act_quant_prefill"} |
+          ({"weight_quant"} if setup.wq_tables else set())}
     ms_b3 = isolated_ms(torch, setup, "decode_linear_b3", args.steps)
     peaks = measured_peaks(torch, bl)
 
@@ -834,17 +839,22 @@ def main():
         mix_bytes, "prefill_and_decode",
         f"{mix_bytes} bytes (the prefill products' {pre_bytes} and the decode leg's {dec_bytes}, "
         f"one launch); {ops} int8 ops; {ops / mix_bytes:.0f} ops/B vs ridge {ridge:.0f}")
+    if "weight_and_act_quant" in ms:
+        wa_bytes = wq_bytes + aq_bytes
+        rooflines["weight_and_act_quant"] = hbm(
+            wa_bytes, "weight_and_act_quant",
+            f"{wa_bytes} bytes (the weight quantization's {wq_bytes} and the activation "
+            f"quantization's {aq_bytes}; two launches: gamma pass + activation codes, then the pack pass)")
     if "weight_quant" in ms:
         rooflines["weight_quant"] = hbm(wq_bytes, "weight_quant",
                                         f"{wq_bytes} bytes (4 N K + N K / 4 + 4 summed; one read "
                                         "of W is the minimum, the two launches read it twice)")
-    # Dominant kernel = largest share of the step.  Where the mixed call could not share one
-    # launch (products on 256 x 256 tiles), its interval is the product's launch followed by
-    # the decode leg's, and the product is the kernel that dominates it.
+    # Dominant kernel = the step's largest single launch: the products' launch (with the decode
+    # blocks when the mixed call shares one launch; the product alone where it cannot, with
+    # 256 x 256 tiles).  The quantization call is two launches (gamma + activation codes, then
+    # the pack pass), each shorter.
     fused = setup.mixed_one_launch()
-    dom = max(in_step, key=lambda k: in_step[k])
-    if dom == "prefill_and_decode" and not fused:
-        dom = "prefill_gemm"
+    dom = "prefill_and_decode" if fused else "prefill_gemm"
     traffic = load_traffic()
     t = traffic.get((dom, wl.key))
     roof = dict(rooflines[dom])
@@ -885,6 +895,7 @@ def main():
                     "us_weight_quant": round(ms["weight_quant"] * 1e3, 3) if "weight_quant" in ms else None,
                     "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3),
                     "us_prefill_and_decode": round(ms["prefill_and_decode"] * 1e3, 3),
+                    "us_weight_and_act_quant": round(ms["weight_and_act_quant"] * 1e3, 3) if "weight_and_act_quant" in ms else None,
                     "us_prefill_plus_decode_separate": round((ms["prefill_gemm"] + ms["decode_linear"]) * 1e3, 3)},
         "roofline": roof,
         "measured_peaks": peaks,

@@ -163,6 +163,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_ex_grouped.restype = ctypes.c_int
     L.bitlinear_forward_mixed.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P]
     L.bitlinear_forward_mixed.restype = ctypes.c_int
+    L.bitlinear_quantize_step.argtypes = [P, ctypes.c_int, P, ctypes.c_size_t, P, ctypes.c_int, P]
+    L.bitlinear_quantize_step.restype = ctypes.c_int
     L.bitlinear_linear_ex_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_ex_grouped.restype = ctypes.c_int
     for fn in ("bitlinear_forward_wonly_grouped", "bitlinear_grad_input_grouped",
@@ -327,6 +329,48 @@ def quantize_acts_grouped(Xs: Sequence[torch.Tensor],
     _check("bitlinear_quantize_acts_grouped",
            lib().bitlinear_quantize_acts_grouped(ctypes.addressof(arr), count, _stream(stream)))
     return outs
+
+
+def quantize_step(Ws: Sequence[torch.Tensor], Xs: Sequence[torch.Tensor],
+                  norm_weights: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                  eps: float = 1e-6, w_outputs=None, x_outputs=None, workspace=None, stream=None):
+    """Weight quantization of Ws and activation quantization of Xs in one call (the gamma pass
+    and the activation codes share a launch when they can); returns ([(W_packed, gamma)],
+    [(X_q, x_scale)]), bit for bit those of the two grouped calls."""
+    nw, na = len(Ws), len(Xs)
+    wa = (_WeightProblem * max(nw, 1))()
+    wouts = []
+    for i, W in enumerate(Ws):
+        _dev(W, f"W[{i}]", torch.float32)
+        N, K = W.shape
+        if w_outputs is not None:
+            P, g = w_outputs[i]
+        else:
+            P = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
+            g = torch.empty(1, dtype=torch.float32, device=W.device)
+        wouts.append((P, g))
+        wa[i] = _WeightProblem(_ptr(W), _ptr(P), _ptr(g), N, K)
+    xa = (_ActProblem * max(na, 1))()
+    xouts = []
+    for i, X in enumerate(Xs):
+        _dev(X, f"X[{i}]")
+        M, K = X.shape
+        g = None if norm_weights is None else norm_weights[i]
+        if x_outputs is not None:
+            Xq, sx = x_outputs[i]
+        else:
+            Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+            sx = torch.empty(M, dtype=torch.float32, device=X.device)
+        xouts.append((Xq, sx))
+        xa[i] = _ActProblem(_ptr(X), _ptr(g), _ptr(Xq), _ptr(sx), M, K, _x_dtype(X), float(eps))
+    ws_bytes = quantize_weights_workspace_bytes(max(nw, 1))
+    if workspace is None and nw:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
+    _check("bitlinear_quantize_step",
+           lib().bitlinear_quantize_step(ctypes.addressof(wa), nw, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                         ctypes.addressof(xa), na, _stream(stream)))
+    return wouts, xouts
 
 
 def forward(X_q: torch.Tensor, x_scale: torch.Tensor, W_packed: torch.Tensor,

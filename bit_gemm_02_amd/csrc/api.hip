@@ -301,7 +301,7 @@ const char *bitlinear_status_string(int status)
     }
 }
 
-int bitlinear_abi_version(void) { return 101; }
+int bitlinear_abi_version(void) { return 102; }
 
 size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
 {
@@ -379,6 +379,43 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int co
         ex[i] = to_ex(problems[i]);
     }
     return run_acts(ex, count, stream);
+}
+
+bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void *workspace,
+                                  size_t workspace_bytes, const bl_act_problem *acts, int na,
+                                  void *stream)
+{
+    if (nw < 0 || na < 0 || nw > BL_MAX_GROUP || na > BL_MAX_GROUP || nw + na == 0)
+        return BL_ERR_COUNT;
+    if ((nw && !weights) || (na && !acts))
+        return BL_ERR_NULL;
+    // Every problem is validated before anything is launched.
+    for (int i = 0; i < nw; ++i) {
+        bl_status s = check_weight(weights[i]);
+        if (s != BL_OK)
+            return s;
+    }
+    bl_act_ex_problem ex[BL_MAX_GROUP];
+    int64_t rows = 0;
+    for (int i = 0; i < na; ++i) {
+        bl_status s = check_act(acts[i]);
+        if (s != BL_OK)
+            return s;
+        ex[i] = to_ex(acts[i]);
+        rows += acts[i].M;
+    }
+    if (rows > INT_MAX)
+        return BL_ERR_SHAPE;
+    if (nw) {
+        if (!workspace)
+            return BL_ERR_NULL;
+        if (!aligned16(workspace))
+            return BL_ERR_ALIGN;
+        if (workspace_bytes < bl::quantize_weights_workspace(nw))
+            return BL_ERR_WORKSPACE;
+    }
+    return from_hip(bl::launch_quantize_step(weights, nw, workspace, ex, na,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 bl_status bitlinear_quantize_acts_ex_grouped(const bl_act_ex_problem *problems, int count,

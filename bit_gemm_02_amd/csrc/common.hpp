@@ -304,6 +304,10 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipS
 // BL_LINEAR_FUSED_MAX_BYTES.
 hipError_t launch_linear_decode(const bl_linear_ex_problem *p, int count, hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
+// Weight quantization + activation quantization of one step (γ pass and activation codes in
+// one launch when every activation problem takes the wave kernel with one dtype).
+hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
+                                const bl_act_ex_problem *aq, int na, hipStream_t stream);
 // Mixed batch (prefill products + fused decode calls) in one launch: eligible when every
 // prefill product has M > 16 and takes the 128 x 128 tile, and every decode call is a fused
 // single projection (no pair, activation or residual) with one activation dtype.

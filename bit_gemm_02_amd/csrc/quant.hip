@@ -59,15 +59,15 @@ static int gamma_parts(int64_t chunks)
     return (int)(parts < 1 ? 1 : parts > kGammaParts ? kGammaParts : parts);
 }
 
-__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(WeightBatch b)
+__device__ __forceinline__ void gamma_partial_block(const WeightBatch &b, int bid)
 {
     __shared__ double lds[kGammaThreads / kWave];
     int prob = 0;
 #pragma unroll 1
-    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].part_begin)
+    while (prob + 1 < b.count && bid >= b.p[prob + 1].part_begin)
         ++prob;
     const WeightDev &p = b.p[prob];
-    const int part = blockIdx.x - p.part_begin;
+    const int part = bid - p.part_begin;
     const int64_t stride = (int64_t)p.parts * kGammaThreads;
     double s = 0.0;
     int64_t i = (int64_t)part * kGammaThreads + threadIdx.x;
@@ -152,6 +152,11 @@ __device__ __forceinline__ uint32_t quad_or(uint32_t v)
     return v;
 }
 
+__global__ __launch_bounds__(kGammaThreads) void gamma_partial_kernel(WeightBatch b)
+{
+    gamma_partial_block(b, blockIdx.x);
+}
+
 __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
 {
     int prob = 0;
@@ -234,37 +239,47 @@ static int64_t group_bytes()
     return v;
 }
 
+// Tensors i0 .. (returned end) - 1 of one launch pair: the γ-pass blocks (parts) and the pack
+// pass blocks (blocks).
+static int build_weight_batch(const bl_weight_problem *q, int i0, int count, void *workspace,
+                              WeightBatch &b, int &parts, int &blocks)
+{
+    parts = 0;
+    blocks = 0;
+    int64_t bytes = 0;
+    int i = i0;
+    for (; i < count; ++i) {
+        const int64_t tb = q[i].N * q[i].K * 4;
+        if (i > i0 && bytes + tb > group_bytes())
+            break;
+        bytes += tb;
+        WeightDev &d = b.p[b.count++];
+        d.W = reinterpret_cast<const float4 *>(q[i].W);
+        d.packed = q[i].W_packed;
+        d.gamma = q[i].gamma;
+        d.partials = static_cast<double *>(workspace) + (size_t)i * kGammaParts;
+        d.chunks = q[i].N * q[i].K / 4;
+        d.parts = gamma_parts(d.chunks);
+        d.part_begin = parts;
+        parts += d.parts;
+        const int64_t per_block = (int64_t)kPackThreads * kPackUnroll;
+        int pb = (int)((d.chunks + per_block - 1) / per_block);
+        if (pb == 0)
+            pb = 1;  // still writes gamma (= 0 for an empty tensor)
+        d.pack_begin = blocks;
+        blocks += pb;
+    }
+    return i;
+}
+
 hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
                                    hipStream_t stream)
 {
     int i0 = 0;
     while (i0 < count) {
         WeightBatch b{};
-        int parts = 0, blocks = 0;
-        int64_t bytes = 0;
-        int i = i0;
-        for (; i < count; ++i) {
-            const int64_t tb = q[i].N * q[i].K * 4;
-            if (i > i0 && bytes + tb > group_bytes())
-                break;
-            bytes += tb;
-            WeightDev &d = b.p[b.count++];
-            d.W = reinterpret_cast<const float4 *>(q[i].W);
-            d.packed = q[i].W_packed;
-            d.gamma = q[i].gamma;
-            d.partials = static_cast<double *>(workspace) + (size_t)i * kGammaParts;
-            d.chunks = q[i].N * q[i].K / 4;
-            d.parts = gamma_parts(d.chunks);
-            d.part_begin = parts;
-            parts += d.parts;
-            const int64_t per_block = (int64_t)kPackThreads * kPackUnroll;
-            int pb = (int)((d.chunks + per_block - 1) / per_block);
-            if (pb == 0)
-                pb = 1;  // still writes gamma (= 0 for an empty tensor)
-            d.pack_begin = blocks;
-            blocks += pb;
-        }
-        i0 = i;
+        int parts, blocks;
+        i0 = build_weight_batch(q, i0, count, workspace, b, parts, blocks);
         hipLaunchKernelGGL(gamma_partial_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -472,13 +487,12 @@ __device__ __forceinline__ void act_quant_row(const RowBuf<CACHE, BF16> &r, cons
 }
 
 template <int CACHE, bool BF16>
-__global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
+__device__ __forceinline__ void act_wave_block(const ActBatch &b, int rows, int bid)
 {
     const int lane = threadIdx.x & (kWave - 1);
     // Wave-uniform row index (readfirstlane keeps the problem lookup and the buffer
     // descriptors in scalar registers; otherwise every load is wrapped in a per-lane loop).
-    const int r = blockIdx.x * (kActThreads / kWave) +
-                  __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int r = bid * (kActThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (r >= rows)
         return;
     RowBuf<CACHE, BF16> A;
@@ -487,6 +501,28 @@ __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b,
     act_load(A, act_row_rsrc(b, r, rows, pa), lane);
     norm_load<CACHE, BF16>(G, b.p[pa], lane);
     act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
+}
+
+template <int CACHE, bool BF16>
+__global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
+{
+    act_wave_block<CACHE, BF16>(b, rows, blockIdx.x);
+}
+
+// The γ partial sums of a weight set and the activation quantization of an input set in one
+// grid: the two are independent (γ needs only W, the codes only X), so their blocks share a
+// launch, γ blocks first; the pack pass follows as its own launch.  Each block runs exactly the
+// code of its own kernel.
+static_assert(kGammaThreads == kActThreads, "one block size for both kinds of block");
+template <int CACHE, bool BF16>
+__global__ __launch_bounds__(kActThreads) void gamma_act_kernel(WeightBatch wb, int gblocks, ActBatch ab,
+                                                               int rows)
+{
+    const int bid = blockIdx.x;
+    if (bid < gblocks)
+        gamma_partial_block(wb, bid);
+    else
+        act_wave_block<CACHE, BF16>(ab, rows, bid - gblocks);
 }
 
 // One block per token row for rows longer than the largest wave class.  Thread t handles the
@@ -706,6 +742,80 @@ static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
     const int per_block = kActThreads / kWave;
     hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16>), dim3((rows + per_block - 1) / per_block),
                        dim3(kActThreads), 0, stream, b, rows);
+}
+
+// Weight quantization and activation quantization of one step: the γ pass and the activation
+// codes in one launch (gamma_act_kernel), then the pack pass.  Taken when every non-empty
+// activation problem fits the wave kernel (K <= 4096, no FFN activation) with one dtype and
+// the weights form one launch pair; otherwise the two calls' own launches.
+hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
+                                const bl_act_ex_problem *aq, int na, hipStream_t stream)
+{
+    int order[BL_MAX_GROUP];
+    int n = 0, bf = -1;
+    bool ok = nw > 0;
+    for (int i = 0; i < na && ok; ++i) {
+        if (aq[i].M == 0)
+            continue;
+        const int cpl = (int)((aq[i].K / 4 + kWave - 1) / kWave);
+        const int dt = aq[i].x_dtype == BL_BF16 ? 1 : 0;
+        ok = aq[i].act == BL_ACT_NONE && cpl <= kActClasses[kActNumClasses - 1] && (bf < 0 || bf == dt);
+        bf = dt;
+        order[n++] = i;
+    }
+    WeightBatch wb{};
+    int parts = 0, blocks = 0;
+    ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks) == nw;
+    if (!ok) {
+        const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream);
+        return e == hipSuccess ? launch_quantize_acts(aq, na, stream) : e;
+    }
+    // Longest rows first, as in the activation launch (the row-to-block map changes nothing
+    // in the results: every row is quantized on its own).
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && aq[order[j]].K > aq[order[j - 1]].K; --j) {
+            const int t = order[j];
+            order[j] = order[j - 1];
+            order[j - 1] = t;
+        }
+    ActBatch ab{};
+    int rows = 0, cls = 0;
+    for (int i = 0; i < n; ++i) {
+        const bl_act_ex_problem &s = aq[order[i]];
+        const int cpl = (int)((s.K / 4 + kWave - 1) / kWave);
+        int c = 0;
+        while (cpl > kActClasses[c])
+            ++c;
+        cls = std::max(cls, c);
+        ActDev &d = ab.p[ab.count++];
+        d.X = s.X;
+        d.g = s.norm_weight;
+        d.Xq = s.X_q;
+        d.sx = s.x_scale;
+        d.M = (int)s.M;
+        d.K = (int)s.K;
+        d.bf16 = bf;
+        d.eps = s.eps;
+        d.row_begin = rows;
+        d.x2 = nullptr;
+        d.act = BL_ACT_NONE;
+        rows += d.M;
+    }
+    const dim3 grid((unsigned)(parts + (rows + kActThreads / kWave - 1) / (kActThreads / kWave)));
+    if (bf) {
+        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        else hipLaunchKernelGGL((gamma_act_kernel<16, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+    } else {
+        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        else hipLaunchKernelGGL((gamma_act_kernel<16, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(quant_pack_kernel, dim3(blocks), dim3(kPackThreads), 0, stream, wb);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream_t stream)

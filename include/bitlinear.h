@@ -164,6 +164,34 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int co
                                           void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Steps 1 + 2 and step 3 of one forward step in one call: a weight set's quantization and an
+ * input set's activation quantization.
+ *
+ * Distillix README, "1. BitNet b1.58 Core", and bitone README, "Features": a training-style
+ * step re-quantizes the weights (gamma, then the codes) and quantizes the step's activations;
+ * the two depend on different inputs (W, X), so the gamma reduction and the activation codes
+ * can run side by side.
+ *
+ *   weights, nw, workspace, workspace_bytes   as for bitlinear_quantize_weights_grouped
+ *                   (0 <= nw <= BL_MAX_GROUP; weights may be NULL and the workspace is not
+ *                   needed when nw == 0).
+ *   acts, na        as for bitlinear_quantize_acts_grouped (0 <= na <= BL_MAX_GROUP; may be
+ *                   NULL when na == 0).
+ * Results: bit for bit those of the two grouped calls.  When every non-empty activation
+ * problem has K <= 4096 and one dtype, the gamma pass and the activation quantization share
+ * one launch and the pack pass follows (two launches instead of three); otherwise the two
+ * calls run in order.  The two sets run concurrently: no buffer one set writes may be read or
+ * written by the other.
+ * Errors: BL_ERR_COUNT (nw or na outside 0 .. BL_MAX_GROUP, or both 0), BL_ERR_NULL (a NULL
+ * array with a nonzero count, or no workspace with nw > 0), then each problem's errors as for
+ * the two calls, BL_ERR_ALIGN / BL_ERR_WORKSPACE for the workspace, and BL_ERR_SHAPE when the
+ * activation rows exceed 2^31 - 1.  Every problem is validated before anything is launched.
+ * ------------------------------------------------------------------------------------- */
+bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void *workspace,
+                                  size_t workspace_bytes, const bl_act_problem *acts, int na,
+                                  void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * Steps 4 + 5: ternary x int8 product with int32 accumulation and the rescale epilogue.
  *
  * bitone README, "Features": Y = X @ W_q^T x gamma, weights [out, in] (nn.Linear layout);

@@ -64,7 +64,7 @@ def test_status_strings(L):
               BL_ERR_HIP, BL_ERR_COUNT):
         assert L.bitlinear_status_string(s)
     assert L.bitlinear_status_string(12345) == b"unknown status"
-    assert L.bitlinear_abi_version() == 101
+    assert L.bitlinear_abi_version() == 102
 
 
 def test_quantize_weights_validation(L):
@@ -136,6 +136,38 @@ def test_forward_mixed_validation(L, bl):
     dec[0].N = 0
     assert m(pa, 1, da, 1, None) == BL_OK
     assert m(None, 0, da, 1, None) == BL_OK
+
+
+def test_quantize_step_validation(L, bl):
+    """Counts, NULL arrays, workspace and each problem's checks, all on the host."""
+    q = L.bitlinear_quantize_step
+    w = (bl._WeightProblem * 2)()
+    w[0] = bl._WeightProblem(A, B, C, 4, 64)
+    a = (bl._ActProblem * 2)()
+    a[0] = bl._ActProblem(A, None, B, C, 2, 64, 0, 1e-6)
+    wa, aa = ctypes.addressof(w), ctypes.addressof(a)
+    ws = L.bitlinear_quantize_weights_grouped_workspace(1)
+    assert q(wa, 0, D, ws, aa, 0, None) == BL_ERR_COUNT
+    assert q(wa, -1, D, ws, aa, 1, None) == BL_ERR_COUNT
+    assert q(wa, 17, D, ws, aa, 1, None) == BL_ERR_COUNT
+    assert q(wa, 1, D, ws, aa, 17, None) == BL_ERR_COUNT
+    assert q(None, 1, D, ws, aa, 1, None) == BL_ERR_NULL
+    assert q(wa, 1, D, ws, None, 1, None) == BL_ERR_NULL
+    assert q(wa, 1, None, ws, aa, 1, None) == BL_ERR_NULL
+    assert q(wa, 1, D + 8, ws, aa, 1, None) == BL_ERR_ALIGN
+    assert q(wa, 1, D, ws - 1, aa, 1, None) == BL_ERR_WORKSPACE
+    w[0].K = 40
+    assert q(wa, 1, D, ws, aa, 1, None) == BL_ERR_SHAPE
+    w[0].K = 64
+    a[0].x_dtype = 3
+    assert q(wa, 1, D, ws, aa, 1, None) == BL_ERR_DTYPE
+    a[0].x_dtype = 0
+    a[0].X_q = B + 1
+    assert q(wa, 1, D, ws, aa, 1, None) == BL_ERR_ALIGN
+    # Activations only: no workspace needed; empty problems launch nothing.
+    a[0].X_q = B
+    a[0].M = 0
+    assert q(None, 0, None, 0, aa, 1, None) == BL_OK
 
 
 def test_pack_codes_validation(L):
