@@ -10,11 +10,13 @@ import os
 import subprocess
 import sys
 import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.hip", "quant.hip", "decode.hip", "prefill.hip", "mixed.hip", "train.hip", "calib.hip"]
+SOURCES = ["api.hip", "quant.hip", "decode.hip", "gemv.hip", "prefill.hip", "mixed.hip", "train.hip",
+           "calib.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -37,16 +39,21 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     with tempfile.TemporaryDirectory(prefix="bitlinear_build_") as tmp:
-        objs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+        objs = [os.path.join(tmp, src.replace(".hip", ".o")) for src in SOURCES]
+
+        def compile_one(src_obj):
+            src, obj = src_obj
             cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            r = subprocess.run(cmd, capture_output=True, text=True)
-            if r.returncode != 0:
-                raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-            objs.append(obj)
+            return src, subprocess.run(cmd, capture_output=True, text=True)
+
+        # One hipcc process per source, several at a time (each is single-threaded).
+        jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for src, r in pool.map(compile_one, zip(SOURCES, objs)):
+                if r.returncode != 0:
+                    raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         tmp_lib = LIBRARY + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -62,6 +62,69 @@ __device__ __forceinline__ int xcd_order(int b, int nb)
     return xcd < r ? xcd * (q + 1) + i : r * (q + 1) + (xcd - r) * q + i;
 }
 
+// ----------------------------------------------------------------- direct-to-LDS loads
+
+// Raw buffer descriptor as four scalar dwords: base address, stride 0, size in bytes, and
+// the gfx9-family raw-access word.  Offsets at or past `bytes` read zero.
+__device__ __forceinline__ v4i make_desc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    v4i d;
+    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    d.w = 0x00020000;
+    return d;
+}
+
+// LDS byte address of a shared-memory pointer, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
+{
+    typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_uchar *)p);
+}
+
+// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at LDS address
+// lds + 16 * l; an out-of-range offset writes zeros.  Issued from inline assembly so that the
+// compiler does not model it: modelled, it cannot tell buffers in flight apart and drains
+// every load before the first LDS read that follows.  The instruction has no register
+// result; its completion is ordered by the caller's explicit vmcnt waits and barriers, and
+// the "memory" clobber keeps LDS accesses from moving across it.  (The compiler's own waits
+// stay correct: they count only the loads it knows of, and waiting for a later load also
+// waits for every earlier one, these included.)
+__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, uint32_t offset)
+{
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "s_nop 0\n\t"
+                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(offset), "s"(desc)
+                 : "memory", "m0");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations (the barrier
+// instruction alone does not stop the compiler from moving LDS accesses across it), without
+// the waits a memory fence would add.
+__device__ __forceinline__ void block_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): wait until at most N vector-memory loads of this wave
+// (direct-to-LDS ones included) are still in flight and every LDS read of this wave has
+// returned.  The second part matters before a barrier that hands an LDS buffer back to
+// the loads: a read of the buffer about to be refilled may have been issued before the
+// barrier and not yet returned, and it could still be queued behind other LDS traffic when
+// another wave's refill lands (a bare s_barrier does not wait for LDS reads).
+template <int N>
+__device__ __forceinline__ void wait_stage()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
 // ----------------------------------------------------------------- packed-code planes
 //
 // A packed word holds 16 codes; the code of weight k = 16w + 4i + b lives at bits
@@ -303,6 +366,15 @@ hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipS
 // Fused decode form: every problem has M <= BL_LINEAR_FUSED_MAX_M and M * K within
 // BL_LINEAR_FUSED_MAX_BYTES.
 hipError_t launch_linear_decode(const bl_linear_ex_problem *p, int count, hipStream_t stream);
+// One-token form of the fused decode call (gemv.hip): every problem has M == 1; one kind per
+// launch (single projections or gated pairs, one activation dtype); gemv_fits says whether the
+// problems' rows fit its LDS budget.
+bool gemv_fits(const bl_linear_ex_problem *const *p, int count, bool bf16, bool b3);
+hipError_t launch_gemv(const bl_linear_ex_problem *const *p, int count, bool pair, bool bf16,
+                       hipStream_t stream);
+// The same on base-3 rows (single projections; W_packed holds bitlinear_pack_b3's rows).
+hipError_t launch_gemv_b3(const bl_linear_ex_problem *const *p, int count, bool bf16,
+                          hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 // Weight quantization + activation quantization of one step (γ pass and activation codes in
 // one launch when every activation problem takes the wave kernel with one dtype).

@@ -125,6 +125,11 @@ static hipError_t launch_linear_kind(const bl_linear_ex_problem *const *q, int n
 {
     if (n == 0)
         return hipSuccess;
+    bool one_token = true;
+    for (int i = 0; i < n; ++i)
+        one_token = one_token && q[i]->M == 1;
+    if (one_token && gemv_fits(q, n, BF16, false))
+        return launch_gemv(q, n, PAIR, BF16, stream);
     if (wrows >= 256 * 64)
         return launch_linear_rg<4, PAIR, BF16>(q, n, stream);
     if constexpr (PAIR) {
@@ -167,6 +172,11 @@ static hipError_t launch_b3_kind(const bl_linear_ex_problem *const *q, int n, in
 {
     if (n == 0)
         return hipSuccess;
+    bool one_token = true;
+    for (int i = 0; i < n; ++i)
+        one_token = one_token && q[i]->M == 1;
+    if (one_token && gemv_fits(q, n, BF16, true))
+        return launch_gemv_b3(q, n, BF16, stream);
     if (rows >= 256 * 64)
         return launch_linear_rg<4, false, BF16, true>(q, n, stream);
     if (rows >= 256 * 32)

@@ -289,36 +289,58 @@ __device__ __forceinline__ void decode_block(const FwdBatch &b, int bid)
         return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                            __uint_as_float(v.w));
     };
-    // One token whose piece takes up to kDecCQ quads per lane: every activation (and norm
-    // weight) load is issued before the weight loads, so the quantization does not wait
-    // behind the weight stream (loads complete in issue order), and u stays in registers for
-    // the quantization pass (the same per-lane order of the sums: quads past the piece read
-    // as zeros and add nothing).  The loads land in raw registers and are converted only
-    // after the weight loads are out: a use next to a load makes the wave wait for it, which
-    // would serialize the loads.  Otherwise four quads per lane at a time after the weight
-    // loads, re-read for the quantization pass.
-    const bool cached = QUANT && p.M == 1 && quads <= kDecCQ * kWave;
-    float4 xc[kDecCQ], uc[kDecCQ];
-    v4u rx[kDecCQ], rgw[kDecCQ];
+    // One token whose row takes up to kDecCQ quads per thread: the row is quantized block-wide
+    // in 16-byte chunks (4 fp32 or 8 bf16 values; thread t takes chunks t, t + 256, ...), in
+    // the same order as the one-token call (gemv.hip) — per thread over its chunks, then
+    // across lanes and across waves in a fixed order — so the two give the same scale bit for
+    // bit.  Every activation (and norm weight) load is issued before the weight loads, so the
+    // quantization does not wait behind the weight stream (loads complete in issue order), and
+    // the loads land in raw registers that are converted only after the weight loads are out
+    // (a use next to a load makes the wave wait for it, which would serialize the loads).
+    // Otherwise each wave quantizes its own piece of every token row, four quads per lane at a
+    // time after the weight loads, re-read for the quantization pass.
+    constexpr int QPC = BF16 ? 2 : 1;                 // quads per chunk
+    constexpr int CH = kDecCQ / QPC;                  // chunks per thread kept in registers
+    const int nchunk = p.K * (BF16 ? 2 : 4) / 16;
+    const bool cached = QUANT && p.M == 1 && nchunk <= CH * kDecThreads;
+    v4u rx[CH], rgw[kDecCQ];
     if (cached) {
         const rsrc_t xr = row(0);
 #pragma unroll
-        for (int c = 0; c < kDecCQ; ++c) {
-            const int q = lane + c * kWave;
-            const int j = q < quads ? e0 / 4 + q : (int)(kOOB / 16u);   // past: zeros
-            rx[c] = rgw[c] = v4u{0, 0, 0, 0};
-            if (c * kWave < quads) {       // wave-uniform: no loads past the piece
-                if (bf16) {
-                    rx[c].x = buf_load4(xr, (uint32_t)j * 8u);
-                    rx[c].y = buf_load4(xr, (uint32_t)j * 8u + 4u);
-                } else {
-                    rx[c] = buf_load16(xr, (uint32_t)j * 16u);
+        for (int c = 0; c < CH; ++c) {
+            const int i = (int)threadIdx.x + c * kDecThreads;
+            rx[c] = v4u{0, 0, 0, 0};
+#pragma unroll
+            for (int h = 0; h < QPC; ++h)
+                rgw[QPC * c + h] = v4u{0, 0, 0, 0};
+            if (c * kDecThreads < nchunk) {      // block-uniform: no loads past the row
+                rx[c] = buf_load16(xr, i < nchunk ? 16u * (uint32_t)i : kOOB);
+                if (norm) {
+#pragma unroll
+                    for (int h = 0; h < QPC; ++h)
+                        rgw[QPC * c + h] = buf_load16(gr, i < nchunk ? 16u * (uint32_t)(QPC * i + h) : kOOB);
                 }
-                if (norm)
-                    rgw[c] = buf_load16(gr, (uint32_t)j * 16u);
             }
         }
     }
+    // Chunk c of the cached row as QPC quads of fp32 values.
+    auto chunk_quads = [&](int c, float4 *x) {
+        const v4u v = rx[c];
+        if (BF16) {
+            x[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+            x[QPC - 1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                                     __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
+        } else {
+            x[0] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                               __uint_as_float(v.w));
+        }
+    };
+    auto g_quad = [&](int c, int h) {
+        const v4u v = rgw[QPC * c + h];
+        return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                           __uint_as_float(v.w));
+    };
     __builtin_amdgcn_sched_barrier(0);
 
     Chunk c0, c1;
@@ -332,27 +354,21 @@ __device__ __forceinline__ void decode_block(const FwdBatch &b, int bid)
         // Partial absmax of u (u = x, or fl32(x * g)) and sum of x^2 over this wave's piece.
         const bool first = bid == p.block_begin;
         if (cached) {
-#pragma unroll
-            for (int c = 0; c < kDecCQ; ++c) {
-                if (bf16)
-                    xc[c] = make_float4(__uint_as_float(rx[c].x << 16), __uint_as_float(rx[c].x & 0xFFFF0000u),
-                                        __uint_as_float(rx[c].y << 16), __uint_as_float(rx[c].y & 0xFFFF0000u));
-                else
-                    xc[c] = make_float4(__uint_as_float(rx[c].x), __uint_as_float(rx[c].y),
-                                        __uint_as_float(rx[c].z), __uint_as_float(rx[c].w));
-                uc[c] = norm ? make_float4(__uint_as_float(rgw[c].x), __uint_as_float(rgw[c].y),
-                                           __uint_as_float(rgw[c].z), __uint_as_float(rgw[c].w))
-                             : xc[c];
-            }
             float amax = 0.0f;
             double ss = 0.0;
 #pragma unroll
-            for (int c = 0; c < kDecCQ; ++c) {
-                if (norm) {
-                    uc[c] = mul4(xc[c], uc[c]);
-                    ss = sumsq4(ss, xc[c]);
+            for (int c = 0; c < CH; ++c) {
+                if (c * kDecThreads < nchunk) {
+                    float4 x[QPC];
+                    chunk_quads(c, x);
+#pragma unroll
+                    for (int h = 0; h < QPC; ++h) {
+                        const float4 u = norm ? mul4(x[h], g_quad(c, h)) : x[h];
+                        amax = fmaxf(amax, absmax4(u));
+                        if (norm)
+                            ss = sumsq4(ss, x[h]);
+                    }
                 }
-                amax = fmaxf(amax, absmax4(uc[c]));
             }
             amax = wave_max(amax);
             if (norm)
@@ -404,14 +420,19 @@ __device__ __forceinline__ void decode_block(const FwdBatch &b, int bid)
                 a = fmaxf(a, q_amax[w][0]);
             const float inv = a == 0.0f ? 0.0f : 127.0f / a;  // correctly rounded division
 #pragma unroll
-            for (int c = 0; c < kDecCQ; ++c) {
-                const int q = lane + c * kWave;
-                if (q < quads) {
-                    const int j = e0 / 4 + q;
-                    const char4 cq = quant4(uc[c], inv);
-                    *reinterpret_cast<char4 *>(xs + 4u * j) = cq;
-                    if (first && p.Xq_out)
-                        *reinterpret_cast<char4 *>(p.Xq_out + 4 * j) = cq;
+            for (int c = 0; c < CH; ++c) {
+                const int i = (int)threadIdx.x + c * kDecThreads;
+                if (c * kDecThreads < nchunk && i < nchunk) {
+                    float4 x[QPC];
+                    chunk_quads(c, x);
+#pragma unroll
+                    for (int h = 0; h < QPC; ++h) {
+                        const int q = QPC * i + h;
+                        const char4 cq = quant4(norm ? mul4(x[h], g_quad(c, h)) : x[h], inv);
+                        *reinterpret_cast<char4 *>(xs + 4u * q) = cq;
+                        if (first && p.Xq_out)
+                            *reinterpret_cast<char4 *>(p.Xq_out + 4 * q) = cq;
+                    }
                 }
             }
         } else {
@@ -468,8 +489,15 @@ __device__ __forceinline__ void decode_block(const FwdBatch &b, int bid)
         }
         if (lane == 0)
             *reinterpret_cast<v4u *>(xs + zero_off) = v4u{0, 0, 0, 0};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (cached) {
+            // The block-wide form: every wave reads codes other waves wrote.
+            __syncthreads();
+        } else {
+            // Each wave reads only the codes it wrote: LDS operations of one wave complete in
+            // order, so a wave-scope fence (no instruction, no wait) suffices.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     } else if (XLDS) {
         // Copy this wave's piece, rows 0 .. M-1, k in [16 * kw0, 16 * kw1), 16 bytes per lane.
         const int kw0 = t_begin * kSuperWords;

@@ -1,0 +1,446 @@
+// gemv.hip — the one-token decode call: activation quantization and the streaming ternary
+// product of a single token row in one launch.
+//
+// At one token the product reads every packed weight once and does almost no arithmetic per
+// byte, so it is bound by HBM (SLM750-Edge card, "Performance": single-token decode is
+// bandwidth-bound).  A launch over a whole layer set moves only a few tens of MB — a few
+// microseconds at full bandwidth — which is about as long as a handful of memory round trips
+// under load.  A wave that streams its weights in several dependent rounds (issue, wait,
+// multiply, issue the next) therefore finishes well after the rest of the chip, with its
+// later rounds queued behind everybody's first.  This kernel cuts the work so that each wave
+// has one round: a wave owns one group of 16 weight rows (two for a gated pair: the same rows
+// of both projections) over one slice of K, and issues every load of that slice before it
+// uses the first.  Long rows are split into 2 or 4 slices (one per wave of the block, summed
+// through LDS at the end, exactly, in a fixed order) so that every wave moves about the same
+// number of bytes whatever the projection's shape; short rows give each wave of a block its
+// own row group.
+//
+// The token's int8 codes need the absmax of the whole row (BitDistill article: INT8
+// activations; absmax scale per token), so every block quantizes the row itself, with the same
+// arithmetic as the activation-quantization kernels (quant4, act_scale): its 256 threads load
+// the row (and the RMSNorm weight) before any weight load, so those loads, which hit L2 after
+// the first block, come back first; the partial maxima (and sums of squares) meet in LDS in a
+// fixed order, and the codes go to LDS, where the waves read them as the MFMA's activation
+// operand.  All of this runs while the block's weight loads are in flight.
+//
+// Product: v_mfma_i32_16x16x64_i8 with 16 weight rows as the B operand (a lane (r, g) holds
+// words 16t + 4g .. 16t + 4g + 3 of row r, one 16-byte load per super-step t of 256 weights,
+// expanded to 64 * c with one shift and one mask per four weights; see plane64) and the
+// token's codes as the A operand.  Only row 0 of the output is used: every lane reads the
+// token's codes for its k range (lanes of one lane group read the same 16 bytes, a broadcast),
+// so the other 15 rows of the result repeat row 0 and are ignored.
+#include <algorithm>
+
+#include "decode_core.hpp"
+
+namespace bl {
+
+constexpr int kGvThreads = 256;
+constexpr int kGvWaves = kGvThreads / kWave;
+constexpr int kGvLoadsPerWave = 12;  // target 16-byte weight loads per lane per wave (one round)
+constexpr size_t kGvMaxLds = 96 * 1024;  // dynamic LDS per block (raw row, norm weight, codes)
+
+// Dynamic LDS of a launch over these problems: the raw row and the norm weight of the longest
+// problem in whole 1 KB copies, then the codes of its super-steps.
+static void gemv_lds(const bl_linear_ex_problem *const *q, int count, bool bf16, bool b3,
+                     int &g_off, int &c_off, size_t &bytes)
+{
+    int k_max = 16;
+    bool any_norm = false;
+    for (int i = 0; i < count; ++i) {
+        k_max = std::max(k_max, (int)q[i]->K);
+        any_norm = any_norm || q[i]->norm_weight != nullptr;
+    }
+    const int esize = bf16 ? 2 : 4;
+    const int supers = b3 ? ((k_max + 79) / 80 + 3) / 4 : (k_max / 16 + 15) / 16;
+    g_off = (k_max * esize + 1023) / 1024 * 1024;
+    c_off = g_off + (any_norm ? (k_max * 4 + 1023) / 1024 * 1024 : 0);
+    bytes = (size_t)c_off + (size_t)(b3 ? 320 : 256) * supers;
+}
+
+bool gemv_fits(const bl_linear_ex_problem *const *q, int count, bool bf16, bool b3)
+{
+    int g_off, c_off;
+    size_t bytes;
+    gemv_lds(q, count, bf16, b3, g_off, c_off, bytes);
+    return bytes <= kGvMaxLds;
+}
+
+struct GvDev {
+    const void *X;          // [K] fp32 or bf16
+    const float *g;         // [K] RMSNorm weight or NULL
+    const uint32_t *W;      // [N][K/16] packed codes (the gate projection of a pair)
+    const uint32_t *W2;     // pair: the up projection
+    const float *gamma;
+    const float *gamma2;
+    const float *R;         // [N] residual or NULL
+    float *Y;               // [N]
+    int8_t *Xq_out;         // optional copies of the codes and the scale
+    float *sx_out;
+    float eps;
+    int N, K;
+    int ks_log2;            // slices per row group: 1, 2 or 4 (log2)
+    int act;
+    int block_begin;
+};
+
+// LDS of a launch: [0, g_off) the raw activation row of the longest problem, [g_off, c_off)
+// its RMSNorm weight (when a problem has one), [c_off, c_off + 256 * supers) the codes.
+struct GvBatch {
+    GvDev p[BL_MAX_GROUP];
+    int count;
+    int g_off, c_off;
+};
+
+// S: super-steps (16-byte loads per lane and row group) in one round; BF16: activation dtype;
+// PAIR: gated pair (two row groups per wave, the epilogue applies the activation); W4: every
+// row has a multiple of 4 words, so a lane's 16 bytes never straddle the end of a row; B3:
+// base-3 rows (16-byte blocks of 80 weights, see b3_table_entry; a super-step is then 320
+// weights and five MFMAs per row group, the expansion a table lookup in LDS).
+template <int S, bool BF16, bool PAIR, bool W4, bool B3 = false>
+__global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
+{
+    constexpr int G = PAIR ? 2 : 1;
+    static_assert(!B3 || (W4 && !PAIR), "base-3 rows: whole 16-byte blocks, single projections");
+    __shared__ __align__(8) uint32_t b3lut[B3 ? 512 : 2];
+    if (B3) {
+        uint32_t lo, hi;
+        b3_table_entry(threadIdx.x, lo, hi);     // 256 threads, one entry each
+        *reinterpret_cast<v2u *>(b3lut + 2 * threadIdx.x) = v2u{lo, hi};
+    }
+    __shared__ float s_amax[kGvWaves];
+    __shared__ double s_ss[kGvWaves];
+    __shared__ int s_red[kGvWaves][G][16];
+    extern __shared__ __align__(16) unsigned char lds[];
+
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && (int)blockIdx.x >= b.p[prob + 1].block_begin)
+        ++prob;
+    const GvDev &p = b.p[prob];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int r = lane & 15;
+    const int g = lane >> 4;
+    const int ksl = p.ks_log2;
+    const int rg = (((int)blockIdx.x - p.block_begin) << (2 - ksl)) + (wave >> ksl);
+    const int slice = wave & ((1 << ksl) - 1);
+    const int n0 = rg * 16;
+    const int n = n0 + r;                 // output row of lanes 0..15
+    const int K = p.K;
+    const int words = K >> 4;
+    const int nblk = (K + 79) / 80;       // base-3 blocks per row
+    const int row_bytes = B3 ? 16 * nblk : K >> 2;
+    const int supers = B3 ? (nblk + 3) >> 2 : (words + 15) >> 4;
+    const int t_begin = (supers * slice) >> ksl;
+    const int t_end = (supers * (slice + 1)) >> ksl;
+    const bool first = (int)blockIdx.x == p.block_begin;
+    const bool norm = p.g != nullptr;
+    unsigned char *const xraw = lds;
+    unsigned char *const graw = lds + b.g_off;
+    unsigned char *const codes = lds + b.c_off;
+
+    // ---- epilogue inputs first, so the epilogue does not wait on a round trip of its own
+    const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
+    const float gamma2f = PAIR ? __uint_as_float(buf_load4(make_rsrc(p.gamma2, 4u), 0u)) : 0.0f;
+    const bool out_lane = lane < 16 && n < p.N;
+    const float resid = __uint_as_float(
+        buf_load4(make_rsrc(p.R, p.R ? (uint32_t)p.N * 4u : 0u), out_lane ? (uint32_t)n * 4u : kOOB));
+
+    // ---- the activation row (and norm weight) straight into LDS, before any weight load:
+    // loads return in issue order, and these hit L2 after the first block.  Wave w copies
+    // 1 KB chunks w, w + 4, ... (the tail of the last chunk reads as zeros).
+    constexpr int esize = BF16 ? 2 : 4;
+    const int xbytes = K * esize;
+    const v4i xdesc = make_desc(p.X, (uint32_t)xbytes);
+    for (int c = wave; c * 1024 < xbytes; c += kGvWaves)
+        dma16(xdesc, lds_addr(xraw + 1024 * c), (uint32_t)(1024 * c + 16 * lane));
+    if (norm) {
+        const v4i gdesc = make_desc(p.g, (uint32_t)K * 4u);
+        for (int c = wave; c * 1024 < K * 4; c += kGvWaves)
+            dma16(gdesc, lds_addr(graw + 1024 * c), (uint32_t)(1024 * c + 16 * lane));
+    }
+
+    // ---- weight loads: rows n0 .. n0+15 (rows past N read as zero), the first round of
+    // this wave's super-steps [t_begin, t_end)
+    const unsigned char *const wrow = reinterpret_cast<const unsigned char *>(p.W) + (int64_t)n0 * row_bytes;
+    const rsrc_t wres = make_rsrc(wrow, rows_bytes(n0, 16, p.N, row_bytes));
+    const rsrc_t wres2 = PAIR ? make_rsrc(p.W2 + (int64_t)n0 * words, rows_bytes(n0, 16, p.N, row_bytes))
+                              : wres;
+    const uint32_t wbase = (uint32_t)r * row_bytes;
+    v4u w[G][S];
+    auto load_round = [&](int base) {
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const int T = base + t;
+            const bool live = T < t_end;
+            const int wd = 16 * T + 4 * g;
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi) {
+                const rsrc_t res = gi ? wres2 : wres;
+                if (B3) {
+                    const int blk = 4 * T + g;
+                    w[gi][t] = buf_load16(res, live && blk < nblk ? wbase + 16u * blk : kOOB);
+                } else if (W4) {
+                    w[gi][t] = buf_load16(res, live && wd < words ? wbase + 4u * wd : kOOB);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        w[gi][t][j] = buf_load4(res, live && wd + j < words ? wbase + 4u * (wd + j) : kOOB);
+                }
+            }
+        }
+    };
+    if (W4) {
+        // G * S <= 32 loads after the copies: the wait below counts them exactly.
+        load_round(t_begin);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_stage<G * S>();
+    } else {
+        // Per-word loads (up to 4 G S of them) would overflow the wait's counter: copy first.
+        wait_stage<0>();
+    }
+    block_sync();
+
+    // ---- activation quantization, block-wide, from LDS: absmax of u = x or fl32(x * g) and
+    // the sum of x^2 (per thread in chunk order, then across lanes and waves in a fixed order)
+    const int nchunk = xbytes / 16;       // 16-byte chunks: 4 fp32 or 8 bf16 values each
+    auto chunk = [&](int i, float4 &x0, float4 &x1) {
+        const v4u v = *reinterpret_cast<const v4u *>(xraw + 16 * i);
+        if (BF16) {
+            x0 = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+            x1 = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                             __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
+        } else {
+            x0 = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                             __uint_as_float(v.w));
+        }
+    };
+    auto gquad = [&](int q) { return *reinterpret_cast<const float4 *>(graw + 16 * q); };
+    constexpr int QPC = BF16 ? 2 : 1;     // quads per chunk
+    float amax = 0.0f;
+    double ss = 0.0;
+    for (int i = tid; i < nchunk; i += kGvThreads) {
+        float4 x[2];
+        chunk(i, x[0], x[1]);
+#pragma unroll
+        for (int h = 0; h < QPC; ++h) {
+            const float4 u = norm ? mul4(x[h], gquad(QPC * i + h)) : x[h];
+            amax = fmaxf(amax, absmax4(u));
+            if (norm)
+                ss = sumsq4(ss, x[h]);
+        }
+    }
+    amax = wave_max(amax);
+    if (norm)
+        ss = wave_sum_fixed(ss);
+    if (lane == 0) {
+        s_amax[wave] = amax;
+        s_ss[wave] = ss;
+    }
+    __syncthreads();
+    float a = s_amax[0];
+    double sst = s_ss[0];
+#pragma unroll
+    for (int v = 1; v < kGvWaves; ++v) {
+        a = fmaxf(a, s_amax[v]);
+        sst += s_ss[v];
+    }
+    const float inv = a == 0.0f ? 0.0f : 127.0f / a;   // correctly rounded division
+    const float sx = act_scale(a, sst, K, p.eps, norm);
+    for (int i = tid; i < nchunk; i += kGvThreads) {
+        float4 x[2];
+        chunk(i, x[0], x[1]);
+#pragma unroll
+        for (int h = 0; h < QPC; ++h) {
+            const int q = QPC * i + h;
+            const char4 cq = quant4(norm ? mul4(x[h], gquad(q)) : x[h], inv);
+            *reinterpret_cast<char4 *>(codes + 4 * q) = cq;
+            if (first && p.Xq_out)
+                *reinterpret_cast<char4 *>(p.Xq_out + 4 * q) = cq;
+        }
+    }
+    if (first && p.sx_out && tid == 0)
+        p.sx_out[0] = sx;
+    // Codes past the row, up to the end of the last super-step, meet zero weights; clear them
+    // so that every value fed to the matrix unit is defined.
+    constexpr int EPS = B3 ? 320 : 256;      // weights per super-step
+    for (int q = K / 4 + tid; q < EPS / 4 * supers; q += kGvThreads)
+        *reinterpret_cast<uint32_t *>(codes + 4 * q) = 0u;
+    __syncthreads();
+    if (!W4) {
+        load_round(t_begin);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- product over this wave's super-steps, S per round
+    v4i acc[G];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+        acc[gi] = v4i{0, 0, 0, 0};
+    for (int base = t_begin; base < t_end; base += S) {
+        if (base != t_begin) {
+            load_round(base);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const int T = base + t;
+            if (T < t_end && B3) {
+                // Operand i of lane group g's block: 16-weight chunk 20 T + 5 g + i.
+                v4i av[5];
+#pragma unroll
+                for (int i = 0; i < 5; ++i)
+                    av[i] = *reinterpret_cast<const v4i *>(codes + 16 * (20 * T + 5 * g + i));
+                v4i op[4];
+                uint32_t op4[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    unpack_b3_dword(w[0][t][v], b3lut, op[v], op4[v]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], op[i], acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    av[4], v4i{(int)op4[0], (int)op4[1], (int)op4[2], (int)op4[3]}, acc[0], 0, 0, 0);
+            } else if (T < t_end) {          // wave-uniform
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4i av = *reinterpret_cast<const v4i *>(codes + 256 * T + 64 * g + 16 * j);
+#pragma unroll
+                    for (int gi = 0; gi < G; ++gi)
+                        acc[gi] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, unpack_word64(w[gi][t][j]),
+                                                                       acc[gi], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- slices of one row group meet in LDS (integer sums: exact, fixed order)
+    int s1 = acc[0].x, s2 = acc[G - 1].x;    // lanes 0..15: 64 * D[0][n0 + r]
+    if (ksl > 0) {
+        if (lane < 16) {
+#pragma unroll
+            for (int gi = 0; gi < G; ++gi)
+                s_red[wave][gi][lane] = acc[gi].x;
+        }
+        __syncthreads();
+        if (slice != 0)
+            return;
+        if (lane < 16) {
+            s1 = 0;
+            s2 = 0;
+            for (int v = 0; v < (1 << ksl); ++v) {
+                s1 += s_red[wave + v][0][lane];
+                s2 += s_red[wave + v][G - 1][lane];
+            }
+        }
+    }
+    if (!out_lane)
+        return;
+    // y = fl32(acc * gamma * s_x): gamma * s_x is exact in fp64 (two 24-bit significands),
+    // so this is the correctly rounded value of the exact product.
+    float y = (float)((double)(s1 >> 6) * ((double)gammaf * (double)sx));
+    if (PAIR)
+        y = ffn_act(p.act, y, (float)((double)(s2 >> 6) * ((double)gamma2f * (double)sx)));
+    else if (p.act != BL_ACT_NONE)
+        y = ffn_act(p.act, y, 0.0f);
+    if (p.R)
+        y = y + resid;
+    p.Y[n] = y;
+}
+
+template <int S, bool BF16, bool PAIR, bool B3>
+static void launch_s(const GvBatch &b, int blocks, size_t lds, bool w4, hipStream_t stream)
+{
+    if constexpr (B3)
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, false, true, true>), dim3(blocks), dim3(kGvThreads),
+                           lds, stream, b);
+    else if (w4)
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, true>), dim3(blocks), dim3(kGvThreads), lds,
+                           stream, b);
+    else
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, false>), dim3(blocks), dim3(kGvThreads), lds,
+                           stream, b);
+}
+
+// One launch for one kind (pair or single, one activation dtype); every problem has M == 1.
+// Slices per row group: the fewest (1, 2 or 4) that keep a wave's loads per lane within
+// kGvLoadsPerWave; the round length S is the longest slice, rounded up to 4, 8, 12 or 16
+// (longer slices take several rounds).  Longest rows first.
+template <bool BF16, bool PAIR, bool B3>
+static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, hipStream_t stream)
+{
+    if (count == 0)
+        return hipSuccess;
+    constexpr int G = PAIR ? 2 : 1;
+    int order[BL_MAX_GROUP];
+    for (int i = 0; i < count; ++i)
+        order[i] = i;
+    std::stable_sort(order, order + count, [&](int a, int c) { return q[a]->K > q[c]->K; });
+    GvBatch b{};
+    int blocks = 0, longest = 1;
+    bool w4 = true;
+    for (int o = 0; o < count; ++o) {
+        const bl_linear_ex_problem &s = *q[order[o]];
+        GvDev &d = b.p[o];
+        const int K = (int)s.K;
+        const int supers = B3 ? ((K + 79) / 80 + 3) / 4 : (K / 16 + 15) / 16;
+        int ksl = 0;
+        while (ksl < 2 && G * ((supers + (1 << ksl) - 1) >> ksl) > kGvLoadsPerWave)
+            ++ksl;
+        longest = std::max(longest, (supers + (1 << ksl) - 1) >> ksl);
+        w4 = w4 && (K / 16) % 4 == 0;
+        d.X = s.X;
+        d.g = s.norm_weight;
+        d.W = s.W_packed;
+        d.W2 = s.W2_packed;
+        d.gamma = s.gamma;
+        d.gamma2 = s.gamma2;
+        d.R = s.residual;
+        d.Y = s.Y;
+        d.Xq_out = s.X_q;
+        d.sx_out = s.x_scale;
+        d.eps = s.eps;
+        d.N = (int)s.N;
+        d.K = K;
+        d.ks_log2 = ksl;
+        d.act = s.act;
+        d.block_begin = blocks;
+        const int groups = (d.N + 15) / 16;
+        const int per_block = 4 >> ksl;
+        blocks += (groups + per_block - 1) / per_block;
+    }
+    b.count = count;
+    size_t lds;
+    gemv_lds(q, count, BF16, B3, b.g_off, b.c_off, lds);
+    if (longest <= 4)
+        launch_s<4, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+    else if (longest <= 8)
+        launch_s<8, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+    else if (longest <= 12)
+        launch_s<12, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+    else
+        launch_s<16, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv(const bl_linear_ex_problem *const *q, int count, bool pair, bool bf16,
+                       hipStream_t stream)
+{
+    if (pair)
+        return bf16 ? launch_kind<true, true, false>(q, count, stream)
+                    : launch_kind<false, true, false>(q, count, stream);
+    return bf16 ? launch_kind<true, false, false>(q, count, stream)
+                : launch_kind<false, false, false>(q, count, stream);
+}
+
+hipError_t launch_gemv_b3(const bl_linear_ex_problem *const *q, int count, bool bf16,
+                          hipStream_t stream)
+{
+    return bf16 ? launch_kind<true, false, true>(q, count, stream)
+                : launch_kind<false, false, true>(q, count, stream);
+}
+
+}  // namespace bl

@@ -32,66 +32,6 @@ struct PreBatch {
     int blocks;
 };
 
-// Raw buffer descriptor as four scalar dwords: base address, stride 0, size in bytes, and
-// the gfx9-family raw-access word.  Offsets at or past `bytes` read zero.
-__device__ __forceinline__ v4i make_desc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)base;
-    v4i d;
-    d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    d.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
-    d.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    d.w = 0x00020000;
-    return d;
-}
-
-// LDS byte address of a shared-memory pointer, wave-uniform.
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p)
-{
-    typedef __attribute__((address_space(3))) const unsigned char lds_uchar;
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_uchar *)p);
-}
-
-// Direct-to-LDS 16-byte buffer load (gfx950): lane l's 16 bytes land at LDS address
-// lds + 16 * l; an out-of-range offset writes zeros.  Issued from inline assembly so that the
-// compiler does not model it: modelled, it cannot tell the in-flight stages apart and drains
-// every load before the first LDS read of each unrolled group of stages.  The instruction
-// has no register result; its completion is ordered by the pipeline's explicit vmcnt waits
-// and barriers, and the "memory" clobber keeps LDS accesses from moving across it.
-__device__ __forceinline__ void dma16(v4i desc, uint32_t lds, uint32_t offset)
-{
-    asm volatile("s_mov_b32 m0, %0\n\t"
-                 "s_nop 0\n\t"
-                 "buffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(offset), "s"(desc)
-                 : "memory", "m0");
-}
-
-// Workgroup barrier that is also a compiler barrier for memory operations (the barrier
-// instruction alone does not stop the compiler from moving LDS accesses across it), without
-// the waits a memory fence would add.
-__device__ __forceinline__ void block_sync()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0): wait until at most N vector-memory loads of this wave
-// (direct-to-LDS ones included) are still in flight and every LDS read of this wave has
-// returned.  The second part matters before the barrier that hands a stage buffer back to
-// the loads: the deferred k-step's activation reads of the buffer about to be refilled are
-// issued at the end of the previous stage and not needed until after the barrier, and
-// without the wait one of them could still be queued behind other LDS traffic when another
-// wave's refill lands (a bare s_barrier does not wait for LDS reads).
-template <int N>
-__device__ __forceinline__ void wait_stage()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
 // Tile configuration: BM x BN block tile split over WM x WN waves (wave tile BM/WM x BN/WN,
 // MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS, EA bytes per
 // activation (1: int8 codes on the int8 matrix unit; 2: bf16 activations on the bf16 one).
