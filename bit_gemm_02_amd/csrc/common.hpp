@@ -40,6 +40,13 @@ __device__ __forceinline__ v4u buf_load16(rsrc_t r, uint32_t offset)
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 0);
 }
 
+// The same with the non-temporal policy, for data read once per launch (a weight stream):
+// it is not kept in the caches for reuse.
+__device__ __forceinline__ v4u buf_load16_nt(rsrc_t r, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, 2);
+}
+
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t offset)
 {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)offset, 0, 0);

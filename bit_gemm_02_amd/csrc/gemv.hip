@@ -9,19 +9,21 @@
 // multiply, issue the next) therefore finishes well after the rest of the chip, with its
 // later rounds queued behind everybody's first.  This kernel cuts the work so that each wave
 // has one round: a wave owns one group of 16 weight rows (two for a gated pair: the same rows
-// of both projections) over one slice of K, and issues every load of that slice before it
-// uses the first.  Long rows are split into 2 or 4 slices (one per wave of the block, summed
+// of both projections) over one slice of K, and has every load of that slice in flight before
+// it multiplies.  Long rows are split into 2 or 4 slices (one per wave of the block, summed
 // through LDS at the end, exactly, in a fixed order) so that every wave moves about the same
 // number of bytes whatever the projection's shape; short rows give each wave of a block its
 // own row group.
 //
 // The token's int8 codes need the absmax of the whole row (BitDistill article: INT8
 // activations; absmax scale per token), so every block quantizes the row itself, with the same
-// arithmetic as the activation-quantization kernels (quant4, act_scale): its 256 threads load
-// the row (and the RMSNorm weight) before any weight load, so those loads, which hit L2 after
-// the first block, come back first; the partial maxima (and sums of squares) meet in LDS in a
-// fixed order, and the codes go to LDS, where the waves read them as the MFMA's activation
-// operand.  All of this runs while the block's weight loads are in flight.
+// arithmetic as the activation-quantization kernels (quant4, act_scale): its four waves copy
+// the row into LDS with direct-to-LDS loads issued before any weight load, the partial maxima
+// (and sums of squares) meet in LDS in a fixed order, and the codes go to LDS, where the waves
+// read them as the MFMA's activation operand.  The row copies get no priority in the memory
+// system: with every wave's full round of weight loads ahead of them they arrived microseconds
+// late (per-wave timestamps), so each wave sends only its first four super-steps of weights
+// before it waits for the row, and the rest right after the quantization.
 //
 // Product: v_mfma_i32_16x16x64_i8 with 16 weight rows as the B operand (a lane (r, g) holds
 // words 16t + 4g .. 16t + 4g + 3 of row r, one 16-byte load per super-step t of 256 weights,
@@ -38,31 +40,30 @@ namespace bl {
 constexpr int kGvThreads = 256;
 constexpr int kGvWaves = kGvThreads / kWave;
 constexpr int kGvLoadsPerWave = 12;  // target 16-byte weight loads per lane per wave (one round)
-constexpr size_t kGvMaxLds = 96 * 1024;  // dynamic LDS per block (raw row, norm weight, codes)
+constexpr int kGvQuads = 12;         // activation quads per thread: rows up to 12288 values
+constexpr size_t kGvMaxLds = 64 * 1024;
 
-// Dynamic LDS of a launch over these problems: the raw row and the norm weight of the longest
-// problem in whole 1 KB copies, then the codes of its super-steps.
+// Dynamic LDS of a launch: the raw row of the longest problem in whole 1 KB copies, then the
+// codes of its super-steps.
 static void gemv_lds(const bl_linear_ex_problem *const *q, int count, bool bf16, bool b3,
-                     int &g_off, int &c_off, size_t &bytes)
+                     int &c_off, size_t &bytes)
 {
     int k_max = 16;
-    bool any_norm = false;
-    for (int i = 0; i < count; ++i) {
+    for (int i = 0; i < count; ++i)
         k_max = std::max(k_max, (int)q[i]->K);
-        any_norm = any_norm || q[i]->norm_weight != nullptr;
-    }
-    const int esize = bf16 ? 2 : 4;
     const int supers = b3 ? ((k_max + 79) / 80 + 3) / 4 : (k_max / 16 + 15) / 16;
-    g_off = (k_max * esize + 1023) / 1024 * 1024;
-    c_off = g_off + (any_norm ? (k_max * 4 + 1023) / 1024 * 1024 : 0);
+    c_off = (k_max * (bf16 ? 2 : 4) + 1023) / 1024 * 1024;
     bytes = (size_t)c_off + (size_t)(b3 ? 320 : 256) * supers;
 }
 
 bool gemv_fits(const bl_linear_ex_problem *const *q, int count, bool bf16, bool b3)
 {
-    int g_off, c_off;
+    for (int i = 0; i < count; ++i)
+        if (q[i]->K > kGvThreads * 4 * kGvQuads || (!b3 && q[i]->K % 64 != 0))
+            return false;
+    int c_off;
     size_t bytes;
-    gemv_lds(q, count, bf16, b3, g_off, c_off, bytes);
+    gemv_lds(q, count, bf16, b3, c_off, bytes);
     return bytes <= kGvMaxLds;
 }
 
@@ -84,24 +85,23 @@ struct GvDev {
     int block_begin;
 };
 
-// LDS of a launch: [0, g_off) the raw activation row of the longest problem, [g_off, c_off)
-// its RMSNorm weight (when a problem has one), [c_off, c_off + 256 * supers) the codes.
 struct GvBatch {
     GvDev p[BL_MAX_GROUP];
     int count;
-    int g_off, c_off;
+    int c_off;              // LDS offset of the codes (the raw row comes first)
 };
 
 // S: super-steps (16-byte loads per lane and row group) in one round; BF16: activation dtype;
-// PAIR: gated pair (two row groups per wave, the epilogue applies the activation); W4: every
-// row has a multiple of 4 words, so a lane's 16 bytes never straddle the end of a row; B3:
+// PAIR: gated pair (two row groups per wave, the epilogue applies the activation); NORM: every
+// problem of the launch has an RMSNorm weight (held in registers: rows of at most 12288); B3:
 // base-3 rows (16-byte blocks of 80 weights, see b3_table_entry; a super-step is then 320
-// weights and five MFMAs per row group, the expansion a table lookup in LDS).
-template <int S, bool BF16, bool PAIR, bool W4, bool B3 = false>
+// weights and five MFMAs per row group, the expansion a table lookup in LDS).  Two-bit rows
+// have K % 64 == 0, so a lane's 16 bytes never straddle the end of a row.
+template <int S, bool BF16, bool PAIR, bool NORM, bool B3>
 __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 {
     constexpr int G = PAIR ? 2 : 1;
-    static_assert(!B3 || (W4 && !PAIR), "base-3 rows: whole 16-byte blocks, single projections");
+    static_assert(!B3 || !PAIR, "base-3 rows: single projections");
     __shared__ __align__(8) uint32_t b3lut[B3 ? 512 : 2];
     if (B3) {
         uint32_t lo, hi;
@@ -136,9 +136,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     const int t_begin = (supers * slice) >> ksl;
     const int t_end = (supers * (slice + 1)) >> ksl;
     const bool first = (int)blockIdx.x == p.block_begin;
-    const bool norm = p.g != nullptr;
     unsigned char *const xraw = lds;
-    unsigned char *const graw = lds + b.g_off;
     unsigned char *const codes = lds + b.c_off;
 
     // ---- epilogue inputs first, so the epilogue does not wait on a round trip of its own
@@ -148,18 +146,30 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     const float resid = __uint_as_float(
         buf_load4(make_rsrc(p.R, p.R ? (uint32_t)p.N * 4u : 0u), out_lane ? (uint32_t)n * 4u : kOOB));
 
-    // ---- the activation row (and norm weight) straight into LDS, before any weight load:
-    // loads return in issue order, and these hit L2 after the first block.  Wave w copies
-    // 1 KB chunks w, w + 4, ... (the tail of the last chunk reads as zeros).
+    // ---- the activation row straight into LDS, before any weight load: loads return in
+    // issue order, and these hit L2 after the first block.  Wave w copies 1 KB chunks w,
+    // w + 4, ... (the tail of the last chunk reads as zeros).
     constexpr int esize = BF16 ? 2 : 4;
     const int xbytes = K * esize;
     const v4i xdesc = make_desc(p.X, (uint32_t)xbytes);
     for (int c = wave; c * 1024 < xbytes; c += kGvWaves)
         dma16(xdesc, lds_addr(xraw + 1024 * c), (uint32_t)(1024 * c + 16 * lane));
-    if (norm) {
-        const v4i gdesc = make_desc(p.g, (uint32_t)K * 4u);
-        for (int c = wave; c * 1024 < K * 4; c += kGvWaves)
-            dma16(gdesc, lds_addr(graw + 1024 * c), (uint32_t)(1024 * c + 16 * lane));
+    // The row in 16-byte chunks (4 fp32 or 8 bf16 values): thread t takes chunks t, t + 256,
+    // ...; its norm weights (one 16-byte quad per 4 values) go to registers, also ahead of the
+    // weights.
+    constexpr int QPC = BF16 ? 2 : 1;                 // quads per chunk
+    constexpr int CH = kGvQuads / QPC;                // chunks per thread
+    const int nchunk = xbytes / 16;
+    v4u rgw[NORM ? kGvQuads : 1];
+    if (NORM) {
+        const rsrc_t gr = make_rsrc(p.g, (uint32_t)K * 4u);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = tid + c * kGvThreads;
+#pragma unroll
+            for (int h = 0; h < QPC; ++h)
+                rgw[QPC * c + h] = buf_load16(gr, i < nchunk ? 16u * (uint32_t)(QPC * i + h) : kOOB);
+        }
     }
 
     // ---- weight loads: rows n0 .. n0+15 (rows past N read as zero), the first round of
@@ -170,71 +180,88 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
                               : wres;
     const uint32_t wbase = (uint32_t)r * row_bytes;
     v4u w[G][S];
-    auto load_round = [&](int base) {
+    // Super-steps lo .. hi-1 of the round starting at super-step `base` (non-temporal: the
+    // weights are read once).
+    auto load_round = [&](int base, int lo, int hi) {
 #pragma unroll
         for (int t = 0; t < S; ++t) {
+            if (t < lo || t >= hi)
+                continue;
             const int T = base + t;
             const bool live = T < t_end;
-            const int wd = 16 * T + 4 * g;
 #pragma unroll
             for (int gi = 0; gi < G; ++gi) {
                 const rsrc_t res = gi ? wres2 : wres;
                 if (B3) {
                     const int blk = 4 * T + g;
-                    w[gi][t] = buf_load16(res, live && blk < nblk ? wbase + 16u * blk : kOOB);
-                } else if (W4) {
-                    w[gi][t] = buf_load16(res, live && wd < words ? wbase + 4u * wd : kOOB);
+                    w[gi][t] = buf_load16_nt(res, live && blk < nblk ? wbase + 16u * blk : kOOB);
                 } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        w[gi][t][j] = buf_load4(res, live && wd + j < words ? wbase + 4u * (wd + j) : kOOB);
+                    const int wd = 16 * T + 4 * g;
+                    w[gi][t] = buf_load16_nt(res, live && wd < words ? wbase + 4u * wd : kOOB);
                 }
             }
         }
     };
-    if (W4) {
-        // G * S <= 32 loads after the copies: the wait below counts them exactly.
-        load_round(t_begin);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_stage<G * S>();
-    } else {
-        // Per-word loads (up to 4 G S of them) would overflow the wait's counter: copy first.
-        wait_stage<0>();
-    }
+    // Only the first few super-steps go out before the row is waited for: the row copies get
+    // no priority in the memory system, and a full round from every wave ahead of them delays
+    // them (and so every block's quantization) by microseconds; the rest follows the
+    // quantization.  The copies (and norm weights) were issued before these G * EARLY loads.
+    constexpr int EARLY = S < 4 ? S : 4;
+    load_round(t_begin, 0, EARLY);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_stage<G * EARLY>();
     block_sync();
 
-    // ---- activation quantization, block-wide, from LDS: absmax of u = x or fl32(x * g) and
-    // the sum of x^2 (per thread in chunk order, then across lanes and waves in a fixed order)
-    const int nchunk = xbytes / 16;       // 16-byte chunks: 4 fp32 or 8 bf16 values each
-    auto chunk = [&](int i, float4 &x0, float4 &x1) {
-        const v4u v = *reinterpret_cast<const v4u *>(xraw + 16 * i);
+    // ---- activation quantization, block-wide: absmax of u = x or fl32(x * g) and the sum of
+    // x^2 (per thread in chunk order, then across lanes and waves in a fixed order), four
+    // chunks' LDS reads in flight at a time
+    auto chunk_quads = [&](const v4u &v, float4 *x) {
         if (BF16) {
-            x0 = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
-                             __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
-            x1 = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
-                             __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
+            x[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+            x[QPC - 1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                                     __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
         } else {
-            x0 = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                             __uint_as_float(v.w));
+            x[0] = make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                               __uint_as_float(v.w));
         }
     };
-    auto gquad = [&](int q) { return *reinterpret_cast<const float4 *>(graw + 16 * q); };
-    constexpr int QPC = BF16 ? 2 : 1;     // quads per chunk
+    auto gq = [&](int c, int h) {
+        const v4u v = rgw[NORM ? QPC * c + h : 0];
+        return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                           __uint_as_float(v.w));
+    };
+    auto read4 = [&](int c0, v4u *v) {     // chunks c0 .. c0+3 of this thread (zeros past the row)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + (c0 + u) * kGvThreads;
+            const v4u t = *reinterpret_cast<const v4u *>(xraw + 16 * (i < nchunk ? i : 0));
+            v[u] = i < nchunk ? t : v4u{0, 0, 0, 0};
+        }
+    };
     float amax = 0.0f;
     double ss = 0.0;
-    for (int i = tid; i < nchunk; i += kGvThreads) {
-        float4 x[2];
-        chunk(i, x[0], x[1]);
 #pragma unroll
-        for (int h = 0; h < QPC; ++h) {
-            const float4 u = norm ? mul4(x[h], gquad(QPC * i + h)) : x[h];
-            amax = fmaxf(amax, absmax4(u));
-            if (norm)
-                ss = sumsq4(ss, x[h]);
+    for (int c0 = 0; c0 < CH; c0 += 4) {
+        if (c0 * kGvThreads < nchunk) {      // block-uniform
+            v4u v[4];
+            read4(c0, v);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float4 x[QPC];
+                chunk_quads(v[u], x);
+#pragma unroll
+                for (int h = 0; h < QPC; ++h) {
+                    const float4 uu = NORM ? mul4(x[h], gq(c0 + u, h)) : x[h];
+                    amax = fmaxf(amax, absmax4(uu));
+                    if (NORM)
+                        ss = sumsq4(ss, x[h]);
+                }
+            }
         }
     }
     amax = wave_max(amax);
-    if (norm)
+    if (NORM)
         ss = wave_sum_fixed(ss);
     if (lane == 0) {
         s_amax[wave] = amax;
@@ -249,17 +276,28 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
         sst += s_ss[v];
     }
     const float inv = a == 0.0f ? 0.0f : 127.0f / a;   // correctly rounded division
-    const float sx = act_scale(a, sst, K, p.eps, norm);
-    for (int i = tid; i < nchunk; i += kGvThreads) {
-        float4 x[2];
-        chunk(i, x[0], x[1]);
+    const float sx = act_scale(a, sst, K, p.eps, NORM);
 #pragma unroll
-        for (int h = 0; h < QPC; ++h) {
-            const int q = QPC * i + h;
-            const char4 cq = quant4(norm ? mul4(x[h], gquad(q)) : x[h], inv);
-            *reinterpret_cast<char4 *>(codes + 4 * q) = cq;
-            if (first && p.Xq_out)
-                *reinterpret_cast<char4 *>(p.Xq_out + 4 * q) = cq;
+    for (int c0 = 0; c0 < CH; c0 += 4) {
+        if (c0 * kGvThreads < nchunk) {
+            v4u v[4];
+            read4(c0, v);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = tid + (c0 + u) * kGvThreads;
+                if (i < nchunk) {
+                    float4 x[QPC];
+                    chunk_quads(v[u], x);
+#pragma unroll
+                    for (int h = 0; h < QPC; ++h) {
+                        const int q = QPC * i + h;
+                        const char4 cq = quant4(NORM ? mul4(x[h], gq(c0 + u, h)) : x[h], inv);
+                        *reinterpret_cast<char4 *>(codes + 4 * q) = cq;
+                        if (first && p.Xq_out)
+                            *reinterpret_cast<char4 *>(p.Xq_out + 4 * q) = cq;
+                    }
+                }
+            }
         }
     }
     if (first && p.sx_out && tid == 0)
@@ -270,10 +308,8 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     for (int q = K / 4 + tid; q < EPS / 4 * supers; q += kGvThreads)
         *reinterpret_cast<uint32_t *>(codes + 4 * q) = 0u;
     __syncthreads();
-    if (!W4) {
-        load_round(t_begin);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    load_round(t_begin, EARLY, S);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- product over this wave's super-steps, S per round
     v4i acc[G];
@@ -282,7 +318,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
         acc[gi] = v4i{0, 0, 0, 0};
     for (int base = t_begin; base < t_end; base += S) {
         if (base != t_begin) {
-            load_round(base);
+            load_round(base, 0, S);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -352,23 +388,21 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 }
 
 template <int S, bool BF16, bool PAIR, bool B3>
-static void launch_s(const GvBatch &b, int blocks, size_t lds, bool w4, hipStream_t stream)
+static void launch_s(const GvBatch &b, int blocks, size_t lds, bool norm, hipStream_t stream)
 {
-    if constexpr (B3)
-        hipLaunchKernelGGL((gemv_kernel<S, BF16, false, true, true>), dim3(blocks), dim3(kGvThreads),
-                           lds, stream, b);
-    else if (w4)
-        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, true>), dim3(blocks), dim3(kGvThreads), lds,
+    if (norm)
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, true, B3>), dim3(blocks), dim3(kGvThreads), lds,
                            stream, b);
     else
-        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, false>), dim3(blocks), dim3(kGvThreads), lds,
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, false, B3>), dim3(blocks), dim3(kGvThreads), lds,
                            stream, b);
 }
 
-// One launch for one kind (pair or single, one activation dtype); every problem has M == 1.
-// Slices per row group: the fewest (1, 2 or 4) that keep a wave's loads per lane within
-// kGvLoadsPerWave; the round length S is the longest slice, rounded up to 4, 8, 12 or 16
-// (longer slices take several rounds).  Longest rows first.
+// One launch for problems of one kind (pair or single, one activation dtype, all with or all
+// without a norm) that gemv_fits; every problem has M == 1.  Slices per row group: the fewest
+// (1, 2 or 4) that keep a wave's loads per lane within kGvLoadsPerWave; the round length S is
+// the longest slice, rounded up to 4, 8, 12 or 16 (longer slices take several rounds).
+// Longest rows first.
 template <bool BF16, bool PAIR, bool B3>
 static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, hipStream_t stream)
 {
@@ -381,7 +415,6 @@ static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, h
     std::stable_sort(order, order + count, [&](int a, int c) { return q[a]->K > q[c]->K; });
     GvBatch b{};
     int blocks = 0, longest = 1;
-    bool w4 = true;
     for (int o = 0; o < count; ++o) {
         const bl_linear_ex_problem &s = *q[order[o]];
         GvDev &d = b.p[o];
@@ -391,7 +424,6 @@ static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, h
         while (ksl < 2 && G * ((supers + (1 << ksl) - 1) >> ksl) > kGvLoadsPerWave)
             ++ksl;
         longest = std::max(longest, (supers + (1 << ksl) - 1) >> ksl);
-        w4 = w4 && (K / 16) % 4 == 0;
         d.X = s.X;
         d.g = s.norm_weight;
         d.W = s.W_packed;
@@ -408,39 +440,57 @@ static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, h
         d.ks_log2 = ksl;
         d.act = s.act;
         d.block_begin = blocks;
-        const int groups = (d.N + 15) / 16;
-        const int per_block = 4 >> ksl;
+        const int groups = (d.N + 15) / 16, per_block = 4 >> ksl;
         blocks += (groups + per_block - 1) / per_block;
     }
     b.count = count;
+    const bool norm = q[0]->norm_weight != nullptr;
     size_t lds;
-    gemv_lds(q, count, BF16, B3, b.g_off, b.c_off, lds);
+    gemv_lds(q, count, BF16, B3, b.c_off, lds);
+    // A pair's wave holds two row groups' loads: rounds of at most 8 super-steps (more would
+    // not fit the register budget of three waves per SIMD).
     if (longest <= 4)
-        launch_s<4, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
-    else if (longest <= 8)
-        launch_s<8, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+        launch_s<4, BF16, PAIR, B3>(b, blocks, lds, norm, stream);
+    else if (longest <= 8 || PAIR)
+        launch_s<8, BF16, PAIR, B3>(b, blocks, lds, norm, stream);
     else if (longest <= 12)
-        launch_s<12, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+        launch_s<12, BF16, false, B3>(b, blocks, lds, norm, stream);
     else
-        launch_s<16, BF16, PAIR, B3>(b, blocks, lds, w4, stream);
+        launch_s<16, BF16, false, B3>(b, blocks, lds, norm, stream);
     return hipGetLastError();
+}
+
+// Problems of one kind, split into those with and without a norm (one launch each).
+template <bool BF16, bool PAIR, bool B3>
+static hipError_t launch_split(const bl_linear_ex_problem *const *q, int count, hipStream_t stream)
+{
+    const bl_linear_ex_problem *part[2][BL_MAX_GROUP];
+    int n[2] = {0, 0};
+    for (int i = 0; i < count; ++i) {
+        const int k = q[i]->norm_weight ? 1 : 0;
+        part[k][n[k]++] = q[i];
+    }
+    hipError_t e = launch_kind<BF16, PAIR, B3>(part[0], n[0], stream);
+    if (e == hipSuccess)
+        e = launch_kind<BF16, PAIR, B3>(part[1], n[1], stream);
+    return e;
 }
 
 hipError_t launch_gemv(const bl_linear_ex_problem *const *q, int count, bool pair, bool bf16,
                        hipStream_t stream)
 {
     if (pair)
-        return bf16 ? launch_kind<true, true, false>(q, count, stream)
-                    : launch_kind<false, true, false>(q, count, stream);
-    return bf16 ? launch_kind<true, false, false>(q, count, stream)
-                : launch_kind<false, false, false>(q, count, stream);
+        return bf16 ? launch_split<true, true, false>(q, count, stream)
+                    : launch_split<false, true, false>(q, count, stream);
+    return bf16 ? launch_split<true, false, false>(q, count, stream)
+                : launch_split<false, false, false>(q, count, stream);
 }
 
 hipError_t launch_gemv_b3(const bl_linear_ex_problem *const *q, int count, bool bf16,
                           hipStream_t stream)
 {
-    return bf16 ? launch_kind<true, false, true>(q, count, stream)
-                : launch_kind<false, false, true>(q, count, stream);
+    return bf16 ? launch_split<true, false, true>(q, count, stream)
+                : launch_split<false, false, true>(q, count, stream);
 }
 
 }  // namespace bl
