@@ -288,7 +288,8 @@ __device__ __forceinline__ float4 ffn_act4(int kind, float4 x, float4 x2)
 // that of any accurate fp64 evaluation only within a few 2^-52 of an fp32 midpoint.  Large
 // |g| saturates as the library's exp does (e^800 = inf, e^-800 = 0); NaN propagates.
 // About 12 fp64 operations per element instead of about 40.
-__device__ __forceinline__ double exp_f64_tab(double t, const double *tab)
+// (Host-callable as well, so that it can be checked against the host library on the CPU.)
+__host__ __device__ inline double exp_f64_tab(double t, const double *tab)
 {
     t = t < -800.0 ? -800.0 : (t > 800.0 ? 800.0 : t);          // NaN compares false: kept
     constexpr double kInvStep = 92.332482616893656877;           // 64 / ln 2

@@ -72,6 +72,10 @@ class Oracle:
         lib.oracle_ffn_act1.restype = ctypes.c_float
         lib.oracle_ffn_act.argtypes = [ctypes.c_int, _P, _P, _I64, _P]
         lib.oracle_ffn_act.restype = None
+        lib.oracle_ffn_act1_f64.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float]
+        lib.oracle_ffn_act1_f64.restype = ctypes.c_double
+        lib.oracle_ffn_act_f64.argtypes = [ctypes.c_int, _P, _P, _I64, _P]
+        lib.oracle_ffn_act_f64.restype = None
         lib.oracle_epilogue_residual.argtypes = [_P, _P, ctypes.c_float, _P, _I64, _I64, _P]
         lib.oracle_epilogue_residual.restype = None
         lib.oracle_forward_entries.argtypes = [_P, _P, _P, ctypes.c_float, _I64, _P, _P, _I64,
@@ -218,6 +222,16 @@ class Oracle:
         H = np.empty_like(X)
         self._lib.oracle_ffn_act(int(kind), _ptr(X), _ptr(X2), X.size, _ptr(H))
         return H
+
+    def ffn_act_f64(self, kind: int, X: np.ndarray, X2: Optional[np.ndarray] = None) -> np.ndarray:
+        """The activation's fp64 value before its one rounding to fp32 (ffn_act rounds it)."""
+        X = _c(X, np.float32)
+        X2 = None if X2 is None else _c(X2, np.float32)
+        if X2 is not None:
+            assert X2.shape == X.shape
+        H64 = np.empty(X.shape, dtype=np.float64)
+        self._lib.oracle_ffn_act_f64(int(kind), _ptr(X), _ptr(X2), X.size, _ptr(H64))
+        return H64
 
     def ffn_act1(self, kind: int, x: float, x2: float = 0.0) -> np.float32:
         return np.float32(self._lib.oracle_ffn_act1(int(kind), float(np.float32(x)),

@@ -323,8 +323,9 @@ int oracle_forward_entries(const int8_t *Xq, const float *s_x, const uint32_t *p
 /* ---------------------------------------------------------- O7: FFN activation (chain) */
 
 /* Activation kinds: 1 = SwiGLU h = silu(x) * x2, 2 = gated ReLU^2 h = relu(x)^2 * x2,
- * 3 = ReLU^2 h = relu(x)^2 (x2 unused).  fp64 evaluation, one rounding to fp32. */
-float oracle_ffn_act1(int kind, float x, float x2)
+ * 3 = ReLU^2 h = relu(x)^2 (x2 unused).  fp64 evaluation; this is the fp64 value before the
+ * one rounding to fp32 (tests use it to tell where that rounding is close to a tie). */
+double oracle_ffn_act1_f64(int kind, float x, float x2)
 {
     double v;
     if (kind == 1) {
@@ -336,7 +337,13 @@ float oracle_ffn_act1(int kind, float x, float x2)
         double r = x > 0.0f ? (double)x : 0.0;
         v = r * r;
     }
-    return (float)v;
+    return v;
+}
+
+/* The activation rounded once to fp32. */
+float oracle_ffn_act1(int kind, float x, float x2)
+{
+    return (float)oracle_ffn_act1_f64(kind, x, x2);
 }
 
 /* H = act(X, X2) elementwise over `count` values (X2 may be NULL for kind 3). */
@@ -344,6 +351,13 @@ void oracle_ffn_act(int kind, const float *X, const float *X2, int64_t count, fl
 {
     for (int64_t i = 0; i < count; ++i)
         H[i] = oracle_ffn_act1(kind, X[i], X2 ? X2[i] : 0.0f);
+}
+
+/* The same, unrounded: H64 = the fp64 value of each activation. */
+void oracle_ffn_act_f64(int kind, const float *X, const float *X2, int64_t count, double *H64)
+{
+    for (int64_t i = 0; i < count; ++i)
+        H64[i] = oracle_ffn_act1_f64(kind, X[i], X2 ? X2[i] : 0.0f);
 }
 
 /* ------------------------------------------------------- O8: residual epilogue (chain) */

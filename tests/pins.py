@@ -420,6 +420,43 @@ def pin_swiglu_high_precision(orc):
         assert abs((a - b) - x) <= 2 * _ulp32(x), (x, a, b)
 
 
+def _silu_times_exact(g, u):
+    """silu(g) * u as a 60-digit decimal."""
+    getcontext().prec = 60
+    dg = Decimal(float(g))
+    return dg / (Decimal(1) + (-dg).exp()) * Decimal(float(u))
+
+
+def pin_ffn_act_fp64_values(orc):
+    """The activations' fp64 values before the fp32 rounding (what the parity tests use to
+    decide whether an fp32 difference sits at a rounding tie): SwiGLU within 4 fp64 ulps of a
+    60-digit decimal evaluation (one correctly rounded exp, an addition, a division and a
+    product; each at most an ulp or so), exact zeros where g or u is 0; ReLU^2 of an fp32 is
+    exact in fp64 (a 24-bit significand squared) and gated ReLU^2 one fp64 rounding of the
+    exact product; each fp64 value rounds to the fp32 activation."""
+    r = _rng(73)
+    G = r.standard_normal(800).astype(np.float32) * np.float32(5)
+    U = r.standard_normal(800).astype(np.float32)
+    G[:6] = np.array([0.0, -0.0, 1e-40, -30.0, 80.0, -700.0], np.float32)
+    H64 = orc.ffn_act_f64(orc.SWIGLU, G, U)
+    assert np.array_equal(H64.astype(np.float32), orc.ffn_act(orc.SWIGLU, G, U))
+    for g, u, h in zip(G, U, H64):
+        exact = _silu_times_exact(g, u)
+        if exact == 0:
+            assert h == 0.0, (g, u, h)
+            continue
+        err = abs(Fraction(float(h)) - Fraction(exact)) / abs(Fraction(exact))
+        assert err <= Fraction(4, 2 ** 52), (g, u, float(h), float(err))
+    X = r.standard_normal(300).astype(np.float32) * np.float32(3)
+    H2 = orc.ffn_act_f64(orc.RELU2, X)
+    for x, h in zip(X, H2):
+        assert Fraction(float(h)) == (Fraction(float(x)) ** 2 if x > 0 else 0), (x, h)
+    H3 = orc.ffn_act_f64(orc.RELU2_GLU, X, U[:300])
+    for x, u, h in zip(X, U[:300], H3):
+        exact = Fraction(float(x)) ** 2 * Fraction(float(u)) if x > 0 else Fraction(0)
+        assert Fraction(float(h)) == exact or abs(Fraction(float(h)) - exact) <= abs(exact) / 2 ** 53, (x, u, h)
+
+
 def pin_residual_epilogue_exact(orc):
     """Residual epilogue: fp32(fp32(acc * gamma * s_x) + r), the second step one exactly
     rounded fp32 addition; r = 0 gives the plain epilogue, r = -y gives +0."""

@@ -14,6 +14,7 @@ fixed order, so within 1e-6).
 import numpy as np
 import pytest
 
+import tie_band
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -176,18 +177,23 @@ EX_SHAPES = [(1, 16, 16), (1, 300, 768), (2, 1000, 2048), (3, 129, 272), (4, 204
 
 
 def ex_reference(orc, call, ref, C2, gamma2, kind, R):
-    """Y from the oracle on the call's reported codes and scales."""
+    """Y from the oracle on the call's reported codes and scales, and for SwiGLU the fp64 value
+    of h = silu(y1) * y2 before its fp32 rounding (else None)."""
     q, s = host(call["X_q"]), host(call["x_scale"])
     y1 = orc.epilogue(orc.matmul(q, ref["C"]), s, GAMMA)
+    h64 = None
     if C2 is not None:
-        h = orc.ffn_act(kind, y1, orc.epilogue(orc.matmul(q, C2), s, gamma2))
+        y2 = orc.epilogue(orc.matmul(q, C2), s, gamma2)
+        h = orc.ffn_act(kind, y1, y2)
+        if kind == orc.SWIGLU:
+            h64 = orc.ffn_act_f64(kind, y1, y2)
     elif kind != 0:
         h = orc.ffn_act(kind, y1)
     else:
         h = y1
     if R is not None:
         h = (h + R).astype(np.float32)      # one fp32 rounding of the fp32 sum
-    return h
+    return h, h64
 
 
 @pytest.mark.parametrize("M,N,K", EX_SHAPES)
@@ -212,12 +218,14 @@ def test_linear_ex(torch, bl, orc, M, N, K, kind, norm, residual):
     nz = s_ref != 0
     assert np.array_equal(s == 0, ~nz), label
     assert rel_err(s[nz], s_ref[nz]) <= REL, label
-    Y_ref = ex_reference(orc, call, ref, C2, gamma2, kind, R)
+    Y_ref, h64 = ex_reference(orc, call, ref, C2, gamma2, kind, R)
     Y = host(call["Y"])
     if kind == bl.ACT_SWIGLU:
-        bad = Y != Y_ref
-        assert np.count_nonzero(bad) <= max(1, Y.size // 100000), label
-        assert rel_err(Y[bad], Y_ref[bad]) <= 2.0 ** -22, label
+        # The device library's exp against the host's: h may take the other rounding where the
+        # oracle's fp64 h is at an fp32 tie, and Y is then exactly that h (plus the residual).
+        flips = tie_band.check_values(Y, h64, label, add=R)
+        if flips:
+            print(f"{label}: {flips} of {Y.size} SwiGLU values at an fp32 tie took the other rounding")
     else:
         assert np.array_equal(Y, Y_ref), label
 
