@@ -139,6 +139,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_abi_version.restype = ctypes.c_int
     L.bitlinear_quantize_weights_workspace.argtypes = [I64, I64]
     L.bitlinear_quantize_weights_workspace.restype = SZ
+    L.bitlinear_workspace_bytes.argtypes = [I64, I64]
+    L.bitlinear_workspace_bytes.restype = SZ
     L.bitlinear_quantize_weights.argtypes = [P, I64, I64, P, P, P, SZ, P]
     L.bitlinear_quantize_weights.restype = ctypes.c_int
     L.bitlinear_quantize_weights_grouped_workspace.argtypes = [ctypes.c_int]

@@ -310,6 +310,11 @@ size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
     return bl::quantize_weights_workspace(1);
 }
 
+size_t bitlinear_workspace_bytes(int64_t N, int64_t K)
+{
+    return bitlinear_quantize_weights_workspace(N, K);
+}
+
 size_t bitlinear_quantize_weights_grouped_workspace(int count)
 {
     if (count <= 0 || count > BL_MAX_GROUP)

@@ -12,7 +12,8 @@
 // launch (prefill_block, decode_block), so the results are bit-identical to the two
 // launches.  The grid uses the 128 x 128 prefill tile (four waves, the decode block's size);
 // its LDS is the sum of both bodies' static buffers (60 KB + 4 KB) plus the decode block's
-// staged activations, still two blocks per compute unit.
+// staged activations (M * K bytes): two blocks per compute unit while those stay under about
+// 16 KB, one block per compute unit for larger decode rows (up to the fused form's 48 KB).
 #include "decode_core.hpp"
 #include "prefill_core.hpp"
 

@@ -15,6 +15,11 @@
  *   5. Y = acc · gamma · s_x, fp32                                bitlinear_forward
  *
  * General rules for every entry point:
+ *   * Deliberate differences from a textbook C signature: the stream is passed as void* (a
+ *     hipStream_t, NULL = the legacy default stream), so that a plain C caller or a ctypes
+ *     binding needs no HIP header; the activation dtype is passed as int (a bl_dtype value),
+ *     for the same reason; and K is limited to BL_MAX_K (below), far under the 127 * K < 2^31
+ *     bound of the exact int32 product, because the kernels accumulate 64 * acc.
  *   * Every pointer argument is a DEVICE pointer (HIP device memory visible to the GPU that
  *     owns `stream`), owned by the caller, 16-byte aligned, and the tensor behind it is dense
  *     row-major.  Pointers to empty tensors (a zero dimension) may be NULL.  The library never
@@ -60,7 +65,9 @@ typedef enum {
 
 typedef enum { BL_F32 = 0, BL_BF16 = 1 } bl_dtype;
 
-/* K limit: 64 * 127 * K must fit in int32 (the kernels accumulate 64 * acc). */
+/* K limit: 64 * 127 * K must fit in int32.  The kernels feed the int8 matrix unit the codes as
+ * 64 * c (one shift and one mask per four weights, see the layout above) and divide the int32
+ * sum by 64 at the end, so the bound is 64 * 127 * K < 2^31, not 127 * K < 2^31. */
 #define BL_MAX_K 262144
 /* M and N limit (row counts are held in 32-bit integers inside the kernels). */
 #define BL_MAX_ROWS 2147483647LL
@@ -93,6 +100,10 @@ int bitlinear_abi_version(void);
  * BL_ERR_ALIGN, BL_ERR_WORKSPACE.
  * ------------------------------------------------------------------------------------- */
 size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K);
+
+/* The same size under the name this library's first specification gave the query (the
+ * workspace holds per-tensor partial sums, so the size does not depend on N or K). */
+size_t bitlinear_workspace_bytes(int64_t N, int64_t K);
 
 bl_status bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, uint32_t *W_packed,
                                      float *gamma, void *workspace, size_t workspace_bytes,

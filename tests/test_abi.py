@@ -70,6 +70,7 @@ def test_status_strings(L):
 def test_quantize_weights_validation(L):
     ws = L.bitlinear_quantize_weights_workspace(64, 64)
     assert ws >= 8
+    assert L.bitlinear_workspace_bytes(64, 64) == ws == L.bitlinear_workspace_bytes(9728, 2560)
     q = L.bitlinear_quantize_weights
     assert q(None, 4, 64, B, C, D, ws, None) == BL_ERR_NULL
     assert q(A, 4, 64, None, C, D, ws, None) == BL_ERR_NULL
