@@ -147,6 +147,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_quantize_weights_grouped_workspace.restype = SZ
     L.bitlinear_quantize_weights_grouped.argtypes = [P, ctypes.c_int, P, SZ, P]
     L.bitlinear_quantize_weights_grouped.restype = ctypes.c_int
+    L.bitlinear_quantize_weights_grouped_noalloc.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_quantize_weights_grouped_noalloc.restype = ctypes.c_int
     L.bitlinear_pack_codes.argtypes = [P, I64, I64, P, P]
     L.bitlinear_pack_codes.restype = ctypes.c_int
     L.bitlinear_quantize_acts.argtypes = [P, ctypes.c_int, I64, I64, P, ctypes.c_float, P, P, P]
@@ -269,6 +271,23 @@ def quantize_weights_grouped(Ws: Sequence[torch.Tensor],
                                                     workspace.numel() * workspace.element_size(),
                                                     _stream(stream)))
     return outs
+
+
+def quantize_weights_grouped_noalloc(Ws: Sequence[torch.Tensor],
+                                     outputs: Sequence[Tuple[torch.Tensor, torch.Tensor]],
+                                     stream=None) -> None:
+    """The grouped weight quantization into caller-provided outputs with no workspace (the
+    library's fixed scratch holds the partial sums; calls overlapping on one GPU race)."""
+    count = len(Ws)
+    arr = (_WeightProblem * max(count, 1))()
+    for i, W in enumerate(Ws):
+        _dev(W, f"W[{i}]", torch.float32)
+        N, K = W.shape
+        P, g = outputs[i]
+        arr[i] = _WeightProblem(_ptr(W), _ptr(P), _ptr(g), N, K)
+    _check("bitlinear_quantize_weights_grouped_noalloc",
+           lib().bitlinear_quantize_weights_grouped_noalloc(ctypes.addressof(arr), count,
+                                                            _stream(stream)))
 
 
 def pack_codes(codes: torch.Tensor, W_packed: Optional[torch.Tensor] = None,

@@ -4,6 +4,8 @@
 // the host before anything is launched, so a rejected call touches no device memory.
 #include <limits.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace {
@@ -120,6 +122,42 @@ bl_forward_ex_problem to_ex(const bl_forward_problem &p)
 }
 
 bl_status from_hip(hipError_t e) { return e == hipSuccess ? BL_OK : BL_ERR_HIP; }
+
+// ---- fixed scratch of the allocation-free weight quantization
+//
+// The γ pass's fp64 partial sums (2 KiB per tensor) for a grouped call of up to BL_MAX_GROUP
+// tensors, in a device array of the library instead of a caller-provided workspace.  Each GPU
+// holds its own copy at its own address, for as long as the process lives.  In host code the
+// array's name is only a stand-in for the symbol: its device address is looked up once per
+// device (with that device current) and only that address is handed to kernels.
+constexpr size_t kScratchBytes = (size_t)BL_MAX_GROUP * 256 * sizeof(double);
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on device `dev`, or NULL if it cannot be had.
+void *scratch_address(int dev)
+{
+    static std::mutex mu;
+    static void *addr[kScratchDevices] = {};
+    if (dev < 0 || dev >= kScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess)
+            return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess)
+            return nullptr;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev)
+            (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            return nullptr;
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
 
 // Validated problems -> launches: act quant of any form in one call.
 bl_status run_acts(const bl_act_ex_problem *q, int count, void *stream)
@@ -343,6 +381,31 @@ bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, 
         return BL_ERR_WORKSPACE;
     return from_hip(bl::launch_quantize_weights(problems, count, workspace,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_quantize_weights_grouped_noalloc(const bl_weight_problem *problems, int count,
+                                                     void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    for (int i = 0; i < count; ++i) {
+        bl_status s = check_weight(problems[i]);
+        if (s != BL_OK)
+            return s;
+    }
+    if (bl::quantize_weights_workspace(count) > kScratchBytes)
+        return BL_ERR_WORKSPACE;      // more partial sums than the fixed scratch holds
+    // The scratch of the device the stream belongs to (NULL: the current device).
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return BL_ERR_HIP;
+    void *ws = scratch_address(dev);
+    if (!ws)
+        return BL_ERR_HIP;
+    return from_hip(bl::launch_quantize_weights(problems, count, ws, st));
 }
 
 bl_status bitlinear_quantize_weights(const float *W, int64_t N, int64_t K, uint32_t *W_packed,

@@ -126,6 +126,20 @@ bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, 
                                              void *workspace, size_t workspace_bytes,
                                              void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): bitlinear_quantize_weights_grouped
+ * without a workspace argument.  The partial sums go to a fixed scratch array inside the
+ * library (2 KiB per tensor, room for BL_MAX_GROUP tensors: 32 KiB per GPU, held until the
+ * process ends); the call allocates nothing.  Every call on one GPU shares that GPU's array,
+ * so two such calls that overlap on one GPU (different streams, or host threads) race and
+ * must be serialized by the caller; a call writes every partial sum it reads, so nothing has
+ * to be cleared between calls.  Results are bit for bit those of
+ * bitlinear_quantize_weights_grouped.  Errors: as for bitlinear_quantize_weights_grouped
+ * (BL_ERR_WORKSPACE if the call needed more partial sums than the scratch holds), and
+ * BL_ERR_HIP if the stream's device or the scratch's address cannot be had. */
+bl_status bitlinear_quantize_weights_grouped_noalloc(const bl_weight_problem *problems, int count,
+                                                     void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * Step 2 for weights that are already ternary (pre-ternarized checkpoints): pack int8 codes.
  *

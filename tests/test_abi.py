@@ -67,6 +67,22 @@ def test_status_strings(L):
     assert L.bitlinear_abi_version() == 102
 
 
+def test_quantize_weights_noalloc_validation(L, bl):
+    q = L.bitlinear_quantize_weights_grouped_noalloc
+    arr = (bl._WeightProblem * 2)()
+    arr[0] = bl._WeightProblem(A, B, C, 4, 64)
+    arr[1] = bl._WeightProblem(A, B, C, 4, 64)
+    assert q(None, 1, None) == BL_ERR_NULL
+    assert q(ctypes.addressof(arr), 0, None) == BL_ERR_COUNT
+    assert q(ctypes.addressof(arr), 17, None) == BL_ERR_COUNT
+    arr[1] = bl._WeightProblem(A, B, C, 4, 24)
+    assert q(ctypes.addressof(arr), 2, None) == BL_ERR_SHAPE
+    arr[1] = bl._WeightProblem(A + 4, B, C, 4, 64)
+    assert q(ctypes.addressof(arr), 2, None) == BL_ERR_ALIGN
+    arr[1] = bl._WeightProblem(None, B, C, 4, 64)
+    assert q(ctypes.addressof(arr), 2, None) == BL_ERR_NULL
+
+
 def test_quantize_weights_validation(L):
     ws = L.bitlinear_quantize_weights_workspace(64, 64)
     assert ws >= 8
