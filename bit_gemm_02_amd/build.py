@@ -36,14 +36,15 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def build(verbose: bool = False, output: str = LIBRARY, extra_flags=(), extra_link_flags=()) -> str:
+    """Compile every source and link the shared library (to `output`, with `extra_flags` on
+    every compile line and `extra_link_flags` on the link line); returns its path."""
     with tempfile.TemporaryDirectory(prefix="bitlinear_build_") as tmp:
         objs = [os.path.join(tmp, src.replace(".hip", ".o")) for src in SOURCES]
 
         def compile_one(src_obj):
             src, obj = src_obj
-            cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             return src, subprocess.run(cmd, capture_output=True, text=True)
@@ -54,13 +55,13 @@ def build(verbose: bool = False) -> str:
             for src, r in pool.map(compile_one, zip(SOURCES, objs)):
                 if r.returncode != 0:
                     raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
-        tmp_lib = LIBRARY + ".tmp"
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        tmp_lib = output + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra_link_flags, *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-        os.replace(tmp_lib, LIBRARY)
-    return LIBRARY
+        os.replace(tmp_lib, output)
+    return output
 
 
 if __name__ == "__main__":
