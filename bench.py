@@ -61,6 +61,12 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-calibration run into profiles/traffic.json")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 --pmc counter_collection.csv files (one per counter pass) "
+                         "into a per-kernel table of MFMA utilisation, instruction mix, waits, LDS "
+                         "bank conflicts and cache figures")
+    ap.add_argument("--simds", type=int, default=1024,
+                    help="SIMDs of the profiled GPU, for --summarize-counters (MI355X: 256 x 4)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole layer chain (six launches per layer, residuals and the "
                          "FFN activation included) instead of the step; prints its own JSON line")
@@ -373,14 +379,64 @@ def interval_ms(ev, a, b):
 # Kernel name fragment -> (roofline key, source file).  (The decode leg quantizes its
 # activations inside decode_kernel, so every act_quant launch belongs to the prefill leg.)
 KERNELS = {
-    "mixed_kernel": ("prefill_and_decode", "mixed.hip+prefill_core.hpp+decode_core.hpp"),
-    "prefill_kernel": ("prefill_gemm", "prefill.hip+prefill_core.hpp"),
-    "decode_kernel": ("decode_linear", "decode.hip+decode_core.hpp"),
-    "act_quant": ("act_quant_prefill", "quant.hip"),
-    "gamma_partial_kernel": ("weight_quant", "quant.hip"),
-    "gamma_act_kernel": ("gamma_and_act_quant", "quant.hip"),
-    "quant_pack_kernel": ("weight_quant", "quant.hip"),
+    "mixed_kernel": ("prefill_and_decode", "mixed.hip+prefill_core.hpp+decode_core.hpp+common.hpp"),
+    "prefill_kernel": ("prefill_gemm", "prefill.hip+prefill_core.hpp+common.hpp"),
+    "gemv_kernel": ("decode_linear", "gemv.hip+decode_core.hpp+common.hpp"),
+    "decode_kernel": ("decode_linear", "decode.hip+decode_core.hpp+common.hpp"),
+    "act_quant": ("act_quant_prefill", "quant.hip+common.hpp"),
+    "gamma_partial_kernel": ("weight_quant", "quant.hip+common.hpp"),
+    "gamma_act_kernel": ("gamma_and_act_quant", "quant.hip+common.hpp"),
+    "quant_pack_kernel": ("weight_quant", "quant.hip+common.hpp"),
 }
+
+# Derived per-kernel figures from hardware counters (per dispatch, averaged over dispatches).
+# SIMDs = compute units x 4; MfmaUtil as rocprofv3 defines it.
+COUNTER_FIGURES = [
+    ("MFMA busy (% of SIMD-cycles)",
+     lambda c, simds: 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds)),
+    ("VALU instructions per MFMA", lambda c, simds: c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]),
+    ("LDS instructions per MFMA", lambda c, simds: c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]),
+    ("waves waiting (% of wave-cycles)", lambda c, simds: 100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("LDS bank-conflict cycles per LDS-active cycle",
+     lambda c, simds: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]),
+    ("VALU active (% of wave-cycles)", lambda c, simds: 100.0 * c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"]),
+    ("vector-memory reads per wave", lambda c, simds: c["SQ_INSTS_VMEM_RD"] / c["SQ_WAVES"]),
+    ("vector-memory writes per wave", lambda c, simds: c["SQ_INSTS_VMEM_WR"] / c["SQ_WAVES"]),
+    ("mean waves in flight per CU", lambda c, simds: c["SQ_WAVE_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds / 4)),
+    ("L2 hit rate (%)", lambda c, simds: 100.0 * c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
+    ("TA busy (% of GPU-active cycles, mean over TAs)", lambda c, simds: 100.0 * c["TA_BUSY_avr"] / c["GRBM_GUI_ACTIVE"]),
+]
+
+
+def summarize_counters(paths, simds: int) -> str:
+    """Markdown table of COUNTER_FIGURES per library kernel from rocprofv3 --pmc CSV files
+    (counter_collection.csv; one file per counter pass of the same command)."""
+    import csv
+    from collections import defaultdict
+    sums = defaultdict(lambda: defaultdict(float))   # kernel -> counter -> sum over dispatches
+    dispatches = defaultdict(lambda: defaultdict(set))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            frag = next((f for f in KERNELS if f in name), None)
+            if frag is None:
+                continue
+            key = name.split("(")[0].replace("void ", "")
+            sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
+            dispatches[key][r["Counter_Name"]].add(r["Dispatch_Id"])
+    lines = ["| kernel | dispatches | " + " | ".join(n for n, _ in COUNTER_FIGURES) + " |",
+             "|---|---|" + "---|" * len(COUNTER_FIGURES)]
+    for key in sorted(sums):
+        c = {k: v / max(1, len(dispatches[key][k])) for k, v in sums[key].items()}
+        vals = []
+        for _, f in COUNTER_FIGURES:
+            try:
+                vals.append(f"{f(c, simds):.3g}")
+            except (KeyError, ZeroDivisionError):
+                vals.append("")
+        n = max(len(d) for d in dispatches[key].values())
+        lines.append(f"| `{key}` | {n} | " + " | ".join(vals) + " |")
+    return "\n".join(lines)
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
@@ -768,6 +824,9 @@ def train_bench(torch, bl, wl: workloads.Workload, M: int, reps: int):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.simds))
+        return
     if args.summarize_pmc:
         cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 "
                f"bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline "

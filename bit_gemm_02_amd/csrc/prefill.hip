@@ -7,10 +7,10 @@
 // packed 2-bit words (0.25 B per weight) travel to LDS and are expanded to int8 in registers
 // right before the multiply (plane64: one shift and one mask per four weights, giving 64 * c).
 //
-// Block tile BM (tokens) x BN (weight rows), 256 x 256 with 8 waves (4 x 2) or 128 x 128
-// with 4 waves (2 x 2); each wave owns a (BM/WM) x (BN/WN) sub-tile of 16 x 16 MFMA tiles.
-// The K loop runs in stages of KS = 128 weights through a ring of NST LDS buffers (4 for the
-// large tile, 3 for the small one):
+// Block tile BM (tokens) x BN (weight rows), 128 x 256 with 4 waves side by side in N (large
+// grids; two blocks per CU) or 128 x 128 with 4 waves (2 x 2); each wave owns a (BM/WM) x
+// (BN/WN) sub-tile of 16 x 16 MFMA tiles.  The K loop runs in stages of KS = 128 weights
+// through a ring of NST = 3 LDS buffers:
 // activation rows (BM x 128 bytes) and packed weight rows (BN x 32 bytes) go global -> LDS
 // by gfx950 direct-to-LDS buffer loads, NST - 1 stages in flight while one is multiplied,
 // one barrier per stage.  Per stage and lane (r = l % 16, g = l / 16): the packed words of its
@@ -22,7 +22,7 @@
 namespace bl {
 
 template <class T, bool FULL_K>
-__global__ __launch_bounds__(T::THREADS) void prefill_kernel(PreBatch b)
+__global__ __launch_bounds__(T::THREADS, T::WPE) void prefill_kernel(PreBatch b)
 {
     prefill_block<T, FULL_K>(b, blockIdx.x);
 }

@@ -35,9 +35,10 @@ struct PreBatch {
 // Tile configuration: BM x BN block tile split over WM x WN waves (wave tile BM/WM x BN/WN,
 // MFMA tiles 16 x 16), KS weights of K per pipeline stage, NST stages in LDS, EA bytes per
 // activation (1: int8 codes on the int8 matrix unit; 2: bf16 activations on the bf16 one).
-template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_, int EA_ = 1>
+template <int BM_, int BN_, int WM_, int WN_, int KS_, int NST_, int EA_ = 1, int WPE_ = 1>
 struct Tile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KS = KS_, NST = NST_, EA = EA_;
+    static constexpr int WPE = WPE_;                     // waves per SIMD the registers must allow
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = WAVES * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;     // wave tile
@@ -446,7 +447,13 @@ static int build_batch(const bl_forward_ex_problem *q, int count, PreBatch &b, b
     return blocks;
 }
 
-using TileBig = Tile<256, 256, 4, 2, 128, 4>;    // 160 KB LDS, one block (8 waves) per CU
+// Large grids: 128 tokens x 256 weight rows, four waves side by side in N (each wave 128
+// tokens x 64 rows: 8 x 4 MFMA tiles, so each expanded weight word feeds eight MFMAs), a 3-stage
+// 72 KB ring and registers for two waves per SIMD: two blocks per CU, so one block's epilogue
+// (fp32 stores) and pipeline fill overlap the other's products.  Measured on the Qwen3-4B set
+// against 256 x 256 tiles with one 160 KB block per CU (4 x 2 waves: 770 us; 2 x 4 waves:
+// 735 us) and 128 x 256 with 2 x 2 waves (746 us): 710-723 us.
+using TileBig = Tile<128, 256, 1, 4, 128, 3, 1, 2>;
 // Small tiles: a 3-stage ring (60 KB LDS, two blocks per CU) measured faster than 4 stages
 // (80 KB, c2 product 27.3 -> 25.9 us) and than 2 stages (40 KB, four blocks per CU).
 using TileSmall = Tile<128, 128, 2, 2, 128, 3>;
