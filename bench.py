@@ -67,6 +67,8 @@ def parse():
                          "bank conflicts and cache figures")
     ap.add_argument("--simds", type=int, default=1024,
                     help="SIMDs of the profiled GPU, for --summarize-counters (MI355X: 256 x 4)")
+    ap.add_argument("--xcds", type=int, default=8,
+                    help="XCDs of the profiled GPU (GRBM_GUI_ACTIVE is summed over them)")
     ap.add_argument("--layer", action="store_true",
                     help="time the whole layer chain (six launches per layer, residuals and the "
                          "FFN activation included) instead of the step; prints its own JSON line")
@@ -390,25 +392,28 @@ KERNELS = {
 }
 
 # Derived per-kernel figures from hardware counters (per dispatch, averaged over dispatches).
-# SIMDs = compute units x 4; MfmaUtil as rocprofv3 defines it.
+# `cyc` = GPU-active cycles of one XCD (GRBM_GUI_ACTIVE is summed over the XCDs); SQ_WAVE_CYCLES
+# and SQ_WAIT_INST_ANY count in units of four cycles; MFMA instructions are among the VALU
+# instructions SQ_INSTS_VALU counts.
 COUNTER_FIGURES = [
     ("MFMA busy (% of SIMD-cycles)",
-     lambda c, simds: 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds)),
-    ("VALU instructions per MFMA", lambda c, simds: c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]),
-    ("LDS instructions per MFMA", lambda c, simds: c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]),
-    ("waves waiting (% of wave-cycles)", lambda c, simds: 100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
-    ("LDS bank-conflict cycles per LDS-active cycle",
-     lambda c, simds: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]),
-    ("VALU active (% of wave-cycles)", lambda c, simds: 100.0 * c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"]),
-    ("vector-memory reads per wave", lambda c, simds: c["SQ_INSTS_VMEM_RD"] / c["SQ_WAVES"]),
-    ("vector-memory writes per wave", lambda c, simds: c["SQ_INSTS_VMEM_WR"] / c["SQ_WAVES"]),
-    ("mean waves in flight per CU", lambda c, simds: c["SQ_WAVE_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * simds / 4)),
-    ("L2 hit rate (%)", lambda c, simds: 100.0 * c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
-    ("TA busy (% of GPU-active cycles, mean over TAs)", lambda c, simds: 100.0 * c["TA_BUSY_avr"] / c["GRBM_GUI_ACTIVE"]),
+     lambda c, simds, cyc: 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)),
+    ("VALU instructions per MFMA (MFMA included)", lambda c, simds, cyc: c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"]),
+    ("LDS instructions per MFMA", lambda c, simds, cyc: c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]),
+    ("waves waiting (% of wave time)", lambda c, simds, cyc: 100.0 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]),
+    ("mean waves resident per CU", lambda c, simds, cyc: 4.0 * c["SQ_WAVE_CYCLES"] / (cyc * simds / 4)),
+    ("LDS bank-conflict cycles per LDS instruction",
+     lambda c, simds, cyc: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"]),
+    ("LDS bank-conflict cycles (% of CU-cycles)",
+     lambda c, simds, cyc: 100.0 * c["SQ_LDS_BANK_CONFLICT"] / (cyc * simds / 4)),
+    ("vector-memory reads per wave", lambda c, simds, cyc: c["SQ_INSTS_VMEM_RD"] / c["SQ_WAVES"]),
+    ("vector-memory writes per wave", lambda c, simds, cyc: c["SQ_INSTS_VMEM_WR"] / c["SQ_WAVES"]),
+    ("L2 hit rate (%)", lambda c, simds, cyc: 100.0 * c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])),
+    ("TA busy (% of cycles, mean over TAs)", lambda c, simds, cyc: 100.0 * c["TA_BUSY_avr"] / cyc),
 ]
 
 
-def summarize_counters(paths, simds: int) -> str:
+def summarize_counters(paths, simds: int, xcds: int) -> str:
     """Markdown table of COUNTER_FIGURES per library kernel from rocprofv3 --pmc CSV files
     (counter_collection.csv; one file per counter pass of the same command)."""
     import csv
@@ -423,18 +428,19 @@ def summarize_counters(paths, simds: int) -> str:
                 continue
             key = name.split("(")[0].replace("void ", "")
             sums[key][r["Counter_Name"]] += float(r["Counter_Value"])
-            dispatches[key][r["Counter_Name"]].add(r["Dispatch_Id"])
+            dispatches[key][r["Counter_Name"]].add((path, r["Dispatch_Id"]))
     lines = ["| kernel | dispatches | " + " | ".join(n for n, _ in COUNTER_FIGURES) + " |",
              "|---|---|" + "---|" * len(COUNTER_FIGURES)]
     for key in sorted(sums):
         c = {k: v / max(1, len(dispatches[key][k])) for k, v in sums[key].items()}
+        cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
         vals = []
         for _, f in COUNTER_FIGURES:
             try:
-                vals.append(f"{f(c, simds):.3g}")
+                vals.append(f"{f(c, simds, cyc):.3g}")
             except (KeyError, ZeroDivisionError):
                 vals.append("")
-        n = max(len(d) for d in dispatches[key].values())
+        n = max(len({i for _, i in d}) for d in dispatches[key].values())
         lines.append(f"| `{key}` | {n} | " + " | ".join(vals) + " |")
     return "\n".join(lines)
 
@@ -472,7 +478,10 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -
         for name, grid, kib in d.values():
             for frag, (key, src) in KERNELS.items():
                 if frag in name:
+                    if key == "decode_linear" and name.split("(")[0].endswith("true>"):
+                        key = "decode_linear_b3"      # the one-token kernel on base-3 rows
                     acc[(key, src)].append((name, kib * 1024.0 * factor))
+                    break
         return acc
 
     fk, wk = by_kernel(fetch, f_fetch), by_kernel(write, f_write)
@@ -825,11 +834,11 @@ def train_bench(torch, bl, wl: workloads.Workload, M: int, reps: int):
 def main():
     args = parse()
     if args.summarize_counters:
-        print(summarize_counters(args.summarize_counters, args.simds))
+        print(summarize_counters(args.summarize_counters, args.simds, args.xcds))
         return
     if args.summarize_pmc:
         cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 "
-               f"bench.py --workload {args.workload} --steps 5 --warmup 2 --no-cpu-baseline "
+               f"bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline "
                "--copy-calibration")
         rec = summarize_pmc(*args.summarize_pmc, args.workload, cmd)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
