@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -80,12 +81,18 @@ def parse():
     return ap.parse_args()
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def source_hash(names: str) -> str:
-    """Hash of the sources a kernel is built from ("a.hip+b.hpp": every file, in order)."""
+    """Hash of the code a kernel is built from ("a.hip+b.hpp": every file, in order), with
+    comments and whitespace runs taken out, so that counters stay attached to a kernel whose
+    comments alone changed."""
     h = hashlib.sha256()
     for name in names.split("+"):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            code = _COMMENT.sub(" ", f.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -245,8 +252,9 @@ class Setup:
     # Work accounting (algorithmic, what the method must move or compute).
     def mixed_one_launch(self) -> bool:
         """Whether bitlinear_forward_mixed runs the step's products and decode leg as one launch:
-        every product has more than 16 tokens on 128 x 128 tiles (fewer than 512 tiles of
-        256 x 256), and the decode calls are fused with one activation dtype (always here)."""
+        every product has more than 16 tokens on 128 x 128 tiles (fewer than 512 units of
+        256 x 256 outputs; larger sets take 128 x 256 tiles), and the decode calls are fused
+        with one activation dtype (always here)."""
         big = sum(-(-self.M_pre // 256) * -(-m.N // 256) for m in self.wl.matrices)
         return self.M_pre > 16 and big < 512 and self.M_dec <= 4
 
@@ -313,7 +321,7 @@ class Setup:
                                            self._addr(self.lin_dec_tables[rd]), n, stream)
             assert rc == 0, rc
         else:
-            # 256 x 256 product tiles: the products, then the decode leg (the two launches the
+            # 128 x 256 product tiles: the products, then the decode leg (the two launches the
             # mixed call makes for such a batch, made here so each can be bracketed).
             rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
             assert rc == 0, rc
@@ -984,7 +992,7 @@ def main():
                                         "of W is the minimum, the two launches read it twice)")
     # Dominant kernel = the step's largest single launch: the products' launch (with the decode
     # blocks when the mixed call shares one launch; the product alone where it cannot, with
-    # 256 x 256 tiles).  The quantization call is two launches (gamma + activation codes, then
+    # 128 x 256 tiles).  The quantization call is two launches (gamma + activation codes, then
     # the pack pass), each shorter.
     fused = setup.mixed_one_launch()
     dom = "prefill_and_decode" if fused else "prefill_gemm"
@@ -1035,7 +1043,7 @@ def main():
         "rooflines": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in rooflines.items()},
         "timing": {"ms_per_step_wall": round(wall_ms, 4),
-                   "mixed_launch": "one launch" if fused else "two launches (256 x 256 product tiles)",
+                   "mixed_launch": "one launch" if fused else "two launches (128 x 256 product tiles)",
                    "ms_per_step_with_launch_events": round(ms_with_events, 4),
                    "schedule": "one stream, launches in step order: weight quantization, "
                                "activation quantization, then the prefill products and the decode "

@@ -478,8 +478,8 @@ inline int tile_override()
     return v;
 }
 
-// Large tiles (half the LDS and cache traffic per operation) when they still give every
-// compute unit at least two tiles; otherwise 128 x 128.
+// Large (128 x 256) tiles when the set is big: at least 512 units of 256 x 256 outputs, so
+// every compute unit still gets several tiles; otherwise 128 x 128.
 inline bool prefill_big_tiles(const bl_forward_ex_problem *q, int count)
 {
     switch (tile_override()) {

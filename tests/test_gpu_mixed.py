@@ -10,7 +10,7 @@ inputs; and both sets checked against the CPU oracle: prefill entries sampled on
 ragged sizes (K not a multiple of the 128-wide prefill stage or of the 256-wide decode step,
 N not a multiple of the tile), bf16 decode activations with a norm, empty problems, and the
 cases that take the two-launch path (a prefill product of at most 16 tokens, a decode call
-past the fused size, mixed decode dtypes, a prefill set large enough for 256 x 256 tiles,
+past the fused size, mixed decode dtypes, a prefill set large enough for 128 x 256 tiles,
 one set empty).
 """
 
@@ -249,7 +249,7 @@ def test_mixed_two_launch_cases(torch, bl, orc, case):
     elif case == "mixed_dtypes":
         dec_specs = dec_specs + [(2, 100, 512, "bf16", False)]
     elif case == "big_tiles":
-        pre_specs = [(4096, 8192, 128)]          # 512 tiles of 256 x 256
+        pre_specs = [(4096, 8192, 128)]          # 512 units of 256 x 256: 128 x 256 tiles
     elif case == "prefill_only":
         dec_specs = []
     elif case == "decode_only":
