@@ -52,6 +52,11 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t offset)
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)offset, 0, 0);
 }
 
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t offset, v4u value)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(value, r, (int)offset, 0, 0);
+}
+
 // Bytes of rows [r0, min(r0 + rows, R)) of a row-major matrix with `row_bytes` per row.
 __device__ __forceinline__ uint32_t rows_bytes(int r0, int rows, int R, int row_bytes)
 {

@@ -296,6 +296,110 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
             dw[ni] = wq[ni][LPW - 1];
     };
 
+    // The int8 product as a rolling pipeline of units.  A unit (stage t, k-step j, row block
+    // mi) is the NI MFMAs of one activation fragment with the NI expanded weight words of step
+    // j; right after them the fragment's registers are refilled with the fragment the next
+    // unit of that row block needs (step j + 1, or step 0 of stage t + 1), so every LDS read
+    // is issued MI units (MI * NI MFMAs) before its use, with no registers beyond one fragment
+    // per row block.  Stage t + 1 is entered in the middle of stage t's last step, after unit
+    // X: by then every read of stage t has been issued for X units (and has returned at the
+    // lgkmcnt(0) wait), the wait for stage t + 1's loads and the barrier follow, then the
+    // refill of stage t's buffer and the first reads of stage t + 1, which the remaining
+    // MI - X units of stage t (operands already in registers) cover.  (The compiler, left to
+    // schedule the deferred-step form below, sank the reads behind the MFMAs and waited for
+    // each read right after issuing it.)  Used for the 128 x 256 tile (MI = 8: four units of
+    // cover on each side of the barrier; the Qwen3-1.7B set at 4096 tokens: 176-184 -> 171 us,
+    // the Qwen3-4B set at 8192 tokens unchanged); the 128 x 128 tile (MI = 4, two units)
+    // measured about 1 us slower with it on the Distillix-125M set at 2048 tokens and keeps
+    // the deferred-step form.
+    auto rolling_pipeline = [&](auto &acc_) {
+        constexpr int X = MI / 2;
+        v4i a[MI];
+        v4i bw[NI];
+        uint32_t wq[NI][LPW];
+        auto read_w = [&](const unsigned char *st) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const unsigned char *src = st + brow + ni * 16 * WROW;
+                if constexpr (LPW == 4) {
+                    const v4u v = *reinterpret_cast<const v4u *>(src);
+                    wq[ni][0] = v.x; wq[ni][1] = v.y; wq[ni][2] = v.z; wq[ni][3] = v.w;
+                } else if constexpr (LPW == 2) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(src);
+                    wq[ni][0] = v.x; wq[ni][1] = v.y;
+                } else {
+                    wq[ni][0] = *reinterpret_cast<const uint32_t *>(src);
+                }
+            }
+        };
+        auto read_a1 = [&](const unsigned char *st, int j, int mi) {
+            const int pos = 16 * ((g * LPW + j) ^ aswz);
+            a[mi] = *reinterpret_cast<const v4i *>(st + arow + mi * 16 * XROW + pos);
+        };
+        auto unpack_b = [&](int j) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                bw[ni] = unpack_word64(wq[ni][j]);
+        };
+        // Enter stage tn (buffer S): its loads have landed in every wave, every LDS read of
+        // the buffer refilled next has returned; refill it, read the stage's weight words and
+        // the fragments of row blocks 0 .. X-1 (whose registers are free by now).
+        auto enter = [&](auto S, int tn) {
+            wait_stage<(NST - 2) * T::LOADS>();
+            block_sync();
+            issue(IC<(decltype(S)::value + NST - 1) % NST>{}, tn + NST - 1);
+            const unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
+            read_w(st);
+#pragma unroll
+            for (int mi = 0; mi < X; ++mi)
+                read_a1(st, 0, mi);
+        };
+
+        static_for<0, NST - 1>([&](auto S) { issue(S, S.value); });
+        enter(IC<0>{}, 0);
+        {
+            const unsigned char *st0 = stage_buf<0, T::STAGE>();
+#pragma unroll
+            for (int mi = X; mi < MI; ++mi)
+                read_a1(st0, 0, mi);
+        }
+        unpack_b(0);
+        // Unrolled by NST so that every buffer is a compile-time choice.  Past the last stage
+        // the same steps run on a dead stage (zeros loaded, reads unused), without branches.
+        for (int t0 = 0; t0 < stages; t0 += NST) {
+            static_for<0, NST>([&](auto S) {
+                constexpr int SN = (decltype(S)::value + 1) % NST;
+                const int t = t0 + S.value;
+                if (t < stages) {
+                    const unsigned char *st = stage_buf<decltype(S)::value, T::STAGE>();
+                    const unsigned char *sn = stage_buf<SN, T::STAGE>();
+#pragma unroll
+                    for (int j = 0; j < LPW; ++j) {
+#pragma unroll
+                        for (int mi = 0; mi < MI; ++mi) {
+                            if (j == LPW - 1 && mi == X)
+                                enter(IC<SN>{}, t + 1);
+                            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                            for (int ni = 0; ni < NI; ++ni)
+                                acc_[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bw[ni], a[mi], acc_[mi][ni],
+                                                                                    0, 0, 0);
+                            if (j < LPW - 1)
+                                read_a1(st, j + 1, mi);
+                            else if (mi >= X)
+                                read_a1(sn, 0, mi);
+                            if (mi == MI - 1)
+                                unpack_b(j < LPW - 1 ? j + 1 : 0);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+            });
+        }
+        // Dead stages issued past the end land before the block ends.
+        __builtin_amdgcn_s_waitcnt((0 & 15) | (0 << 14) | (7 << 4) | (15 << 8));
+    };
+
     // Row scales and gamma, loaded before the pipeline starts: older than every stage load,
     // they have landed by the first stage wait, and the epilogue does not wait on memory.
     float sxv[MI];
@@ -309,6 +413,9 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
     }
     const float gammaf = __uint_as_float(buf_load4(make_rsrc(p.gamma, 4u), 0u));
 
+    if constexpr (!BF && MI >= 8) {
+        rolling_pipeline(acc);
+    } else {
     // Prologue: stages 0 .. NST-2 in flight.
     static_for<0, NST - 1>([&](auto S) { issue(S, S.value); });
     // Main loop, unrolled by NST so every stage buffer is a compile-time choice.  Stage t has
@@ -327,6 +434,7 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
         });
     }
     mfma_step(dw, da);              // the last stage's deferred k-step
+    }
 
     // Epilogue.  The MFMA takes the weights as its row operand, so acc[mi][ni] register v
     // holds 64 * D[m][n] for m = m0 + wm * TM + mi * 16 + r and n = n0 + wn * TN + ni * 16 +
@@ -359,6 +467,31 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
         return;
     } else {
     const double gamma = (double)gammaf;
+    // A full 128 x 256 tile with neither residual nor int32 copy (every tile of a product
+    // whose M and N are multiples of the tile): straight-line code, one 16-byte buffer store
+    // per four outputs at a 32-bit offset from the tile's first row.  The general form below,
+    // with its per-group branches and 64-bit addresses, measured 6-7 us per such tile whether
+    // or not it stored anything (the unrolled code is large and runs once per tile); this one
+    // 2.3 us plus the stores' drain.  (The 128 x 128 tile measured about 1 us slower per
+    // product with it and keeps the general form.)
+    if (MI >= 8 && !p.R && !p.acc && m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0 &&
+        ((uintptr_t)p.Y & 15) == 0 && (int64_t)BM * p.N * 4 <= (int64_t)0xFFFFFFFFu) {
+        const rsrc_t yres = make_rsrc(p.Y + (int64_t)m0 * p.N, (uint32_t)BM * (uint32_t)p.N * 4u);
+        const uint32_t col = (uint32_t)(n0 + wn * T::TN + 4 * g) * 4u;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const double scale = gamma * (double)sxv[mi];
+            const uint32_t roff = (uint32_t)(wm * T::TM + mi * 16 + r) * (uint32_t)p.N * 4u + col;
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                v4u y;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    y[v] = __float_as_uint((float)((double)(acc[mi][ni][v] >> 6) * scale));
+                buf_store16(yres, roff + (uint32_t)(ni * 16 * 4), y);
+            }
+        }
+    } else {
     const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0 &&
                      (!p.acc || ((uintptr_t)p.acc & 15) == 0) &&
                      (!p.R || ((uintptr_t)p.R & 15) == 0);
@@ -403,6 +536,7 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
                 }
             }
         }
+    }
     }
     }
 }
@@ -455,7 +589,7 @@ static int build_batch(const bl_forward_ex_problem *q, int count, PreBatch &b, b
 // 735 us) and 128 x 256 with 2 x 2 waves (746 us): 710-723 us.
 using TileBig = Tile<128, 256, 1, 4, 128, 3, 1, 2>;
 // Small tiles: a 3-stage ring (60 KB LDS, two blocks per CU) measured faster than 4 stages
-// (80 KB, c2 product 27.3 -> 25.9 us) and than 2 stages (40 KB, four blocks per CU).
+// (80 KB, Distillix-125M set at 2048 tokens: 27.3 -> 25.9 us) and than 2 stages (40 KB, four blocks per CU).
 using TileSmall = Tile<128, 128, 2, 2, 128, 3>;
 
 // The weight-only product with bf16 activations (the W1.58.A16 forward and the input gradient
