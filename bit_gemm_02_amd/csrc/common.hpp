@@ -57,6 +57,13 @@ __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t offset, v4u value
     __builtin_amdgcn_raw_buffer_store_b128(value, r, (int)offset, 0, 0);
 }
 
+// The same with the non-temporal policy, for output written once and not read back by the
+// launch: it is not kept in the caches (evicting operands other blocks still read).
+__device__ __forceinline__ void buf_store16_nt(rsrc_t r, uint32_t offset, v4u value)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(value, r, (int)offset, 0, 2);
+}
+
 // Bytes of rows [r0, min(r0 + rows, R)) of a row-major matrix with `row_bytes` per row.
 __device__ __forceinline__ uint32_t rows_bytes(int r0, int rows, int R, int row_bytes)
 {
