@@ -467,8 +467,8 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
         return;
     } else {
     const double gamma = (double)gammaf;
-    // A full 128 x 256 tile with neither residual nor int32 copy (every tile of a product
-    // whose M and N are multiples of the tile): straight-line code with whole-line,
+    // A full tile with neither residual nor int32 copy (every tile of a product whose M and
+    // N are multiples of the tile): straight-line code with whole-line,
     // non-temporal stores.  Lane (r, g) holds four consecutive outputs of row r for each
     // 16-column group ni; the pieces of the column groups 2p and 2p + 1 are exchanged between
     // lanes r and r ^ 8 (one DPP rotation by 8 within each row of 16 lanes), so that one
@@ -477,12 +477,12 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
     // stores bypass the caches, which then keep the operand panels the other tiles read.
     // Measured on the Qwen3-4B set at 8192 tokens: product 707-718 -> 672-677 us, step
     // 1.132-1.139 -> 1.099-1.105 ms (non-temporal 64-byte pieces were slower than plain
-    // stores in the step, whole lines without the hint no faster).  The general form below,
-    // with its per-group branches and 64-bit addresses, measured 6-7 us per tile whether or
-    // not it stored anything (the unrolled code is large and runs once per tile); this one
-    // 2.3 us plus the stores' drain.  (The 128 x 128 tile measured about 1 us slower per
-    // product with the straight-line form and keeps the general one.)
-    if (MI >= 8 && !p.R && !p.acc && m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0 &&
+    // stores in the step, whole lines without the hint no faster); Distillix-125M set at
+    // 2048 tokens (128 x 128 tiles): product 25.9-26.7 -> 23.3-24.8 us.  The general form
+    // below, with its per-group branches and 64-bit addresses, measured 6-7 us per 128 x 256
+    // tile whether or not it stored anything (the unrolled code is large and runs once per
+    // tile); this one 2.3 us plus the stores' drain.
+    if (!p.R && !p.acc && m0 + BM <= p.M && n0 + BN <= p.N && (p.N & 3) == 0 &&
         ((uintptr_t)p.Y & 15) == 0 && (int64_t)BM * p.N * 4 <= (int64_t)0xFFFFFFFFu) {
         static_assert(NI % 2 == 0, "column groups in pairs");
         const rsrc_t yres = make_rsrc(p.Y + (int64_t)m0 * p.N, (uint32_t)BM * (uint32_t)p.N * 4u);
