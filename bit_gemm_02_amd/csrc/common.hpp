@@ -64,6 +64,31 @@ __device__ __forceinline__ void buf_store16_nt(rsrc_t r, uint32_t offset, v4u va
     __builtin_amdgcn_raw_buffer_store_b128(value, r, (int)offset, 0, 2);
 }
 
+// Whole-line output stores from a 16 x 16 MFMA result layout.  Lane (r, g), r = lane % 16,
+// g = lane / 16, holds four consecutive fp32 outputs of tile row r at columns 4g .. 4g + 3 of
+// two adjacent 16-column groups: e (columns 0-15) and o (columns 16-31).  Lanes r and r ^ 8
+// exchange one piece (a DPP rotation by 8 within each row of 16 lanes), after which one
+// 16-byte store per lane writes tile rows 0-7 and a second one rows 8-15, each row as one
+// 128-byte segment of 32 outputs (instead of 16 rows of 64 bytes per store), with the
+// non-temporal policy.  `off` is the byte offset of row (r & 7), column 4g + (r < 8 ? 0 : 16)
+// in `res`; `pitch8` is eight rows' bytes.
+__device__ __forceinline__ void store_pair_lines_nt(rsrc_t res, uint32_t off, uint32_t pitch8,
+                                                    bool lo, v4u e, v4u o)
+{
+    v4u v1, v2;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        // r < 8 sends its piece of o to r + 8 and receives that lane's piece of e; r >= 8 the
+        // other way round.
+        const uint32_t snd = lo ? o[v] : e[v];
+        const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xF, 0xF, false);
+        v1[v] = lo ? e[v] : rcv;      // row (r & 7)
+        v2[v] = lo ? rcv : o[v];      // row (r & 7) + 8
+    }
+    buf_store16_nt(res, off, v1);
+    buf_store16_nt(res, off + pitch8, v2);
+}
+
 // Bytes of rows [r0, min(r0 + rows, R)) of a row-major matrix with `row_bytes` per row.
 __device__ __forceinline__ uint32_t rows_bytes(int r0, int rows, int R, int row_bytes)
 {

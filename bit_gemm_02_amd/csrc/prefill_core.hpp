@@ -444,6 +444,26 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
     if constexpr (BF) {
         // Weight-only product: y = fl32(gamma * acc), acc the fp32 matrix-unit sum.
         const bool vecb = (p.N & 3) == 0 && ((uintptr_t)p.Y & 15) == 0;
+        // A full tile: whole-line non-temporal stores (store_pair_lines_nt), as below.
+        if (vecb && m0 + BM <= p.M && n0 + BN <= p.N && (int64_t)BM * p.N * 4 <= (int64_t)0xFFFFFFFFu) {
+            static_assert(NI % 2 == 0, "column groups in pairs");
+            const rsrc_t yres = make_rsrc(p.Y + (int64_t)m0 * p.N, (uint32_t)BM * (uint32_t)p.N * 4u);
+            const bool lo = r < 8;
+            const uint32_t pitch8 = 8u * (uint32_t)p.N * 4u;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const uint32_t base = (uint32_t)(wm * T::TM + mi * 16 + (r & 7)) * (uint32_t)p.N * 4u +
+                                      (uint32_t)(n0 + wn * T::TN + 4 * g + (lo ? 0 : 16)) * 4u;
+#pragma unroll
+                for (int pp = 0; pp < NI / 2; ++pp) {
+                    const f32x4 ye = acc[mi][2 * pp] * gammaf;
+                    const f32x4 yo = acc[mi][2 * pp + 1] * gammaf;
+                    store_pair_lines_nt(yres, base + (uint32_t)(pp * 32 * 4), pitch8, lo,
+                                        __builtin_bit_cast(v4u, ye), __builtin_bit_cast(v4u, yo));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const int m = m0 + wm * T::TM + mi * 16 + r;
@@ -469,12 +489,9 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
     const double gamma = (double)gammaf;
     // A full tile with neither residual nor int32 copy (every tile of a product whose M and
     // N are multiples of the tile): straight-line code with whole-line,
-    // non-temporal stores.  Lane (r, g) holds four consecutive outputs of row r for each
-    // 16-column group ni; the pieces of the column groups 2p and 2p + 1 are exchanged between
-    // lanes r and r ^ 8 (one DPP rotation by 8 within each row of 16 lanes), so that one
-    // 16-byte store per lane covers rows 0-7 of the MFMA tile and the next rows 8-15, each
-    // row as a whole 128-byte segment (32 outputs), instead of 16 rows of 64 bytes.  The
-    // stores bypass the caches, which then keep the operand panels the other tiles read.
+    // non-temporal stores (store_pair_lines_nt: column groups 2p and 2p + 1 exchanged
+    // between lanes r and r ^ 8, each store a whole 128-byte row segment).  The stores bypass
+    // the caches, which then keep the operand panels the other tiles read.
     // Measured on the Qwen3-4B set at 8192 tokens: product 707-718 -> 672-677 us, step
     // 1.132-1.139 -> 1.099-1.105 ms (non-temporal 64-byte pieces were slower than plain
     // stores in the step, whole lines without the hint no faster); Distillix-125M set at
@@ -497,21 +514,13 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
                                   (uint32_t)(n0 + wn * T::TN + 4 * g + (lo ? 0 : 16)) * 4u;
 #pragma unroll
             for (int pp = 0; pp < NI / 2; ++pp) {
-                v4u ye, yo, v1, v2;
+                v4u ye, yo;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     ye[v] = __float_as_uint((float)((double)(acc[mi][2 * pp][v] >> 6) * scale));
                     yo[v] = __float_as_uint((float)((double)(acc[mi][2 * pp + 1][v] >> 6) * scale));
-                    // r < 8 sends its odd group's piece to r + 8 and receives that lane's
-                    // even group's piece; r >= 8 the other way round.
-                    const uint32_t snd = lo ? yo[v] : ye[v];
-                    const uint32_t rcv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)snd, 0x128, 0xF, 0xF, false);
-                    v1[v] = lo ? ye[v] : rcv;      // row (r & 7)
-                    v2[v] = lo ? rcv : yo[v];      // row (r & 7) + 8
                 }
-                const uint32_t o = base + (uint32_t)(pp * 32 * 4);
-                buf_store16_nt(yres, o, v1);
-                buf_store16_nt(yres, o + pitch8, v2);
+                store_pair_lines_nt(yres, base + (uint32_t)(pp * 32 * 4), pitch8, lo, ye, yo);
             }
         }
     } else {

@@ -217,6 +217,26 @@ __global__ __launch_bounds__(kWgThreads) void wgemm_kernel(WgBatch b)
     // m = m0 + wm * 64 + mi * 16 + r (the codes are the MFMA's row operand): four
     // consecutive outputs of one row per lane.
     const bool vec = (p.O & 3) == 0 && ((uintptr_t)p.Y & 15) == 0;
+    // A full tile: whole-line non-temporal stores (store_pair_lines_nt), as in the prefill
+    // product's epilogue.
+    if (vec && m0 + kWgBM <= p.M && o0 + kWgBO <= p.O && (int64_t)kWgBM * p.O * 4 <= (int64_t)0xFFFFFFFFu) {
+        const rsrc_t yres = make_rsrc(p.Y + (int64_t)m0 * p.O, (uint32_t)kWgBM * (uint32_t)p.O * 4u);
+        const bool lo = r < 8;
+        const uint32_t pitch8 = 8u * (uint32_t)p.O * 4u;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const uint32_t base = (uint32_t)(wm * 64 + mi * 16 + (r & 7)) * (uint32_t)p.O * 4u +
+                                  (uint32_t)(o0 + wn * 64 + 4 * g + (lo ? 0 : 16)) * 4u;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                const f32x4 ye = acc[mi][2 * pp] * gammaf;
+                const f32x4 yo = acc[mi][2 * pp + 1] * gammaf;
+                store_pair_lines_nt(yres, base + (uint32_t)(pp * 32 * 4), pitch8, lo,
+                                    __builtin_bit_cast(v4u, ye), __builtin_bit_cast(v4u, yo));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int m = m0 + wm * 64 + mi * 16 + r;
@@ -487,6 +507,61 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
     // quantizer's division; gamma == 0 gives t = 0).
     const bool vec = ((uintptr_t)p.dW & 15) == 0 && (!p.W || ((uintptr_t)p.W & 15) == 0);
     const double beta = (double)p.beta;
+    // The four outputs of group (mi, ni): row n, columns k .. k + 3.
+    auto outputs = [&](int mi, int ni, int n, int k, float (&y)[4]) {
+        float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (p.ste != 0) {
+            const float *wrow = p.W + (int64_t)n * K + k;
+            if (vec) {
+                const float4 wv = *reinterpret_cast<const float4 *>(wrow);
+                w[0] = wv.x; w[1] = wv.y; w[2] = wv.z; w[3] = wv.w;
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    w[v] = wrow[v];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float a = acc[ni][mi][v];
+            if (p.ste == 0) {
+                y[v] = a;
+            } else {
+                const float t = gammaf == 0.0f ? 0.0f : w[v] / gammaf;   // correctly rounded
+                if (p.ste == 1) {
+                    y[v] = fabsf(t) <= 1.0f ? a : 0.0f;
+                } else {
+                    // sech^2(x) = 4 e / (1 + e)^2 with e = exp(-2 |x|): one exponential.
+                    const double e = exp(-2.0 * fabs(beta * (double)t));
+                    const double d = 1.0 + e;
+                    y[v] = (float)((4.0 * e / (d * d)) * (double)a);
+                }
+            }
+        }
+    };
+    // A full tile: whole-line non-temporal stores (store_pair_lines_nt), as in the prefill
+    // product's epilogue.
+    if (vec && n0 + kGwBN <= N && k0 + kGwBK <= K && (int64_t)kGwBN * K * 4 <= (int64_t)0xFFFFFFFFu) {
+        const rsrc_t dres = make_rsrc(p.dW + (int64_t)n0 * K, (uint32_t)kGwBN * (uint32_t)K * 4u);
+        const bool lo = r < 8;
+        const uint32_t pitch8 = 8u * (uint32_t)K * 4u;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int n = n0 + wm * 64 + mi * 16 + r;
+            const uint32_t base = (uint32_t)(wm * 64 + mi * 16 + (r & 7)) * (uint32_t)K * 4u +
+                                  (uint32_t)(k0 + wn * 64 + 4 * g + (lo ? 0 : 16)) * 4u;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                float ye[4], yo[4];
+                outputs(mi, 2 * pp, n, k0 + wn * 64 + 2 * pp * 16 + 4 * g, ye);
+                outputs(mi, 2 * pp + 1, n, k0 + wn * 64 + (2 * pp + 1) * 16 + 4 * g, yo);
+                const v4u e = {__float_as_uint(ye[0]), __float_as_uint(ye[1]), __float_as_uint(ye[2]), __float_as_uint(ye[3])};
+                const v4u o = {__float_as_uint(yo[0]), __float_as_uint(yo[1]), __float_as_uint(yo[2]), __float_as_uint(yo[3])};
+                store_pair_lines_nt(dres, base + (uint32_t)(pp * 32 * 4), pitch8, lo, e, o);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         const int n = n0 + wm * 64 + mi * 16 + r;
@@ -498,35 +573,7 @@ __global__ __launch_bounds__(kGwThreads) void gradw_kernel(GwBatch b)
             if (k >= K)
                 continue;     // K % 16 == 0: the four columns are all in or all out
             float y[4];
-            float w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (p.ste != 0) {
-                const float *wrow = p.W + (int64_t)n * K + k;
-                if (vec) {
-                    const float4 wv = *reinterpret_cast<const float4 *>(wrow);
-                    w[0] = wv.x; w[1] = wv.y; w[2] = wv.z; w[3] = wv.w;
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        w[v] = wrow[v];
-                }
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float a = acc[ni][mi][v];
-                if (p.ste == 0) {
-                    y[v] = a;
-                } else {
-                    const float t = gammaf == 0.0f ? 0.0f : w[v] / gammaf;   // correctly rounded
-                    if (p.ste == 1) {
-                        y[v] = fabsf(t) <= 1.0f ? a : 0.0f;
-                    } else {
-                        // sech^2(x) = 4 e / (1 + e)^2 with e = exp(-2 |x|): one exponential.
-                        const double e = exp(-2.0 * fabs(beta * (double)t));
-                        const double d = 1.0 + e;
-                        y[v] = (float)((4.0 * e / (d * d)) * (double)a);
-                    }
-                }
-            }
+            outputs(mi, ni, n, k, y);
             float *dst = p.dW + (int64_t)n * K + k;
             if (vec) {
                 *reinterpret_cast<float4 *>(dst) = make_float4(y[0], y[1], y[2], y[3]);
