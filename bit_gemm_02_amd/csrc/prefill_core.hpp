@@ -61,13 +61,19 @@ struct Tile {
     static_assert((NST - 2) * LOADS < 64, "vmcnt range");
 };
 
-// Activation chunk swizzle: chunk c of tile row m sits at position c ^ f(m), chosen so that
-// the 16 rows of one MFMA A-operand read (same c) fall in 16 different 16-byte bank slots of
-// a 256-byte bank cycle: f(m) = (m / (16 / CPR)) % CPR.
+// Activation chunk swizzle: chunk c of tile row m sits at position c ^ f(m).  For 128-byte
+// rows (CPR = 8, int8 stages) f(m) = (m & 7) ^ ((m >> 3) & 1): an LDS probe of the fragment
+// read (lane (r, g) reads chunk (2g + j) ^ f(r) of row r) measured 186 bytes per clock per CU
+// with it, the rate of a linear read, against 128 with f(m) = (m / 2) & 7, which puts the 16
+// rows in 16 different 16-byte slots of 256 bytes but still conflicts in the hardware's lane
+// grouping.  Other row lengths: f(m) = (m / (16 / CPR)) % CPR.
 template <int CPR>
 __device__ __forceinline__ int xswz(int row)
 {
-    return (row / (16 / CPR)) & (CPR - 1);
+    if constexpr (CPR == 8)
+        return (row & 7) ^ ((row >> 3) & 1);
+    else
+        return (row / (16 / CPR)) & (CPR - 1);
 }
 
 // Weight chunk swizzle (16-byte chunks, WCH per row): rows m and m + 8 of a 16-row B-operand
