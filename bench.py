@@ -359,10 +359,11 @@ class Setup:
         assert rc == 0, rc
 
 
-def isolated_ms(torch, setup: Setup, key: str, reps: int) -> float:
-    """Average duration of one launch group run alone, back to back.  The launches are
-    captured into a HIP graph and replayed, so the host's per-launch cost (several us, as
-    long as the shortest kernels here) stays out of the figure; events on the replay stream."""
+def isolated_ms(torch, setup: Setup, key: str, reps: int, loops: int = 5) -> float:
+    """Duration of one launch group run alone, back to back: the median over `loops` timed
+    replays of a HIP graph of `reps` launches (rotating through the input copies), divided by
+    `reps`.  The graph keeps the host's per-launch cost (several us, as long as the shortest
+    kernels here) out of the figure; events on the replay stream."""
     s_ = torch.cuda.Stream()
     with torch.cuda.stream(s_):
         for i in range(3):
@@ -373,16 +374,16 @@ def isolated_ms(torch, setup: Setup, key: str, reps: int) -> float:
         for i in range(reps):
             setup.launch_only(key, i, s_.cuda_stream)
     torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(loops)]
     with torch.cuda.stream(s_):
         graph.replay()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record(s_)
-        for _ in range(3):
+        for s, e in evs:
+            s.record(s_)
             graph.replay()
-        e.record(s_)
+            e.record(s_)
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / (3 * reps)
+    return float(np.median([s.elapsed_time(e) for s, e in evs])) / reps
 
 
 def interval_ms(ev, a, b):
