@@ -256,11 +256,11 @@ class Setup:
     # Work accounting (algorithmic, what the method must move or compute).
     def mixed_one_launch(self) -> bool:
         """Whether bitlinear_forward_mixed runs the step's products and decode leg as one launch:
-        every product has more than 16 tokens on 128 x 128 tiles (fewer than 512 units of
+        every product has more than 16 tokens on 128 x 128 tiles (fewer than 256 units of
         256 x 256 outputs; larger sets take 128 x 256 tiles), and the decode calls are fused
         with one activation dtype (always here)."""
         big = sum(-(-self.M_pre // 256) * -(-m.N // 256) for m in self.wl.matrices)
-        return self.M_pre > 16 and big < 512 and self.M_dec <= 4
+        return self.M_pre > 16 and big < 256 and self.M_dec <= 4
 
     def prefill_ops(self) -> int:
         return sum(2 * self.M_pre * m.N * m.K for m in self.wl.matrices)

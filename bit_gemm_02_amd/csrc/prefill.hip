@@ -15,8 +15,12 @@
 // by gfx950 direct-to-LDS buffer loads, NST - 1 stages in flight while one is multiplied,
 // one barrier per stage.  Per stage and lane (r = l % 16, g = l / 16): the packed words of its
 // weight rows from LDS, expanded into B operands; the A operands (16 activation bytes of
-// token row r, k group g) from LDS with one 16-byte read each.
-// Epilogue: y = fl32(fp64(acc * gamma * s_x[m])), acc = (MFMA sum) / 64 (exact shift).
+// token row r, k group g) from LDS with one 16-byte read each.  The 128 x 256 tile runs these
+// reads as a rolling pipeline (each fragment re-read right after its last use, the stage
+// barrier in the middle of the last k-step); the 128 x 128 tile defers each stage's last
+// k-step past the next barrier.
+// Epilogue: y = fl32(fp64(acc * gamma * s_x[m])), acc = (MFMA sum) / 64 (exact shift); full
+// tiles store whole 128-byte row segments with the non-temporal hint.
 #include "prefill_core.hpp"
 
 namespace bl {

@@ -372,7 +372,7 @@ bl_status bitlinear_forward_ex_grouped(const bl_forward_ex_problem *problems, in
  *                   may be NULL when ndec == 0).
  * Results: bit for bit those of bitlinear_forward_ex_grouped(prefill, npre) followed by
  * bitlinear_linear_grouped(decode, ndec).  When every non-empty prefill product has M > 16
- * and the products take 128 x 128 tiles (they do while the set has fewer than 512 units of
+ * and the products take 128 x 128 tiles (they do while the set has fewer than 256 units of
  * 256 x 256 outputs; larger sets take 128 x 256 tiles), and every
  * non-empty decode call takes the fused form with one activation dtype, both sets share one
  * launch: the decode blocks run on the compute units the product's last tiles leave idle.
