@@ -217,6 +217,32 @@ def test_forward(torch, bl, orc, M, N, K):
     assert rel_err(Yh[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL
 
 
+# Shapes whose products have full tiles, so that without the int32 copy they take the
+# straight-line epilogue (whole 128-byte row segments, lanes r and r ^ 8 exchanging pieces):
+# 128 x 128 tiles with a row pitch that is not a multiple of 128 bytes (N = 260, 2060) and
+# ragged last tiles, and 128 x 256 tiles (at least 256 units of 256 x 256 outputs), one set
+# with a ragged last column tile (N = 8200).
+FULL_TILE_SHAPES = [(256, 260, 512), (300, 640, 768), (1100, 2060, 256), (2048, 8192, 256),
+                    (2048, 8200, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", FULL_TILE_SHAPES)
+def test_forward_full_tiles(torch, bl, orc, M, N, K):
+    W = workloads.gaussian((N, K), (117, M, N, K), 0.02)
+    X = workloads.gaussian((M, K), (118, M, N, K), 1.0)
+    P, g = bl.quantize_weights(dev(torch, W))
+    Xq, sx = bl.quantize_acts(dev(torch, X))
+    Y = bl.forward(Xq, sx, P, g)                              # full tiles: straight-line epilogue
+    Y_gen, acc = bl.forward(Xq, sx, P, g, return_acc=True)    # general epilogue everywhere
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y_gen), (M, N, K)
+    acc_ref, Y_ref = orc.forward(host(Xq), host(sx), words(P), host(g)[0])
+    assert np.array_equal(host(acc), acc_ref), (M, N, K)
+    Yh = host(Y)
+    assert np.array_equal(Yh == 0, Y_ref == 0)
+    assert rel_err(Yh[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL
+
+
 def test_forward_without_acc_matches(torch, bl):
     W = dev(torch, workloads.gaussian((300, 512), (112,), 0.02))
     X = dev(torch, workloads.gaussian((40, 512), (113,), 1.0))
