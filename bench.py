@@ -110,6 +110,32 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def mixed_one_launch(wl: workloads.Workload, M_pre: int, M_dec: int = 1) -> bool:
+    """Whether bitlinear_forward_mixed runs the step's products and decode leg as one launch:
+    every product has more than 16 tokens on 128 x 128 tiles (fewer than 256 units of
+    256 x 256 outputs; larger sets take 128 x 256 tiles), and the decode calls are fused
+    with one activation dtype (always here)."""
+    big = sum(-(-M_pre // 256) * -(-m.N // 256) for m in wl.matrices)
+    return M_pre > 16 and big < 256 and M_dec <= 4
+
+
+def decode_on_tiles(wl: workloads.Workload, M_pre: int) -> bool:
+    """Whether the step's one-token decode leg runs on the decode tile layout (packed once,
+    outside timing, from the two-bit rows): where the leg is a launch of its own (the products
+    take 128 x 256 tiles) and every projection fits the one-token kernel."""
+    return (not mixed_one_launch(wl, M_pre) and
+            all(m.K % 64 == 0 and m.K <= 12288 for m in wl.matrices))
+
+
+def gemv_layout(name: str) -> str:
+    """'b3', 'tiles' or 'rows' for a gemv_kernel<S, BF16, PAIR, NORM, B3, TL> name."""
+    args = name.split("(")[0].split("<", 1)[1].rstrip(">").split(",")
+    args = [a.strip() for a in args]
+    if args[4] == "true":
+        return "b3"
+    return "tiles" if len(args) > 5 and args[5] == "true" else "rows"
+
+
 class Setup:
     """Device buffers and pre-built grouped problem tables for one workload."""
 
@@ -171,6 +197,10 @@ class Setup:
         # The same decode weights in the base-3 layout (five codes per byte), for the
         # base-3 decode figure reported beside the step (not part of the step).
         self.B3_dec = [[bl.pack_b3(p) for p in Ps] for Ps in self.P_dec]
+        # ... and in the decode tile layout, which the step's decode leg reads where it is a
+        # launch of its own (the two-bit rows are then reported beside it).
+        self.dec_tiles = decode_on_tiles(wl, M_pre)
+        self.T_dec = [[bl.pack_tiles(p, m.K) for p, m in zip(Ps, mats)] for Ps in self.P_dec]
         self.g_dec = [g.clone() for _, g in dec_packed]
         self.X_dec = [to_dev(x) for x in X_dec]
 
@@ -248,6 +278,18 @@ class Setup:
                                            self.Y_dec[i].data_ptr(), None, None,
                                            self.M_dec, m.N, m.K, dt, 1e-6)
             self.lin_dec_b3_tables.append(arr)
+        self.lin_dec_tiles_tables = []
+        for r in range(self.R_dec):
+            arr = (bl._LinearProblem * n)()
+            for i, m in enumerate(mats):
+                X = self.X_dec[i]
+                g = self.norms[i]
+                dt = bl.BL_BF16 if X.dtype == self.torch.bfloat16 else bl.BL_F32
+                arr[i] = bl._LinearProblem(X.data_ptr(), None if g is None else g.data_ptr(),
+                                           self.T_dec[r][i].data_ptr(), self.g_dec[i].data_ptr(),
+                                           self.Y_dec[i].data_ptr(), None, None,
+                                           self.M_dec, m.N, m.K, dt, 1e-6)
+            self.lin_dec_tiles_tables.append(arr)
         import ctypes as C
         self._addr = C.addressof
         self.ws_ptr = self.ws.data_ptr()
@@ -255,12 +297,14 @@ class Setup:
 
     # Work accounting (algorithmic, what the method must move or compute).
     def mixed_one_launch(self) -> bool:
-        """Whether bitlinear_forward_mixed runs the step's products and decode leg as one launch:
-        every product has more than 16 tokens on 128 x 128 tiles (fewer than 256 units of
-        256 x 256 outputs; larger sets take 128 x 256 tiles), and the decode calls are fused
-        with one activation dtype (always here)."""
-        big = sum(-(-self.M_pre // 256) * -(-m.N // 256) for m in self.wl.matrices)
-        return self.M_pre > 16 and big < 256 and self.M_dec <= 4
+        return mixed_one_launch(self.wl, self.M_pre, self.M_dec)
+
+    def decode_leg(self, L, rd: int, stream) -> int:
+        """The step's decode leg as its own launch (tiles or two-bit rows)."""
+        if self.dec_tiles:
+            return L.bitlinear_linear_tiles_grouped(self._addr(self.lin_dec_tiles_tables[rd]),
+                                                    self.count, stream)
+        return L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[rd]), self.count, stream)
 
     def prefill_ops(self) -> int:
         return sum(2 * self.M_pre * m.N * m.K for m in self.wl.matrices)
@@ -330,7 +374,7 @@ class Setup:
             rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
             assert rc == 0, rc
             mark("t_pre")
-            rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[rd]), n, stream)
+            rc = self.decode_leg(L, rd, stream)
             assert rc == 0, rc
         mark("t_mix")
 
@@ -348,6 +392,8 @@ class Setup:
             rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
                                            self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
         elif key == "decode_linear":
+            rc = self.decode_leg(L, i % self.R_dec, stream)
+        elif key == "decode_linear_rows":
             rc = L.bitlinear_linear_grouped(self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
         elif key == "decode_linear_b3":
             rc = L.bitlinear_linear_b3_grouped(self._addr(self.lin_dec_b3_tables[i % self.R_dec]), n, stream)
@@ -462,6 +508,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -
     """Per-launch HBM bytes of each kernel, scaled by a plain 256 MiB device copy."""
     import csv
     from collections import defaultdict
+    wlw = workloads.WORKLOADS[workload]
+    tiles_leg = decode_on_tiles(wlw, max(wlw.token_counts))
 
     def per_dispatch(path, counter):
         out = {}
@@ -491,8 +539,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -
         for name, grid, kib in d.values():
             for frag, (key, src) in KERNELS.items():
                 if frag in name:
-                    if key == "decode_linear" and name.split("(")[0].endswith("true>"):
-                        key = "decode_linear_b3"      # the one-token kernel on base-3 rows
+                    if frag == "gemv_kernel":
+                        lay = gemv_layout(name)       # the one-token kernel: which weight layout
+                        if lay == "b3":
+                            key = "decode_linear_b3"
+                        elif (lay == "tiles") != tiles_leg:
+                            key = "decode_linear_rows" if lay == "rows" else "decode_linear_tiles"
                     acc[(key, src)].append((name, kib * 1024.0 * factor))
                     break
         return acc
@@ -937,7 +989,8 @@ def main():
     # Isolated launches: the step's own, plus the product and the decode leg each alone.
     ms = {k: isolated_ms(torch, setup, k, args.steps)
           for k in set(in_step) | {"prefill_gemm", "decode_linear", "act_quant_prefill"} |
-          ({"weight_quant"} if setup.wq_tables else set())}
+          ({"weight_quant"} if setup.wq_tables else set()) |
+          ({"decode_linear_rows"} if setup.dec_tiles else set())}
     ms_b3 = isolated_ms(torch, setup, "decode_linear_b3", args.steps)
     peaks = measured_peaks(torch, bl)
 
@@ -984,7 +1037,8 @@ def main():
         "prefill_gemm": pre_roof,
         "decode_linear": hbm(dec_bytes, "decode_linear",
                              f"{dec_bytes} bytes (N K / 4 + M K x-bytes (+ 4 K norm) + 4 + 4 M N "
-                             "summed; activation quantization fused)"),
+                             "summed; activation quantization fused; weights in the "
+                             f"{'decode tile layout' if setup.dec_tiles else 'two-bit rows'})"),
         "act_quant_prefill": hbm(aq_bytes, "act_quant_prefill",
                                  f"{aq_bytes} bytes (M K x-bytes + M K + 4 M (+ 4 K norm) summed)"),
     }
@@ -1038,6 +1092,12 @@ def main():
                    "rotation_copies": {"prefill": setup.R_pre, "decode": setup.R_dec}},
         "decode": {"gbps": round(dec_gbps, 2), "frac_hbm": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "bytes": dec_bytes, "us_linear": round(ms["decode_linear"] * 1e3, 3),
+                   "layout": "tiles" if setup.dec_tiles else "rows",
+                   **({"rows": {"us_linear": round(ms["decode_linear_rows"] * 1e3, 3),
+                                "gbps": round(dec_bytes / (ms["decode_linear_rows"] * 1e-3) / 1e9, 2),
+                                "note": "the same call on the two-bit rows [N][K/16]; the step's leg "
+                                        "reads the decode tiles (same codes, packed once outside "
+                                        "timing)"}} if setup.dec_tiles else {}),
                    "base3": {"us_linear": round(ms_b3 * 1e3, 3), "bytes": setup.decode_b3_bytes(),
                              "gbps": round(setup.decode_b3_bytes() / (ms_b3 * 1e-3) / 1e9, 2),
                              "speedup_vs_two_bit": round(ms["decode_linear"] / ms_b3, 3),

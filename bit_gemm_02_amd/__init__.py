@@ -183,6 +183,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_b3.restype = ctypes.c_int
     L.bitlinear_linear_b3_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_b3_grouped.restype = ctypes.c_int
+    L.bitlinear_tiles_bytes.argtypes = [I64, I64]
+    L.bitlinear_tiles_bytes.restype = I64
+    L.bitlinear_pack_tiles.argtypes = [P, I64, I64, P, P]
+    L.bitlinear_pack_tiles.restype = ctypes.c_int
+    L.bitlinear_linear_tiles_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_linear_tiles_grouped.restype = ctypes.c_int
     L.bitlinear_calib_stream.argtypes = [P, I64, P, P]
     L.bitlinear_calib_stream.restype = ctypes.c_int
     L.bitlinear_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -689,6 +695,52 @@ def linear_b3_grouped(problems: Sequence[dict], stream=None) -> None:
     arr = linear_b3_table(problems)
     _check("bitlinear_linear_b3_grouped",
            lib().bitlinear_linear_b3_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+# ------------------------------------------------------------- decode tiles
+
+def tiles_bytes(N: int, K: int) -> int:
+    """Bytes of the decode tile layout of an N x K weight matrix."""
+    return int(lib().bitlinear_tiles_bytes(int(N), int(K)))
+
+
+def pack_tiles(W_packed: torch.Tensor, K: Optional[int] = None, W_tiles: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Two-bit packed codes [N, K/16] -> decode tiles (flat int32 [tiles_bytes(N, K) / 4])."""
+    _dev(W_packed, "W_packed", torch.int32)
+    N = W_packed.shape[0]
+    K = W_packed.shape[1] * 16 if K is None else K
+    if W_tiles is None:
+        W_tiles = torch.empty(tiles_bytes(N, K) // 4, dtype=torch.int32, device=W_packed.device)
+    _check("bitlinear_pack_tiles", lib().bitlinear_pack_tiles(_ptr(W_packed), N, K, _ptr(W_tiles),
+                                                              _stream(stream)))
+    return W_tiles
+
+
+def linear_tiles_table(problems: Sequence[dict]):
+    """ctypes array for bitlinear_linear_tiles_grouped: dicts as for linear_grouped, with
+    W_tiles (flat int32, at least tiles_bytes(N, K) / 4 elements) in place of W_packed; N is
+    Y's column count."""
+    arr = (_LinearProblem * max(len(problems), 1))()
+    for i, p in enumerate(problems):
+        X = _dev(p["X"], f"X[{i}]")
+        M, K = X.shape
+        Y = _dev(p["Y"], f"Y[{i}]", torch.float32)
+        N = Y.shape[1]
+        Wt = _dev(p["W_tiles"], f"W_tiles[{i}]", torch.int32)
+        if Wt.numel() * 4 < tiles_bytes(N, K):
+            raise ValueError(f"W_tiles[{i}] must hold tiles_bytes(N, K) bytes")
+        arr[i] = _LinearProblem(_ptr(X), _ptr(p.get("norm_weight")), _ptr(Wt), _ptr(p["gamma"]),
+                                _ptr(Y), _ptr(p.get("X_q")), _ptr(p.get("x_scale")), M, N, K,
+                                _x_dtype(X), float(p.get("eps", 1e-6)))
+    return arr
+
+
+def linear_tiles_grouped(problems: Sequence[dict], stream=None) -> None:
+    """The fused one-token layer call on decode tiles."""
+    arr = linear_tiles_table(problems)
+    _check("bitlinear_linear_tiles_grouped",
+           lib().bitlinear_linear_tiles_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
 
 
 # ----------------------------------------------------------------- measurement helpers

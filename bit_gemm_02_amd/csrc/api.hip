@@ -784,6 +784,61 @@ bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int cou
     return from_hip(bl::launch_linear_decode_b3(ex, count, static_cast<hipStream_t>(stream)));
 }
 
+int64_t bitlinear_tiles_bytes(int64_t N, int64_t K)
+{
+    return (N < 0 || K <= 0 || K % 16 != 0) ? 0 : bl::tiles_bytes(N, K);
+}
+
+bl_status bitlinear_pack_tiles(const uint32_t *W_packed, int64_t N, int64_t K, uint32_t *W_tiles,
+                               void *stream)
+{
+    bl_status s = check_rows(N);
+    if (s == BL_OK && N != 0 && (!W_packed || !W_tiles))
+        return BL_ERR_NULL;
+    if (s == BL_OK)
+        s = check_k(K);
+    if (s != BL_OK)
+        return s;
+    if (bl::tiles_bytes(N, K) / 16 > (int64_t)INT_MAX * 256)
+        return BL_ERR_SHAPE;
+    if (!aligned16(W_packed) || !aligned16(W_tiles))
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_pack_tiles(W_packed, N, K, W_tiles, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_linear_tiles_grouped(const bl_linear_problem *problems, int count, void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl_linear_ex_problem ex[BL_MAX_GROUP];
+    const bl_linear_ex_problem *part[2][BL_MAX_GROUP];
+    int n[2] = {0, 0};
+    for (int i = 0; i < count; ++i) {
+        const bl_linear_problem &p = problems[i];
+        bl_status s = check_linear(p);
+        if (s != BL_OK)
+            return s;
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (p.M != 1)
+            return BL_ERR_SHAPE;         // the tile layout feeds the one-token product only
+        ex[i] = to_ex(p);
+        const int k = p.x_dtype == BL_BF16 ? 1 : 0;
+        part[k][n[k]++] = &ex[i];
+    }
+    for (int k = 0; k < 2; ++k)
+        if (n[k] && !bl::gemv_fits(part[k], n[k], k == 1, false))
+            return BL_ERR_SHAPE;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    for (int k = 0; k < 2 && e == hipSuccess; ++k)
+        if (n[k])
+            e = bl::launch_gemv_tiles(part[k], n[k], k == 1, st);
+    return from_hip(e);
+}
+
 bl_status bitlinear_calib_stream(const void *buf, int64_t bytes, uint32_t *xor_out, void *stream)
 {
     if (bytes < 0 || bytes % 16 != 0)

@@ -420,6 +420,11 @@ hipError_t launch_gemv(const bl_linear_ex_problem *const *p, int count, bool pai
 // The same on base-3 rows (single projections; W_packed holds bitlinear_pack_b3's rows).
 hipError_t launch_gemv_b3(const bl_linear_ex_problem *const *p, int count, bool bf16,
                           hipStream_t stream);
+hipError_t launch_gemv_tiles(const bl_linear_ex_problem *const *q, int count, bool bf16,
+                             hipStream_t stream);
+int64_t tiles_bytes(int64_t N, int64_t K);
+hipError_t launch_pack_tiles(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
+                             hipStream_t stream);
 hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 // Weight quantization + activation quantization of one step (γ pass and activation codes in
 // one launch when every activation problem takes the wave kernel with one dtype).

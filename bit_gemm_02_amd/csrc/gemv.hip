@@ -97,9 +97,10 @@ struct GvBatch {
 // base-3 rows (16-byte blocks of 80 weights, see b3_table_entry; a super-step is then 320
 // weights and five MFMAs per row group, the expansion a table lookup in LDS).  Two-bit rows
 // have K % 64 == 0, so a lane's 16 bytes never straddle the end of a row.
-template <int S, bool BF16, bool PAIR, bool NORM, bool B3>
+template <int S, bool BF16, bool PAIR, bool NORM, bool B3, bool TL>
 __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 {
+    static_assert(!(TL && (PAIR || B3)), "decode tiles: single two-bit projections");
     constexpr int G = PAIR ? 2 : 1;
     static_assert(!B3 || !PAIR, "base-3 rows: single projections");
     __shared__ __align__(8) uint32_t b3lut[B3 ? 512 : 2];
@@ -174,11 +175,17 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 
     // ---- weight loads: rows n0 .. n0+15 (rows past N read as zero), the first round of
     // this wave's super-steps [t_begin, t_end)
-    const unsigned char *const wrow = reinterpret_cast<const unsigned char *>(p.W) + (int64_t)n0 * row_bytes;
-    const rsrc_t wres = make_rsrc(wrow, rows_bytes(n0, 16, p.N, row_bytes));
+    // Decode tiles (TL): the row group's super-step T is one contiguous KB at T * 1024, lane l
+    // at byte 16 l (the words this lane loads from the two-bit rows), zero-padded.
+    const int64_t tile_bytes = (int64_t)supers * 1024;
+    const unsigned char *const wrow = reinterpret_cast<const unsigned char *>(p.W) +
+                                      (TL ? (int64_t)rg * tile_bytes : (int64_t)n0 * row_bytes);
+    // (A wave whose row group lies past N gets an empty resource: every load reads zero.)
+    const rsrc_t wres = make_rsrc(wrow, TL ? (n0 < p.N ? (uint32_t)tile_bytes : 0u)
+                                           : rows_bytes(n0, 16, p.N, row_bytes));
     const rsrc_t wres2 = PAIR ? make_rsrc(p.W2 + (int64_t)n0 * words, rows_bytes(n0, 16, p.N, row_bytes))
                               : wres;
-    const uint32_t wbase = (uint32_t)r * row_bytes;
+    const uint32_t wbase = TL ? 16u * (uint32_t)lane : (uint32_t)r * row_bytes;
     v4u w[G][S];
     // Super-steps lo .. hi-1 of the round starting at super-step `base` (non-temporal: the
     // weights are read once).
@@ -195,6 +202,8 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
                 if (B3) {
                     const int blk = 4 * T + g;
                     w[gi][t] = buf_load16_nt(res, live && blk < nblk ? wbase + 16u * blk : kOOB);
+                } else if (TL) {
+                    w[gi][t] = buf_load16_nt(res, live ? (uint32_t)T * 1024u + wbase : kOOB);
                 } else {
                     const int wd = 16 * T + 4 * g;
                     w[gi][t] = buf_load16_nt(res, live && wd < words ? wbase + 4u * wd : kOOB);
@@ -387,14 +396,14 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     p.Y[n] = y;
 }
 
-template <int S, bool BF16, bool PAIR, bool B3>
+template <int S, bool BF16, bool PAIR, bool B3, bool TL>
 static void launch_s(const GvBatch &b, int blocks, size_t lds, bool norm, hipStream_t stream)
 {
     if (norm)
-        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, true, B3>), dim3(blocks), dim3(kGvThreads), lds,
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, true, B3, TL>), dim3(blocks), dim3(kGvThreads), lds,
                            stream, b);
     else
-        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, false, B3>), dim3(blocks), dim3(kGvThreads), lds,
+        hipLaunchKernelGGL((gemv_kernel<S, BF16, PAIR, false, B3, TL>), dim3(blocks), dim3(kGvThreads), lds,
                            stream, b);
 }
 
@@ -403,7 +412,7 @@ static void launch_s(const GvBatch &b, int blocks, size_t lds, bool norm, hipStr
 // (1, 2 or 4) that keep a wave's loads per lane within kGvLoadsPerWave; the round length S is
 // the longest slice, rounded up to 4, 8, 12 or 16 (longer slices take several rounds).
 // Longest rows first.
-template <bool BF16, bool PAIR, bool B3>
+template <bool BF16, bool PAIR, bool B3, bool TL>
 static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, hipStream_t stream)
 {
     if (count == 0)
@@ -450,18 +459,18 @@ static hipError_t launch_kind(const bl_linear_ex_problem *const *q, int count, h
     // A pair's wave holds two row groups' loads: rounds of at most 8 super-steps (more would
     // not fit the register budget of three waves per SIMD).
     if (longest <= 4)
-        launch_s<4, BF16, PAIR, B3>(b, blocks, lds, norm, stream);
+        launch_s<4, BF16, PAIR, B3, TL>(b, blocks, lds, norm, stream);
     else if (longest <= 8 || PAIR)
-        launch_s<8, BF16, PAIR, B3>(b, blocks, lds, norm, stream);
+        launch_s<8, BF16, PAIR, B3, TL>(b, blocks, lds, norm, stream);
     else if (longest <= 12)
-        launch_s<12, BF16, false, B3>(b, blocks, lds, norm, stream);
+        launch_s<12, BF16, false, B3, TL>(b, blocks, lds, norm, stream);
     else
-        launch_s<16, BF16, false, B3>(b, blocks, lds, norm, stream);
+        launch_s<16, BF16, false, B3, TL>(b, blocks, lds, norm, stream);
     return hipGetLastError();
 }
 
 // Problems of one kind, split into those with and without a norm (one launch each).
-template <bool BF16, bool PAIR, bool B3>
+template <bool BF16, bool PAIR, bool B3, bool TL>
 static hipError_t launch_split(const bl_linear_ex_problem *const *q, int count, hipStream_t stream)
 {
     const bl_linear_ex_problem *part[2][BL_MAX_GROUP];
@@ -470,9 +479,9 @@ static hipError_t launch_split(const bl_linear_ex_problem *const *q, int count, 
         const int k = q[i]->norm_weight ? 1 : 0;
         part[k][n[k]++] = q[i];
     }
-    hipError_t e = launch_kind<BF16, PAIR, B3>(part[0], n[0], stream);
+    hipError_t e = launch_kind<BF16, PAIR, B3, TL>(part[0], n[0], stream);
     if (e == hipSuccess)
-        e = launch_kind<BF16, PAIR, B3>(part[1], n[1], stream);
+        e = launch_kind<BF16, PAIR, B3, TL>(part[1], n[1], stream);
     return e;
 }
 
@@ -480,17 +489,67 @@ hipError_t launch_gemv(const bl_linear_ex_problem *const *q, int count, bool pai
                        hipStream_t stream)
 {
     if (pair)
-        return bf16 ? launch_split<true, true, false>(q, count, stream)
-                    : launch_split<false, true, false>(q, count, stream);
-    return bf16 ? launch_split<true, false, false>(q, count, stream)
-                : launch_split<false, false, false>(q, count, stream);
+        return bf16 ? launch_split<true, true, false, false>(q, count, stream)
+                    : launch_split<false, true, false, false>(q, count, stream);
+    return bf16 ? launch_split<true, false, false, false>(q, count, stream)
+                : launch_split<false, false, false, false>(q, count, stream);
 }
 
 hipError_t launch_gemv_b3(const bl_linear_ex_problem *const *q, int count, bool bf16,
                           hipStream_t stream)
 {
-    return bf16 ? launch_split<true, false, true>(q, count, stream)
-                : launch_split<false, false, true>(q, count, stream);
+    return bf16 ? launch_split<true, false, true, false>(q, count, stream)
+                : launch_split<false, false, true, false>(q, count, stream);
+}
+
+hipError_t launch_gemv_tiles(const bl_linear_ex_problem *const *q, int count, bool bf16,
+                             hipStream_t stream)
+{
+    return bf16 ? launch_split<true, false, false, true>(q, count, stream)
+                : launch_split<false, false, false, true>(q, count, stream);
+}
+
+// Decode tiles from two-bit rows: output chunk c (16 bytes) of tile (row group rg, super-step
+// T) holds, for lane l = c % 64 (r = l % 16, g = l / 16), words 16 T + 4 g .. + 3 of row
+// 16 rg + r; words past the row and rows past N are zero.
+__global__ __launch_bounds__(256) void pack_tiles_kernel(const uint32_t *__restrict__ P, int N,
+                                                         int words, int supers, int64_t chunks,
+                                                         uint4 *__restrict__ out)
+{
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks)
+        return;
+    const int l = (int)(c & 63);
+    const int64_t tile = c >> 6;
+    const int T = (int)(tile % supers);
+    const int64_t rg = tile / supers;
+    const int64_t row = rg * 16 + (l & 15);
+    const int w0 = 16 * T + 4 * (l >> 4);
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (row < N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (w0 + i < words)
+                v[i] = P[row * words + w0 + i];
+    }
+    out[c] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+int64_t tiles_bytes(int64_t N, int64_t K)
+{
+    return ((N + 15) / 16) * ((K / 16 + 15) / 16) * 1024;
+}
+
+hipError_t launch_pack_tiles(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
+                             hipStream_t stream)
+{
+    const int words = (int)(K / 16), supers = (words + 15) / 16;
+    const int64_t chunks = tiles_bytes(N, K) / 16;
+    if (chunks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                       P, (int)N, words, supers, chunks, reinterpret_cast<uint4 *>(out));
+    return hipGetLastError();
 }
 
 }  // namespace bl

@@ -557,6 +557,40 @@ bl_status bitlinear_pack_b3(const uint32_t *W_packed, int64_t N, int64_t K, uint
 bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int count, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Decode tiles: the same two-bit codes arranged for the one-token product.
+ *
+ * SLM750-Edge card, "Performance": single-token decode is bandwidth-bound, so its weight
+ * stream should run at the memory's rate.  The one-token product feeds the int8 matrix unit
+ * 16 weight rows at a time, one 16-byte piece of each of 16 rows per lane group, and from
+ * [N][K/16] rows each of its load instructions gathers 16 rows x 64 bytes (measured: 3.55
+ * TB/s, against 5.0 TB/s for 1 KB contiguous per instruction).  The tile layout (this
+ * library's own, not the pages') stores every group of 16 rows (16 rg .. 16 rg + 15, rows past
+ * N zero) and every 256 weights of K (super-step T, words 16 T .. 16 T + 15 of each row, words
+ * past K/16 zero) as one contiguous KB: 16-byte chunk l = 16 g + r (r, g in 0..15, 0..3) holds
+ * words 16 T + 4 g .. 16 T + 4 g + 3 of row 16 rg + r.  Tile (rg, T) starts at byte
+ * (rg * ceil(K / 256) + T) * 1024.  Same codes, same bytes per weight (plus the padding).
+ * ------------------------------------------------------------------------------------- */
+
+/* Bytes of the tile layout of an N x K weight matrix: ceil(N / 16) * ceil(K / 256) * 1024
+ * (0 for N < 0 or K not a positive multiple of 16). */
+int64_t bitlinear_tiles_bytes(int64_t N, int64_t K);
+
+/* Two-bit packed codes W_packed [N][K/16] -> W_tiles [bitlinear_tiles_bytes(N, K) bytes].
+ * N == 0 is a no-op.  Errors: BL_ERR_NULL, BL_ERR_SHAPE (K not a positive multiple of 16, or
+ * past the limits of bitlinear_pack_codes), BL_ERR_ALIGN (both 16-byte aligned). */
+bl_status bitlinear_pack_tiles(const uint32_t *W_packed, int64_t N, int64_t K, uint32_t *W_tiles,
+                               void *stream);
+
+/* The fused one-token layer call (bitlinear_linear_grouped's fused form at M == 1:
+ * activation quantization, product and epilogue in one launch) on tiled weights: each
+ * problem's W_packed points to the problem's tiles (16-byte aligned).  Results are
+ * bit-identical to bitlinear_linear_grouped on the same codes in the two-bit layout.  Every
+ * problem with N > 0 needs M == 1 (or M == 0: skipped), K % 64 == 0 and K <= 12288 (the
+ * one-token kernel's limits), BL_ERR_SHAPE otherwise; X_q and x_scale are optional outputs.
+ * Other errors as for bitlinear_linear_grouped; nothing is launched on an error. */
+bl_status bitlinear_linear_tiles_grouped(const bl_linear_problem *problems, int count, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * Measurement helpers (not part of the method): what this GPU attains, so that a kernel's
  * roofline can be quoted against a measured peak beside the published one.
  * ------------------------------------------------------------------------------------- */

@@ -401,6 +401,38 @@ def test_training_entry_points_validation(L, bl):
     assert gwt(N=0, dW=None) == BL_OK
 
 
+def test_tiles_entry_points_validation(L, bl):
+    assert L.bitlinear_tiles_bytes(16, 256) == 1024 and L.bitlinear_tiles_bytes(17, 256) == 2048
+    assert L.bitlinear_tiles_bytes(16, 272) == 2048 and L.bitlinear_tiles_bytes(0, 256) == 0
+    assert L.bitlinear_tiles_bytes(16, 40) == 0 and L.bitlinear_tiles_bytes(-1, 256) == 0
+    pk = L.bitlinear_pack_tiles
+    assert pk(None, 4, 64, B, None) == BL_ERR_NULL
+    assert pk(A, 4, 40, B, None) == BL_ERR_SHAPE
+    assert pk(A, -1, 64, B, None) == BL_ERR_SHAPE
+    assert pk(A + 4, 4, 64, B, None) == BL_ERR_ALIGN
+    assert pk(A, 4, 64, B + 8, None) == BL_ERR_ALIGN
+    assert pk(None, 0, 64, None, None) == BL_OK
+    g = L.bitlinear_linear_tiles_grouped
+
+    def call(**kw):
+        d = dict(X=A, norm_weight=None, W_packed=B, gamma=C, Y=D, X_q=None, x_scale=None,
+                 M=1, N=4, K=64, x_dtype=0, eps=1e-6)
+        d.update(kw)
+        arr = (bl._LinearProblem * 1)()
+        arr[0] = bl._LinearProblem(**d)
+        return g(ctypes.addressof(arr), 1, None)
+
+    assert g(None, 1, None) == BL_ERR_NULL
+    assert call(X=None) == BL_ERR_NULL
+    assert call(M=2) == BL_ERR_SHAPE              # one token only
+    assert call(K=80) == BL_ERR_SHAPE             # K % 64 != 0
+    assert call(K=12288 + 64) == BL_ERR_SHAPE     # past the one-token kernel's row length
+    assert call(K=40) == BL_ERR_SHAPE
+    assert call(x_dtype=2) == BL_ERR_DTYPE
+    assert call(W_packed=B + 4) == BL_ERR_ALIGN
+    assert call(M=0) == BL_OK
+
+
 def test_b3_entry_points_validation(L, bl):
     assert L.bitlinear_b3_row_bytes(80) == 16 and L.bitlinear_b3_row_bytes(96) == 32
     assert L.bitlinear_b3_row_bytes(2560) == 512 and L.bitlinear_b3_row_bytes(0) == 0
