@@ -904,7 +904,7 @@ def main():
     if args.summarize_pmc:
         cmd = ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- python3 "
                f"bench.py --workload {args.workload} --steps 3 --warmup 1 --no-cpu-baseline "
-               "--copy-calibration")
+               "--min-warmup-s 0.2 --copy-calibration")
         rec = summarize_pmc(*args.summarize_pmc, args.workload, cmd)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
         old = {}
