@@ -35,6 +35,15 @@ FLAGS = [
     "-Wall",
 ]
 
+# Per-source additions.  The one-token kernels keep their MFMA accumulators in ordinary VGPRs:
+# the decode-tile product accumulates four planes separately across wave-uniform branches, and
+# in the accumulation registers the compiler copied all four in and out around every
+# super-step (32 register moves per 16 weight rows x 256 weights, each read stalling on the
+# MFMA that had just written it).
+SOURCE_FLAGS = {
+    "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def build(verbose: bool = False, output: str = LIBRARY, extra_flags=(), extra_link_flags=()) -> str:
     """Compile every source and link the shared library (to `output`, with `extra_flags` on
@@ -44,7 +53,8 @@ def build(verbose: bool = False, output: str = LIBRARY, extra_flags=(), extra_li
 
         def compile_one(src_obj):
             src, obj = src_obj
-            cmd = [HIPCC, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, ()), *extra_flags, "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             return src, subprocess.run(cmd, capture_output=True, text=True)

@@ -28,7 +28,10 @@
 // Product: v_mfma_i32_16x16x64_i8 with 16 weight rows as the B operand (a lane (r, g) holds
 // words 16t + 4g .. 16t + 4g + 3 of row r, one 16-byte load per super-step t of 256 weights,
 // expanded to 64 * c with one shift and one mask per four weights; see plane64) and the
-// token's codes as the A operand.  Only row 0 of the output is used: every lane reads the
+// token's codes as the A operand.  On decode tiles the same codes are stored plane-major with
+// three of the four planes offset by one, which leaves one mask per four weights and no shift
+// (the instruction count of the expansion set the kernel's tail); the offsets are removed
+// exactly with the sum of the affected activation codes.  Only row 0 of the output is used: every lane reads the
 // token's codes for its k range (lanes of one lane group read the same 16 bytes, a broadcast),
 // so the other 15 rows of the result repeat row 0 and are ignored.
 #include <algorithm>
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     __shared__ float s_amax[kGvWaves];
     __shared__ double s_ss[kGvWaves];
     __shared__ int s_red[kGvWaves][G][16];
+    __shared__ int s_csum[kGvWaves];        // decode tiles: per wave, sum of offset-plane codes
     extern __shared__ __align__(16) unsigned char lds[];
 
     int prob = 0;
@@ -176,7 +180,12 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     // ---- weight loads: rows n0 .. n0+15 (rows past N read as zero), the first round of
     // this wave's super-steps [t_begin, t_end)
     // Decode tiles (TL): the row group's super-step T is one contiguous KB at T * 1024, lane l
-    // at byte 16 l (the words this lane loads from the two-bit rows), zero-padded.
+    // at byte 16 l: the codes this lane loads from the two-bit rows, arranged plane-major so
+    // that each MFMA operand is one mask per word.  Field j of byte b of dword i holds the
+    // code of k = 256 T + 64 g + 16 j + 4 i + b: for j = 3 (the byte's top bits) in two's
+    // complement, so the masked byte is 64 c; for j < 3 as c + 1, so the masked byte is
+    // 4^j (c + 1) and the sum over plane j exceeds 4^j times its share of the dot product by
+    // 4^j times the sum of its activation codes, removed once in the epilogue (s_csum).
     const int64_t tile_bytes = (int64_t)supers * 1024;
     const unsigned char *const wrow = reinterpret_cast<const unsigned char *>(p.W) +
                                       (TL ? (int64_t)rg * tile_bytes : (int64_t)n0 * row_bytes);
@@ -250,6 +259,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     };
     float amax = 0.0f;
     double ss = 0.0;
+    int csum = 0;
 #pragma unroll
     for (int c0 = 0; c0 < CH; c0 += 4) {
         if (c0 * kGvThreads < nchunk) {      // block-uniform
@@ -302,6 +312,11 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
                         const int q = QPC * i + h;
                         const char4 cq = quant4(NORM ? mul4(x[h], gq(c0 + u, h)) : x[h], inv);
                         *reinterpret_cast<char4 *>(codes + 4 * q) = cq;
+                        if (TL && ((q >> 2) & 3) != 3) {
+                            int cw;
+                            __builtin_memcpy(&cw, &cq, 4);
+                            csum = __builtin_amdgcn_sdot4(cw, 0x01010101, csum, false);
+                        }
                         if (first && p.Xq_out)
                             *reinterpret_cast<char4 *>(p.Xq_out + 4 * q) = cq;
                     }
@@ -316,6 +331,18 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     constexpr int EPS = B3 ? 320 : 256;      // weights per super-step
     for (int q = K / 4 + tid; q < EPS / 4 * supers; q += kGvThreads)
         *reinterpret_cast<uint32_t *>(codes + 4 * q) = 0u;
+    if (TL) {
+        // Integer sums, exact in any order: each row of 16 lanes by shifts (lane 15 of the
+        // row ends with the row's sum), then the four rows' last lanes.
+        csum += __builtin_amdgcn_update_dpp(0, csum, 0x111, 0xF, 0xF, false);   // row_shr:1
+        csum += __builtin_amdgcn_update_dpp(0, csum, 0x112, 0xF, 0xF, false);   // row_shr:2
+        csum += __builtin_amdgcn_update_dpp(0, csum, 0x114, 0xF, 0xF, false);   // row_shr:4
+        csum += __builtin_amdgcn_update_dpp(0, csum, 0x118, 0xF, 0xF, false);   // row_shr:8
+        const int wsum = __builtin_amdgcn_readlane(csum, 15) + __builtin_amdgcn_readlane(csum, 31) +
+                         __builtin_amdgcn_readlane(csum, 47) + __builtin_amdgcn_readlane(csum, 63);
+        if (lane == 0)
+            s_csum[wave] = wsum;
+    }
     __syncthreads();
     load_round(t_begin, EARLY, S);
     __builtin_amdgcn_sched_barrier(0);
@@ -325,6 +352,10 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 #pragma unroll
     for (int gi = 0; gi < G; ++gi)
         acc[gi] = v4i{0, 0, 0, 0};
+    v4i accp[TL ? 4 : 1];                    // decode tiles: one accumulator per plane
+#pragma unroll
+    for (int j = 0; j < (TL ? 4 : 1); ++j)
+        accp[j] = v4i{0, 0, 0, 0};
     for (int base = t_begin; base < t_end; base += S) {
         if (base != t_begin) {
             load_round(base, 0, S);
@@ -349,6 +380,18 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
                     acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[i], op[i], acc[0], 0, 0, 0);
                 acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
                     av[4], v4i{(int)op4[0], (int)op4[1], (int)op4[2], (int)op4[3]}, acc[0], 0, 0, 0);
+            } else if (TL && T < t_end) {    // wave-uniform
+                // Plane j of the lane's four words holds the codes of k = 256 T + 64 g + 16 j
+                // + 0..15 in byte order (see tile_plane): one mask per word, no shift.
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4i av = *reinterpret_cast<const v4i *>(codes + 256 * T + 64 * g + 16 * j);
+                    const v4u ww = w[0][t];
+                    const uint32_t m = 0x03030303u << (2 * j);
+                    accp[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        av, v4i{(int)(ww.x & m), (int)(ww.y & m), (int)(ww.z & m), (int)(ww.w & m)}, accp[j],
+                        0, 0, 0);
+                }
             } else if (T < t_end) {          // wave-uniform
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -364,11 +407,13 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
 
     // ---- slices of one row group meet in LDS (integer sums: exact, fixed order)
     int s1 = acc[0].x, s2 = acc[G - 1].x;    // lanes 0..15: 64 * D[0][n0 + r]
+    if (TL)    // 64x the slice's sum with the offset planes' codes counted once too many
+        s1 = accp[3].x + 4 * accp[2].x + 16 * accp[1].x + 64 * accp[0].x;
     if (ksl > 0) {
         if (lane < 16) {
 #pragma unroll
             for (int gi = 0; gi < G; ++gi)
-                s_red[wave][gi][lane] = acc[gi].x;
+                s_red[wave][gi][lane] = gi ? s2 : s1;
         }
         __syncthreads();
         if (slice != 0)
@@ -384,6 +429,9 @@ __global__ __launch_bounds__(kGvThreads) void gemv_kernel(GvBatch b)
     }
     if (!out_lane)
         return;
+    if (TL)
+        for (int v = 0; v < kGvWaves; ++v)
+            s1 -= 64 * s_csum[v];
     // y = fl32(acc * gamma * s_x): gamma * s_x is exact in fp64 (two 24-bit significands),
     // so this is the correctly rounded value of the exact product.
     float y = (float)((double)(s1 >> 6) * ((double)gammaf * (double)sx));
@@ -525,14 +573,26 @@ __global__ __launch_bounds__(256) void pack_tiles_kernel(const uint32_t *__restr
     const int64_t rg = tile / supers;
     const int64_t row = rg * 16 + (l & 15);
     const int w0 = 16 * T + 4 * (l >> 4);
+    // Row words w0 + j hold k = 256 T + 64 g + 16 j + 4 i + b at bits 8 b + 2 i (two-bit rows);
+    // the chunk's dword i holds the same code at bits 8 b + 2 j, offset by one for j < 3.
     uint32_t v[4] = {0u, 0u, 0u, 0u};
     if (row < N) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (w0 + i < words)
-                v[i] = P[row * words + w0 + i];
+        for (int j = 0; j < 4; ++j)
+            if (w0 + j < words)
+                v[j] = P[row * words + w0 + j];
     }
-    out[c] = make_uint4(v[0], v[1], v[2], v[3]);
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t f = (v[j] >> (8 * b + 2 * i)) & 3u;
+                o[i] |= (j < 3 ? (f + 1u) & 3u : f) << (8 * b + 2 * j);
+            }
+    out[c] = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 int64_t tiles_bytes(int64_t N, int64_t K)

@@ -564,11 +564,15 @@ bl_status bitlinear_linear_b3_grouped(const bl_linear_problem *problems, int cou
  * 16 weight rows at a time, one 16-byte piece of each of 16 rows per lane group, and from
  * [N][K/16] rows each of its load instructions gathers 16 rows x 64 bytes (measured: 3.55
  * TB/s, against 5.0 TB/s for 1 KB contiguous per instruction).  The tile layout (this
- * library's own, not the pages') stores every group of 16 rows (16 rg .. 16 rg + 15, rows past
- * N zero) and every 256 weights of K (super-step T, words 16 T .. 16 T + 15 of each row, words
- * past K/16 zero) as one contiguous KB: 16-byte chunk l = 16 g + r (r, g in 0..15, 0..3) holds
- * words 16 T + 4 g .. 16 T + 4 g + 3 of row 16 rg + r.  Tile (rg, T) starts at byte
- * (rg * ceil(K / 256) + T) * 1024.  Same codes, same bytes per weight (plus the padding).
+ * library's own, not the pages') stores every group of 16 rows (16 rg .. 16 rg + 15) and every
+ * 256 weights of K (super-step T) as one contiguous KB: 16-byte chunk l = 16 g + r (r, g in
+ * 0..15, 0..3) holds the codes of row 16 rg + r for k = 256 T + 64 g .. 256 T + 64 g + 63 (the
+ * weights that the chunk's lane multiplies) as four 32-bit little-endian dwords i = 0..3, and
+ * bits 8 b + 2 j .. 8 b + 2 j + 1 of dword i hold the code c of k = 256 T + 64 g + 16 j + 4 i + b:
+ * as c mod 4 (two's complement) for j = 3, as c + 1 for j = 0, 1, 2.  With one mask per dword
+ * the product then reads every plane j as int8 values 4^j (c + 1) or 64 c, without shifts.
+ * Rows past N and k past K hold c = 0.  Tile (rg, T) starts at byte (rg * ceil(K / 256) + T) *
+ * 1024.  Same codes, same bytes per weight (plus the padding).
  * ------------------------------------------------------------------------------------- */
 
 /* Bytes of the tile layout of an N x K weight matrix: ceil(N / 16) * ceil(K / 256) * 1024

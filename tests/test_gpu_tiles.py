@@ -43,16 +43,21 @@ def rel_err(a, b):
     return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-300))) if a.size else 0.0
 
 
-def tile_layout(P, N, K):
-    """The documented layout: tile (rg, T) is 64 chunks of 16 bytes; chunk 16 g + r holds words
-    16 T + 4 g .. + 3 of row 16 rg + r; rows past N and words past K / 16 are zero."""
-    words = K // 16
-    supers = (words + 15) // 16
+def tile_layout(C, N, K):
+    """The documented layout, written out from the codes C [N][K]: tile (rg, T) is 64 chunks of
+    16 bytes; chunk 16 g + r holds row 16 rg + r as four dwords i, and field j (bits 8 b + 2 j)
+    of byte b of dword i holds the code c of k = 256 T + 64 g + 16 j + 4 i + b, as c mod 4 for
+    j = 3 and as c + 1 for j < 3; rows past N and k past K hold c = 0."""
+    supers = (K // 16 + 15) // 16
     groups = (N + 15) // 16
-    Pp = np.zeros((groups * 16, supers * 16), np.uint32)
-    Pp[:N, :words] = P.view(np.uint32).reshape(N, words)
-    t = Pp.reshape(groups, 16, supers, 4, 4)          # [rg][r][T][g][i]
-    return t.transpose(0, 2, 3, 1, 4).reshape(-1)     # [rg][T][g][r][i]
+    Cp = np.zeros((groups * 16, supers * 256), np.int64)
+    Cp[:N, :K] = C
+    c = Cp.reshape(groups, 16, supers, 4, 4, 4, 4)               # [rg][r][T][g][j][i][b]
+    j = np.arange(4).reshape(4, 1, 1)
+    b = np.arange(4).reshape(1, 1, 4)
+    enc = np.where(j == 3, c & 3, (c + 1) & 3)
+    dw = (enc << (8 * b + 2 * j)).sum(axis=(4, 6))             # [rg][r][T][g][i]
+    return dw.transpose(0, 2, 3, 1, 4).reshape(-1).astype(np.uint32)
 
 
 @pytest.mark.parametrize("N,K", [(1, 16), (16, 256), (17, 272), (300, 768), (129, 9728), (8, 12288),
@@ -63,7 +68,7 @@ def test_pack_tiles(torch, bl, orc, N, K):
     T = bl.pack_tiles(dev(torch, P.view(np.int32)), K)
     torch.cuda.synchronize()
     assert T.numel() * 4 == bl.tiles_bytes(N, K)
-    assert np.array_equal(host(T).view(np.uint32), tile_layout(P, N, K))
+    assert np.array_equal(host(T).view(np.uint32), tile_layout(C, N, K))
 
 
 SHAPES = [(1, 64), (37, 128), (300, 768), (768, 768), (129, 2048), (96, 9728), (40, 12288),
@@ -112,6 +117,60 @@ def test_linear_tiles(torch, bl, orc, N, K, dtype, norm):
     Y = host(tiles["Y"])
     assert np.array_equal(Y == 0, Y_ref == 0), label
     assert rel_err(Y[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL, label
+
+
+def extreme_case(kind, N, K):
+    """Activations and codes at the ends of the ranges the offset planes and their correction
+    must hold exactly: every activation code +-127 against weights all +1, all -1 or mixed,
+    a one-hot row, and a row whose codes cancel within each plane."""
+    k = np.arange(K)
+    if kind == "all_plus":
+        X, C = np.full((1, K), 3.0, np.float32), np.ones((N, K), np.int8)
+    elif kind == "all_minus":
+        X, C = np.full((1, K), -3.0, np.float32), -np.ones((N, K), np.int8)
+    elif kind == "mixed_max":
+        X = np.where(k % 3 == 0, 5.0, -5.0).astype(np.float32)[None, :]
+        C = np.where((np.arange(N)[:, None] + k) % 2 == 0, 1, -1).astype(np.int8)
+    elif kind == "one_hot":
+        X = np.zeros((1, K), np.float32)
+        X[0, K - 1] = -2.5
+        C = workloads.ternary((N, K), (514, N, K))
+    else:                                       # "cancel": +-x in neighbouring codes
+        X = np.where(k % 2 == 0, 1.0, -1.0).astype(np.float32)[None, :]
+        C = workloads.ternary((N, K), (515, N, K))
+    return X, C
+
+
+@pytest.mark.parametrize("kind", ["all_plus", "all_minus", "mixed_max", "one_hot", "cancel"])
+@pytest.mark.parametrize("N,K", [(48, 12288), (33, 9728), (16, 64)])
+def test_linear_tiles_extremes(torch, bl, orc, kind, N, K):
+    X, C = extreme_case(kind, N, K)
+    P = bl.pack_codes(dev(torch, C))
+    gt = dev(torch, np.array([GAMMA], np.float32))
+
+    def call(tiles):
+        d = dict(X=dev(torch, X), gamma=gt, eps=1e-6, Y=torch.empty((1, N), device="cuda"),
+                 X_q=torch.empty((1, K), dtype=torch.int8, device="cuda"),
+                 x_scale=torch.empty(1, device="cuda"))
+        if tiles:
+            d["W_tiles"] = bl.pack_tiles(P, K)
+            bl.linear_tiles_grouped([d])
+        else:
+            d["W_packed"] = P
+            bl.linear_grouped([d])
+        return d
+    a, b = call(True), call(False)
+    torch.cuda.synchronize()
+    for key in ("Y", "X_q", "x_scale"):
+        assert torch.equal(a[key], b[key]), (kind, N, K, key)
+    q_ref, s_ref = orc.quantize_acts(X, None, 1e-6)
+    assert np.array_equal(host(a["X_q"]), q_ref)
+    acc = orc.matmul(q_ref, C)
+    Y_ref = orc.epilogue(acc, s_ref, GAMMA)
+    Y = host(a["Y"])
+    assert np.array_equal(Y == 0, Y_ref == 0), (kind, N, K)
+    nz = Y_ref != 0
+    assert rel_err(Y[nz], Y_ref[nz]) <= REL, (kind, N, K)
 
 
 def test_linear_tiles_layer_set(torch, bl):
