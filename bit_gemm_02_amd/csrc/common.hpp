@@ -156,6 +156,18 @@ __device__ __forceinline__ void block_sync()
     asm volatile("" ::: "memory");
 }
 
+// Barrier for LDS traffic only: every LDS access of this wave has completed (lgkmcnt(0)),
+// then s_barrier.  __syncthreads() also waits for every outstanding vector-memory load of the
+// wave (vmcnt(0)); where loads still in flight do not feed the LDS data being handed over,
+// this barrier lets the waves go on without them.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (7 << 4) | (0 << 8));   // vmcnt max, lgkmcnt 0
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0): wait until at most N vector-memory loads of this wave
 // (direct-to-LDS ones included) are still in flight and every LDS read of this wave has
 // returned.  The second part matters before a barrier that hands an LDS buffer back to
