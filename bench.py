@@ -127,6 +127,14 @@ def decode_on_tiles(wl: workloads.Workload, M_pre: int) -> bool:
             all(m.K % 64 == 0 and m.K <= 12288 for m in wl.matrices))
 
 
+def prefill_on_quad_rows(wl: workloads.Workload, M_pre: int) -> bool:
+    """Whether the step's prefill weights are quantized into (or packed once as) the quad-row
+    layout and the products read them there: where the products are a launch of their own
+    (128 x 256 tiles) and every matrix fits the layout (N % 4 == 0, K % 128 == 0)."""
+    return (not mixed_one_launch(wl, M_pre) and M_pre > 16 and
+            all(m.N % 4 == 0 and m.K % 128 == 0 for m in wl.matrices))
+
+
 def gemv_layout(name: str) -> str:
     """'b3', 'tiles' or 'rows' for a gemv_kernel<S, BF16, PAIR, NORM, B3, TL> name."""
     args = name.split("(")[0].split("<", 1)[1].rstrip(">").split(",")
@@ -181,6 +189,7 @@ class Setup:
         # packed once from pre-ternarized codes).
         self.P_pre = [t.empty((m.N, m.K // 16), dtype=t.int32, device=dev) for m in mats]
         self.g_pre = [t.empty(1, dtype=t.float32, device=dev) for m in mats]
+        self.quad = prefill_on_quad_rows(wl, M_pre)
         if W_host is None:
             for i, m in enumerate(mats):
                 bl.pack_codes(to_dev(workloads.weight_codes(wl, i)), self.P_pre[i])
@@ -190,7 +199,11 @@ class Setup:
         if W_host is not None:
             dec_packed = bl.quantize_weights_grouped([to_dev(w) for w in W_host])
         else:
-            dec_packed = list(zip(self.P_pre, self.g_pre))
+            dec_packed = [(P.clone(), g) for P, g in zip(self.P_pre, self.g_pre)]
+        if self.quad and W_host is None:
+            # Pre-packed codes go to the quad-row layout once (the in-step quantization writes
+            # that layout itself).
+            self.P_pre = [bl.pack_quad_rows(P) for P in self.P_pre]
         packed_bytes = sum(p.numel() * 4 for p, _ in dec_packed)
         self.R_dec = int(max(1, min(4096, np.ceil(rotate_bytes / packed_bytes))))
         self.P_dec = [[p.clone() for p, _ in dec_packed] for _ in range(self.R_dec)]
@@ -299,6 +312,18 @@ class Setup:
     def mixed_one_launch(self) -> bool:
         return mixed_one_launch(self.wl, self.M_pre, self.M_dec)
 
+    def quantize_step(self, L, rp: int, stream) -> int:
+        """The step's weight + activation quantization (weights into quad rows where the
+        products read them there)."""
+        fn = L.bitlinear_quantize_step_quad_rows if self.quad else L.bitlinear_quantize_step
+        return fn(self._addr(self.wq_tables[rp]), self.count, self.ws_ptr, self.ws_bytes,
+                  self._addr(self.aq_pre_tables[rp]), self.count, stream)
+
+    def prefill(self, L, stream) -> int:
+        """The step's prefill products as their own launch (on quad rows where they fit)."""
+        fn = L.bitlinear_forward_quad_rows_grouped if self.quad else L.bitlinear_forward_grouped
+        return fn(self._addr(self.fwd_pre_table), self.count, stream)
+
     def decode_leg(self, L, rd: int, stream) -> int:
         """The step's decode leg as its own launch (tiles or two-bit rows)."""
         if self.dec_tiles:
@@ -355,9 +380,7 @@ class Setup:
         if self.wq_tables:
             # Weight quantization and the prefill activations' quantization in one call: the
             # gamma pass and the activation codes share a launch, the pack pass follows.
-            rc = L.bitlinear_quantize_step(self._addr(self.wq_tables[rp]), n, self.ws_ptr,
-                                           self.ws_bytes, self._addr(self.aq_pre_tables[rp]), n,
-                                           stream)
+            rc = self.quantize_step(L, rp, stream)
         else:
             rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[rp]), n, stream)
         assert rc == 0, rc
@@ -371,7 +394,7 @@ class Setup:
         else:
             # 128 x 256 product tiles: the products, then the decode leg (the two launches the
             # mixed call makes for such a batch, made here so each can be bracketed).
-            rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+            rc = self.prefill(L, stream)
             assert rc == 0, rc
             mark("t_pre")
             rc = self.decode_leg(L, rd, stream)
@@ -383,14 +406,17 @@ class Setup:
         L = self.bl.lib()
         n = self.count
         if key == "prefill_gemm":
-            rc = L.bitlinear_forward_grouped(self._addr(self.fwd_pre_table), n, stream)
+            rc = self.prefill(L, stream)
         elif key == "weight_and_act_quant":
-            rc = L.bitlinear_quantize_step(self._addr(self.wq_tables[i % self.R_pre]), n, self.ws_ptr,
-                                           self.ws_bytes, self._addr(self.aq_pre_tables[i % self.R_pre]),
-                                           n, stream)
+            rc = self.quantize_step(L, i % self.R_pre, stream)
         elif key == "prefill_and_decode":
-            rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
-                                           self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
+            if self.mixed_one_launch():
+                rc = L.bitlinear_forward_mixed(self._addr(self.fwd_pre_ex_table), n,
+                                               self._addr(self.lin_dec_tables[i % self.R_dec]), n, stream)
+            else:       # the step's two launches
+                rc = self.prefill(L, stream)
+                assert rc == 0, rc
+                rc = self.decode_leg(L, i % self.R_dec, stream)
         elif key == "decode_linear":
             rc = self.decode_leg(L, i % self.R_dec, stream)
         elif key == "decode_linear_rows":
@@ -399,6 +425,11 @@ class Setup:
             rc = L.bitlinear_linear_b3_grouped(self._addr(self.lin_dec_b3_tables[i % self.R_dec]), n, stream)
         elif key == "act_quant_prefill":
             rc = L.bitlinear_quantize_acts_grouped(self._addr(self.aq_pre_tables[i % self.R_pre]), n, stream)
+        elif self.quad:
+            # Weight quantization alone, into the quad-row layout (the step call without
+            # activations).
+            rc = L.bitlinear_quantize_step_quad_rows(self._addr(self.wq_tables[i % self.R_pre]), n,
+                                                     self.ws_ptr, self.ws_bytes, None, 0, stream)
         else:
             rc = L.bitlinear_quantize_weights_grouped(self._addr(self.wq_tables[i % self.R_pre]), n,
                                                        self.ws_ptr, self.ws_bytes, stream)
@@ -1103,7 +1134,8 @@ def main():
                              "speedup_vs_two_bit": round(ms["decode_linear"] / ms_b3, 3),
                              "note": "same codes in the base-3 layout (1.6 bits per weight), "
                                      "fused decode call; not part of the step"}},
-        "prefill": {"gemm_tops": round(gemm_tops, 2), "frac_int8": round(gemm_tops / INT8_PEAK_TOPS, 4),
+        "prefill": {"weight_layout": "quad_rows" if setup.quad else "rows",
+                    "gemm_tops": round(gemm_tops, 2), "frac_int8": round(gemm_tops / INT8_PEAK_TOPS, 4),
                     "gemm_gbps": round(gemm_gbps, 1), "ops_per_byte": round(ai, 1),
                     "frac_attainable": round(gemm_tops / attainable, 4),
                     "ops": ops, "us_gemm": round(ms["prefill_gemm"] * 1e3, 3),

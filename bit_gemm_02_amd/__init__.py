@@ -189,6 +189,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_tiles.restype = ctypes.c_int
     L.bitlinear_linear_tiles_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_linear_tiles_grouped.restype = ctypes.c_int
+    L.bitlinear_pack_quad_rows.argtypes = [P, I64, I64, P, P]
+    L.bitlinear_pack_quad_rows.restype = ctypes.c_int
+    L.bitlinear_quantize_step_quad_rows.argtypes = [P, ctypes.c_int, P, ctypes.c_size_t, P, ctypes.c_int, P]
+    L.bitlinear_quantize_step_quad_rows.restype = ctypes.c_int
+    L.bitlinear_forward_quad_rows_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_forward_quad_rows_grouped.restype = ctypes.c_int
     L.bitlinear_calib_stream.argtypes = [P, I64, P, P]
     L.bitlinear_calib_stream.restype = ctypes.c_int
     L.bitlinear_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -360,10 +366,12 @@ def quantize_acts_grouped(Xs: Sequence[torch.Tensor],
 
 def quantize_step(Ws: Sequence[torch.Tensor], Xs: Sequence[torch.Tensor],
                   norm_weights: Optional[Sequence[Optional[torch.Tensor]]] = None,
-                  eps: float = 1e-6, w_outputs=None, x_outputs=None, workspace=None, stream=None):
+                  eps: float = 1e-6, w_outputs=None, x_outputs=None, workspace=None, stream=None,
+                  quad_rows: bool = False):
     """Weight quantization of Ws and activation quantization of Xs in one call (the gamma pass
     and the activation codes share a launch when they can); returns ([(W_packed, gamma)],
-    [(X_q, x_scale)]), bit for bit those of the two grouped calls."""
+    [(X_q, x_scale)]), bit for bit those of the two grouped calls.  quad_rows: the packed
+    words in the quad-row layout (bitlinear_quantize_step_quad_rows)."""
     nw, na = len(Ws), len(Xs)
     wa = (_WeightProblem * max(nw, 1))()
     wouts = []
@@ -393,10 +401,10 @@ def quantize_step(Ws: Sequence[torch.Tensor], Xs: Sequence[torch.Tensor],
     ws_bytes = quantize_weights_workspace_bytes(max(nw, 1))
     if workspace is None and nw:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
-    _check("bitlinear_quantize_step",
-           lib().bitlinear_quantize_step(ctypes.addressof(wa), nw, _ptr(workspace),
-                                         0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                         ctypes.addressof(xa), na, _stream(stream)))
+    fn = "bitlinear_quantize_step_quad_rows" if quad_rows else "bitlinear_quantize_step"
+    _check(fn, getattr(lib(), fn)(ctypes.addressof(wa), nw, _ptr(workspace),
+                                  0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                  ctypes.addressof(xa), na, _stream(stream)))
     return wouts, xouts
 
 
@@ -417,9 +425,10 @@ def forward(X_q: torch.Tensor, x_scale: torch.Tensor, W_packed: torch.Tensor,
     return (Y, acc) if return_acc else Y
 
 
-def forward_grouped(problems: Sequence[dict], stream=None) -> None:
+def forward_grouped(problems: Sequence[dict], stream=None, quad_rows: bool = False) -> None:
     """Problems as dicts with keys X_q, x_scale, W_packed, gamma, Y and optional acc; all
-    outputs preallocated.  Decode-sized problems (M <= 16) share one launch, the rest another."""
+    outputs preallocated.  Decode-sized problems (M <= 16) share one launch, the rest another.
+    quad_rows: W_packed in the quad-row layout (bitlinear_forward_quad_rows_grouped)."""
     count = len(problems)
     arr = (_ForwardProblem * max(count, 1))()
     for i, p in enumerate(problems):
@@ -427,8 +436,8 @@ def forward_grouped(problems: Sequence[dict], stream=None) -> None:
         N = p["W_packed"].shape[0]
         arr[i] = _ForwardProblem(_ptr(p["X_q"]), _ptr(p["x_scale"]), _ptr(p["W_packed"]),
                                  _ptr(p["gamma"]), _ptr(p["Y"]), _ptr(p.get("acc")), M, N, K)
-    _check("bitlinear_forward_grouped",
-           lib().bitlinear_forward_grouped(ctypes.addressof(arr), count, _stream(stream)))
+    fn = "bitlinear_forward_quad_rows_grouped" if quad_rows else "bitlinear_forward_grouped"
+    _check(fn, getattr(lib(), fn)(ctypes.addressof(arr), count, _stream(stream)))
 
 
 def linear_fused(M: int, K: int) -> bool:
@@ -741,6 +750,21 @@ def linear_tiles_grouped(problems: Sequence[dict], stream=None) -> None:
     arr = linear_tiles_table(problems)
     _check("bitlinear_linear_tiles_grouped",
            lib().bitlinear_linear_tiles_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+
+
+# ---------------------------------------------------------------- quad rows
+
+def pack_quad_rows(W_packed: torch.Tensor, W_quad: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Two-bit packed codes [N, K/16] -> the quad-row layout (a new [N, K/16] int32 tensor
+    unless W_quad is given; N % 4 == 0, K % 128 == 0)."""
+    _dev(W_packed, "W_packed", torch.int32)
+    N, words = W_packed.shape
+    if W_quad is None:
+        W_quad = torch.empty_like(W_packed)
+    _check("bitlinear_pack_quad_rows", lib().bitlinear_pack_quad_rows(_ptr(W_packed), N, words * 16,
+                                                                        _ptr(W_quad), _stream(stream)))
+    return W_quad
 
 
 # ----------------------------------------------------------------- measurement helpers

@@ -43,6 +43,15 @@ bl_status check_weight(const bl_weight_problem &p)
     return BL_OK;
 }
 
+// The quad-row layout's shape limits: whole groups of four rows and whole 128-weight stages
+// (so the layout is a permutation of the rows with no padding), and word indices below 2^32.
+bl_status check_quad(int64_t N, int64_t K)
+{
+    if (N % 4 != 0 || K % 128 != 0 || N * (K / 16) > (int64_t)UINT_MAX)
+        return BL_ERR_SHAPE;
+    return BL_OK;
+}
+
 bl_status check_act(const bl_act_problem &p)
 {
     if (p.M != 0 && (!p.X || !p.X_q || !p.x_scale))
@@ -339,7 +348,7 @@ const char *bitlinear_status_string(int status)
     }
 }
 
-int bitlinear_abi_version(void) { return 102; }
+int bitlinear_abi_version(void) { return 103; }
 
 size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
 {
@@ -449,9 +458,9 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int co
     return run_acts(ex, count, stream);
 }
 
-bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void *workspace,
-                                  size_t workspace_bytes, const bl_act_problem *acts, int na,
-                                  void *stream)
+static bl_status quantize_step(const bl_weight_problem *weights, int nw, void *workspace,
+                               size_t workspace_bytes, const bl_act_problem *acts, int na,
+                               void *stream, bool quad)
 {
     if (nw < 0 || na < 0 || nw > BL_MAX_GROUP || na > BL_MAX_GROUP || nw + na == 0)
         return BL_ERR_COUNT;
@@ -460,6 +469,8 @@ bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void
     // Every problem is validated before anything is launched.
     for (int i = 0; i < nw; ++i) {
         bl_status s = check_weight(weights[i]);
+        if (s == BL_OK && quad)
+            s = check_quad(weights[i].N, weights[i].K);
         if (s != BL_OK)
             return s;
     }
@@ -483,7 +494,21 @@ bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void
             return BL_ERR_WORKSPACE;
     }
     return from_hip(bl::launch_quantize_step(weights, nw, workspace, ex, na,
-                                             static_cast<hipStream_t>(stream)));
+                                             static_cast<hipStream_t>(stream), quad));
+}
+
+bl_status bitlinear_quantize_step(const bl_weight_problem *weights, int nw, void *workspace,
+                                  size_t workspace_bytes, const bl_act_problem *acts, int na,
+                                  void *stream)
+{
+    return quantize_step(weights, nw, workspace, workspace_bytes, acts, na, stream, false);
+}
+
+bl_status bitlinear_quantize_step_quad_rows(const bl_weight_problem *weights, int nw,
+                                            void *workspace, size_t workspace_bytes,
+                                            const bl_act_problem *acts, int na, void *stream)
+{
+    return quantize_step(weights, nw, workspace, workspace_bytes, acts, na, stream, true);
 }
 
 bl_status bitlinear_quantize_acts_ex_grouped(const bl_act_ex_problem *problems, int count,
@@ -546,6 +571,55 @@ bl_status bitlinear_forward(const int8_t *X_q, const float *x_scale, const uint3
 {
     bl_forward_problem p{X_q, x_scale, W_packed, gamma, Y, acc, M, N, K};
     return bitlinear_forward_grouped(&p, 1, stream);
+}
+
+bl_status bitlinear_pack_quad_rows(const uint32_t *W_packed, int64_t N, int64_t K, uint32_t *W_quad,
+                                   void *stream)
+{
+    bl_status s = check_rows(N);
+    if (s == BL_OK && N != 0 && (!W_packed || !W_quad))
+        return BL_ERR_NULL;
+    if (s == BL_OK)
+        s = check_k(K);
+    if (s == BL_OK)
+        s = check_quad(N, K);
+    if (s != BL_OK)
+        return s;
+    if (!aligned16(W_packed) || !aligned16(W_quad))
+        return BL_ERR_ALIGN;
+    return from_hip(bl::launch_pack_quad_rows(W_packed, N, K, W_quad, static_cast<hipStream_t>(stream)));
+}
+
+bl_status bitlinear_forward_quad_rows_grouped(const bl_forward_problem *problems, int count,
+                                              void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    bl_forward_ex_problem ex[BL_MAX_GROUP];
+    int n = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_forward_problem &p = problems[i];
+        bl_status s = check_forward(p);
+        if (s != BL_OK)
+            return s;
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (p.M <= bl::kDecodeMaxM)
+            return BL_ERR_SHAPE;         // the quad-row layout feeds the prefill product only
+        s = check_quad(p.N, p.K);
+        if (s != BL_OK)
+            return s;
+        ex[n++] = to_ex(p);
+        blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    if (n == 0)
+        return BL_OK;
+    return from_hip(bl::launch_forward_prefill(ex, n, static_cast<hipStream_t>(stream), true));
 }
 
 bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count, void *stream)

@@ -206,6 +206,18 @@ __device__ __forceinline__ v4i unpack_word64(uint32_t word)
     return r;
 }
 
+// Quad-row layout of packed words (N % 4 == 0, K % 128 == 0; the same words as the rows
+// [N][K/16], permuted within every group of four rows): for rows 4q .. 4q + 3 and every 128
+// weights of K (stage t, words 8t .. 8t + 7 of a row), one 128-byte line holds the four
+// rows' 32-byte pieces in row order.  Word w of row n, with wpr = K / 16 words per row, sits
+// at word ((n / 4) * (wpr / 8) + w / 8) * 32 + 8 * (n % 4) + w % 8.  `wi` is the word's
+// index in the rows layout, n * wpr + w (below 2^32).
+__device__ __forceinline__ uint32_t quad_row_word(uint32_t wi, uint32_t wpr)
+{
+    const uint32_t n = wi / wpr, w = wi - n * wpr;
+    return ((n >> 2) * (wpr >> 3) + (w >> 3)) * 32u + 8u * (n & 3u) + (w & 7u);
+}
+
 // 2-bit field of one code (+1 -> 01, 0 -> 00, -1 -> 11), from "is nonzero" and "is negative".
 __device__ __forceinline__ uint32_t code_field(bool nonzero, bool negative)
 {
@@ -413,8 +425,9 @@ __device__ __forceinline__ v4u ternary_bf16(uint32_t w, int j)
 
 // ----------------------------------------------------------------- launchers
 
+// quad: write the packed words in the quad-row layout (quad_row_word) instead of rows.
 hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *workspace,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool quad = false);
 size_t quantize_weights_workspace(int count);
 hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
                              hipStream_t stream);
@@ -437,11 +450,16 @@ hipError_t launch_gemv_tiles(const bl_linear_ex_problem *const *q, int count, bo
 int64_t tiles_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_tiles(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
                              hipStream_t stream);
-hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream);
+// quad: W_packed of every problem is in the quad-row layout (N % 4 == 0, K % 128 == 0).
+hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hipStream_t stream,
+                                  bool quad = false);
+hipError_t launch_pack_quad_rows(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
+                                 hipStream_t stream);
 // Weight quantization + activation quantization of one step (γ pass and activation codes in
 // one launch when every activation problem takes the wave kernel with one dtype).
 hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
-                                const bl_act_ex_problem *aq, int na, hipStream_t stream);
+                                const bl_act_ex_problem *aq, int na, hipStream_t stream,
+                                bool quad = false);
 // Mixed batch (prefill products + fused decode calls) in one launch: eligible when every
 // prefill product has M > 16 and takes the 128 x 128 tile, and every decode call is a fused
 // single projection (no pair, activation or residual) with one activation dtype.

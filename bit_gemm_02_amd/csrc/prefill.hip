@@ -25,13 +25,13 @@
 
 namespace bl {
 
-template <class T, bool FULL_K>
+template <class T, bool FULL_K, bool QR>
 __global__ __launch_bounds__(T::THREADS, T::WPE) void prefill_kernel(PreBatch b)
 {
-    prefill_block<T, FULL_K>(b, blockIdx.x);
+    prefill_block<T, FULL_K, QR>(b, blockIdx.x);
 }
 
-template <class T>
+template <class T, bool QR = false>
 static hipError_t launch_tiles(const bl_forward_ex_problem *q, int count, hipStream_t stream)
 {
     PreBatch b{};
@@ -39,10 +39,12 @@ static hipError_t launch_tiles(const bl_forward_ex_problem *q, int count, hipStr
     const int blocks = build_batch<T>(q, count, b, full_k);
     if (blocks == 0)
         return hipSuccess;
-    if (full_k)
-        hipLaunchKernelGGL((prefill_kernel<T, true>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
+    if (QR)     // K % 128 == 0 for every problem (checked at the boundary): one form
+        hipLaunchKernelGGL((prefill_kernel<T, true, true>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
+    else if (full_k)
+        hipLaunchKernelGGL((prefill_kernel<T, true, false>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, false>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
+        hipLaunchKernelGGL((prefill_kernel<T, false, false>), dim3(blocks), dim3(T::THREADS), 0, stream, b);
     return hipGetLastError();
 }
 
@@ -66,11 +68,12 @@ hipError_t launch_wonly_prefill(const WgProblem *q, int count, hipStream_t strea
     return launch_tiles<TileWSmall>(ex, n, stream);
 }
 
-hipError_t launch_forward_prefill(const bl_forward_ex_problem *q, int count, hipStream_t stream)
+hipError_t launch_forward_prefill(const bl_forward_ex_problem *q, int count, hipStream_t stream,
+                                  bool quad)
 {
     if (prefill_big_tiles(q, count))
-        return launch_tiles<TileBig>(q, count, stream);
-    return launch_tiles<TileSmall>(q, count, stream);
+        return quad ? launch_tiles<TileBig, true>(q, count, stream) : launch_tiles<TileBig>(q, count, stream);
+    return quad ? launch_tiles<TileSmall, true>(q, count, stream) : launch_tiles<TileSmall>(q, count, stream);
 }
 
 }  // namespace bl

@@ -112,8 +112,10 @@ __device__ __forceinline__ void static_for(F &&f)
 // The prefill kernel.  Per stage, activations (BM rows x KS bytes, swizzled) and packed
 // weights (BN rows x KS/4 bytes) travel global -> LDS by direct buffer loads; NST - 1 stages
 // are in flight while one is computed, and one barrier per stage orders reuse of the buffers.
-// FULL_K: every problem has K % KS == 0 (no stage runs past a row).
-template <class T, bool FULL_K>
+// FULL_K: every problem has K % KS == 0 (no stage runs past a row).  QR: the packed weights
+// are in the quad-row layout (quad_row_word), so each 1 KB weight load reads eight whole
+// 128-byte lines (four rows' 32-byte stage pieces each) instead of 32 rows x 32 bytes.
+template <class T, bool FULL_K, bool QR = false>
 __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
 {
     constexpr int BM = T::BM, BN = T::BN, KS = T::KS, NST = T::NST, WAVES = T::WAVES;
@@ -191,10 +193,19 @@ __device__ __forceinline__ void prefill_block(const PreBatch &b, int bid)
         for (int i = 0; i < T::WINST; ++i) {
             const int row0 = wave * (BN / WAVES) + i * WR;
             const int row = row0 + wrow_l;
-            const int kb = t * WROW + 16 * (wcol ^ wswz<WCH>(row));   // byte offset in the row
-            uint32_t off = ((uint32_t)row * row_bytes + (uint32_t)kb) | dead;
-            if (!FULL_K)
-                off = kb < row_bytes ? off : kOOB;
+            uint32_t off;
+            if constexpr (QR) {
+                // Row `row`'s piece of stage t in the line of rows 4 (row / 4) .. + 3 (K % 128
+                // == 0 on this path: no stage runs past a row).
+                static_assert(WROW == 32, "quad-row lines hold four 32-byte stage pieces");
+                off = ((uint32_t)((row >> 2) * stages + t) * 128u +
+                       (uint32_t)(32 * (row & 3) + 16 * (wcol ^ wswz<WCH>(row)))) | dead;
+            } else {
+                const int kb = t * WROW + 16 * (wcol ^ wswz<WCH>(row));   // byte offset in the row
+                off = ((uint32_t)row * row_bytes + (uint32_t)kb) | dead;
+                if (!FULL_K)
+                    off = kb < row_bytes ? off : kOOB;
+            }
             dma16(wres, lds_addr(st + T::XBYTES + row0 * WROW), off);
         }
     };

@@ -43,6 +43,7 @@ struct WeightDev {
     int parts;          // partial sums (blocks of gamma_partial_kernel) for this tensor
     int part_begin;     // first block of this tensor in gamma_partial_kernel's grid
     int pack_begin;     // first block of this tensor in quant_pack_kernel's grid
+    uint32_t quad_wpr;  // 0: rows [N][K/16]; else K/16, and the words go to the quad-row layout
 };
 
 struct WeightBatch {
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
         bits |= code_field(fabsf(vw) > tau, vw < 0.0f) << (24 + sh);
         bits = quad_or(bits);
         if (j < p.chunks && (j & 3) == 0)
-            p.packed[j >> 2] = bits;
+            p.packed[p.quad_wpr ? quad_row_word((uint32_t)(j >> 2), p.quad_wpr) : j >> 2] = bits;
     }
 }
 
@@ -246,7 +247,7 @@ static int64_t group_bytes()
 // Tensors i0 .. (returned end) - 1 of one launch pair: the γ-pass blocks (parts) and the pack
 // pass blocks (blocks).
 static int build_weight_batch(const bl_weight_problem *q, int i0, int count, void *workspace,
-                              WeightBatch &b, int &parts, int &blocks)
+                              WeightBatch &b, int &parts, int &blocks, bool quad)
 {
     parts = 0;
     blocks = 0;
@@ -263,6 +264,7 @@ static int build_weight_batch(const bl_weight_problem *q, int i0, int count, voi
         d.gamma = q[i].gamma;
         d.partials = static_cast<double *>(workspace) + (size_t)i * kGammaParts;
         d.chunks = q[i].N * q[i].K / 4;
+        d.quad_wpr = quad ? (uint32_t)(q[i].K / 16) : 0u;
         d.parts = gamma_parts(d.chunks);
         d.part_begin = parts;
         parts += d.parts;
@@ -277,13 +279,13 @@ static int build_weight_batch(const bl_weight_problem *q, int i0, int count, voi
 }
 
 hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
-                                   hipStream_t stream)
+                                   hipStream_t stream, bool quad)
 {
     int i0 = 0;
     while (i0 < count) {
         WeightBatch b{};
         int parts, blocks;
-        i0 = build_weight_batch(q, i0, count, workspace, b, parts, blocks);
+        i0 = build_weight_batch(q, i0, count, workspace, b, parts, blocks, quad);
         hipLaunchKernelGGL(gamma_partial_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -324,6 +326,37 @@ hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t
     const int64_t blocks = (words + 255) / 256;
     hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const uint4 *>(codes), W_packed, words);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- quad rows
+
+// Two-bit rows [N][K/16] -> the quad-row layout (a permutation of the same words; see
+// quad_row_word): one thread per four words, which stay consecutive in both layouts.
+__global__ __launch_bounds__(256) void pack_quad_rows_kernel(const uint4 *__restrict__ P,
+                                                              uint4 *__restrict__ out,
+                                                              uint32_t wpr, uint32_t quads)
+{
+    const uint32_t c = blockIdx.x * 256u + threadIdx.x;      // 16-byte chunk of the output
+    if (c >= quads)
+        return;
+    // Output words 4c .. 4c + 3: line L = 4c / 32 (rows 4q .. 4q + 3 of stage t), row
+    // 4q + i, words 8t + j .. 8t + j + 3 with i = (4c % 32) / 8, j = 4c % 8.
+    const uint32_t o = 4u * c, S = wpr / 8u;
+    const uint32_t L = o / 32u, i = (o % 32u) / 8u, j = o % 8u;
+    const uint32_t q = L / S, t = L % S;
+    out[c] = P[((4u * q + i) * wpr + 8u * t + j) / 4u];
+}
+
+hipError_t launch_pack_quad_rows(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
+                                 hipStream_t stream)
+{
+    const int64_t quads = N * K / 64;                        // 16-byte chunks
+    if (quads == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pack_quad_rows_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       stream, reinterpret_cast<const uint4 *>(P), reinterpret_cast<uint4 *>(out),
+                       (uint32_t)(K / 16), (uint32_t)quads);
     return hipGetLastError();
 }
 
@@ -753,7 +786,7 @@ static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
 // activation problem fits the wave kernel (K <= 4096, no FFN activation) with one dtype and
 // the weights form one launch pair; otherwise the two calls' own launches.
 hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
-                                const bl_act_ex_problem *aq, int na, hipStream_t stream)
+                                const bl_act_ex_problem *aq, int na, hipStream_t stream, bool quad)
 {
     int order[BL_MAX_GROUP];
     int n = 0, bf = -1;
@@ -769,9 +802,9 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
     }
     WeightBatch wb{};
     int parts = 0, blocks = 0;
-    ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks) == nw;
+    ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks, quad) == nw;
     if (!ok) {
-        const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream);
+        const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream, quad);
         return e == hipSuccess ? launch_quantize_acts(aq, na, stream) : e;
     }
     // Longest rows first, as in the activation launch (the row-to-block map changes nothing

@@ -595,6 +595,45 @@ bl_status bitlinear_pack_tiles(const uint32_t *W_packed, int64_t N, int64_t K, u
 bl_status bitlinear_linear_tiles_grouped(const bl_linear_problem *problems, int count, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Quad rows: the same two-bit words arranged for the prefill product's weight loads.
+ *
+ * bitone README, "Features": the fused BitLinear GEMM (Y = X @ W_q^T x gamma).  The prefill
+ * product stages 128 weights of K at a time, i.e. 32 bytes of each of its weight rows, and
+ * from [N][K/16] rows every 128-byte line it touches serves one row's stage piece (a quarter
+ * of the line per request; measured: the 8192-token product of the Qwen3-4B set 5 % faster
+ * with whole-line requests).  The quad-row layout (this library's own, not the pages')
+ * needs N % 4 == 0 and K % 128 == 0 and permutes the words of every four rows: for rows
+ * 4 q .. 4 q + 3 and stage t (words 8 t .. 8 t + 7 of each row), one 128-byte line holds the
+ * four rows' 32-byte pieces in row order.  Word w of row n sits at word
+ * ((n / 4) * (K / 128) + w / 8) * 32 + 8 * (n % 4) + w % 8; same size as the rows (N * K / 4
+ * bytes), no padding.
+ * ------------------------------------------------------------------------------------- */
+
+/* Two-bit rows W_packed [N][K/16] -> W_quad (N * K / 4 bytes, not overlapping W_packed).
+ * N == 0 is a no-op.  Errors: BL_ERR_NULL, BL_ERR_SHAPE (N % 4 != 0, K % 128 != 0, the
+ * limits of bitlinear_pack_codes, or N * K / 16 >= 2^32), BL_ERR_ALIGN (both 16-byte
+ * aligned). */
+bl_status bitlinear_pack_quad_rows(const uint32_t *W_packed, int64_t N, int64_t K, uint32_t *W_quad,
+                                   void *stream);
+
+/* bitlinear_quantize_step with every weight problem's W_packed receiving the quad-row layout
+ * (the same words as bitlinear_quantize_step writes, permuted; gamma and the activation
+ * results unchanged).  Every weight problem needs N % 4 == 0, K % 128 == 0 and
+ * N * K / 16 < 2^32 (BL_ERR_SHAPE); other errors as for bitlinear_quantize_step. */
+bl_status bitlinear_quantize_step_quad_rows(const bl_weight_problem *weights, int nw,
+                                            void *workspace, size_t workspace_bytes,
+                                            const bl_act_problem *acts, int na, void *stream);
+
+/* bitlinear_forward_grouped on weights in the quad-row layout: one prefill launch, results
+ * (Y and the optional int32 acc) bit-identical to bitlinear_forward_grouped on the same codes
+ * in rows.  Every problem with M > 0 and N > 0 needs M > 16 (the prefill product; decode-sized
+ * products read rows), N % 4 == 0, K % 128 == 0 and N * K / 16 < 2^32, BL_ERR_SHAPE
+ * otherwise; empty problems are skipped.  Other errors as for bitlinear_forward_grouped;
+ * nothing is launched on an error. */
+bl_status bitlinear_forward_quad_rows_grouped(const bl_forward_problem *problems, int count,
+                                              void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * Measurement helpers (not part of the method): what this GPU attains, so that a kernel's
  * roofline can be quoted against a measured peak beside the published one.
  * ------------------------------------------------------------------------------------- */

@@ -64,7 +64,7 @@ def test_status_strings(L):
               BL_ERR_HIP, BL_ERR_COUNT):
         assert L.bitlinear_status_string(s)
     assert L.bitlinear_status_string(12345) == b"unknown status"
-    assert L.bitlinear_abi_version() == 102
+    assert L.bitlinear_abi_version() == 103
 
 
 def test_quantize_weights_noalloc_validation(L, bl):
@@ -431,6 +431,57 @@ def test_tiles_entry_points_validation(L, bl):
     assert call(x_dtype=2) == BL_ERR_DTYPE
     assert call(W_packed=B + 4) == BL_ERR_ALIGN
     assert call(M=0) == BL_OK
+
+
+def test_quad_rows_entry_points_validation(L, bl):
+    """The quad-row calls reject what the layout cannot hold (N % 4, K % 128), decode-sized
+    products and the usual NULL / alignment cases on the host; nothing is launched."""
+    pk = L.bitlinear_pack_quad_rows
+    assert pk(None, 4, 128, B, None) == BL_ERR_NULL
+    assert pk(A, 4, 128, None, None) == BL_ERR_NULL
+    assert pk(A, 6, 128, B, None) == BL_ERR_SHAPE      # N % 4 != 0
+    assert pk(A, 4, 192, B, None) == BL_ERR_SHAPE      # K % 128 != 0
+    assert pk(A, 4, 40, B, None) == BL_ERR_SHAPE
+    assert pk(A, -4, 128, B, None) == BL_ERR_SHAPE
+    assert pk(A + 4, 4, 128, B, None) == BL_ERR_ALIGN
+    assert pk(A, 4, 128, B + 8, None) == BL_ERR_ALIGN
+    assert pk(None, 0, 128, None, None) == BL_OK
+    f = L.bitlinear_forward_quad_rows_grouped
+    fa = (bl._ForwardProblem * 2)()
+    fa[0] = bl._ForwardProblem(A, B, C, D, E, None, 300, 64, 256)
+    addr = ctypes.addressof(fa)
+    assert f(None, 1, None) == BL_ERR_NULL
+    assert f(addr, 0, None) == BL_ERR_COUNT and f(addr, 17, None) == BL_ERR_COUNT
+    fa[0].M = 16
+    assert f(addr, 1, None) == BL_ERR_SHAPE             # decode-sized products read rows
+    fa[0].M = 300
+    fa[0].N = 66
+    assert f(addr, 1, None) == BL_ERR_SHAPE
+    fa[0].N = 64
+    fa[0].K = 320
+    assert f(addr, 1, None) == BL_ERR_SHAPE
+    fa[0].K = 256
+    fa[0].W_packed = C + 4
+    assert f(addr, 1, None) == BL_ERR_ALIGN
+    fa[0].W_packed = C
+    fa[1] = bl._ForwardProblem(None, None, None, D, None, None, 300, 64, 256)
+    assert f(addr, 2, None) == BL_ERR_NULL              # the second problem's operands
+    fa[1].M = 0
+    fa[0].M = 0
+    assert f(addr, 2, None) == BL_OK                    # all empty: nothing launched
+    q = L.bitlinear_quantize_step_quad_rows
+    w = (bl._WeightProblem * 1)()
+    w[0] = bl._WeightProblem(A, B, C, 6, 128)
+    a = (bl._ActProblem * 1)()
+    a[0] = bl._ActProblem(A, None, B, C, 2, 128, 0, 1e-6)
+    ws = L.bitlinear_quantize_weights_grouped_workspace(1)
+    wa, aa = ctypes.addressof(w), ctypes.addressof(a)
+    assert q(wa, 1, D, ws, aa, 1, None) == BL_ERR_SHAPE     # N % 4 != 0
+    w[0].N, w[0].K = 4, 192
+    assert q(wa, 1, D, ws, aa, 1, None) == BL_ERR_SHAPE     # K % 128 != 0
+    w[0].K = 128
+    assert q(wa, 1, D, ws - 1, aa, 1, None) == BL_ERR_WORKSPACE
+    assert q(wa, 0, D, ws, aa, 0, None) == BL_ERR_COUNT
 
 
 def test_b3_entry_points_validation(L, bl):
