@@ -132,9 +132,10 @@ def test_forward_quad_rows_grouped_mixed_shapes(torch, bl):
         assert torch.equal(a["acc"], b["acc"]) and torch.equal(a["Y"], b["Y"])
 
 
-def test_forward_quad_rows_layer_set(torch, bl):
+def test_forward_quad_rows_layer_set(torch, bl, orc):
     """The Qwen3-4B layer set at 8192 tokens (the 128 x 256 tiles, as the benchmark step runs
-    it): every accumulator and output equals the rows call's."""
+    it): every accumulator and output equals the rows call's, and 1024 sampled entries of each
+    projection (the corners among them) equal the oracle's, computed one by one."""
     mats = workloads.WORKLOADS["c5_qwen3_4b_layer"].matrices
     M = 8192
     ps = []
@@ -149,3 +150,13 @@ def test_forward_quad_rows_layer_set(torch, bl):
     for a, b, m in zip(rows, quad, mats):
         assert torch.equal(a["acc"], b["acc"]), (m.N, m.K)
         assert torch.equal(a["Y"], b["Y"]), (m.N, m.K)
+    rng = np.random.default_rng(527)
+    for p, b, m in zip(ps, quad, mats):
+        mi = np.concatenate([[0, M - 1, 0, M - 1], rng.integers(0, M, 1020)])
+        ni = np.concatenate([[0, 0, m.N - 1, m.N - 1], rng.integers(0, m.N, 1020)])
+        acc_ref, y_ref = orc.forward_entries(host(p["Xq"]), host(p["sx"]), host(p["P"]).view(np.uint32),
+                                             0.021, mi, ni)
+        assert np.array_equal(host(b["acc"])[mi, ni], acc_ref), (m.N, m.K)
+        y = host(b["Y"])[mi, ni]
+        assert np.array_equal(y == 0, y_ref == 0)
+        assert rel_err(y[y_ref != 0], y_ref[y_ref != 0]) <= REL, (m.N, m.K)

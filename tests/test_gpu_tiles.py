@@ -173,15 +173,16 @@ def test_linear_tiles_extremes(torch, bl, orc, kind, N, K):
     assert rel_err(Y[nz], Y_ref[nz]) <= REL, (kind, N, K)
 
 
-def test_linear_tiles_layer_set(torch, bl):
+def test_linear_tiles_layer_set(torch, bl, orc):
     """The Qwen3-4B decode layer set (one token) in one call, twice in a row: every output
-    equals the two-bit call's."""
+    equals the two-bit call's, and the oracle's (codes exact, Y within 1e-6)."""
     mats = workloads.WORKLOADS["c5_qwen3_4b_layer"].matrices
-    ts, twos = [], []
+    ts, twos, refs = [], [], []
     for i, m in enumerate(mats):
-        t, two, _ = make(torch, bl, m.N, m.K, "f32", i % 2 == 0, (1, i))
+        t, two, ref = make(torch, bl, m.N, m.K, "f32", i % 2 == 0, (1, i))
         ts.append(t)
         twos.append(two)
+        refs.append(ref)
     bl.linear_grouped(twos)
     for _ in range(2):
         for t in ts:
@@ -190,6 +191,13 @@ def test_linear_tiles_layer_set(torch, bl):
         torch.cuda.synchronize()
         for a, b in zip(ts, twos):
             assert torch.equal(a["Y"], b["Y"])
+    for t, ref, m in zip(ts, refs, mats):
+        q_ref, s_ref = orc.quantize_acts(ref["x"], ref["g"], 1e-6)
+        assert np.array_equal(host(t["X_q"]), q_ref), (m.N, m.K)
+        Y_ref = orc.epilogue(orc.matmul(q_ref, ref["C"]), s_ref, GAMMA)
+        Y = host(t["Y"])
+        assert np.array_equal(Y == 0, Y_ref == 0)
+        assert rel_err(Y[Y_ref != 0], Y_ref[Y_ref != 0]) <= REL, (m.N, m.K)
 
 
 def test_linear_tiles_rejects_more_tokens(torch, bl):
