@@ -61,9 +61,11 @@ def test_pack_quad_rows(torch, bl, orc, N, K):
 
 
 @pytest.mark.parametrize("shapes", [[(4, 128)], [(300, 512), (64, 2560), (8, 1024)],
-                                    [(2560, 4096), (1024, 2560)]])
+                                    [(2560, 4096), (1024, 2560)], [(2560, 9728), (4096, 2560)]])
 def test_quantize_step_quad_rows(torch, bl, shapes):
-    """Same gamma, same activation results, and the rows call's words re-arranged."""
+    """Same gamma, same activation results, and the rows call's words re-arranged (rows of up
+    to 4096 values share the gamma pass's launch; 9728 takes the separate launches, as the
+    Qwen3-4B set's down projection does in the benchmark step)."""
     Ws = [dev(torch, workloads.gaussian(s, (521, i) + s, 0.02)) for i, s in enumerate(shapes)]
     Xs = [dev(torch, workloads.gaussian((33, s[1]), (522, i) + s, 1.0)) for i, s in enumerate(shapes)]
     w_rows, x_rows = bl.quantize_step(Ws, Xs)
