@@ -195,6 +195,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_quantize_step_quad_rows.restype = ctypes.c_int
     L.bitlinear_forward_quad_rows_grouped.argtypes = [P, ctypes.c_int, P]
     L.bitlinear_forward_quad_rows_grouped.restype = ctypes.c_int
+    L.bitlinear_forward_ex_quad_rows_grouped.argtypes = [P, ctypes.c_int, P]
+    L.bitlinear_forward_ex_quad_rows_grouped.restype = ctypes.c_int
     L.bitlinear_calib_stream.argtypes = [P, I64, P, P]
     L.bitlinear_calib_stream.restype = ctypes.c_int
     L.bitlinear_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
@@ -528,11 +530,12 @@ def forward_ex_table(problems: Sequence[dict]):
     return arr
 
 
-def forward_ex_grouped(problems: Sequence[dict], stream=None) -> None:
-    """Products with an optional residual added in the epilogue; outputs preallocated."""
+def forward_ex_grouped(problems: Sequence[dict], stream=None, quad_rows: bool = False) -> None:
+    """Products with an optional residual added in the epilogue; outputs preallocated.
+    quad_rows: W_packed in the quad-row layout (bitlinear_forward_ex_quad_rows_grouped)."""
     arr = forward_ex_table(problems)
-    _check("bitlinear_forward_ex_grouped",
-           lib().bitlinear_forward_ex_grouped(ctypes.addressof(arr), len(problems), _stream(stream)))
+    fn = "bitlinear_forward_ex_quad_rows_grouped" if quad_rows else "bitlinear_forward_ex_grouped"
+    _check(fn, getattr(lib(), fn)(ctypes.addressof(arr), len(problems), _stream(stream)))
 
 
 def forward_mixed(prefill: Sequence[dict], decode: Sequence[dict], stream=None) -> None:

@@ -590,6 +590,32 @@ bl_status bitlinear_pack_quad_rows(const uint32_t *W_packed, int64_t N, int64_t 
     return from_hip(bl::launch_pack_quad_rows(W_packed, N, K, W_quad, static_cast<hipStream_t>(stream)));
 }
 
+// The prefill products of a set on quad rows: every non-empty problem needs M > 16, N % 4 == 0
+// and K % 128 == 0; problems are validated before anything is launched.
+static bl_status forward_quad(const bl_forward_ex_problem *q, int count, void *stream)
+{
+    bl_forward_ex_problem ex[BL_MAX_GROUP];
+    int n = 0;
+    int64_t blocks = 0;
+    for (int i = 0; i < count; ++i) {
+        const bl_forward_ex_problem &p = q[i];
+        if (p.M == 0 || p.N == 0)
+            continue;
+        if (p.M <= bl::kDecodeMaxM)
+            return BL_ERR_SHAPE;         // the quad-row layout feeds the prefill product only
+        const bl_status s = check_quad(p.N, p.K);
+        if (s != BL_OK)
+            return s;
+        ex[n++] = p;
+        blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    }
+    if (blocks > INT_MAX)
+        return BL_ERR_SHAPE;
+    if (n == 0)
+        return BL_OK;
+    return from_hip(bl::launch_forward_prefill(ex, n, static_cast<hipStream_t>(stream), true));
+}
+
 bl_status bitlinear_forward_quad_rows_grouped(const bl_forward_problem *problems, int count,
                                               void *stream)
 {
@@ -598,28 +624,28 @@ bl_status bitlinear_forward_quad_rows_grouped(const bl_forward_problem *problems
     if (count <= 0 || count > BL_MAX_GROUP)
         return BL_ERR_COUNT;
     bl_forward_ex_problem ex[BL_MAX_GROUP];
-    int n = 0;
-    int64_t blocks = 0;
     for (int i = 0; i < count; ++i) {
-        const bl_forward_problem &p = problems[i];
-        bl_status s = check_forward(p);
+        const bl_status s = check_forward(problems[i]);
         if (s != BL_OK)
             return s;
-        if (p.M == 0 || p.N == 0)
-            continue;
-        if (p.M <= bl::kDecodeMaxM)
-            return BL_ERR_SHAPE;         // the quad-row layout feeds the prefill product only
-        s = check_quad(p.N, p.K);
-        if (s != BL_OK)
-            return s;
-        ex[n++] = to_ex(p);
-        blocks += ((p.M + 127) / 128) * ((p.N + 127) / 128);
+        ex[i] = to_ex(problems[i]);
     }
-    if (blocks > INT_MAX)
-        return BL_ERR_SHAPE;
-    if (n == 0)
-        return BL_OK;
-    return from_hip(bl::launch_forward_prefill(ex, n, static_cast<hipStream_t>(stream), true));
+    return forward_quad(ex, count, stream);
+}
+
+bl_status bitlinear_forward_ex_quad_rows_grouped(const bl_forward_ex_problem *problems, int count,
+                                                 void *stream)
+{
+    if (!problems)
+        return BL_ERR_NULL;
+    if (count <= 0 || count > BL_MAX_GROUP)
+        return BL_ERR_COUNT;
+    for (int i = 0; i < count; ++i) {
+        const bl_status s = check_forward_ex(problems[i]);
+        if (s != BL_OK)
+            return s;
+    }
+    return forward_quad(problems, count, stream);
 }
 
 bl_status bitlinear_linear_grouped(const bl_linear_problem *problems, int count, void *stream)

@@ -43,8 +43,8 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import (ACT_NONE, ACT_RELU2, ACT_RELU2_GLU, ACT_SWIGLU, _check, _stream, act_ex_table,
-               forward_ex_table, lib, linear_ex_table, linear_fused)
+from . import (ACT_NONE, ACT_RELU2, ACT_RELU2_GLU, ACT_SWIGLU, DECODE_MAX_M, _check, _stream,
+               act_ex_table, forward_ex_table, lib, linear_ex_table, linear_fused, pack_quad_rows)
 
 ATTN_IN = ("q", "k", "v", "qkv")
 
@@ -57,6 +57,17 @@ class LayerWeights:
     gamma: Dict[str, torch.Tensor]
     norms: Dict[str, Optional[torch.Tensor]] = field(default_factory=dict)
     act: int = ACT_SWIGLU
+    _quad: Dict[str, torch.Tensor] = field(default_factory=dict, repr=False)
+
+    def quad_rows(self, name: str) -> torch.Tensor:
+        """The projection's words in the quad-row layout (packed once, on first use)."""
+        if name not in self._quad:
+            self._quad[name] = pack_quad_rows(self.packed[name])
+        return self._quad[name]
+
+    def fits_quad_rows(self) -> bool:
+        """Whether every projection fits the quad-row layout (N % 4 == 0, K % 128 == 0)."""
+        return all(self.N(n) % 4 == 0 and self.K(n) % 128 == 0 for n in self.packed)
 
     def K(self, name: str) -> int:
         return self.packed[name].shape[1] * 16
@@ -127,6 +138,7 @@ class LayerChain:
         self.out = t(M, d)
         nrm = w.norms.get
         L = lib()
+        self.quad = False
         if self.fused:
             self._build_fused(nrm, glu, keep_codes, L)
             return
@@ -134,26 +146,31 @@ class LayerChain:
                     dict(X=self.attn, X_q=self.aq, x_scale=self.as_, norm_weight=nrm("o"), eps=eps)]
         if not w.attn_in:
             self._a1 = self._a1[1:]
-        p1 = [dict(X_q=self.xq, x_scale=self.xs, W_packed=w.packed[n], gamma=w.gamma[n], Y=self.y[n])
+        # Prefill-sized products read the quad-row layout where every projection fits it (whole
+        # 128-byte lines per weight load; the same results as on rows).
+        self.quad = M > DECODE_MAX_M and w.fits_quad_rows()
+        W = w.quad_rows if self.quad else w.packed.__getitem__
+        fwd = L.bitlinear_forward_ex_quad_rows_grouped if self.quad else L.bitlinear_forward_ex_grouped
+        p1 = [dict(X_q=self.xq, x_scale=self.xs, W_packed=W(n), gamma=w.gamma[n], Y=self.y[n])
               for n in w.attn_in]
-        p1.append(dict(X_q=self.aq, x_scale=self.as_, W_packed=w.packed["o"], gamma=w.gamma["o"],
+        p1.append(dict(X_q=self.aq, x_scale=self.as_, W_packed=W("o"), gamma=w.gamma["o"],
                        Y=self.x1, residual=self.x))
         a2 = [dict(X=self.x1, X_q=self.fq, x_scale=self.fs, norm_weight=nrm("ffn"), eps=eps)]
-        p2 = [dict(X_q=self.fq, x_scale=self.fs, W_packed=w.packed["up"], gamma=w.gamma["up"], Y=self.up)]
+        p2 = [dict(X_q=self.fq, x_scale=self.fs, W_packed=W("up"), gamma=w.gamma["up"], Y=self.up)]
         if glu:
-            p2.insert(0, dict(X_q=self.fq, x_scale=self.fs, W_packed=w.packed["gate"],
+            p2.insert(0, dict(X_q=self.fq, x_scale=self.fs, W_packed=W("gate"),
                               gamma=w.gamma["gate"], Y=self.gate))
         a3 = [dict(X=self.gate if glu else self.up, X2=self.up if glu else None, act=w.act,
                    X_q=self.hq, x_scale=self.hs, norm_weight=nrm("down"), eps=eps)]
-        p3 = [dict(X_q=self.hq, x_scale=self.hs, W_packed=w.packed["down"], gamma=w.gamma["down"],
+        p3 = [dict(X_q=self.hq, x_scale=self.hs, W_packed=W("down"), gamma=w.gamma["down"],
                    Y=self.out, residual=self.x1)]
         self._calls = [
             (L.bitlinear_quantize_acts_ex_grouped, act_ex_table(self._a1), len(self._a1)),
-            (L.bitlinear_forward_ex_grouped, forward_ex_table(p1), len(p1)),
+            (fwd, forward_ex_table(p1), len(p1)),
             (L.bitlinear_quantize_acts_ex_grouped, act_ex_table(a2), 1),
-            (L.bitlinear_forward_ex_grouped, forward_ex_table(p2), len(p2)),
+            (fwd, forward_ex_table(p2), len(p2)),
             (L.bitlinear_quantize_acts_ex_grouped, act_ex_table(a3), 1),
-            (L.bitlinear_forward_ex_grouped, forward_ex_table(p3), 1),
+            (fwd, forward_ex_table(p3), 1),
         ]
         self._addr = [ctypes.addressof(arr) for _, arr, _ in self._calls]
 

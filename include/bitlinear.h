@@ -633,6 +633,13 @@ bl_status bitlinear_quantize_step_quad_rows(const bl_weight_problem *weights, in
 bl_status bitlinear_forward_quad_rows_grouped(const bl_forward_problem *problems, int count,
                                               void *stream);
 
+/* bitlinear_forward_ex_grouped (the layer chain's products, with the optional residual added
+ * in the epilogue) on weights in the quad-row layout: the same limits and errors as
+ * bitlinear_forward_quad_rows_grouped, otherwise as bitlinear_forward_ex_grouped; results
+ * bit-identical to bitlinear_forward_ex_grouped on the same codes in rows. */
+bl_status bitlinear_forward_ex_quad_rows_grouped(const bl_forward_ex_problem *problems, int count,
+                                                 void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * Measurement helpers (not part of the method): what this GPU attains, so that a kernel's
  * roofline can be quoted against a measured peak beside the published one.

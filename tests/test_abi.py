@@ -469,6 +469,22 @@ def test_quad_rows_entry_points_validation(L, bl):
     fa[1].M = 0
     fa[0].M = 0
     assert f(addr, 2, None) == BL_OK                    # all empty: nothing launched
+    fx = L.bitlinear_forward_ex_quad_rows_grouped
+    xa = (bl._ForwardExProblem * 1)()
+    xa[0] = bl._ForwardExProblem(A, B, C, D, E, None, None, 300, 64, 256)
+    xaddr = ctypes.addressof(xa)
+    assert fx(None, 1, None) == BL_ERR_NULL and fx(xaddr, 0, None) == BL_ERR_COUNT
+    xa[0].M = 8
+    assert fx(xaddr, 1, None) == BL_ERR_SHAPE
+    xa[0].M = 300
+    xa[0].K = 320
+    assert fx(xaddr, 1, None) == BL_ERR_SHAPE
+    xa[0].K = 256
+    xa[0].residual = 0x60002
+    assert fx(xaddr, 1, None) == BL_ERR_ALIGN
+    xa[0].residual = None
+    xa[0].N = 0
+    assert fx(xaddr, 1, None) == BL_OK
     q = L.bitlinear_quantize_step_quad_rows
     w = (bl._WeightProblem * 1)()
     w[0] = bl._WeightProblem(A, B, C, 6, 128)

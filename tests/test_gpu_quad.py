@@ -134,6 +134,23 @@ def test_forward_quad_rows_grouped_mixed_shapes(torch, bl):
         assert torch.equal(a["acc"], b["acc"]) and torch.equal(a["Y"], b["Y"])
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 132, 384), (2048, 4096, 1024)])
+def test_forward_ex_quad_rows_residual(torch, bl, M, N, K):
+    """The layer chain's product form (residual added in the epilogue, here also in place) on
+    quad rows: bit for bit the rows call's."""
+    p = make_problem(torch, bl, M, N, K, (2,))
+    R = dev(torch, workloads.gaussian((M, N), (528, M, N, K), 1.0))
+    outs = []
+    for quad in (False, True):
+        Y = R.clone()
+        bl.forward_ex_grouped([dict(X_q=p["Xq"], x_scale=p["sx"], gamma=p["g"], Y=Y, residual=Y,
+                                    W_packed=bl.pack_quad_rows(p["P"]) if quad else p["P"])],
+                              quad_rows=quad)
+        outs.append(Y)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]), (M, N, K)
+
+
 def test_forward_quad_rows_layer_set(torch, bl, orc):
     """The Qwen3-4B layer set at 8192 tokens (the 128 x 256 tiles, as the benchmark step runs
     it): every accumulator and output equals the rows call's, and 1024 sampled entries of each
