@@ -224,7 +224,16 @@ class Setup:
                          t.empty(1, dtype=t.float32, device=dev)) for m in mats]
         self.Y_pre = [t.empty((M_pre, m.N), dtype=t.float32, device=dev) for m in mats]
         self.Y_dec = [t.empty((1, m.N), dtype=t.float32, device=dev) for m in mats]
-        self.ws = t.empty(max(16, bl.quantize_weights_workspace_bytes(self.count)),
+        # Weight-quantization workspace: large enough for the one-read form (each fp32 master
+        # read once; the library takes it for sets of 64 MB and more).
+        shapes = (bl._WeightProblem * self.count)()
+        for i, m in enumerate(mats):
+            shapes[i] = bl._WeightProblem(None, None, None, m.N, m.K)
+        self.one_read_bytes = bl.quantize_weights_one_read_workspace_bytes(shapes, self.count)
+        self.one_read = (W_host is not None and
+                         sum(4 * m.N * m.K for m in mats) >= 64 << 20)
+        self.ws = t.empty(max(16, bl.quantize_weights_workspace_bytes(self.count),
+                              self.one_read_bytes if self.one_read else 0),
                           dtype=t.uint8, device=dev)
         self._build_tables()
 
@@ -1140,6 +1149,9 @@ def main():
                     "frac_attainable": round(gemm_tops / attainable, 4),
                     "ops": ops, "us_gemm": round(ms["prefill_gemm"] * 1e3, 3),
                     "us_weight_quant": round(ms["weight_quant"] * 1e3, 3) if "weight_quant" in ms else None,
+                    "weight_quant_form": (("one read (sample, pass with listed band, fix-up)"
+                                           if setup.one_read else "two reads (gamma pass, pack pass)")
+                                          if setup.W_pre is not None else None),
                     "us_act_quant": round(ms["act_quant_prefill"] * 1e3, 3),
                     "us_prefill_and_decode": round(ms["prefill_and_decode"] * 1e3, 3),
                     "us_weight_and_act_quant": round(ms["weight_and_act_quant"] * 1e3, 3) if "weight_and_act_quant" in ms else None,
@@ -1153,9 +1165,12 @@ def main():
                    "ms_per_step_with_launch_events": round(ms_with_events, 4),
                    "schedule": "one stream, launches in step order: weight quantization, "
                                "activation quantization, then the prefill products and the decode "
-                               "leg as one mixed launch (three streams, weight quant beside act "
-                               "quant and decode beside prefill, and the decode leg alone on a "
-                               "second stream, measured slower than one stream)"},
+                               "leg (one mixed launch where the products take 128 x 128 tiles). "
+                               "Measured slower than one stream: three streams (weight quant "
+                               "beside act quant, decode beside prefill), the decode leg alone on "
+                               "a second stream, and on the Qwen3-4B set the quantization of later "
+                               "projections on a second stream beside the products of earlier "
+                               "ones (the product's 128 x 256 tile fills every register file)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)

@@ -145,6 +145,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_quantize_weights.restype = ctypes.c_int
     L.bitlinear_quantize_weights_grouped_workspace.argtypes = [ctypes.c_int]
     L.bitlinear_quantize_weights_grouped_workspace.restype = SZ
+    L.bitlinear_quantize_weights_one_read_workspace.argtypes = [P, ctypes.c_int]
+    L.bitlinear_quantize_weights_one_read_workspace.restype = SZ
     L.bitlinear_quantize_weights_grouped.argtypes = [P, ctypes.c_int, P, SZ, P]
     L.bitlinear_quantize_weights_grouped.restype = ctypes.c_int
     L.bitlinear_quantize_weights_grouped_noalloc.argtypes = [P, ctypes.c_int, P]
@@ -238,6 +240,19 @@ def quantize_weights_workspace_bytes(count: int = 1) -> int:
     return int(lib().bitlinear_quantize_weights_grouped_workspace(count))
 
 
+def quantize_weights_one_read_workspace_bytes(problems, count: int) -> int:
+    """Workspace bytes with which the grouped and step calls read each fp32 master once
+    (problems: a ctypes array of _WeightProblem)."""
+    return int(lib().bitlinear_quantize_weights_one_read_workspace(ctypes.addressof(problems), count))
+
+
+def _weight_workspace(arr, count: int, one_read: bool, device) -> torch.Tensor:
+    nbytes = quantize_weights_workspace_bytes(max(count, 1))
+    if one_read and count:
+        nbytes = max(nbytes, quantize_weights_one_read_workspace_bytes(arr, count))
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def quantize_weights(W: torch.Tensor, W_packed: Optional[torch.Tensor] = None,
                      gamma: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
@@ -262,8 +277,9 @@ def quantize_weights(W: torch.Tensor, W_packed: Optional[torch.Tensor] = None,
 def quantize_weights_grouped(Ws: Sequence[torch.Tensor],
                              outputs: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor]]] = None,
                              workspace: Optional[torch.Tensor] = None,
-                             stream=None) -> List[Tuple[torch.Tensor, torch.Tensor]]:
-    """Several independent weight tensors in one grouped call (two kernel launches)."""
+                             stream=None, one_read: bool = True) -> List[Tuple[torch.Tensor, torch.Tensor]]:
+    """Several independent weight tensors in one grouped call (two kernel launches; three that
+    read W once for large sets when the workspace allows: one_read, the default, allocates it)."""
     count = len(Ws)
     arr = (_WeightProblem * max(count, 1))()
     outs = []
@@ -277,9 +293,8 @@ def quantize_weights_grouped(Ws: Sequence[torch.Tensor],
             g = torch.empty(1, dtype=torch.float32, device=W.device)
         outs.append((P, g))
         arr[i] = _WeightProblem(_ptr(W), _ptr(P), _ptr(g), N, K)
-    ws_bytes = quantize_weights_workspace_bytes(max(count, 1))
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
+        workspace = _weight_workspace(arr, count, one_read, Ws[0].device)
     _check("bitlinear_quantize_weights_grouped",
            lib().bitlinear_quantize_weights_grouped(ctypes.addressof(arr), count, _ptr(workspace),
                                                     workspace.numel() * workspace.element_size(),
@@ -369,11 +384,12 @@ def quantize_acts_grouped(Xs: Sequence[torch.Tensor],
 def quantize_step(Ws: Sequence[torch.Tensor], Xs: Sequence[torch.Tensor],
                   norm_weights: Optional[Sequence[Optional[torch.Tensor]]] = None,
                   eps: float = 1e-6, w_outputs=None, x_outputs=None, workspace=None, stream=None,
-                  quad_rows: bool = False):
+                  quad_rows: bool = False, one_read: bool = True):
     """Weight quantization of Ws and activation quantization of Xs in one call (the gamma pass
     and the activation codes share a launch when they can); returns ([(W_packed, gamma)],
     [(X_q, x_scale)]), bit for bit those of the two grouped calls.  quad_rows: the packed
-    words in the quad-row layout (bitlinear_quantize_step_quad_rows)."""
+    words in the quad-row layout (bitlinear_quantize_step_quad_rows).  one_read: allocate the
+    workspace with which large sets read each master once (same results)."""
     nw, na = len(Ws), len(Xs)
     wa = (_WeightProblem * max(nw, 1))()
     wouts = []
@@ -400,9 +416,8 @@ def quantize_step(Ws: Sequence[torch.Tensor], Xs: Sequence[torch.Tensor],
             sx = torch.empty(M, dtype=torch.float32, device=X.device)
         xouts.append((Xq, sx))
         xa[i] = _ActProblem(_ptr(X), _ptr(g), _ptr(Xq), _ptr(sx), M, K, _x_dtype(X), float(eps))
-    ws_bytes = quantize_weights_workspace_bytes(max(nw, 1))
     if workspace is None and nw:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=Ws[0].device)
+        workspace = _weight_workspace(wa, nw, one_read, Ws[0].device)
     fn = "bitlinear_quantize_step_quad_rows" if quad_rows else "bitlinear_quantize_step"
     _check(fn, getattr(lib(), fn)(ctypes.addressof(wa), nw, _ptr(workspace),
                                   0 if workspace is None else workspace.numel() * workspace.element_size(),

@@ -348,7 +348,7 @@ const char *bitlinear_status_string(int status)
     }
 }
 
-int bitlinear_abi_version(void) { return 103; }
+int bitlinear_abi_version(void) { return 104; }
 
 size_t bitlinear_quantize_weights_workspace(int64_t N, int64_t K)
 {
@@ -367,6 +367,17 @@ size_t bitlinear_quantize_weights_grouped_workspace(int count)
     if (count <= 0 || count > BL_MAX_GROUP)
         return 0;
     return bl::quantize_weights_workspace(count);
+}
+
+size_t bitlinear_quantize_weights_one_read_workspace(const bl_weight_problem *problems, int count)
+{
+    if (!problems || count <= 0 || count > BL_MAX_GROUP)
+        return 0;
+    for (int i = 0; i < count; ++i)
+        if (check_rows(problems[i].N) != BL_OK || check_k(problems[i].K) != BL_OK ||
+            problems[i].N * problems[i].K / 4 > (int64_t)INT_MAX * 4096)
+            return 0;
+    return bl::quantize_weights_one_read_workspace(problems, count);
 }
 
 bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, int count,
@@ -389,7 +400,8 @@ bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, 
     if (workspace_bytes < bl::quantize_weights_workspace(count))
         return BL_ERR_WORKSPACE;
     return from_hip(bl::launch_quantize_weights(problems, count, workspace,
-                                                static_cast<hipStream_t>(stream)));
+                                                static_cast<hipStream_t>(stream), false,
+                                                workspace_bytes));
 }
 
 bl_status bitlinear_quantize_weights_grouped_noalloc(const bl_weight_problem *problems, int count,
@@ -493,7 +505,7 @@ static bl_status quantize_step(const bl_weight_problem *weights, int nw, void *w
         if (workspace_bytes < bl::quantize_weights_workspace(nw))
             return BL_ERR_WORKSPACE;
     }
-    return from_hip(bl::launch_quantize_step(weights, nw, workspace, ex, na,
+    return from_hip(bl::launch_quantize_step(weights, nw, workspace, workspace_bytes, ex, na,
                                              static_cast<hipStream_t>(stream), quad));
 }
 

@@ -426,9 +426,12 @@ __device__ __forceinline__ v4u ternary_bf16(uint32_t w, int j)
 // ----------------------------------------------------------------- launchers
 
 // quad: write the packed words in the quad-row layout (quad_row_word) instead of rows.
+// workspace_bytes: with at least quantize_weights_one_read_workspace(p, count) bytes, a large
+// enough set reads W once (the one-read form, same codes and gamma); else W is read twice.
 hipError_t launch_quantize_weights(const bl_weight_problem *p, int count, void *workspace,
-                                   hipStream_t stream, bool quad = false);
+                                   hipStream_t stream, bool quad = false, size_t workspace_bytes = 0);
 size_t quantize_weights_workspace(int count);
+size_t quantize_weights_one_read_workspace(const bl_weight_problem *p, int count);
 hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
                              hipStream_t stream);
 hipError_t launch_quantize_acts(const bl_act_ex_problem *p, int count, hipStream_t stream);
@@ -458,8 +461,8 @@ hipError_t launch_pack_quad_rows(const uint32_t *P, int64_t N, int64_t K, uint32
 // Weight quantization + activation quantization of one step (γ pass and activation codes in
 // one launch when every activation problem takes the wave kernel with one dtype).
 hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
-                                const bl_act_ex_problem *aq, int na, hipStream_t stream,
-                                bool quad = false);
+                                size_t workspace_bytes, const bl_act_ex_problem *aq, int na,
+                                hipStream_t stream, bool quad = false);
 // Mixed batch (prefill products + fused decode calls) in one launch: eligible when every
 // prefill product has M > 16 and takes the 128 x 128 tile, and every decode call is a fused
 // single projection (no pair, activation or residual) with one activation dtype.

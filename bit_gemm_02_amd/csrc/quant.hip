@@ -44,6 +44,15 @@ struct WeightDev {
     int part_begin;     // first block of this tensor in gamma_partial_kernel's grid
     int pack_begin;     // first block of this tensor in quant_pack_kernel's grid
     uint32_t quad_wpr;  // 0: rows [N][K/16]; else K/16, and the words go to the quad-row layout
+    // One-read form only (the workspace regions of this tensor; see one_read_pass_kernel):
+    double *sample;     // [kSampleBlocks][2]: sum |w| and sum w^2 of the sampled pieces
+    float *band;        // [2]: the band (lo, hi) the pass used; lo > hi: the pass listed nothing
+    uint32_t *counts;   // [parts * 4]: chunks each wave listed
+    uint32_t *keys;     // [parts * 4][cap]: chunk index << 4 | mask of its band weights
+    v4u *vals;          // [parts * 4][cap]: the chunk's four fp32 values
+    uint32_t cap;       // list entries per wave
+    int sparts;         // sample blocks of this tensor
+    int sample_begin;   // first block of this tensor in the sample grid
 };
 
 struct WeightBatch {
@@ -226,6 +235,360 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(WeightBatch b)
     }
 }
 
+// --------------------------------------------------------- one-read quantize + pack
+//
+// The two passes above read W twice: the codes need gamma, and gamma needs all of W.  The
+// one-read form reads W once and still gives the codes of the exact rule above, bit for bit:
+//
+//   sample     (sample_block)  reads one 4 KB piece out of every 64 KB of W and sums |w| and
+//              w^2 in fp64: an estimate g of gamma and its standard error;
+//   pass       (one_read_pass_kernel) is the gamma pass (the same blocks, loads and summation
+//              order, so the partial sums and gamma are the same bits), and meanwhile writes
+//              each weight's code against a band lo < hi around the estimated threshold g/2:
+//              |w| > hi gives sign(w), |w| <= lo gives 0, and a weight inside the band gets 0
+//              for now; a chunk (four weights) holding such a weight is listed (its index, a
+//              mask of those weights, its four values) in its wave's region;
+//   fix-up     (one_read_fix_kernel) reduces gamma and tau exactly as quant_pack_kernel does,
+//              checks lo <= tau <= hi, and then ORs the code of every listed weight with
+//              |w| > tau into its word.
+//
+// With lo <= tau <= hi, an unlisted |w| > hi exceeds tau and an unlisted |w| <= lo does not,
+// so every unlisted code equals the exact rule's; the listed ones are decided against tau
+// itself.  The estimate therefore sets only how many weights are listed, never a code.  When
+// the check fails (an unrepresentative sample, gamma == 0, a NaN or an infinity in W, a band
+// too wide to be useful) or a wave's list overflowed, the fix-up block reads its own chunks
+// of W again and writes their codes from tau, as the pack pass would.  A block's chunks are
+// the gamma pass's (chunk i = part * 256 + t + r * parts * 256), so the words of different
+// blocks are disjoint and a block may rewrite its words while other blocks OR fields into
+// theirs.
+
+constexpr int kSampleBlocks = 256;        // sample partial sums per tensor (at most)
+constexpr int64_t kSampleGroup = 4096;    // chunks per 64 KB group; its first 256 are sampled
+constexpr int kSampleChunks = 256;
+constexpr double kBandSigmas = 8.0;       // band half-width in standard errors of the estimate
+constexpr double kBandFloor = 0x1p-12;    // ... plus this relative floor
+constexpr double kBandMax = 0.03;         // wider bands (small samples): no listing, one re-read
+constexpr int kListShare = 16;            // list capacity: one chunk in 16 per wave, plus 64
+
+__host__ __device__ inline int64_t sample_groups(int64_t chunks)
+{
+    return (chunks + kSampleGroup - 1) / kSampleGroup;
+}
+
+// Weights the sample covers: every group's first 256 chunks (fewer in a short last group).
+__host__ __device__ inline double sample_weights(int64_t chunks)
+{
+    const int64_t g = sample_groups(chunks);
+    if (g == 0)
+        return 0.0;
+    const int64_t last = chunks - (g - 1) * kSampleGroup;
+    return 4.0 * (double)((g - 1) * kSampleChunks + (last < kSampleChunks ? last : kSampleChunks));
+}
+
+__device__ __forceinline__ void sample_block(const WeightBatch &b, int bid)
+{
+    __shared__ double lds[2][kGammaThreads / kWave];
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && bid >= b.p[prob + 1].sample_begin)
+        ++prob;
+    const WeightDev &p = b.p[prob];
+    const int s = bid - p.sample_begin;
+    const int64_t groups = sample_groups(p.chunks);
+    const rsrc_t wr = make_rsrc(p.W, (uint32_t)(p.chunks * 16));
+    double a = 0.0, q = 0.0;
+    for (int64_t g = s; g < groups; g += 4 * (int64_t)p.sparts) {
+        v4u v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = (g + u * (int64_t)p.sparts) * kSampleGroup + threadIdx.x;
+            const bool in = g + u * (int64_t)p.sparts < groups && j < p.chunks;
+            v[u] = buf_load16_nt(wr, in ? (uint32_t)(j * 16) : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float x[4] = {__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                                __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a += fabs((double)x[e]);
+                q += (double)x[e] * (double)x[e];
+            }
+        }
+    }
+    a = wave_sum_fixed(a);
+    q = wave_sum_fixed(q);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        lds[0][wave] = a;
+        lds[1][wave] = q;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double ta = lds[0][0], tq = lds[1][0];
+#pragma unroll
+        for (int w = 1; w < kGammaThreads / kWave; ++w) {
+            ta = ta + lds[0][w];
+            tq = tq + lds[1][w];
+        }
+        p.sample[2 * s] = ta;
+        p.sample[2 * s + 1] = tq;
+    }
+}
+
+__global__ __launch_bounds__(kGammaThreads) void sample_kernel(WeightBatch b)
+{
+    sample_block(b, blockIdx.x);
+}
+
+// The band from the sample: the estimated threshold g/2 widened by kBandSigmas standard errors
+// of g (plus kBandFloor), relative.  lo > hi (no band) when the sample says nothing useful.
+// Every wave of the pass computes it from the same sums in the same order, so all agree.
+__device__ __forceinline__ void one_read_band(const WeightDev &p, int lane, float &lo, float &hi)
+{
+    double a = 0.0, q = 0.0;
+#pragma unroll
+    for (int k = 0; k < kSampleBlocks / kWave; ++k) {
+        const int s = lane + k * kWave;
+        a += s < p.sparts ? p.sample[2 * s] : 0.0;
+        q += s < p.sparts ? p.sample[2 * s + 1] : 0.0;
+    }
+    a = wave_sum_fixed(a);
+    q = wave_sum_fixed(q);
+    const double n = sample_weights(p.chunks);
+    const double g = a / n;
+    const double var = q / n - g * g;                  // of |w|
+    const double d = kBandSigmas * sqrt(fmax(var, 0.0) / n) / g + kBandFloor;
+    lo = 1.0f;
+    hi = 0.0f;
+    if (g > 0.0 && g < 1e30 && d < kBandMax) {
+        const double t = 0.5 * g;
+        lo = (float)(t * (1.0 - d));
+        hi = (float)(t * (1.0 + d));
+    }
+}
+
+// A wave-uniform pointer as an opaque register value (not re-read from the kernel arguments).
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *ptr)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
+// The one-read kernels index in 32 bits: their tensors are below 2 GiB (2^27 chunks).
+__device__ __forceinline__ uint32_t word_index(uint32_t quad_wpr, uint32_t j)
+{
+    return quad_wpr ? quad_row_word(j >> 2, quad_wpr) : j >> 2;
+}
+
+// Each wave lists, in a region of its own, the chunks (four weights) that hold a weight inside
+// the band: entry e of wave w (of the tensor's parts * 4 waves) sits at slot w * cap + e, its
+// key (chunk index << 4 | mask of the band's weights) in keys[slot] and the four fp32 values in
+// vals[slot].  The lanes that list a chunk at the same step take consecutive slots (a ballot
+// and a count of the lower lanes), so the stores are contiguous and no lane waits for another.
+__global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatch b)
+{
+    __shared__ double lds[kGammaThreads / kWave];
+    const int bid = blockIdx.x;
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && bid >= b.p[prob + 1].part_begin)
+        ++prob;
+    const WeightDev &p = b.p[prob];
+    const int part = bid - p.part_begin;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    float lo, hi;
+    one_read_band(p, lane, lo, hi);
+    const bool spec = lo <= hi;
+    if (part == 0 && threadIdx.x == 0) {
+        p.band[0] = lo;
+        p.band[1] = hi;
+    }
+    // The band compared on the bits of |w| (non-negative floats order as their bits).  A NaN
+    // or an infinity in W compares above hi and gets a provisional code, but it also makes
+    // gamma NaN or infinite, so the fix-up's check fails and codes this tensor again.
+    const uint32_t lo_bits = __float_as_uint(lo), hi_bits = __float_as_uint(hi);
+    const int wave_global = part * (kGammaThreads / kWave) + wave;
+    // The list's capacity and addresses held in registers for the loop (left as reads of the
+    // kernel arguments, they are loaded again, and waited for, at every listed chunk).
+    const uint32_t cap = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.cap);
+    uint32_t *const keys = uniform_ptr(p.keys) + (size_t)wave_global * cap;
+    v4u *const vals = uniform_ptr(p.vals) + (size_t)wave_global * cap;
+    uint32_t *const packed = uniform_ptr(p.packed);
+    const uint32_t wpr = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.quad_wpr);
+    uint32_t listed = 0;
+    const uint32_t stride = (uint32_t)p.parts * kGammaThreads;
+    const uint32_t chunks = (uint32_t)p.chunks;
+    const rsrc_t wr = make_rsrc(p.W, chunks * 16u);
+    const uint32_t q = (uint32_t)lane & 3u;      // this lane's place in its quad
+    double s = 0.0;
+    auto add4 = [&s](float x, float y, float z, float w) {
+        s += fabs((double)x); s += fabs((double)y);
+        s += fabs((double)z); s += fabs((double)w);
+    };
+    // The loop runs while the wave's first lane has chunks, so every lane takes part in the
+    // quad OR; a lane past the tensor loads zeros, which add nothing to its sum (the gamma
+    // pass's thread would have stopped with the same sum).
+    for (uint32_t iw = (uint32_t)(part * kGammaThreads + wave * kWave); iw < chunks; iw += 8 * stride) {
+        const uint32_t i = iw + lane;
+        v4u v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t j = i + u * stride;
+            v[u] = buf_load16_nt(wr, j < chunks ? j * 16u : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            add4(__uint_as_float(v[u].x), __uint_as_float(v[u].y), __uint_as_float(v[u].z),
+                 __uint_as_float(v[u].w));
+        if (!spec)
+            continue;
+        // Chunk i + u * stride covers word (i + u * stride) / 4, plane q: the lane's byte
+        // plane of the word; the quad OR assembles the word in all four lanes, and the quad's
+        // lane q keeps the words of u = q (wa) and u = q + 4 (wb) to store.
+        uint32_t wa = 0, wb = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t j = i + u * stride;
+            const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            uint32_t bits = 0, m = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t a = x[e] & 0x7FFFFFFFu;
+                bits |= code_field(a > hi_bits, (x[e] >> 31) != 0) << (8 * e);
+                m |= (uint32_t)(a - lo_bits - 1u < hi_bits - lo_bits) << e;   // lo < a <= hi
+            }
+            const uint32_t word = quad_or(bits << (2 * q));
+            if (u < 4)
+                wa = q == (uint32_t)u ? word : wa;
+            else
+                wb = q == (uint32_t)(u - 4) ? word : wb;
+            const bool list = m && j < chunks;
+            const uint64_t mask = __ballot(list);
+            if (mask) {
+                const uint32_t at = listed + __builtin_amdgcn_mbcnt_hi(
+                                                 (uint32_t)(mask >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                if (list && at < cap) {
+                    keys[at] = (j << 4) | m;
+                    vals[at] = v[u];
+                }
+                listed += (uint32_t)__popcll(mask);
+            }
+        }
+        const uint32_t ja = i - q + q * stride;               // the quad's chunks for u = q
+        const uint32_t jb = ja + 4 * stride;
+        if (ja < chunks)
+            packed[word_index(wpr, ja)] = wa;
+        if (jb < chunks)
+            packed[word_index(wpr, jb)] = wb;
+    }
+    if (spec && lane == 0)
+        p.counts[wave_global] = listed;
+    // The gamma pass's block sum, in its order.
+    s = wave_sum_fixed(s);
+    if (lane == 0)
+        lds[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = lds[0];
+#pragma unroll
+        for (int w = 1; w < kGammaThreads / kWave; ++w)
+            t = t + lds[w];
+        p.partials[part] = t;
+    }
+}
+
+__global__ __launch_bounds__(kGammaThreads) void one_read_fix_kernel(WeightBatch b)
+{
+    const int bid = blockIdx.x;
+    int prob = 0;
+#pragma unroll 1
+    while (prob + 1 < b.count && bid >= b.p[prob + 1].part_begin)
+        ++prob;
+    const WeightDev &p = b.p[prob];
+    const int part = bid - p.part_begin;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int wave_global = part * (kGammaThreads / kWave) + wave;
+
+    // gamma and tau exactly as in quant_pack_kernel (the same partial sums, the same order).
+    double part_sum = 0.0;
+    {
+        const rsrc_t pr = make_rsrc(p.partials, (uint32_t)p.parts * 8u);
+        v2u v[kGammaParts / kWave];
+#pragma unroll
+        for (int k = 0; k < kGammaParts / kWave; ++k)
+            v[k] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                                               pr, (lane + k * kWave) * 8, 0, 0));
+#pragma unroll
+        for (int k = 0; k < kGammaParts / kWave; ++k)
+            part_sum += __longlong_as_double((long long)(((uint64_t)v[k].y << 32) | v[k].x));
+    }
+    const double sum = wave_sum_fixed(part_sum);
+    const double count = (double)(p.chunks * 4);
+    const float gamma = p.chunks > 0 ? (float)(sum / count) : 0.0f;
+    if (part == 0 && threadIdx.x == 0)
+        *p.gamma = gamma;
+    const float tau = code_threshold(gamma);
+
+    const float lo = p.band[0], hi = p.band[1];
+    const bool in_band = lo <= hi && lo <= tau && tau <= hi;     // block-uniform
+    const uint32_t n = in_band ? p.counts[wave_global] : 0u;
+    // Every wave of the block must have kept all its entries.
+    const bool listed_ok = in_band && !__syncthreads_or(n > p.cap);
+    if (listed_ok) {
+        for (uint32_t e = lane; e < n; e += kWave) {
+            const size_t slot = (size_t)wave_global * p.cap + e;
+            const uint32_t key = p.keys[slot];
+            const v4u v = p.vals[slot];
+            const uint32_t j = key >> 4, m = key & 15u;
+            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+            uint32_t bits = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float f = __uint_as_float(x[k]);
+                if ((m >> k) & 1u)
+                    bits |= code_field(fabsf(f) > tau, f < 0.0f) << (8 * k);
+            }
+            if (bits)
+                atomicOr(&p.packed[word_index(p.quad_wpr, j)], bits << (2 * (j & 3u)));
+        }
+        return;
+    }
+    // This block's chunks again, coded from tau.
+    const uint32_t stride = (uint32_t)p.parts * kGammaThreads;
+    const uint32_t chunks = (uint32_t)p.chunks;
+    const rsrc_t wr = make_rsrc(p.W, chunks * 16u);
+    for (uint32_t iw = (uint32_t)(part * kGammaThreads + wave * kWave); iw < chunks; iw += 8 * stride) {
+        const uint32_t i = iw + lane;
+        v4u v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t j = i + u * stride;
+            v[u] = buf_load16_nt(wr, j < chunks ? j * 16u : kOOB);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint32_t j = i + u * stride;
+            const int sh = 2 * (int)(j & 3);
+            const float vx = __uint_as_float(v[u].x), vy = __uint_as_float(v[u].y);
+            const float vz = __uint_as_float(v[u].z), vw = __uint_as_float(v[u].w);
+            uint32_t bits = code_field(fabsf(vx) > tau, vx < 0.0f) << (0 + sh);
+            bits |= code_field(fabsf(vy) > tau, vy < 0.0f) << (8 + sh);
+            bits |= code_field(fabsf(vz) > tau, vz < 0.0f) << (16 + sh);
+            bits |= code_field(fabsf(vw) > tau, vw < 0.0f) << (24 + sh);
+            bits = quad_or(bits);
+            if (j < chunks && (j & 3) == 0)
+                p.packed[word_index(p.quad_wpr, j)] = bits;
+        }
+    }
+}
+
 size_t quantize_weights_workspace(int count)
 {
     return (size_t)count * kGammaParts * sizeof(double);
@@ -278,9 +641,139 @@ static int build_weight_batch(const bl_weight_problem *q, int i0, int count, voi
     return i;
 }
 
-hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
-                                   hipStream_t stream, bool quad)
+// ---- one-read form: workspace layout, eligibility, launches
+//
+// Workspace: the count * kGammaParts partial sums of the two-pass form, then per tensor (each
+// piece 256-byte aligned) its sample sums, band, per-wave list counts and list.
+constexpr int64_t kOneReadMinBytes = (int64_t)64 << 20;   // smaller sets keep the two passes
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct OneReadRegion {
+    size_t sample, band, counts, keys, vals, end;
+    uint32_t cap;
+};
+
+static OneReadRegion one_read_region(int64_t chunks, size_t at)
 {
+    OneReadRegion r;
+    const int64_t parts = gamma_parts(chunks);
+    const int64_t per_lane = (chunks + parts * kGammaThreads - 1) / (parts * kGammaThreads);
+    r.cap = (uint32_t)(per_lane * kWave / kListShare + kWave);
+    r.sample = at;
+    at = align256(at + kSampleBlocks * 2 * sizeof(double));
+    r.band = at;
+    at = align256(at + 2 * sizeof(float));
+    const size_t waves = (size_t)parts * (kGammaThreads / kWave);
+    r.counts = at;
+    at = align256(at + waves * sizeof(uint32_t));
+    r.keys = at;
+    at = align256(at + waves * r.cap * sizeof(uint32_t));
+    r.vals = at;
+    at = align256(at + waves * r.cap * sizeof(v4u));
+    r.end = at;
+    return r;
+}
+
+size_t quantize_weights_one_read_workspace(const bl_weight_problem *q, int count)
+{
+    size_t at = align256((size_t)count * kGammaParts * sizeof(double));
+    for (int i = 0; i < count; ++i)
+        at = one_read_region(q[i].N * q[i].K / 4, at).end;
+    return at;
+}
+
+// The one-read form runs when the set is large enough for one read to pay, every tensor is
+// below 2 GiB (32-bit buffer offsets, list keys) and the workspace holds its regions.
+static bool one_read_eligible(const bl_weight_problem *q, int count, size_t workspace_bytes)
+{
+    if (count <= 0 || workspace_bytes == 0)
+        return false;
+    int64_t bytes = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t b = q[i].N * q[i].K * 4;
+        if (b >= ((int64_t)1 << 31))
+            return false;
+        bytes += b;
+    }
+    return bytes >= kOneReadMinBytes && workspace_bytes >= quantize_weights_one_read_workspace(q, count);
+}
+
+static void build_one_read_batch(const bl_weight_problem *q, int count, void *workspace,
+                                 WeightBatch &b, int &sblocks, int &parts, bool quad)
+{
+    char *ws = static_cast<char *>(workspace);
+    size_t region[BL_MAX_GROUP];
+    size_t at = align256((size_t)count * kGammaParts * sizeof(double));
+    for (int i = 0; i < count; ++i) {
+        region[i] = at;
+        at = one_read_region(q[i].N * q[i].K / 4, at).end;
+    }
+    // Largest tensors first in the grids (their blocks run longest); the block-to-chunk map
+    // of each tensor, and so every result, does not depend on the order.
+    int order[BL_MAX_GROUP];
+    for (int i = 0; i < count; ++i) {
+        int j = i;
+        for (; j > 0 && q[order[j - 1]].N * q[order[j - 1]].K < q[i].N * q[i].K; --j)
+            order[j] = order[j - 1];
+        order[j] = i;
+    }
+    sblocks = 0;
+    parts = 0;
+    b.count = 0;
+    for (int k = 0; k < count; ++k) {
+        const int i = order[k];
+        WeightDev &d = b.p[b.count++];
+        d.W = reinterpret_cast<const float4 *>(q[i].W);
+        d.packed = q[i].W_packed;
+        d.gamma = q[i].gamma;
+        d.partials = reinterpret_cast<double *>(ws) + (size_t)i * kGammaParts;
+        d.chunks = q[i].N * q[i].K / 4;
+        d.quad_wpr = quad ? (uint32_t)(q[i].K / 16) : 0u;
+        d.parts = gamma_parts(d.chunks);
+        d.part_begin = parts;
+        parts += d.parts;
+        d.pack_begin = 0;
+        const OneReadRegion r = one_read_region(d.chunks, region[i]);
+        d.sample = reinterpret_cast<double *>(ws + r.sample);
+        d.band = reinterpret_cast<float *>(ws + r.band);
+        d.counts = reinterpret_cast<uint32_t *>(ws + r.counts);
+        d.keys = reinterpret_cast<uint32_t *>(ws + r.keys);
+        d.vals = reinterpret_cast<v4u *>(ws + r.vals);
+        d.cap = r.cap;
+        const int64_t g = sample_groups(d.chunks);
+        d.sparts = (int)(g < kSampleBlocks ? g : kSampleBlocks);
+        d.sample_begin = sblocks;
+        sblocks += d.sparts;
+    }
+}
+
+// The pass and the fix-up (the sample has run before them on the same stream).
+static hipError_t launch_one_read_passes(const WeightBatch &b, int parts, hipStream_t stream)
+{
+    hipLaunchKernelGGL(one_read_pass_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(one_read_fix_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
+                                   hipStream_t stream, bool quad, size_t workspace_bytes)
+{
+    if (one_read_eligible(q, count, workspace_bytes)) {
+        WeightBatch b{};
+        int sblocks, parts;
+        build_one_read_batch(q, count, workspace, b, sblocks, parts, quad);
+        if (sblocks) {
+            hipLaunchKernelGGL(sample_kernel, dim3(sblocks), dim3(kGammaThreads), 0, stream, b);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+        return launch_one_read_passes(b, parts, stream);
+    }
     int i0 = 0;
     while (i0 < count) {
         WeightBatch b{};
@@ -551,15 +1044,20 @@ __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b,
 // launch, γ blocks first; the pack pass follows as its own launch.  Each block runs exactly the
 // code of its own kernel.
 static_assert(kGammaThreads == kActThreads, "one block size for both kinds of block");
-template <int CACHE, bool BF16>
+// SAMPLE: the weight blocks are the one-read form's sample blocks instead of the γ pass.
+template <int CACHE, bool BF16, bool SAMPLE>
 __global__ __launch_bounds__(kActThreads) void gamma_act_kernel(WeightBatch wb, int gblocks, ActBatch ab,
                                                                int rows)
 {
     const int bid = blockIdx.x;
-    if (bid < gblocks)
-        gamma_partial_block(wb, bid);
-    else
+    if (bid < gblocks) {
+        if (SAMPLE)
+            sample_block(wb, bid);
+        else
+            gamma_partial_block(wb, bid);
+    } else {
         act_wave_block<CACHE, BF16>(ab, rows, bid - gblocks);
+    }
 }
 
 // One block per token row for rows longer than the largest wave class.  Thread t handles the
@@ -785,40 +1283,22 @@ static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
 // codes in one launch (gamma_act_kernel), then the pack pass.  Taken when every non-empty
 // activation problem fits the wave kernel (K <= 4096, no FFN activation) with one dtype and
 // the weights form one launch pair; otherwise the two calls' own launches.
-hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
-                                const bl_act_ex_problem *aq, int na, hipStream_t stream, bool quad)
+// The wave-kernel batch of activation problems idx[0 .. n) (one dtype, bf), longest rows first
+// (the row-to-block map changes nothing in the results: every row is quantized on its own).
+static void build_wave_acts(const bl_act_ex_problem *aq, int *idx, int n, int bf, ActBatch &ab,
+                            int &rows, int &cls)
 {
-    int order[BL_MAX_GROUP];
-    int n = 0, bf = -1;
-    bool ok = nw > 0;
-    for (int i = 0; i < na && ok; ++i) {
-        if (aq[i].M == 0)
-            continue;
-        const int cpl = (int)((aq[i].K / 4 + kWave - 1) / kWave);
-        const int dt = aq[i].x_dtype == BL_BF16 ? 1 : 0;
-        ok = aq[i].act == BL_ACT_NONE && cpl <= kActClasses[kActNumClasses - 1] && (bf < 0 || bf == dt);
-        bf = dt;
-        order[n++] = i;
-    }
-    WeightBatch wb{};
-    int parts = 0, blocks = 0;
-    ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks, quad) == nw;
-    if (!ok) {
-        const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream, quad);
-        return e == hipSuccess ? launch_quantize_acts(aq, na, stream) : e;
-    }
-    // Longest rows first, as in the activation launch (the row-to-block map changes nothing
-    // in the results: every row is quantized on its own).
     for (int i = 1; i < n; ++i)
-        for (int j = i; j > 0 && aq[order[j]].K > aq[order[j - 1]].K; --j) {
-            const int t = order[j];
-            order[j] = order[j - 1];
-            order[j - 1] = t;
+        for (int j = i; j > 0 && aq[idx[j]].K > aq[idx[j - 1]].K; --j) {
+            const int t = idx[j];
+            idx[j] = idx[j - 1];
+            idx[j - 1] = t;
         }
-    ActBatch ab{};
-    int rows = 0, cls = 0;
+    ab.count = 0;
+    rows = 0;
+    cls = 0;
     for (int i = 0; i < n; ++i) {
-        const bl_act_ex_problem &s = aq[order[i]];
+        const bl_act_ex_problem &s = aq[idx[i]];
         const int cpl = (int)((s.K / 4 + kWave - 1) / kWave);
         int c = 0;
         while (cpl > kActClasses[c])
@@ -838,17 +1318,89 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
         d.act = BL_ACT_NONE;
         rows += d.M;
     }
-    const dim3 grid((unsigned)(parts + (rows + kActThreads / kWave - 1) / (kActThreads / kWave)));
+}
+
+// One launch: `wblocks` weight blocks (γ pass, or the one-read sample when SAMPLE) and then
+// the wave-kernel activation blocks.
+template <bool SAMPLE>
+static hipError_t launch_weight_act(const WeightBatch &wb, int wblocks, const ActBatch &ab, int rows,
+                                    int cls, int bf, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(wblocks + (rows + kActThreads / kWave - 1) / (kActThreads / kWave)));
     if (bf) {
-        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
-        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
-        else hipLaunchKernelGGL((gamma_act_kernel<16, true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, true, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
+        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, true, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
+        else hipLaunchKernelGGL((gamma_act_kernel<16, true, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
     } else {
-        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
-        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
-        else hipLaunchKernelGGL((gamma_act_kernel<16, false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab, rows);
+        if (cls == 0) hipLaunchKernelGGL((gamma_act_kernel<4, false, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
+        else if (cls == 1) hipLaunchKernelGGL((gamma_act_kernel<8, false, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
+        else hipLaunchKernelGGL((gamma_act_kernel<16, false, SAMPLE>), grid, dim3(kActThreads), 0, stream, wb, wblocks, ab, rows);
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
+                                size_t workspace_bytes, const bl_act_ex_problem *aq, int na,
+                                hipStream_t stream, bool quad)
+{
+    int order[BL_MAX_GROUP];
+    int n = 0, bf = -1;
+    if (one_read_eligible(wq, nw, workspace_bytes)) {
+        // One read of W: the sample shares a launch with the activation problems the wave
+        // kernel takes (one dtype); the other activation problems follow as their own
+        // launches, then the pass and the fix-up.
+        WeightBatch wb{};
+        int sblocks, parts;
+        build_one_read_batch(wq, nw, workspace, wb, sblocks, parts, quad);
+        bl_act_ex_problem rest[BL_MAX_GROUP];
+        int nr = 0;
+        for (int i = 0; i < na; ++i) {
+            if (aq[i].M == 0)
+                continue;
+            const int cpl = (int)((aq[i].K / 4 + kWave - 1) / kWave);
+            const int dt = aq[i].x_dtype == BL_BF16 ? 1 : 0;
+            if (aq[i].act == BL_ACT_NONE && cpl <= kActClasses[kActNumClasses - 1] && (bf < 0 || bf == dt)) {
+                bf = dt;
+                order[n++] = i;
+            } else {
+                rest[nr++] = aq[i];
+            }
+        }
+        hipError_t e = hipSuccess;
+        if (n > 0) {
+            ActBatch ab{};
+            int rows, cls;
+            build_wave_acts(aq, order, n, bf, ab, rows, cls);
+            e = launch_weight_act<true>(wb, sblocks, ab, rows, cls, bf, stream);
+        } else if (sblocks) {
+            hipLaunchKernelGGL(sample_kernel, dim3(sblocks), dim3(kGammaThreads), 0, stream, wb);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess && nr)
+            e = launch_quantize_acts(rest, nr, stream);
+        return e == hipSuccess ? launch_one_read_passes(wb, parts, stream) : e;
+    }
+    bool ok = nw > 0;
+    for (int i = 0; i < na && ok; ++i) {
+        if (aq[i].M == 0)
+            continue;
+        const int cpl = (int)((aq[i].K / 4 + kWave - 1) / kWave);
+        const int dt = aq[i].x_dtype == BL_BF16 ? 1 : 0;
+        ok = aq[i].act == BL_ACT_NONE && cpl <= kActClasses[kActNumClasses - 1] && (bf < 0 || bf == dt);
+        bf = dt;
+        order[n++] = i;
+    }
+    WeightBatch wb{};
+    int parts = 0, blocks = 0;
+    ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks, quad) == nw;
+    if (!ok) {
+        const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream, quad, 0);
+        return e == hipSuccess ? launch_quantize_acts(aq, na, stream) : e;
+    }
+    ActBatch ab{};
+    int rows, cls;
+    build_wave_acts(aq, order, n, bf, ab, rows, cls);
+    hipError_t e = launch_weight_act<false>(wb, parts, ab, rows, cls, bf, stream);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(quant_pack_kernel, dim3(blocks), dim3(kPackThreads), 0, stream, wb);

@@ -126,6 +126,21 @@ bl_status bitlinear_quantize_weights_grouped(const bl_weight_problem *problems, 
                                              void *workspace, size_t workspace_bytes,
                                              void *stream);
 
+/* Workspace with which bitlinear_quantize_weights_grouped, bitlinear_quantize_step and
+ * bitlinear_quantize_step_quad_rows read every fp32 master once instead of twice (steps 1 and
+ * 2 as above, the same codes and gamma bit for bit).  The one-read form samples one 4 KB piece
+ * of every 64 KB of W for an estimate of gamma, and during the gamma pass writes each code
+ * against a band around the estimated threshold, listing the weights inside the band; a short
+ * fix-up pass then reduces gamma exactly, checks that the exact threshold lies inside the
+ * band and decides the listed weights against it (or, where the check fails or a list
+ * overflowed, codes that part of W again from gamma).  It is taken for sets of at least 64 MB
+ * of fp32 weights with every tensor below 2 GiB, when workspace_bytes is at least this size
+ * (about 0.31 N K bytes plus 1.3 MiB per tensor); otherwise the calls read W twice, as with the
+ * smaller workspace.  Returns 0 for an invalid array, count or shape (the errors the calls
+ * report as BL_ERR_NULL, BL_ERR_COUNT and BL_ERR_SHAPE).  The workspace may be reused between
+ * calls on the same stream; calls that overlap on different streams need their own. */
+size_t bitlinear_quantize_weights_one_read_workspace(const bl_weight_problem *problems, int count);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): bitlinear_quantize_weights_grouped
  * without a workspace argument.  The partial sums go to a fixed scratch array inside the

@@ -64,7 +64,7 @@ def test_status_strings(L):
               BL_ERR_HIP, BL_ERR_COUNT):
         assert L.bitlinear_status_string(s)
     assert L.bitlinear_status_string(12345) == b"unknown status"
-    assert L.bitlinear_abi_version() == 103
+    assert L.bitlinear_abi_version() == 104
 
 
 def test_quantize_weights_noalloc_validation(L, bl):
@@ -115,6 +115,29 @@ def test_grouped_count_validation(L, bl):
     assert L.bitlinear_forward_grouped(ctypes.addressof(fa), 0, None) == BL_ERR_COUNT
     aa = (bl._ActProblem * 1)()
     assert L.bitlinear_quantize_acts_grouped(ctypes.addressof(aa), 17, None) == BL_ERR_COUNT
+
+
+def test_one_read_workspace_query(L, bl):
+    """Invalid input gives 0; the size covers the two-read workspace and grows with the
+    tensors (lists of one 20-byte entry per 16 four-weight chunks, plus 64 entries per wave:
+    about 0.31 N K bytes and 1.3 MiB per tensor)."""
+    q = L.bitlinear_quantize_weights_one_read_workspace
+    arr = (bl._WeightProblem * 3)()
+    arr[0] = bl._WeightProblem(A, B, C, 4096, 2560)
+    arr[1] = bl._WeightProblem(A, B, C, 2560, 9728)
+    arr[2] = bl._WeightProblem(A, B, C, 0, 64)
+    assert q(None, 1) == 0
+    assert q(ctypes.addressof(arr), 0) == 0
+    assert q(ctypes.addressof(arr), 17) == 0
+    one, two, three = (q(ctypes.addressof(arr), n) for n in (1, 2, 3))
+    assert one >= L.bitlinear_quantize_weights_grouped_workspace(1)
+    assert one < two < three
+    assert 0.3125 * 4096 * 2560 <= one <= 0.3125 * 4096 * 2560 * 1.05 + (3 << 19)
+    assert 0.3125 * 2560 * 9728 <= two - one <= 0.3125 * 2560 * 9728 * 1.05 + (3 << 19)
+    arr[1] = bl._WeightProblem(A, B, C, 4, 24)
+    assert q(ctypes.addressof(arr), 2) == 0
+    arr[1] = bl._WeightProblem(A, B, C, -1, 64)
+    assert q(ctypes.addressof(arr), 2) == 0
 
 
 def test_forward_mixed_validation(L, bl):

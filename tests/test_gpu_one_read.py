@@ -1,0 +1,137 @@
+"""One-read weight quantization (sample, pass with a listed band, fix-up; taken for sets of at
+least 64 MB of fp32 weights when the workspace holds its lists): gamma and every packed word
+equal bit for bit to the two-read form's, and the codes equal the oracle's at the GPU's gamma
+(gamma within 1e-6 of the oracle's).  Cases: Qwen3-4B-shaped projections in rows and quad rows
+with their step activations; tensors that make the fix-up code its part of W again (a sample
+ten times larger than the rest of the tensor, a list overflow from half the weights sitting on
+the rounding boundary, all zeros, a NaN, an inf), ragged, one-row and empty tensors in a large
+set; and repeated calls giving the same words (the lists' order never reaches a result).
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-6
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def bl(torch):
+    import bit_gemm_02_amd as m
+    m.lib()
+    return m
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def sampled_mask(N, K):
+    """Weights the sample reads: the first 1024 of every 16384 (flat index)."""
+    m = np.zeros(N * K, dtype=bool)
+    for s in range(0, N * K, 16384):
+        m[s:s + 1024] = True
+    return m.reshape(N, K)
+
+
+def check_set(torch, bl, orc, Ws_h, quad=False, acts=False, label=""):
+    """One-read against two-read (bit for bit) and against the oracle."""
+    Ws = [dev(torch, W) for W in Ws_h]
+    total = sum(W.nbytes for W in Ws_h)
+    assert total >= 64 << 20, "the set must be large enough for the one-read form"
+    Xs = [dev(torch, workloads.gaussian((3, W.shape[1]), (611, i), 1.0)) for i, W in enumerate(Ws_h)] if acts else []
+    if acts or quad:
+        w1, x1 = bl.quantize_step(Ws, Xs, quad_rows=quad, one_read=True)
+        w2, x2 = bl.quantize_step(Ws, Xs, quad_rows=quad, one_read=False)
+        for (a, b), (c, d) in zip(x1, x2):
+            assert torch.equal(a, c) and torch.equal(b, d), label
+    else:
+        w1 = bl.quantize_weights_grouped(Ws, one_read=True)
+        w2 = bl.quantize_weights_grouped(Ws, one_read=False)
+    torch.cuda.synchronize()
+    for i, ((P1, g1), (P2, g2), W) in enumerate(zip(w1, w2, Ws_h)):
+        tag = (label, i, W.shape)
+        assert np.array_equal(host(g1).view(np.uint32), host(g2).view(np.uint32)), tag
+        assert torch.equal(P1, P2), tag
+        if W.size == 0:
+            continue
+        g_gpu = np.float32(host(g1)[0])
+        g_orc, _ = orc.gamma(W)
+        if np.isfinite(g_orc):
+            assert abs(float(g_gpu) / float(g_orc) - 1.0) <= REL if g_orc != 0 else g_gpu == 0, tag
+        else:
+            assert not np.isfinite(g_gpu), tag
+        ref = orc.pack(orc.ternary_codes(W, g_gpu))
+        if quad:
+            N, K = W.shape
+            ref = ref.reshape(N // 4, 4, K // 128, 8).transpose(0, 2, 1, 3).reshape(-1)
+        assert np.array_equal(host(P1).view(np.uint32).reshape(-1), ref.reshape(-1)), tag
+
+
+QWEN = [(4096, 2560), (1024, 2560), (1024, 2560), (2560, 4096), (2560, 9728)]
+
+
+@pytest.mark.parametrize("quad", [False, True])
+def test_one_read_qwen_projections(torch, bl, orc, quad):
+    Ws = [workloads.gaussian(s, (610, i), 0.02) for i, s in enumerate(QWEN)]
+    check_set(torch, bl, orc, Ws, quad=quad, acts=True, label=("qwen", quad))
+
+
+def test_one_read_grouped_call(torch, bl, orc):
+    Ws = [workloads.gaussian(s, (612, i), 0.02) for i, s in enumerate(QWEN[:4])]
+    check_set(torch, bl, orc, Ws, label="grouped")
+
+
+def test_one_read_fallbacks(torch, bl, orc):
+    base = workloads.gaussian((4096, 4096), (613, 0), 0.02)
+    # Sample unrepresentative: the sampled pieces ten times larger (the band misses tau).
+    skew = workloads.gaussian((1024, 2560), (613, 1), 0.02)
+    skew[sampled_mask(*skew.shape)] *= np.float32(10)
+    # Half the weights exactly on the boundary: |w| in {1, 3}, gamma = 2, tau = 1 (ties to 0);
+    # every weight of magnitude 1 is listed, far more than a list holds.
+    rng = np.random.default_rng(614)
+    tie = np.where(rng.random((512, 2048)) < 0.5, 1.0, 3.0).astype(np.float32)
+    tie *= np.where(rng.random(tie.shape) < 0.5, -1, 1).astype(np.float32)
+    zero = np.zeros((256, 512), np.float32)
+    nan = workloads.gaussian((64, 1024), (613, 2), 0.02)
+    nan[17, 300] = np.nan
+    inf = workloads.gaussian((64, 1024), (613, 3), 0.02)
+    inf[5, 7] = -np.inf
+    ragged = workloads.gaussian((1001, 2576), (613, 4), 0.02)
+    one = workloads.gaussian((1, 16), (613, 5), 0.02)
+    empty = np.zeros((0, 64), np.float32)
+    Ws = [base, skew, tie, zero, nan, inf, ragged, one, empty]
+    check_set(torch, bl, orc, Ws, label="fallbacks")
+
+
+def test_one_read_tie_and_ragged_quad(torch, bl, orc):
+    """The fall-back coding and the fix-up in the quad-row layout."""
+    base = workloads.gaussian((4096, 4096), (615, 0), 0.02)
+    rng = np.random.default_rng(616)
+    tie = np.where(rng.random((512, 2048)) < 0.5, 1.0, 3.0).astype(np.float32)
+    ragged = workloads.gaussian((1004, 2560), (615, 1), 0.02)
+    check_set(torch, bl, orc, [base, tie, ragged], quad=True, label="quad fallbacks")
+
+
+def test_one_read_repeatable(torch, bl):
+    Ws = [dev(torch, workloads.gaussian(s, (617, i), 0.02)) for i, s in enumerate(QWEN[:4])]
+    a = bl.quantize_weights_grouped(Ws, one_read=True)
+    b = bl.quantize_weights_grouped(Ws, one_read=True)
+    torch.cuda.synchronize()
+    for (P1, g1), (P2, g2) in zip(a, b):
+        assert torch.equal(P1, P2) and torch.equal(g1, g2)
