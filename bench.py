@@ -488,6 +488,9 @@ KERNELS = {
     "gamma_partial_kernel": ("weight_quant", "quant.hip+common.hpp"),
     "gamma_act_kernel": ("gamma_and_act_quant", "quant.hip+common.hpp"),
     "quant_pack_kernel": ("weight_quant", "quant.hip+common.hpp"),
+    "sample_kernel": ("weight_quant", "quant.hip+common.hpp"),
+    "one_read_pass_kernel": ("weight_quant", "quant.hip+common.hpp"),
+    "one_read_fix_kernel": ("weight_quant", "quant.hip+common.hpp"),
 }
 
 # Derived per-kernel figures from hardware counters (per dispatch, averaged over dispatches).
@@ -591,19 +594,27 @@ def summarize_pmc(fetch_csv: str, write_csv: str, workload: str, command: str) -
 
     fk, wk = by_kernel(fetch, f_fetch), by_kernel(write, f_write)
     kernels = {}
+    def per_call(vals):
+        # A call may be several kernels (weight quantization: gamma pass + pack pass, or sample +
+        # pass + fix-up; activation quantization: wave and block kernels): the sum over the
+        # call's kernels of each kernel's mean bytes per dispatch.
+        by_name = defaultdict(list)
+        for name, v in vals:
+            by_name[name].append(v)
+        return (sum(float(np.mean(v)) for v in by_name.values()),
+                min(len(v) for v in by_name.values()), len(by_name))
+
     for (key, src), vals in fk.items():
-        # Weight quantization is a pair of launches per call: report the pair.
-        per_launch = float(np.mean([v for _, v in vals]))
-        wvals = [v for _, v in wk.get((key, src), [])]
-        wr = float(np.mean(wvals)) if wvals else 0.0
-        pair = 2 if key == "weight_quant" else 1
+        fetch_b, launches, nk = per_call(vals)
+        wvals = wk.get((key, src), [])
+        write_b = per_call(wvals)[0] if wvals else 0.0
         kernels[f"{key}@{workload}"] = {"kernel": key, "source": src, "source_sha": source_hash(src),
                                         "workload": workload, "fetch_scale": round(f_fetch, 4),
                                         "write_scale": round(f_write, 4),
-                        "launches": len(vals) // pair,
-                        "fetch_bytes_per_launch": round(per_launch * pair),
-                        "write_bytes_per_launch": round(wr * pair),
-                        "bytes_per_launch": round((per_launch + wr) * pair)}
+                        "launches": launches, "kernels_per_call": nk,
+                        "fetch_bytes_per_launch": round(fetch_b),
+                        "write_bytes_per_launch": round(write_b),
+                        "bytes_per_launch": round(fetch_b + write_b)}
     return {"command": command, "copy_calibration_bytes": copy_bytes,
             "fetch_scale": f_fetch, "write_scale": f_write, "kernels": kernels}
 
