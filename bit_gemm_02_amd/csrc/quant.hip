@@ -368,16 +368,6 @@ __device__ __forceinline__ void one_read_band(const WeightDev &p, int lane, floa
     }
 }
 
-// A wave-uniform pointer as an opaque register value (not re-read from the kernel arguments).
-template <typename T>
-__device__ __forceinline__ T *uniform_ptr(T *ptr)
-{
-    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
-}
-
 // The one-read kernels index in 32 bits: their tensors are below 2 GiB (2^27 chunks).
 __device__ __forceinline__ uint32_t word_index(uint32_t quad_wpr, uint32_t j)
 {
@@ -400,7 +390,7 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatc
     const WeightDev &p = b.p[prob];
     const int part = bid - p.part_begin;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     float lo, hi;
     one_read_band(p, lane, lo, hi);
     const bool spec = lo <= hi;
@@ -413,17 +403,19 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatc
     // gamma NaN or infinite, so the fix-up's check fails and codes this tensor again.
     const uint32_t lo_bits = __float_as_uint(lo), hi_bits = __float_as_uint(hi);
     const int wave_global = part * (kGammaThreads / kWave) + wave;
-    // The list's capacity and addresses held in registers for the loop (left as reads of the
-    // kernel arguments, they are loaded again, and waited for, at every listed chunk).
+    // Every store goes through a buffer resource: buffer stores complete in order with the
+    // weight loads, so the loop waits for each load alone (with flat stores in the loop the
+    // compiler had to wait for all of a step's loads before coding its first chunk), and the
+    // list's stores past this wave's capacity are dropped by the resource's range check.
     const uint32_t cap = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.cap);
-    uint32_t *const keys = uniform_ptr(p.keys) + (size_t)wave_global * cap;
-    v4u *const vals = uniform_ptr(p.vals) + (size_t)wave_global * cap;
-    uint32_t *const packed = uniform_ptr(p.packed);
+    const rsrc_t keys = make_rsrc(p.keys + (size_t)wave_global * cap, cap * 4u);
+    const rsrc_t vals = make_rsrc(p.vals + (size_t)wave_global * cap, cap * 16u);
     const uint32_t wpr = (uint32_t)__builtin_amdgcn_readfirstlane((int)p.quad_wpr);
     uint32_t listed = 0;
     const uint32_t stride = (uint32_t)p.parts * kGammaThreads;
     const uint32_t chunks = (uint32_t)p.chunks;
     const rsrc_t wr = make_rsrc(p.W, chunks * 16u);
+    const rsrc_t pk = make_rsrc(p.packed, chunks);    // chunks / 4 words of 4 bytes
     const uint32_t q = (uint32_t)lane & 3u;      // this lane's place in its quad
     double s = 0.0;
     auto add4 = [&s](float x, float y, float z, float w) {
@@ -473,19 +465,17 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatc
                 const uint32_t at = listed + __builtin_amdgcn_mbcnt_hi(
                                                  (uint32_t)(mask >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-                if (list && at < cap) {
-                    keys[at] = (j << 4) | m;
-                    vals[at] = v[u];
+                if (list) {
+                    __builtin_amdgcn_raw_buffer_store_b32((j << 4) | m, keys, (int)(at * 4u), 0, 0);
+                    buf_store16(vals, at * 16u, v[u]);
                 }
                 listed += (uint32_t)__popcll(mask);
             }
         }
         const uint32_t ja = i - q + q * stride;               // the quad's chunks for u = q
         const uint32_t jb = ja + 4 * stride;
-        if (ja < chunks)
-            packed[word_index(wpr, ja)] = wa;
-        if (jb < chunks)
-            packed[word_index(wpr, jb)] = wb;
+        __builtin_amdgcn_raw_buffer_store_b32(wa, pk, (int)(ja < chunks ? 4u * word_index(wpr, ja) : kOOB), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(wb, pk, (int)(jb < chunks ? 4u * word_index(wpr, jb) : kOOB), 0, 0);
     }
     if (spec && lane == 0)
         p.counts[wave_global] = listed;
