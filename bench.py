@@ -491,6 +491,7 @@ KERNELS = {
     "sample_kernel": ("weight_quant", "quant.hip+common.hpp"),
     "one_read_pass_kernel": ("weight_quant", "quant.hip+common.hpp"),
     "one_read_fix_kernel": ("weight_quant", "quant.hip+common.hpp"),
+    "fix_act_kernel": ("fix_and_act_quant", "quant.hip+common.hpp"),
 }
 
 # Derived per-kernel figures from hardware counters (per dispatch, averaged over dispatches).

@@ -493,9 +493,8 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatc
     }
 }
 
-__global__ __launch_bounds__(kGammaThreads) void one_read_fix_kernel(WeightBatch b)
+__device__ __forceinline__ void one_read_fix_block(const WeightBatch &b, int bid)
 {
-    const int bid = blockIdx.x;
     int prob = 0;
 #pragma unroll 1
     while (prob + 1 < b.count && bid >= b.p[prob + 1].part_begin)
@@ -577,6 +576,11 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_fix_kernel(WeightBatch
                 p.packed[word_index(p.quad_wpr, j)] = bits;
         }
     }
+}
+
+__global__ __launch_bounds__(kGammaThreads) void one_read_fix_kernel(WeightBatch b)
+{
+    one_read_fix_block(b, blockIdx.x);
 }
 
 size_t quantize_weights_workspace(int count)
@@ -739,14 +743,13 @@ static void build_one_read_batch(const bl_weight_problem *q, int count, void *wo
 }
 
 // The pass and the fix-up (the sample has run before them on the same stream).
+static hipError_t launch_one_read_fix(const WeightBatch &b, int parts, hipStream_t stream);
+
 static hipError_t launch_one_read_passes(const WeightBatch &b, int parts, hipStream_t stream)
 {
     hipLaunchKernelGGL(one_read_pass_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(one_read_fix_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? launch_one_read_fix(b, parts, stream) : e;
 }
 
 hipError_t launch_quantize_weights(const bl_weight_problem *q, int count, void *workspace,
@@ -1056,13 +1059,13 @@ __global__ __launch_bounds__(kActThreads) void gamma_act_kernel(WeightBatch wb, 
 // remainder is read again (from L2).  Groups past the row load zeros.  The norm weights are
 // read per group in both passes (L2 hits: every row of the problem shares them).
 template <int C, bool BF16>
-__global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
+__device__ __forceinline__ void act_block_body(const ActBatch &b, int bid)
 {
     constexpr int EPG = BF16 ? 8 : 4;   // activations per 16-byte group
     __shared__ float lds_max[kActThreads / kWave];
     __shared__ double lds_sum[kActThreads / kWave];
-    const ActDev &p = b.p[find_problem(b, (int)blockIdx.x)];
-    const int m = blockIdx.x - p.row_begin;
+    const ActDev &p = b.p[find_problem(b, bid)];
+    const int m = bid - p.row_begin;
     const int groups = p.K / EPG;
     const bool norm = p.g != nullptr;
     const rsrc_t xr = row_rsrc(p, m);
@@ -1155,6 +1158,27 @@ __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b
         quant_group(buf_load16(xr, (uint32_t)j * 16u), j, inv);
     if (tid == 0)
         write_scale(p, m, a, sum, norm);
+}
+
+template <int C, bool BF16>
+__global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
+{
+    act_block_body<C, BF16>(b, blockIdx.x);
+}
+
+// The one-read form's fix-up beside the block kernel's activation rows (the longest rows of a
+// step): blocks [0, fblocks) are fix-up blocks, the rest activation rows; each block runs
+// exactly the code of its own kernel.  The fix-up's short, latency-bound blocks then run
+// under the rows' stream instead of as a launch of their own.
+static_assert(kGammaThreads == kActThreads, "one block size for both kinds of block");
+template <int C, bool BF16>
+__global__ __launch_bounds__(kActThreads) void fix_act_kernel(WeightBatch wb, int fblocks, ActBatch ab)
+{
+    const int bid = blockIdx.x;
+    if (bid < fblocks)
+        one_read_fix_block(wb, bid);
+    else
+        act_block_body<C, BF16>(ab, bid - fblocks);
 }
 
 // One block per token row of an FFN hidden state: h = act(gate, up) from two fp32 rows, then
@@ -1329,6 +1353,62 @@ static hipError_t launch_weight_act(const WeightBatch &wb, int wblocks, const Ac
     return hipGetLastError();
 }
 
+static hipError_t launch_one_read_fix(const WeightBatch &b, int parts, hipStream_t stream)
+{
+    hipLaunchKernelGGL(one_read_fix_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, b);
+    return hipGetLastError();
+}
+
+// The fix-up's `parts` blocks and the block kernel's rows of q[0 .. n) (every row longer than
+// 4096 values, one dtype bf) in one launch, longest rows first.
+static hipError_t launch_fix_acts(const WeightBatch &wb, int parts, const bl_act_ex_problem *q, int n,
+                                  int bf, hipStream_t stream)
+{
+    int order[BL_MAX_GROUP];
+    for (int i = 0; i < n; ++i) {
+        int j = i;
+        for (; j > 0 && q[order[j - 1]].K < q[i].K; --j)
+            order[j] = order[j - 1];
+        order[j] = i;
+    }
+    ActBatch ab{};
+    int rows = 0, gpt = 0;   // gpt: 16-byte groups per thread of the longest row
+    for (int i = 0; i < n; ++i) {
+        const bl_act_ex_problem &s = q[order[i]];
+        ActDev &d = ab.p[ab.count++];
+        d.X = s.X;
+        d.g = s.norm_weight;
+        d.Xq = s.X_q;
+        d.sx = s.x_scale;
+        d.M = (int)s.M;
+        d.K = (int)s.K;
+        d.bf16 = bf;
+        d.eps = s.eps;
+        d.row_begin = rows;
+        d.x2 = nullptr;
+        d.act = BL_ACT_NONE;
+        rows += d.M;
+        gpt = std::max(gpt, (int)((s.K / (bf ? 8 : 4) + kActThreads - 1) / kActThreads));
+    }
+    const dim3 grid((unsigned)(parts + rows));
+    if (bf) {
+        if (gpt <= kActBlockClasses[0])
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[0], true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+        else if (gpt <= kActBlockClasses[1])
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[1], true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+        else
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[2], true>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+    } else {
+        if (gpt <= kActBlockClasses[0])
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[0], false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+        else if (gpt <= kActBlockClasses[1])
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[1], false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+        else
+            hipLaunchKernelGGL((fix_act_kernel<kActBlockClasses[2], false>), grid, dim3(kActThreads), 0, stream, wb, parts, ab);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
                                 size_t workspace_bytes, const bl_act_ex_problem *aq, int na,
                                 hipStream_t stream, bool quad)
@@ -1337,8 +1417,8 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
     int n = 0, bf = -1;
     if (one_read_eligible(wq, nw, workspace_bytes)) {
         // One read of W: the sample shares a launch with the activation problems the wave
-        // kernel takes (one dtype); the other activation problems follow as their own
-        // launches, then the pass and the fix-up.
+        // kernel takes (one dtype), and the fix-up one with those the block kernel takes (one
+        // dtype); the pass runs between them.
         WeightBatch wb{};
         int sblocks, parts;
         build_one_read_batch(wq, nw, workspace, wb, sblocks, parts, quad);
@@ -1366,9 +1446,29 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
             hipLaunchKernelGGL(sample_kernel, dim3(sblocks), dim3(kGammaThreads), 0, stream, wb);
             e = hipGetLastError();
         }
-        if (e == hipSuccess && nr)
-            e = launch_quantize_acts(rest, nr, stream);
-        return e == hipSuccess ? launch_one_read_passes(wb, parts, stream) : e;
+        // Of the rest, the block kernel's rows (longer than 4096, one dtype) share the
+        // fix-up's launch; any others run as launches of their own before the pass.
+        bl_act_ex_problem wide[BL_MAX_GROUP], other[BL_MAX_GROUP];
+        int nwide = 0, nother = 0, wbf = -1;
+        for (int i = 0; i < nr; ++i) {
+            const int cpl = (int)((rest[i].K / 4 + kWave - 1) / kWave);
+            const int dt = rest[i].x_dtype == BL_BF16 ? 1 : 0;
+            if (rest[i].act == BL_ACT_NONE && cpl > kActClasses[kActNumClasses - 1] && (wbf < 0 || wbf == dt)) {
+                wbf = dt;
+                wide[nwide++] = rest[i];
+            } else {
+                other[nother++] = rest[i];
+            }
+        }
+        if (e == hipSuccess && nother)
+            e = launch_quantize_acts(other, nother, stream);
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(one_read_pass_kernel, dim3(parts), dim3(kGammaThreads), 0, stream, wb);
+        e = hipGetLastError();
+        if (e != hipSuccess || nwide == 0)
+            return e == hipSuccess ? launch_one_read_fix(wb, parts, stream) : e;
+        return launch_fix_acts(wb, parts, wide, nwide, wbf, stream);
     }
     bool ok = nw > 0;
     for (int i = 0; i < na && ok; ++i) {

@@ -135,3 +135,41 @@ def test_one_read_repeatable(torch, bl):
     torch.cuda.synchronize()
     for (P1, g1), (P2, g2) in zip(a, b):
         assert torch.equal(P1, P2) and torch.equal(g1, g2)
+
+
+def test_one_read_step_activation_routing(torch, bl, orc):
+    """The step call's activation rows in every launch the one-read form routes them to: fp32
+    rows of up to 4096 values with the sample, bf16 rows longer than 4096 with the fix-up, and
+    the rest (fp32 rows longer than 4096, bf16 rows of up to 4096, a norm) as launches of their
+    own; codes and scales against the two-read call and the oracle."""
+    shapes = [(4096, 2560), (2560, 9728), (1024, 1024)]
+    Ws = [dev(torch, workloads.gaussian(s, (618, i), 0.02)) for i, s in enumerate(shapes)]
+    specs = [(17, 2560, False, False), (9, 9728, True, True), (5, 9728, False, False),
+             (33, 1024, True, False), (3, 4096, False, True)]
+    Xs, host_x, gs = [], [], []
+    for i, (M, K, bf, nm) in enumerate(specs):
+        X = workloads.gaussian((M, K), (619, i), 1.0)
+        g = (np.float32(1) + workloads.gaussian((K,), (620, i), 0.1)) if nm else None
+        if bf:
+            bits = workloads.f32_to_bf16_bits(X)
+            Xs.append(dev(torch, bits.view(np.int16)).view(torch.bfloat16))
+            host_x.append((bits, g, True))
+        else:
+            Xs.append(dev(torch, X))
+            host_x.append((X, g, False))
+        gs.append(None if g is None else dev(torch, g))
+    for quad in (False, True):
+        w1, x1 = bl.quantize_step(Ws, Xs, gs, 1e-6, quad_rows=quad, one_read=True)
+        w2, x2 = bl.quantize_step(Ws, Xs, gs, 1e-6, quad_rows=quad, one_read=False)
+        torch.cuda.synchronize()
+        for (P1, g1), (P2, g2) in zip(w1, w2):
+            assert torch.equal(P1, P2) and torch.equal(g1, g2), quad
+        for i, ((q1, s1), (q2, s2)) in enumerate(zip(x1, x2)):
+            assert torch.equal(q1, q2) and torch.equal(s1, s2), (quad, i)
+            x, g, bf = host_x[i]
+            q_ref, s_ref = orc.quantize_acts(x, g, 1e-6, bf16=bf)
+            assert np.array_equal(host(q1), q_ref), (quad, i)
+            sn = host(s1)
+            nz = s_ref != 0
+            assert np.array_equal(sn == 0, ~nz), (quad, i)
+            assert np.max(np.abs(sn[nz].astype(np.float64) / s_ref[nz] - 1.0)) <= REL, (quad, i)
