@@ -368,6 +368,12 @@ __device__ __forceinline__ void one_read_band(const WeightDev &p, int lane, floa
     }
 }
 
+// Byte e of the result is the top byte of v[e].
+__device__ __forceinline__ uint32_t top_bytes(const uint32_t (&v)[4])
+{
+    return __builtin_amdgcn_perm(v[1], v[0], 0x0c0c0703u) | __builtin_amdgcn_perm(v[3], v[2], 0x07030c0cu);
+}
+
 // The one-read kernels index in 32 bits: their tensors are below 2 GiB (2^27 chunks).
 __device__ __forceinline__ uint32_t word_index(uint32_t quad_wpr, uint32_t j)
 {
@@ -447,25 +453,35 @@ __global__ __launch_bounds__(kGammaThreads) void one_read_pass_kernel(WeightBatc
         for (int u = 0; u < 8; ++u) {
             const uint32_t j = i + u * stride;
             const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            uint32_t bits = 0, m = 0;
+            // Comparisons as sign bits, no compare instructions: with a = |w| and hi below 2^31,
+            // hi - a is negative exactly when a > hi, lo - a when a > lo, and (lo - a) & ~(hi - a)
+            // when lo < a <= hi.  Three byte permutes gather the four weights' top bytes.
+            uint32_t d[4], nb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t a = x[e] & 0x7FFFFFFFu;
-                bits |= code_field(a > hi_bits, (x[e] >> 31) != 0) << (8 * e);
-                m |= (uint32_t)(a - lo_bits - 1u < hi_bits - lo_bits) << e;   // lo < a <= hi
+                d[e] = hi_bits - a;
+                nb[e] = (lo_bits - a) & ~d[e];
             }
+            const uint32_t dtop = top_bytes(d);                // bit 7 of byte e: |w_e| > hi
+            const uint32_t xtop = top_bytes(x);                // bit 7 of byte e: w_e < 0
+            const uint32_t ntop = top_bytes(nb) & 0x80808080u; // bit 7 of byte e: in the band
+            // Byte e: 01 for +1, 11 for -1, 00 for 0 (code_field's fields).
+            const uint32_t bits = ((dtop >> 7) & 0x01010101u) | (((dtop & xtop) >> 6) & 0x02020202u);
             const uint32_t word = quad_or(bits << (2 * q));
             if (u < 4)
                 wa = q == (uint32_t)u ? word : wa;
             else
                 wb = q == (uint32_t)(u - 4) ? word : wb;
-            const bool list = m && j < chunks;
+            const bool list = ntop != 0 && j < chunks;
             const uint64_t mask = __ballot(list);
             if (mask) {
                 const uint32_t at = listed + __builtin_amdgcn_mbcnt_hi(
                                                  (uint32_t)(mask >> 32),
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
                 if (list) {
+                    // The band's weights as a 4-bit mask (bit e of m: weight e).
+                    const uint32_t m = (((ntop >> 7) * 0x01020408u) >> 24) & 15u;
                     __builtin_amdgcn_raw_buffer_store_b32((j << 4) | m, keys, (int)(at * 4u), 0, 0);
                     buf_store16(vals, at * 16u, v[u]);
                 }
