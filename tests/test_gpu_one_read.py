@@ -5,7 +5,9 @@ equal bit for bit to the two-read form's, and the codes equal the oracle's at th
 with their step activations; tensors that make the fix-up code its part of W again (a sample
 ten times larger than the rest of the tensor, a list overflow from half the weights sitting on
 the rounding boundary, all zeros, a NaN, an inf), ragged, one-row and empty tensors in a large
-set; and repeated calls giving the same words (the lists' order never reaches a result).
+set; weights planted on the code boundary and its fp32 neighbours in a tensor whose band holds,
+so that the fix-up decides them; the step call's activation rows in each launch they can take;
+and repeated calls giving the same words (the lists' order never reaches a result).
 """
 
 import numpy as np
@@ -173,3 +175,30 @@ def test_one_read_step_activation_routing(torch, bl, orc):
             nz = s_ref != 0
             assert np.array_equal(sn == 0, ~nz), (quad, i)
             assert np.max(np.abs(sn[nz].astype(np.float64) / s_ref[nz] - 1.0)) <= REL, (quad, i)
+
+
+def test_one_read_weights_on_the_threshold(torch, bl, orc):
+    """Weights at the code boundary and its fp32 neighbours, inside a tensor whose sample gives
+    a good band, so they are listed by the pass and decided by the fix-up."""
+    rng = np.random.default_rng(621)
+    W = workloads.gaussian((4096, 4096), (622, 0), 0.02)
+    idx = rng.choice(W.size, size=600, replace=False)
+    flat = W.reshape(-1)
+    for _ in range(3):
+        g32, _ = orc.gamma(W)
+        # The boundary from the oracle's codes: the smallest fp32 magnitude coded nonzero.
+        cand = np.float32(g32) * np.float32(0.5)
+        probe = np.array([np.nextafter(cand, np.float32(0), dtype=np.float32), cand,
+                          np.nextafter(cand, np.float32(1), dtype=np.float32),
+                          np.nextafter(np.nextafter(cand, np.float32(1), dtype=np.float32),
+                                       np.float32(1), dtype=np.float32)], np.float32)
+        codes = orc.ternary_codes(probe.reshape(1, -1), g32)[0]
+        lo_zero = probe[codes == 0].max()
+        hi_one = probe[codes != 0].min()
+        vals = np.array([lo_zero, hi_one, np.nextafter(lo_zero, np.float32(0), dtype=np.float32),
+                         np.nextafter(hi_one, np.float32(1), dtype=np.float32)], np.float32)
+        signs = np.where(np.arange(idx.size) % 2 == 0, 1, -1).astype(np.float32)
+        flat[idx] = vals[np.arange(idx.size) % 4] * signs
+    Ws = [W, workloads.gaussian((2560, 4096), (622, 1), 0.02)]
+    check_set(torch, bl, orc, Ws, label="threshold")
+    check_set(torch, bl, orc, Ws, quad=True, acts=True, label="threshold quad")
