@@ -256,17 +256,19 @@ def _weight_workspace(arr, count: int, one_read: bool, device) -> torch.Tensor:
 def quantize_weights(W: torch.Tensor, W_packed: Optional[torch.Tensor] = None,
                      gamma: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """W fp32 [N, K] -> (W_packed int32 [N, K/16] holding uint32 words, gamma fp32 [1])."""
+                     stream=None, one_read: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    """W fp32 [N, K] -> (W_packed int32 [N, K/16] holding uint32 words, gamma fp32 [1]).
+    one_read: allocate the workspace with which a tensor of 64 MB or more is read once."""
     _dev(W, "W", torch.float32)
     N, K = W.shape
     if W_packed is None:
         W_packed = torch.empty((N, K // 16), dtype=torch.int32, device=W.device)
     if gamma is None:
         gamma = torch.empty(1, dtype=torch.float32, device=W.device)
-    ws_bytes = quantize_weights_workspace_bytes(1)
     if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=W.device)
+        arr = (_WeightProblem * 1)()
+        arr[0] = _WeightProblem(_ptr(W), _ptr(W_packed), _ptr(gamma), N, K)
+        workspace = _weight_workspace(arr, 1, one_read, W.device)
     _check("bitlinear_quantize_weights",
            lib().bitlinear_quantize_weights(_ptr(W), N, K, _ptr(W_packed), _ptr(gamma),
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),

@@ -202,3 +202,18 @@ def test_one_read_weights_on_the_threshold(torch, bl, orc):
     Ws = [W, workloads.gaussian((2560, 4096), (622, 1), 0.02)]
     check_set(torch, bl, orc, Ws, label="threshold")
     check_set(torch, bl, orc, Ws, quad=True, acts=True, label="threshold quad")
+
+
+def test_one_read_single_tensor_call(torch, bl, orc):
+    """bitlinear_quantize_weights on one 64 MB tensor (the one-read form through the single
+    call) against the two-read call and the oracle."""
+    W = workloads.gaussian((4096, 4096), (623, 0), 0.02)
+    Wd = dev(torch, W)
+    P1, g1 = bl.quantize_weights(Wd, one_read=True)
+    P2, g2 = bl.quantize_weights(Wd, one_read=False)
+    torch.cuda.synchronize()
+    assert torch.equal(P1, P2) and torch.equal(g1, g2)
+    g_gpu = np.float32(host(g1)[0])
+    g_orc, _ = orc.gamma(W)
+    assert abs(float(g_gpu) / float(g_orc) - 1.0) <= REL
+    assert np.array_equal(host(P1).view(np.uint32), orc.pack(orc.ternary_codes(W, g_gpu)))
