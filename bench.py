@@ -1188,7 +1188,8 @@ def main():
                                "beside act quant, decode beside prefill), the decode leg alone on "
                                "a second stream, and on the Qwen3-4B set the quantization of later "
                                "projections on a second stream beside the products of earlier "
-                               "ones (the product's 128 x 256 tile fills every register file)"},
+                               "ones (the product's 128 x 256 tile fills every register file) and "
+                               "the decode leg on a second stream beside the quantization (no gain)"},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(setup, args.cpu_budget_s)
