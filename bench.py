@@ -1105,8 +1105,8 @@ def main():
             wa_bytes, "weight_and_act_quant",
             f"{wa_bytes} bytes (the weight quantization's {wq_bytes} and the activation "
             f"quantization's {aq_bytes}; " +
-            ("one read of W: the sample beside the activation rows of up to 4096 values, the pass, "
-             "then the fix-up beside the longer rows)" if setup.one_read else
+            ("one read of W: the sample, the pass, the fix-up beside the activation rows longer "
+             "than 4096 values, then the other activation rows)" if setup.one_read else
              "two reads of W: gamma pass + activation codes, then the pack pass)"))
     if "weight_quant" in ms:
         rooflines["weight_quant"] = hbm(wq_bytes, "weight_quant",
@@ -1116,9 +1116,9 @@ def main():
                                          if setup.one_read else "the two launches read it twice)"))
     # Dominant kernel = the step's largest single launch: the products' launch (with the decode
     # blocks when the mixed call shares one launch; the product alone where it cannot, with
-    # 128 x 256 tiles).  The quantization call is two or three launches (one-read form: sample
-    # + activation rows, pass, fix-up + long rows; else gamma + activation codes, then the pack
-    # pass), each shorter.
+    # 128 x 256 tiles).  The quantization call is two to four launches (one-read form: sample,
+    # pass, fix-up + long rows, other rows; else gamma + activation codes, then the pack pass),
+    # each shorter.
     fused = setup.mixed_one_launch()
     dom = "prefill_and_decode" if fused else "prefill_gemm"
     traffic = load_traffic()
