@@ -7,7 +7,8 @@ ten times larger than the rest of the tensor, a list overflow from half the weig
 the rounding boundary, all zeros, a NaN, an inf), ragged, one-row and empty tensors in a large
 set; weights planted on the code boundary and its fp32 neighbours in a tensor whose band holds,
 so that the fix-up decides them; the step call's activation rows in each launch they can take;
-and repeated calls giving the same words (the lists' order never reaches a result).
+repeated calls giving the same words (the lists' order never reaches a result); and the step
+call replayed from a captured HIP graph, with eager calls sharing its workspace in between.
 """
 
 import numpy as np
@@ -217,3 +218,51 @@ def test_one_read_single_tensor_call(torch, bl, orc):
     g_orc, _ = orc.gamma(W)
     assert abs(float(g_gpu) / float(g_orc) - 1.0) <= REL
     assert np.array_equal(host(P1).view(np.uint32), orc.pack(orc.ternary_codes(W, g_gpu)))
+
+
+def test_one_read_graph_replays(torch, bl):
+    """The step call in the one-read form captured in a HIP graph and replayed three times,
+    with eager calls on other inputs in between (the workspace's lists, counts and band are
+    rewritten by every call): every replay equals the eager call bit for bit."""
+    shapes = [(4096, 2560), (2560, 9728)]
+    Ws = [dev(torch, workloads.gaussian(s, (624, i), 0.02)) for i, s in enumerate(shapes)]
+    Xs = [dev(torch, workloads.gaussian((65, s[1]), (625, i), 1.0)) for i, s in enumerate(shapes)]
+    Wo = [dev(torch, workloads.gaussian(s, (626, i), 0.03)) for i, s in enumerate(shapes)]
+    ref_w, ref_x = bl.quantize_step(Ws, Xs, quad_rows=True)
+    torch.cuda.synchronize()
+    outs_w = [(torch.empty_like(P), torch.empty_like(g)) for P, g in ref_w]
+    outs_x = [(torch.empty_like(q), torch.empty_like(s)) for q, s in ref_x]
+    nbytes = max(bl.quantize_weights_workspace_bytes(len(Ws)),
+                 bl.quantize_weights_one_read_workspace_bytes(_problems(bl, Ws), len(Ws)))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        bl.quantize_step(Ws, Xs, w_outputs=outs_w, x_outputs=outs_x, workspace=ws, quad_rows=True,
+                         stream=stream)          # warm-up outside capture
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        bl.quantize_step(Ws, Xs, w_outputs=outs_w, x_outputs=outs_x, workspace=ws, quad_rows=True,
+                         stream=stream)
+    for rep in range(3):
+        for P, g in outs_w:
+            P.zero_()
+            g.zero_()
+        # Eager work on other weights through the same workspace between replays.
+        bl.quantize_step(Wo, [], workspace=ws, quad_rows=True)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (P, g), (P2, g2) in zip(outs_w, ref_w):
+            assert torch.equal(P, P2) and torch.equal(g, g2), rep
+        for (q, s), (q2, s2) in zip(outs_x, ref_x):
+            assert torch.equal(q, q2) and torch.equal(s, s2), rep
+
+
+def _problems(bl, Ws):
+    import ctypes
+    arr = (bl._WeightProblem * len(Ws))()
+    for i, W in enumerate(Ws):
+        N, K = W.shape
+        arr[i] = bl._WeightProblem(W.data_ptr(), None, None, N, K)
+    return arr
