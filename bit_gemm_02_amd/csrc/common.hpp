@@ -434,7 +434,9 @@ size_t quantize_weights_workspace(int count);
 size_t quantize_weights_one_read_workspace(const bl_weight_problem *p, int count);
 hipError_t launch_pack_codes(const int8_t *codes, int64_t N, int64_t K, uint32_t *W_packed,
                              hipStream_t stream);
-hipError_t launch_quantize_acts(const bl_act_ex_problem *p, int count, hipStream_t stream);
+// nt: read the rows with the non-temporal hint (a step's fresh inputs, read once).
+hipError_t launch_quantize_acts(const bl_act_ex_problem *p, int count, hipStream_t stream,
+                                bool nt = false);
 hipError_t launch_forward_decode(const bl_forward_ex_problem *p, int count, hipStream_t stream);
 // Fused decode form: every problem has M <= BL_LINEAR_FUSED_MAX_M and M * K within
 // BL_LINEAR_FUSED_MAX_BYTES.

@@ -888,11 +888,9 @@ template <bool BF16>
 struct Group {
     static constexpr int EPG = BF16 ? 8 : 4;
     v4u v;
-    // Non-temporal: a row is read once, and left uncached it does not evict the codes written
-    // just before the product that reads them (the Qwen3-4B step, with the activation rows
-    // quantized last: 0.947-0.958 -> 0.909-0.927 ms; with the rows ahead of the weight pass
-    // the same hint had made the activation launches slower, 195 -> 203-205 us).
-    __device__ __forceinline__ void load(rsrc_t r, int j) { v = buf_load16_nt(r, (uint32_t)j * 16u); }
+    __device__ __forceinline__ void load(rsrc_t r, int j) { v = buf_load16(r, (uint32_t)j * 16u); }
+    // Non-temporal, for the step call's inputs (see kStepNT).
+    __device__ __forceinline__ void load_nt(rsrc_t r, int j) { v = buf_load16_nt(r, (uint32_t)j * 16u); }
     // The group's values as one (fp32) or two (bf16: lo then hi) float4.
     __device__ __forceinline__ float4 f(int half) const
     {
@@ -942,6 +940,14 @@ __device__ __forceinline__ int find_problem(const T &b, int key)
 // all reductions are wave-local (no LDS, no barriers).  Groups past the row load from
 // outside the buffer resource (zeros).
 // Lane l holds the 16-byte groups c * 64 + l (CACHE fp32 groups, or CACHE / 2 bf16 groups).
+// The step call (bitlinear_quantize_step*) reads its activation rows with the non-temporal
+// hint: a step's inputs are read once, and left uncached they do not evict the codes (and
+// packed weights) written just before the product that reads them.  On the Qwen3-4B step,
+// with the activation rows quantized last: 0.947-0.958 -> 0.909-0.927 ms.  The standalone
+// activation calls keep cached loads: in the layer chain a row was written by the previous
+// product and may still be in the caches (there the hint cost 969-974 -> 983-990 us per layer).
+constexpr bool kStepNT = true;
+
 template <int CACHE, bool BF16>
 struct RowBuf {
     static constexpr int NG = BF16 ? CACHE / 2 : CACHE;
@@ -958,12 +964,16 @@ __device__ __forceinline__ rsrc_t act_row_rsrc(const ActBatch &b, int row, int r
     return row_rsrc(b.p[prob], row - b.p[prob].row_begin);
 }
 
-template <int CACHE, bool BF16>
+template <int CACHE, bool BF16, bool NT>
 __device__ __forceinline__ void act_load(RowBuf<CACHE, BF16> &r, rsrc_t xr, int lane)
 {
 #pragma unroll
-    for (int c = 0; c < RowBuf<CACHE, BF16>::NG; ++c)
-        r.x[c].load(xr, c * kWave + lane);  // groups past the row read as zero
+    for (int c = 0; c < RowBuf<CACHE, BF16>::NG; ++c) {  // groups past the row read as zero
+        if constexpr (NT)
+            r.x[c].load_nt(xr, c * kWave + lane);
+        else
+            r.x[c].load(xr, c * kWave + lane);
+    }
 }
 
 // RMSNorm weights of a row's problem (zeros, unused, without a norm): the fp32 quads that
@@ -1029,7 +1039,7 @@ __device__ __forceinline__ void act_quant_row(const RowBuf<CACHE, BF16> &r, cons
         write_scale(p, m, a, ss, norm);
 }
 
-template <int CACHE, bool BF16>
+template <int CACHE, bool BF16, bool NT = false>
 __device__ __forceinline__ void act_wave_block(const ActBatch &b, int rows, int bid)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -1041,15 +1051,15 @@ __device__ __forceinline__ void act_wave_block(const ActBatch &b, int rows, int 
     RowBuf<CACHE, BF16> A;
     NormBuf<CACHE> G;
     int pa;
-    act_load(A, act_row_rsrc(b, r, rows, pa), lane);
+    act_load<CACHE, BF16, NT>(A, act_row_rsrc(b, r, rows, pa), lane);
     norm_load<CACHE, BF16>(G, b.p[pa], lane);
     act_quant_row(A, G, b.p[pa], r - b.p[pa].row_begin, lane);
 }
 
-template <int CACHE, bool BF16>
+template <int CACHE, bool BF16, bool NT>
 __global__ __launch_bounds__(kActThreads) void act_quant_wave_kernel(ActBatch b, int rows)
 {
-    act_wave_block<CACHE, BF16>(b, rows, blockIdx.x);
+    act_wave_block<CACHE, BF16, NT>(b, rows, blockIdx.x);
 }
 
 // The γ partial sums of a weight set and the activation quantization of an input set in one
@@ -1065,7 +1075,7 @@ __global__ __launch_bounds__(kActThreads) void gamma_act_kernel(WeightBatch wb, 
     if (bid < gblocks)
         gamma_partial_block(wb, bid);
     else
-        act_wave_block<CACHE, BF16>(ab, rows, bid - gblocks);
+        act_wave_block<CACHE, BF16, kStepNT>(ab, rows, bid - gblocks);
 }
 
 // One block per token row for rows longer than the largest wave class.  Thread t handles the
@@ -1073,7 +1083,7 @@ __global__ __launch_bounds__(kActThreads) void gamma_act_kernel(WeightBatch wb, 
 // C groups per thread stay in registers between the reduction and the quantization, any
 // remainder is read again (from L2).  Groups past the row load zeros.  The norm weights are
 // read per group in both passes (L2 hits: every row of the problem shares them).
-template <int C, bool BF16>
+template <int C, bool BF16, bool NT>
 __device__ __forceinline__ void act_block_body(const ActBatch &b, int bid)
 {
     constexpr int EPG = BF16 ? 8 : 4;   // activations per 16-byte group
@@ -1134,7 +1144,8 @@ __device__ __forceinline__ void act_block_body(const ActBatch &b, int bid)
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int j = c * kActThreads + tid;
-        raw[c] = buf_load16_nt(xr, j < groups ? (uint32_t)j * 16u : kOOB);   // read once (see Group)
+        raw[c] = NT ? buf_load16_nt(xr, j < groups ? (uint32_t)j * 16u : kOOB)
+                    : buf_load16(xr, j < groups ? (uint32_t)j * 16u : kOOB);
     }
     float amax = 0.0f;
     double ss = 0.0;
@@ -1175,10 +1186,10 @@ __device__ __forceinline__ void act_block_body(const ActBatch &b, int bid)
         write_scale(p, m, a, sum, norm);
 }
 
-template <int C, bool BF16>
+template <int C, bool BF16, bool NT>
 __global__ __launch_bounds__(kActThreads) void act_quant_block_kernel(ActBatch b)
 {
-    act_block_body<C, BF16>(b, blockIdx.x);
+    act_block_body<C, BF16, NT>(b, blockIdx.x);
 }
 
 // The one-read form's fix-up beside the block kernel's activation rows (the longest rows of a
@@ -1193,7 +1204,7 @@ __global__ __launch_bounds__(kActThreads) void fix_act_kernel(WeightBatch wb, in
     if (bid < fblocks)
         one_read_fix_block(wb, bid);
     else
-        act_block_body<C, BF16>(ab, bid - fblocks);
+        act_block_body<C, BF16, kStepNT>(ab, bid - fblocks);
 }
 
 // One block per token row of an FFN hidden state: h = act(gate, up) from two fp32 rows, then
@@ -1300,11 +1311,11 @@ constexpr int kActBlockClasses[] = {4, 8, 16};
 constexpr int kActClasses[] = {4, 8, 16};
 constexpr int kActNumClasses = 3;
 
-template <int CACHE, bool BF16>
+template <int CACHE, bool BF16, bool NT>
 static void launch_wave(const ActBatch &b, int rows, hipStream_t stream)
 {
     const int per_block = kActThreads / kWave;
-    hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16>), dim3((rows + per_block - 1) / per_block),
+    hipLaunchKernelGGL((act_quant_wave_kernel<CACHE, BF16, NT>), dim3((rows + per_block - 1) / per_block),
                        dim3(kActThreads), 0, stream, b, rows);
 }
 
@@ -1464,7 +1475,7 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
             e = nwide ? launch_fix_acts(wb, parts, wide, nwide, wbf, stream)
                       : launch_one_read_fix(wb, parts, stream);
         if (e == hipSuccess && nother)
-            e = launch_quantize_acts(other, nother, stream);
+            e = launch_quantize_acts(other, nother, stream, kStepNT);
         return e;
     }
     bool ok = nw > 0;
@@ -1482,7 +1493,7 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
     ok = ok && n > 0 && build_weight_batch(wq, 0, nw, workspace, wb, parts, blocks, quad) == nw;
     if (!ok) {
         const hipError_t e = launch_quantize_weights(wq, nw, workspace, stream, quad, 0);
-        return e == hipSuccess ? launch_quantize_acts(aq, na, stream) : e;
+        return e == hipSuccess ? launch_quantize_acts(aq, na, stream, kStepNT) : e;
     }
     ActBatch ab{};
     int rows, cls;
@@ -1494,7 +1505,8 @@ hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *works
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream_t stream)
+template <bool NT>
+static hipError_t launch_acts(const bl_act_ex_problem *q, int count, hipStream_t stream)
 {
     // Problems with rows up to 4096 share one wave-kernel launch per dtype, sized by their
     // longest row (shorter rows load zeros past their end); longer rows use the block kernel.
@@ -1548,27 +1560,27 @@ hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream
                 }
                 if (bf) {
                     if (gpt <= kActBlockClasses[0])
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], true, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                     else if (gpt <= kActBlockClasses[1])
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], true, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                     else
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], true>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], true, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                 } else {
                     if (gpt <= kActBlockClasses[0])
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[0], false, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                     else if (gpt <= kActBlockClasses[1])
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[1], false, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                     else
-                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], false>), dim3(rows), dim3(kActThreads), 0, stream, b);
+                        hipLaunchKernelGGL((act_quant_block_kernel<kActBlockClasses[2], false, NT>), dim3(rows), dim3(kActThreads), 0, stream, b);
                 }
             } else if (bf) {
-                if (cls == 0) launch_wave<4, true>(b, rows, stream);
-                else if (cls == 1) launch_wave<8, true>(b, rows, stream);
-                else launch_wave<16, true>(b, rows, stream);
+                if (cls == 0) launch_wave<4, true, NT>(b, rows, stream);
+                else if (cls == 1) launch_wave<8, true, NT>(b, rows, stream);
+                else launch_wave<16, true, NT>(b, rows, stream);
             } else {
-                if (cls == 0) launch_wave<4, false>(b, rows, stream);
-                else if (cls == 1) launch_wave<8, false>(b, rows, stream);
-                else launch_wave<16, false>(b, rows, stream);
+                if (cls == 0) launch_wave<4, false, NT>(b, rows, stream);
+                else if (cls == 1) launch_wave<8, false, NT>(b, rows, stream);
+                else launch_wave<16, false, NT>(b, rows, stream);
             }
             hipError_t e = hipGetLastError();
             if (e != hipSuccess)
@@ -1609,6 +1621,11 @@ hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream
         }
     }
     return hipSuccess;
+}
+
+hipError_t launch_quantize_acts(const bl_act_ex_problem *q, int count, hipStream_t stream, bool nt)
+{
+    return nt ? launch_acts<true>(q, count, stream) : launch_acts<false>(q, count, stream);
 }
 
 // Two-bit packed rows -> base-3 rows (five codes per byte, 80 weights per 16-byte block; byte
