@@ -217,11 +217,16 @@ bl_status bitlinear_quantize_acts_grouped(const bl_act_problem *problems, int co
  *                   needed when nw == 0).
  *   acts, na        as for bitlinear_quantize_acts_grouped (0 <= na <= BL_MAX_GROUP; may be
  *                   NULL when na == 0).
- * Results: bit for bit those of the two grouped calls.  When every non-empty activation
- * problem has K <= 4096 and one dtype, the gamma pass and the activation quantization share
- * one launch and the pack pass follows (two launches instead of three); otherwise the two
- * calls run in order.  The two sets run concurrently: no buffer one set writes may be read or
- * written by the other.
+ * Results: bit for bit those of the two grouped calls.  With the one-read workspace
+ * (bitlinear_quantize_weights_one_read_workspace) and a large enough weight set: the sample,
+ * the one-read pass, the fix-up beside the activation rows longer than 4096 values, then the
+ * other activation rows.  Otherwise, when every non-empty activation problem has K <= 4096 and
+ * one dtype, the gamma pass and the activation quantization share one launch and the pack pass
+ * follows (two launches instead of three), else the two calls run in order.  The activation
+ * rows are read with the non-temporal hint (a step's inputs are read once; left uncached they
+ * do not evict the codes that the step's product reads next); bitlinear_quantize_acts_grouped
+ * reads them through the caches.  The two sets run concurrently: no buffer one set writes may
+ * be read or written by the other.
  * Errors: BL_ERR_COUNT (nw or na outside 0 .. BL_MAX_GROUP, or both 0), BL_ERR_NULL (a NULL
  * array with a nonzero count, or no workspace with nw > 0), then each problem's errors as for
  * the two calls, BL_ERR_ALIGN / BL_ERR_WORKSPACE for the workspace, and BL_ERR_SHAPE when the
