@@ -460,8 +460,11 @@ hipError_t launch_forward_prefill(const bl_forward_ex_problem *p, int count, hip
                                   bool quad = false);
 hipError_t launch_pack_quad_rows(const uint32_t *P, int64_t N, int64_t K, uint32_t *out,
                                  hipStream_t stream);
-// Weight quantization + activation quantization of one step (γ pass and activation codes in
-// one launch when every activation problem takes the wave kernel with one dtype).
+// Weight quantization + activation quantization of one step.  One-read form (workspace large
+// enough, set of 64 MB or more): sample, pass, fix-up beside the block kernel's activation rows,
+// then the other activation rows; else the γ pass and the activation codes in one launch when
+// every activation problem takes the wave kernel with one dtype, then the pack pass.  The
+// activation rows are read non-temporally (a step's inputs, read once).
 hipError_t launch_quantize_step(const bl_weight_problem *wq, int nw, void *workspace,
                                 size_t workspace_bytes, const bl_act_ex_problem *aq, int na,
                                 hipStream_t stream, bool quad = false);
